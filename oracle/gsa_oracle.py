@@ -1,0 +1,361 @@
+"""Plain fp64 CPU oracle for Gist Sparse Attention (GSA) decode and prefill.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this file: only ``tests/``, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` use it. It shares no code, table or helper with
+the HIP library; the two meet only through the seeded inputs.
+
+What is computed follows the pages' description of the method, step by step,
+in float64 on the exact input values (bf16 inputs are widened exactly):
+
+  * interleaved cache -- the sequence is cut into chunks of C raw tokens and
+    one gist token follows every chunk (gist.science explainer "Forget, Then
+    Recall", section 2 'Key Concepts: Interleaved Gist Tokens'; Taki-lab
+    slide deck, slide 3);
+  * routing -- the current query scores every gist key by a dot product
+    (same section, 'Gist as Routing Signals'; German gist.science explainer,
+    'Methodik', step 2);
+  * selection -- the k chunks whose gists score highest are chosen (same
+    section, 'Selective Unfolding'; slide deck, slide 10 worked example);
+  * unfolding + hybrid attention -- softmax attention over the raw tokens of
+    the chosen chunks, their gists and the gists of the chunks not chosen
+    (same section, 'Hybrid Attention'), plus the trailing raw tokens that
+    have no gist yet or that form the uncompressed suffix (slide deck,
+    slide 9, prefix/suffix split);
+  * two-level variant -- meta-gists are scored first, then the gists inside
+    the chosen meta-gist groups, then raw chunks are unfolded (gist.science
+    explainer, 'Hierarchical Extension (H-GSA)', 'Coarse-to-Fine Selection');
+  * prefill -- the same rule applied per query position under causality, i.e.
+    the forward pass of the top-k attention mask of selective finetuning
+    (gist.science explainer, 'Training Procedure: Selective Finetuning').
+
+Readings where the pages are silent (each also listed in the design notes):
+  R1 score = scale * (q . k_gist), scale = 1/sqrt(D) unless given;
+  R2 with grouped-query attention one selection is made per (batch, kv-head):
+     the group score is the mean over the group's query heads of the scaled
+     per-head scores;
+  R3 ties: larger score first, then smaller chunk index; selections are
+     reported in ascending chunk order;
+  R4 every row enters the attention set once (set union) -- a selected chunk
+     that overlaps the tail or window is not counted twice;
+  R5 the tail is the last T raw positions; raw rows past the last gist
+     (0..C of them) must lie inside the tail;
+  R6 prefill eligibility: query t may use gist m only if m < floor(t / C);
+     the window is raw positions [t - W + 1, t];
+  R7 two-level: level-2 gists live in their own array; group i covers chunks
+     [i G, (i + 1) G); the level-1 gists that no full group covers are always
+     candidates; the attention set holds every level-2 gist, every candidate
+     level-1 gist, the raw rows of the selected chunks and the tail.
+
+Parity pins for every function here live in tests/test_oracle.py.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "gist_row_index", "raw_row_index", "topk_ascending",
+    "decode_unit", "decode", "decode_hier_unit", "decode_hier",
+    "prefill_query", "prefill",
+]
+
+
+# ---------------------------------------------------------------- layout ---
+
+def gist_row_index(m: int, C: int) -> int:
+    """Row of gist g_m: the C raw tokens of chunk m come first, then g_m."""
+    return m * (C + 1) + C
+
+
+def raw_row_index(p: int, C: int, M: int) -> int:
+    """Row of raw token at position p (0-based).
+
+    Positions inside the M gisted chunks sit at slot p mod C of chunk p div C;
+    the (at most C) positions after the last gisted chunk follow the last gist.
+    """
+    if p < M * C:
+        return (p // C) * (C + 1) + (p % C)
+    return M * (C + 1) + (p - M * C)
+
+
+# ------------------------------------------------------------- selection ---
+
+def topk_ascending(scores: Sequence[float], ids: Sequence[int], k: int) -> List[int]:
+    """The k ids with the largest score; ties go to the smaller id (R3).
+
+    Returned in ascending id order. If fewer than k ids exist, all are returned.
+    """
+    order = sorted(range(len(ids)), key=lambda i: (-float(scores[i]), int(ids[i])))
+    chosen = [int(ids[i]) for i in order[:k]]
+    return sorted(chosen)
+
+
+def _group_scores(qg: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
+    """S = mean over the group's heads of scale * (q_h . key)  (R1, R2)."""
+    per_head = scale * (keys @ qg.T)          # [n, g]
+    return per_head.mean(axis=1)
+
+
+# ------------------------------------------------------------- attention ---
+
+def _softmax_attend(qg: np.ndarray, keys: np.ndarray, vals: np.ndarray,
+                    scale: float) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Exact softmax attention of each query head over the given rows.
+
+    Returns out [g, D], lse [g] (natural log of sum exp of the scaled logits)
+    and the sum of the softmax weights [g] (1 up to rounding).
+    """
+    g, D = qg.shape
+    out = np.zeros((g, vals.shape[1] if vals.ndim == 2 else D))
+    lse = np.full(g, -np.inf)
+    wsum = np.zeros(g)
+    if keys.shape[0] == 0:
+        out[:] = np.nan
+        return out, lse, wsum
+    for h in range(g):
+        logits = scale * (keys @ qg[h])
+        mx = logits.max()
+        e = np.exp(logits - mx)
+        z = e.sum()
+        w = e / z
+        out[h] = w @ vals
+        lse[h] = mx + math.log(z)
+        wsum[h] = w.sum()
+    return out, lse, wsum
+
+
+def _f64(a: np.ndarray) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def _check_common(n_raw: int, n_gist: int, C: int, R: int) -> None:
+    if C <= 0:
+        raise ValueError("chunk must be positive")
+    if not (0 <= n_raw - n_gist * C <= C):
+        raise ValueError("n_gist must leave 0..C raw tokens after the last gist")
+    if R != n_raw + n_gist:
+        raise ValueError(f"cache has {R} rows, expected {n_raw + n_gist}")
+
+
+# ---------------------------------------------------------------- decode ---
+
+def decode_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, *, n_raw: int,
+                n_gist: int, chunk: int, topk: int, tail: int,
+                scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """One (batch, kv-head) unit of single-level GSA decode.
+
+    qg: [g, D] query heads sharing this kv-head.  K, V: [R, D] interleaved
+    cache of the unit, R = n_raw + n_gist.  Returns out [g, D], lse [g],
+    wsum [g], sel [k] (ascending chunk ids), rows (sorted attention-set rows)
+    and scores [M] (group scores of every gist).
+    """
+    qg = _f64(qg)
+    g, D = qg.shape
+    C, M, N, T = chunk, n_gist, n_raw, tail
+    _check_common(N, M, C, K.shape[0])
+    if not (0 <= topk <= M):
+        raise ValueError("need 0 <= topk <= n_gist")
+    if not (N - M * C <= T <= N):
+        raise ValueError("tail must cover the raw tokens after the last gist")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+    # 1. routing: score every gist
+    gist_rows = [gist_row_index(m, C) for m in range(M)]
+    S = _group_scores(qg, _f64(K[gist_rows]), scale) if M else np.zeros(0)
+    # 2. top-k chunks
+    sel = topk_ascending(S, list(range(M)), topk)
+    # 3. unfold: attention set = all gists + raw of selected chunks + tail
+    A = set(gist_rows)
+    for m in sel:
+        for j in range(C):
+            A.add(raw_row_index(m * C + j, C, M))
+    for p in range(N - T, N):
+        A.add(raw_row_index(p, C, M))
+    rows = np.array(sorted(A), dtype=np.int64)
+    # 4. hybrid softmax attention
+    out, lse, wsum = _softmax_attend(qg, _f64(K[rows]), _f64(V[rows]), scale)
+    return {"out": out, "lse": lse, "wsum": wsum,
+            "sel": np.array(sel, dtype=np.int64), "rows": rows, "scores": S}
+
+
+def _units(B: int, Hkv: int, units: Optional[Iterable[Tuple[int, int]]]):
+    if units is None:
+        return [(b, j) for b in range(B) for j in range(Hkv)]
+    return [(int(b), int(j)) for b, j in units]
+
+
+def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, *, chunk: int,
+           topk: int, tail: int, n_gist: Optional[int] = None,
+           scale: Optional[float] = None,
+           units: Optional[Iterable[Tuple[int, int]]] = None):
+    """Batched single-level decode. q [B, Hq, D]; caches [B, Hkv, R, D].
+
+    Returns out [B, Hq, D], lse [B, Hq], sel [B, Hkv, k] (units not listed in
+    ``units`` are left as NaN / -1).
+    """
+    B, Hq, D = q.shape
+    Hkv, R = k_cache.shape[1], k_cache.shape[2]
+    g = Hq // Hkv
+    if n_gist is None:
+        n_gist = R // (chunk + 1)
+    n_raw = R - n_gist
+    out = np.full((B, Hq, D), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    sel = np.full((B, Hkv, topk), -1, dtype=np.int64)
+    for b, j in _units(B, Hkv, units):
+        r = decode_unit(q[b, j * g:(j + 1) * g], k_cache[b, j], v_cache[b, j],
+                        n_raw=n_raw, n_gist=n_gist, chunk=chunk, topk=topk, tail=tail,
+                        scale=scale)
+        out[b, j * g:(j + 1) * g] = r["out"]
+        lse[b, j * g:(j + 1) * g] = r["lse"]
+        sel[b, j] = r["sel"]
+    return out, lse, sel
+
+
+# ----------------------------------------------------- two-level decode ---
+
+def decode_hier_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, K2: np.ndarray,
+                     V2: np.ndarray, *, n_raw: int, n_gist: int, chunk: int,
+                     fanout: int, topk1: int, topk2: int, tail: int,
+                     scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """One unit of two-level (gist-of-gist) decode (R7).
+
+    K2, V2: [M2, D] level-2 gists, M2 = floor(M / G).
+    Returns out, lse, wsum, sel2 [k2], sel1 [k1] (ascending), cand1 (sorted
+    candidate chunk ids), rows (level-1 cache rows attended).
+    """
+    qg = _f64(qg)
+    g, D = qg.shape
+    C, M, N, T, G = chunk, n_gist, n_raw, tail, fanout
+    _check_common(N, M, C, K.shape[0])
+    if G <= 0:
+        raise ValueError("fanout must be positive")
+    M2 = M // G
+    if K2.shape[0] != M2:
+        raise ValueError(f"level-2 array has {K2.shape[0]} rows, expected {M2}")
+    if not (0 <= topk2 <= M2):
+        raise ValueError("need 0 <= topk2 <= M2")
+    if not (0 <= topk1 <= topk2 * G + (M - M2 * G)):
+        raise ValueError("topk1 exceeds the number of level-1 candidates")
+    if not (N - M * C <= T <= N):
+        raise ValueError("tail must cover the raw tokens after the last gist")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+    # level 2: score the meta-gists, keep the top-k2 groups
+    S2 = _group_scores(qg, _f64(K2), scale) if M2 else np.zeros(0)
+    sel2 = topk_ascending(S2, list(range(M2)), topk2)
+    # level 1 candidates: children of the chosen groups + ungrouped gists
+    cand = sorted({i * G + c for i in sel2 for c in range(G)} | set(range(M2 * G, M)))
+    cand_rows = [gist_row_index(m, C) for m in cand]
+    S1 = _group_scores(qg, _f64(K[cand_rows]), scale) if cand else np.zeros(0)
+    sel1 = topk_ascending(S1, cand, topk1)
+    # attention set: every level-2 gist + candidate gists + unfolded + tail
+    A = set(cand_rows)
+    for m in sel1:
+        for j in range(C):
+            A.add(raw_row_index(m * C + j, C, M))
+    for p in range(N - T, N):
+        A.add(raw_row_index(p, C, M))
+    rows = np.array(sorted(A), dtype=np.int64)
+    keys = np.concatenate([_f64(K2), _f64(K[rows])], axis=0)
+    vals = np.concatenate([_f64(V2), _f64(V[rows])], axis=0)
+    out, lse, wsum = _softmax_attend(qg, keys, vals, scale)
+    return {"out": out, "lse": lse, "wsum": wsum,
+            "sel2": np.array(sel2, dtype=np.int64), "sel1": np.array(sel1, dtype=np.int64),
+            "cand1": np.array(cand, dtype=np.int64), "rows": rows}
+
+
+def decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int, topk1: int,
+                topk2: int, tail: int, n_gist: Optional[int] = None,
+                scale: Optional[float] = None, units=None):
+    """Batched two-level decode. Returns out, lse, sel2 [B,Hkv,k2], sel1 [B,Hkv,k1]."""
+    B, Hq, D = q.shape
+    Hkv, R = k_cache.shape[1], k_cache.shape[2]
+    g = Hq // Hkv
+    if n_gist is None:
+        n_gist = R // (chunk + 1)
+    n_raw = R - n_gist
+    out = np.full((B, Hq, D), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    sel2 = np.full((B, Hkv, topk2), -1, dtype=np.int64)
+    sel1 = np.full((B, Hkv, topk1), -1, dtype=np.int64)
+    for b, j in _units(B, Hkv, units):
+        r = decode_hier_unit(q[b, j * g:(j + 1) * g], k_cache[b, j], v_cache[b, j],
+                             k_l2[b, j], v_l2[b, j], n_raw=n_raw, n_gist=n_gist,
+                             chunk=chunk, fanout=fanout, topk1=topk1, topk2=topk2,
+                             tail=tail, scale=scale)
+        out[b, j * g:(j + 1) * g] = r["out"]
+        lse[b, j * g:(j + 1) * g] = r["lse"]
+        sel2[b, j] = r["sel2"]
+        sel1[b, j, :len(r["sel1"])] = r["sel1"]
+    return out, lse, sel2, sel1
+
+
+# --------------------------------------------------------------- prefill ---
+
+def prefill_query(qg_t: np.ndarray, K: np.ndarray, V: np.ndarray, *, t: int, n_raw: int,
+                  n_gist: int, chunk: int, topk: int, window: int,
+                  scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Causal block-sparse prefill for one query position t and one kv-head (R6).
+
+    qg_t: [g, D] the group's query heads at position t.  K, V: [R, D].
+    Returns out [g, D], lse [g], wsum [g], sel [k] (ascending, -1 padded),
+    rows (sorted attention-set rows).
+    """
+    qg = _f64(qg_t)
+    g, D = qg.shape
+    C, M, N, W = chunk, n_gist, n_raw, window
+    _check_common(N, M, C, K.shape[0])
+    if not (0 <= t < N):
+        raise ValueError("query position outside the sequence")
+    if topk < 0 or W < 1:
+        raise ValueError("need topk >= 0 and window >= 1")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+    # gists of chunks complete before t (their gist row precedes t's row)
+    elig = list(range(min(M, t // C)))
+    erows = [gist_row_index(m, C) for m in elig]
+    S = _group_scores(qg, _f64(K[erows]), scale) if elig else np.zeros(0)
+    sel = topk_ascending(S, elig, topk)
+    A = set(erows)
+    for m in sel:
+        for j in range(C):
+            A.add(raw_row_index(m * C + j, C, M))
+    for p in range(max(0, t - W + 1), t + 1):
+        A.add(raw_row_index(p, C, M))
+    rows = np.array(sorted(A), dtype=np.int64)
+    out, lse, wsum = _softmax_attend(qg, _f64(K[rows]), _f64(V[rows]), scale)
+    padded = np.full(topk, -1, dtype=np.int64)
+    padded[:len(sel)] = sel
+    return {"out": out, "lse": lse, "wsum": wsum, "sel": padded, "rows": rows}
+
+
+def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, *, chunk: int,
+            topk: int, window: int, q_start: int, n_gist: Optional[int] = None,
+            scale: Optional[float] = None,
+            queries: Optional[Iterable[Tuple[int, int]]] = None):
+    """Prefill for query positions q_start + i, i < n_q, of one sequence.
+
+    q: [Hq, n_q, D]; caches [Hkv, R, D]. ``queries`` lists (i, kv_head) pairs
+    to compute (default: all). Returns out [Hq, n_q, D], sel [Hkv, n_q, k].
+    """
+    Hq, n_q, D = q.shape
+    Hkv, R = k_cache.shape[0], k_cache.shape[1]
+    g = Hq // Hkv
+    if n_gist is None:
+        n_gist = R // (chunk + 1)
+    n_raw = R - n_gist
+    out = np.full((Hq, n_q, D), np.nan)
+    sel = np.full((Hkv, n_q, topk), -1, dtype=np.int64)
+    todo = ([(i, j) for j in range(Hkv) for i in range(n_q)] if queries is None
+            else [(int(i), int(j)) for i, j in queries])
+    for i, j in todo:
+        r = prefill_query(q[j * g:(j + 1) * g, i], k_cache[j], v_cache[j], t=q_start + i,
+                          n_raw=n_raw, n_gist=n_gist, chunk=chunk, topk=topk,
+                          window=window, scale=scale)
+        out[j * g:(j + 1) * g, i] = r["out"]
+        sel[j, i] = r["sel"]
+    return out, sel

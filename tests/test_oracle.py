@@ -1,0 +1,414 @@
+"""Pins for the fp64 oracle: each checks it against something other than itself.
+
+Kinds of pin (so that a dropped term, a wrong sign or index, or a transposed
+operand in the oracle fails at least one):
+  * values printed on the pages (slide 10 worked example, tests/golden/);
+  * brute force over all k-subsets on tiny inputs;
+  * reductions to an independent library routine (torch SDPA in float64):
+    k = M gives full attention, k = 0 gives gists + tail, two-level with
+    everything selected gives full attention over both levels, prefill with
+    k >= |eligible| gives row-causal full attention;
+  * closed forms (q = 0 -> plain mean over the attention set; constant V;
+    one saturating key);
+  * metamorphic relations (chunk permutation) and an independent dense-mask
+    formulation that maps rows back to positions (the oracle maps positions
+    to rows).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------- helpers ----
+
+def sdpa(qg, K, V, mask, scale):
+    """Independent reference: torch SDPA (float64, CPU) of g heads over masked rows."""
+    q = torch.tensor(qg, dtype=torch.float64)[None, :, None, :]          # [1,g,1,D]
+    k = torch.tensor(K, dtype=torch.float64)[None, None].expand(1, qg.shape[0], -1, -1)
+    v = torch.tensor(V, dtype=torch.float64)[None, None].expand(1, qg.shape[0], -1, -1)
+    m = torch.tensor(mask, dtype=torch.bool)[None, None, None, :]
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m, scale=scale)
+    return o[0, :, 0, :].numpy()
+
+
+def rand_unit(rng, g, D, N, C, M=None):
+    M = N // C if M is None else M
+    R = N + M
+    return (rng.standard_normal((g, D)), rng.standard_normal((R, D)),
+            rng.standard_normal((R, D)), M, R)
+
+
+def row_kind(r, C, M):
+    """Inverse map, written independently of the oracle: row -> ('gist', m) or ('raw', p)."""
+    if r < M * (C + 1):
+        m, s = divmod(r, C + 1)
+        return ("gist", m) if s == C else ("raw", m * C + s)
+    return ("raw", M * C + (r - M * (C + 1)))
+
+
+# ------------------------------------------------- values from the pages ---
+
+def test_slide10_worked_example():
+    """Slide 10: scores 0.1/0.8/0.7/0.2 with k=2 select g2, g3 and unfold chunks 2, 3."""
+    gold = json.load(open(os.path.join(GOLDEN, "slide10_topk.json")))
+    S = gold["scores"]
+    M, C, D = len(S), 2, 4
+    N = M * C
+    R = N + M
+    K = np.zeros((R, D))
+    V = np.arange(R * D, dtype=np.float64).reshape(R, D)
+    for m, s in enumerate(S):
+        K[m * (C + 1) + C, 0] = s          # gist key of chunk m scores exactly s
+    qg = np.array([[1.0, 0.0, 0.0, 0.0]])
+    r = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=gold["k"], tail=0,
+                           scale=1.0)
+    assert list(r["sel"] + 1) == gold["selected_gists_1based"]
+    np.testing.assert_allclose(r["scores"], S, rtol=0, atol=0)
+    # unfolded chunks: their raw rows are in the set; other chunks' raw rows are not
+    raw_in = sorted({row_kind(x, C, M)[1] // C + 1 for x in r["rows"]
+                     if row_kind(x, C, M)[0] == "raw"})
+    assert raw_in == gold["unfolded_chunks_1based"]
+    gists_in = sorted(row_kind(x, C, M)[1] for x in r["rows"] if row_kind(x, C, M)[0] == "gist")
+    assert gists_in == list(range(M))      # every gist stays (hybrid attention)
+
+
+def test_score_formula_one_hot_queries():
+    """With q_h = e_{d_h} / scale, the group score of gist m is the mean of K[g_m, d_h]."""
+    rng = np.random.default_rng(0)
+    g, D, C, N = 3, 8, 4, 32
+    _, K, V, M, R = rand_unit(rng, g, D, N, C)
+    scale = 0.37
+    dims = [5, 1, 6]
+    qg = np.zeros((g, D))
+    for h, d in enumerate(dims):
+        qg[h, d] = 1.0 / scale
+    r = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=2, tail=4, scale=scale)
+    for m in range(M):
+        want = (K[m * (C + 1) + C, 5] + K[m * (C + 1) + C, 1] + K[m * (C + 1) + C, 6]) / 3
+        assert abs(r["scores"][m] - want) < 1e-12
+
+
+# ------------------------------------------------------------ brute force --
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_bruteforce_subsets(seed):
+    """Selected set maximises the summed group score over all C(M, k) subsets."""
+    rng = np.random.default_rng(100 + seed)
+    g, D, C = 2, 6, 3
+    M = int(rng.integers(1, 11))
+    N = M * C
+    _, K, V, M, R = rand_unit(rng, g, D, N, C, M)
+    qg = rng.standard_normal((g, D))
+    k = int(rng.integers(0, M + 1))
+    r = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=k, tail=0)
+    S = r["scores"]
+    best, second = None, -math.inf
+    best_val = -math.inf
+    for sub in itertools.combinations(range(M), k):
+        val = sum(S[list(sub)]) if sub else 0.0
+        if val > best_val:
+            best, second, best_val = sub, best_val, val
+        elif val > second:
+            second = val
+    assert tuple(r["sel"]) == tuple(sorted(best))
+    assert list(r["sel"]) == sorted(r["sel"])
+
+
+def test_topk_ties_prefer_smaller_index_and_negative_zero():
+    """q = 0 gives every score +0 or -0: the k smallest chunk ids win."""
+    C, D, M = 4, 8, 9
+    N = M * C
+    R = N + M
+    K = -np.abs(np.random.default_rng(1).standard_normal((R, D)))   # 0 * negative = -0
+    V = np.random.default_rng(2).standard_normal((R, D))
+    r = oracle.decode_unit(np.zeros((2, D)), K, V, n_raw=N, n_gist=M, chunk=C, topk=4, tail=0)
+    assert list(r["sel"]) == [0, 1, 2, 3]
+
+
+# --------------------------------------------------- library reductions ---
+
+@pytest.mark.parametrize("C,M,r", [(4, 12, 0), (8, 5, 3), (16, 6, 16), (3, 7, 1)])
+def test_k_equals_M_is_full_attention(C, M, r):
+    rng = np.random.default_rng(C * 100 + M)
+    g, D = 4, 16
+    N = M * C + r
+    R = N + M
+    qg, K, V = rng.standard_normal((g, D)), rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    res = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=M, tail=r)
+    ref = sdpa(qg, K, V, np.ones(R, bool), 1 / math.sqrt(D))
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+    assert len(res["rows"]) == R
+
+
+@pytest.mark.parametrize("T", [0, 1, 5, 16, 23])
+def test_k_zero_is_gists_plus_tail(T):
+    rng = np.random.default_rng(T)
+    g, D, C, M = 2, 8, 4, 10
+    N = M * C
+    R = N + M
+    qg, K, V = rng.standard_normal((g, D)), rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    res = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=0, tail=T, scale=0.3)
+    mask = np.zeros(R, bool)
+    mask[np.arange(C, R, C + 1)] = True                       # gist rows
+    raw = np.setdiff1d(np.arange(R), np.arange(C, R, C + 1))  # raw rows in position order
+    if T:
+        mask[raw[-T:]] = True
+    ref = sdpa(qg, K, V, mask, 0.3)
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+
+
+def test_softmax_weights_sum_to_one_and_lse():
+    rng = np.random.default_rng(7)
+    g, D, C, M = 4, 32, 16, 40
+    N = M * C
+    qg, K, V = (rng.standard_normal((g, D)) * 3, rng.standard_normal((N + M, D)),
+                rng.standard_normal((N + M, D)))
+    res = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=5, tail=20)
+    assert np.all(np.abs(res["wsum"] - 1) <= 1e-12)
+    # lse against a direct log-sum-exp over the attention set (scipy routine)
+    from scipy.special import logsumexp
+    for h in range(g):
+        lg = (K[res["rows"]] @ qg[h]) / math.sqrt(D)
+        assert abs(res["lse"][h] - logsumexp(lg)) < 1e-10
+
+
+# ----------------------------------------------------------- closed forms --
+
+def test_q_zero_mean_over_attention_set_with_tail_overlap():
+    """q = 0: uniform weights; set = gists + chunks 0..k-1 + tail, overlap counted once.
+
+    M=6, C=4, N=24, k=3, T=14: the tail (positions 10..23) overlaps chunk 2.
+    Rows written out by hand: gists 4,9,14,19,24,29; chunk 0 rows 0-3; chunk 1
+    rows 5-8; chunk 2 rows 10-13 (positions 8..11, of which 10,11 are also tail);
+    tail positions 12..23 -> rows 15-18, 20-23, 25-28.
+    """
+    C, M, N, k, T, D = 4, 6, 24, 3, 14, 5
+    R = N + M
+    V = np.random.default_rng(3).standard_normal((R, D))
+    K = np.random.default_rng(4).standard_normal((R, D))
+    res = oracle.decode_unit(np.zeros((1, D)), K, V, n_raw=N, n_gist=M, chunk=C, topk=k,
+                             tail=T)
+    rows = [4, 9, 14, 19, 24, 29, 0, 1, 2, 3, 5, 6, 7, 8, 10, 11, 12, 13,
+            15, 16, 17, 18, 20, 21, 22, 23, 25, 26, 27, 28]
+    assert sorted(rows) == list(res["rows"])
+    assert len(rows) == M + k * C + T - 2
+    np.testing.assert_allclose(res["out"][0], V[rows].mean(0), rtol=0, atol=1e-13)
+
+
+def test_constant_values_give_constant_output():
+    rng = np.random.default_rng(5)
+    g, D, C, M = 4, 16, 8, 20
+    N = M * C
+    R = N + M
+    c = rng.standard_normal(D)
+    V = np.tile(c, (R, 1))
+    res = oracle.decode_unit(rng.standard_normal((g, D)) * 4, rng.standard_normal((R, D)), V,
+                             n_raw=N, n_gist=M, chunk=C, topk=3, tail=8)
+    np.testing.assert_allclose(res["out"], np.tile(c, (g, 1)), rtol=0, atol=1e-12)
+
+
+def test_saturating_key_returns_its_value():
+    rng = np.random.default_rng(6)
+    D, C, M = 16, 4, 10
+    N = M * C
+    R = N + M
+    K = rng.standard_normal((R, D)) * 0.1
+    V = rng.standard_normal((R, D))
+    q = rng.standard_normal(D)
+    q /= np.linalg.norm(q)
+    # row 48 (raw position 39, the newest token, in the tail) scores +40 above the rest
+    K[48] = q * 40 * math.sqrt(D)
+    res = oracle.decode_unit(q[None], K, V, n_raw=N, n_gist=M, chunk=C, topk=2, tail=4)
+    assert 48 in res["rows"]
+    np.testing.assert_allclose(res["out"][0], V[48], rtol=0, atol=50 * math.exp(-40) + 1e-15)
+
+
+# --------------------------------------------- metamorphic / formulations --
+
+def test_chunk_permutation_permutes_selection():
+    rng = np.random.default_rng(8)
+    g, D, C, M, T = 2, 8, 4, 12, 8          # tail = chunks 10, 11
+    N = M * C
+    R = N + M
+    qg, K, V = rng.standard_normal((g, D)), rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    base = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=4, tail=T)
+    perm = list(rng.permutation(10)) + [10, 11]      # move whole chunks (raw + gist)
+    K2, V2 = np.empty_like(K), np.empty_like(V)
+    for new, old in enumerate(perm):
+        K2[new * (C + 1):(new + 1) * (C + 1)] = K[old * (C + 1):(old + 1) * (C + 1)]
+        V2[new * (C + 1):(new + 1) * (C + 1)] = V[old * (C + 1):(old + 1) * (C + 1)]
+    res = oracle.decode_unit(qg, K2, V2, n_raw=N, n_gist=M, chunk=C, topk=4, tail=T)
+    assert sorted(perm[m] for m in res["sel"]) == list(base["sel"])
+    np.testing.assert_allclose(res["out"], base["out"], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("C,M,r,k,T", [(4, 10, 0, 3, 6), (8, 7, 5, 2, 13), (16, 9, 16, 4, 40),
+                                       (2, 15, 1, 15, 3)])
+def test_gather_equals_dense_mask(C, M, r, k, T):
+    """Logits over every row, masked by a row->position classification of our own."""
+    rng = np.random.default_rng(C + M + r)
+    g, D = 3, 8
+    N = M * C + r
+    R = N + M
+    qg, K, V = rng.standard_normal((g, D)), rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    res = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=k, tail=T)
+    sel = set(res["sel"].tolist())
+    mask = np.zeros(R, bool)
+    for x in range(R):
+        kind, v = row_kind(x, C, M)
+        if kind == "gist":
+            mask[x] = True
+        elif v >= N - T or (v // C < M and v // C in sel):
+            mask[x] = True
+    ref = sdpa(qg, K, V, mask, 1 / math.sqrt(D))
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+    assert mask.sum() == len(res["rows"])
+
+
+# ------------------------------------------------------------- two-level ---
+
+def _hier_inputs(rng, g, D, C, M, G, r=0):
+    N = M * C + r
+    R = N + M
+    M2 = M // G
+    return (rng.standard_normal((g, D)), rng.standard_normal((R, D)),
+            rng.standard_normal((R, D)), rng.standard_normal((M2, D)),
+            rng.standard_normal((M2, D)), N, R, M2)
+
+
+def test_hier_everything_selected_is_full_attention_over_both_levels():
+    rng = np.random.default_rng(11)
+    g, D, C, M, G = 4, 16, 4, 22, 4          # M2 = 5 groups, 2 orphan gists
+    qg, K, V, K2, V2, N, R, M2 = _hier_inputs(rng, g, D, C, M, G)
+    res = oracle.decode_hier_unit(qg, K, V, K2, V2, n_raw=N, n_gist=M, chunk=C, fanout=G,
+                                  topk1=M, topk2=M2, tail=0)
+    ref = sdpa(qg, np.concatenate([K2, K]), np.concatenate([V2, V]), np.ones(M2 + R, bool),
+               1 / math.sqrt(D))
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+
+
+def test_hier_all_groups_reduces_to_single_level_plus_level2_rows():
+    rng = np.random.default_rng(12)
+    g, D, C, M, G, k1, T = 2, 8, 4, 16, 4, 3, 6
+    qg, K, V, K2, V2, N, R, M2 = _hier_inputs(rng, g, D, C, M, G)
+    h = oracle.decode_hier_unit(qg, K, V, K2, V2, n_raw=N, n_gist=M, chunk=C, fanout=G,
+                                topk1=k1, topk2=M2, tail=T)
+    s = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=k1, tail=T)
+    assert list(h["sel1"]) == list(s["sel"])
+    mask = np.zeros(R, bool)
+    mask[s["rows"]] = True
+    ref = sdpa(qg, np.concatenate([K2, K]), np.concatenate([V2, V]),
+               np.concatenate([np.ones(M2, bool), mask]), 1 / math.sqrt(D))
+    np.testing.assert_allclose(h["out"], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_hier_coarse_to_fine_bruteforce(seed):
+    """Level 2 picks the best k2 groups by brute force; level 1 the best k1 of their
+    children (plus orphans); the set holds all candidates' gists."""
+    rng = np.random.default_rng(200 + seed)
+    g, D, C, G = 2, 6, 2, 3
+    M = int(rng.integers(3, 14))
+    qg, K, V, K2, V2, N, R, M2 = _hier_inputs(rng, g, D, C, M, G)
+    k2 = int(rng.integers(0, M2 + 1))
+    n_c = k2 * G + (M - M2 * G)
+    k1 = int(rng.integers(0, n_c + 1))
+    h = oracle.decode_hier_unit(qg, K, V, K2, V2, n_raw=N, n_gist=M, chunk=C, fanout=G,
+                                topk1=k1, topk2=k2, tail=0)
+    s2 = (K2 @ qg.T).mean(1)
+    best2 = max(itertools.combinations(range(M2), k2), key=lambda s: sum(s2[list(s)]))
+    assert tuple(h["sel2"]) == tuple(sorted(best2))
+    cand = sorted({i * G + c for i in best2 for c in range(G)} | set(range(M2 * G, M)))
+    assert list(h["cand1"]) == cand
+    s1 = {m: (K[m * (C + 1) + C] @ qg.T).mean() for m in cand}
+    best1 = max(itertools.combinations(cand, k1), key=lambda s: sum(s1[m] for m in s))
+    assert tuple(h["sel1"]) == tuple(sorted(best1))
+    gist_rows = {m * (C + 1) + C for m in cand}
+    assert gist_rows <= set(h["rows"].tolist())
+
+
+def test_hier_orphan_gist_is_always_a_candidate():
+    rng = np.random.default_rng(13)
+    g, D, C, M, G = 1, 4, 2, 7, 3            # groups {0,1,2},{3,4,5}; orphan 6
+    qg, K, V, K2, V2, N, R, M2 = _hier_inputs(rng, g, D, C, M, G)
+    qg = np.array([[1.0, 0, 0, 0]])
+    K2[:, 0] = [5.0, -5.0]                   # group 0 wins level 2
+    K[6 * (C + 1) + C, 0] = 50.0             # orphan 6 is the best level-1 gist overall
+    h = oracle.decode_hier_unit(qg, K, V, K2, V2, n_raw=N, n_gist=M, chunk=C, fanout=G,
+                                topk1=1, topk2=1, tail=0, scale=1.0)
+    assert list(h["sel2"]) == [0]
+    assert list(h["sel1"]) == [6]
+    assert list(h["cand1"]) == [0, 1, 2, 6]
+
+
+# ---------------------------------------------------------------- prefill --
+
+@pytest.mark.parametrize("k", [0, 3])
+@pytest.mark.parametrize("t", [0, 3, 15, 16, 31, 47, 63, 100, 127])
+def test_prefill_row_equals_decode_on_truncated_cache(t, k):
+    rng = np.random.default_rng(14)
+    g, D, C, W = 2, 8, 16, 24
+    N = 128
+    M = N // C
+    R = N + M
+    K, V = rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    qg = rng.standard_normal((g, D))
+    p = oracle.prefill_query(qg, K, V, t=t, n_raw=N, n_gist=M, chunk=C, topk=k, window=W)
+    Mt = t // C
+    Rt = (t + 1) + Mt
+    d = oracle.decode_unit(qg, K[:Rt], V[:Rt], n_raw=t + 1, n_gist=Mt, chunk=C,
+                           topk=min(k, Mt), tail=min(W, t + 1))
+    np.testing.assert_allclose(p["out"], d["out"], rtol=0, atol=1e-13)
+    assert list(p["sel"][:len(d["sel"])]) == list(d["sel"])
+    assert all(x == -1 for x in p["sel"][len(d["sel"]):])
+
+
+@pytest.mark.parametrize("t", [0, 5, 16, 40, 79])
+def test_prefill_all_eligible_is_row_causal_full_attention(t):
+    rng = np.random.default_rng(15)
+    g, D, C, N = 2, 8, 8, 80
+    M = N // C
+    R = N + M
+    K, V, qg = rng.standard_normal((R, D)), rng.standard_normal((R, D)), rng.standard_normal((g, D))
+    # window C covers the query's own, still gist-less chunk
+    p = oracle.prefill_query(qg, K, V, t=t, n_raw=N, n_gist=M, chunk=C, topk=M, window=C)
+    own_row = (t // C) * (C + 1) + t % C
+    mask = np.arange(R) <= own_row
+    ref = sdpa(qg, K, V, mask, 1 / math.sqrt(D))
+    np.testing.assert_allclose(p["out"], ref, rtol=0, atol=1e-12)
+
+
+def test_prefill_own_chunk_gist_is_not_eligible():
+    D, C, N = 4, 4, 32
+    M = N // C
+    R = N + M
+    K = np.zeros((R, D))
+    V = np.random.default_rng(16).standard_normal((R, D))
+    t = 3 * C + C - 1                        # last raw token of chunk 3
+    K[3 * (C + 1) + C, 0] = 100.0            # gist of chunk 3 comes after t's row
+    K[1 * (C + 1) + C, 0] = 1.0
+    p = oracle.prefill_query(np.array([[1.0, 0, 0, 0]]), K, V, t=t, n_raw=N, n_gist=M, chunk=C,
+                             topk=1, window=2, scale=1.0)
+    assert list(p["sel"]) == [1]
+    assert 3 * (C + 1) + C not in p["rows"]
+
+
+def test_prefill_window_rows_literal():
+    """t=10, C=4, W=3, k=0: gists 0,1 (rows 4, 9) + positions 8,9,10 (rows 10, 11, 12)."""
+    D, C, N = 4, 4, 24
+    M = N // C
+    R = N + M
+    rng = np.random.default_rng(17)
+    K, V = rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    p = oracle.prefill_query(rng.standard_normal((1, D)), K, V, t=10, n_raw=N, n_gist=M,
+                             chunk=C, topk=0, window=3)
+    assert list(p["rows"]) == [4, 9, 10, 11, 12]
