@@ -1,0 +1,266 @@
+"""Python binding of libgsa, the MI355X (gfx950) Gist Sparse Attention library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libgsa.so`` behind the C ABI declared in ``include/gsa.h``.
+PyTorch supplies device memory and the stream. If the library has not been
+built, every call raises (there is no fallback path).
+
+Entry points (same names as the C ABI):
+  gsa_decode(q, k_cache, v_cache, chunk=, topk=, tail=, ...)
+  gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, chunk=, fanout=, topk1=, topk2=, tail=, ...)
+  gsa_prefill_blocksparse(q, k_cache, v_cache, chunk=, topk=, window=, q_start=, ...)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "GsaError", "lib", "LIB_PATH", "DecodeParams", "HierParams", "PrefillParams",
+    "GSA_F32", "GSA_BF16", "EXPORTED_SYMBOLS",
+    "decode_params", "hier_params", "prefill_params",
+    "decode_workspace_size", "hier_workspace_size", "prefill_workspace_size",
+    "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
+GSA_F32, GSA_BF16 = 0, 1
+EXPORTED_SYMBOLS = (
+    "gsa_decode_workspace_size", "gsa_decode",
+    "gsa_decode_hier_workspace_size", "gsa_decode_hier",
+    "gsa_prefill_workspace_size", "gsa_prefill_blocksparse",
+    "gsa_status_string", "gsa_last_error",
+)
+
+_c_i32, _c_i64, _c_f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                    ctypes.c_void_p, ctypes.c_size_t)
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [("batch", _c_i32), ("n_q_heads", _c_i32), ("n_kv_heads", _c_i32),
+                ("head_dim", _c_i32), ("n_raw", _c_i64), ("n_gist", _c_i64),
+                ("chunk", _c_i32), ("topk", _c_i32), ("tail", _c_i32), ("scale", _c_f32),
+                ("dtype", _c_i32)]
+
+
+class HierParams(ctypes.Structure):
+    _fields_ = [("base", DecodeParams), ("fanout", _c_i32), ("topk2", _c_i32)]
+
+
+class PrefillParams(ctypes.Structure):
+    _fields_ = [("n_q_heads", _c_i32), ("n_kv_heads", _c_i32), ("head_dim", _c_i32),
+                ("chunk", _c_i32), ("topk", _c_i32), ("window", _c_i32), ("n_raw", _c_i64),
+                ("n_gist", _c_i64), ("q_start", _c_i64), ("n_q", _c_i64), ("scale", _c_f32),
+                ("dtype", _c_i32)]
+
+
+class GsaError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {message}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise GsaError(-1, "libgsa", f"{LIB_PATH} is missing; build it with "
+                           "`python -m decode_gsa_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.gsa_decode_workspace_size.argtypes = [P(DecodeParams), P(_sz)]
+        L.gsa_decode.argtypes = [P(DecodeParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.gsa_decode_hier_workspace_size.argtypes = [P(HierParams), P(_sz)]
+        L.gsa_decode_hier.argtypes = [P(HierParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _sz, _vp]
+        L.gsa_prefill_workspace_size.argtypes = [P(PrefillParams), P(_sz)]
+        L.gsa_prefill_blocksparse.argtypes = [P(PrefillParams), _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                              _vp]
+        for f in ("gsa_decode_workspace_size", "gsa_decode", "gsa_decode_hier_workspace_size",
+                  "gsa_decode_hier", "gsa_prefill_workspace_size", "gsa_prefill_blocksparse"):
+            getattr(L, f).restype = _c_i32
+        L.gsa_status_string.argtypes = [_c_i32]
+        L.gsa_status_string.restype = ctypes.c_char_p
+        L.gsa_last_error.argtypes = []
+        L.gsa_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        msg = lib().gsa_last_error().decode(errors="replace")
+        raise GsaError(status, where, msg or lib().gsa_status_string(status).decode())
+
+
+# ------------------------------------------------------------ parameters ---
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GSA_BF16
+    if t.dtype == torch.float32:
+        return GSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def decode_params(batch, n_q_heads, n_kv_heads, head_dim, n_raw, n_gist, chunk, topk, tail,
+                  scale=0.0, dtype=GSA_BF16) -> DecodeParams:
+    return DecodeParams(batch, n_q_heads, n_kv_heads, head_dim, n_raw, n_gist, chunk, topk,
+                        tail, scale, dtype)
+
+
+def hier_params(base: DecodeParams, fanout: int, topk2: int) -> HierParams:
+    return HierParams(base, fanout, topk2)
+
+
+def prefill_params(n_q_heads, n_kv_heads, head_dim, chunk, topk, window, n_raw, n_gist, q_start,
+                   n_q, scale=0.0, dtype=GSA_BF16) -> PrefillParams:
+    return PrefillParams(n_q_heads, n_kv_heads, head_dim, chunk, topk, window, n_raw, n_gist,
+                         q_start, n_q, scale, dtype)
+
+
+def decode_workspace_size(p: DecodeParams) -> int:
+    n = _sz(0)
+    _check(lib().gsa_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)),
+           "gsa_decode_workspace_size")
+    return n.value
+
+
+def hier_workspace_size(p: HierParams) -> int:
+    n = _sz(0)
+    _check(lib().gsa_decode_hier_workspace_size(ctypes.byref(p), ctypes.byref(n)),
+           "gsa_decode_hier_workspace_size")
+    return n.value
+
+
+def prefill_workspace_size(p: PrefillParams) -> int:
+    n = _sz(0)
+    _check(lib().gsa_prefill_workspace_size(ctypes.byref(p), ctypes.byref(n)),
+           "gsa_prefill_workspace_size")
+    return n.value
+
+
+# ------------------------------------------------------------- tensors -----
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def _workspace(ws, nbytes, device):
+    import torch
+    if ws is not None:
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def gsa_decode(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int,
+               n_gist: Optional[int] = None, scale: float = 0.0, out=None, lse=None,
+               sel_idx=None, workspace=None, stream=None, want_lse: bool = True,
+               want_sel: bool = True):
+    """Single-level GSA decode. q [B,Hq,D]; caches [B,Hkv,R,D] (bf16 or fp32).
+
+    Returns (out [B,Hq,D] fp32, lse [B,Hq] fp32 or None, sel [B,Hkv,k] int32 or None).
+    """
+    import torch
+    B, Hq, D = q.shape
+    Hkv, R = k_cache.shape[1], k_cache.shape[2]
+    M = R // (chunk + 1) if n_gist is None else n_gist
+    p = decode_params(B, Hq, Hkv, D, R - M, M, chunk, topk, tail, scale, _dtype_code(q))
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache, v_cache must share one dtype")
+    if tuple(k_cache.shape) != (B, Hkv, R, D) or tuple(v_cache.shape) != (B, Hkv, R, D):
+        raise ValueError("cache shape mismatch")
+    dev = q.device
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    if sel_idx is None and want_sel:
+        sel_idx = torch.empty(B, Hkv, max(topk, 0), dtype=torch.int32, device=dev)
+    nbytes = decode_workspace_size(p)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib().gsa_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                            _ptr(lse), _ptr(sel_idx) if topk > 0 else None, _ptr(ws),
+                            _nbytes(ws), _stream(stream, dev)), "gsa_decode")
+    return out, lse, sel_idx
+
+
+def gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int, topk1: int,
+                    topk2: int, tail: int, n_gist: Optional[int] = None, scale: float = 0.0,
+                    out=None, lse=None, sel2=None, sel1=None, workspace=None, stream=None,
+                    want_lse: bool = True, want_sel: bool = True):
+    """Two-level (gist-of-gist) decode. k_l2, v_l2 [B,Hkv,M2,D].
+
+    Returns (out, lse, sel2 [B,Hkv,k2], sel1 [B,Hkv,k1]).
+    """
+    import torch
+    B, Hq, D = q.shape
+    Hkv, R = k_cache.shape[1], k_cache.shape[2]
+    M = R // (chunk + 1) if n_gist is None else n_gist
+    base = decode_params(B, Hq, Hkv, D, R - M, M, chunk, topk1, tail, scale, _dtype_code(q))
+    p = hier_params(base, fanout, topk2)
+    dev = q.device
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    if want_sel:
+        if sel2 is None:
+            sel2 = torch.empty(B, Hkv, max(topk2, 0), dtype=torch.int32, device=dev)
+        if sel1 is None:
+            sel1 = torch.empty(B, Hkv, max(topk1, 0), dtype=torch.int32, device=dev)
+    nbytes = hier_workspace_size(p)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib().gsa_decode_hier(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(k_l2), _ptr(v_l2), _ptr(out), _ptr(lse),
+                                 _ptr(sel2) if topk2 > 0 else None,
+                                 _ptr(sel1) if topk1 > 0 else None, _ptr(ws), _nbytes(ws),
+                                 _stream(stream, dev)), "gsa_decode_hier")
+    return out, lse, sel2, sel1
+
+
+def gsa_prefill_blocksparse(q, k_cache, v_cache, *, chunk: int, topk: int, window: int,
+                            q_start: int, n_gist: Optional[int] = None, scale: float = 0.0,
+                            out=None, sel=None, workspace=None, stream=None,
+                            want_sel: bool = True):
+    """Causal block-sparse prefill. q [Hq,n_q,D]; caches [Hkv,R,D] (bf16).
+
+    Returns (out [Hq,n_q,D] fp32, sel [Hkv,n_q,k] int32 or None).
+    """
+    import torch
+    Hq, n_q, D = q.shape
+    Hkv, R = k_cache.shape[0], k_cache.shape[1]
+    M = R // (chunk + 1) if n_gist is None else n_gist
+    p = prefill_params(Hq, Hkv, D, chunk, topk, window, R - M, M, q_start, n_q, scale,
+                       _dtype_code(q))
+    dev = q.device
+    out = torch.empty(Hq, n_q, D, dtype=torch.float32, device=dev) if out is None else out
+    if sel is None and want_sel:
+        sel = torch.empty(Hkv, n_q, max(topk, 0), dtype=torch.int32, device=dev)
+    nbytes = prefill_workspace_size(p)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib().gsa_prefill_blocksparse(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(out), _ptr(sel) if topk > 0 else None, _ptr(ws),
+                                         _nbytes(ws), _stream(stream, dev)),
+           "gsa_prefill_blocksparse")
+    return out, sel

@@ -1,0 +1,237 @@
+// Host-side validation and planning for libgsa (no HIP calls in this file).
+#include "gsa_plan.hpp"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+namespace gsa {
+
+namespace {
+thread_local char g_last_error[512] = "";
+
+int32_t clamp_i(int64_t v, int64_t lo, int64_t hi) {
+  return (int32_t)(v < lo ? lo : (v > hi ? hi : v));
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workgroups per unit for a streaming pass over `rows` rows: enough to put
+// about kTargetWGs workgroups on the chip, but never fewer than kMinRows rows
+// per workgroup.
+constexpr int64_t kTargetWGs = 2048;
+constexpr int64_t kMinRows = 64;
+
+int32_t splits_for(int64_t rows, int64_t units) {
+  if (rows <= 0) return 1;
+  int64_t want = ceil_div(kTargetWGs, units);
+  int64_t cap = ceil_div(rows, kMinRows);
+  return clamp_i(want < cap ? want : cap, 1, 1 << 16);
+}
+
+bool g_supported(int32_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+}  // namespace
+
+gsa_status_t fail(gsa_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+const char* last_error_message() { return g_last_error; }
+
+gsa_status_t check_ptr(const void* p, const char* name, bool allow_null) {
+  if (!p) return allow_null ? GSA_OK : fail(GSA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (((uintptr_t)p) % 16 != 0) return fail(GSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return GSA_OK;
+}
+
+gsa_status_t check_workspace(const void* ws, size_t have, size_t need) {
+  if (need == 0) return GSA_OK;
+  if (!ws) return fail(GSA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (have < need)
+    return fail(GSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  if (((uintptr_t)ws) % kAlign != 0)
+    return fail(GSA_ERR_INVALID_ARG, "workspace is not %zu-byte aligned", kAlign);
+  return GSA_OK;
+}
+
+static gsa_status_t check_geometry(int64_t n_raw, int64_t n_gist, int32_t chunk) {
+  if (chunk < 1 || chunk > 4096) return fail(GSA_ERR_INVALID_ARG, "chunk=%d outside [1, 4096]", chunk);
+  if (n_raw < 1) return fail(GSA_ERR_INVALID_ARG, "n_raw=%lld must be >= 1", (long long)n_raw);
+  if (n_gist < 0) return fail(GSA_ERR_INVALID_ARG, "n_gist=%lld is negative", (long long)n_gist);
+  if (n_gist > n_raw / chunk)
+    return fail(GSA_ERR_INVALID_ARG, "n_gist=%lld exceeds n_raw/chunk", (long long)n_gist);
+  int64_t r = n_raw - n_gist * (int64_t)chunk;
+  if (r > chunk)
+    return fail(GSA_ERR_INVALID_ARG, "%lld raw tokens follow the last gist (at most chunk=%d)",
+                (long long)r, chunk);
+  if (n_raw > ((int64_t)1 << 40)) return fail(GSA_ERR_UNSUPPORTED, "n_raw too large");
+  return GSA_OK;
+}
+
+static gsa_status_t check_heads(int32_t hq, int32_t hkv, int32_t d, int32_t dtype) {
+  if (hq < 1 || hkv < 1) return fail(GSA_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (hq % hkv != 0)
+    return fail(GSA_ERR_INVALID_ARG, "n_q_heads=%d is not a multiple of n_kv_heads=%d", hq, hkv);
+  if (!g_supported(hq / hkv))
+    return fail(GSA_ERR_UNSUPPORTED, "query heads per kv-head %d not in {1,2,4,8}", hq / hkv);
+  if (dtype != GSA_F32 && dtype != GSA_BF16) return fail(GSA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (d != 64 && d != 128) return fail(GSA_ERR_UNSUPPORTED, "head_dim=%d not in {64,128}", d);
+  return GSA_OK;
+}
+
+static float resolve_scale(float s, int32_t d) {
+  return (s > 0.f && isfinite(s)) ? s : 1.0f / sqrtf((float)d);
+}
+
+gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
+  if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 1) return fail(GSA_ERR_INVALID_ARG, "batch=%d must be >= 1", p->batch);
+  gsa_status_t s = check_heads(p->n_q_heads, p->n_kv_heads, p->head_dim, p->dtype);
+  if (s != GSA_OK) return s;
+  if ((s = check_geometry(p->n_raw, p->n_gist, p->chunk)) != GSA_OK) return s;
+  if (isnan(p->scale)) return fail(GSA_ERR_INVALID_ARG, "scale is NaN");
+  if (p->topk < 0 || p->topk > p->n_gist)
+    return fail(GSA_ERR_INVALID_ARG, "topk=%d outside [0, n_gist=%lld]", p->topk, (long long)p->n_gist);
+  int64_t r = p->n_raw - p->n_gist * (int64_t)p->chunk;
+  if (p->tail < r || p->tail > p->n_raw)
+    return fail(GSA_ERR_INVALID_ARG, "tail=%d outside [%lld, n_raw=%lld]", p->tail, (long long)r,
+                (long long)p->n_raw);
+  int64_t units = (int64_t)p->batch * p->n_kv_heads;
+  if (units > (1 << 24)) return fail(GSA_ERR_UNSUPPORTED, "too many (batch, kv-head) units");
+  int64_t items = (int64_t)p->topk * p->chunk + p->tail;
+  if (items > (1 << 30) || p->n_gist > (1 << 30))
+    return fail(GSA_ERR_UNSUPPORTED, "selection too large");
+
+  DecodePlan d{};
+  d.units = (int32_t)units;
+  d.g = p->n_q_heads / p->n_kv_heads;
+  d.D = p->head_dim;
+  d.M = p->n_gist;
+  d.N = p->n_raw;
+  d.R = cache_rows(p->n_raw, p->n_gist);
+  d.C = p->chunk;
+  d.k = p->topk;
+  d.T = p->tail;
+  d.scale = resolve_scale(p->scale, p->head_dim);
+  d.dtype = p->dtype;
+  d.S = splits_for(d.M, units);
+  d.gists_per_split = d.M > 0 ? ceil_div(d.M, d.S) : 0;
+  d.S = d.M > 0 ? (int32_t)ceil_div(d.M, d.gists_per_split) : 1;
+  d.n_items = (int32_t)items;
+  d.S2 = splits_for(items, units);
+  d.items_per_split = items > 0 ? (int32_t)ceil_div(items, d.S2) : 0;
+  d.S2 = items > 0 ? (int32_t)ceil_div(items, d.items_per_split) : 1;
+  d.NP = d.S + d.S2;
+  d.score_stride = (d.M + 63) / 64 * 64;
+  size_t off = 0;
+  d.off_scores = off;
+  off = align_up(off + sizeof(float) * (size_t)units * (size_t)d.score_stride);
+  d.off_sel = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)(d.k > 0 ? d.k : 1));
+  d.off_part = off;
+  off = align_up(off + sizeof(float) * (size_t)units * d.NP * d.g * (d.D + 2));
+  d.total = off;
+  *o = d;
+  return GSA_OK;
+}
+
+gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
+  if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
+  gsa_status_t s = plan_decode(&p->base, &o->base);
+  if (s != GSA_OK) return s;
+  HierPlan h{};
+  h.base = o->base;
+  const DecodePlan& d = h.base;
+  if (p->fanout < 1) return fail(GSA_ERR_INVALID_ARG, "fanout=%d must be >= 1", p->fanout);
+  h.G = p->fanout;
+  h.M2 = d.M / h.G;
+  h.k2 = p->topk2;
+  if (h.k2 < 0 || h.k2 > h.M2)
+    return fail(GSA_ERR_INVALID_ARG, "topk2=%d outside [0, M2=%lld]", h.k2, (long long)h.M2);
+  h.n_orphan = (int32_t)(d.M - h.M2 * h.G);
+  int64_t n_cand = (int64_t)h.k2 * h.G + h.n_orphan;
+  if (n_cand > (1 << 30)) return fail(GSA_ERR_UNSUPPORTED, "too many level-1 candidates");
+  h.n_cand = (int32_t)n_cand;
+  if (d.k > h.n_cand)
+    return fail(GSA_ERR_INVALID_ARG, "topk=%d exceeds the %d level-1 candidates", d.k, h.n_cand);
+  int64_t units = d.units;
+  h.S_l2 = splits_for(h.M2, units);
+  h.l2_per_split = h.M2 > 0 ? ceil_div(h.M2, h.S_l2) : 0;
+  h.S_l2 = h.M2 > 0 ? (int32_t)ceil_div(h.M2, h.l2_per_split) : 1;
+  h.S_c = splits_for(h.n_cand, units);
+  h.cand_per_split = h.n_cand > 0 ? (int32_t)ceil_div(h.n_cand, h.S_c) : 0;
+  h.S_c = h.n_cand > 0 ? (int32_t)ceil_div(h.n_cand, h.cand_per_split) : 1;
+  h.NP = h.S_l2 + h.S_c + d.S2;
+  h.s2_stride = (h.M2 + 63) / 64 * 64;
+  h.sc_stride = (h.n_cand + 63) / 64 * 64;
+  size_t off = 0;
+  h.off_s2 = off;
+  off = align_up(off + sizeof(float) * (size_t)units * (size_t)(h.s2_stride ? h.s2_stride : 1));
+  h.off_sc = off;
+  off = align_up(off + sizeof(float) * (size_t)units * (size_t)(h.sc_stride ? h.sc_stride : 1));
+  h.off_sel2 = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)(h.k2 > 0 ? h.k2 : 1));
+  h.off_sel1 = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)(d.k > 0 ? d.k : 1));
+  h.off_part = off;
+  off = align_up(off + sizeof(float) * (size_t)units * h.NP * d.g * (d.D + 2));
+  h.total = off;
+  *o = h;
+  return GSA_OK;
+}
+
+gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* o) {
+  if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
+  gsa_status_t s = check_heads(p->n_q_heads, p->n_kv_heads, p->head_dim, p->dtype);
+  if (s != GSA_OK) return s;
+  if (p->head_dim != 128) return fail(GSA_ERR_UNSUPPORTED, "prefill needs head_dim=128");
+  if (p->dtype != GSA_BF16) return fail(GSA_ERR_UNSUPPORTED, "prefill needs bf16 inputs");
+  if ((s = check_geometry(p->n_raw, p->n_gist, p->chunk)) != GSA_OK) return s;
+  if (isnan(p->scale)) return fail(GSA_ERR_INVALID_ARG, "scale is NaN");
+  if (p->topk < 0 || p->topk > 256) return fail(GSA_ERR_INVALID_ARG, "topk=%d outside [0, 256]", p->topk);
+  if (p->window < 1 || p->window > (1 << 20))
+    return fail(GSA_ERR_INVALID_ARG, "window=%d outside [1, 2^20]", p->window);
+  if (p->q_start < 0 || p->n_q < 0 || p->q_start + p->n_q > p->n_raw)
+    return fail(GSA_ERR_INVALID_ARG, "query range [%lld, %lld) outside [0, n_raw=%lld)",
+                (long long)p->q_start, (long long)(p->q_start + p->n_q), (long long)p->n_raw);
+  if (p->n_q > ((int64_t)1 << 24)) return fail(GSA_ERR_UNSUPPORTED, "too many queries");
+  PrefillPlan d{};
+  d.Hq = p->n_q_heads;
+  d.Hkv = p->n_kv_heads;
+  d.g = d.Hq / d.Hkv;
+  d.D = p->head_dim;
+  d.C = p->chunk;
+  d.k = p->topk;
+  d.W = p->window;
+  d.N = p->n_raw;
+  d.M = p->n_gist;
+  d.R = cache_rows(d.N, d.M);
+  d.q_start = p->q_start;
+  d.n_q = p->n_q;
+  d.scale = resolve_scale(p->scale, p->head_dim);
+  d.n_blocks = (int32_t)ceil_div(d.n_q, kQBlock);
+  d.total = 0;
+  *o = d;
+  return GSA_OK;
+}
+
+}  // namespace gsa
+
+extern "C" const char* gsa_status_string(gsa_status_t s) {
+  switch (s) {
+    case GSA_OK: return "GSA_OK";
+    case GSA_ERR_INVALID_ARG: return "GSA_ERR_INVALID_ARG: an argument is outside its documented range";
+    case GSA_ERR_UNSUPPORTED: return "GSA_ERR_UNSUPPORTED: valid arguments this build does not run";
+    case GSA_ERR_WORKSPACE: return "GSA_ERR_WORKSPACE: workspace missing or too small";
+    case GSA_ERR_HIP: return "GSA_ERR_HIP: a HIP call or kernel launch failed";
+  }
+  return "unknown gsa_status_t";
+}
+
+extern "C" const char* gsa_last_error(void) { return gsa::last_error_message(); }

@@ -1,0 +1,82 @@
+// Host-side argument validation, work splitting and workspace layout for libgsa.
+// Pure C++ (no HIP calls): every check runs before any launch.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gsa.h"
+
+namespace gsa {
+
+// Record the reason for a failure on this thread; returns `s` for chaining.
+gsa_status_t fail(gsa_status_t s, const char* fmt, ...);
+void clear_error();
+const char* last_error_message();
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Number of rows of the interleaved cache of one unit.
+inline int64_t cache_rows(int64_t n_raw, int64_t n_gist) { return n_raw + n_gist; }
+
+// Workspace layout and launch shape of one single-level decode call.
+struct DecodePlan {
+  int32_t units;        // B * Hkv
+  int32_t g;            // query heads per kv-head
+  int32_t D;
+  int64_t M, R, N;
+  int32_t C, k, T;
+  float scale;          // resolved (> 0)
+  int32_t dtype;
+  // gist pass: S workgroups per unit, each over a contiguous gist range
+  int32_t S;
+  int64_t gists_per_split;
+  // unfold pass: S2 workgroups per unit over the k*C + T unfold items
+  int32_t S2;
+  int32_t items_per_split;
+  int32_t n_items;      // k*C + T
+  int32_t NP;           // partial states per unit = S + S2
+  // byte offsets inside the workspace
+  size_t off_scores, off_sel, off_part, total;
+  int64_t score_stride; // floats per unit in the score region
+};
+
+gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* out);
+
+// Two-level plan: level-2 gist pass, candidate level-1 gist pass, unfold.
+struct HierPlan {
+  DecodePlan base;      // level-1 geometry (k = k1); base.S is unused
+  int32_t G, k2;
+  int64_t M2;
+  int32_t n_orphan;     // M - M2*G
+  int32_t n_cand;       // k2*G + n_orphan
+  int32_t S_l2;         // workgroups per unit over the level-2 gists
+  int64_t l2_per_split;
+  int32_t S_c;          // workgroups per unit over the level-1 candidates
+  int32_t cand_per_split;
+  int32_t NP;           // S_l2 + S_c + S2
+  size_t off_s2, off_sc, off_sel2, off_sel1, off_part, total;
+  int64_t s2_stride, sc_stride;
+};
+
+gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* out);
+
+// Prefill plan.
+struct PrefillPlan {
+  int32_t Hq, Hkv, g, D, C, k, W;
+  int64_t N, M, R, q_start, n_q;
+  float scale;
+  int32_t n_blocks;     // query blocks of kQBlock queries
+  size_t total;
+};
+
+constexpr int kQBlock = 64;
+
+gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* out);
+
+// Pointer checks shared by the entry points.
+gsa_status_t check_ptr(const void* p, const char* name, bool allow_null = false);
+gsa_status_t check_workspace(const void* ws, size_t have, size_t need);
+
+}  // namespace gsa

@@ -1,0 +1,183 @@
+/*
+ * gsa.h -- C ABI of libgsa: Gist Sparse Attention (GSA) decode and prefill
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method (gist.science explainer "Forget, Then Recall: Learnable
+ * Compression and Selective Unfolding via Gist Sparse Attention", section 2
+ * 'Key Concepts'; Taki-lab slide deck on the same paper, slides 3 and 6-10):
+ * a sequence is cut into chunks of C raw tokens and one gist token follows
+ * every chunk. At each step the query scores every gist key by a dot
+ * product, keeps the k best chunks, restores ("unfolds") their raw K/V, and
+ * runs softmax attention over all gists, the unfolded raw tokens and the
+ * trailing raw tokens that have no gist yet.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor arguments are DEVICE pointers, dense and row-major as stated,
+ *    16-byte aligned. The caller owns every buffer; the library allocates no
+ *    memory and never synchronizes.
+ *  - q, K and V share one element type (gsa_dtype_t). out and lse are fp32.
+ *  - Interleaved cache of one (batch, kv-head) unit: R = n_raw + n_gist rows
+ *    of head_dim elements. Row m*(C+1)+j (j < C) holds raw token m*C+j; row
+ *    m*(C+1)+C holds the gist of chunk m; the 0..C raw tokens after the last
+ *    gisted chunk follow in rows n_gist*(C+1) onwards.
+ *  - scale <= 0 selects 1/sqrt(head_dim). Logits are scale * (q . k).
+ *  - With grouped-query attention (g = n_q_heads / n_kv_heads query heads per
+ *    kv-head) one selection is made per (batch, kv-head): the group score of
+ *    a gist is the mean over the g heads of their scaled logits.
+ *  - Ties in a top-k go to the smaller chunk index; selections are written in
+ *    ascending chunk order.
+ *  - Every row enters the attention set once even when a selected chunk
+ *    overlaps the tail (decode) or the window (prefill).
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = default
+ *    stream). Results are valid after the caller synchronizes the stream.
+ *  - Every argument is validated on the host before any launch; a rejected
+ *    call returns a non-zero status, launches nothing and writes nothing.
+ *    A launch failure returns GSA_ERR_HIP. gsa_last_error() gives a
+ *    human-readable reason for the last failure on the calling thread.
+ *  - Calls keep no state between them (re-entrant). The workspace of a call
+ *    must not be used by another call that runs concurrently.
+ */
+#ifndef GSA_H_
+#define GSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GSA_OK = 0,
+  GSA_ERR_INVALID_ARG = 1, /* argument out of its documented range / NULL */
+  GSA_ERR_UNSUPPORTED = 2, /* valid, but a shape or type this build does not run */
+  GSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  GSA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} gsa_status_t;
+
+typedef enum { GSA_F32 = 0, GSA_BF16 = 1 } gsa_dtype_t;
+
+/* ------------------------------------------------------------------------
+ * Single-level decode: one new query per sequence.
+ * Source: gist.science explainer, section 2 'Key Concepts' (gist as routing
+ * signal; selective unfolding; hybrid attention) and the slide deck's
+ * slide 10 worked example (scores 0.1/0.8/0.7/0.2, k=2 -> chunks 2 and 3).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;       /* B >= 1 */
+  int32_t n_q_heads;   /* Hq >= 1, multiple of n_kv_heads */
+  int32_t n_kv_heads;  /* Hkv >= 1; g = Hq/Hkv must be 1, 2, 4 or 8 */
+  int32_t head_dim;    /* D: 64 or 128 */
+  int64_t n_raw;       /* N >= 1 raw tokens per sequence (same for all) */
+  int64_t n_gist;      /* M gisted chunks; 0 <= N - M*C <= C */
+  int32_t chunk;       /* C >= 1 raw tokens per chunk */
+  int32_t topk;        /* 0 <= k <= M chunks to unfold */
+  int32_t tail;        /* T: the last T raw tokens are always attended;
+                          N - M*C <= T <= N */
+  float scale;         /* <= 0: 1/sqrt(D) */
+  int32_t dtype;       /* gsa_dtype_t of q, K, V */
+} gsa_decode_params;
+
+/* Bytes of device workspace gsa_decode needs for these parameters. */
+gsa_status_t gsa_decode_workspace_size(const gsa_decode_params* p, size_t* bytes);
+
+/*
+ * q        [B, Hq, D]        query of the new token, per head
+ * k_cache  [B, Hkv, R, D]    interleaved key cache, R = N + M
+ * v_cache  [B, Hkv, R, D]    interleaved value cache
+ * out      [B, Hq, D] fp32   attention output (written)
+ * lse      [B, Hq]    fp32   natural-log sum-exp of the attended logits, or NULL
+ * sel_idx  [B, Hkv, k] int32 selected chunk ids, ascending, or NULL
+ * workspace / workspace_bytes: device scratch of at least
+ *          gsa_decode_workspace_size() bytes (contents need no initialisation)
+ */
+gsa_status_t gsa_decode(const gsa_decode_params* p, const void* q, const void* k_cache,
+                        const void* v_cache, float* out, float* lse, int32_t* sel_idx,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Two-level (gist-of-gist) decode.
+ * Source: gist.science explainer, 'Hierarchical Extension (H-GSA)': meta-gists
+ * summarise groups of gists; selection scores the meta-gists, then the gists
+ * inside the chosen groups, then unfolds raw chunks (also the slide deck,
+ * slide 11, and the authors' abstract on multi-resolution access).
+ * Level-2 gist i summarises level-1 gists [i*G, (i+1)*G); M2 = floor(M/G).
+ * The M - M2*G level-1 gists no group covers are always candidates.
+ * Attention set: every level-2 gist, every candidate level-1 gist (all G
+ * children of each chosen group, plus the ungrouped ones), the raw rows of
+ * the k1 chosen chunks and the tail.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  gsa_decode_params base; /* level-1 cache; base.topk = k1 */
+  int32_t fanout;         /* G >= 1 */
+  int32_t topk2;          /* 0 <= k2 <= M2; k1 <= k2*G + (M - M2*G) */
+} gsa_hier_params;
+
+gsa_status_t gsa_decode_hier_workspace_size(const gsa_hier_params* p, size_t* bytes);
+
+/*
+ * q, k_cache, v_cache, out, lse: as gsa_decode.
+ * k_l2, v_l2 [B, Hkv, M2, D]  level-2 gist keys / values (dense rows)
+ * sel2 [B, Hkv, k2] int32     chosen level-2 groups, ascending, or NULL
+ * sel1 [B, Hkv, k1] int32     chosen chunks, ascending, or NULL
+ */
+gsa_status_t gsa_decode_hier(const gsa_hier_params* p, const void* q, const void* k_cache,
+                             const void* v_cache, const void* k_l2, const void* v_l2,
+                             float* out, float* lse, int32_t* sel2, int32_t* sel1,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Causal block-sparse prefill of query positions [q_start, q_start + n_q)
+ * of one sequence.
+ * Source: gist.science explainer, 'Training Procedure: Selective Finetuning'
+ * (the attention mask admits only the top-k chunks and their raw tokens),
+ * with the gist causal order of section 2 'Key Concepts' (a gist sees its
+ * own chunk and earlier gists; slide deck slide 7).
+ * Query t may use gist m only when m < floor(t/C) (the chunk is complete
+ * before t). It selects the top-k of those by group score (all of them when
+ * fewer than k, the rest of sel padded with -1) and attends to every
+ * eligible gist, the raw rows of its chosen chunks, and the raw tokens in
+ * [t - W + 1, t].
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_q_heads;   /* Hq, multiple of n_kv_heads; g in {1, 2, 4, 8} */
+  int32_t n_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;    /* D: 128 */
+  int32_t chunk;       /* C >= 1 */
+  int32_t topk;        /* k >= 0 */
+  int32_t window;      /* W >= 1 */
+  int64_t n_raw;       /* N raw tokens in the cache */
+  int64_t n_gist;      /* M; 0 <= N - M*C <= C */
+  int64_t q_start;     /* first query position, 0 <= q_start */
+  int64_t n_q;         /* queries; q_start + n_q <= N */
+  float scale;         /* <= 0: 1/sqrt(D) */
+  int32_t dtype;       /* GSA_BF16 */
+} gsa_prefill_params;
+
+gsa_status_t gsa_prefill_workspace_size(const gsa_prefill_params* p, size_t* bytes);
+
+/*
+ * q       [Hq, n_q, D]        queries (row i is position q_start + i)
+ * k_cache [Hkv, R, D]         interleaved cache of the sequence, R = N + M
+ * v_cache [Hkv, R, D]
+ * out     [Hq, n_q, D] fp32   attention output (written)
+ * sel     [Hkv, n_q, k] int32 chosen chunks per query, ascending, -1 padded,
+ *                             or NULL
+ */
+gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, const void* q,
+                                     const void* k_cache, const void* v_cache, float* out,
+                                     int32_t* sel, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/* Static description of a status code. */
+const char* gsa_status_string(gsa_status_t s);
+
+/* Reason for the last non-OK status returned on the calling thread ("" if none). */
+const char* gsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSA_H_ */

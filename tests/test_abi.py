@@ -1,0 +1,190 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, the ctypes structs match the C layout, and every invalid
+argument is rejected on the host with the documented status before any launch.
+
+None of these calls passes validation, so no kernel is ever launched here.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import decode_gsa_amd as gsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gsa.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 1 << 20            # 16-byte aligned, never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gsa.LIB_PATH):
+        pytest.skip("libgsa.so not built")
+    return gsa.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:gsa_status_t|const char\*)\s+(gsa_\w+)\s*\(", text, re.M))
+    assert declared == set(gsa.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "gsa.h"
+#define F(T, m) printf(#T "." #m " %zu\n", offsetof(T, m))
+int main(void) {
+  printf("gsa_decode_params %zu\n", sizeof(gsa_decode_params));
+  printf("gsa_hier_params %zu\n", sizeof(gsa_hier_params));
+  printf("gsa_prefill_params %zu\n", sizeof(gsa_prefill_params));
+  F(gsa_decode_params, n_raw); F(gsa_decode_params, n_gist); F(gsa_decode_params, chunk);
+  F(gsa_decode_params, scale); F(gsa_decode_params, dtype);
+  F(gsa_hier_params, fanout); F(gsa_hier_params, topk2);
+  F(gsa_prefill_params, n_raw); F(gsa_prefill_params, q_start); F(gsa_prefill_params, n_q);
+  F(gsa_prefill_params, scale); F(gsa_prefill_params, dtype);
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                 check=True).stdout.splitlines())
+    assert int(got["gsa_decode_params"]) == ctypes.sizeof(gsa.DecodeParams)
+    assert int(got["gsa_hier_params"]) == ctypes.sizeof(gsa.HierParams)
+    assert int(got["gsa_prefill_params"]) == ctypes.sizeof(gsa.PrefillParams)
+    for key, val in got.items():
+        if "." in key:
+            t, m = key.split(".")
+            cls = {"gsa_decode_params": gsa.DecodeParams, "gsa_hier_params": gsa.HierParams,
+                   "gsa_prefill_params": gsa.PrefillParams}[t]
+            assert getattr(cls, m).offset == int(val), key
+
+
+def good_decode(**kw):
+    p = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_raw=1024, n_gist=64, chunk=16,
+             topk=4, tail=32, scale=0.0, dtype=gsa.GSA_BF16)
+    p.update(kw)
+    return gsa.DecodeParams(**p)
+
+
+def ws_size(L, p):
+    n = ctypes.c_size_t(0)
+    st = L.gsa_decode_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, OK),
+    ({"batch": 0}, INVALID),
+    ({"n_q_heads": 7}, INVALID),              # not a multiple of n_kv_heads
+    ({"n_q_heads": 6, "n_kv_heads": 2}, UNSUPPORTED),   # g = 3
+    ({"head_dim": 96}, UNSUPPORTED),
+    ({"dtype": 7}, INVALID),
+    ({"chunk": 0}, INVALID),
+    ({"n_raw": 0, "n_gist": 0}, INVALID),
+    ({"n_gist": 65}, INVALID),                # more gists than chunks
+    ({"n_gist": 62}, INVALID),                # 32 raw tokens after the last gist > C
+    ({"n_gist": -1}, INVALID),
+    ({"topk": -1}, INVALID),
+    ({"topk": 65}, INVALID),                  # k > M
+    ({"topk": 64}, OK),                       # k = M allowed
+    ({"topk": 0}, OK),
+    ({"n_raw": 1030, "tail": 5}, INVALID),    # 6 gist-less raw tokens need tail >= 6
+    ({"n_raw": 1030, "tail": 6}, OK),
+    ({"tail": 1025}, INVALID),                # tail > n_raw
+    ({"scale": float("nan")}, INVALID),
+])
+def test_decode_param_validation(L, kw, status):
+    st, n = ws_size(L, good_decode(**kw))
+    assert st == status, L.gsa_last_error()
+    if status == OK:
+        assert n > 0 and n % 256 == 0
+
+
+def test_decode_rejects_bad_pointers_and_workspace(L):
+    p = good_decode()
+    st, need = ws_size(L, p)
+    assert st == OK
+    args = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=None, sel=None, ws=FAKE, nws=need)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L.gsa_decode(ctypes.byref(p), a["q"], a["k"], a["v"], a["out"], a["lse"], a["sel"],
+                            a["ws"], a["nws"], None)
+    assert call(q=None) == INVALID
+    assert call(k=None) == INVALID
+    assert call(v=FAKE + 4) == INVALID          # misaligned
+    assert call(out=None) == INVALID
+    assert call(lse=FAKE + 8) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(nws=need - 1) == WORKSPACE
+    assert call(ws=FAKE + 16) == INVALID        # workspace must be 256-byte aligned
+    assert b"aligned" in L.gsa_last_error()
+
+
+def test_hier_param_validation(L):
+    base = good_decode(n_raw=16 * 16 * 10 + 16 * 3, n_gist=16 * 10 + 3, topk=8, tail=64)
+    # M = 163, G = 16 -> M2 = 10 groups, 3 orphan gists
+    n = ctypes.c_size_t(0)
+
+    def st(fanout, k2, k1=None):
+        b = gsa.DecodeParams.from_buffer_copy(base)
+        if k1 is not None:
+            b.topk = k1
+        return L.gsa_decode_hier_workspace_size(ctypes.byref(gsa.HierParams(b, fanout, k2)),
+                                                ctypes.byref(n))
+    assert st(16, 2) == OK
+    assert st(0, 2) == INVALID
+    assert st(16, 11) == INVALID                # k2 > M2
+    assert st(16, 10) == OK
+    assert st(16, 1, 19) == OK                  # 16 children + 3 orphans
+    assert st(16, 1, 20) == INVALID             # more than the candidates
+    assert st(16, 0, 3) == OK                   # orphans only
+    assert st(16, 0, 4) == INVALID
+
+
+def good_prefill(**kw):
+    p = dict(n_q_heads=8, n_kv_heads=2, head_dim=128, chunk=16, topk=4, window=64, n_raw=4096,
+             n_gist=256, q_start=3072, n_q=1024, scale=0.0, dtype=gsa.GSA_BF16)
+    p.update(kw)
+    return gsa.PrefillParams(**p)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, OK),
+    ({"head_dim": 64}, UNSUPPORTED),
+    ({"dtype": gsa.GSA_F32}, UNSUPPORTED),
+    ({"window": 0}, INVALID),
+    ({"topk": -1}, INVALID),
+    ({"q_start": -1}, INVALID),
+    ({"n_q": 1025}, INVALID),                   # runs past n_raw
+    ({"n_gist": 257}, INVALID),
+    ({"n_q_heads": 12, "n_kv_heads": 4}, UNSUPPORTED),
+])
+def test_prefill_param_validation(L, kw, status):
+    n = ctypes.c_size_t(0)
+    assert L.gsa_prefill_workspace_size(ctypes.byref(good_prefill(**kw)), ctypes.byref(n)) == status
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.gsa_status_string(s).startswith(b"GSA_")
+    assert L.gsa_status_string(99) == b"unknown gsa_status_t"
+
+
+def test_python_binding_raises_without_gpu_tensors():
+    import torch
+    with pytest.raises((ValueError, gsa.GsaError)):
+        q = torch.zeros(1, 1, 64)
+        k = torch.zeros(1, 1, 17, 64)
+        gsa.gsa_decode(q, k, k, chunk=16, topk=1, tail=0)

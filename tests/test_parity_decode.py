@@ -1,0 +1,230 @@
+"""GPU parity of gsa_decode / gsa_decode_hier against the fp64 oracle.
+
+Selected chunk indices must match bit for bit; outputs within the stated
+tolerance (tests/gpu_util.py). Small cases compare every unit; the full-size
+workloads run in the launch configuration the benchmark times and compare
+sampled units.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gsa_inputs as gi
+import oracle
+from conftest import to_np
+from gpu_util import check_lse, check_out, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_gsa_amd
+    decode_gsa_amd.lib()          # raises if the library is missing: no fallback
+    return decode_gsa_amd
+
+
+def run_decode(gsa, inp, cfg, units=None):
+    """Run the GPU path once, then compare the listed units (default: all) with
+    the oracle, copying only those units' cache slabs to the host."""
+    out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=cfg.chunk,
+                                   topk=cfg.topk, tail=cfg.tail, n_gist=cfg.M)
+    torch.cuda.synchronize()
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    us = [(b, j) for b in range(cfg.batch) for j in range(cfg.n_kv_heads)] if units is None else units
+    got, ref, got_l, ref_l = [], [], [], []
+    for b, j in us:
+        r = oracle.decode_unit(to_np(inp.q[b, j * g:(j + 1) * g]), to_np(inp.k_cache[b, j]),
+                               to_np(inp.v_cache[b, j]), n_raw=cfg.n_raw, n_gist=cfg.M,
+                               chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail)
+        if cfg.topk > 0:
+            np.testing.assert_array_equal(to_np(sel[b, j]), r["sel"], err_msg=f"unit {(b, j)}")
+        got.append(to_np(out[b, j * g:(j + 1) * g]))
+        ref.append(r["out"])
+        got_l.append(to_np(lse[b, j * g:(j + 1) * g]))
+        ref_l.append(r["lse"])
+    err = check_out(np.stack(got), np.stack(ref), cfg.dtype, cfg.name)
+    check_lse(np.stack(got_l), np.stack(ref_l), cfg.dtype, cfg.name)
+    return err
+
+
+def small(name, **kw):
+    return dataclasses.replace(gi.CONFIGS[name], **kw)
+
+
+# ---------------------------------------------------------------- small ---
+
+CASES = [
+    ("tiny_f32", {}),                                           # the parity config itself
+    ("gqa_32k", dict(batch=2, n_raw=4096)),                     # 16x, several splits
+    ("gqa_32k", dict(batch=3, n_kv_heads=2, n_q_heads=16, n_raw=2009, n_gist=125, tail=16)),
+    ("c8_131k", dict(batch=1, n_raw=8192)),                     # C=8, k=64
+    ("c32_131k", dict(batch=1, n_raw=8192)),                    # C=32
+    ("gqa_32k", dict(batch=2, n_q_heads=8, n_raw=3000, n_gist=187, tail=40)),   # g=1, ragged
+    ("gqa_32k", dict(batch=1, n_q_heads=16, n_raw=2048)),       # g=2
+    ("gqa_32k", dict(batch=1, n_q_heads=64, n_raw=2048)),       # g=8
+    ("gqa_32k", dict(batch=2, head_dim=64, n_raw=4096)),        # bf16, D=64
+    ("gqa_32k", dict(batch=1, dtype="f32", n_raw=4096)),        # fp32, D=128
+    ("tiny_f32", dict(chunk=7, n_raw=700, topk=5, tail=9, plant="none")),
+    ("gqa_32k", dict(batch=1, chunk=1, n_raw=600, topk=30, tail=3, plant="none")),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[f"{n}-{i}" for i, (n, _) in enumerate(CASES)])
+def test_decode_small(gsa, name, kw):
+    cfg = small(name, **kw)
+    say(f"decode small {cfg}")
+    inp = gi.make_decode(cfg, 2000, device="cuda")
+    err = run_decode(gsa, inp, cfg)
+    say(f"  max err / rms = {err:.2e}")
+
+
+def test_decode_k_zero_and_k_all(gsa):
+    for k in (0, 128):
+        cfg = small("gqa_32k", batch=2, n_raw=2048, topk=k, plant="none")
+        say(f"decode k={k}")
+        inp = gi.make_decode(cfg, 2001, device="cuda")
+        run_decode(gsa, inp, cfg)
+
+
+def test_decode_q_zero_ties_and_tail_overlap(gsa):
+    """q = 0: every score is +-0, so chunks 0..k-1 win; the tail overlaps chunk k-1."""
+    C, M, k = 16, 64, 8
+    T = M * C - ((k - 1) * C + 8)             # tail starts mid-way through chunk k-1
+    cfg = small("gqa_32k", batch=2, n_raw=M * C, topk=k, tail=T, plant="none")
+    inp = gi.make_decode(cfg, 2002, device="cuda")
+    inp.q.zero_()
+    inp.k_cache.neg_()                         # mixes -0 and +0 products
+    out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=C, topk=k, tail=T)
+    torch.cuda.synchronize()
+    assert (to_np(sel) == np.arange(k)[None, None, :]).all()
+    run_decode(gsa, inp, cfg)
+
+
+def test_decode_selects_chunk_inside_tail(gsa):
+    """A planted chunk that lies inside the tail: its rows must be attended once."""
+    cfg = small("gqa_32k", batch=1, n_raw=2048, topk=4, tail=40, plant="none")
+    inp = gi.make_decode(cfg, 2003, device="cuda")
+    C = cfg.chunk
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    last = cfg.M - 1                           # its raw rows are all in the tail
+    for j in range(cfg.n_kv_heads):
+        qbar = inp.q[0, j * g:(j + 1) * g].float().mean(0)
+        inp.k_cache[0, j, last * (C + 1) + C] = (qbar / qbar.norm() * 40).to(inp.k_cache.dtype)
+    out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=C, topk=4, tail=40)
+    torch.cuda.synchronize()
+    assert (to_np(sel)[..., -1] == last).all()
+    run_decode(gsa, inp, cfg)
+
+
+def test_decode_no_gists(gsa):
+    cfg = small("gqa_32k", batch=2, n_raw=12, n_gist=0, topk=0, tail=12, plant="none")
+    inp = gi.make_decode(cfg, 2004, device="cuda")
+    run_decode(gsa, inp, cfg)
+
+
+def test_decode_repeatable_and_stream(gsa):
+    cfg = small("gqa_32k", batch=2, n_raw=4096)
+    inp = gi.make_decode(cfg, 2005, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=16, tail=64, stream=s)
+        b = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=16, tail=64, stream=s)
+    s.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[2], b[2]) and torch.equal(a[1], b[1])
+
+
+# ----------------------------------------------------------- full sizes ---
+
+def sample_units(cfg, n=6, seed=0):
+    rng = np.random.default_rng(seed)
+    allu = [(b, j) for b in range(cfg.batch) for j in range(cfg.n_kv_heads)]
+    pick = {allu[0], allu[-1]}
+    while len(pick) < min(n, len(allu)):
+        pick.add(allu[int(rng.integers(len(allu)))])
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", ["gqa_32k", "c8_131k", "c32_131k"])
+def test_decode_full_size_sampled(gsa, name):
+    cfg = gi.CONFIGS[name]
+    say(f"decode full {name}")
+    inp = gi.make_decode(cfg, 1000 + {"gqa_32k": 2, "c8_131k": 3, "c32_131k": 4}[name],
+                         device="cuda")
+    # every unit's selection must be the planted (margin >= 0.5) set
+    out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=cfg.chunk,
+                                   topk=cfg.topk, tail=cfg.tail)
+    torch.cuda.synchronize()
+    assert torch.equal(sel.long(), inp.planted)
+    err = run_decode(gsa, inp, cfg, units=sample_units(cfg))
+    say(f"  sampled max err / rms = {err:.2e}")
+
+
+# ------------------------------------------------------------ two-level ---
+
+def run_hier(gsa, inp, cfg, units=None):
+    b = cfg.base
+    out, lse, s2, s1 = gsa.gsa_decode_hier(inp.q, inp.k_cache, inp.v_cache, inp.k_l2, inp.v_l2,
+                                           chunk=b.chunk, fanout=cfg.fanout, topk1=b.topk,
+                                           topk2=cfg.topk2, tail=b.tail, n_gist=b.M)
+    torch.cuda.synchronize()
+    g = b.n_q_heads // b.n_kv_heads
+    us = ([(x, j) for x in range(b.batch) for j in range(b.n_kv_heads)] if units is None
+          else units)
+    errs = []
+    for (x, j) in us:
+        r = oracle.decode_hier_unit(to_np(inp.q[x, j * g:(j + 1) * g]), to_np(inp.k_cache[x, j]),
+                                    to_np(inp.v_cache[x, j]), to_np(inp.k_l2[x, j]),
+                                    to_np(inp.v_l2[x, j]), n_raw=b.n_raw, n_gist=b.M,
+                                    chunk=b.chunk, fanout=cfg.fanout, topk1=b.topk,
+                                    topk2=cfg.topk2, tail=b.tail)
+        if cfg.topk2 > 0:
+            np.testing.assert_array_equal(to_np(s2[x, j]), r["sel2"])
+        if b.topk > 0:
+            np.testing.assert_array_equal(to_np(s1[x, j]), r["sel1"])
+        errs.append((to_np(out[x, j * g:(j + 1) * g]), r["out"], to_np(lse[x, j * g:(j + 1) * g]),
+                     r["lse"]))
+    got = np.stack([e[0] for e in errs])
+    ref = np.stack([e[1] for e in errs])
+    err = check_out(got, ref, b.dtype, b.name)
+    check_lse(np.stack([e[2] for e in errs]), np.stack([e[3] for e in errs]), b.dtype, b.name)
+    return err
+
+
+HIER_CASES = [
+    dict(batch=2, n_raw=16 * 16 * 64, fanout=16, topk2=8),            # 64 groups
+    dict(batch=1, n_raw=16 * (16 * 20 + 5) + 9, n_gist=16 * 20 + 5, fanout=16, topk2=3,
+         topk=10, plant="none"),                                        # orphans + partial chunk
+    dict(batch=1, n_raw=16 * 16 * 8, fanout=16, topk2=8, topk=128, plant="none"),  # all chosen
+    dict(batch=1, n_raw=16 * 16 * 8, fanout=16, topk2=0, topk=0, plant="none"),
+]
+
+
+@pytest.mark.parametrize("kw", HIER_CASES)
+def test_hier_small(gsa, kw):
+    kw = dict(kw)
+    fanout, topk2 = kw.pop("fanout"), kw.pop("topk2")
+    base = dataclasses.replace(gi.CONFIGS["hier_1m"].base, **kw)
+    cfg = gi.HierConfig(base, fanout, topk2)
+    say(f"hier small {kw} G={fanout} k2={topk2}")
+    inp = gi.make_hier(cfg, 3000, device="cuda")
+    err = run_hier(gsa, inp, cfg)
+    say(f"  max err / rms = {err:.2e}")
+
+
+def test_hier_full_size_sampled(gsa):
+    cfg = gi.CONFIGS["hier_1m"]
+    say("hier full 1M")
+    inp = gi.make_hier(cfg, 1004, device="cuda")
+    b = cfg.base
+    out, lse, s2, s1 = gsa.gsa_decode_hier(inp.q, inp.k_cache, inp.v_cache, inp.k_l2, inp.v_l2,
+                                           chunk=b.chunk, fanout=cfg.fanout, topk1=b.topk,
+                                           topk2=cfg.topk2, tail=b.tail)
+    torch.cuda.synchronize()
+    assert torch.equal(s2.long(), inp.planted2) and torch.equal(s1.long(), inp.planted1)
+    err = run_hier(gsa, inp, cfg, units=[(0, 0), (1, 3), (3, 7)])
+    say(f"  sampled max err / rms = {err:.2e}")
