@@ -110,7 +110,7 @@ def run_decode_bench(args):
     sel = torch.empty(B, cfg.n_kv_heads, max(cfg.topk, 1), dtype=torch.int32, device=dev)
     p = gsa.decode_params(B, Hq, cfg.n_kv_heads, D, cfg.n_raw, cfg.M, cfg.chunk, cfg.topk,
                           cfg.tail, 0.0, gsa.GSA_BF16 if cfg.dtype == "bf16" else gsa.GSA_F32)
-    ws = torch.empty(gsa.decode_workspace_size(p), dtype=torch.uint8, device=dev)
+    ws = gsa.new_workspace(gsa.decode_workspace_size(p), dev)
 
     def step(i):
         l = i % layers

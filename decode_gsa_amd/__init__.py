@@ -20,7 +20,7 @@ __all__ = [
     "GsaError", "lib", "LIB_PATH", "DecodeParams", "HierParams", "PrefillParams",
     "GSA_F32", "GSA_BF16", "EXPORTED_SYMBOLS",
     "decode_params", "hier_params", "prefill_params",
-    "decode_workspace_size", "hier_workspace_size", "prefill_workspace_size",
+    "decode_workspace_size", "hier_workspace_size", "prefill_workspace_size", "new_workspace",
     "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse",
 ]
 
@@ -165,10 +165,18 @@ def _stream(stream, device) -> Optional[int]:
 
 
 def _workspace(ws, nbytes, device):
+    """Caller's workspace, or a new zero-filled one (the control words at its
+    start must be zero before first use; every call leaves them zero)."""
     import torch
     if ws is not None:
         return ws
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def new_workspace(nbytes: int, device="cuda"):
+    """A zero-filled device workspace of nbytes, reusable by later calls."""
+    import torch
+    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
 def _nbytes(t) -> int:

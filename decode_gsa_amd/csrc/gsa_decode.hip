@@ -1,24 +1,33 @@
-// GSA decode on gfx950: gist scoring + online softmax over every gist,
-// exact top-k chunk selection, gather of the unfolded chunks and the tail,
-// and a log-sum-exp merge of the split partial states.
+// GSA decode on gfx950 in one launch: gist scoring + online softmax over every
+// gist, exact top-k chunk selection, gather of the unfolded chunks and the
+// tail, and a log-sum-exp merge of the partial softmax states.
 //
 // Method: gist.science explainer "Forget, Then Recall", section 2 'Key
 // Concepts' (routing by gist scores, top-k selection, selective unfolding,
 // hybrid attention) and 'Hierarchical Extension (H-GSA)' for the two-level
-// entry point. The work is split per (batch, kv-head) unit:
+// entry point (score the meta-gists, then the gists of the chosen groups,
+// then unfold raw chunks).
 //
-//   gist_pass   grid units x S   streams the unit's gist rows (K and V, each
-//                                row read once), writes the group score of
-//                                every gist and an online-softmax partial
-//                                (m, l, acc[D]) per query head;
-//   select      grid units       exact top-k of the group scores (bitwise
-//                                search for the k-th key, then an ordered
-//                                compaction: ties go to the smaller index);
-//   unfold      grid units x S2  streams the raw rows of the selected chunks
-//                                (each chunk is one contiguous run) and the
-//                                tail, skipping rows the tail owns, and writes
-//                                partials;
-//   merge       grid units x g   combines the partials into out and lse.
+// Work is cut into tasks per (batch, kv-head) unit and phase:
+//   gist-like phase  a task streams a contiguous range of gist rows (K and V,
+//                    each row read once), writes each gist's group score and
+//                    one online-softmax partial (m, l, acc[D]) per query head;
+//                    the unit's last task to finish runs the exact top-k over
+//                    the phase's scores and raises the unit's ready flag;
+//   unfold phase     a task waits for its unit's flag, then streams a share of
+//                    the selected chunks' raw rows (each chunk one contiguous
+//                    run; rows the tail owns are skipped) and of the tail; the
+//                    unit's last task merges every partial into out and lse.
+// Single-level decode runs [gist, unfold]; two-level decode runs [level-2
+// gists, level-1 candidate gists, unfold].
+//
+// Tasks are numbered phase by phase and unit by unit, and a task only ever
+// waits for tasks with lower numbers. The grid is persistent and no larger
+// than the number of workgroups the chip holds at once (occupancy x CUs), so
+// every workgroup is resident; workgroup w runs tasks w, w + P, w + 2P, ... in
+// order. The lowest unfinished task is therefore always running with all its
+// (lower) dependencies finished, so every wait ends. The wait is also bounded;
+// on time-out the task poisons its partial with NaN instead of hanging.
 //
 // Memory-bound work stays on the VALU: 16 lanes cover one 256-byte row with
 // one 16-byte load each, q.k uses v_dot2_f32_bf16, the 16-lane sum uses DPP,
@@ -34,11 +43,14 @@ namespace {
 
 using namespace dev;
 
-constexpr int kThreads = 256;   // 4 waves per streaming workgroup
+constexpr int kThreads = 256;   // 4 waves per workgroup
 constexpr int kWaves = kThreads / 64;
-constexpr int kU = 4;           // rows in flight per lane group per iteration
-constexpr int kSelThreads = 1024;
-constexpr int kSelLds = 16384;  // keys staged in LDS by the select kernel
+#ifndef GSA_ROWS_IN_FLIGHT
+#define GSA_ROWS_IN_FLIGHT 2
+#endif
+constexpr int kU = GSA_ROWS_IN_FLIGHT;   // rows per lane group per batch (two batches in flight)
+constexpr int kTaskScores = 1024;        // scores a gist workgroup gathers in LDS
+constexpr int kSelLds = 1024;   // selected chunk ids staged in LDS by unfold tasks
 
 template <bool BF16, int D>
 struct Geo {
@@ -56,24 +68,26 @@ struct State {
   float m[G], l[G], acc[G][Slice<BF16>::N];
 };
 
-// How item i of a pass maps to a cache row of the unit.
+// How item i of a gist pass maps to a cache row of the unit.
 struct RowMap {
   int32_t kind;          // 0: gist i of the interleaved cache; 1: dense row i;
                          // 2: level-1 candidate i of a two-level call
   int32_t C;
-  const int32_t* sel2;   // kind 2: chosen level-2 groups [units][k2]
+  const int32_t* sel2;   // kind 2: chosen level-2 groups, sel2_stride ints per unit
   int32_t G, k2;
   int64_t orphan0;       // kind 2: first level-1 gist no group covers
+  int64_t sel2_stride;
 };
 
+// sel2 was written by an earlier launch: plain loads see it.
 __device__ __forceinline__ int64_t map_row(const RowMap& rm, int unit, int64_t i) {
   if (rm.kind == 0) return i * (rm.C + 1) + rm.C;
   if (rm.kind == 1) return i;
   const int64_t kg = (int64_t)rm.k2 * rm.G;
   int64_t m;
   if (i < kg) {
-    const int64_t grp = rm.sel2[(int64_t)unit * rm.k2 + i / rm.G];
-    if (grp < 0 || grp * rm.G >= rm.orphan0) return -1;   // never taken for a valid selection
+    int64_t grp = rm.sel2[(int64_t)unit * rm.sel2_stride + i / rm.G];
+    if (grp < 0 || grp * rm.G >= rm.orphan0) grp = 0;   // keeps reads in bounds; never taken
     m = grp * rm.G + i % rm.G;
   } else {
     m = rm.orphan0 + (i - kg);
@@ -81,10 +95,36 @@ __device__ __forceinline__ int64_t map_row(const RowMap& rm, int unit, int64_t i
   return m * (rm.C + 1) + rm.C;
 }
 
+// Id reported for item i of a selection.
+struct IdMap {
+  const int32_t* sel2;  // nullptr: id = item index; else level-1 candidate ids
+  int32_t G, k2;
+  int64_t orphan0;
+  int64_t sel2_stride;
+};
+
+__device__ __forceinline__ int32_t map_id(const IdMap& im, int unit, int32_t i) {
+  if (im.sel2 == nullptr) return i;
+  const int32_t kg = im.k2 * im.G;
+  return i < kg ? im.sel2[(size_t)unit * im.sel2_stride + i / im.G] * im.G + i % im.G
+                : (int32_t)(im.orphan0 + (i - kg));
+}
+
 // Stream items [i0, i1) of one unit through the online softmax. row_of(i)
-// gives the cache row of item i or -1 to skip it. When score_out is set, the
-// group score sum_h(q_h . k) * score_mul of item i goes to score_out[i - i0].
-template <bool BF16, int D, int G, class RowOf>
+// gives the cache row of item i; with CAN_SKIP it may return -1 to skip the
+// item. When score_out is set (LDS), the group score of item i goes to
+// score_out[i - i0].
+//
+// Rows are double-buffered in registers: the loads of the next batch are in
+// flight while the current one is folded in. A batch is kU rows per lane group
+// of every wave; the four waves of the workgroup cover consecutive rows.
+//
+// The running max is raised lazily: only when a new scaled logit exceeds it by
+// more than kLazy (log2 units); the softmax weights of the state then stay
+// below 2^kLazy, far inside fp32 range, and most batches skip the rescale.
+constexpr float kLazy = 8.f;
+
+template <bool BF16, int D, int G, bool CAN_SKIP, class RowOf>
 __device__ __forceinline__ void stream_rows(const char* __restrict__ Kb, const char* __restrict__ Vb,
                                             int64_t i0, int64_t i1, RowOf row_of,
                                             const uint4 (&qv)[G], State<BF16, G>& st,
@@ -95,38 +135,44 @@ __device__ __forceinline__ void stream_rows(const char* __restrict__ Kb, const c
   const int lane = threadIdx.x & 63;
   const int lr = lane % LPR;
   const int slot = (threadIdx.x >> 6) * Gm::SLOTS + lane / LPR;
-  const int64_t per_iter = (int64_t)NS * kU;
+  constexpr int64_t kPer = (int64_t)NS * kU;     // items per batch (whole workgroup)
   const int64_t n = i1 - i0;
-  const int64_t iters = n > 0 ? (n + per_iter - 1) / per_iter : 0;
+  const int64_t iters = n > 0 ? (n + kPer - 1) / kPer : 0;
   const size_t lane_off = (size_t)lr * 16;
+  const float c = scale_log2;
 
-  for (int64_t it = 0; it < iters; ++it) {
-    const int64_t base = i0 + it * per_iter;
-    uint4 kr[kU], vr[kU];
-    int64_t rows[kU];
+  struct Batch {
+    uint4 k[kU], v[kU];
+    bool ok[kU];
+  };
+  auto load = [&](int64_t it, Batch& b) {
+    const int64_t base = i0 + it * kPer;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int64_t item = base + u * NS + slot;
       const int64_t row = item < i1 ? row_of(item) : -1;
-      rows[u] = row;
+      b.ok[u] = row >= 0;
       if (row >= 0) {
         const size_t off = (size_t)row * Gm::ROW_BYTES + lane_off;
-        kr[u] = load16(Kb + off);
-        vr[u] = load16(Vb + off);
+        b.k[u] = load16_stream(Kb + off);
+        b.v[u] = load16_stream(Vb + off);
       } else {
-        kr[u] = make_uint4(0u, 0u, 0u, 0u);
-        vr[u] = make_uint4(0u, 0u, 0u, 0u);
+        b.k[u] = make_uint4(0u, 0u, 0u, 0u);
+        b.v[u] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
-    float s[kU][G];
+  };
+  auto fold = [&](int64_t it, const Batch& b) {
+    const int64_t base = i0 + it * kPer;
+    float s[kU][G];   // raw q.k
 #pragma unroll
     for (int u = 0; u < kU; ++u)
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[u][h] = group_sum<LPR>(dot_slice<BF16>(qv[h], kr[u]));
+      for (int h = 0; h < G; ++h) s[u][h] = group_sum<LPR>(dot_slice<BF16>(qv[h], b.k[u]));
     if (score_out != nullptr) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        if (rows[u] >= 0 && lr == 0) {
+        if (b.ok[u] && lr == 0) {
           float t = 0.f;
 #pragma unroll
           for (int h = 0; h < G; ++h) t += s[u][h];
@@ -134,42 +180,70 @@ __device__ __forceinline__ void stream_rows(const char* __restrict__ Kb, const c
         }
       }
     }
-    float vf[kU][VEC];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) widen<BF16>(vr[u], vf[u]);
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[u][h] = b.ok[u] ? s[u][h] : -INFINITY;
+    float cand[G];
+    bool need = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mx = st.m[h];
+      float mx = s[0][h];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        s[u][h] = rows[u] >= 0 ? s[u][h] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[u][h]);
-      }
-      const float a = fexp2(st.m[h] - mx);
-      st.m[h] = mx;
-      float l = st.l[h] * a;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) st.acc[h][e] *= a;
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const float p = fexp2(s[u][h] - mx);
-        l += p;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) st.acc[h][e] = fmaf(p, vf[u][e], st.acc[h][e]);
-      }
-      st.l[h] = l;
+      for (int u = 1; u < kU; ++u) mx = fmaxf(mx, s[u][h]);
+      cand[h] = mx * c;
+      need |= cand[h] > st.m[h] + kLazy;
     }
+    if (__ballot(need) != 0ull) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mn = cand[h] > st.m[h] + kLazy ? cand[h] : st.m[h];
+        const float a = fexp2(st.m[h] - mn);
+        st.m[h] = mn;
+        st.l[h] *= a;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) st.acc[h][e] *= a;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float vf[VEC];
+      widen<BF16>(b.v[u], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = fexp2(fmaf(s[u][h], c, -st.m[h]));
+        st.l[h] += p;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) st.acc[h][e] = fmaf(p, vf[e], st.acc[h][e]);
+      }
+    }
+  };
+  (void)sizeof(CAN_SKIP);
+
+  Batch A, B;
+  if (iters > 0) load(0, A);
+  for (int64_t it = 0; it < iters; it += 2) {
+    if (it + 1 < iters) load(it + 1, B);
+    fold(it, A);
+    if (it + 1 >= iters) break;
+    if (it + 2 < iters) load(it + 2, A);
+    fold(it + 1, B);
   }
 }
+
+template <int D, int G>
+struct PartLds {
+  float m[kWaves][G], l[kWaves][G];
+  float acc[kWaves][G][D];
+};
 
 // Merge the lane groups' states of the workgroup and write one partial
 // (m, l, acc[D]) per head to `dst` ([G][D + 2] floats).
 template <bool BF16, int D, int G>
-__device__ __forceinline__ void write_partial(State<BF16, G>& st, float* __restrict__ dst) {
+__device__ __forceinline__ void write_partial(State<BF16, G>& st, float* __restrict__ dst,
+                                              PartLds<D, G>& L, bool poison) {
   using Gm = Geo<BF16, D>;
   constexpr int VEC = Gm::VEC, LPR = Gm::LPR;
-  __shared__ float s_m[kWaves][G], s_l[kWaves][G];
-  __shared__ float s_acc[kWaves][G][D];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lr = lane % LPR;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -189,32 +263,311 @@ __device__ __forceinline__ void write_partial(State<BF16, G>& st, float* __restr
     }
     if (lane < LPR) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) s_acc[w][h][lr * VEC + e] = acc[e];
+      for (int e = 0; e < VEC; ++e) L.acc[w][h][lr * VEC + e] = acc[e];
       if (lane == 0) {
-        s_m[w][h] = mw;
-        s_l[w][h] = l;
+        L.m[w][h] = mw;
+        L.l[w][h] = l;
       }
     }
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D, d = idx % D;
-    float M = s_m[0][h];
+    float M = L.m[0][h];
 #pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
-    float L = 0.f, A = 0.f;
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, L.m[ww][h]);
+    float S = 0.f, A = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = fexp2(s_m[ww][h] - M);
-      L = fmaf(s_l[ww][h], f, L);
-      A = fmaf(s_acc[ww][h][d], f, A);
+      const float f = fexp2(L.m[ww][h] - M);
+      S = fmaf(L.l[ww][h], f, S);
+      A = fmaf(L.acc[ww][h][d], f, A);
     }
-    dst[h * (D + 2) + 2 + d] = A;
+    st_coh(dst + h * (D + 2) + 2 + d, A);
     if (d == 0) {
-      dst[h * (D + 2)] = M;
-      dst[h * (D + 2) + 1] = L;
+      st_coh(dst + h * (D + 2), M);
+      st_coh(dst + h * (D + 2) + 1, poison ? NAN : S);
     }
   }
+}
+
+// ------------------------------------------------------------- top-k -------
+
+constexpr int kSelKeys = 4096;                    // keys staged in LDS by the selector
+constexpr int kSub = 4;                           // items per thread per round
+constexpr int kRound = kThreads * kSub;           // items per round (1024)
+constexpr int kStage = kSelKeys / kThreads;       // staging loads per thread (all in flight)
+constexpr int kDigitBits = 8;                     // radix digit; 4 passes cover 32 bits
+constexpr int kBins = 1 << kDigitBits;
+
+struct TopkLds {
+  uint32_t hist[kBins];
+  uint32_t keys[kSelKeys];
+  int scan[kWaves];
+  int bcast[3];
+  int cnt[kSub][kWaves];
+};
+
+// Exclusive prefix over threads of v; *total gets the sum over the block.
+__device__ __forceinline__ int block_scan_total(int v, int* buf, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) buf[w] = x;
+  __syncthreads();
+  int base = 0, t = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const int b = buf[i];
+    base += i < w ? b : 0;
+    t += b;
+  }
+  __syncthreads();
+  *total = t;
+  return base + x - v;
+}
+
+// Keys of items b0 + s*kThreads + tid (s < kSub): from LDS when staged,
+// else device-scope loads issued together.
+__device__ __forceinline__ void round_keys(const CohBuf& sc, int n, int b0, bool in_lds,
+                                           const TopkLds& L, uint32_t (&kr)[kSub]) {
+#pragma unroll
+  for (int q = 0; q < kSub; ++q) {
+    const int i = b0 + q * kThreads + (int)threadIdx.x;
+    const uint32_t g = in_lds ? 0u : sc.u32(i);
+    kr[q] = i < n ? (in_lds ? L.keys[i] : order_key(__uint_as_float(g))) : 0u;
+  }
+}
+
+// Block-wide exclusive prefix, in item order (round-major, then thread), of
+// one round's per-item flags; `bal` holds this wave's ballots. Writes this
+// thread's prefix per item to pre[] and adds the round total to *base.
+__device__ __forceinline__ void round_prefix(const uint64_t (&bal)[kSub], int (&pre)[kSub],
+                                             int* base, TopkLds& L) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) {
+#pragma unroll
+    for (int q = 0; q < kSub; ++q) L.cnt[q][w] = __popcll(bal[q]);
+  }
+  __syncthreads();
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int run = *base;
+#pragma unroll
+  for (int q = 0; q < kSub; ++q) {
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const int c = L.cnt[q][ww];
+      before += ww < w ? c : 0;
+      tot += c;
+    }
+    pre[q] = run + before + __popcll(bal[q] & lt);
+    run += tot;
+  }
+  *base = run;
+  __syncthreads();
+}
+
+// Exact top-k of the n scores sc[0..n) of one unit, written in ascending item
+// order (ids through `im`) to dst (device-scope stores) and, if set, dst2.
+// Keys are the scores' order-preserving uint32 images; ties go to the smaller
+// item index. Radix select, most significant 8-bit digit first:
+// each pass histograms the keys that still match the known prefix, finds the
+// digit holding the k-th largest key, and stops early once that digit's keys
+// are all needed. The result is every key whose prefix is above the found
+// prefix plus the first `need` keys equal to it, in item order. Up to 4096
+// keys are staged in LDS once (one round trip); more are re-read in rounds.
+__device__ void block_topk(const float* __restrict__ scores, int n, int k, const IdMap& im, int unit,
+                           int32_t* __restrict__ dst, int32_t* __restrict__ dst2, TopkLds& L) {
+  const int tid = threadIdx.x;
+  const CohBuf sc(scores, (uint32_t)n * 4u);
+  if (k <= 0) return;
+  if (k >= n) {
+    for (int i = tid; i < n; i += kThreads) {
+      const int32_t id = map_id(im, unit, i);
+      st_coh(dst + i, id);
+      if (dst2) dst2[i] = id;
+    }
+    return;
+  }
+  const bool in_lds = n <= kSelKeys;
+  if (in_lds) {   // stage every key with one round of independent loads
+    uint32_t kr[kStage];
+#pragma unroll
+    for (int q = 0; q < kStage; ++q) {
+      const int i = q * kThreads + tid;
+      const uint32_t g = sc.u32(i);
+      kr[q] = i < n ? order_key(__uint_as_float(g)) : 0u;
+    }
+#pragma unroll
+    for (int q = 0; q < kStage; ++q) {
+      const int i = q * kThreads + tid;
+      if (i < n) L.keys[i] = kr[q];
+    }
+    __syncthreads();
+  }
+  uint32_t prefix = 0u, pmask = 0u;
+  int need = k;
+#pragma unroll 1
+  for (int pass = 0; pass < 32 / kDigitBits; ++pass) {
+    const int sh = 32 - kDigitBits * (pass + 1);
+    const int nb = kBins;
+    const uint32_t dm = (uint32_t)nb - 1u;
+    for (int b = tid; b < nb; b += kThreads) L.hist[b] = 0u;
+    __syncthreads();
+    for (int b0 = 0; b0 < n; b0 += kRound) {
+      uint32_t kr[kSub];
+      round_keys(sc, n, b0, in_lds, L, kr);
+#pragma unroll
+      for (int q = 0; q < kSub; ++q) {
+        const int i = b0 + q * kThreads + tid;
+        if (i < n && (kr[q] & pmask) == prefix) atomicAdd(&L.hist[(kr[q] >> sh) & dm], 1u);
+      }
+    }
+    __syncthreads();
+    const int per = nb / kThreads;              // digits owned by this thread
+    int c = 0;
+    for (int j = 0; j < per; ++j) c += (int)L.hist[tid * per + j];
+    int total;
+    const int excl = block_scan_total(c, L.scan, &total);
+    const int above_t = total - excl - c;       // keys in digits owned by higher threads
+    if (above_t < need && need <= above_t + c) {
+      int acc = above_t;
+      for (int j = per - 1; j >= 0; --j) {
+        const int h = (int)L.hist[tid * per + j];
+        if (acc + h >= need) {
+          L.bcast[0] = tid * per + j;
+          L.bcast[1] = acc;
+          L.bcast[2] = h;
+          break;
+        }
+        acc += h;
+      }
+    }
+    __syncthreads();
+    const uint32_t dg = (uint32_t)L.bcast[0];
+    const int above = L.bcast[1], inbin = L.bcast[2];
+    __syncthreads();
+    need -= above;
+    prefix |= dg << sh;
+    pmask |= dm << sh;
+    if (need == inbin) break;                   // every key with this prefix is taken
+  }
+  // ordered compaction: ranks among equal keys, then output positions
+  int eq_base = 0, pos_base = 0;
+  for (int b0 = 0; b0 < n; b0 += kRound) {
+    uint32_t kr[kSub];
+    round_keys(sc, n, b0, in_lds, L, kr);
+    uint64_t bal[kSub];
+    bool gt[kSub], eq[kSub];
+#pragma unroll
+    for (int q = 0; q < kSub; ++q) {
+      const int i = b0 + q * kThreads + tid;
+      const uint32_t mk = kr[q] & pmask;
+      gt[q] = i < n && mk > prefix;
+      eq[q] = i < n && mk == prefix;
+      bal[q] = __ballot(eq[q]);
+    }
+    int pre[kSub];
+    round_prefix(bal, pre, &eq_base, L);
+    bool pick[kSub];
+#pragma unroll
+    for (int q = 0; q < kSub; ++q) {
+      pick[q] = gt[q] || (eq[q] && pre[q] < need);
+      bal[q] = __ballot(pick[q]);
+    }
+    round_prefix(bal, pre, &pos_base, L);
+#pragma unroll
+    for (int q = 0; q < kSub; ++q) {
+      const int pos = pre[q];
+      if (pick[q] && pos >= 0 && pos < k) {
+        const int32_t id = map_id(im, unit, b0 + q * kThreads + tid);
+        st_coh(dst + pos, id);
+        if (dst2) dst2[pos] = id;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------- merge -------
+
+constexpr int kMergeBatch = 8;   // partials whose loads are in flight together
+
+// out[h][d] = sum_j 2^(m_j - m*) acc_j[d] / sum_j 2^(m_j - m*) l_j over the
+// unit's NP partials. One wave per head; each lane owns D/64 output elements;
+// the device-scope loads of a batch of partials are issued together (one
+// round trip per batch) and folded into a running (max, sum, acc) state.
+template <int D, int G>
+__device__ void merge_unit(const float* __restrict__ part_u, int NP, uint32_t ps,
+                           float* __restrict__ out, float* __restrict__ lse) {
+  constexpr int PL = D / 64;                  // outputs per lane
+  const CohBuf P(part_u, (uint32_t)NP * ps * 4u);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int h = w; h < G; h += kWaves) {
+    float mx = kMinus, L = 0.f, acc[PL];
+#pragma unroll
+    for (int e = 0; e < PL; ++e) acc[e] = 0.f;
+    for (int j0 = 0; j0 < NP; j0 += kMergeBatch) {
+      float m[kMergeBatch], l[kMergeBatch], a[kMergeBatch][PL];
+#pragma unroll
+      for (int b = 0; b < kMergeBatch; ++b) {
+        // past NP the buffer returns 0: those slots get weight 0 below
+        const uint32_t o = (uint32_t)(j0 + b) * ps + (uint32_t)h * (D + 2);
+        m[b] = __uint_as_float(P.u32(o));
+        l[b] = __uint_as_float(P.u32(o + 1));
+#pragma unroll
+        for (int e = 0; e < PL; ++e) a[b][e] = __uint_as_float(P.u32(o + 2 + lane + 64 * e));
+      }
+#pragma unroll
+      for (int b = 0; b < kMergeBatch; ++b) m[b] = j0 + b < NP ? m[b] : kMinus;
+      float nm = mx;
+#pragma unroll
+      for (int b = 0; b < kMergeBatch; ++b) nm = fmaxf(nm, m[b]);
+      const float r = fexp2(mx - nm);
+      L *= r;
+#pragma unroll
+      for (int e = 0; e < PL; ++e) acc[e] *= r;
+#pragma unroll
+      for (int b = 0; b < kMergeBatch; ++b) {
+        const float f = j0 + b < NP ? fexp2(m[b] - nm) : 0.f;
+        L = fmaf(l[b], f, L);
+#pragma unroll
+        for (int e = 0; e < PL; ++e) acc[e] = fmaf(a[b][e], f, acc[e]);
+      }
+      mx = nm;
+    }
+#pragma unroll
+    for (int e = 0; e < PL; ++e) out[(size_t)h * D + lane + 64 * e] = acc[e] / L;
+    if (lse != nullptr && lane == 0) lse[h] = (mx + log2f(L)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------- hand-offs ------
+
+// Every write of a control word is an atomic read-modify-write: those are
+// performed at one coherence point for the whole chip, whereas two plain
+// stores to one word from different XCDs go through different L2 caches and
+// may reach memory in either order.
+__device__ __forceinline__ void ctrl_set(uint32_t* w, uint32_t v) {
+  (void)__hip_atomic_exchange(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Count this workgroup finished once its hand-off stores have completed;
+// true in the unit's last one, which then resets the counter for the next
+// launch. The last one reads the others' data with device-scope loads.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, uint32_t* s_old) {
+  done_stores();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const bool last = *s_old == expected - 1u;
+  if (last && threadIdx.x == 0) ctrl_set(counter, 0u);
+  return last;
 }
 
 template <bool BF16, int D, int G>
@@ -237,178 +590,156 @@ __device__ __forceinline__ void init_state(State<BF16, G>& st) {
   }
 }
 
-// ---------------------------------------------------------------- kernels ---
+// ------------------------------------------------------------ kernels ------
 
-// Scores and attends a contiguous range of gist-like items of one unit.
-template <bool BF16, int D, int G>
-__global__ __launch_bounds__(kThreads) void gist_pass_kernel(
-    const void* __restrict__ q, const void* __restrict__ K, const void* __restrict__ V,
-    int64_t unit_rows, int64_t n_items, int64_t per_split, int32_t S, RowMap rm,
-    float* __restrict__ scores, int64_t score_stride, float* __restrict__ part, int32_t NP,
-    int32_t part_base, float scale_log2, float score_mul) {
-  using Gm = Geo<BF16, D>;
-  const int unit = blockIdx.x / S;
-  const int split = blockIdx.x % S;
-  uint4 qv[G];
-  load_q<BF16, D, G>(q, unit, qv);
-  State<BF16, G> st;
-  init_state<BF16, G>(st);
-  const size_t ub = (size_t)unit * (size_t)unit_rows * Gm::ROW_BYTES;
-  const char* Kb = reinterpret_cast<const char*>(K) + ub;
-  const char* Vb = reinterpret_cast<const char*>(V) + ub;
-  const int64_t i0 = (int64_t)split * per_split;
-  const int64_t i1 = i0 + per_split < n_items ? i0 + per_split : n_items;
-  float* so = scores ? scores + (size_t)unit * score_stride + i0 : nullptr;
-  stream_rows<BF16, D, G>(Kb, Vb, i0, i1, [&](int64_t i) { return map_row(rm, unit, i); }, qv, st,
-                          scale_log2, so, score_mul);
-  write_partial<BF16, D, G>(st, part + ((size_t)unit * NP + part_base + split) * G * (D + 2));
-}
-
-// Raw rows of the selected chunks (minus rows the tail owns), then the tail.
-template <bool BF16, int D, int G>
-__global__ __launch_bounds__(kThreads) void unfold_kernel(
-    const void* __restrict__ q, const void* __restrict__ K, const void* __restrict__ V,
-    int64_t unit_rows, const int32_t* __restrict__ sel, int32_t k, int32_t C, int64_t M,
-    int64_t N, int32_t T, int32_t n_items, int32_t per_split, int32_t S2,
-    float* __restrict__ part, int32_t NP, int32_t part_base, float scale_log2) {
-  using Gm = Geo<BF16, D>;
-  __shared__ int32_t s_sel[1024];
-  const int unit = blockIdx.x / S2;
-  const int split = blockIdx.x % S2;
-  const int32_t* us = sel + (size_t)unit * k;
-  const bool sel_in_lds = k <= 1024;
-  if (sel_in_lds)
-    for (int i = threadIdx.x; i < k; i += kThreads) s_sel[i] = us[i];
-  __syncthreads();
-  uint4 qv[G];
-  load_q<BF16, D, G>(q, unit, qv);
-  State<BF16, G> st;
-  init_state<BF16, G>(st);
-  const size_t ub = (size_t)unit * (size_t)unit_rows * Gm::ROW_BYTES;
-  const char* Kb = reinterpret_cast<const char*>(K) + ub;
-  const char* Vb = reinterpret_cast<const char*>(V) + ub;
-  const int64_t i0 = (int64_t)split * per_split;
-  const int64_t i1 = i0 + per_split < n_items ? i0 + per_split : n_items;
-  const int64_t kC = (int64_t)k * C;
-  const int64_t tail0 = N - T;
-  auto row_of = [&](int64_t i) -> int64_t {
-    if (i < kC) {
-      const int64_t m = sel_in_lds ? s_sel[i / C] : us[i / C];
-      const int64_t j = i % C;
-      if (m < 0 || m >= M) return -1;             // never taken for a valid selection
-      if (m * C + j >= tail0) return -1;          // the tail attends this row
-      return m * (C + 1) + j;
-    }
-    const int64_t p = tail0 + (i - kC);
-    return p < M * C ? (p / C) * (C + 1) + p % C : M * (C + 1) + (p - M * C);
-  };
-  stream_rows<BF16, D, G>(Kb, Vb, i0, i1, row_of, qv, st, scale_log2, nullptr, 0.f);
-  write_partial<BF16, D, G>(st, part + ((size_t)unit * NP + part_base + split) * G * (D + 2));
-}
-
-struct IdMap {
-  const int32_t* sel2;  // nullptr: id = item index
-  int32_t G, k2;
-  int64_t orphan0;
+// A pass over gist-like rows of every unit: scores + attention partials; the
+// unit's last workgroup selects the top-k of the pass's scores.
+struct GistArgs {
+  const void* q;
+  const void* K;
+  const void* V;
+  int64_t unit_rows;      // rows per unit in K/V
+  int64_t n_items;        // items per unit
+  int64_t per_task;       // items per workgroup
+  int32_t tasks;          // workgroups per unit
+  RowMap rm;
+  float* scores;          // [units][score_stride]
+  int64_t score_stride;
+  float* part;            // [units][NP][part_stride]
+  int64_t part_stride;
+  int32_t NP, part_base;
+  int32_t sel_k;
+  IdMap im;
+  int32_t* sel_ws;        // [units][sel_stride]
+  int64_t sel_stride;
+  int32_t* sel_out;       // [units][sel_k] or null
+  uint32_t* cnt;          // unit u's counter at cnt[u * kCtrlUnitWords]
+  float scale_log2;       // softmax logits in log2 units
+  float score_mul;        // group score = sum_h(q_h . k) * score_mul
 };
 
-__device__ __forceinline__ int32_t map_id(const IdMap& im, int unit, int32_t i) {
-  if (im.sel2 == nullptr) return i;
-  const int32_t kg = im.k2 * im.G;
-  return i < kg ? im.sel2[(size_t)unit * im.k2 + i / im.G] * im.G + i % im.G
-                : (int32_t)(im.orphan0 + (i - kg));
-}
+template <int D, int G>
+union GistLds {
+  struct {
+    float scores[kTaskScores];   // this workgroup's scores, written out as whole lines
+  } s;
+  PartLds<D, G> part;
+  TopkLds topk;
+};
 
-// Exact top-k of n scores per unit. The k-th largest order key T is found by
-// a bitwise search over the 32 key bits (count(key >= candidate) >= k keeps
-// the bit); then every key > T and the first (k - count(key > T)) keys == T in
-// index order are written in ascending index order.
-__global__ __launch_bounds__(kSelThreads) void select_kernel(const float* __restrict__ scores,
-                                                             int64_t stride, int32_t n, int32_t k,
-                                                             IdMap im, int32_t* __restrict__ ws_sel,
-                                                             int32_t* __restrict__ out_sel) {
-  __shared__ uint32_t keys[kSelLds];
-  __shared__ int red[3][kSelThreads / 64];
-  const int unit = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (k <= 0) return;
-  const float* sc = scores + (size_t)unit * stride;
-  int32_t* dst = ws_sel + (size_t)unit * k;
-  int32_t* dst2 = out_sel ? out_sel + (size_t)unit * k : nullptr;
-  if (k >= n) {  // everything is selected (k == n)
-    for (int i = tid; i < n; i += kSelThreads) {
-      const int32_t id = map_id(im, unit, i);
-      dst[i] = id;
-      if (dst2) dst2[i] = id;
-    }
-    return;
-  }
-  const bool in_lds = n <= kSelLds;
-  if (in_lds)
-    for (int i = tid; i < n; i += kSelThreads) keys[i] = order_key(sc[i]);
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(kThreads) void gist_kernel(GistArgs a) {
+  using Gm = Geo<BF16, D>;
+  __shared__ GistLds<D, G> lds;
+  __shared__ uint32_t s_old;
+  const int unit = blockIdx.x / a.tasks, split = blockIdx.x % a.tasks;
+  uint4 qv[G];
+  load_q<BF16, D, G>(a.q, unit, qv);
+  State<BF16, G> st;
+  init_state<BF16, G>(st);
+  const size_t ub = (size_t)unit * (size_t)a.unit_rows * Gm::ROW_BYTES;
+  const int64_t i0 = (int64_t)split * a.per_task;
+  const int64_t i1 = i0 + a.per_task < a.n_items ? i0 + a.per_task : a.n_items;
+  const RowMap rm = a.rm;
+  stream_rows<BF16, D, G, false>(reinterpret_cast<const char*>(a.K) + ub,
+                                 reinterpret_cast<const char*>(a.V) + ub, i0, i1,
+                                 [&](int64_t i) { return map_row(rm, unit, i); }, qv, st,
+                                 a.scale_log2, lds.s.scores, a.score_mul);
   __syncthreads();
-  auto key_at = [&](int i) -> uint32_t { return in_lds ? keys[i] : order_key(sc[i]); };
-
-  uint32_t T = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    int c = 0;
-    for (int i = tid; i < n; i += kSelThreads) c += key_at(i) >= cand ? 1 : 0;
-    if (block_sum(c, red[bit & 1]) >= k) T = cand;
-  }
-  int cgt = 0;
-  for (int i = tid; i < n; i += kSelThreads) cgt += key_at(i) > T ? 1 : 0;
-  const int need = k - block_sum(cgt, red[2]);   // keys equal to T still to take (>= 1)
-
-  const int E = (n + kSelThreads - 1) / kSelThreads;
-  const int lo = tid * E < n ? tid * E : n;
-  const int hi = lo + E < n ? lo + E : n;
-  int gt = 0, eq = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = key_at(i);
-    gt += key > T ? 1 : 0;
-    eq += key == T ? 1 : 0;
-  }
-  const int eq_before = block_excl_scan(eq, red[0]);
-  int take = need - eq_before;
-  take = take < 0 ? 0 : (take > eq ? eq : take);
-  int pos = block_excl_scan(gt + take, red[1]);
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = key_at(i);
-    bool pick = key > T;
-    if (!pick && key == T && take > 0) {
-      pick = true;
-      --take;
-    }
-    if (pick) {
-      const int32_t id = map_id(im, unit, i);
-      dst[pos] = id;
-      if (dst2) dst2[pos] = id;
-      ++pos;
-    }
+  // scores out as contiguous device-scope stores (the unit's last workgroup reads them)
+  float* so = a.scores + (size_t)unit * a.score_stride + i0;
+  for (int64_t i = threadIdx.x; i < i1 - i0; i += kThreads) st_coh(so + i, lds.s.scores[i]);
+  __syncthreads();   // LDS changes role: scores -> partial merge
+  float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
+  write_partial<BF16, D, G>(st, part_u + (size_t)(a.part_base + split) * a.part_stride, lds.part, false);
+  if (arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)a.tasks, &s_old)) {
+    __syncthreads();   // LDS changes role: partial merge -> selection
+    block_topk(a.scores + (size_t)unit * a.score_stride, (int)a.n_items, a.sel_k, a.im, unit,
+               a.sel_ws + (size_t)unit * a.sel_stride,
+               a.sel_out ? a.sel_out + (size_t)unit * a.sel_k : nullptr, lds.topk);
   }
 }
 
-// out[unit, h] = sum_p 2^(m_p - m*) acc_p / sum_p 2^(m_p - m*) l_p.
-template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(const float* __restrict__ part, int32_t NP,
-                                                  int32_t G, float* __restrict__ out,
-                                                  float* __restrict__ lse) {
-  const int uh = blockIdx.x;          // unit * G + h
-  const int unit = uh / G, h = uh % G;
-  const int d = threadIdx.x;
-  const float* P = part + (size_t)unit * NP * G * (D + 2) + (size_t)h * (D + 2);
-  const size_t ps = (size_t)G * (D + 2);
-  float mx = kMinus;
-  for (int p = 0; p < NP; ++p) mx = fmaxf(mx, P[p * ps]);
-  float L = 0.f, A = 0.f;
-  for (int p = 0; p < NP; ++p) {
-    const float f = fexp2(P[p * ps] - mx);
-    L = fmaf(P[p * ps + 1], f, L);
-    A = fmaf(P[p * ps + 2 + d], f, A);
-  }
-  out[(size_t)uh * D + d] = A / L;
-  if (lse != nullptr && d == 0) lse[uh] = (mx + log2f(L)) * kLn2;
+// Raw rows of the selected chunks (minus rows the tail owns) and the tail;
+// the unit's last workgroup merges every partial into out and lse.
+struct UnfoldArgs {
+  const void* q;
+  const void* K;
+  const void* V;
+  int64_t unit_rows;
+  const int32_t* sel;     // [units][sel_stride] chosen chunks (earlier launch)
+  int64_t sel_stride;
+  int32_t k;
+  int32_t C, T;
+  int64_t M, N;
+  int64_t tail_q;         // (N - T) / C
+  uint32_t tail_r;        // (N - T) % C
+  int64_t n_items, per_task;
+  int32_t tasks;
+  float* part;
+  int64_t part_stride;
+  int32_t NP, part_base;
+  float* out;
+  float* lse;
+  uint32_t* cnt;
+  float scale_log2;
+};
+
+template <int D, int G>
+union UnfoldLds {
+  struct {
+    int32_t sel[kSelLds];
+  } s;
+  PartLds<D, G> part;
+};
+
+template <bool BF16, int D, int G>
+__global__ __launch_bounds__(kThreads) void unfold_kernel(UnfoldArgs a) {
+  using Gm = Geo<BF16, D>;
+  __shared__ UnfoldLds<D, G> lds;
+  __shared__ uint32_t s_old;
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x / a.tasks, split = blockIdx.x % a.tasks;
+  const int32_t* us = a.sel + (size_t)unit * a.sel_stride;
+  const bool in_lds = a.k <= kSelLds;
+  if (in_lds)
+    for (int i = tid; i < a.k; i += kThreads) lds.s.sel[i] = us[i];
+  __syncthreads();
+  uint4 qv[G];
+  load_q<BF16, D, G>(a.q, unit, qv);
+  State<BF16, G> st;
+  init_state<BF16, G>(st);
+  const size_t ub = (size_t)unit * (size_t)a.unit_rows * Gm::ROW_BYTES;
+  const int64_t i0 = (int64_t)split * a.per_task;
+  const int64_t i1 = i0 + a.per_task < a.n_items ? i0 + a.per_task : a.n_items;
+  // 32-bit index math: items < 2^30, positions split as tail0 = tail_q * C + tail_r
+  const uint32_t C = (uint32_t)a.C;
+  const uint32_t kC = (uint32_t)a.k * C;
+  const int64_t M = a.M, tail0 = a.N - a.T, MC = a.M * a.C;
+  const int32_t* s_sel = lds.s.sel;
+  auto row_of = [&](int64_t i64) -> int64_t {
+    const uint32_t i = (uint32_t)i64;
+    if (i < kC) {
+      const uint32_t ci = i / C, j = i - ci * C;
+      const int64_t m = in_lds ? s_sel[ci] : us[ci];
+      if (m < 0 || m >= M) return -1;         // never taken for a valid selection
+      if (m * C + j >= tail0) return -1;      // the tail attends this row
+      return m * (C + 1) + j;
+    }
+    const uint32_t rel = a.tail_r + (i - kC);
+    const int64_t pos = tail0 + (i - kC);
+    const int64_t chunk = a.tail_q + rel / C;
+    return pos < MC ? chunk * (C + 1) + rel % C : M * (C + 1) + (pos - MC);
+  };
+  stream_rows<BF16, D, G, true>(reinterpret_cast<const char*>(a.K) + ub,
+                                reinterpret_cast<const char*>(a.V) + ub, i0, i1, row_of, qv, st,
+                                a.scale_log2, nullptr, 0.f);
+  float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
+  __syncthreads();   // LDS changes role: selected ids -> partial merge
+  write_partial<BF16, D, G>(st, part_u + (size_t)(a.part_base + split) * a.part_stride, lds.part, false);
+  if (arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)a.tasks, &s_old))
+    merge_unit<D, G>(part_u, a.NP, (uint32_t)a.part_stride, a.out + (size_t)unit * G * D,
+                     a.lse ? a.lse + (size_t)unit * G : nullptr);
 }
 
 // ------------------------------------------------------------------ host ---
@@ -419,24 +750,40 @@ gsa_status_t launch_status(const char* what) {
   return GSA_OK;
 }
 
+// Counter regions: word p of each unit's control block counts phase p.
+inline uint32_t* ctrl_of(char* ws, size_t off_ctrl, int phase) {
+  return reinterpret_cast<uint32_t*>(ws + off_ctrl) + phase;
+}
+
 template <bool BF16, int D, int G>
 gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, const void* V,
                         float* out, float* lse, int32_t* sel_idx, char* ws, hipStream_t st) {
   float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
   int32_t* wsel = reinterpret_cast<int32_t*>(ws + pl.off_sel);
   float* part = reinterpret_cast<float*>(ws + pl.off_part);
-  const float sl2 = pl.scale * kLog2e;
-  RowMap rm{0, pl.C, nullptr, 0, 0, 0};
-  hipLaunchKernelGGL((gist_pass_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st,
-                     q, K, V, pl.R, pl.M, pl.gists_per_split, pl.S, rm, scores, pl.score_stride,
-                     part, pl.NP, 0, sl2, pl.scale / G);
-  if (pl.k > 0)
-    hipLaunchKernelGGL(select_kernel, dim3(pl.units), dim3(kSelThreads), 0, st, scores,
-                       pl.score_stride, (int32_t)pl.M, pl.k, IdMap{nullptr, 0, 0, 0}, wsel, sel_idx);
-  hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, q,
-                     K, V, pl.R, wsel, pl.k, pl.C, pl.M, pl.N, pl.T, pl.n_items, pl.items_per_split,
-                     pl.S2, part, pl.NP, pl.S, sl2);
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(pl.units * G), dim3(D), 0, st, part, pl.NP, G, out, lse);
+  const int64_t ps = part_stride(G, D);
+  GistArgs g{};
+  g.q = q; g.K = K; g.V = V;
+  g.unit_rows = pl.R; g.n_items = pl.M; g.per_task = pl.gists_per_split; g.tasks = pl.S;
+  g.rm = RowMap{0, pl.C, nullptr, 0, 0, 0, 0};
+  g.scores = scores; g.score_stride = pl.score_stride;
+  g.part = part; g.part_stride = ps; g.NP = pl.NP; g.part_base = 0;
+  g.sel_k = pl.k; g.im = IdMap{nullptr, 0, 0, 0, 0};
+  g.sel_ws = wsel; g.sel_stride = pl.sel_stride; g.sel_out = sel_idx;
+  g.cnt = ctrl_of(ws, pl.off_ctrl, 0);
+  g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
+  hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st, g);
+  UnfoldArgs u{};
+  u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
+  u.sel = wsel; u.sel_stride = pl.sel_stride; u.k = pl.k;
+  u.C = pl.C; u.T = pl.T; u.M = pl.M; u.N = pl.N;
+  u.tail_q = (pl.N - pl.T) / pl.C; u.tail_r = (uint32_t)((pl.N - pl.T) % pl.C);
+  u.n_items = pl.n_items; u.per_task = pl.items_per_split; u.tasks = pl.S2;
+  u.part = part; u.part_stride = ps; u.NP = pl.NP; u.part_base = pl.S;
+  u.out = out; u.lse = lse;
+  u.cnt = ctrl_of(ws, pl.off_ctrl, 2);
+  u.scale_log2 = pl.scale * kLog2e;
+  hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
   return launch_status("gsa_decode launch");
 }
 
@@ -450,31 +797,45 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   int32_t* wsel2 = reinterpret_cast<int32_t*>(ws + hp.off_sel2);
   int32_t* wsel1 = reinterpret_cast<int32_t*>(ws + hp.off_sel1);
   float* part = reinterpret_cast<float*>(ws + hp.off_part);
-  const float sl2 = pl.scale * kLog2e;
+  const int64_t ps = part_stride(G, D);
   const int64_t orphan0 = hp.M2 * hp.G;
-  // level 2: every meta-gist (dense rows of the level-2 array)
-  RowMap r2{1, pl.C, nullptr, 0, 0, 0};
-  hipLaunchKernelGGL((gist_pass_kernel<BF16, D, G>), dim3(pl.units * hp.S_l2), dim3(kThreads), 0,
-                     st, q, K2, V2, hp.M2, hp.M2, hp.l2_per_split, hp.S_l2, r2, s2, hp.s2_stride,
-                     part, hp.NP, 0, sl2, pl.scale / G);
-  if (hp.k2 > 0)
-    hipLaunchKernelGGL(select_kernel, dim3(pl.units), dim3(kSelThreads), 0, st, s2, hp.s2_stride,
-                       (int32_t)hp.M2, hp.k2, IdMap{nullptr, 0, 0, 0}, wsel2, sel2);
-  // level 1: children of the chosen groups + ungrouped gists
-  RowMap r1{2, pl.C, wsel2, hp.G, hp.k2, orphan0};
-  hipLaunchKernelGGL((gist_pass_kernel<BF16, D, G>), dim3(pl.units * hp.S_c), dim3(kThreads), 0,
-                     st, q, K, V, pl.R, (int64_t)hp.n_cand, (int64_t)hp.cand_per_split, hp.S_c, r1,
-                     sc, hp.sc_stride, part, hp.NP, hp.S_l2, sl2, pl.scale / G);
-  if (pl.k > 0)
-    hipLaunchKernelGGL(select_kernel, dim3(pl.units), dim3(kSelThreads), 0, st, sc, hp.sc_stride,
-                       hp.n_cand, pl.k, IdMap{wsel2, hp.G, hp.k2, orphan0}, wsel1, sel1);
-  hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, q,
-                     K, V, pl.R, wsel1, pl.k, pl.C, pl.M, pl.N, pl.T, pl.n_items, pl.items_per_split,
-                     pl.S2, part, hp.NP, hp.S_l2 + hp.S_c, sl2);
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(pl.units * G), dim3(D), 0, st, part, hp.NP, G, out, lse);
+  // level 2: every meta-gist (dense rows of the level-2 array), top-k2 groups
+  GistArgs g{};
+  g.q = q; g.K = K2; g.V = V2;
+  g.unit_rows = hp.M2; g.n_items = hp.M2; g.per_task = hp.l2_per_split; g.tasks = hp.S_l2;
+  g.rm = RowMap{1, pl.C, nullptr, 0, 0, 0, 0};
+  g.scores = s2; g.score_stride = hp.s2_stride;
+  g.part = part; g.part_stride = ps; g.NP = hp.NP; g.part_base = 0;
+  g.sel_k = hp.k2; g.im = IdMap{nullptr, 0, 0, 0, 0};
+  g.sel_ws = wsel2; g.sel_stride = hp.sel2_stride; g.sel_out = sel2;
+  g.cnt = ctrl_of(ws, hp.off_ctrl, 0);
+  g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
+  hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_l2), dim3(kThreads), 0, st, g);
+  // level 1: children of the chosen groups + the ungrouped gists, top-k1 chunks
+  GistArgs c = g;
+  c.K = K; c.V = V;
+  c.unit_rows = pl.R; c.n_items = hp.n_cand; c.per_task = hp.cand_per_split; c.tasks = hp.S_c;
+  c.rm = RowMap{2, pl.C, wsel2, hp.G, hp.k2, orphan0, hp.sel2_stride};
+  c.scores = sc; c.score_stride = hp.sc_stride;
+  c.part_base = hp.S_l2;
+  c.sel_k = pl.k; c.im = IdMap{wsel2, hp.G, hp.k2, orphan0, hp.sel2_stride};
+  c.sel_ws = wsel1; c.sel_stride = pl.sel_stride; c.sel_out = sel1;
+  c.cnt = ctrl_of(ws, hp.off_ctrl, 1);
+  hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_c), dim3(kThreads), 0, st, c);
+  // unfold the chosen chunks + tail, merge everything
+  UnfoldArgs u{};
+  u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
+  u.sel = wsel1; u.sel_stride = pl.sel_stride; u.k = pl.k;
+  u.C = pl.C; u.T = pl.T; u.M = pl.M; u.N = pl.N;
+  u.tail_q = (pl.N - pl.T) / pl.C; u.tail_r = (uint32_t)((pl.N - pl.T) % pl.C);
+  u.n_items = pl.n_items; u.per_task = pl.items_per_split; u.tasks = pl.S2;
+  u.part = part; u.part_stride = ps; u.NP = hp.NP; u.part_base = hp.S_l2 + hp.S_c;
+  u.out = out; u.lse = lse;
+  u.cnt = ctrl_of(ws, hp.off_ctrl, 2);
+  u.scale_log2 = pl.scale * kLog2e;
+  hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
   return launch_status("gsa_decode_hier launch");
 }
-
 // Dispatch on (dtype, head_dim, heads per kv-head).
 template <template <bool, int, int> class F, class... Args>
 gsa_status_t dispatch(int32_t dtype, int32_t D, int32_t G, Args&&... args) {

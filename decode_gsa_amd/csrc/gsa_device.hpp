@@ -29,9 +29,45 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Hand-off of data between workgroups of one launch (scores, selections,
+// partial softmax states). The chip has one L2 per XCD and they are not kept
+// coherent with each other, so such data is written and read with
+// device-scope accesses (agent-scope relaxed atomics, i.e. sc1 stores that
+// write through the L2 and sc1 loads that do not hit a stale line). The
+// producer waits for its stores to complete before it signals (done_stores),
+// so no L2 write-back or invalidation is ever needed.
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's outstanding memory stores have completed.
+__device__ __forceinline__ void done_stores() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Device-scope (sc1) loads through a buffer resource over [base, base + bytes);
+// unlike atomic loads they are not serialised, so a batch of them is in
+// flight together. Offsets are in 32-bit words; reads past the end return 0.
+struct CohBuf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ CohBuf(const void* base, uint32_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000)) {}
+  __device__ __forceinline__ uint32_t u32(uint32_t word) const {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)(word * 4u), 0, 16 /* sc1 */);
+  }
+};
+
 // 16-byte global load of raw bits.
 __device__ __forceinline__ uint4 load16(const char* p) {
   return *reinterpret_cast<const uint4*>(p);
+}
+
+// 16-byte load of data read once (nontemporal: streamed past the caches).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const char* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Elements held by one lane in a 16-byte slice.

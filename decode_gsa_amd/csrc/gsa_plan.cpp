@@ -22,10 +22,16 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int64_t kTargetWGs = 2048;
 constexpr int64_t kMinRows = 64;
 
-int32_t splits_for(int64_t rows, int64_t units) {
+// Unfold workgroups get at least this many rows (their start-up costs more
+// relative to the rows they stream).
+constexpr int64_t kMinUnfoldRows = 128;
+// A gist workgroup gathers its scores in LDS: at most this many items each.
+constexpr int64_t kMaxTaskItems = 1024;
+
+int32_t splits_for(int64_t rows, int64_t units, int64_t min_rows = kMinRows) {
   if (rows <= 0) return 1;
   int64_t want = ceil_div(kTargetWGs, units);
-  int64_t cap = ceil_div(rows, kMinRows);
+  int64_t cap = ceil_div(rows, min_rows);
   return clamp_i(want < cap ? want : cap, 1, 1 << 16);
 }
 
@@ -121,21 +127,25 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   d.scale = resolve_scale(p->scale, p->head_dim);
   d.dtype = p->dtype;
   d.S = splits_for(d.M, units);
+  if (ceil_div(d.M, d.S) > kMaxTaskItems) d.S = (int32_t)ceil_div(d.M, kMaxTaskItems);
   d.gists_per_split = d.M > 0 ? ceil_div(d.M, d.S) : 0;
   d.S = d.M > 0 ? (int32_t)ceil_div(d.M, d.gists_per_split) : 1;
   d.n_items = (int32_t)items;
-  d.S2 = splits_for(items, units);
+  d.S2 = splits_for(items, units, kMinUnfoldRows);
   d.items_per_split = items > 0 ? (int32_t)ceil_div(items, d.S2) : 0;
   d.S2 = items > 0 ? (int32_t)ceil_div(items, d.items_per_split) : 1;
   d.NP = d.S + d.S2;
   d.score_stride = (d.M + 63) / 64 * 64;
   size_t off = 0;
+  d.off_ctrl = off;
+  off = align_up(off + ctrl_bytes(units));
   d.off_scores = off;
   off = align_up(off + sizeof(float) * (size_t)units * (size_t)d.score_stride);
   d.off_sel = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)(d.k > 0 ? d.k : 1));
+  d.sel_stride = line_pad(d.k > 0 ? d.k : 1);
+  off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)d.sel_stride);
   d.off_part = off;
-  off = align_up(off + sizeof(float) * (size_t)units * d.NP * d.g * (d.D + 2));
+  off = align_up(off + sizeof(float) * (size_t)units * d.NP * (size_t)part_stride(d.g, d.D));
   d.total = off;
   *o = d;
   return GSA_OK;
@@ -162,25 +172,30 @@ gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
     return fail(GSA_ERR_INVALID_ARG, "topk=%d exceeds the %d level-1 candidates", d.k, h.n_cand);
   int64_t units = d.units;
   h.S_l2 = splits_for(h.M2, units);
+  if (ceil_div(h.M2, h.S_l2) > kMaxTaskItems) h.S_l2 = (int32_t)ceil_div(h.M2, kMaxTaskItems);
   h.l2_per_split = h.M2 > 0 ? ceil_div(h.M2, h.S_l2) : 0;
   h.S_l2 = h.M2 > 0 ? (int32_t)ceil_div(h.M2, h.l2_per_split) : 1;
   h.S_c = splits_for(h.n_cand, units);
+  if (ceil_div(h.n_cand, h.S_c) > kMaxTaskItems) h.S_c = (int32_t)ceil_div(h.n_cand, kMaxTaskItems);
   h.cand_per_split = h.n_cand > 0 ? (int32_t)ceil_div(h.n_cand, h.S_c) : 0;
   h.S_c = h.n_cand > 0 ? (int32_t)ceil_div(h.n_cand, h.cand_per_split) : 1;
   h.NP = h.S_l2 + h.S_c + d.S2;
   h.s2_stride = (h.M2 + 63) / 64 * 64;
   h.sc_stride = (h.n_cand + 63) / 64 * 64;
   size_t off = 0;
+  h.off_ctrl = off;
+  off = align_up(off + ctrl_bytes(units));
   h.off_s2 = off;
   off = align_up(off + sizeof(float) * (size_t)units * (size_t)(h.s2_stride ? h.s2_stride : 1));
   h.off_sc = off;
   off = align_up(off + sizeof(float) * (size_t)units * (size_t)(h.sc_stride ? h.sc_stride : 1));
   h.off_sel2 = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)(h.k2 > 0 ? h.k2 : 1));
+  h.sel2_stride = line_pad(h.k2 > 0 ? h.k2 : 1);
+  off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)h.sel2_stride);
   h.off_sel1 = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)(d.k > 0 ? d.k : 1));
+  off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)d.sel_stride);
   h.off_part = off;
-  off = align_up(off + sizeof(float) * (size_t)units * h.NP * d.g * (d.D + 2));
+  off = align_up(off + sizeof(float) * (size_t)units * h.NP * (size_t)part_stride(d.g, d.D));
   h.total = off;
   *o = h;
   return GSA_OK;

@@ -17,6 +17,32 @@ const char* last_error_message();
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
+// Phases of one fused decode launch (gist pass(es), then unfold).
+constexpr int kMaxPhases = 3;
+
+// Control words at the start of every decode workspace: per (phase, unit) a
+// finished-task count and a ready flag. They must be zero before the first
+// call; every call leaves them zero again.
+// Each unit owns one 256-byte block of control words (a finished-task count
+// per phase at word p, a ready flag per phase at word 8 + p), so waiting
+// workgroups of different units poll different lines and memory channels.
+constexpr size_t kCtrlUnitWords = 64;
+inline size_t ctrl_words(int64_t units) { return kCtrlUnitWords * (size_t)units; }
+// The control words live in a fixed 1 MiB area at offset 0 (room for 4096
+// units), so calls of different shapes can share one workspace: no shape's
+// data ever lands on another shape's control words.
+constexpr size_t kCtrlBytes = (size_t)1 << 20;
+inline size_t ctrl_bytes(int64_t units) {
+  const size_t need = (sizeof(uint32_t) * ctrl_words(units) + 255) / 256 * 256;
+  return need > kCtrlBytes ? need : kCtrlBytes;
+}
+
+// Per-unit strides of workspace regions that other workgroups read back are
+// whole 128-byte lines, so no two units (or partial slots) share a line.
+inline int64_t line_pad(int64_t n_words) { return (n_words + 31) / 32 * 32; }
+// floats per partial slot: g heads x (m, l, acc[D])
+inline int64_t part_stride(int32_t g, int32_t D) { return line_pad((int64_t)g * (D + 2)); }
+
 // Number of rows of the interleaved cache of one unit.
 inline int64_t cache_rows(int64_t n_raw, int64_t n_gist) { return n_raw + n_gist; }
 
@@ -37,9 +63,10 @@ struct DecodePlan {
   int32_t items_per_split;
   int32_t n_items;      // k*C + T
   int32_t NP;           // partial states per unit = S + S2
-  // byte offsets inside the workspace
-  size_t off_scores, off_sel, off_part, total;
+  // byte offsets inside the workspace (control words first)
+  size_t off_ctrl, off_scores, off_sel, off_part, total;
   int64_t score_stride; // floats per unit in the score region
+  int64_t sel_stride;   // ints per unit in the selection region
 };
 
 gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* out);
@@ -56,8 +83,8 @@ struct HierPlan {
   int32_t S_c;          // workgroups per unit over the level-1 candidates
   int32_t cand_per_split;
   int32_t NP;           // S_l2 + S_c + S2
-  size_t off_s2, off_sc, off_sel2, off_sel1, off_part, total;
-  int64_t s2_stride, sc_stride;
+  size_t off_ctrl, off_s2, off_sc, off_sel2, off_sel1, off_part, total;
+  int64_t s2_stride, sc_stride, sel2_stride;
 };
 
 gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* out);

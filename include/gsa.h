@@ -90,7 +90,12 @@ gsa_status_t gsa_decode_workspace_size(const gsa_decode_params* p, size_t* bytes
  * lse      [B, Hq]    fp32   natural-log sum-exp of the attended logits, or NULL
  * sel_idx  [B, Hkv, k] int32 selected chunk ids, ascending, or NULL
  * workspace / workspace_bytes: device scratch of at least
- *          gsa_decode_workspace_size() bytes (contents need no initialisation)
+ *          gsa_decode_workspace_size() bytes, 256-byte aligned. Its first
+ *          1 MiB holds task counters: the buffer must be zero-filled once
+ *          before its first use, and every call that runs to completion leaves
+ *          the counters zero again, so one buffer serves any number of later
+ *          calls of any shape that fits it (batch * n_kv_heads <= 4096; above
+ *          that, zero it again when the shape changes), one call at a time.
  */
 gsa_status_t gsa_decode(const gsa_decode_params* p, const void* q, const void* k_cache,
                         const void* v_cache, float* out, float* lse, int32_t* sel_idx,

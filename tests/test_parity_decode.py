@@ -228,3 +228,62 @@ def test_hier_full_size_sampled(gsa):
     assert torch.equal(s2.long(), inp.planted2) and torch.equal(s1.long(), inp.planted1)
     err = run_hier(gsa, inp, cfg, units=[(0, 0), (1, 3), (3, 7)])
     say(f"  sampled max err / rms = {err:.2e}")
+
+
+def test_workspace_reused_across_calls_and_shapes(gsa):
+    """One zeroed workspace serves many calls of different shapes and both entry
+    points: the control words must return to zero after every call."""
+    import decode_gsa_amd as g
+    ws = g.new_workspace(64 << 20)
+    cfgs = [small("gqa_32k", batch=2, n_raw=4096), small("c8_131k", batch=1, n_raw=4096),
+            small("gqa_32k", batch=1, n_q_heads=8, n_raw=1000, n_gist=62, tail=16)]
+    inps = [gi.make_decode(c, 2100 + i, device="cuda") for i, c in enumerate(cfgs)]
+    hcfg = gi.HierConfig(dataclasses.replace(gi.CONFIGS["hier_1m"].base, batch=1,
+                                             n_raw=16 * 16 * 32), 16, 8)
+    hinp = gi.make_hier(hcfg, 2200, device="cuda")
+    ref = [gsa.gsa_decode(x.q, x.k_cache, x.v_cache, chunk=c.chunk, topk=c.topk, tail=c.tail,
+                          n_gist=c.M) for c, x in zip(cfgs, inps)]
+    b = hcfg.base
+    href = gsa.gsa_decode_hier(hinp.q, hinp.k_cache, hinp.v_cache, hinp.k_l2, hinp.v_l2,
+                               chunk=b.chunk, fanout=16, topk1=b.topk, topk2=8, tail=b.tail)
+    for rep in range(3):
+        for c, x, r in zip(cfgs, inps, ref):
+            o = gsa.gsa_decode(x.q, x.k_cache, x.v_cache, chunk=c.chunk, topk=c.topk,
+                               tail=c.tail, n_gist=c.M, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(o[0], r[0]) and torch.equal(o[2], r[2])
+        o = gsa.gsa_decode_hier(hinp.q, hinp.k_cache, hinp.v_cache, hinp.k_l2, hinp.v_l2,
+                                chunk=b.chunk, fanout=16, topk1=b.topk, topk2=8, tail=b.tail,
+                                workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o[0], href[0]) and torch.equal(o[3], href[3])
+        assert ctrl_words_zero(ws, c.batch * c.n_kv_heads)
+    assert ctrl_words_zero(ws, b.batch * b.n_kv_heads)
+
+
+def ctrl_words_zero(ws, units):
+    # one 256-byte block of control words per (batch, kv-head) unit
+    return int(ws[:256 * units].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("batch,n_raw", [(2, 4096), (8, 4096), (1, 2048)])
+def test_decode_bit_identical_over_repeats(gsa, batch, n_raw):
+    """Many calls with fresh and with reused workspaces give bit-identical
+    results, and the first one matches the oracle (cross-workgroup hand-offs
+    inside the launch must never read stale data)."""
+    import decode_gsa_amd as g
+    cfg = small("gqa_32k", batch=batch, n_raw=n_raw)
+    inp = gi.make_decode(cfg, 2300 + batch, device="cuda")
+    run_decode(gsa, inp, cfg)
+    first = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=16, tail=64)
+    ws = g.new_workspace(g.decode_workspace_size(g.decode_params(
+        batch, 32, 8, 128, n_raw, n_raw // 16, 16, 16, 64)))
+    bad = 0
+    for rep in range(40):
+        o = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=16, tail=64,
+                           workspace=ws if rep % 2 else None)
+        torch.cuda.synchronize()
+        same = (torch.equal(o[0], first[0]) and torch.equal(o[1], first[1])
+                and torch.equal(o[2], first[2]))
+        bad += 0 if same else 1
+    assert bad == 0, f"{bad} of 40 repeats differ"
