@@ -493,6 +493,106 @@ __device__ void block_topk(const float* __restrict__ scores, int n, int k, const
   }
 }
 
+// Exact top-k inside one wave, without barriers or LDS. The wave holds up to
+// 64*EM items, item (e, lane) = e*64 + lane, in ascending id order; key is the
+// order-preserving image of the score (order_key), 0 for "no item". A bit-
+// serial radix search (one ballot per slot and bit) finds P, the k-th largest
+// key; every key above P is taken and the keys equal to P fill the remaining
+// places in item order, so ties go to the smaller id. Returns per slot the
+// ballot of taken items; fewer than k valid items are all taken.
+template <int EM>
+__device__ __forceinline__ void wave_topk(const uint32_t (&key)[EM], int E, int k, uint64_t (&take)[EM]) {
+  const int lane = threadIdx.x & 63;
+  uint32_t P = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = P | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < EM; ++e)
+      if (e < E) cnt += __popcll(__ballot(key[e] >= c));
+    if (cnt >= k) P = c;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int e = 0; e < EM; ++e)
+    if (e < E) gt += __popcll(__ballot(key[e] > P));
+  const int need = k - gt;
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int eq_before = 0;
+#pragma unroll
+  for (int e = 0; e < EM; ++e) {
+    take[e] = 0ull;
+    if (e < E) {
+      const uint64_t be = __ballot(key[e] == P && key[e] != 0u);
+      const bool eq = (be >> lane) & 1ull;
+      take[e] = __ballot(key[e] > P || (eq && eq_before + __popcll(be & lt) < need));
+      eq_before += __popcll(be);
+    }
+  }
+}
+
+constexpr int kSlots = 5;           // wave_topk slots: the running selection + 256 items
+constexpr int kFastSel = kFastSelect;
+static_assert(kFastSel <= 64, "the running selection must fit one slot");
+
+// Position of this lane's item (e) among the taken items, in item order.
+template <int EM>
+__device__ __forceinline__ int taken_before(const uint64_t (&take)[EM], int e) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int pos = __popcll(take[e] & lt);
+#pragma unroll
+  for (int f = 0; f < EM; ++f)
+    if (f < e) pos += __popcll(take[f]);
+  return pos;
+}
+
+// Make this wave's LDS writes visible to its own later reads in other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wave: top-k over n items (key, id) in ascending id order, fetched by
+// item(i, &key, &id) (key 0 = no item). Items are taken in blocks of
+// 64*(kSlots-1); slot 0 carries the selection so far, whose ids precede the
+// block's. xs is this wave's LDS scratch. Afterwards lane j < k holds the j-th
+// selected item (ascending id) in run_key / run_id.
+template <class Item>
+__device__ __forceinline__ void wave_select(int n, int k, Item item, uint32_t (*xs)[64],
+                                            uint32_t& run_key, uint32_t& run_id) {
+  const int lane = threadIdx.x & 63;
+  run_key = 0u;
+  run_id = 0u;
+  constexpr int kBlock = 64 * (kSlots - 1);
+  for (int c0 = 0; c0 < n; c0 += kBlock) {
+    uint32_t key[kSlots], id[kSlots];
+    key[0] = run_key;
+    id[0] = run_id;
+#pragma unroll
+    for (int e = 1; e < kSlots; ++e) item(c0 + (e - 1) * 64 + lane, key[e], id[e]);
+    const int rest = n - c0 < kBlock ? n - c0 : kBlock;
+    const int E = 1 + (rest + 63) / 64;
+    uint64_t take[kSlots];
+    wave_topk<kSlots>(key, E, k, take);
+    int total = 0;
+#pragma unroll
+    for (int e = 0; e < kSlots; ++e) {
+      if (e < E && ((take[e] >> lane) & 1ull)) {
+        const int pos = taken_before<kSlots>(take, e);
+        xs[0][pos] = key[e];
+        xs[1][pos] = id[e];
+      }
+      total += __popcll(take[e]);
+    }
+    wave_lds_sync();
+    run_key = lane < total ? xs[0][lane] : 0u;
+    run_id = lane < total ? xs[1][lane] : 0u;
+    wave_lds_sync();
+  }
+}
+
 // ------------------------------------------------------------- merge -------
 
 constexpr int kMergeBatch = 8;   // partials whose loads are in flight together
@@ -503,11 +603,11 @@ constexpr int kMergeBatch = 8;   // partials whose loads are in flight together
 // round trip per batch) and folded into a running (max, sum, acc) state.
 template <int D, int G>
 __device__ void merge_unit(const float* __restrict__ part_u, int NP, uint32_t ps,
-                           float* __restrict__ out, float* __restrict__ lse) {
+                           float* __restrict__ out, float* __restrict__ lse, int waves) {
   constexpr int PL = D / 64;                  // outputs per lane
   const CohBuf P(part_u, (uint32_t)NP * ps * 4u);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int h = w; h < G; h += kWaves) {
+  for (int h = w; h < G; h += waves) {
     float mx = kMinus, L = 0.f, acc[PL];
 #pragma unroll
     for (int e = 0; e < PL; ++e) acc[e] = 0.f;
@@ -592,8 +692,18 @@ __device__ __forceinline__ void init_state(State<BF16, G>& st) {
 
 // ------------------------------------------------------------ kernels ------
 
-// A pass over gist-like rows of every unit: scores + attention partials; the
-// unit's last workgroup selects the top-k of the pass's scores.
+// Cache row of tail item i (position N - T + i) of the interleaved cache.
+__device__ __forceinline__ int64_t tail_row(int64_t i, int64_t N, int32_t T, int64_t M, int32_t C) {
+  const int64_t pos = N - T + i, MC = M * C;
+  return pos < MC ? (pos / C) * (C + 1) + pos % C : M * (C + 1) + (pos - MC);
+}
+
+// A pass over gist-like rows of every unit: scores + attention partials, plus
+// a share of the tail rows (attended, not scored). Selection of the pass's
+// top-k: for k <= kFastSel each workgroup reduces its scores to its own top-k
+// candidates and the unit's last workgroup merges them; for larger k every
+// score goes out and the last workgroup runs a radix select. With out set the
+// last workgroup also merges the unit's partials (the pass is the last one).
 struct GistArgs {
   const void* q;
   const void* K;
@@ -603,28 +713,41 @@ struct GistArgs {
   int64_t per_task;       // items per workgroup
   int32_t tasks;          // workgroups per unit
   RowMap rm;
-  float* scores;          // [units][score_stride]
-  int64_t score_stride;
-  float* part;            // [units][NP][part_stride]
-  int64_t part_stride;
-  int32_t NP, part_base;
+  // tail rows, from the interleaved cache Kt/Vt
+  const void* Kt;
+  const void* Vt;
+  int64_t tail_unit_rows;
+  int64_t N, M;
+  int32_t C, T, tail_per_task;
+  // selection
   int32_t sel_k;
   IdMap im;
+  float* scores;          // [units][score_stride] (k > kFastSel)
+  int64_t score_stride;
+  uint32_t* cand;         // [units][cand_stride] words: tasks * k keys (k <= kFastSel)
+  int64_t cand_stride;
   int32_t* sel_ws;        // [units][sel_stride]
   int64_t sel_stride;
   int32_t* sel_out;       // [units][sel_k] or null
+  // partial softmax states
+  float* part;            // [units][NP][part_stride]
+  int64_t part_stride;
+  int32_t NP, part_base;
+  float* out;             // set: the last workgroup merges into out / lse
+  float* lse;
   uint32_t* cnt;          // unit u's counter at cnt[u * kCtrlUnitWords]
   float scale_log2;       // softmax logits in log2 units
   float score_mul;        // group score = sum_h(q_h . k) * score_mul
 };
 
 template <int D, int G>
-union GistLds {
-  struct {
-    float scores[kTaskScores];   // this workgroup's scores, written out as whole lines
-  } s;
-  PartLds<D, G> part;
-  TopkLds topk;
+struct GistLds {
+  float scores[kTaskScores];   // this workgroup's scores
+  uint32_t xs[2][64];          // wave 0's selection scratch
+  union {
+    PartLds<D, G> part;
+    TopkLds topk;
+  } u;
 };
 
 template <bool BF16, int D, int G>
@@ -632,6 +755,7 @@ __global__ __launch_bounds__(kThreads) void gist_kernel(GistArgs a) {
   using Gm = Geo<BF16, D>;
   __shared__ GistLds<D, G> lds;
   __shared__ uint32_t s_old;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int unit = blockIdx.x / a.tasks, split = blockIdx.x % a.tasks;
   uint4 qv[G];
   load_q<BF16, D, G>(a.q, unit, qv);
@@ -644,24 +768,92 @@ __global__ __launch_bounds__(kThreads) void gist_kernel(GistArgs a) {
   stream_rows<BF16, D, G, false>(reinterpret_cast<const char*>(a.K) + ub,
                                  reinterpret_cast<const char*>(a.V) + ub, i0, i1,
                                  [&](int64_t i) { return map_row(rm, unit, i); }, qv, st,
-                                 a.scale_log2, lds.s.scores, a.score_mul);
-  __syncthreads();
-  // scores out as contiguous device-scope stores (the unit's last workgroup reads them)
-  float* so = a.scores + (size_t)unit * a.score_stride + i0;
-  for (int64_t i = threadIdx.x; i < i1 - i0; i += kThreads) st_coh(so + i, lds.s.scores[i]);
-  __syncthreads();   // LDS changes role: scores -> partial merge
-  float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
-  write_partial<BF16, D, G>(st, part_u + (size_t)(a.part_base + split) * a.part_stride, lds.part, false);
-  if (arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)a.tasks, &s_old)) {
-    __syncthreads();   // LDS changes role: partial merge -> selection
-    block_topk(a.scores + (size_t)unit * a.score_stride, (int)a.n_items, a.sel_k, a.im, unit,
-               a.sel_ws + (size_t)unit * a.sel_stride,
-               a.sel_out ? a.sel_out + (size_t)unit * a.sel_k : nullptr, lds.topk);
+                                 a.scale_log2, lds.scores, a.score_mul);
+  // this workgroup's share of the tail
+  const int64_t t0 = (int64_t)split * a.tail_per_task;
+  const int64_t t1 = t0 + a.tail_per_task < a.T ? t0 + a.tail_per_task : a.T;
+  if (t0 < t1) {
+    const size_t tb = (size_t)unit * (size_t)a.tail_unit_rows * Gm::ROW_BYTES;
+    const int64_t N = a.N, M = a.M;
+    const int32_t C = a.C, T = a.T;
+    stream_rows<BF16, D, G, false>(reinterpret_cast<const char*>(a.Kt) + tb,
+                                   reinterpret_cast<const char*>(a.Vt) + tb, t0, t1,
+                                   [&](int64_t i) { return tail_row(i, N, T, M, C); }, qv, st,
+                                   a.scale_log2, nullptr, 0.f);
   }
+  const int nw = (int)(i1 > i0 ? i1 - i0 : 0);
+  float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
+  write_partial<BF16, D, G>(st, part_u + (size_t)(a.part_base + split) * a.part_stride, lds.u.part, false);
+  uint32_t* ctr = a.cnt + (size_t)unit * kCtrlUnitWords;
+
+  if (a.sel_k > kFastSel) {
+    // every score out (contiguous device-scope stores), radix select in the last workgroup
+    float* so = a.scores + (size_t)unit * a.score_stride + i0;
+    for (int i = tid; i < nw; i += kThreads) st_coh(so + i, lds.scores[i]);
+    if (arrive_last(ctr, (uint32_t)a.tasks, &s_old)) {
+      __syncthreads();   // LDS changes role: partial merge -> selection
+      block_topk(a.scores + (size_t)unit * a.score_stride, (int)a.n_items, a.sel_k, a.im, unit,
+                 a.sel_ws + (size_t)unit * a.sel_stride,
+                 a.sel_out ? a.sel_out + (size_t)unit * a.sel_k : nullptr, lds.u.topk);
+      if (a.out != nullptr)
+        merge_unit<D, G>(part_u, a.NP, (uint32_t)a.part_stride, a.out + (size_t)unit * G * D,
+                         a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
+    }
+    return;
+  }
+
+  // k <= kFastSel: wave 0 alone finishes the workgroup (the other waves leave
+  // once their partial stores have completed)
+  done_stores();
+  __syncthreads();   // scores in LDS; every wave's partial stores done
+  if (w != 0) return;
+  if (a.sel_k > 0) {
+    // this workgroup's top-k candidates (key, id), in id order; unused slots
+    // get key 0 (no item)
+    const IdMap im = a.im;
+    uint32_t rk, ri;
+    wave_select(nw, a.sel_k,
+                [&](int i, uint32_t& key, uint32_t& id) {
+                  key = i < nw ? order_key(lds.scores[i]) : 0u;
+                  id = i < nw ? (uint32_t)map_id(im, unit, (int32_t)(i0 + i)) : 0u;
+                },
+                lds.xs, rk, ri);
+    if (lane < a.sel_k) {
+      uint32_t* cb = a.cand + (size_t)unit * a.cand_stride + 2u * ((size_t)split * a.sel_k + lane);
+      st_coh(reinterpret_cast<int32_t*>(cb), (int32_t)rk);
+      st_coh(reinterpret_cast<int32_t*>(cb + 1), (int32_t)ri);
+    }
+  }
+  // count this workgroup finished (wave 0's stores complete first)
+  done_stores();
+  uint32_t old = 0u;
+  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
+  if (old != (uint32_t)a.tasks - 1u) return;
+  if (lane == 0) ctrl_set(ctr, 0u);
+  if (a.sel_k > 0) {
+    // merge the candidates of every workgroup of the unit (split order = id order)
+    const int n = a.tasks * a.sel_k;
+    const CohBuf cb(a.cand + (size_t)unit * a.cand_stride, (uint32_t)n * 8u);
+    uint32_t rk, ri;
+    wave_select(n, a.sel_k,
+                [&](int i, uint32_t& key, uint32_t& id) {   // past n the buffer returns 0
+                  key = cb.u32(2u * (uint32_t)i);
+                  id = cb.u32(2u * (uint32_t)i + 1u);
+                },
+                lds.xs, rk, ri);
+    if (lane < a.sel_k) {
+      st_coh(a.sel_ws + (size_t)unit * a.sel_stride + lane, (int32_t)ri);
+      if (a.sel_out) a.sel_out[(size_t)unit * a.sel_k + lane] = (int32_t)ri;
+    }
+  }
+  if (a.out != nullptr)
+    merge_unit<D, G>(part_u, a.NP, (uint32_t)a.part_stride, a.out + (size_t)unit * G * D,
+                     a.lse ? a.lse + (size_t)unit * G : nullptr, 1);
 }
 
-// Raw rows of the selected chunks (minus rows the tail owns) and the tail;
-// the unit's last workgroup merges every partial into out and lse.
+// Raw rows of the selected chunks (minus rows the tail owns); the unit's last
+// workgroup merges every partial into out and lse.
 struct UnfoldArgs {
   const void* q;
   const void* K;
@@ -672,9 +864,7 @@ struct UnfoldArgs {
   int32_t k;
   int32_t C, T;
   int64_t M, N;
-  int64_t tail_q;         // (N - T) / C
-  uint32_t tail_r;        // (N - T) % C
-  int64_t n_items, per_task;
+  int64_t n_items, per_task;   // n_items = k * C
   int32_t tasks;
   float* part;
   int64_t part_stride;
@@ -712,24 +902,17 @@ __global__ __launch_bounds__(kThreads) void unfold_kernel(UnfoldArgs a) {
   const size_t ub = (size_t)unit * (size_t)a.unit_rows * Gm::ROW_BYTES;
   const int64_t i0 = (int64_t)split * a.per_task;
   const int64_t i1 = i0 + a.per_task < a.n_items ? i0 + a.per_task : a.n_items;
-  // 32-bit index math: items < 2^30, positions split as tail0 = tail_q * C + tail_r
+  // 32-bit index math: items < 2^30
   const uint32_t C = (uint32_t)a.C;
-  const uint32_t kC = (uint32_t)a.k * C;
-  const int64_t M = a.M, tail0 = a.N - a.T, MC = a.M * a.C;
+  const int64_t M = a.M, tail0 = a.N - a.T;
   const int32_t* s_sel = lds.s.sel;
   auto row_of = [&](int64_t i64) -> int64_t {
     const uint32_t i = (uint32_t)i64;
-    if (i < kC) {
-      const uint32_t ci = i / C, j = i - ci * C;
-      const int64_t m = in_lds ? s_sel[ci] : us[ci];
-      if (m < 0 || m >= M) return -1;         // never taken for a valid selection
-      if (m * C + j >= tail0) return -1;      // the tail attends this row
-      return m * (C + 1) + j;
-    }
-    const uint32_t rel = a.tail_r + (i - kC);
-    const int64_t pos = tail0 + (i - kC);
-    const int64_t chunk = a.tail_q + rel / C;
-    return pos < MC ? chunk * (C + 1) + rel % C : M * (C + 1) + (pos - MC);
+    const uint32_t ci = i / C, j = i - ci * C;
+    const int64_t m = in_lds ? s_sel[ci] : us[ci];
+    if (m < 0 || m >= M) return -1;         // never taken for a valid selection
+    if (m * C + j >= tail0) return -1;      // the tail attends this row
+    return m * (C + 1) + j;
   };
   stream_rows<BF16, D, G, true>(reinterpret_cast<const char*>(a.K) + ub,
                                 reinterpret_cast<const char*>(a.V) + ub, i0, i1, row_of, qv, st,
@@ -739,7 +922,7 @@ __global__ __launch_bounds__(kThreads) void unfold_kernel(UnfoldArgs a) {
   write_partial<BF16, D, G>(st, part_u + (size_t)(a.part_base + split) * a.part_stride, lds.part, false);
   if (arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)a.tasks, &s_old))
     merge_unit<D, G>(part_u, a.NP, (uint32_t)a.part_stride, a.out + (size_t)unit * G * D,
-                     a.lse ? a.lse + (size_t)unit * G : nullptr);
+                     a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
 }
 
 // ------------------------------------------------------------------ host ---
@@ -758,32 +941,36 @@ inline uint32_t* ctrl_of(char* ws, size_t off_ctrl, int phase) {
 template <bool BF16, int D, int G>
 gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, const void* V,
                         float* out, float* lse, int32_t* sel_idx, char* ws, hipStream_t st) {
-  float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
-  int32_t* wsel = reinterpret_cast<int32_t*>(ws + pl.off_sel);
   float* part = reinterpret_cast<float*>(ws + pl.off_part);
+  int32_t* wsel = reinterpret_cast<int32_t*>(ws + pl.off_sel);
   const int64_t ps = part_stride(G, D);
   GistArgs g{};
   g.q = q; g.K = K; g.V = V;
   g.unit_rows = pl.R; g.n_items = pl.M; g.per_task = pl.gists_per_split; g.tasks = pl.S;
   g.rm = RowMap{0, pl.C, nullptr, 0, 0, 0, 0};
-  g.scores = scores; g.score_stride = pl.score_stride;
-  g.part = part; g.part_stride = ps; g.NP = pl.NP; g.part_base = 0;
+  g.Kt = K; g.Vt = V; g.tail_unit_rows = pl.R;
+  g.N = pl.N; g.M = pl.M; g.C = pl.C; g.T = pl.T; g.tail_per_task = pl.tail_per_split;
   g.sel_k = pl.k; g.im = IdMap{nullptr, 0, 0, 0, 0};
+  g.scores = reinterpret_cast<float*>(ws + pl.off_scores); g.score_stride = pl.score_stride;
+  g.cand = reinterpret_cast<uint32_t*>(ws + pl.off_cand); g.cand_stride = pl.cand_stride;
   g.sel_ws = wsel; g.sel_stride = pl.sel_stride; g.sel_out = sel_idx;
+  g.part = part; g.part_stride = ps; g.NP = pl.NP; g.part_base = 0;
+  g.out = pl.k > 0 ? nullptr : out; g.lse = pl.k > 0 ? nullptr : lse;
   g.cnt = ctrl_of(ws, pl.off_ctrl, 0);
   g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
   hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st, g);
-  UnfoldArgs u{};
-  u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
-  u.sel = wsel; u.sel_stride = pl.sel_stride; u.k = pl.k;
-  u.C = pl.C; u.T = pl.T; u.M = pl.M; u.N = pl.N;
-  u.tail_q = (pl.N - pl.T) / pl.C; u.tail_r = (uint32_t)((pl.N - pl.T) % pl.C);
-  u.n_items = pl.n_items; u.per_task = pl.items_per_split; u.tasks = pl.S2;
-  u.part = part; u.part_stride = ps; u.NP = pl.NP; u.part_base = pl.S;
-  u.out = out; u.lse = lse;
-  u.cnt = ctrl_of(ws, pl.off_ctrl, 2);
-  u.scale_log2 = pl.scale * kLog2e;
-  hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
+  if (pl.k > 0) {
+    UnfoldArgs u{};
+    u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
+    u.sel = wsel; u.sel_stride = pl.sel_stride; u.k = pl.k;
+    u.C = pl.C; u.T = pl.T; u.M = pl.M; u.N = pl.N;
+    u.n_items = pl.n_items; u.per_task = pl.items_per_split; u.tasks = pl.S2;
+    u.part = part; u.part_stride = ps; u.NP = pl.NP; u.part_base = pl.S;
+    u.out = out; u.lse = lse;
+    u.cnt = ctrl_of(ws, pl.off_ctrl, 2);
+    u.scale_log2 = pl.scale * kLog2e;
+    hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
+  }
   return launch_status("gsa_decode launch");
 }
 
@@ -792,22 +979,25 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
                       const void* K2, const void* V2, float* out, float* lse, int32_t* sel2,
                       int32_t* sel1, char* ws, hipStream_t st) {
   const DecodePlan& pl = hp.base;
-  float* s2 = reinterpret_cast<float*>(ws + hp.off_s2);
-  float* sc = reinterpret_cast<float*>(ws + hp.off_sc);
   int32_t* wsel2 = reinterpret_cast<int32_t*>(ws + hp.off_sel2);
   int32_t* wsel1 = reinterpret_cast<int32_t*>(ws + hp.off_sel1);
   float* part = reinterpret_cast<float*>(ws + hp.off_part);
   const int64_t ps = part_stride(G, D);
   const int64_t orphan0 = hp.M2 * hp.G;
-  // level 2: every meta-gist (dense rows of the level-2 array), top-k2 groups
+  // level 2: every meta-gist (dense rows of the level-2 array) and the tail,
+  // top-k2 groups
   GistArgs g{};
   g.q = q; g.K = K2; g.V = V2;
   g.unit_rows = hp.M2; g.n_items = hp.M2; g.per_task = hp.l2_per_split; g.tasks = hp.S_l2;
   g.rm = RowMap{1, pl.C, nullptr, 0, 0, 0, 0};
-  g.scores = s2; g.score_stride = hp.s2_stride;
-  g.part = part; g.part_stride = ps; g.NP = hp.NP; g.part_base = 0;
+  g.Kt = K; g.Vt = V; g.tail_unit_rows = pl.R;
+  g.N = pl.N; g.M = pl.M; g.C = pl.C; g.T = pl.T; g.tail_per_task = hp.tail_per_split;
   g.sel_k = hp.k2; g.im = IdMap{nullptr, 0, 0, 0, 0};
+  g.scores = reinterpret_cast<float*>(ws + hp.off_s2); g.score_stride = hp.s2_stride;
+  g.cand = reinterpret_cast<uint32_t*>(ws + hp.off_cand2); g.cand_stride = hp.cand2_stride;
   g.sel_ws = wsel2; g.sel_stride = hp.sel2_stride; g.sel_out = sel2;
+  g.part = part; g.part_stride = ps; g.NP = hp.NP; g.part_base = 0;
+  g.out = nullptr; g.lse = nullptr;
   g.cnt = ctrl_of(ws, hp.off_ctrl, 0);
   g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
   hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_l2), dim3(kThreads), 0, st, g);
@@ -816,26 +1006,31 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   c.K = K; c.V = V;
   c.unit_rows = pl.R; c.n_items = hp.n_cand; c.per_task = hp.cand_per_split; c.tasks = hp.S_c;
   c.rm = RowMap{2, pl.C, wsel2, hp.G, hp.k2, orphan0, hp.sel2_stride};
-  c.scores = sc; c.score_stride = hp.sc_stride;
-  c.part_base = hp.S_l2;
+  c.T = 0; c.tail_per_task = 0;
   c.sel_k = pl.k; c.im = IdMap{wsel2, hp.G, hp.k2, orphan0, hp.sel2_stride};
+  c.scores = reinterpret_cast<float*>(ws + hp.off_sc); c.score_stride = hp.sc_stride;
+  c.cand = reinterpret_cast<uint32_t*>(ws + hp.off_cand1); c.cand_stride = hp.cand1_stride;
   c.sel_ws = wsel1; c.sel_stride = pl.sel_stride; c.sel_out = sel1;
+  c.part_base = hp.S_l2;
+  c.out = pl.k > 0 ? nullptr : out; c.lse = pl.k > 0 ? nullptr : lse;
   c.cnt = ctrl_of(ws, hp.off_ctrl, 1);
   hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_c), dim3(kThreads), 0, st, c);
-  // unfold the chosen chunks + tail, merge everything
-  UnfoldArgs u{};
-  u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
-  u.sel = wsel1; u.sel_stride = pl.sel_stride; u.k = pl.k;
-  u.C = pl.C; u.T = pl.T; u.M = pl.M; u.N = pl.N;
-  u.tail_q = (pl.N - pl.T) / pl.C; u.tail_r = (uint32_t)((pl.N - pl.T) % pl.C);
-  u.n_items = pl.n_items; u.per_task = pl.items_per_split; u.tasks = pl.S2;
-  u.part = part; u.part_stride = ps; u.NP = hp.NP; u.part_base = hp.S_l2 + hp.S_c;
-  u.out = out; u.lse = lse;
-  u.cnt = ctrl_of(ws, hp.off_ctrl, 2);
-  u.scale_log2 = pl.scale * kLog2e;
-  hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
+  // unfold the chosen chunks, merge everything
+  if (pl.k > 0) {
+    UnfoldArgs u{};
+    u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
+    u.sel = wsel1; u.sel_stride = pl.sel_stride; u.k = pl.k;
+    u.C = pl.C; u.T = pl.T; u.M = pl.M; u.N = pl.N;
+    u.n_items = pl.n_items; u.per_task = pl.items_per_split; u.tasks = pl.S2;
+    u.part = part; u.part_stride = ps; u.NP = hp.NP; u.part_base = hp.S_l2 + hp.S_c;
+    u.out = out; u.lse = lse;
+    u.cnt = ctrl_of(ws, hp.off_ctrl, 2);
+    u.scale_log2 = pl.scale * kLog2e;
+    hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
+  }
   return launch_status("gsa_decode_hier launch");
 }
+
 // Dispatch on (dtype, head_dim, heads per kv-head).
 template <template <bool, int, int> class F, class... Args>
 gsa_status_t dispatch(int32_t dtype, int32_t D, int32_t G, Args&&... args) {

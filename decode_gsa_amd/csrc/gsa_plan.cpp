@@ -22,9 +22,12 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int64_t kTargetWGs = 2048;
 constexpr int64_t kMinRows = 64;
 
-// Unfold workgroups get at least this many rows (their start-up costs more
-// relative to the rows they stream).
-constexpr int64_t kMinUnfoldRows = 128;
+// Unfold workgroups get at least this many rows: few rows each keep the
+// latency of the pass short (it starts only after the selection).
+#ifndef GSA_MIN_UNFOLD_ROWS
+#define GSA_MIN_UNFOLD_ROWS 64
+#endif
+constexpr int64_t kMinUnfoldRows = GSA_MIN_UNFOLD_ROWS;
 // A gist workgroup gathers its scores in LDS: at most this many items each.
 constexpr int64_t kMaxTaskItems = 1024;
 
@@ -110,7 +113,7 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
                 (long long)p->n_raw);
   int64_t units = (int64_t)p->batch * p->n_kv_heads;
   if (units > (1 << 24)) return fail(GSA_ERR_UNSUPPORTED, "too many (batch, kv-head) units");
-  int64_t items = (int64_t)p->topk * p->chunk + p->tail;
+  int64_t items = (int64_t)p->topk * p->chunk;
   if (items > (1 << 30) || p->n_gist > (1 << 30))
     return fail(GSA_ERR_UNSUPPORTED, "selection too large");
 
@@ -130,17 +133,22 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   if (ceil_div(d.M, d.S) > kMaxTaskItems) d.S = (int32_t)ceil_div(d.M, kMaxTaskItems);
   d.gists_per_split = d.M > 0 ? ceil_div(d.M, d.S) : 0;
   d.S = d.M > 0 ? (int32_t)ceil_div(d.M, d.gists_per_split) : 1;
+  d.tail_per_split = (int32_t)ceil_div(d.T, d.S);
   d.n_items = (int32_t)items;
   d.S2 = splits_for(items, units, kMinUnfoldRows);
   d.items_per_split = items > 0 ? (int32_t)ceil_div(items, d.S2) : 0;
-  d.S2 = items > 0 ? (int32_t)ceil_div(items, d.items_per_split) : 1;
+  d.S2 = items > 0 ? (int32_t)ceil_div(items, d.items_per_split) : 0;
   d.NP = d.S + d.S2;
-  d.score_stride = (d.M + 63) / 64 * 64;
+  const bool fast = d.k <= kFastSelect;
+  d.score_stride = fast ? 0 : (d.M + 63) / 64 * 64;
+  d.cand_stride = fast ? line_pad(2 * (int64_t)d.S * d.k) : 0;
   size_t off = 0;
   d.off_ctrl = off;
   off = align_up(off + ctrl_bytes(units));
   d.off_scores = off;
   off = align_up(off + sizeof(float) * (size_t)units * (size_t)d.score_stride);
+  d.off_cand = off;
+  off = align_up(off + sizeof(uint32_t) * (size_t)units * (size_t)d.cand_stride);
   d.off_sel = off;
   d.sel_stride = line_pad(d.k > 0 ? d.k : 1);
   off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)d.sel_stride);
@@ -179,16 +187,24 @@ gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
   if (ceil_div(h.n_cand, h.S_c) > kMaxTaskItems) h.S_c = (int32_t)ceil_div(h.n_cand, kMaxTaskItems);
   h.cand_per_split = h.n_cand > 0 ? (int32_t)ceil_div(h.n_cand, h.S_c) : 0;
   h.S_c = h.n_cand > 0 ? (int32_t)ceil_div(h.n_cand, h.cand_per_split) : 1;
+  h.tail_per_split = (int32_t)ceil_div(d.T, h.S_l2);
   h.NP = h.S_l2 + h.S_c + d.S2;
-  h.s2_stride = (h.M2 + 63) / 64 * 64;
-  h.sc_stride = (h.n_cand + 63) / 64 * 64;
+  const bool fast2 = h.k2 <= kFastSelect, fast1 = d.k <= kFastSelect;
+  h.s2_stride = fast2 ? 0 : (h.M2 + 63) / 64 * 64;
+  h.sc_stride = fast1 ? 0 : (h.n_cand + 63) / 64 * 64;
+  h.cand2_stride = fast2 ? line_pad(2 * (int64_t)h.S_l2 * h.k2) : 0;
+  h.cand1_stride = fast1 ? line_pad(2 * (int64_t)h.S_c * d.k) : 0;
   size_t off = 0;
   h.off_ctrl = off;
   off = align_up(off + ctrl_bytes(units));
   h.off_s2 = off;
-  off = align_up(off + sizeof(float) * (size_t)units * (size_t)(h.s2_stride ? h.s2_stride : 1));
+  off = align_up(off + sizeof(float) * (size_t)units * (size_t)h.s2_stride);
   h.off_sc = off;
-  off = align_up(off + sizeof(float) * (size_t)units * (size_t)(h.sc_stride ? h.sc_stride : 1));
+  off = align_up(off + sizeof(float) * (size_t)units * (size_t)h.sc_stride);
+  h.off_cand2 = off;
+  off = align_up(off + sizeof(uint32_t) * (size_t)units * (size_t)h.cand2_stride);
+  h.off_cand1 = off;
+  off = align_up(off + sizeof(uint32_t) * (size_t)units * (size_t)h.cand1_stride);
   h.off_sel2 = off;
   h.sel2_stride = line_pad(h.k2 > 0 ? h.k2 : 1);
   off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)h.sel2_stride);

@@ -15,6 +15,10 @@ void clear_error();
 const char* last_error_message();
 
 constexpr size_t kAlign = 256;
+
+// Selections of at most this many items use per-workgroup candidate lists
+// (64-bit keys); larger ones keep every score for a radix select.
+constexpr int32_t kFastSelect = 64;
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
 // Phases of one fused decode launch (gist pass(es), then unfold).
@@ -58,14 +62,17 @@ struct DecodePlan {
   // gist pass: S workgroups per unit, each over a contiguous gist range
   int32_t S;
   int64_t gists_per_split;
-  // unfold pass: S2 workgroups per unit over the k*C + T unfold items
+  int32_t tail_per_split;   // tail rows per gist workgroup (the gist pass attends the tail)
+  // unfold pass (k > 0 only): S2 workgroups per unit over the k*C raw rows of
+  // the selected chunks
   int32_t S2;
   int32_t items_per_split;
-  int32_t n_items;      // k*C + T
-  int32_t NP;           // partial states per unit = S + S2
+  int32_t n_items;      // k*C
+  int32_t NP;           // partial states per unit = S (+ S2 when k > 0)
   // byte offsets inside the workspace (control words first)
-  size_t off_ctrl, off_scores, off_sel, off_part, total;
-  int64_t score_stride; // floats per unit in the score region
+  size_t off_ctrl, off_scores, off_cand, off_sel, off_part, total;
+  int64_t score_stride; // floats per unit in the score region (k > kFastSelect)
+  int64_t cand_stride;  // words per unit in the candidate region (k <= kFastSelect)
   int64_t sel_stride;   // ints per unit in the selection region
 };
 
@@ -82,9 +89,10 @@ struct HierPlan {
   int64_t l2_per_split;
   int32_t S_c;          // workgroups per unit over the level-1 candidates
   int32_t cand_per_split;
-  int32_t NP;           // S_l2 + S_c + S2
-  size_t off_ctrl, off_s2, off_sc, off_sel2, off_sel1, off_part, total;
-  int64_t s2_stride, sc_stride, sel2_stride;
+  int32_t tail_per_split;   // tail rows per level-2 workgroup
+  int32_t NP;           // S_l2 + S_c (+ S2 when k1 > 0)
+  size_t off_ctrl, off_s2, off_sc, off_cand2, off_cand1, off_sel2, off_sel1, off_part, total;
+  int64_t s2_stride, sc_stride, cand2_stride, cand1_stride, sel2_stride;
 };
 
 gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* out);
