@@ -221,21 +221,28 @@ gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* o) {
   if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
   gsa_status_t s = check_heads(p->n_q_heads, p->n_kv_heads, p->head_dim, p->dtype);
   if (s != GSA_OK) return s;
-  if (p->head_dim != 128) return fail(GSA_ERR_UNSUPPORTED, "prefill needs head_dim=128");
-  if (p->dtype != GSA_BF16) return fail(GSA_ERR_UNSUPPORTED, "prefill needs bf16 inputs");
   if ((s = check_geometry(p->n_raw, p->n_gist, p->chunk)) != GSA_OK) return s;
   if (isnan(p->scale)) return fail(GSA_ERR_INVALID_ARG, "scale is NaN");
-  if (p->topk < 0 || p->topk > 256) return fail(GSA_ERR_INVALID_ARG, "topk=%d outside [0, 256]", p->topk);
-  if (p->window < 1 || p->window > (1 << 20))
-    return fail(GSA_ERR_INVALID_ARG, "window=%d outside [1, 2^20]", p->window);
+  if (p->topk < 0) return fail(GSA_ERR_INVALID_ARG, "topk=%d is negative", p->topk);
+  if (p->window < 1) return fail(GSA_ERR_INVALID_ARG, "window=%d must be >= 1", p->window);
   if (p->q_start < 0 || p->n_q < 0 || p->q_start + p->n_q > p->n_raw)
     return fail(GSA_ERR_INVALID_ARG, "query range [%lld, %lld) outside [0, n_raw=%lld)",
                 (long long)p->q_start, (long long)(p->q_start + p->n_q), (long long)p->n_raw);
-  if (p->n_q > ((int64_t)1 << 24)) return fail(GSA_ERR_UNSUPPORTED, "too many queries");
+  if (p->head_dim != 128) return fail(GSA_ERR_UNSUPPORTED, "prefill needs head_dim=128");
+  if (p->dtype != GSA_BF16) return fail(GSA_ERR_UNSUPPORTED, "prefill needs bf16 inputs");
+  const int32_t g = p->n_q_heads / p->n_kv_heads;
+  if (g != 1 && g != 2 && g != 4)
+    return fail(GSA_ERR_UNSUPPORTED, "prefill: %d query heads per kv-head not in {1, 2, 4}", g);
+  if (p->topk > kPrefillMaxK)
+    return fail(GSA_ERR_UNSUPPORTED, "prefill: topk=%d above %d", p->topk, kPrefillMaxK);
+  if (p->n_gist > kPrefillMaxGist)
+    return fail(GSA_ERR_UNSUPPORTED, "prefill: n_gist=%lld above %d", (long long)p->n_gist, kPrefillMaxGist);
+  if (p->n_raw + p->n_gist >= ((int64_t)1 << 31) || p->window > (1 << 30))
+    return fail(GSA_ERR_UNSUPPORTED, "prefill: sequence too long for 32-bit positions");
   PrefillPlan d{};
   d.Hq = p->n_q_heads;
   d.Hkv = p->n_kv_heads;
-  d.g = d.Hq / d.Hkv;
+  d.g = g;
   d.D = p->head_dim;
   d.C = p->chunk;
   d.k = p->topk;
@@ -247,7 +254,9 @@ gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* o) {
   d.n_q = p->n_q;
   d.scale = resolve_scale(p->scale, p->head_dim);
   d.n_blocks = (int32_t)ceil_div(d.n_q, kQBlock);
-  d.total = 0;
+  if ((int64_t)d.n_blocks * d.Hkv > (1 << 30)) return fail(GSA_ERR_UNSUPPORTED, "prefill: too many blocks");
+  // workspace: the selection [Hkv][n_q][k] handed from the select to the attend kernel
+  d.total = align_up(sizeof(int32_t) * (size_t)d.Hkv * (size_t)d.n_q * (size_t)d.k);
   *o = d;
   return GSA_OK;
 }

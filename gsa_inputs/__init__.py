@@ -93,6 +93,7 @@ class PrefillConfig:
     alpha: float = 8.0    # weight of the per-block shared query direction
     margin: float = 0.5
     n_gist: Optional[int] = None
+    values: str = "gauss"  # "int": q/K/V entries uniform in {-2..2} (exact scores, many ties)
 
     @property
     def M(self) -> int:
@@ -388,6 +389,15 @@ def _prefill_once(cfg: PrefillConfig, seed: int, device, check: bool) -> Prefill
     gen = _gen(device, seed)
     dt = _TORCH_DT[cfg.dtype]
     scale = _scale(D)
+    if cfg.values == "int":
+        # small integers: every dot product is exact in fp32 and fp64, so equal
+        # group scores are equal on both sides and ties are decided by index
+        def ints(*shape):
+            return torch.randint(-2, 3, shape, generator=gen, device=device).to(torch.float32)
+        q = _store(ints(Hq, nq, D), cfg.dtype)
+        k_cache = _store(ints(Hkv, R, D), cfg.dtype)
+        v_cache = _store(ints(Hkv, R, D), cfg.dtype)
+        return PrefillInputs(cfg, q, k_cache, v_cache, None, seed, math.inf)
     # chunks complete before the first query and clear of every window
     n_far = max(0, min(M, (q0 - W) // C))
     do_plant = k > 0 and nblk * k <= n_far

@@ -94,9 +94,15 @@ def topk_ascending(scores: Sequence[float], ids: Sequence[int], k: int) -> List[
 
 
 def _group_scores(qg: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
-    """S = mean over the group's heads of scale * (q_h . key)  (R1, R2)."""
-    per_head = scale * (keys @ qg.T)          # [n, g]
-    return per_head.mean(axis=1)
+    """S = mean over the group's heads of scale * (q_h . key)  (R1, R2).
+
+    Written as (scale / g) * sum_h (q_h . key): the same value, with one
+    rounding after the head sum, so that equal dot-product sums (exact for
+    small-integer inputs) give exactly equal scores and the tie rule decides.
+    """
+    g = qg.shape[0]
+    dots = keys @ qg.T                        # [n, g]
+    return (scale / g) * dots.sum(axis=1)
 
 
 # ------------------------------------------------------------- attention ---

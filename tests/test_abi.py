@@ -170,10 +170,23 @@ def good_prefill(**kw):
     ({"n_q": 1025}, INVALID),                   # runs past n_raw
     ({"n_gist": 257}, INVALID),
     ({"n_q_heads": 12, "n_kv_heads": 4}, UNSUPPORTED),
+    ({"n_q_heads": 16, "n_kv_heads": 2}, UNSUPPORTED),   # g = 8: no prefill kernel
+    ({"topk": 32}, OK),
+    ({"topk": 33}, UNSUPPORTED),                  # above the per-block union bound
+    ({"n_raw": 16 * 65537, "n_gist": 65537, "q_start": 0, "n_q": 64}, UNSUPPORTED),
+    ({"n_q": 0}, OK),
 ])
 def test_prefill_param_validation(L, kw, status):
     n = ctypes.c_size_t(0)
     assert L.gsa_prefill_workspace_size(ctypes.byref(good_prefill(**kw)), ctypes.byref(n)) == status
+
+
+def test_prefill_workspace_holds_the_selection(L):
+    n = ctypes.c_size_t(0)
+    assert L.gsa_prefill_workspace_size(ctypes.byref(good_prefill()), ctypes.byref(n)) == OK
+    assert n.value >= 2 * 1024 * 4 * 4                # [Hkv, n_q, k] int32
+    assert L.gsa_prefill_workspace_size(ctypes.byref(good_prefill(topk=0)), ctypes.byref(n)) == OK
+    assert n.value == 0
 
 
 def test_status_strings(L):

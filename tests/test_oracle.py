@@ -134,6 +134,31 @@ def test_topk_ties_prefer_smaller_index_and_negative_zero():
     assert list(r["sel"]) == [0, 1, 2, 3]
 
 
+def test_equal_head_sums_tie_and_go_to_the_smaller_index():
+    """Group score = mean of the heads' scaled logits: two gists whose per-head
+    dot products differ but sum to the same value score exactly the same, so
+    the smaller chunk id wins; a gist with a larger sum wins outright."""
+    # D = 12: scale = 1/sqrt(12) is irrational, and summing the two heads'
+    # separately rounded scaled logits would split this tie by one ulp
+    C, D, M, g = 2, 12, 5, 2
+    N = M * C
+    R = N + M
+    qg = np.zeros((g, D))
+    qg[0, 0] = 1.0
+    qg[1, 1] = 1.0
+    K = np.zeros((R, D))
+    gist = [m * (C + 1) + C for m in range(M)]
+    K[gist[1], :2] = [5.0, 4.0]           # head dots (5, 4), sum 9
+    K[gist[3], :2] = [6.0, 3.0]           # head dots (6, 3), sum 9: tie with chunk 1
+    K[gist[4], :2] = [4.0, 4.0]           # sum 8
+    V = np.random.default_rng(3).standard_normal((R, D))
+    r1 = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=1, tail=0)
+    assert list(r1["sel"]) == [1]
+    assert r1["scores"][1] == r1["scores"][3]
+    r2 = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=3, tail=0)
+    assert list(r2["sel"]) == [1, 3, 4]
+
+
 # --------------------------------------------------- library reductions ---
 
 @pytest.mark.parametrize("C,M,r", [(4, 12, 0), (8, 5, 3), (16, 6, 16), (3, 7, 1)])
