@@ -1,11 +1,15 @@
 #!/usr/bin/env python3
-"""Benchmark of the GSA decode / prefill hot path on one MI355X.
+"""Benchmark of the GSA hot path on one MI355X.
 
-Default workload: the batched GQA decode step (batch 32, 32 query heads over 8
-kv-heads, head_dim 128, bf16 cache, 32768-token context, chunk 16, top-16
-chunks, 64-token tail). One step = one gsa_decode call over the whole batch,
-i.e. every stage of the path: gist scoring + attention over all gists, exact
-top-k, unfold gather + attention over the chosen chunks and the tail, merge.
+Default workload (gqa_32k): the batched GQA decode step -- batch 32, 32 query
+heads over 8 kv-heads, head_dim 128, bf16 interleaved cache, 32768-token
+context, chunk 16, top-16 chunks, 64-token tail. One step = one gsa_decode
+call over the whole batch, i.e. every stage of the path: gist scoring +
+attention over all gists and the tail (gist pass), exact top-k, unfold of the
+chosen chunks + merge (unfold pass).
+
+`--config prefill_64k` times the causal block-sparse prefill instead (4096
+query positions at the end of a 65536-token sequence, 32/8 heads, k=16, W=64).
 
 Cold-cache protocol without flushes: the benchmark keeps several copies
 ("layers") of the KV cache and step i reads layer i mod L, so a step's data was
@@ -13,12 +17,17 @@ last touched L-1 steps (>= 0.9 GB of other traffic) earlier and is no longer in
 the 256 MB Infinity Cache -- as in a real model, where each layer has its own
 cache. Inputs are resident in HBM before timing starts.
 
-Prints one JSON line (see the fields below). `--config` picks another
-workload (parity configs listed in gsa_inputs.CONFIGS).
+Per-kernel times come from HIP events that the library records on the launch
+stream between its kernels (gsa_profile_events), so the roofline of the
+dominant kernel is measured live in the timed region.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import math
 import os
@@ -30,39 +39,119 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "GSA decode query-heads/s + achieved HBM GB/s (32K ctx, C=16, k=16, bf16)"
+DECODE_METRIC = "GSA decode query-heads/s + achieved HBM GB/s (32K ctx, C=16, k=16, bf16)"
+PREFILL_METRIC = "GSA block-sparse prefill query-positions/s + MFMA utilisation (64K ctx, 4096 queries)"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def decode_algorithmic_bytes(cfg, sel) -> int:
-    """Bytes the method must touch once per step: every gist row (K+V), the raw
-    rows of the selected chunks not already in the tail, the tail rows, q, the
-    fp32 output, lse and the selected indices."""
+# ------------------------------------------------------------ HIP events ---
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library's timing hook records them)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def ms(self, a: int, b: int) -> float:
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(self.ev[a]),
+                                        ctypes.c_void_p(self.ev[b])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for h in self.ev:
+            self.hip.hipEventDestroy(ctypes.c_void_p(h))
+
+
+def timed_steps(gsa, step, args, n_marks):
+    """Warm up, then time exactly args.steps steps; the library records
+    n_marks events per step. Returns (wall ms per step, [steps, n_marks-1] ms)."""
+    import torch
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = HipEvents(args.steps * n_marks)
+    try:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            gsa.gsa_profile_events(ev.ev[i * n_marks:(i + 1) * n_marks])
+            step(args.warmup + i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gsa.gsa_profile_events([])
+        per = np.array([[ev.ms(i * n_marks + j, i * n_marks + j + 1) for j in range(n_marks - 1)]
+                        for i in range(args.steps)])
+    finally:
+        gsa.gsa_profile_events([])
+        ev.close()
+    return 1e3 * wall / args.steps, per
+
+
+def source_sha(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "decode_gsa_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key: str, sha: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(key)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("source_sha") != sha:
+        return None
+    return t.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- decode ---
+
+def decode_bytes(cfg, sel):
+    """Algorithmic bytes per call: (gist pass, unfold pass). Gist pass: every
+    gist row and every tail row (K + V), q. Unfold pass: the raw rows of the
+    selected chunks not in the tail (K + V), the fp32 output, lse and the
+    selected ids."""
     eb = 2 if cfg.dtype == "bf16" else 4
-    row = 2 * cfg.head_dim * eb                      # K + V
+    row = 2 * cfg.head_dim * eb
     units = cfg.batch * cfg.n_kv_heads
     tail0 = cfg.n_raw - cfg.tail
-    sel = np.asarray(sel).reshape(units, -1) if cfg.topk else np.zeros((units, 0), np.int64)
     raw_sel = 0
-    C = cfg.chunk
-    for u in range(units):
-        for m in sel[u]:
-            raw_sel += max(0, min(C, tail0 - int(m) * C))
-    rows = units * cfg.M + raw_sel + units * cfg.tail
+    if cfg.topk:
+        sel = np.asarray(sel).reshape(units, -1)
+        for u in range(units):
+            for m in sel[u]:
+                raw_sel += max(0, min(cfg.chunk, tail0 - int(m) * cfg.chunk))
     q = cfg.batch * cfg.n_q_heads * cfg.head_dim * eb
-    out = cfg.batch * cfg.n_q_heads * cfg.head_dim * 4
-    lse = cfg.batch * cfg.n_q_heads * 4
-    idx = units * cfg.topk * 4
-    return rows * row + q + out + lse + idx
+    gist = units * (cfg.M + cfg.tail) * row + q
+    out = cfg.batch * cfg.n_q_heads * (cfg.head_dim + 1) * 4 + units * cfg.topk * 4
+    unfold = raw_sel * row + out
+    return gist, unfold
 
 
 def cpu_baseline_decode(inp, cfg, budget_s: float):
-    """Time the fp64 oracle (as it stands) on whole decode steps, single thread."""
+    """The fp64 oracle (as it stands) on whole decode units, one thread."""
     import oracle
     from threadpoolctl import threadpool_limits
     g = cfg.n_q_heads // cfg.n_kv_heads
@@ -97,9 +186,8 @@ def run_decode_bench(args):
     log(f"[bench] generating {cfg.name} inputs ...")
     inp = gi.make_decode(cfg, 1000 + 2, device=dev)
     stream = torch.cuda.current_stream(dev)
-    # cache copies for the cold-cache rotation
     step_bytes_cache = cfg.batch * cfg.n_kv_heads * cfg.R * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4) * 2
-    layers = args.layers or max(1, min(8, math.ceil(1.0e9 / max(1.0, 0.3e9)) + 1))
+    layers = args.layers or 5
     free = torch.cuda.mem_get_info(dev)[0]
     layers = max(1, min(layers, int(0.8 * free // step_bytes_cache)))
     ks = [inp.k_cache] + [inp.k_cache.clone() for _ in range(layers - 1)]
@@ -117,36 +205,28 @@ def run_decode_bench(args):
         gsa.gsa_decode(inp.q, ks[l], vs[l], chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail,
                        n_gist=cfg.M, out=out, lse=lse, sel_idx=sel, workspace=ws, stream=stream)
 
-    # parity spot check of this exact launch configuration (selection must be the planted set)
+    # parity spot check of this exact launch configuration (selection = planted set)
     step(0)
     torch.cuda.synchronize()
     if cfg.topk > 0 and inp.planted is not None:
         assert torch.equal(sel.long(), inp.planted), "selection differs from the planted top-k"
-    alg_bytes = decode_algorithmic_bytes(cfg, sel.cpu().numpy() if cfg.topk else [])
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        evs[i][0].record(stream)
-        step(args.warmup + i)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    ms_per_step = 1e3 * wall / args.steps
+    gist_b, unfold_b = decode_bytes(cfg, sel.cpu().numpy() if cfg.topk else [])
+    n_marks = 3 if cfg.topk > 0 else 2
+    ms_per_step, per = timed_steps(gsa, step, args, n_marks)
+    gist_ms = float(per[:, 0].mean())
+    call_ms = float(per.sum(axis=1).mean())
     qheads = B * Hq
-    value = qheads / (ms_per_step / 1e3)
-    call_ms = float(np.mean(ev_ms))
-    achieved = alg_bytes / (call_ms / 1e3) / 1e9
-
+    achieved = gist_b / (gist_ms / 1e3) / 1e9
+    sha = source_sha("gsa_decode.hip", "gsa_device.hpp")
+    kernels = {"gist_kernel": {"ms": gist_ms, "alg_bytes": gist_b,
+                               "GB_s": gist_b / (gist_ms / 1e3) / 1e9}}
+    if cfg.topk > 0:
+        unfold_ms = float(per[:, 1].mean())
+        kernels["unfold_kernel"] = {"ms": unfold_ms, "alg_bytes": unfold_b,
+                                    "GB_s": unfold_b / (unfold_ms / 1e3) / 1e9}
     res = {
-        "metric": METRIC,
-        "value": value,
+        "metric": DECODE_METRIC,
+        "value": qheads / (ms_per_step / 1e3),
         "unit": "query-heads/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -156,7 +236,7 @@ def run_decode_bench(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
-        "data": "synthetic (seeded Gaussian q/K/V, planted top-k margin >= 0.5)",
+        "data": "synthetic (seeded Gaussian q/K/V, planted top-k with margin >= 0.5)",
         "config": {"workload": f"{cfg.name}: GQA decode step, B={cfg.batch}, Hq={cfg.n_q_heads}, "
                                f"Hkv={cfg.n_kv_heads}, D={cfg.head_dim}, N={cfg.n_raw}, "
                                f"C={cfg.chunk}, k={cfg.topk}, T={cfg.tail}, {cfg.dtype} cache",
@@ -164,17 +244,144 @@ def run_decode_bench(args):
                    "cache_layers_rotated": layers},
         "tokens_per_s": cfg.batch / (ms_per_step / 1e3),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "scope": "whole gsa_decode call (all its kernels) per step, HIP events on "
-                              "the launch stream",
-                     "algorithmic_bytes_per_call": alg_bytes,
-                     "call_ms_mean": call_ms, "call_ms_p10": float(np.percentile(ev_ms, 10)),
-                     "call_ms_p90": float(np.percentile(ev_ms, 90))},
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(f"gist_kernel/{cfg.name}", sha),
+                     "kernel": "gist_kernel", "alg_bytes_per_launch": gist_b,
+                     "launch_ms_mean": gist_ms},
+        "call": {"ms_mean": call_ms, "alg_bytes": gist_b + unfold_b,
+                 "GB_s": (gist_b + unfold_b) / (call_ms / 1e3) / 1e9},
+        "kernels": kernels,
+        "source_sha": sha,
     }
     if not args.no_cpu:
         log("[bench] timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline_decode(inp, cfg, args.cpu_seconds)
     return res
+
+
+# --------------------------------------------------------------- prefill ---
+
+def prefill_flops(cfg):
+    """Algorithmic FLOPs: 2 * D for q.k and 2 * D for p.v over every attended
+    (query head, row) pair. Per query t: the eligible gists, the k*C rows of
+    its chunks outside its window (planted chunks lie outside every window)
+    and the window rows."""
+    t = cfg.q_start + np.arange(cfg.n_q)
+    elig = np.minimum(cfg.M, t // cfg.chunk)
+    win = np.minimum(cfg.window, t + 1)
+    rows = elig + np.minimum(elig, cfg.topk) * cfg.chunk + win
+    g = cfg.n_q_heads
+    total = float(rows.sum()) * g * cfg.head_dim * 4
+    gist_qk = float(elig.sum()) * g * cfg.head_dim * 2      # the selection pass' group scores
+    return total, gist_qk
+
+
+def cpu_baseline_prefill(inp, cfg, budget_s: float):
+    import oracle
+    from threadpoolctl import threadpool_limits
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    q = inp.q.float().cpu().numpy()
+    K = [inp.k_cache[j].float().cpu().numpy() for j in range(cfg.n_kv_heads)]
+    V = [inp.v_cache[j].float().cpu().numpy() for j in range(cfg.n_kv_heads)]
+    rng = np.random.default_rng(5)
+    t_total, n = 0.0, 0
+    with threadpool_limits(1):
+        while t_total < budget_s and n < 100000:
+            i, j = int(rng.integers(cfg.n_q)), int(rng.integers(cfg.n_kv_heads))
+            t0 = time.perf_counter()
+            oracle.prefill_query(q[j * g:(j + 1) * g, i], K[j], V[j], t=cfg.q_start + i,
+                                 n_raw=cfg.n_raw, n_gist=cfg.M, chunk=cfg.chunk, topk=cfg.topk,
+                                 window=cfg.window)
+            t_total += time.perf_counter() - t0
+            n += 1
+    # one query position = all kv-heads
+    return {"value": n / cfg.n_kv_heads / t_total, "unit": "query-positions/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} random (query, kv-head) pairs of the same workload, fp64 numpy, "
+                      f"1 thread, {t_total:.1f} s"}
+
+
+def run_prefill_bench(args):
+    import torch
+    import decode_gsa_amd as gsa
+    import gsa_inputs as gi
+
+    cfg = gi.CONFIGS[args.config]
+    dev = torch.device("cuda", 0)
+    log(f"[bench] generating {cfg.name} inputs ...")
+    inp = gi.make_prefill(cfg, 2000 + 5, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = torch.empty(cfg.n_q_heads, cfg.n_q, cfg.head_dim, dtype=torch.float32, device=dev)
+    sel = torch.empty(cfg.n_kv_heads, cfg.n_q, max(cfg.topk, 1), dtype=torch.int32, device=dev)
+    p = gsa.prefill_params(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.chunk, cfg.topk,
+                           cfg.window, cfg.n_raw, cfg.M, cfg.q_start, cfg.n_q)
+    ws = gsa.new_workspace(gsa.prefill_workspace_size(p), dev)
+
+    def step(i):
+        gsa.gsa_prefill_blocksparse(inp.q, inp.k_cache, inp.v_cache, chunk=cfg.chunk,
+                                    topk=cfg.topk, window=cfg.window, q_start=cfg.q_start,
+                                    n_gist=cfg.M, out=out, sel=sel, workspace=ws, stream=stream)
+
+    step(0)
+    torch.cuda.synchronize()
+    if cfg.topk > 0 and inp.planted is not None:
+        blk = torch.arange(cfg.n_q, device=dev) // cfg.q_block
+        assert torch.equal(sel.permute(1, 0, 2).long(), inp.planted[blk]), "selection differs"
+    n_marks = 3 if cfg.topk > 0 else 2
+    ms_per_step, per = timed_steps(gsa, step, args, n_marks)
+    att_ms = float(per[:, -1].mean())
+    total_fl, sel_fl = prefill_flops(cfg)
+    achieved = total_fl / (att_ms / 1e3) / 1e12
+    call_ms = float(per.sum(axis=1).mean())
+    kernels = {"prefill_attend": {"ms": att_ms, "alg_flops": total_fl,
+                                  "TFLOP_s": total_fl / (att_ms / 1e3) / 1e12}}
+    if cfg.topk > 0:
+        sel_ms = float(per[:, 0].mean())
+        kernels["prefill_select"] = {"ms": sel_ms, "alg_flops": sel_fl,
+                                     "TFLOP_s": sel_fl / (sel_ms / 1e3) / 1e12}
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": cfg.n_q / (ms_per_step / 1e3),
+        "unit": "query-positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian q/K/V, planted top-k per 64-query block)",
+        "config": {"workload": f"{cfg.name}: causal block-sparse prefill of positions "
+                               f"[{cfg.q_start}, {cfg.n_raw}), Hq={cfg.n_q_heads}, "
+                               f"Hkv={cfg.n_kv_heads}, D={cfg.head_dim}, N={cfg.n_raw}, "
+                               f"C={cfg.chunk}, k={cfg.topk}, W={cfg.window}, bf16",
+                   "seq_len": cfg.n_raw, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "prefill_attend", "alg_flops_per_launch": total_fl,
+                     "launch_ms_mean": att_ms},
+        "call": {"ms_mean": call_ms, "TFLOP_s": total_fl / (call_ms / 1e3) / 1e12},
+        "kernels": kernels,
+        "source_sha": source_sha("gsa_prefill.hip"),
+    }
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline_prefill(inp, cfg, args.cpu_seconds)
+    return res
+
+
+def run_copy_calibration():
+    """A plain device copy of a known size (for scaling FETCH_SIZE / WRITE_SIZE
+    counters: run under rocprofv3 --pmc and compare with the bytes moved)."""
+    import torch
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
 
 
 def main():
@@ -186,22 +393,28 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="cache copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(decode units are independent; sharding is described in DESIGN.md).",
-              file=sys.stderr)
+              "(decode units and prefill query blocks are independent; the sharding plan is "
+              "written up with the design).", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        run_copy_calibration()
+        return
     import gsa_inputs as gi
     cfg = gi.CONFIGS[args.config]
     if isinstance(cfg, gi.DecodeConfig):
         res = run_decode_bench(args)
+    elif isinstance(cfg, gi.PrefillConfig):
+        res = run_prefill_bench(args)
     else:
-        raise SystemExit(f"--config {args.config}: not a single-level decode workload yet")
+        raise SystemExit(f"--config {args.config}: no benchmark for this workload yet")
     print(json.dumps(res), flush=True)
 
 

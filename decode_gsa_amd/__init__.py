@@ -21,7 +21,7 @@ __all__ = [
     "GSA_F32", "GSA_BF16", "EXPORTED_SYMBOLS",
     "decode_params", "hier_params", "prefill_params",
     "decode_workspace_size", "hier_workspace_size", "prefill_workspace_size", "new_workspace",
-    "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse",
+    "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse", "gsa_profile_events",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = (
     "gsa_decode_workspace_size", "gsa_decode",
     "gsa_decode_hier_workspace_size", "gsa_decode_hier",
     "gsa_prefill_workspace_size", "gsa_prefill_blocksparse",
-    "gsa_status_string", "gsa_last_error",
+    "gsa_profile_events", "gsa_status_string", "gsa_last_error",
 )
 
 _c_i32, _c_i64, _c_f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -81,8 +81,10 @@ def lib() -> ctypes.CDLL:
         L.gsa_prefill_workspace_size.argtypes = [P(PrefillParams), P(_sz)]
         L.gsa_prefill_blocksparse.argtypes = [P(PrefillParams), _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                               _vp]
+        L.gsa_profile_events.argtypes = [P(_vp), _c_i32]
         for f in ("gsa_decode_workspace_size", "gsa_decode", "gsa_decode_hier_workspace_size",
-                  "gsa_decode_hier", "gsa_prefill_workspace_size", "gsa_prefill_blocksparse"):
+                  "gsa_decode_hier", "gsa_prefill_workspace_size", "gsa_prefill_blocksparse",
+                  "gsa_profile_events"):
             getattr(L, f).restype = _c_i32
         L.gsa_status_string.argtypes = [_c_i32]
         L.gsa_status_string.restype = ctypes.c_char_p
@@ -90,6 +92,13 @@ def lib() -> ctypes.CDLL:
         L.gsa_last_error.restype = ctypes.c_char_p
         _lib = L
     return _lib
+
+
+def gsa_profile_events(handles) -> None:
+    """Arm this thread's timing hook with raw hipEvent_t handles (ints); an
+    empty sequence disarms it. See gsa_profile_events in include/gsa.h."""
+    arr = (_vp * max(1, len(handles)))(*[_vp(h) for h in handles])
+    _check(lib().gsa_profile_events(arr, len(handles)), "gsa_profile_events")
 
 
 def _check(status: int, where: str) -> None:

@@ -37,6 +37,7 @@
 #include "gsa.h"
 #include "gsa_device.hpp"
 #include "gsa_plan.hpp"
+#include "gsa_profile.hpp"
 
 namespace gsa {
 namespace {
@@ -958,7 +959,10 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
   g.out = pl.k > 0 ? nullptr : out; g.lse = pl.k > 0 ? nullptr : lse;
   g.cnt = ctrl_of(ws, pl.off_ctrl, 0);
   g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
+  prof_begin_call();
+  prof_mark(st);
   hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st, g);
+  prof_mark(st);
   if (pl.k > 0) {
     UnfoldArgs u{};
     u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
@@ -970,6 +974,7 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
     u.cnt = ctrl_of(ws, pl.off_ctrl, 2);
     u.scale_log2 = pl.scale * kLog2e;
     hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
+    prof_mark(st);
   }
   return launch_status("gsa_decode launch");
 }
@@ -1000,7 +1005,10 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   g.out = nullptr; g.lse = nullptr;
   g.cnt = ctrl_of(ws, hp.off_ctrl, 0);
   g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
+  prof_begin_call();
+  prof_mark(st);
   hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_l2), dim3(kThreads), 0, st, g);
+  prof_mark(st);
   // level 1: children of the chosen groups + the ungrouped gists, top-k1 chunks
   GistArgs c = g;
   c.K = K; c.V = V;
@@ -1015,6 +1023,7 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   c.out = pl.k > 0 ? nullptr : out; c.lse = pl.k > 0 ? nullptr : lse;
   c.cnt = ctrl_of(ws, hp.off_ctrl, 1);
   hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_c), dim3(kThreads), 0, st, c);
+  prof_mark(st);
   // unfold the chosen chunks, merge everything
   if (pl.k > 0) {
     UnfoldArgs u{};
@@ -1027,6 +1036,7 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
     u.cnt = ctrl_of(ws, hp.off_ctrl, 2);
     u.scale_log2 = pl.scale * kLog2e;
     hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
+    prof_mark(st);
   }
   return launch_status("gsa_decode_hier launch");
 }

@@ -33,6 +33,7 @@
 #include "gsa.h"
 #include "gsa_device.hpp"
 #include "gsa_plan.hpp"
+#include "gsa_profile.hpp"
 
 namespace gsa {
 namespace {
@@ -616,6 +617,8 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
   if (pl.n_q == 0) return GSA_OK;
   int32_t* wsel = reinterpret_cast<int32_t*>(ws);
   const int grid = pl.n_blocks * pl.Hkv;
+  prof_begin_call();
+  prof_mark(stream);
   if (pl.k > 0) {
     SelArgs s{};
     s.q = q; s.K = K; s.R = pl.R;
@@ -624,6 +627,7 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
     s.score_mul = pl.scale / G;
     s.sel_ws = wsel; s.sel_out = sel;
     hipLaunchKernelGGL((prefill_select<G>), dim3(grid), dim3(kPThreads), 0, stream, s);
+    prof_mark(stream);
   }
   AttArgs t{};
   t.q = q; t.K = K; t.V = V; t.out = out; t.sel = wsel; t.R = pl.R;
@@ -631,6 +635,7 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
   t.q_start = (int32_t)pl.q_start; t.n_q = (int32_t)pl.n_q;
   t.scale_log2 = pl.scale * kLog2e;
   hipLaunchKernelGGL((prefill_attend<G>), dim3(grid), dim3(kPThreads), 0, stream, t);
+  prof_mark(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GSA_ERR_HIP, "gsa_prefill_blocksparse launch: %s", hipGetErrorString(e));
   return GSA_OK;

@@ -189,6 +189,16 @@ def test_prefill_workspace_holds_the_selection(L):
     assert n.value == 0
 
 
+def test_profile_events_validation(L):
+    arr = (ctypes.c_void_p * 9)(*([ctypes.c_void_p(16)] * 9))
+    assert L.gsa_profile_events(arr, -1) == INVALID
+    assert L.gsa_profile_events(arr, 9) == INVALID
+    assert L.gsa_profile_events(None, 2) == INVALID
+    nul = (ctypes.c_void_p * 2)(ctypes.c_void_p(16), None)
+    assert L.gsa_profile_events(nul, 2) == INVALID
+    assert L.gsa_profile_events(None, 0) == OK     # disarm
+
+
 def test_status_strings(L):
     for s in range(5):
         assert L.gsa_status_string(s).startswith(b"GSA_")
