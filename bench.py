@@ -358,7 +358,8 @@ def run_prefill_bench(args):
                                f"C={cfg.chunk}, k={cfg.topk}, W={cfg.window}, bf16",
                    "seq_len": cfg.n_raw, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                     "traffic": measured_traffic(f"prefill_attend/{cfg.name}", source_sha("gsa_prefill.hip")),
                      "kernel": "prefill_attend", "alg_flops_per_launch": total_fl,
                      "launch_ms_mean": att_ms},
         "call": {"ms_mean": call_ms, "TFLOP_s": total_fl / (call_ms / 1e3) / 1e12},
