@@ -7,9 +7,9 @@
 // 2 'Key Concepts' (a gist follows its chunk, so query t may use gist m only
 // once chunk m is complete: m < floor(t/C)); the slide deck's slides 7-10.
 //
-// One workgroup per (kv-head, block of 64 query positions); wave w owns
-// queries 16w..16w+15 of the block with all g query heads of the kv-head, so
-// every K/V tile staged in LDS serves 64*g query rows.
+// One workgroup per (kv-head, block of 64 query positions); its waves own
+// 16-query tiles of the block, so every K/V tile staged in LDS serves 64*g
+// query rows.
 //
 //   prefill_select  group score S[t][m] = (scale/g) * sum_h q_h(t) . k(gist m)
 //                   for eligible gists, per query the exact top-k (ties to the
@@ -27,7 +27,16 @@
 //                   results keep one query row per lane; V^T comes from the
 //                   row-major V tile through the transposing LDS read
 //                   (ds_read_b64_tr_b16). P is split into bf16 hi + lo parts so
-//                   that P.V keeps about 16 bits of the fp32 weights.
+//                   that P.V keeps about 16 bits of the fp32 weights. With g = 4
+//                   two waves share a query tile (two heads each), so each SIMD
+//                   runs two waves.
+//
+// K/V tiles reach LDS by direct-to-LDS loads (global_load_lds_dwordx4) into a
+// ring of tiles, several tiles in flight. Such a load writes lane i's 16 bytes
+// at LDS base + 16 i, so the layout is made conflict-free by choosing which
+// 16-byte chunk of the row each lane fetches: chunk c of tile row r sits in
+// slot c ^ (r & 15) for K (16-byte operand reads, 16 rows at a time) and in
+// slot c ^ 2(r & 7) for V (8-byte transposed reads of 8 rows).
 #include <hip/hip_runtime.h>
 
 #include "gsa.h"
@@ -43,19 +52,10 @@ using namespace dev;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short __attribute__((ext_vector_type(4))) __attribute__((address_space(3)))* lds_i16x4_ptr;
 
-constexpr int kPThreads = 256;          // 4 waves
-constexpr int kPWaves = 4;
 constexpr int kQB = kQBlock;            // queries per workgroup (64)
-static_assert(kQB == 16 * kPWaves, "one 16-query tile per wave");
 constexpr int kD = 128;
-constexpr int kRowBytes = kD * 2;       // bf16 row
-constexpr int kKStride = 272;           // LDS row stride of K tiles: conflict-free 16 B operand reads
-constexpr int kVStride = 288;           // LDS row stride of V tiles: conflict-free transposed reads
-constexpr int kSelTile = 64;            // gists per selection tile
-constexpr int kCap = 64;                // survivor buffer entries per query
-constexpr int kAttTile = 32;            // rows per attention tile (the K of the P.V MFMA)
+constexpr int kRowBytes = kD * 2;       // bf16 row: 16 chunks of 16 bytes
 constexpr float kPLazy = 8.f;           // lazy running max, log2 units
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -66,17 +66,76 @@ __device__ __forceinline__ bf16x8 lds_b128(const char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Four bf16 of a transposed LDS read (see the file header).
-__device__ __forceinline__ i16x4 lds_tr(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4_ptr)((__attribute__((address_space(3))) char*)p));
-}
-
 __device__ __forceinline__ bf16x8 cat8(const i16x4& lo, const i16x4& hi) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
+
+// One direct-to-LDS load per lane: 16 bytes from src to lds_base + 16 * lane
+// (lds_base is the same for the whole wave).
+__device__ __forceinline__ void dma16(const char* src, char* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without the memory fences of __syncthreads(). The fences
+// would make every wave wait for all of its loads in flight, including the
+// direct-to-LDS loads of later tiles; the hand-off of a tile is ordered instead
+// by each wave's own vmcnt wait before the barrier. lgkmcnt(0) retires this
+// wave's LDS reads of the tile whose buffer the next loads overwrite.
+__device__ __forceinline__ void tile_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
+}
+
+// The V^T operands of a 32-row tile for all 8 column blocks of 16: two
+// transposed 8-byte reads per block (rows 0-15 and 16-31 of the tile, the
+// second 4096 bytes further). Written out as one asm block that also waits
+// for its reads: the builtin form makes the compiler wait for every direct-to-
+// LDS load in flight first.
+__device__ __forceinline__ void lds_tr_tile(const uint32_t (&addr)[8], bf16x8 (&vf)[8]) {
+  i16x4 a[8], b[8];
+  __asm__ volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %2, %17\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %10, %21\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %12, %22\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %14, %23\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(b[0]), "=&v"(a[1]), "=&v"(b[1]), "=&v"(a[2]), "=&v"(b[2]), "=&v"(a[3]),
+        "=&v"(b[3]), "=&v"(a[4]), "=&v"(b[4]), "=&v"(a[5]), "=&v"(b[5]), "=&v"(a[6]), "=&v"(b[6]),
+        "=&v"(a[7]), "=&v"(b[7])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+        "v"(addr[7])
+      : "memory");
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) vf[dt] = cat8(a[dt], b[dt]);
+}
+
+// LDS slot of chunk c of tile row r.
+__device__ __forceinline__ int k_slot(int c, int r) { return c ^ (r & 15); }
+__device__ __forceinline__ int v_slot(int c, int r) { return c ^ (2 * (r & 7)); }
 
 // Cache row of raw position p of the interleaved cache.
 __device__ __forceinline__ int32_t raw_row(int32_t p, int32_t C, int32_t M) {
@@ -123,24 +182,42 @@ __device__ __forceinline__ void wg_coords(int n_blocks, int Hkv, int* kvh, int* 
   *blk = x % n_blocks;
 }
 
-// Query fragments (B operand of S^T = K Q^T): lane holds q_h[query][32ks + 8jg .. +7].
-template <int G>
+// Query fragments (B operand of S^T = K Q^T) of heads h0..h0+H-1: lane holds
+// q_h[query][32ks + 8jg .. +7].
+template <int H>
 __device__ __forceinline__ void load_qfrag(const char* qbase, int64_t n_q, int64_t t_idx, bool valid,
-                                           int jg, bf16x8 (&qf)[G][4]) {
+                                           int h0, int jg, bf16x8 (&qf)[H][4]) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < H; ++h)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (valid) {
-        const uint4 v = load16(qbase + (((int64_t)h * n_q + t_idx) * kD + 32 * ks + 8 * jg) * 2);
+        const uint4 v = load16(qbase + (((int64_t)(h0 + h) * n_q + t_idx) * kD + 32 * ks + 8 * jg) * 2);
         qf[h][ks] = __builtin_bit_cast(bf16x8, v);
       } else {
         qf[h][ks] = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
       }
     }
+  // Settle the fragments here: a first use inside the tile loop would make the
+  // compiler wait for every load in flight (the tile loads too) in each tile.
+#pragma unroll
+  for (int h = 0; h < H; ++h)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) __asm__ volatile("" : "+v"(qf[h][ks]));
 }
 
 // ------------------------------------------------------------ selection ----
+
+constexpr int kSelThreads = 256;        // 4 waves, one 16-query tile each
+constexpr int kSelWaves = 4;
+constexpr int kSelTile = 64;            // gists per tile
+constexpr int kSelNB = 3;               // tiles in the LDS ring
+constexpr int kSelTileBytes = kSelTile * kRowBytes;
+constexpr int kSelPer = kSelTile / 4 / kSelWaves;   // direct loads per wave per tile (4 rows each)
+constexpr int kCap = 48;                // survivor buffer entries per query
+constexpr int kCapLane = kCap / 4;      // entries per lane in a compaction
+constexpr int kBufStride = kQB + 4;     // words per buffer entry row (bank spread)
+static_assert(kPrefillMaxK <= kCap - 16, "a compaction must leave room for a 16-gist subtile");
 
 struct SelArgs {
   const void* q;          // [Hq][n_q][D] bf16
@@ -153,31 +230,32 @@ struct SelArgs {
 };
 
 struct SelLds {
-  char kt[2][kSelTile * kKStride];
-  uint32_t bkey[kQB][kCap];
-  uint32_t bid[kQB][kCap];
+  char ring[kSelNB][kSelTileBytes];
+  uint32_t bkey[kCap][kBufStride];   // entry-major: lanes of one entry hit distinct banks
+  uint32_t bid[kCap][kBufStride];
 };
 
 // Compact every query's survivor buffer of the wave to its exact top-k.
-// Lanes (qi, jg) own entries [16jg, 16jg + 16) of query qloc's buffer (in
-// gist order). Returns the new count; tau gets the k-th best key (0 if fewer
-// than k entries: then every later eligible gist still enters).
+// Lanes (qi, jg) own entries [kCapLane*jg, kCapLane*(jg+1)) of query qloc's
+// buffer (in gist order). Returns the new count; tau gets the k-th best key
+// (0 if fewer than k entries: then every later eligible gist still enters).
 __device__ __forceinline__ int compact_query(SelLds& L, int qloc, int jg, int cnt, int k, uint32_t* tau) {
-  uint32_t kk[16];
+  uint32_t kk[kCapLane];
+  const int e0 = kCapLane * jg;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) kk[e] = 16 * jg + e < cnt ? L.bkey[qloc][16 * jg + e] : 0u;
+  for (int e = 0; e < kCapLane; ++e) kk[e] = e0 + e < cnt ? L.bkey[e0 + e][qloc] : 0u;
   uint32_t P = 0u;
   for (int b = 31; b >= 0; --b) {
     const uint32_t c = P | (1u << b);
     int n = 0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) n += kk[e] >= c ? 1 : 0;
+    for (int e = 0; e < kCapLane; ++e) n += kk[e] >= c ? 1 : 0;
     n = sum4(n);
     P = n >= k ? c : P;
   }
   int gt = 0, ce = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < kCapLane; ++e) {
     gt += kk[e] > P ? 1 : 0;
     ce += (kk[e] == P && kk[e] != 0u) ? 1 : 0;
   }
@@ -185,10 +263,10 @@ __device__ __forceinline__ int compact_query(SelLds& L, int qloc, int jg, int cn
   const int need = k - gt;
   int ce_tot;
   int eqb = excl4(ce, jg, &ce_tot);
-  bool take[16];
+  bool take[kCapLane];
   int ct = 0;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < kCapLane; ++e) {
     const bool eq = kk[e] == P && kk[e] != 0u;
     take[e] = kk[e] > P || (eq && eqb < need);
     eqb += eq ? 1 : 0;
@@ -196,15 +274,15 @@ __device__ __forceinline__ int compact_query(SelLds& L, int qloc, int jg, int cn
   }
   int tot;
   int pos = excl4(ct, jg, &tot);
-  uint32_t ii[16];
+  uint32_t ii[kCapLane];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) ii[e] = take[e] ? L.bid[qloc][16 * jg + e] : 0u;
+  for (int e = 0; e < kCapLane; ++e) ii[e] = take[e] ? L.bid[e0 + e][qloc] : 0u;
   wave_lds_sync();
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < kCapLane; ++e) {
     if (take[e]) {
-      L.bkey[qloc][pos] = kk[e];
-      L.bid[qloc][pos] = ii[e];
+      L.bkey[pos][qloc] = kk[e];
+      L.bid[pos][qloc] = ii[e];
       ++pos;
     }
   }
@@ -213,28 +291,23 @@ __device__ __forceinline__ int compact_query(SelLds& L, int qloc, int jg, int cn
   return tot;
 }
 
-// Stage gist rows [m0, m0 + kSelTile) of one kv-head into registers (zero rows
-// past E); 4 x 16 B per thread, 16 consecutive threads per 256-byte row.
-__device__ __forceinline__ void sel_load(const char* Kh, int m0, int E, int C, uint4 (&r)[4]) {
+// Direct loads of gist tile `it` (rows m = 64 it + r; rows past E read gist 0,
+// whose scores the eligibility mask drops).
+__device__ __forceinline__ void sel_issue(char* buf, const char* Kh, int it, int E, int C) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int pair = (int)threadIdx.x + kPThreads * u;
-    const int i = pair >> 4, ch = pair & 15;
-    const int m = m0 + i;
-    r[u] = m < E ? load16(Kh + ((int64_t)m * (C + 1) + C) * kRowBytes + ch * 16) : make_uint4(0u, 0u, 0u, 0u);
-  }
-}
-__device__ __forceinline__ void sel_store(char* kt, const uint4 (&r)[4]) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int pair = (int)threadIdx.x + kPThreads * u;
-    *reinterpret_cast<uint4*>(kt + (pair >> 4) * kKStride + (pair & 15) * 16) = r[u];
+  for (int u = 0; u < kSelPer; ++u) {
+    const int rb = 4 * (w + kSelWaves * u);
+    const int r = rb + (lane >> 4);
+    const int m = it * kSelTile + r;
+    const int64_t row = m < E ? (int64_t)m * (C + 1) + C : C;
+    dma16(Kh + row * kRowBytes + k_slot(lane & 15, r) * 16, buf + rb * kRowBytes);
   }
 }
 
 template <int G>
-__global__ __launch_bounds__(kPThreads) void prefill_select(SelArgs a) {
-  __shared__ SelLds L;
+__global__ __launch_bounds__(kSelThreads) void prefill_select(SelArgs a) {
+  __shared__ __attribute__((aligned(16))) SelLds L;
   int kvh, blk;
   wg_coords(a.n_blocks, a.Hkv, &kvh, &blk);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -249,31 +322,38 @@ __global__ __launch_bounds__(kPThreads) void prefill_select(SelArgs a) {
 
   bf16x8 qf[G][4];
   load_qfrag<G>(reinterpret_cast<const char*>(a.q) + (int64_t)kvh * G * a.n_q * kRowBytes, a.n_q, t_idx,
-                valid, jg, qf);
+                valid, 0, jg, qf);
   const char* Kh = reinterpret_cast<const char*>(a.K) + (int64_t)kvh * a.R * kRowBytes;
 
   int cnt = 0;
   uint32_t tau = 0u;
   const int n_tiles = (E + kSelTile - 1) / kSelTile;
-  uint4 stage[4];
-  if (n_tiles > 0) {
-    sel_load(Kh, 0, E, a.C, stage);
-    sel_store(L.kt[0], stage);
-  }
-  __syncthreads();
+  // this lane's operand offsets inside a tile: row 16s + qi, chunk 4ks + jg
+  int koff[4][4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) koff[s][ks] = (16 * s + qi) * kRowBytes + k_slot(4 * ks + jg, qi) * 16;
+
+  for (int it = 0; it < kSelNB - 1 && it < n_tiles; ++it) sel_issue(L.ring[it], Kh, it, E, a.C);
   for (int it = 0; it < n_tiles; ++it) {
-    if (it + 1 < n_tiles) sel_load(Kh, (it + 1) * kSelTile, E, a.C, stage);
-    const char* kt = L.kt[it & 1];
+    // this wave's loads of tile `it` are done once at most (tiles issued
+    // after it) x kSelPer loads are outstanding
+    if (it + 1 < n_tiles) wait_vm<kSelPer * (kSelNB - 2)>();
+    else wait_vm<0>();
+    tile_barrier();    // every wave's loads of tile it landed; tile it-1's buffer is free
+    if (it + kSelNB - 1 < n_tiles) sel_issue(L.ring[(it + kSelNB - 1) % kSelNB], Kh, it + kSelNB - 1, E, a.C);
+    const char* kt = L.ring[it % kSelNB];
 #pragma unroll
     for (int s = 0; s < kSelTile / 16; ++s) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kf = lds_b128(kt + (16 * s + qi) * kKStride + ks * 64 + jg * 16);
+        const bf16x8 kf = lds_b128(kt + koff[s][ks]);
 #pragma unroll
         for (int h = 0; h < G; ++h) acc = mfma(kf, qf[h][ks], acc);
       }
-      // acc[r]: gist it*64 + 16s + 4jg + r against query qi (all heads summed)
+      // acc[r]: gist 64 it + 16 s + 4 jg + r against query qi (heads summed)
       uint32_t key[4];
       bool sv[4];
       int c = 0;
@@ -290,8 +370,8 @@ __global__ __launch_bounds__(kPThreads) void prefill_select(SelArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (sv[r]) {
-            L.bkey[qloc][pos] = key[r];
-            L.bid[qloc][pos] = (uint32_t)(it * kSelTile + 16 * s + 4 * jg + r);
+            L.bkey[pos][qloc] = key[r];
+            L.bid[pos][qloc] = (uint32_t)(it * kSelTile + 16 * s + 4 * jg + r);
             ++pos;
           }
         }
@@ -300,18 +380,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_select(SelArgs a) {
         if (__ballot(cnt > kCap - 16) != 0ull) cnt = compact_query(L, qloc, jg, cnt, a.k, &tau);
       }
     }
-    __syncthreads();   // every wave is done with the other buffer
-    if (it + 1 < n_tiles) sel_store(L.kt[(it + 1) & 1], stage);
-    __syncthreads();
   }
   cnt = compact_query(L, qloc, jg, cnt, a.k, &tau);
   if (valid) {
     const int64_t o = ((int64_t)kvh * a.n_q + t_idx) * a.k;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int i = 16 * jg + e;
+    for (int e = 0; e < kCapLane; ++e) {
+      const int i = kCapLane * jg + e;
       if (i < a.k) {
-        const int32_t v = i < cnt ? (int32_t)L.bid[qloc][i] : -1;
+        const int32_t v = i < cnt ? (int32_t)L.bid[i][qloc] : -1;
         a.sel_ws[o + i] = v;
         if (a.sel_out) a.sel_out[o + i] = v;
       }
@@ -323,6 +400,18 @@ __global__ __launch_bounds__(kPThreads) void prefill_select(SelArgs a) {
 
 constexpr int kMaxChunkWords = kPrefillMaxGist / 32;   // bitmap of selectable chunks
 constexpr int kMaxUnion = kQB * kPrefillMaxK;           // distinct chunks a block can select
+constexpr int kAttTile = 32;            // rows per tile (the K of the P.V MFMA)
+constexpr int kAttNB = 4;               // tiles in the LDS ring
+constexpr int kHalfTile = kAttTile * kRowBytes;          // K or V part of a tile (8 KB)
+
+// Waves per 16-query tile and heads per wave.
+template <int G> struct AttShape {
+  static constexpr int WPQ = G == 4 ? 2 : 1;
+  static constexpr int HPW = G / WPQ;
+  static constexpr int NW = 4 * WPQ;          // waves per workgroup
+  static constexpr int NT = 64 * NW;          // threads per workgroup
+  static constexpr int PER = 16 / NW;         // direct loads (4 rows each) per wave per tile
+};
 
 struct AttArgs {
   const void* q;
@@ -336,124 +425,110 @@ struct AttArgs {
 };
 
 struct AttLds {
-  char kt[2][kAttTile * kKStride];
-  char vt[2][kAttTile * kVStride];
+  char ring[kAttNB][2 * kHalfTile];   // [tile][K rows | V rows]
   uint32_t bitmap[kMaxChunkWords];
   uint32_t wpre[kMaxChunkWords];
   int32_t U[kMaxUnion];
   uint32_t qm[kMaxUnion][2];
-  int scan[kPWaves];
+  int scan[8];
   int nU;
 };
 
 // What a tile row is: a gist, a raw row of a selected chunk, a window row.
 enum { kGist = 0, kChunk = 1, kWin = 2 };
 
-struct Phase {
-  int kind;
-  int n;        // rows in the phase
-  int lo;       // kWin: first position
-};
-
-__device__ __forceinline__ int phase_row(const Phase& ph, const AttLds& L, int i, int C, int M) {
-  if (i >= ph.n) return -1;
-  if (ph.kind == kGist) return i * (C + 1) + C;
-  if (ph.kind == kChunk) {
-    const int m = L.U[i / C];
-    return m * (C + 1) + i % C;
-  }
-  return raw_row(ph.lo + i, C, M);
+// Cache row of phase item i (a valid row for items past n: their scores are masked).
+template <int KIND>
+__device__ __forceinline__ int64_t phase_row(const AttLds& L, int i, int n, int lo, int C, int M) {
+  if (i >= n) return 0;
+  if (KIND == kGist) return (int64_t)i * (C + 1) + C;
+  if (KIND == kChunk) return (int64_t)L.U[i / C] * (C + 1) + i % C;
+  return raw_row(lo + i, C, M);
 }
 
-// Stage rows [i0, i0 + kAttTile) of a phase: K and V, 2 x 16 B each per thread.
-__device__ __forceinline__ void att_load(const char* Kh, const char* Vh, const Phase& ph, const AttLds& L,
-                                         int i0, int C, int M, uint4 (&rk)[2], uint4 (&rv)[2]) {
+template <int NW, int KIND>
+__device__ __forceinline__ void att_issue(char* buf, const char* Kh, const char* Vh, const AttLds& L,
+                                          int i0, int n, int lo, int C, int M) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int pair = (int)threadIdx.x + kPThreads * u;
-    const int i = pair >> 4, ch = pair & 15;
-    const int row = phase_row(ph, L, i0 + i, C, M);
-    if (row >= 0) {
-      rk[u] = load16(Kh + (int64_t)row * kRowBytes + ch * 16);
-      rv[u] = load16(Vh + (int64_t)row * kRowBytes + ch * 16);
-    } else {
-      rk[u] = make_uint4(0u, 0u, 0u, 0u);
-      rv[u] = rk[u];
-    }
-  }
-}
-__device__ __forceinline__ void att_store(char* kt, char* vt, const uint4 (&rk)[2], const uint4 (&rv)[2]) {
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int pair = (int)threadIdx.x + kPThreads * u;
-    const int i = pair >> 4, ch = pair & 15;
-    *reinterpret_cast<uint4*>(kt + i * kKStride + ch * 16) = rk[u];
-    *reinterpret_cast<uint4*>(vt + i * kVStride + ch * 16) = rv[u];
+  for (int u = 0; u < 16 / NW; ++u) {
+    const int j = w + NW * u;                 // wave-uniform: K rows for j < 8, V rows after
+    const int rb = 4 * (j & 7);
+    const int r = rb + (lane >> 4);
+    const int64_t row = phase_row<KIND>(L, i0 + r, n, lo, C, M);
+    if (j < 8)
+      dma16(Kh + row * kRowBytes + k_slot(lane & 15, r) * 16, buf + rb * kRowBytes);
+    else
+      dma16(Vh + row * kRowBytes + v_slot(lane & 15, r) * 16, buf + kHalfTile + rb * kRowBytes);
   }
 }
 
-template <int G>
+template <int H>
 struct AttState {
-  f32x4 o[G][8];      // O^T[16dt + 4jg + r][query qi] of head h
-  float m[G], l[G];   // running max (log2 units) and this lane's share of the sum
+  f32x4 o[H][8];      // O^T[16dt + 4jg + r][query qi] of head h
+  float m[H], l[H];   // running max (log2 units) and this lane's share of the sum
 };
 
-// May query (t, qi) use row i of the phase?
-__device__ __forceinline__ bool row_ok(const Phase& ph, const AttLds& L, int i, int qi, int t, int elig,
-                                       int W, int C) {
-  if (i >= ph.n) return false;
-  if (ph.kind == kGist) return i < elig;
-  if (ph.kind == kChunk) {
-    const int u = i / C;
-    if (!((L.qm[u][qi >> 5] >> (qi & 31)) & 1u)) return false;
-    const int pos = L.U[u] * C + i % C;
-    return pos < t - W + 1;                    // the window attends that row
+struct AttCtx {
+  int qloc, t, elig, W, C, lo;
+  bool valid;
+  float c;            // scale * log2(e)
+};
+
+// May the lane's query use phase row i?
+template <int KIND>
+__device__ __forceinline__ bool row_ok(const AttLds& L, const AttCtx& x, int i, int n) {
+  if (!x.valid || i >= n) return false;
+  if (KIND == kGist) return i < x.elig;
+  if (KIND == kChunk) {
+    const int u = i / x.C;
+    if (!((L.qm[u][x.qloc >> 5] >> (x.qloc & 31)) & 1u)) return false;
+    return L.U[u] * x.C + i % x.C < x.t - x.W + 1;   // the window attends that row
   }
-  const int pos = ph.lo + i;
-  return pos >= t - W + 1 && pos <= t;
+  const int pos = x.lo + i;
+  return pos >= x.t - x.W + 1 && pos <= x.t;
 }
 
-template <int G>
-__device__ __forceinline__ void att_tile(const char* kt, const char* vt, const Phase& ph, const AttLds& L,
-                                         int i0, int qloc, int t, int elig, bool valid, int W, int C,
-                                         float c, const bf16x8 (&qf)[G][4], AttState<G>& st) {
+template <int H, int KIND>
+__device__ __forceinline__ void att_tile(const char* kt, const char* vt, const AttLds& L, const AttCtx& x,
+                                         int i0, int n, bool masked, const bf16x8 (&qf)[H][4],
+                                         AttState<H>& st) {
   const int lane = threadIdx.x & 63, qi = lane & 15, jg = lane >> 4;
-  f32x4 s[2][G];
+  f32x4 s[2][H];
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[sb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < H; ++h) s[sb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 kf = lds_b128(kt + (16 * sb + qi) * kKStride + ks * 64 + jg * 16);
+      const bf16x8 kf = lds_b128(kt + (16 * sb + qi) * kRowBytes + k_slot(4 * ks + jg, qi) * 16);
 #pragma unroll
-      for (int h = 0; h < G; ++h) s[sb][h] = mfma(kf, qf[h][ks], s[sb][h]);
+      for (int h = 0; h < H; ++h) s[sb][h] = mfma(kf, qf[h][ks], s[sb][h]);
     }
-  // s[sb][h][r]: row i0 + 16sb + 4jg + r against query qi, head h
-  bool ok[2][4];
+  // s[sb][h][r]: row i0 + 16sb + 4jg + r against the lane's query, head h
+  if (masked) {
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      ok[sb][r] = valid && row_ok(ph, L, i0 + 16 * sb + 4 * jg + r, qloc, t, elig, W, C);
-  bf16x8 phi[G], plo[G];
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = row_ok<KIND>(L, x, i0 + 16 * sb + 4 * jg + r, n);
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x[8];
+        for (int h = 0; h < H; ++h) s[sb][h][r] = ok ? s[sb][h][r] : -INFINITY;
+      }
+  }
+  bf16x8 phi[H], plo[H];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int sb = e >> 2, r = e & 3;
-      x[e] = ok[sb][r] ? s[sb][h][r] * c : -INFINITY;
-    }
-    float mx = x[0];
+  for (int h = 0; h < H; ++h) {
+    float mx = s[0][h][0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-    mx = max4(mx);
-    const bool need = mx > st.m[h] + kPLazy;
-    if (__ballot(need) != 0ull) {
-      const float mn = need ? mx : st.m[h];
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e >> 2][h][e & 3]);
+    const float cand = mx * x.c;
+    if (__ballot(cand > st.m[h] + kPLazy) != 0ull) {
+      // raise the row's max (the same on the row's four lanes) and rescale
+      const float c4 = max4(cand);
+      const float mn = c4 > st.m[h] + kPLazy ? c4 : st.m[h];
       const float al = fexp2(st.m[h] - mn);
       st.m[h] = mn;
       st.l[h] *= al;
@@ -462,10 +537,11 @@ __device__ __forceinline__ void att_tile(const char* kt, const char* vt, const P
 #pragma unroll
         for (int r = 0; r < 4; ++r) st.o[h][dt][r] *= al;
     }
+    const float nm = -st.m[h];
     float ps = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float p = fexp2(x[e] - st.m[h]);
+      const float p = fexp2(fmaf(s[e >> 2][h][e & 3], x.c, nm));
       ps += p;
       const __bf16 hi = (__bf16)p;
       phi[h][e] = hi;
@@ -473,70 +549,85 @@ __device__ __forceinline__ void att_tile(const char* kt, const char* vt, const P
     }
     st.l[h] += ps;
   }
-  // O^T += V^T P^T: A operand = V^T rows of this tile, transposed out of LDS
+  // O^T += V^T P^T; the V^T operand comes transposed out of LDS
   const int s16 = lane & 15;
+  const int R = 4 * jg + (s16 >> 2);
+  const uint32_t vrow = lds_addr(vt) + R * kRowBytes + 8 * (s16 & 1);
+  uint32_t va[8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    const char* p1 = vt + (4 * jg + (s16 >> 2)) * kVStride + (16 * dt + 4 * (s16 & 3)) * 2;
-    const char* p2 = p1 + 16 * kVStride;
-    const bf16x8 vf = cat8(lds_tr(p1), lds_tr(p2));
+  for (int dt = 0; dt < 8; ++dt) va[dt] = vrow + v_slot(2 * dt + ((s16 & 3) >> 1), R) * 16;
+  bf16x8 vf[8];
+  lds_tr_tile(va, vf);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      st.o[h][dt] = mfma(vf, phi[h], st.o[h][dt]);
-      st.o[h][dt] = mfma(vf, plo[h], st.o[h][dt]);
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      st.o[h][dt] = mfma(vf[dt], phi[h], st.o[h][dt]);
+      st.o[h][dt] = mfma(vf[dt], plo[h], st.o[h][dt]);
     }
+}
+
+// One phase: rows [0, n) of kind KIND, kAttTile rows per tile, kAttNB tiles
+// in the LDS ring. `all_ok` = items [0, all_ok) need no mask for any query.
+template <int G, int KIND>
+__device__ __forceinline__ void att_phase(AttLds& L, const char* Kh, const char* Vh, const AttCtx& x, int n,
+                                          int all_ok, int M, const bf16x8 (&qf)[AttShape<G>::HPW][4],
+                                          AttState<AttShape<G>::HPW>& st) {
+  constexpr int NW = AttShape<G>::NW, PER = AttShape<G>::PER, H = AttShape<G>::HPW;
+  const int nt = (n + kAttTile - 1) / kAttTile;
+  if (nt == 0) return;
+  __syncthreads();   // the ring is free (the previous phase's last tile was read)
+  for (int t = 0; t < kAttNB - 1 && t < nt; ++t)
+    att_issue<NW, KIND>(L.ring[t], Kh, Vh, L, t * kAttTile, n, x.lo, x.C, M);
+  for (int t = 0; t < nt; ++t) {
+    const int ahead = min(kAttNB - 2, nt - 1 - t);   // tiles issued after tile t
+    if (ahead >= 2) wait_vm<2 * PER>();
+    else if (ahead == 1) wait_vm<PER>();
+    else wait_vm<0>();
+    tile_barrier();    // every wave's loads of tile t landed; tile t-1's buffer is free
+    if (t + kAttNB - 1 < nt)
+      att_issue<NW, KIND>(L.ring[(t + kAttNB - 1) % kAttNB], Kh, Vh, L, (t + kAttNB - 1) * kAttTile, n, x.lo,
+                          x.C, M);
+    const char* buf = L.ring[t % kAttNB];
+    const bool masked = KIND != kGist || (t + 1) * kAttTile > all_ok;
+    att_tile<H, KIND>(buf, buf + kHalfTile, L, x, t * kAttTile, n, masked, qf, st);
   }
 }
 
 template <int G>
-__device__ __forceinline__ void att_phase(const char* Kh, const char* Vh, const Phase& ph, AttLds& L,
-                                          int qloc, int t, int elig, bool valid, int W, int C, int M, float c,
-                                          const bf16x8 (&qf)[G][4], AttState<G>& st) {
-  const int n_tiles = (ph.n + kAttTile - 1) / kAttTile;
-  if (n_tiles == 0) return;
-  uint4 rk[2], rv[2];
-  att_load(Kh, Vh, ph, L, 0, C, M, rk, rv);
-  att_store(L.kt[0], L.vt[0], rk, rv);
-  __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
-    if (it + 1 < n_tiles) att_load(Kh, Vh, ph, L, (it + 1) * kAttTile, C, M, rk, rv);
-    att_tile<G>(L.kt[it & 1], L.vt[it & 1], ph, L, it * kAttTile, qloc, t, elig, valid, W, C, c, qf, st);
-    __syncthreads();
-    if (it + 1 < n_tiles) att_store(L.kt[(it + 1) & 1], L.vt[(it + 1) & 1], rk, rv);
-    __syncthreads();
-  }
-}
-
-template <int G>
-__global__ __launch_bounds__(kPThreads) void prefill_attend(AttArgs a) {
-  __shared__ AttLds L;
+__global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
+  using S = AttShape<G>;
+  constexpr int H = S::HPW, NT = S::NT;
+  __shared__ __attribute__((aligned(16))) AttLds L;
   int kvh, blk;
   wg_coords(a.n_blocks, a.Hkv, &kvh, &blk);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int qi = lane & 15, jg = lane >> 4;
-  const int qloc = 16 * w + qi;
+  const int qt = w % 4;                 // 16-query tile of this wave
+  const int h0 = (w / 4) * H;           // first head of this wave
+  const int qloc = 16 * qt + qi;
   const int t_idx = blk * kQB + qloc;
   const bool valid = t_idx < a.n_q;
   const int t = a.q_start + t_idx;
-  const int elig = valid ? min(a.M, t / a.C) : 0;
   const int nq_blk = min(kQB, a.n_q - blk * kQB);
   const int t_first = a.q_start + blk * kQB;
   const int t_last = t_first + nq_blk - 1;
   const int E = min(a.M, t_last / a.C);
+  const int E0 = min(a.M, t_first / a.C);   // gists every query of the block may use
 
   // union of the block's selected chunks (ascending) and, per chunk, the
   // mask of the queries that selected it
   const int nwords = (E + 31) / 32;
-  for (int i = tid; i < nwords; i += kPThreads) L.bitmap[i] = 0u;
+  for (int i = tid; i < nwords; i += NT) L.bitmap[i] = 0u;
   __syncthreads();
   const int32_t* sb = a.sel + ((int64_t)kvh * a.n_q + (int64_t)blk * kQB) * a.k;
-  for (int pr = tid; pr < nq_blk * a.k; pr += kPThreads) {
+  for (int pr = tid; pr < nq_blk * a.k; pr += NT) {
     const int m = sb[pr];
     if (m >= 0 && m < E) atomicOr(&L.bitmap[m >> 5], 1u << (m & 31));
   }
   __syncthreads();
   {
-    constexpr int kPer = kMaxChunkWords / kPThreads;
+    constexpr int kPer = kMaxChunkWords / NT;
     int cnt = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
@@ -559,16 +650,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_attend(AttArgs a) {
         run = r;
       }
     }
-    if (tid == kPThreads - 1) L.nU = run;
+    if (tid == NT - 1) L.nU = run;
   }
   __syncthreads();
   const int nU = L.nU;
-  for (int i = tid; i < nU; i += kPThreads) {
+  for (int i = tid; i < nU; i += NT) {
     L.qm[i][0] = 0u;
     L.qm[i][1] = 0u;
   }
   __syncthreads();
-  for (int pr = tid; pr < nq_blk * a.k; pr += kPThreads) {
+  for (int pr = tid; pr < nq_blk * a.k; pr += NT) {
     const int m = sb[pr];
     if (m >= 0 && m < E) {
       const int u = (int)L.wpre[m >> 5] + __popc(L.bitmap[m >> 5] & ((1u << (m & 31)) - 1u));
@@ -578,30 +669,40 @@ __global__ __launch_bounds__(kPThreads) void prefill_attend(AttArgs a) {
   }
   __syncthreads();
 
-  bf16x8 qf[G][4];
-  load_qfrag<G>(reinterpret_cast<const char*>(a.q) + (int64_t)kvh * G * a.n_q * kRowBytes, a.n_q, t_idx,
-                valid, jg, qf);
+  bf16x8 qf[H][4];
+  load_qfrag<H>(reinterpret_cast<const char*>(a.q) + (int64_t)kvh * G * a.n_q * kRowBytes, a.n_q, t_idx,
+                valid, h0, jg, qf);
   const char* Kh = reinterpret_cast<const char*>(a.K) + (int64_t)kvh * a.R * kRowBytes;
   const char* Vh = reinterpret_cast<const char*>(a.V) + (int64_t)kvh * a.R * kRowBytes;
-  AttState<G> st;
+  AttState<H> st;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < H; ++h) {
     st.m[h] = kMinus;
     st.l[h] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) st.o[h][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int lo = max(0, t_first - a.W + 1);
-  const Phase phases[3] = {{kGist, E, 0}, {kChunk, nU * a.C, 0}, {kWin, t_last - lo + 1, lo}};
-#pragma unroll 1
-  for (int p = 0; p < 3; ++p)
-    att_phase<G>(Kh, Vh, phases[p], L, qloc, t, elig, valid, a.W, a.C, a.M, a.scale_log2, qf, st);
+  AttCtx x;
+  x.qloc = qloc;
+  x.t = t;
+  x.elig = valid ? min(a.M, t / a.C) : 0;
+  x.W = a.W;
+  x.C = a.C;
+  x.lo = max(0, t_first - a.W + 1);
+  x.valid = valid;
+  x.c = a.scale_log2;
+  // rows every query of the block may use without a mask: the first E0 gists,
+  // unless some query of the block is past n_q (then everything is masked)
+  const int all_ok = nq_blk == kQB ? E0 : 0;
+  att_phase<G, kGist>(L, Kh, Vh, x, E, all_ok, a.M, qf, st);
+  att_phase<G, kChunk>(L, Kh, Vh, x, nU * a.C, 0, a.M, qf, st);
+  att_phase<G, kWin>(L, Kh, Vh, x, t_last - x.lo + 1, 0, a.M, qf, st);
 
   if (!valid) return;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int h = 0; h < H; ++h) {
     const float inv = 1.f / fsum4(st.l[h]);
-    float* o = a.out + (((int64_t)kvh * G + h) * a.n_q + t_idx) * kD;
+    float* o = a.out + (((int64_t)kvh * G + h0 + h) * a.n_q + t_idx) * kD;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const float4 v = make_float4(st.o[h][dt][0] * inv, st.o[h][dt][1] * inv, st.o[h][dt][2] * inv,
@@ -626,7 +727,7 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
     s.q_start = (int32_t)pl.q_start; s.n_q = (int32_t)pl.n_q;
     s.score_mul = pl.scale / G;
     s.sel_ws = wsel; s.sel_out = sel;
-    hipLaunchKernelGGL((prefill_select<G>), dim3(grid), dim3(kPThreads), 0, stream, s);
+    hipLaunchKernelGGL((prefill_select<G>), dim3(grid), dim3(kSelThreads), 0, stream, s);
     prof_mark(stream);
   }
   AttArgs t{};
@@ -634,7 +735,7 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
   t.M = (int32_t)pl.M; t.C = pl.C; t.k = pl.k; t.W = pl.W; t.Hkv = pl.Hkv; t.n_blocks = pl.n_blocks;
   t.q_start = (int32_t)pl.q_start; t.n_q = (int32_t)pl.n_q;
   t.scale_log2 = pl.scale * kLog2e;
-  hipLaunchKernelGGL((prefill_attend<G>), dim3(grid), dim3(kPThreads), 0, stream, t);
+  hipLaunchKernelGGL((prefill_attend<G>), dim3(grid), dim3(AttShape<G>::NT), 0, stream, t);
   prof_mark(stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GSA_ERR_HIP, "gsa_prefill_blocksparse launch: %s", hipGetErrorString(e));
