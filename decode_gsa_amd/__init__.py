@@ -22,6 +22,7 @@ __all__ = [
     "decode_params", "hier_params", "prefill_params",
     "decode_workspace_size", "hier_workspace_size", "prefill_workspace_size", "new_workspace",
     "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse", "gsa_profile_events",
+    "gsa_profile_marks",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -30,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "gsa_decode_workspace_size", "gsa_decode",
     "gsa_decode_hier_workspace_size", "gsa_decode_hier",
     "gsa_prefill_workspace_size", "gsa_prefill_blocksparse",
-    "gsa_profile_events", "gsa_status_string", "gsa_last_error",
+    "gsa_profile_events", "gsa_profile_marks", "gsa_status_string", "gsa_last_error",
 )
 
 _c_i32, _c_i64, _c_f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -82,9 +83,10 @@ def lib() -> ctypes.CDLL:
         L.gsa_prefill_blocksparse.argtypes = [P(PrefillParams), _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                               _vp]
         L.gsa_profile_events.argtypes = [P(_vp), _c_i32]
+        L.gsa_profile_marks.argtypes = [P(_c_i32)]
         for f in ("gsa_decode_workspace_size", "gsa_decode", "gsa_decode_hier_workspace_size",
                   "gsa_decode_hier", "gsa_prefill_workspace_size", "gsa_prefill_blocksparse",
-                  "gsa_profile_events"):
+                  "gsa_profile_events", "gsa_profile_marks"):
             getattr(L, f).restype = _c_i32
         L.gsa_status_string.argtypes = [_c_i32]
         L.gsa_status_string.restype = ctypes.c_char_p
@@ -99,6 +101,13 @@ def gsa_profile_events(handles) -> None:
     empty sequence disarms it. See gsa_profile_events in include/gsa.h."""
     arr = (_vp * max(1, len(handles)))(*[_vp(h) for h in handles])
     _check(lib().gsa_profile_events(arr, len(handles)), "gsa_profile_events")
+
+
+def gsa_profile_marks() -> int:
+    """Kernel launches + 1 of the last library call on this thread."""
+    n = _c_i32(0)
+    _check(lib().gsa_profile_marks(ctypes.byref(n)), "gsa_profile_marks")
+    return n.value
 
 
 def _check(status: int, where: str) -> None:

@@ -383,16 +383,12 @@ __device__ __forceinline__ void round_prefix(const uint64_t (&bal)[kSub], int (&
 // prefix plus the first `need` keys equal to it, in item order. Up to 4096
 // keys are staged in LDS once (one round trip); more are re-read in rounds.
 __device__ void block_topk(const float* __restrict__ scores, int n, int k, const IdMap& im, int unit,
-                           int32_t* __restrict__ dst, int32_t* __restrict__ dst2, TopkLds& L) {
+                           int32_t* __restrict__ dst, TopkLds& L) {
   const int tid = threadIdx.x;
   const CohBuf sc(scores, (uint32_t)n * 4u);
   if (k <= 0) return;
   if (k >= n) {
-    for (int i = tid; i < n; i += kThreads) {
-      const int32_t id = map_id(im, unit, i);
-      st_coh(dst + i, id);
-      if (dst2) dst2[i] = id;
-    }
+    for (int i = tid; i < n; i += kThreads) dst[i] = map_id(im, unit, i);
     return;
   }
   const bool in_lds = n <= kSelKeys;
@@ -485,11 +481,7 @@ __device__ void block_topk(const float* __restrict__ scores, int n, int k, const
 #pragma unroll
     for (int q = 0; q < kSub; ++q) {
       const int pos = pre[q];
-      if (pick[q] && pos >= 0 && pos < k) {
-        const int32_t id = map_id(im, unit, b0 + q * kThreads + tid);
-        st_coh(dst + pos, id);
-        if (dst2) dst2[pos] = id;
-      }
+      if (pick[q] && pos >= 0 && pos < k) dst[pos] = map_id(im, unit, b0 + q * kThreads + tid);
     }
   }
 }
@@ -691,7 +683,7 @@ __device__ __forceinline__ void init_state(State<BF16, G>& st) {
   }
 }
 
-// ------------------------------------------------------------ kernels ------
+// -------------------------------------------------------------- tail rows ---
 
 // Cache row of tail item i (position N - T + i) of the interleaved cache.
 __device__ __forceinline__ int64_t tail_row(int64_t i, int64_t N, int32_t T, int64_t M, int32_t C) {
@@ -699,12 +691,181 @@ __device__ __forceinline__ int64_t tail_row(int64_t i, int64_t N, int32_t T, int
   return pos < MC ? (pos / C) * (C + 1) + pos % C : M * (C + 1) + (pos - MC);
 }
 
-// A pass over gist-like rows of every unit: scores + attention partials, plus
-// a share of the tail rows (attended, not scored). Selection of the pass's
-// top-k: for k <= kFastSel each workgroup reduces its scores to its own top-k
-// candidates and the unit's last workgroup merges them; for larger k every
-// score goes out and the last workgroup runs a radix select. With out set the
-// last workgroup also merges the unit's partials (the pass is the last one).
+// ------------------------------------------------------------ selection ----
+
+constexpr int kSelLdsMax = 1024;   // selections staged in LDS by the workgroups that use them
+constexpr int kCandMax = 64;       // candidates above the threshold: one per lane of a wave
+
+struct SelectLds {
+  uint32_t tw[kWaves];             // per-wave lower bounds on the k-th largest key
+  uint32_t ck[kCandMax];           // candidates (key, id), in no particular order
+  uint32_t ci[kCandMax];
+  int cnt;
+};
+
+// The value of lane (lane ^ J). Within a 16-lane row the exchange uses DPP
+// (quad permutes, row shifts, row rotate by 8); across rows a permute.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x104, 0xF, 0xF, false);   // row_shl:4, lane+4
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xF, 0xF, false);   // row_shr:4, lane-4
+    return (threadIdx.x & 4) ? dn : up;
+  } else if constexpr (J == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else {
+    return (uint32_t)__shfl_xor((int)v, J);
+  }
+}
+template <int J>
+__device__ __forceinline__ unsigned long long lane_xor(unsigned long long v) {
+  return ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
+}
+
+// One compare-exchange step of a bitonic network at distance J within blocks of K.
+template <bool DESC, int K, int J, class T>
+__device__ __forceinline__ T bitonic_step(T x) {
+  const int lane = threadIdx.x & 63;
+  const T y = lane_xor<J>(x);
+  const bool seg_desc = ((lane & K) == 0) == DESC;
+  const bool keep_max = ((lane & J) == 0) == seg_desc;
+  return keep_max ? (x > y ? x : y) : (x < y ? x : y);
+}
+template <bool DESC, int K, int J, class T>
+__device__ __forceinline__ T bitonic_stage(T x) {
+  x = bitonic_step<DESC, K, J>(x);
+  if constexpr (J > 1) x = bitonic_stage<DESC, K, J / 2>(x);
+  return x;
+}
+template <bool DESC, int K, class T>
+__device__ __forceinline__ T bitonic_from(T x) {
+  x = bitonic_stage<DESC, K, K / 2>(x);
+  if constexpr (K < 64) x = bitonic_from<DESC, K * 2>(x);
+  return x;
+}
+
+// Bitonic sort of one value per lane over the wave's 64 lanes, descending
+// (lane 0 largest) or ascending.
+template <bool DESC, class T>
+__device__ __forceinline__ T wave_sort(T x) {
+  return bitonic_from<DESC, 2>(x);
+}
+
+// Exact top-k (ties to the smaller id) of the n scores sc[0..n) of one unit,
+// written by an earlier launch; ids through im. The k ids go, ascending, to
+// dst (LDS or global). Every thread of the workgroup calls it; dst is valid
+// after the caller's next barrier.
+// k <= kFastSel: thread t owns scores [t*per, (t+1)*per). In each wave the
+// k-th largest of its 64 per-thread maxima bounds the unit's k-th largest
+// score from below (those maxima are k distinct scores); tau is the largest
+// of the four bounds. The scores >= tau (at least k) are gathered and, if at
+// most 64, wave 0 sorts them by (score, smaller id first), keeps k and sorts
+// their ids. More candidates (heavy ties) or a larger k take the block-wide
+// radix select.
+__device__ void unit_topk(const float* __restrict__ sc, int n, int k, const IdMap& im, int unit,
+                          int32_t* __restrict__ dst, SelectLds& S, TopkLds& T,
+                          const float* __restrict__ lds_sc = nullptr) {
+  if (k <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (k >= n) {
+    for (int i = tid; i < n; i += kThreads) dst[i] = map_id(im, unit, i);
+    return;
+  }
+  if (k > kFastSel) {
+    block_topk(sc, n, k, im, unit, dst, T);
+    return;
+  }
+  const int per = (n + kThreads - 1) / kThreads;
+  const int i0 = tid * per, i1 = min(n, i0 + per);
+  // this thread's keys, kPer at a time with every load of a round in flight
+  // (device-scope loads: the scores may come from other workgroups of this launch)
+  constexpr int kPer = 8;
+  // (lds_sc: the same scores already in this workgroup's LDS)
+  const CohBuf scb(sc, (uint32_t)n * 4u);
+  auto keys_at = [&](int r0, uint32_t (&kv)[kPer]) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      kv[j] = r0 + j < i1 ? order_key(lds_sc ? lds_sc[r0 + j] : __uint_as_float(scb.u32(r0 + j))) : 0u;
+  };
+  uint32_t kv[kPer];
+  keys_at(i0, kv);
+  uint32_t mx = 0u;
+  for (int r0 = i0;; ) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) mx = max(mx, kv[j]);
+    r0 += kPer;
+    if (r0 >= i1) break;
+    keys_at(r0, kv);
+  }
+  const uint32_t sorted = wave_sort<true>(mx);
+  const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)sorted, k - 1);
+  if (lane == 0) S.tw[w] = tw;
+  if (tid == 0) S.cnt = 0;
+  __syncthreads();
+  uint32_t tau = S.tw[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) tau = max(tau, S.tw[i]);
+  const bool one_round = per <= kPer;   // then kv still holds every key of this thread
+  int c = 0;
+  if (one_round) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) c += kv[j] >= tau ? 1 : 0;   // 0 (no item) < tau unless tau = 0
+    if (tau == 0u) c = i1 > i0 ? i1 - i0 : 0;
+  } else {
+    for (int r0 = i0; r0 < i1; r0 += kPer) {
+      keys_at(r0, kv);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) c += (kv[j] >= tau && r0 + j < i1) ? 1 : 0;
+    }
+  }
+  int pos = c > 0 ? atomicAdd(&S.cnt, c) : 0;
+  for (int r0 = i0; r0 < i1; r0 += kPer) {
+    if (!one_round) keys_at(r0, kv);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (kv[j] >= tau && r0 + j < i1) {
+        if (pos < kCandMax) {
+          S.ck[pos] = kv[j];
+          S.ci[pos] = (uint32_t)map_id(im, unit, r0 + j);
+        }
+        ++pos;
+      }
+    }
+  }
+  __syncthreads();
+  const int total = S.cnt;
+  if (total > kCandMax) {   // uniform: heavy ties at the threshold
+    if (lds_sc) {             // the radix select reads the scores from memory
+      float* scw = const_cast<float*>(sc);
+      for (int i = tid; i < n; i += kThreads) scw[i] = lds_sc[i];
+      done_stores();
+    }
+    __syncthreads();
+    block_topk(sc, n, k, im, unit, dst, T);
+    return;
+  }
+  if (w == 0) {
+    typedef unsigned long long u64;
+    u64 key = lane < total ? (((u64)S.ck[lane] << 32) | (u64)(~S.ci[lane])) : 0ull;
+    key = wave_sort<true>(key);                       // best first; equal scores: smaller id first
+    uint32_t id = lane < k ? ~(uint32_t)key : 0xFFFFFFFFu;
+    id = wave_sort<false>(id);                        // the k ids ascending
+    if (lane < k) dst[lane] = (int32_t)id;
+  }
+}
+
+// ------------------------------------------------------------ kernels ------
+
+// A pass over gist-like rows of every unit: the group score of every item
+// (for the selection made by the next launch) and one attention partial per
+// workgroup, plus a share of the tail rows (attended, not scored). With out
+// set (the call's last pass) the unit's last workgroup merges the partials.
+// Candidate passes of a two-level call first select the unit's level-2
+// groups from the previous pass's scores.
 struct GistArgs {
   const void* q;
   const void* K;
@@ -713,23 +874,22 @@ struct GistArgs {
   int64_t n_items;        // items per unit
   int64_t per_task;       // items per workgroup
   int32_t tasks;          // workgroups per unit
-  RowMap rm;
+  RowMap rm;              // kind 2: rm.sel2 unused (the selection is made here)
   // tail rows, from the interleaved cache Kt/Vt
   const void* Kt;
   const void* Vt;
   int64_t tail_unit_rows;
   int64_t N, M;
   int32_t C, T, tail_per_task;
-  // selection
-  int32_t sel_k;
-  IdMap im;
-  float* scores;          // [units][score_stride] (k > kFastSel)
+  float* scores;          // [units][score_stride] or null (no later selection)
   int64_t score_stride;
-  uint32_t* cand;         // [units][cand_stride] words: tasks * k keys (k <= kFastSel)
-  int64_t cand_stride;
-  int32_t* sel_ws;        // [units][sel_stride]
-  int64_t sel_stride;
-  int32_t* sel_out;       // [units][sel_k] or null
+  // kind 2: level-2 selection from the previous pass's scores
+  const float* prev_scores;
+  int64_t prev_stride;
+  int32_t prev_n, prev_k;
+  int32_t* sel2_ws;       // [units][sel2_stride] (for the unfold pass' ids)
+  int64_t sel2_stride;
+  int32_t* sel2_out;      // [units][prev_k] or null
   // partial softmax states
   float* part;            // [units][NP][part_stride]
   int64_t part_stride;
@@ -739,25 +899,52 @@ struct GistArgs {
   uint32_t* cnt;          // unit u's counter at cnt[u * kCtrlUnitWords]
   float scale_log2;       // softmax logits in log2 units
   float score_mul;        // group score = sum_h(q_h . k) * score_mul
+  // single-level decode with k > 0: the unit's last workgroup selects the
+  // top-k chunks from this pass's scores for the unfold launch
+  int32_t fuse_k;
+  int32_t* sel_ws;        // [units][sel_stride] (k > kSelLdsMax: the selection lives here)
+  int64_t sel_stride;
+  int32_t* sel_out;       // [units][k] or null
 };
 
 template <int D, int G>
 struct GistLds {
   float scores[kTaskScores];   // this workgroup's scores
-  uint32_t xs[2][64];          // wave 0's selection scratch
+  int32_t sel2[kSelLdsMax];    // kind 2: the unit's level-2 selection; fused: the chunk selection
   union {
     PartLds<D, G> part;
-    TopkLds topk;
+    struct {
+      SelectLds s;
+      TopkLds t;
+    } sel;
   } u;
 };
 
+// At least 4 waves per SIMD: the rare selection code must not cost the
+// streaming loop its occupancy.
 template <bool BF16, int D, int G>
-__global__ __launch_bounds__(kThreads) void gist_kernel(GistArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : 2, 8)))
+void gist_kernel(GistArgs a) {
   using Gm = Geo<BF16, D>;
   __shared__ GistLds<D, G> lds;
   __shared__ uint32_t s_old;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x;
   const int unit = blockIdx.x / a.tasks, split = blockIdx.x % a.tasks;
+  RowMap rm = a.rm;
+  if (rm.kind == 2) {
+    // the unit's level-2 groups (every workgroup of the unit makes the same selection)
+    unit_topk(a.prev_scores + (size_t)unit * a.prev_stride, a.prev_n, a.prev_k, IdMap{nullptr, 0, 0, 0, 0},
+              unit, lds.sel2, lds.u.sel.s, lds.u.sel.t);
+    __syncthreads();
+    if (split == 0)
+      for (int i = tid; i < a.prev_k; i += kThreads) {
+        a.sel2_ws[(size_t)unit * a.sel2_stride + i] = lds.sel2[i];
+        if (a.sel2_out) a.sel2_out[(size_t)unit * a.prev_k + i] = lds.sel2[i];
+      }
+    rm.sel2 = lds.sel2;
+    rm.sel2_stride = 0;
+    __syncthreads();   // LDS changes role: selection scratch -> partial merge
+  }
   uint4 qv[G];
   load_q<BF16, D, G>(a.q, unit, qv);
   State<BF16, G> st;
@@ -765,10 +952,9 @@ __global__ __launch_bounds__(kThreads) void gist_kernel(GistArgs a) {
   const size_t ub = (size_t)unit * (size_t)a.unit_rows * Gm::ROW_BYTES;
   const int64_t i0 = (int64_t)split * a.per_task;
   const int64_t i1 = i0 + a.per_task < a.n_items ? i0 + a.per_task : a.n_items;
-  const RowMap rm = a.rm;
   stream_rows<BF16, D, G, false>(reinterpret_cast<const char*>(a.K) + ub,
                                  reinterpret_cast<const char*>(a.V) + ub, i0, i1,
-                                 [&](int64_t i) { return map_row(rm, unit, i); }, qv, st,
+                                 [&](int64_t i) { return map_row(rm, 0, i); }, qv, st,
                                  a.scale_log2, lds.scores, a.score_mul);
   // this workgroup's share of the tail
   const int64_t t0 = (int64_t)split * a.tail_per_task;
@@ -782,86 +968,49 @@ __global__ __launch_bounds__(kThreads) void gist_kernel(GistArgs a) {
                                    [&](int64_t i) { return tail_row(i, N, T, M, C); }, qv, st,
                                    a.scale_log2, nullptr, 0.f);
   }
-  const int nw = (int)(i1 > i0 ? i1 - i0 : 0);
+  __syncthreads();
+  if (a.scores != nullptr) {
+    // scores out for the selection (device-scope stores: the unit's last
+    // workgroup or the next launch reads them)
+    float* so = a.scores + (size_t)unit * a.score_stride + i0;
+    for (int64_t i = tid; i < i1 - i0; i += kThreads) st_coh(so + i, lds.scores[i]);
+  }
   float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
   write_partial<BF16, D, G>(st, part_u + (size_t)(a.part_base + split) * a.part_stride, lds.u.part, false);
-  uint32_t* ctr = a.cnt + (size_t)unit * kCtrlUnitWords;
-
-  if (a.sel_k > kFastSel) {
-    // every score out (contiguous device-scope stores), radix select in the last workgroup
-    float* so = a.scores + (size_t)unit * a.score_stride + i0;
-    for (int i = tid; i < nw; i += kThreads) st_coh(so + i, lds.scores[i]);
-    if (arrive_last(ctr, (uint32_t)a.tasks, &s_old)) {
-      __syncthreads();   // LDS changes role: partial merge -> selection
-      block_topk(a.scores + (size_t)unit * a.score_stride, (int)a.n_items, a.sel_k, a.im, unit,
-                 a.sel_ws + (size_t)unit * a.sel_stride,
-                 a.sel_out ? a.sel_out + (size_t)unit * a.sel_k : nullptr, lds.u.topk);
-      if (a.out != nullptr)
-        merge_unit<D, G>(part_u, a.NP, (uint32_t)a.part_stride, a.out + (size_t)unit * G * D,
-                         a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
-    }
-    return;
-  }
-
-  // k <= kFastSel: wave 0 alone finishes the workgroup (the other waves leave
-  // once their partial stores have completed)
-  done_stores();
-  __syncthreads();   // scores in LDS; every wave's partial stores done
-  if (w != 0) return;
-  if (a.sel_k > 0) {
-    // this workgroup's top-k candidates (key, id), in id order; unused slots
-    // get key 0 (no item)
-    const IdMap im = a.im;
-    uint32_t rk, ri;
-    wave_select(nw, a.sel_k,
-                [&](int i, uint32_t& key, uint32_t& id) {
-                  key = i < nw ? order_key(lds.scores[i]) : 0u;
-                  id = i < nw ? (uint32_t)map_id(im, unit, (int32_t)(i0 + i)) : 0u;
-                },
-                lds.xs, rk, ri);
-    if (lane < a.sel_k) {
-      uint32_t* cb = a.cand + (size_t)unit * a.cand_stride + 2u * ((size_t)split * a.sel_k + lane);
-      st_coh(reinterpret_cast<int32_t*>(cb), (int32_t)rk);
-      st_coh(reinterpret_cast<int32_t*>(cb + 1), (int32_t)ri);
-    }
-  }
-  // count this workgroup finished (wave 0's stores complete first)
-  done_stores();
-  uint32_t old = 0u;
-  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0);
-  if (old != (uint32_t)a.tasks - 1u) return;
-  if (lane == 0) ctrl_set(ctr, 0u);
-  if (a.sel_k > 0) {
-    // merge the candidates of every workgroup of the unit (split order = id order)
-    const int n = a.tasks * a.sel_k;
-    const CohBuf cb(a.cand + (size_t)unit * a.cand_stride, (uint32_t)n * 8u);
-    uint32_t rk, ri;
-    wave_select(n, a.sel_k,
-                [&](int i, uint32_t& key, uint32_t& id) {   // past n the buffer returns 0
-                  key = cb.u32(2u * (uint32_t)i);
-                  id = cb.u32(2u * (uint32_t)i + 1u);
-                },
-                lds.xs, rk, ri);
-    if (lane < a.sel_k) {
-      st_coh(a.sel_ws + (size_t)unit * a.sel_stride + lane, (int32_t)ri);
-      if (a.sel_out) a.sel_out[(size_t)unit * a.sel_k + lane] = (int32_t)ri;
-    }
+  if (a.out == nullptr && a.fuse_k == 0) return;
+  if (!arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)a.tasks, &s_old)) return;
+  if (a.fuse_k > 0) {
+    // the unit's selection, for the unfold launch
+    __syncthreads();   // LDS changes role: partial merge -> selection
+    const int k = a.fuse_k;
+    int32_t* us = a.sel_ws + (size_t)unit * a.sel_stride;
+    unit_topk(a.scores + (size_t)unit * a.score_stride, (int)a.n_items, k, IdMap{nullptr, 0, 0, 0, 0}, unit, us,
+              lds.u.sel.s, lds.u.sel.t);
+    __syncthreads();
+    if (a.sel_out)
+      for (int i = tid; i < k; i += kThreads) a.sel_out[(size_t)unit * k + i] = us[i];
   }
   if (a.out != nullptr)
     merge_unit<D, G>(part_u, a.NP, (uint32_t)a.part_stride, a.out + (size_t)unit * G * D,
-                     a.lse ? a.lse + (size_t)unit * G : nullptr, 1);
+                     a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
 }
 
-// Raw rows of the selected chunks (minus rows the tail owns); the unit's last
-// workgroup merges every partial into out and lse.
+// Raw rows of the selected chunks (minus rows the tail owns); every workgroup
+// first makes the unit's selection from the previous pass's scores, and the
+// unit's last workgroup merges every partial into out and lse.
 struct UnfoldArgs {
   const void* q;
   const void* K;
   const void* V;
   int64_t unit_rows;
-  const int32_t* sel;     // [units][sel_stride] chosen chunks (earlier launch)
+  const float* scores;    // [units][score_stride] the previous pass's scores, or null:
+                          // the selection is ready in sel_ws
+  int64_t score_stride;
+  int32_t n_cand;         // scores per unit
+  IdMap im;               // score index -> chunk id
+  int32_t* sel_ws;        // [units][sel_stride] (k > kSelLdsMax: the selection lives here)
   int64_t sel_stride;
+  int32_t* sel_out;       // [units][k] or null
   int32_t k;
   int32_t C, T;
   int64_t M, N;
@@ -877,11 +1026,15 @@ struct UnfoldArgs {
 };
 
 template <int D, int G>
-union UnfoldLds {
-  struct {
-    int32_t sel[kSelLds];
-  } s;
-  PartLds<D, G> part;
+struct UnfoldLds {
+  int32_t sel[kSelLdsMax];
+  union {
+    PartLds<D, G> part;
+    struct {
+      SelectLds s;
+      TopkLds t;
+    } sel;
+  } u;
 };
 
 template <bool BF16, int D, int G>
@@ -891,11 +1044,20 @@ __global__ __launch_bounds__(kThreads) void unfold_kernel(UnfoldArgs a) {
   __shared__ uint32_t s_old;
   const int tid = threadIdx.x;
   const int unit = blockIdx.x / a.tasks, split = blockIdx.x % a.tasks;
-  const int32_t* us = a.sel + (size_t)unit * a.sel_stride;
-  const bool in_lds = a.k <= kSelLds;
-  if (in_lds)
-    for (int i = tid; i < a.k; i += kThreads) lds.s.sel[i] = us[i];
-  __syncthreads();
+  const bool in_lds = a.k <= kSelLdsMax;
+  int32_t* us = in_lds ? lds.sel : a.sel_ws + (size_t)unit * a.sel_stride;
+  if (a.scores != nullptr) {
+    // make the unit's selection from the previous pass's scores
+    unit_topk(a.scores + (size_t)unit * a.score_stride, a.n_cand, a.k, a.im, unit, us, lds.u.sel.s, lds.u.sel.t);
+    __syncthreads();
+    if (split == 0 && a.sel_out)
+      for (int i = tid; i < a.k; i += kThreads) a.sel_out[(size_t)unit * a.k + i] = us[i];
+  } else if (in_lds) {
+    // the previous launch made it
+    const int32_t* ws_sel = a.sel_ws + (size_t)unit * a.sel_stride;
+    for (int i = tid; i < a.k; i += kThreads) lds.sel[i] = ws_sel[i];
+    __syncthreads();
+  }
   uint4 qv[G];
   load_q<BF16, D, G>(a.q, unit, qv);
   State<BF16, G> st;
@@ -906,11 +1068,10 @@ __global__ __launch_bounds__(kThreads) void unfold_kernel(UnfoldArgs a) {
   // 32-bit index math: items < 2^30
   const uint32_t C = (uint32_t)a.C;
   const int64_t M = a.M, tail0 = a.N - a.T;
-  const int32_t* s_sel = lds.s.sel;
   auto row_of = [&](int64_t i64) -> int64_t {
     const uint32_t i = (uint32_t)i64;
     const uint32_t ci = i / C, j = i - ci * C;
-    const int64_t m = in_lds ? s_sel[ci] : us[ci];
+    const int64_t m = us[ci];
     if (m < 0 || m >= M) return -1;         // never taken for a valid selection
     if (m * C + j >= tail0) return -1;      // the tail attends this row
     return m * (C + 1) + j;
@@ -919,8 +1080,8 @@ __global__ __launch_bounds__(kThreads) void unfold_kernel(UnfoldArgs a) {
                                 reinterpret_cast<const char*>(a.V) + ub, i0, i1, row_of, qv, st,
                                 a.scale_log2, nullptr, 0.f);
   float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
-  __syncthreads();   // LDS changes role: selected ids -> partial merge
-  write_partial<BF16, D, G>(st, part_u + (size_t)(a.part_base + split) * a.part_stride, lds.part, false);
+  __syncthreads();   // LDS changes role: selection scratch -> partial merge
+  write_partial<BF16, D, G>(st, part_u + (size_t)(a.part_base + split) * a.part_stride, lds.u.part, false);
   if (arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)a.tasks, &s_old))
     merge_unit<D, G>(part_u, a.NP, (uint32_t)a.part_stride, a.out + (size_t)unit * G * D,
                      a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
@@ -943,6 +1104,7 @@ template <bool BF16, int D, int G>
 gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, const void* V,
                         float* out, float* lse, int32_t* sel_idx, char* ws, hipStream_t st) {
   float* part = reinterpret_cast<float*>(ws + pl.off_part);
+  float* scores = reinterpret_cast<float*>(ws + pl.off_scores);
   int32_t* wsel = reinterpret_cast<int32_t*>(ws + pl.off_sel);
   const int64_t ps = part_stride(G, D);
   GistArgs g{};
@@ -951,14 +1113,13 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
   g.rm = RowMap{0, pl.C, nullptr, 0, 0, 0, 0};
   g.Kt = K; g.Vt = V; g.tail_unit_rows = pl.R;
   g.N = pl.N; g.M = pl.M; g.C = pl.C; g.T = pl.T; g.tail_per_task = pl.tail_per_split;
-  g.sel_k = pl.k; g.im = IdMap{nullptr, 0, 0, 0, 0};
-  g.scores = reinterpret_cast<float*>(ws + pl.off_scores); g.score_stride = pl.score_stride;
-  g.cand = reinterpret_cast<uint32_t*>(ws + pl.off_cand); g.cand_stride = pl.cand_stride;
-  g.sel_ws = wsel; g.sel_stride = pl.sel_stride; g.sel_out = sel_idx;
+  g.scores = pl.k > 0 ? scores : nullptr; g.score_stride = pl.score_stride;
   g.part = part; g.part_stride = ps; g.NP = pl.NP; g.part_base = 0;
   g.out = pl.k > 0 ? nullptr : out; g.lse = pl.k > 0 ? nullptr : lse;
   g.cnt = ctrl_of(ws, pl.off_ctrl, 0);
   g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
+  g.fuse_k = pl.k;
+  g.sel_ws = wsel; g.sel_stride = pl.sel_stride; g.sel_out = sel_idx;
   prof_begin_call();
   prof_mark(st);
   hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st, g);
@@ -966,7 +1127,8 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
   if (pl.k > 0) {
     UnfoldArgs u{};
     u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
-    u.sel = wsel; u.sel_stride = pl.sel_stride; u.k = pl.k;
+    u.scores = nullptr;
+    u.sel_ws = wsel; u.sel_stride = pl.sel_stride; u.sel_out = nullptr; u.k = pl.k;
     u.C = pl.C; u.T = pl.T; u.M = pl.M; u.N = pl.N;
     u.n_items = pl.n_items; u.per_task = pl.items_per_split; u.tasks = pl.S2;
     u.part = part; u.part_stride = ps; u.NP = pl.NP; u.part_base = pl.S;
@@ -984,41 +1146,39 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
                       const void* K2, const void* V2, float* out, float* lse, int32_t* sel2,
                       int32_t* sel1, char* ws, hipStream_t st) {
   const DecodePlan& pl = hp.base;
+  float* s2 = reinterpret_cast<float*>(ws + hp.off_s2);
+  float* sc = reinterpret_cast<float*>(ws + hp.off_sc);
   int32_t* wsel2 = reinterpret_cast<int32_t*>(ws + hp.off_sel2);
-  int32_t* wsel1 = reinterpret_cast<int32_t*>(ws + hp.off_sel1);
   float* part = reinterpret_cast<float*>(ws + hp.off_part);
   const int64_t ps = part_stride(G, D);
   const int64_t orphan0 = hp.M2 * hp.G;
-  // level 2: every meta-gist (dense rows of the level-2 array) and the tail,
-  // top-k2 groups
+  // level 2: every meta-gist (dense rows of the level-2 array) and the tail
   GistArgs g{};
   g.q = q; g.K = K2; g.V = V2;
   g.unit_rows = hp.M2; g.n_items = hp.M2; g.per_task = hp.l2_per_split; g.tasks = hp.S_l2;
   g.rm = RowMap{1, pl.C, nullptr, 0, 0, 0, 0};
   g.Kt = K; g.Vt = V; g.tail_unit_rows = pl.R;
   g.N = pl.N; g.M = pl.M; g.C = pl.C; g.T = pl.T; g.tail_per_task = hp.tail_per_split;
-  g.sel_k = hp.k2; g.im = IdMap{nullptr, 0, 0, 0, 0};
-  g.scores = reinterpret_cast<float*>(ws + hp.off_s2); g.score_stride = hp.s2_stride;
-  g.cand = reinterpret_cast<uint32_t*>(ws + hp.off_cand2); g.cand_stride = hp.cand2_stride;
-  g.sel_ws = wsel2; g.sel_stride = hp.sel2_stride; g.sel_out = sel2;
+  g.scores = s2; g.score_stride = hp.s2_stride;
   g.part = part; g.part_stride = ps; g.NP = hp.NP; g.part_base = 0;
   g.out = nullptr; g.lse = nullptr;
   g.cnt = ctrl_of(ws, hp.off_ctrl, 0);
   g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
+  g.fuse_k = 0;
   prof_begin_call();
   prof_mark(st);
   hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_l2), dim3(kThreads), 0, st, g);
   prof_mark(st);
-  // level 1: children of the chosen groups + the ungrouped gists, top-k1 chunks
+  // level 1: select the groups, then score and attend their children and the
+  // ungrouped gists
   GistArgs c = g;
   c.K = K; c.V = V;
   c.unit_rows = pl.R; c.n_items = hp.n_cand; c.per_task = hp.cand_per_split; c.tasks = hp.S_c;
-  c.rm = RowMap{2, pl.C, wsel2, hp.G, hp.k2, orphan0, hp.sel2_stride};
+  c.rm = RowMap{2, pl.C, nullptr, hp.G, hp.k2, orphan0, 0};
   c.T = 0; c.tail_per_task = 0;
-  c.sel_k = pl.k; c.im = IdMap{wsel2, hp.G, hp.k2, orphan0, hp.sel2_stride};
-  c.scores = reinterpret_cast<float*>(ws + hp.off_sc); c.score_stride = hp.sc_stride;
-  c.cand = reinterpret_cast<uint32_t*>(ws + hp.off_cand1); c.cand_stride = hp.cand1_stride;
-  c.sel_ws = wsel1; c.sel_stride = pl.sel_stride; c.sel_out = sel1;
+  c.scores = pl.k > 0 ? sc : nullptr; c.score_stride = hp.sc_stride;
+  c.prev_scores = s2; c.prev_stride = hp.s2_stride; c.prev_n = (int32_t)hp.M2; c.prev_k = hp.k2;
+  c.sel2_ws = wsel2; c.sel2_stride = hp.sel2_stride; c.sel2_out = sel2;
   c.part_base = hp.S_l2;
   c.out = pl.k > 0 ? nullptr : out; c.lse = pl.k > 0 ? nullptr : lse;
   c.cnt = ctrl_of(ws, hp.off_ctrl, 1);
@@ -1028,7 +1188,10 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   if (pl.k > 0) {
     UnfoldArgs u{};
     u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
-    u.sel = wsel1; u.sel_stride = pl.sel_stride; u.k = pl.k;
+    u.scores = sc; u.score_stride = hp.sc_stride; u.n_cand = hp.n_cand;
+    u.im = IdMap{wsel2, hp.G, hp.k2, orphan0, hp.sel2_stride};
+    u.sel_ws = reinterpret_cast<int32_t*>(ws + hp.off_sel1); u.sel_stride = pl.sel_stride;
+    u.sel_out = sel1; u.k = pl.k;
     u.C = pl.C; u.T = pl.T; u.M = pl.M; u.N = pl.N;
     u.n_items = pl.n_items; u.per_task = pl.items_per_split; u.tasks = pl.S2;
     u.part = part; u.part_stride = ps; u.NP = hp.NP; u.part_base = hp.S_l2 + hp.S_c;
@@ -1039,6 +1202,353 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
     prof_mark(st);
   }
   return launch_status("gsa_decode_hier launch");
+}
+
+
+// ===================================================== one workgroup per unit
+//
+// bf16, D = 128, one workgroup per (batch, kv-head) unit when there are enough
+// units to fill the chip: the whole decode step of a unit -- every gist and
+// tail row, the selection, the chosen chunks' raw rows and the merge -- with
+// no hand-off through memory. Each of the four waves streams its own share of
+// rows, 16 at a time, through a private ring of LDS stages filled by
+// direct-to-LDS loads three stages ahead, and folds them in on MFMA:
+//   S^T = K Q^T     16x16x32: A = 16 K rows (LDS, 16-byte reads), B = the g
+//                   query heads padded to 16 columns with zeros;
+//   O^T += V^T P^T  16x16x16: A = V^T read transposed (ds_read_b64_tr_b16),
+//                   B = the softmax weights, split into bf16 hi + lo.
+// Lane (h = lane%16, j = lane/16) holds head h's logits of rows 4j..4j+3 of a
+// stage, exactly the B operand of the second product; the sum over the 16
+// lanes of a row (DPP) is that row's group score (heads past g add 0).
+
+constexpr int kUW = 4;                  // waves per unit workgroup
+constexpr int kUBR = 16;                // rows per stage
+constexpr int kUNB = 4;                 // stages in a wave's ring
+constexpr int kUTile = kUBR * 256;      // one stage's K (or V) rows
+constexpr int kUStage = 2 * kUTile;
+constexpr int kUMaxGist = 4096;         // group scores kept in LDS
+constexpr int kUMinUnits = 256;         // units needed to fill the chip
+static_assert(kUW == kWaves, "the selection helpers assume the workgroup size");
+
+typedef __bf16 bf16x8u __attribute__((ext_vector_type(8)));
+typedef float f32x4u __attribute__((ext_vector_type(4)));
+typedef short i16x4u __attribute__((ext_vector_type(4)));
+
+template <int N>
+__device__ __forceinline__ void uwait_vm() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16-byte chunk c of stage row r sits in LDS slot uk_slot (K) / uv_slot (V):
+// conflict-free K-fragment reads and transposed V reads.
+__device__ __forceinline__ int uk_slot(int c, int r) { return c ^ (r & 15); }
+__device__ __forceinline__ int uv_slot(int c, int r) { return c ^ (2 * (r & 7)); }
+
+// The K operands of a stage (four 16-byte reads), waiting for them in the same
+// asm block: the compiler does not see these LDS reads, so it adds no wait for
+// the direct-to-LDS loads still in flight.
+__device__ __forceinline__ void u_k_frag(const uint32_t (&addr)[4], bf16x8u (&kf)[4]) {
+  uint4 a0, a1, a2, a3;
+  __asm__ volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3)
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3])
+      : "memory");
+  kf[0] = __builtin_bit_cast(bf16x8u, a0);
+  kf[1] = __builtin_bit_cast(bf16x8u, a1);
+  kf[2] = __builtin_bit_cast(bf16x8u, a2);
+  kf[3] = __builtin_bit_cast(bf16x8u, a3);
+}
+
+// The V^T operands of a stage for the eight 16-column blocks of d.
+__device__ __forceinline__ void u_v_frag(const uint32_t (&addr)[8], i16x4u (&vf)[8]) {
+  __asm__ volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3]), "=&v"(vf[4]), "=&v"(vf[5]), "=&v"(vf[6]),
+        "=&v"(vf[7])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+        "v"(addr[7])
+      : "memory");
+}
+
+struct UnitArgs {
+  const void* q;          // [B][Hq][D] bf16
+  const void* K;          // [B][Hkv][R][D]
+  const void* V;
+  float* out;             // [B][Hq][D]
+  float* lse;             // [B][Hq] or null
+  int32_t* sel;           // [B][Hkv][k] or null
+  float* scores;          // [units][score_stride] workspace (selection fallback)
+  int64_t score_stride;
+  int64_t R, N, M;
+  int32_t C, k, T;
+  float scale_log2;       // softmax logits in log2 units
+  float score_mul;        // group score = sum_h(q_h . k) * score_mul
+};
+
+struct UnitLds {
+  union {
+    char ring[kUW][kUNB][kUStage];      // streaming
+    struct {                            // selection (rings idle)
+      SelectLds s;
+      TopkLds t;
+    } sel;
+    struct {                            // merge of the waves' states
+      float m[kUW][16], l[kUW][16];
+      float o[kUW][16][128];
+    } mrg;
+  } u;
+  float scores[kUMaxGist];
+  int32_t sel[kFastSel];
+};
+
+// One wave's running softmax state: lane (h, j) holds head h's max and its
+// share of the sum, and O^T[16 dt + 4 j + r][h] in o[dt][r].
+struct UState {
+  f32x4u o[8];
+  float m, l;
+};
+
+// Stream items [i0, i1) through the wave's state. FIRST: items below M are
+// the gists (group scores kept in LDS), the rest the tail rows; otherwise the
+// raw rows of the selected chunks, skipping those the tail attends.
+template <bool FIRST>
+__device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const char* __restrict__ Vb, int i0,
+                                            int i1, const UnitArgs& a, const bf16x8u (&qf)[4], UState& st,
+                                            char* ring, float* lds_scores, const int32_t* lds_sel) {
+  const int n = i1 - i0;
+  if (n <= 0) return;
+  const int lane = threadIdx.x & 63;
+  const int hq = lane & 15, jg = lane >> 4;
+  const int nb = (n + kUBR - 1) / kUBR;
+  const int C = a.C, M = (int)a.M;
+  const unsigned tail0 = (unsigned)(a.N - a.T);   // rows and positions fit in 31 bits here
+  // cache row of item i; -1 when there is no such item or the tail owns it.
+  // Raw position p sits in row p + p / C (p + M past the last gist).
+  auto row_of = [&](int i) -> int {
+    if (i >= i1) return -1;
+    if (FIRST) {
+      if (i < M) return i * (C + 1) + C;
+      const unsigned pos = tail0 + (unsigned)(i - M);
+      return (int)(pos + min(pos / (unsigned)C, (unsigned)M));
+    }
+    const unsigned ci = (unsigned)i / (unsigned)C, jj = (unsigned)i - ci * (unsigned)C;
+    const unsigned m = min((unsigned)lds_sel[ci], (unsigned)(M - 1));   // k <= M, so M >= 1
+    const unsigned pos = m * (unsigned)C + jj;
+    return pos >= tail0 ? -1 : (int)(pos + m);
+  };
+  // stage b -> ring slot b % kUNB: lane i loads 16 bytes of row 4u + i/16 into
+  // LDS slot i%16, K and V alike. Items past the end read row 0 (in bounds,
+  // discarded), so that every stage issues the same eight loads.
+  auto issue = [&](int b) {
+    char* kd = ring + (b % kUNB) * kUStage;
+    char* vd = kd + kUTile;
+    const int sl = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = 4 * u + (lane >> 4);
+      const int row = row_of(i0 + b * kUBR + r);
+      const int64_t off = (int64_t)(row >= 0 ? row : 0) * 256;
+      __builtin_amdgcn_global_load_lds(Kb + off + uk_slot(sl, r) * 16, kd + u * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Vb + off + uv_slot(sl, r) * 16, vd + u * 1024, 16, 0, 0);
+    }
+  };
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)ring;
+  // per-lane LDS offsets within a stage
+  uint32_t koff[4], voff[8];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) koff[ks] = hq * 256 + uk_slot(4 * ks + jg, hq) * 16;
+  {
+    // transposed read: lane s of 16-lane group j fetches 4 columns of row
+    // 4j + s/4, so that lane m receives column m of rows 4j..4j+3
+    const int R = 4 * jg + (hq >> 2);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      voff[dt] = kUTile + R * 256 + uv_slot(2 * dt + ((hq & 3) >> 1), R) * 16 + 8 * (hq & 1);
+  }
+  auto compute = [&](int b) {
+    const uint32_t base = ring_lds + (b % kUNB) * kUStage;
+    uint32_t ka[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) ka[ks] = base + koff[ks];
+    bf16x8u kf[4];
+    u_k_frag(ka, kf);
+    f32x4u s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+    // s[r]: head hq against stage row 4 jg + r
+    const int i_base = i0 + b * kUBR + 4 * jg;
+    bool ok[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ok[r] = FIRST ? i_base + r < i1 : row_of(i_base + r) >= 0;
+    if (FIRST) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float g = group_sum<16>(s[r]);
+        if (hq == 0 && i_base + r < i1 && i_base + r < M) lds_scores[i_base + r] = g * a.score_mul;
+      }
+    }
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = ok[r] ? s[r] * a.scale_log2 : -INFINITY;
+    const float cand = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__ballot(cand > st.m + kLazy) != 0ull) {
+      // raise head h's max on its four lanes (j = 0..3) and rescale
+      float c4 = fmaxf(cand, __shfl_xor(cand, 16));
+      c4 = fmaxf(c4, __shfl_xor(c4, 32));
+      const float mn = c4 > st.m + kLazy ? c4 : st.m;
+      const float al = fexp2(st.m - mn);
+      st.m = mn;
+      st.l *= al;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st.o[dt][r] *= al;
+    }
+    i16x4u phi, plo;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = fexp2(x[r] - st.m);
+      st.l += p;
+      const __bf16 hi = (__bf16)p;
+      const __bf16 lo = (__bf16)(p - (float)hi);
+      phi[r] = __builtin_bit_cast(short, hi);
+      plo[r] = __builtin_bit_cast(short, lo);
+    }
+    uint32_t va[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) va[dt] = base + voff[dt];
+    i16x4u vf[8];
+    u_v_frag(va, vf);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[dt], phi, st.o[dt], 0, 0, 0);
+      st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[dt], plo, st.o[dt], 0, 0, 0);
+    }
+  };
+  // stages 0..2 in flight; step b issues stage b + 3 into the slot stage b - 1
+  // left (its reads completed inside their asm blocks) and waits for stage b:
+  // the 24 loads of stages b+1..b+3 may still be outstanding
+  issue(0);
+  issue(1);
+  issue(2);
+  for (int b = 0; b < nb; ++b) {
+    issue(b + 3);
+    uwait_vm<24>();
+    compute(b);
+  }
+  // the discarded loads land before the ring is refilled
+  uwait_vm<0>();
+}
+
+template <int G>
+__global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
+  __shared__ __attribute__((aligned(16))) UnitLds L;
+  // the wave index as a scalar: each wave's item ranges and trip counts are
+  // then uniform, and the row loops branch on scalars
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hq = lane & 15, jg = lane >> 4;
+  const int unit = blockIdx.x;
+  const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
+  const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
+  // query fragments: lane (h, j) holds q_h[32 ks + 8 j .. +8], zero past g heads
+  bf16x8u qf[4];
+  {
+    const char* qb = reinterpret_cast<const char*>(a.q) + ((size_t)unit * G + (hq < G ? hq : 0)) * 256 + 16 * jg;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 v = hq < G ? load16(qb + 64 * ks) : make_uint4(0u, 0u, 0u, 0u);
+      qf[ks] = __builtin_bit_cast(bf16x8u, v);
+    }
+    // settle here: a first use inside the row loop would wait for every load
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) __asm__ volatile("" : "+v"(qf[ks]));
+  }
+  UState st;
+  st.m = kMinus;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4u{0.f, 0.f, 0.f, 0.f};
+  char* ring = L.u.ring[w][0];
+  // gists and tail as one item range, split in four consecutive shares
+  const int M = (int)a.M;
+  const int n1 = M + a.T;
+  const int per1 = (n1 + kUW - 1) / kUW;
+  unit_stream<true>(Kb, Vb, min(n1, w * per1), min(n1, (w + 1) * per1), a, qf, st, ring, L.scores, L.sel);
+  if (a.k > 0) {
+    __syncthreads();   // every group score is in LDS, every ring idle
+    float* gs = a.scores + (size_t)unit * a.score_stride;
+    unit_topk(gs, M, a.k, IdMap{nullptr, 0, 0, 0, 0}, unit, L.sel, L.u.sel.s, L.u.sel.t, L.scores);
+    __syncthreads();
+    if (a.sel)
+      for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
+    const int items = a.k * a.C;
+    const int per2 = (items + kUW - 1) / kUW;
+    unit_stream<false>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
+                       L.sel);
+  }
+  // merge the four waves' states
+  __syncthreads();   // LDS changes role: rings -> merge
+  float lw = st.l + __shfl_xor(st.l, 16);
+  lw += __shfl_xor(lw, 32);
+  if (jg == 0) {
+    L.u.mrg.m[w][hq] = st.m;
+    L.u.mrg.l[w][hq] = lw;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) L.u.mrg.o[w][hq][16 * dt + 4 * jg + r] = st.o[dt][r];
+  __syncthreads();
+  for (int idx = tid; idx < G * 128; idx += kUW * 64) {
+    const int h = idx >> 7, d = idx & 127;
+    float Mx = L.u.mrg.m[0][h];
+#pragma unroll
+    for (int ww = 1; ww < kUW; ++ww) Mx = fmaxf(Mx, L.u.mrg.m[ww][h]);
+    float Sm = 0.f, Ac = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kUW; ++ww) {
+      const float f = fexp2(L.u.mrg.m[ww][h] - Mx);
+      Sm = fmaf(L.u.mrg.l[ww][h], f, Sm);
+      Ac = fmaf(L.u.mrg.o[ww][h][d], f, Ac);
+    }
+    a.out[((size_t)unit * G + h) * 128 + d] = Ac / Sm;
+    if (d == 0 && a.lse) a.lse[(size_t)unit * G + h] = (Mx + log2f(Sm)) * kLn2;
+  }
+}
+
+// The one-workgroup-per-unit path applies: bf16, D = 128, enough units to
+// fill the chip, the group scores and the selection small enough for LDS.
+bool unit_path_ok(const DecodePlan& pl) {
+  return pl.dtype == GSA_BF16 && pl.D == 128 && pl.units >= kUMinUnits && pl.M <= kUMaxGist &&
+         pl.k <= kFastSel && pl.R < (1ll << 31) && (int64_t)pl.k * pl.C + pl.M + pl.T < (1ll << 31);
+}
+
+template <int G>
+gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const void* V, float* out, float* lse,
+                      int32_t* sel, char* ws, hipStream_t st) {
+  UnitArgs u{};
+  u.q = q; u.K = K; u.V = V; u.out = out; u.lse = lse; u.sel = pl.k > 0 ? sel : nullptr;
+  u.scores = reinterpret_cast<float*>(ws + pl.off_scores); u.score_stride = pl.score_stride;
+  u.R = pl.R; u.N = pl.N; u.M = pl.M; u.C = pl.C; u.k = pl.k; u.T = pl.T;
+  u.scale_log2 = pl.scale * kLog2e; u.score_mul = pl.scale / G;
+  prof_begin_call();
+  prof_mark(st);
+  hipLaunchKernelGGL((unit_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+  prof_mark(st);
+  return launch_status("gsa_decode launch");
 }
 
 // Dispatch on (dtype, head_dim, heads per kv-head).
@@ -1094,9 +1604,17 @@ extern "C" gsa_status_t gsa_decode(const gsa_decode_params* p, const void* q, co
       (s = check_ptr(lse, "lse", true)) != GSA_OK || (s = check_ptr(sel_idx, "sel_idx", true)) != GSA_OK)
     return s;
   if ((s = check_workspace(workspace, workspace_bytes, pl.total)) != GSA_OK) return s;
-  return dispatch<DecodeRunner>(pl.dtype, pl.D, pl.g, pl, q, k_cache, v_cache, out, lse, sel_idx,
-                                reinterpret_cast<char*>(workspace),
-                                reinterpret_cast<hipStream_t>(stream));
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (unit_path_ok(pl)) {
+    switch (pl.g) {
+      case 1: return run_unit<1>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
+      case 2: return run_unit<2>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
+      case 4: return run_unit<4>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
+      case 8: return run_unit<8>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
+    }
+  }
+  return dispatch<DecodeRunner>(pl.dtype, pl.D, pl.g, pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
 }
 
 extern "C" gsa_status_t gsa_decode_hier_workspace_size(const gsa_hier_params* p, size_t* bytes) {

@@ -139,16 +139,12 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   d.items_per_split = items > 0 ? (int32_t)ceil_div(items, d.S2) : 0;
   d.S2 = items > 0 ? (int32_t)ceil_div(items, d.items_per_split) : 0;
   d.NP = d.S + d.S2;
-  const bool fast = d.k <= kFastSelect;
-  d.score_stride = fast ? 0 : (d.M + 63) / 64 * 64;
-  d.cand_stride = fast ? line_pad(2 * (int64_t)d.S * d.k) : 0;
+  d.score_stride = d.k > 0 ? (d.M + 63) / 64 * 64 : 0;
   size_t off = 0;
   d.off_ctrl = off;
   off = align_up(off + ctrl_bytes(units));
   d.off_scores = off;
   off = align_up(off + sizeof(float) * (size_t)units * (size_t)d.score_stride);
-  d.off_cand = off;
-  off = align_up(off + sizeof(uint32_t) * (size_t)units * (size_t)d.cand_stride);
   d.off_sel = off;
   d.sel_stride = line_pad(d.k > 0 ? d.k : 1);
   off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)d.sel_stride);
@@ -178,6 +174,7 @@ gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
   h.n_cand = (int32_t)n_cand;
   if (d.k > h.n_cand)
     return fail(GSA_ERR_INVALID_ARG, "topk=%d exceeds the %d level-1 candidates", d.k, h.n_cand);
+  if (h.k2 > kMaxTopk2) return fail(GSA_ERR_UNSUPPORTED, "topk2=%d above %d", h.k2, kMaxTopk2);
   int64_t units = d.units;
   h.S_l2 = splits_for(h.M2, units);
   if (ceil_div(h.M2, h.S_l2) > kMaxTaskItems) h.S_l2 = (int32_t)ceil_div(h.M2, kMaxTaskItems);
@@ -189,11 +186,8 @@ gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
   h.S_c = h.n_cand > 0 ? (int32_t)ceil_div(h.n_cand, h.cand_per_split) : 1;
   h.tail_per_split = (int32_t)ceil_div(d.T, h.S_l2);
   h.NP = h.S_l2 + h.S_c + d.S2;
-  const bool fast2 = h.k2 <= kFastSelect, fast1 = d.k <= kFastSelect;
-  h.s2_stride = fast2 ? 0 : (h.M2 + 63) / 64 * 64;
-  h.sc_stride = fast1 ? 0 : (h.n_cand + 63) / 64 * 64;
-  h.cand2_stride = fast2 ? line_pad(2 * (int64_t)h.S_l2 * h.k2) : 0;
-  h.cand1_stride = fast1 ? line_pad(2 * (int64_t)h.S_c * d.k) : 0;
+  h.s2_stride = (h.M2 + 63) / 64 * 64;
+  h.sc_stride = d.k > 0 ? (h.n_cand + 63) / 64 * 64 : 0;
   size_t off = 0;
   h.off_ctrl = off;
   off = align_up(off + ctrl_bytes(units));
@@ -201,10 +195,6 @@ gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
   off = align_up(off + sizeof(float) * (size_t)units * (size_t)h.s2_stride);
   h.off_sc = off;
   off = align_up(off + sizeof(float) * (size_t)units * (size_t)h.sc_stride);
-  h.off_cand2 = off;
-  off = align_up(off + sizeof(uint32_t) * (size_t)units * (size_t)h.cand2_stride);
-  h.off_cand1 = off;
-  off = align_up(off + sizeof(uint32_t) * (size_t)units * (size_t)h.cand1_stride);
   h.off_sel2 = off;
   h.sel2_stride = line_pad(h.k2 > 0 ? h.k2 : 1);
   off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)h.sel2_stride);

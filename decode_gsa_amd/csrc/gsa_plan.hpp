@@ -16,9 +16,11 @@ const char* last_error_message();
 
 constexpr size_t kAlign = 256;
 
-// Selections of at most this many items use per-workgroup candidate lists
-// (64-bit keys); larger ones keep every score for a radix select.
+// Selections of at most this many items use wave-level bit-serial selects;
+// larger ones a block-wide radix select.
 constexpr int32_t kFastSelect = 64;
+// A two-level call's level-2 selection is staged in LDS: topk2 at most this.
+constexpr int32_t kMaxTopk2 = 1024;
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
 // Phases of one fused decode launch (gist pass(es), then unfold).
@@ -70,10 +72,9 @@ struct DecodePlan {
   int32_t n_items;      // k*C
   int32_t NP;           // partial states per unit = S (+ S2 when k > 0)
   // byte offsets inside the workspace (control words first)
-  size_t off_ctrl, off_scores, off_cand, off_sel, off_part, total;
-  int64_t score_stride; // floats per unit in the score region (k > kFastSelect)
-  int64_t cand_stride;  // words per unit in the candidate region (k <= kFastSelect)
-  int64_t sel_stride;   // ints per unit in the selection region
+  size_t off_ctrl, off_scores, off_sel, off_part, total;
+  int64_t score_stride; // floats per unit in the score region (read by the unfold pass)
+  int64_t sel_stride;   // ints per unit in the selection region (large k only)
 };
 
 gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* out);
@@ -91,8 +92,8 @@ struct HierPlan {
   int32_t cand_per_split;
   int32_t tail_per_split;   // tail rows per level-2 workgroup
   int32_t NP;           // S_l2 + S_c (+ S2 when k1 > 0)
-  size_t off_ctrl, off_s2, off_sc, off_cand2, off_cand1, off_sel2, off_sel1, off_part, total;
-  int64_t s2_stride, sc_stride, cand2_stride, cand1_stride, sel2_stride;
+  size_t off_ctrl, off_s2, off_sc, off_sel2, off_sel1, off_part, total;
+  int64_t s2_stride, sc_stride, sel2_stride;
 };
 
 gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* out);

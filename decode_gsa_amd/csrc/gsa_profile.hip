@@ -35,3 +35,10 @@ extern "C" gsa_status_t gsa_profile_events(void* const* events, int32_t n) {
   gsa::g_next = 0;
   return GSA_OK;
 }
+
+extern "C" gsa_status_t gsa_profile_marks(int32_t* n) {
+  gsa::clear_error();
+  if (n == nullptr) return gsa::fail(GSA_ERR_INVALID_ARG, "n is NULL");
+  *n = gsa::g_next;
+  return GSA_OK;
+}

@@ -179,14 +179,22 @@ gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, const void* q,
  * Timing hook (not part of the method): arm this thread with n caller-owned
  * hipEvent_t handles (passed as void*). Every later call on this thread
  * records events[0] on its stream before its first kernel launch and
- * events[i] right after its i-th launch, for as many events as there are
- * (gsa_decode: gist pass, then unfold pass when topk > 0; gsa_decode_hier:
- * level-2 pass, level-1 candidate pass, unfold pass when topk > 0;
- * gsa_prefill_blocksparse: selection when topk > 0, then attention). The
- * library never creates, waits on or destroys the events. n = 0 disarms.
+ * events[i] right after its i-th launch, for as many events as there are.
+ * Launches per call:
+ *   gsa_decode: one (the whole step of each (batch, kv-head) unit in one
+ *     workgroup) for bf16 with D = 128, B*Hkv >= 256, n_gist <= 4096 and
+ *     topk <= 64; otherwise a gist pass, then an unfold pass when topk > 0;
+ *   gsa_decode_hier: level-2 pass, level-1 candidate pass, unfold pass when
+ *     topk1 > 0;
+ *   gsa_prefill_blocksparse: selection when topk > 0, then attention.
+ * The library never creates, waits on or destroys the events. n = 0 disarms.
  * Returns GSA_ERR_INVALID_ARG for n outside [0, 8] or a NULL handle.
  * ---------------------------------------------------------------------- */
 gsa_status_t gsa_profile_events(void* const* events, int32_t n);
+
+/* Number of marks (kernel launches + 1) the last call on this thread made,
+ * armed or not; 0 before any call. GSA_ERR_INVALID_ARG for a NULL n. */
+gsa_status_t gsa_profile_marks(int32_t* n);
 
 /* Static description of a status code. */
 const char* gsa_status_string(gsa_status_t s);

@@ -199,6 +199,13 @@ def test_profile_events_validation(L):
     assert L.gsa_profile_events(None, 0) == OK     # disarm
 
 
+def test_profile_marks_validation(L):
+    assert L.gsa_profile_marks(None) == INVALID
+    n = ctypes.c_int32(-1)
+    assert L.gsa_profile_marks(ctypes.byref(n)) == OK
+    assert n.value >= 0
+
+
 def test_status_strings(L):
     for s in range(5):
         assert L.gsa_status_string(s).startswith(b"GSA_")

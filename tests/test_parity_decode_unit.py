@@ -1,0 +1,100 @@
+"""GPU parity of gsa_decode in its one-workgroup-per-unit launch (bf16,
+head_dim 128, at least 256 (batch, kv-head) units, at most 4096 gists and
+topk <= 64) against the fp64 oracle: bit-exact selections, outputs and lse
+within the stated tolerance (tests/gpu_util.py).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gsa_inputs as gi
+from conftest import to_np
+from gpu_util import say
+from test_parity_decode import run_decode, sample_units
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_gsa_amd
+    decode_gsa_amd.lib()          # raises if the library is missing: no fallback
+    return decode_gsa_amd
+
+
+def cfg_of(name, **kw):
+    return dataclasses.replace(gi.CONFIGS[name], **kw)
+
+
+# (config, units compared: None = every unit, else that many sampled)
+CASES = [
+    (cfg_of("gqa_32k", n_raw=4096), None),                                  # 256 units, g = 4
+    (cfg_of("gqa_32k", n_q_heads=8, n_raw=3000, n_gist=187, tail=40), None),    # g = 1, ragged
+    (cfg_of("gqa_32k", n_q_heads=16, n_raw=2048, tail=5), 64),             # g = 2
+    (cfg_of("gqa_32k", n_q_heads=64, n_raw=2048), 64),                     # g = 8
+    (cfg_of("gqa_32k", batch=40, n_raw=1500, tail=12), 64),                # 320 units, shortest tail
+    (cfg_of("c8_131k", batch=32, n_raw=8192), 48),                         # C = 8, k = 64
+    (cfg_of("c32_131k", batch=32, n_raw=8192), 48),                        # C = 32
+    (cfg_of("gqa_32k", n_raw=2048, topk=0, plant="none"), 64),             # gists + tail only
+    (cfg_of("gqa_32k", n_raw=1024, topk=64, plant="none"), 64),            # every chunk selected
+    (cfg_of("gqa_32k", n_raw=12, n_gist=0, topk=0, tail=12, plant="none"), 64),   # no gists
+    (cfg_of("gqa_32k", n_raw=65536, tail=300), 12),                        # 4096 gists: the LDS limit
+    (cfg_of("gqa_32k", n_raw=65552, tail=64), 12),                         # 4097 gists: the other path
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)), ids=[f"unit{i}" for i in range(len(CASES))])
+def test_decode_unit_path(gsa, case):
+    cfg, n = CASES[case]
+    say(f"decode unit-path {cfg} units={'all' if n is None else n}")
+    inp = gi.make_decode(cfg, 3000 + case, device="cuda")
+    units = None if n is None else sample_units(cfg, n=n, seed=case)
+    err = run_decode(gsa, inp, cfg, units=units)
+    say(f"  max err / rms = {err:.2e}")
+
+
+def test_decode_unit_ties_fall_back_to_radix(gsa):
+    """q = 0: all 2048 group scores are +-0, more ties at the threshold than the
+    candidate buffer holds, so the radix select decides: chunks 0..k-1, with
+    the tail starting inside chunk k-1."""
+    C, M, k = 16, 128, 16
+    T = M * C - ((k - 1) * C + 8)
+    cfg = cfg_of("gqa_32k", n_raw=M * C, topk=k, tail=T, plant="none")
+    say(f"decode unit-path ties {cfg}")
+    inp = gi.make_decode(cfg, 3100, device="cuda")
+    inp.q.zero_()
+    inp.k_cache.neg_()
+    out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=C, topk=k, tail=T)
+    torch.cuda.synchronize()
+    assert (to_np(sel) == np.arange(k)[None, None, :]).all()
+    run_decode(gsa, inp, cfg, units=sample_units(cfg, n=32, seed=1))
+
+
+def test_decode_unit_selects_chunk_inside_tail(gsa):
+    """A planted chunk whose raw rows all lie in the tail is attended once."""
+    cfg = cfg_of("gqa_32k", n_raw=2048, topk=4, tail=40, plant="none")
+    say(f"decode unit-path chunk in tail {cfg}")
+    inp = gi.make_decode(cfg, 3101, device="cuda")
+    C = cfg.chunk
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    last = cfg.M - 1
+    qbar = inp.q.float().view(cfg.batch, cfg.n_kv_heads, g, -1).mean(2)
+    inp.k_cache[:, :, last * (C + 1) + C] = (qbar / qbar.norm(dim=-1, keepdim=True) * 40).to(
+        inp.k_cache.dtype)
+    out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=C, topk=4, tail=40)
+    torch.cuda.synchronize()
+    assert (to_np(sel)[..., -1] == last).all()
+    run_decode(gsa, inp, cfg, units=sample_units(cfg, n=32, seed=2))
+
+
+def test_decode_unit_repeatable(gsa):
+    cfg = cfg_of("gqa_32k", n_raw=4096)
+    inp = gi.make_decode(cfg, 3102, device="cuda")
+    a = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=16, tail=64)
+    b = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=16, tail=64)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
