@@ -717,8 +717,15 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
     return (threadIdx.x & 4) ? dn : up;
   } else if constexpr (J == 8) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (J == 16) {
+    // v_permlane16_swap of v with itself: [0] holds rows (0,0,2,2), [1] rows (1,1,3,3)
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
   } else {
-    return (uint32_t)__shfl_xor((int)v, J);
+    static_assert(J == 32, "lane_xor: distance 1..32");
+    // v_permlane32_swap of v with itself: [0] holds halves (0,0), [1] halves (1,1)
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
   }
 }
 template <int J>
@@ -767,8 +774,7 @@ __device__ __forceinline__ T wave_sort(T x) {
 // their ids. More candidates (heavy ties) or a larger k take the block-wide
 // radix select.
 __device__ void unit_topk(const float* __restrict__ sc, int n, int k, const IdMap& im, int unit,
-                          int32_t* __restrict__ dst, SelectLds& S, TopkLds& T,
-                          const float* __restrict__ lds_sc = nullptr) {
+                          int32_t* __restrict__ dst, SelectLds& S, TopkLds& T) {
   if (k <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if (k >= n) {
@@ -784,12 +790,11 @@ __device__ void unit_topk(const float* __restrict__ sc, int n, int k, const IdMa
   // this thread's keys, kPer at a time with every load of a round in flight
   // (device-scope loads: the scores may come from other workgroups of this launch)
   constexpr int kPer = 8;
-  // (lds_sc: the same scores already in this workgroup's LDS)
   const CohBuf scb(sc, (uint32_t)n * 4u);
   auto keys_at = [&](int r0, uint32_t (&kv)[kPer]) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-      kv[j] = r0 + j < i1 ? order_key(lds_sc ? lds_sc[r0 + j] : __uint_as_float(scb.u32(r0 + j))) : 0u;
+      kv[j] = r0 + j < i1 ? order_key(__uint_as_float(scb.u32(r0 + j))) : 0u;
   };
   uint32_t kv[kPer];
   keys_at(i0, kv);
@@ -839,11 +844,6 @@ __device__ void unit_topk(const float* __restrict__ sc, int n, int k, const IdMa
   __syncthreads();
   const int total = S.cnt;
   if (total > kCandMax) {   // uniform: heavy ties at the threshold
-    if (lds_sc) {             // the radix select reads the scores from memory
-      float* scw = const_cast<float*>(sc);
-      for (int i = tid; i < n; i += kThreads) scw[i] = lds_sc[i];
-      done_stores();
-    }
     __syncthreads();
     block_topk(sc, n, k, im, unit, dst, T);
     return;
@@ -1228,7 +1228,13 @@ constexpr int kUTile = kUBR * 256;      // one stage's K (or V) rows
 constexpr int kUStage = 2 * kUTile;
 constexpr int kUMaxGist = 4096;         // group scores kept in LDS
 constexpr int kUMinUnits = 256;         // units needed to fill the chip
+// cache policy of the row loads: nontemporal (each row is read once per call)
+#ifndef GSA_UNT
+#define GSA_UNT 2
+#endif
+constexpr int kUNt = GSA_UNT;
 static_assert(kUW == kWaves, "the selection helpers assume the workgroup size");
+static_assert(kUMaxGist / kThreads * kWaves == 64 && kCandMax == 64, "selection layout: one count per lane");
 
 typedef __bf16 bf16x8u __attribute__((ext_vector_type(8)));
 typedef float f32x4u __attribute__((ext_vector_type(4)));
@@ -1283,6 +1289,131 @@ __device__ __forceinline__ void u_v_frag(const uint32_t (&addr)[8], i16x4u (&vf)
       : "memory");
 }
 
+// Exact top-k of the unit's n group scores (k <= 64 < n <= 4096), all in
+// LDS: the same result as the radix select (larger score first, equal
+// scores: smaller id first), ids written ascending to dst (LDS).
+//  1. thread t holds the keys of items t, t + 256, ...; each wave's k-th
+//     largest per-thread maximum is a lower bound on the k-th largest key,
+//     tau = the largest of the four bounds;
+//  2. the items with key >= tau are compacted in id order (ballots per
+//     round of 256 ids);
+//  3. each candidate's rank among the candidates decides; the selected ones
+//     keep their id order.
+// More than kCandMax candidates (ties at tau) go to the radix select over a
+// copy of the scores in gscratch (device memory).
+struct UnitSelLds {
+  uint32_t tw[kWaves];
+  int wc[kUMaxGist / kThreads][kWaves];   // candidates per (round, wave): 64 counts
+  uint32_t ck[kCandMax];
+  uint32_t ci[kCandMax];
+  int pr[kWaves][kCandMax];               // partial ranks
+  TopkLds t;
+};
+
+__device__ __forceinline__ void lds_topk(const float* __restrict__ sc, int n, int k, float* __restrict__ gscratch,
+                                         int unit, int32_t* __restrict__ dst, UnitSelLds& S) {
+  constexpr int kRounds = kUMaxGist / kThreads;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (k >= n) {
+    for (int i = tid; i < n; i += kThreads) dst[i] = i;
+    return;
+  }
+  // 1. keys (every read in bounds, no branches: the reads issue back to back)
+  uint32_t key[kRounds];
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const int i = tid + kThreads * j;
+    const float v = sc[min(i, n - 1)];
+    key[j] = i < n ? order_key(v) : 0u;
+    mx = max(mx, key[j]);
+  }
+  // (the lane read stays outside any branch: every lane takes part)
+  const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(mx), k - 1);
+  if (lane == 0) S.tw[w] = tw;
+  __syncthreads();
+  uint32_t tau = S.tw[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) tau = max(tau, S.tw[i]);
+  // 2. candidates: key >= tau among the items (every item when tau = 0);
+  // lane j of each wave publishes the wave's count of round j
+  uint64_t bal[kRounds];
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    bal[j] = __ballot(tid + kThreads * j < n && key[j] >= tau);
+    cnt = lane == j ? (int)__popcll(bal[j]) : cnt;
+  }
+  if (lane < kRounds) S.wc[lane][w] = cnt;
+  __syncthreads();
+  // exclusive prefix over (round, wave) in that order = each (round, wave)'s
+  // first slot in id order: lane l holds the count of round l/4, wave l%4
+  const int c = reinterpret_cast<const int*>(S.wc)[lane];
+  // inclusive scan within rows of 16 (row_shr:1, 2, 4, 8 with 0 fill), then
+  // the totals of the rows below
+  int x = c;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+  {
+    const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+              r2 = __builtin_amdgcn_readlane(x, 47);
+    x += (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+  }
+  const int total = __builtin_amdgcn_readlane(x, 63);
+  const int excl = x - c;
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const int first = __builtin_amdgcn_readlane(excl, kWaves * j + w);
+    const uint64_t m = bal[j];
+    if ((m >> lane) & 1ull) {
+      const int pos = first + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      if (pos < kCandMax) {
+        S.ck[pos] = key[j];
+        S.ci[pos] = (uint32_t)(tid + kThreads * j);
+      }
+    }
+  }
+  __syncthreads();
+  if (total > kCandMax) {   // uniform: heavy ties at the threshold
+    for (int i = tid; i < n; i += kThreads) gscratch[i] = sc[i];
+    done_stores();
+    __syncthreads();
+    block_topk(gscratch, n, k, IdMap{nullptr, 0, 0, 0, 0}, unit, dst, S.t);
+    return;
+  }
+  // 3. rank of candidate `lane` against candidates 16 w .. 16 w + 15 (equal
+  // keys: the smaller index, i.e. the smaller id, ranks first)
+  {
+    const uint32_t mine = S.ck[lane];
+    uint32_t o[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = reinterpret_cast<const uint4*>(S.ck)[4 * w + q];
+      o[4 * q] = v.x; o[4 * q + 1] = v.y; o[4 * q + 2] = v.z; o[4 * q + 3] = v.w;
+    }
+    int r = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int j = 16 * w + q;
+      r += (j < total && (o[q] > mine || (o[q] == mine && j < lane))) ? 1 : 0;
+    }
+    S.pr[w][lane] = r;
+  }
+  __syncthreads();
+  if (w == 0) {
+    const int r = S.pr[0][lane] + S.pr[1][lane] + S.pr[2][lane] + S.pr[3][lane];
+    const bool chosen = lane < total && r < k;
+    const uint64_t m = __ballot(chosen);
+    if (chosen)
+      dst[__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
+          (int32_t)S.ci[lane];
+  }
+}
+
 struct UnitArgs {
   const void* q;          // [B][Hq][D] bf16
   const void* K;          // [B][Hkv][R][D]
@@ -1301,10 +1432,7 @@ struct UnitArgs {
 struct UnitLds {
   union {
     char ring[kUW][kUNB][kUStage];      // streaming
-    struct {                            // selection (rings idle)
-      SelectLds s;
-      TopkLds t;
-    } sel;
+    UnitSelLds sel;                     // selection (rings idle)
     struct {                            // merge of the waves' states
       float m[kUW][16], l[kUW][16];
       float o[kUW][16][128];
@@ -1361,8 +1489,8 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
       const int r = 4 * u + (lane >> 4);
       const int row = row_of(i0 + b * kUBR + r);
       const int64_t off = (int64_t)(row >= 0 ? row : 0) * 256;
-      __builtin_amdgcn_global_load_lds(Kb + off + uk_slot(sl, r) * 16, kd + u * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(Vb + off + uv_slot(sl, r) * 16, vd + u * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(Kb + off + uk_slot(sl, r) * 16, kd + u * 1024, 16, 0, kUNt);
+      __builtin_amdgcn_global_load_lds(Vb + off + uv_slot(sl, r) * 16, vd + u * 1024, 16, 0, kUNt);
     }
   };
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)ring;
@@ -1490,7 +1618,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
   if (a.k > 0) {
     __syncthreads();   // every group score is in LDS, every ring idle
     float* gs = a.scores + (size_t)unit * a.score_stride;
-    unit_topk(gs, M, a.k, IdMap{nullptr, 0, 0, 0, 0}, unit, L.sel, L.u.sel.s, L.u.sel.t, L.scores);
+    lds_topk(L.scores, M, a.k, gs, unit, L.sel, L.u.sel);
     __syncthreads();
     if (a.sel)
       for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];

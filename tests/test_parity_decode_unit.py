@@ -98,3 +98,26 @@ def test_decode_unit_repeatable(gsa):
     b = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=16, tail=64)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def test_decode_unit_ties_inside_candidates(gsa):
+    """Equal group scores at the k-th place, few enough for the candidate
+    buffer: 10 gists share the best score and 10 the second best; with k = 16
+    all of the first group and the 6 smallest ids of the second are chosen."""
+    cfg = cfg_of("gqa_32k", n_raw=4096, topk=16, plant="none")
+    say(f"decode unit-path partial ties {cfg}")
+    inp = gi.make_decode(cfg, 3103, device="cuda")
+    C = cfg.chunk
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    qbar = inp.q.float().view(cfg.batch, cfg.n_kv_heads, g, -1).mean(2)
+    unit_dir = qbar / qbar.norm(dim=-1, keepdim=True)
+    first = [7 + 19 * i for i in range(10)]
+    second = [4 + 23 * i for i in range(10)]      # disjoint from the first group
+    for ids, mag in ((first, 40.0), (second, 30.0)):
+        for m in ids:
+            inp.k_cache[:, :, m * (C + 1) + C] = (unit_dir * mag).to(inp.k_cache.dtype)
+    out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=C, topk=16, tail=cfg.tail)
+    torch.cuda.synchronize()
+    want = np.array(sorted(first + sorted(second)[:6]))
+    assert (to_np(sel) == want[None, None, :]).all()
+    run_decode(gsa, inp, cfg, units=sample_units(cfg, n=24, seed=3))
