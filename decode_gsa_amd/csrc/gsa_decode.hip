@@ -1234,7 +1234,8 @@ constexpr int kUMinUnits = 256;         // units needed to fill the chip
 #endif
 constexpr int kUNt = GSA_UNT;
 static_assert(kUW == kWaves, "the selection helpers assume the workgroup size");
-static_assert(kUMaxGist / kThreads * kWaves == 64 && kCandMax == 64, "selection layout: one count per lane");
+static_assert(kUW == 4, "the merge combines four wave states");
+static_assert(kUMaxGist / kThreads == 16 && kCandMax == 64, "selection layout: four 16-byte reads per thread");
 
 typedef __bf16 bf16x8u __attribute__((ext_vector_type(8)));
 typedef float f32x4u __attribute__((ext_vector_type(4)));
@@ -1292,43 +1293,66 @@ __device__ __forceinline__ void u_v_frag(const uint32_t (&addr)[8], i16x4u (&vf)
 // Exact top-k of the unit's n group scores (k <= 64 < n <= 4096), all in
 // LDS: the same result as the radix select (larger score first, equal
 // scores: smaller id first), ids written ascending to dst (LDS).
-//  1. thread t holds the keys of items t, t + 256, ...; each wave's k-th
+//  1. thread t holds the keys of items t*per .. t*per + per - 1 (per a multiple
+//     of 4); each wave's k-th
 //     largest per-thread maximum is a lower bound on the k-th largest key,
 //     tau = the largest of the four bounds;
-//  2. the items with key >= tau are compacted in id order (ballots per
-//     round of 256 ids);
+//  2. the items with key >= tau are compacted in id order (thread t holds
+//     a contiguous id range; a scan of the per-thread counts places them);
 //  3. each candidate's rank among the candidates decides; the selected ones
 //     keep their id order.
 // More than kCandMax candidates (ties at tau) go to the radix select over a
 // copy of the scores in gscratch (device memory).
 struct UnitSelLds {
   uint32_t tw[kWaves];
-  int wc[kUMaxGist / kThreads][kWaves];   // candidates per (round, wave): 64 counts
-  uint32_t ck[kCandMax];
-  uint32_t ci[kCandMax];
+  int wsum[kWaves];
+  // candidates (key << 32 | ~id) in id order; [kCandMax, 2 kCandMax) takes
+  // the writes of the other items
+  unsigned long long ck[2 * kCandMax];
   int pr[kWaves][kCandMax];               // partial ranks
-  TopkLds t;
 };
 
 __device__ __forceinline__ void lds_topk(const float* __restrict__ sc, int n, int k, float* __restrict__ gscratch,
-                                         int unit, int32_t* __restrict__ dst, UnitSelLds& S) {
-  constexpr int kRounds = kUMaxGist / kThreads;
+                                         int unit, int32_t* __restrict__ dst, UnitSelLds& S, TopkLds& T) {
+  // Written to keep decisions in vector arithmetic: with one wave per SIMD
+  // every vector -> scalar -> vector round trip costs a full pipeline drain.
+  typedef unsigned long long u64;
+  constexpr int kPerMax = kUMaxGist / kThreads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (k >= n) {
     for (int i = tid; i < n; i += kThreads) dst[i] = i;
     return;
   }
-  // 1. keys (every read in bounds, no branches: the reads issue back to back)
-  uint32_t key[kRounds];
+  const int per = (n + 4 * kThreads - 1) / (4 * kThreads) * 4;   // a multiple of 4, <= 16
+  const int i0 = tid * per;
+  const int nv = max(0, min(per, n - i0));   // this thread's items
+  // 1. keys: four 16-byte reads inside the score array (kUMaxGist floats),
+  // all in flight together; entries past this thread's items are ignored
+  uint32_t key[kPerMax];
+  {
+    const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)sc;
+    uint32_t ad[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ad[q] = base + 16u * (uint32_t)min(i0 / 4 + q, kUMaxGist / 4 - 1);
+    uint4 v0, v1, v2, v3;
+    __asm__ volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+    const uint32_t raw[kPerMax] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
+                                   v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+#pragma unroll
+    for (int j = 0; j < kPerMax; ++j) key[j] = j < nv ? order_key(__uint_as_float(raw[j])) : 0u;
+  }
   uint32_t mx = 0u;
 #pragma unroll
-  for (int j = 0; j < kRounds; ++j) {
-    const int i = tid + kThreads * j;
-    const float v = sc[min(i, n - 1)];
-    key[j] = i < n ? order_key(v) : 0u;
-    mx = max(mx, key[j]);
-  }
+  for (int j = 0; j < kPerMax; ++j) mx = max(mx, key[j]);
   // (the lane read stays outside any branch: every lane takes part)
   const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(mx), k - 1);
   if (lane == 0) S.tw[w] = tw;
@@ -1336,22 +1360,15 @@ __device__ __forceinline__ void lds_topk(const float* __restrict__ sc, int n, in
   uint32_t tau = S.tw[0];
 #pragma unroll
   for (int i = 1; i < kWaves; ++i) tau = max(tau, S.tw[i]);
-  // 2. candidates: key >= tau among the items (every item when tau = 0);
-  // lane j of each wave publishes the wave's count of round j
-  uint64_t bal[kRounds];
-  int cnt = 0;
+  // Items that are not there have key 0; a real item has key 0 only for a
+  // NaN score with every bit set, so tau >= 1 selects exactly the items.
+  tau = max(tau, 1u);
+  // 2. count, scan, compact
+  int c = 0;
 #pragma unroll
-  for (int j = 0; j < kRounds; ++j) {
-    bal[j] = __ballot(tid + kThreads * j < n && key[j] >= tau);
-    cnt = lane == j ? (int)__popcll(bal[j]) : cnt;
-  }
-  if (lane < kRounds) S.wc[lane][w] = cnt;
-  __syncthreads();
-  // exclusive prefix over (round, wave) in that order = each (round, wave)'s
-  // first slot in id order: lane l holds the count of round l/4, wave l%4
-  const int c = reinterpret_cast<const int*>(S.wc)[lane];
-  // inclusive scan within rows of 16 (row_shr:1, 2, 4, 8 with 0 fill), then
-  // the totals of the rows below
+  for (int j = 0; j < kPerMax; ++j) c += key[j] >= tau ? 1 : 0;
+  // inclusive scan over the wave: rows of 16 (row_shr 1, 2, 4, 8 with 0 fill),
+  // then the totals of the rows below
   int x = c;
   x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
   x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
@@ -1362,44 +1379,43 @@ __device__ __forceinline__ void lds_topk(const float* __restrict__ sc, int n, in
               r2 = __builtin_amdgcn_readlane(x, 47);
     x += (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
   }
-  const int total = __builtin_amdgcn_readlane(x, 63);
-  const int excl = x - c;
+  const int wtot = __builtin_amdgcn_readlane(x, 63);
+  if (lane == 0) S.wsum[w] = wtot;
+  __syncthreads();
+  int run = x - c, total = 0;
 #pragma unroll
-  for (int j = 0; j < kRounds; ++j) {
-    const int first = __builtin_amdgcn_readlane(excl, kWaves * j + w);
-    const uint64_t m = bal[j];
-    if ((m >> lane) & 1ull) {
-      const int pos = first + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      if (pos < kCandMax) {
-        S.ck[pos] = key[j];
-        S.ci[pos] = (uint32_t)(tid + kThreads * j);
-      }
-    }
+  for (int i = 0; i < kWaves; ++i) {
+    const int t = S.wsum[i];
+    run += i < w ? t : 0;
+    total += t;
+  }
+#pragma unroll
+  for (int j = 0; j < kPerMax; ++j) {
+    const bool f = key[j] >= tau;
+    const int p = f ? run : kCandMax;
+    S.ck[p < kCandMax ? p : kCandMax + lane] = ((u64)key[j] << 32) | (uint32_t)~(uint32_t)(i0 + j);
+    run += f ? 1 : 0;
   }
   __syncthreads();
   if (total > kCandMax) {   // uniform: heavy ties at the threshold
     for (int i = tid; i < n; i += kThreads) gscratch[i] = sc[i];
     done_stores();
     __syncthreads();
-    block_topk(gscratch, n, k, IdMap{nullptr, 0, 0, 0, 0}, unit, dst, S.t);
+    block_topk(gscratch, n, k, IdMap{nullptr, 0, 0, 0, 0}, unit, dst, T);
     return;
   }
-  // 3. rank of candidate `lane` against candidates 16 w .. 16 w + 15 (equal
-  // keys: the smaller index, i.e. the smaller id, ranks first)
+  // 3. rank of candidate `lane` against candidates 16 w .. 16 w + 15: the
+  // composite keys are distinct, larger first (equal scores: smaller id)
   {
-    const uint32_t mine = S.ck[lane];
-    uint32_t o[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 v = reinterpret_cast<const uint4*>(S.ck)[4 * w + q];
-      o[4 * q] = v.x; o[4 * q + 1] = v.y; o[4 * q + 2] = v.z; o[4 * q + 3] = v.w;
-    }
+    const u64 mine = S.ck[lane];
     int r = 0;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int j = 16 * w + q;
-      r += (j < total && (o[q] > mine || (o[q] == mine && j < lane))) ? 1 : 0;
+    for (int q = 0; q < 16; q += 2) {
+      const ulonglong2 v = reinterpret_cast<const ulonglong2*>(S.ck)[8 * w + q / 2];
+      const u64 o0 = 16 * w + q < total ? v.x : 0ull;
+      const u64 o1 = 16 * w + q + 1 < total ? v.y : 0ull;
+      r += o0 > mine ? 1 : 0;
+      r += o1 > mine ? 1 : 0;
     }
     S.pr[w][lane] = r;
   }
@@ -1410,7 +1426,7 @@ __device__ __forceinline__ void lds_topk(const float* __restrict__ sc, int n, in
     const uint64_t m = __ballot(chosen);
     if (chosen)
       dst[__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u))] =
-          (int32_t)S.ci[lane];
+          (int32_t)~(uint32_t)S.ck[lane];
   }
 }
 
@@ -1432,9 +1448,12 @@ struct UnitArgs {
 struct UnitLds {
   union {
     char ring[kUW][kUNB][kUStage];      // streaming
-    UnitSelLds sel;                     // selection (rings idle)
+    struct {                            // selection (rings idle)
+      UnitSelLds s;
+      TopkLds t;
+    } sel;
     struct {                            // merge of the waves' states
-      float m[kUW][16], l[kUW][16];
+      float m[16][kUW], l[16][kUW];     // head-major: one 16-byte read per head
       float o[kUW][16][128];
     } mrg;
   } u;
@@ -1478,8 +1497,8 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     return pos >= tail0 ? -1 : (int)(pos + m);
   };
   // stage b -> ring slot b % kUNB: lane i loads 16 bytes of row 4u + i/16 into
-  // LDS slot i%16, K and V alike. Items past the end read row 0 (in bounds,
-  // discarded), so that every stage issues the same eight loads.
+  // LDS slot i%16, K and V alike. Items past the end of the last stage read
+  // row 0 (in bounds, masked), so that every stage issues the same eight loads.
   auto issue = [&](int b) {
     char* kd = ring + (b % kUNB) * kUStage;
     char* vd = kd + kUTile;
@@ -1566,19 +1585,25 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
       st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[dt], plo, st.o[dt], 0, 0, 0);
     }
   };
-  // stages 0..2 in flight; step b issues stage b + 3 into the slot stage b - 1
-  // left (its reads completed inside their asm blocks) and waits for stage b:
-  // the 24 loads of stages b+1..b+3 may still be outstanding
+  // stages 0..2 in flight; step b issues stage b + 3 (if any) into the slot
+  // stage b - 1 left (its reads completed inside their asm blocks) and waits
+  // for stage b: the 8 loads of each later stage may still be outstanding
   issue(0);
-  issue(1);
-  issue(2);
+  if (nb > 1) issue(1);
+  if (nb > 2) issue(2);
   for (int b = 0; b < nb; ++b) {
-    issue(b + 3);
-    uwait_vm<24>();
+    if (b + 3 < nb) {
+      issue(b + 3);
+      uwait_vm<24>();
+    } else if (b + 2 < nb) {
+      uwait_vm<16>();
+    } else if (b + 1 < nb) {
+      uwait_vm<8>();
+    } else {
+      uwait_vm<0>();   // the last stage: nothing of this stream left in flight
+    }
     compute(b);
   }
-  // the discarded loads land before the ring is refilled
-  uwait_vm<0>();
 }
 
 template <int G>
@@ -1618,10 +1643,8 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
   if (a.k > 0) {
     __syncthreads();   // every group score is in LDS, every ring idle
     float* gs = a.scores + (size_t)unit * a.score_stride;
-    lds_topk(L.scores, M, a.k, gs, unit, L.sel, L.u.sel);
+    lds_topk(L.scores, M, a.k, gs, unit, L.sel, L.u.sel.s, L.u.sel.t);
     __syncthreads();
-    if (a.sel)
-      for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
     const int items = a.k * a.C;
     const int per2 = (items + kUW - 1) / kUW;
     unit_stream<false>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
@@ -1629,32 +1652,42 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
   }
   // merge the four waves' states
   __syncthreads();   // LDS changes role: rings -> merge
-  float lw = st.l + __shfl_xor(st.l, 16);
-  lw += __shfl_xor(lw, 32);
+  float lw = st.l + __uint_as_float(lane_xor<16>(__float_as_uint(st.l)));
+  lw += __uint_as_float(lane_xor<32>(__float_as_uint(lw)));
   if (jg == 0) {
-    L.u.mrg.m[w][hq] = st.m;
-    L.u.mrg.l[w][hq] = lw;
+    L.u.mrg.m[hq][w] = st.m;
+    L.u.mrg.l[hq][w] = lw;
   }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) L.u.mrg.o[w][hq][16 * dt + 4 * jg + r] = st.o[dt][r];
+    *reinterpret_cast<f32x4u*>(&L.u.mrg.o[w][hq][16 * dt + 4 * jg]) = st.o[dt];
   __syncthreads();
-  for (int idx = tid; idx < G * 128; idx += kUW * 64) {
-    const int h = idx >> 7, d = idx & 127;
-    float Mx = L.u.mrg.m[0][h];
+  // thread (h, 4 columns): G * 32 threads, every read of a thread in flight at once
+  if (tid < G * 32) {
+    const int h = tid >> 5, d4 = 4 * (tid & 31);
+    const float4 mm = *reinterpret_cast<const float4*>(L.u.mrg.m[h]);
+    const float4 ll = *reinterpret_cast<const float4*>(L.u.mrg.l[h]);
+    float4 ov[kUW];
 #pragma unroll
-    for (int ww = 1; ww < kUW; ++ww) Mx = fmaxf(Mx, L.u.mrg.m[ww][h]);
-    float Sm = 0.f, Ac = 0.f;
+    for (int ww = 0; ww < kUW; ++ww) ov[ww] = *reinterpret_cast<const float4*>(&L.u.mrg.o[ww][h][d4]);
+    const float Mx = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
+    const float f[kUW] = {fexp2(mm.x - Mx), fexp2(mm.y - Mx), fexp2(mm.z - Mx), fexp2(mm.w - Mx)};
+    const float Sm = ll.x * f[0] + ll.y * f[1] + ll.z * f[2] + ll.w * f[3];
+    float4 ac = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int ww = 0; ww < kUW; ++ww) {
-      const float f = fexp2(L.u.mrg.m[ww][h] - Mx);
-      Sm = fmaf(L.u.mrg.l[ww][h], f, Sm);
-      Ac = fmaf(L.u.mrg.o[ww][h][d], f, Ac);
+      ac.x = fmaf(ov[ww].x, f[ww], ac.x);
+      ac.y = fmaf(ov[ww].y, f[ww], ac.y);
+      ac.z = fmaf(ov[ww].z, f[ww], ac.z);
+      ac.w = fmaf(ov[ww].w, f[ww], ac.w);
     }
-    a.out[((size_t)unit * G + h) * 128 + d] = Ac / Sm;
-    if (d == 0 && a.lse) a.lse[(size_t)unit * G + h] = (Mx + log2f(Sm)) * kLn2;
+    const float inv = 1.f / Sm;
+    *reinterpret_cast<float4*>(a.out + ((size_t)unit * G + h) * 128 + d4) =
+        make_float4(ac.x * inv, ac.y * inv, ac.z * inv, ac.w * inv);
+    if (d4 == 0 && a.lse) a.lse[(size_t)unit * G + h] = (Mx + log2f(Sm)) * kLn2;
   }
+  if (a.sel)
+    for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
 }
 
 // The one-workgroup-per-unit path applies: bf16, D = 128, enough units to
