@@ -20,9 +20,10 @@ last touched L-1 steps (>= 0.9 GB of other traffic) earlier and is no longer in
 the 256 MB Infinity Cache -- as in a real model, where each layer has its own
 cache. Inputs are resident in HBM before timing starts.
 
-Per-kernel times come from HIP events that the library records on the launch
-stream between its kernels (gsa_profile_events), so the roofline of the
-dominant kernel is measured live in the timed region.
+Per-kernel times come from HIP events that the library attaches to its
+kernel launches (gsa_profile_events: the runtime stamps them with each
+kernel's start and end), so the roofline of the dominant kernel is measured
+live in the timed region.
 
 Prints one JSON line.
 """

@@ -1121,9 +1121,7 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
   g.fuse_k = pl.k;
   g.sel_ws = wsel; g.sel_stride = pl.sel_stride; g.sel_out = sel_idx;
   prof_begin_call();
-  prof_mark(st);
-  hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st, g);
-  prof_mark(st);
+  prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st, g);
   if (pl.k > 0) {
     UnfoldArgs u{};
     u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
@@ -1135,8 +1133,7 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
     u.out = out; u.lse = lse;
     u.cnt = ctrl_of(ws, pl.off_ctrl, 2);
     u.scale_log2 = pl.scale * kLog2e;
-    hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
-    prof_mark(st);
+    prof_launch((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
   }
   return launch_status("gsa_decode launch");
 }
@@ -1166,9 +1163,7 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
   g.fuse_k = 0;
   prof_begin_call();
-  prof_mark(st);
-  hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_l2), dim3(kThreads), 0, st, g);
-  prof_mark(st);
+  prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_l2), dim3(kThreads), 0, st, g);
   // level 1: select the groups, then score and attend their children and the
   // ungrouped gists
   GistArgs c = g;
@@ -1182,8 +1177,7 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   c.part_base = hp.S_l2;
   c.out = pl.k > 0 ? nullptr : out; c.lse = pl.k > 0 ? nullptr : lse;
   c.cnt = ctrl_of(ws, hp.off_ctrl, 1);
-  hipLaunchKernelGGL((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_c), dim3(kThreads), 0, st, c);
-  prof_mark(st);
+  prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_c), dim3(kThreads), 0, st, c);
   // unfold the chosen chunks, merge everything
   if (pl.k > 0) {
     UnfoldArgs u{};
@@ -1198,8 +1192,7 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
     u.out = out; u.lse = lse;
     u.cnt = ctrl_of(ws, hp.off_ctrl, 2);
     u.scale_log2 = pl.scale * kLog2e;
-    hipLaunchKernelGGL((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
-    prof_mark(st);
+    prof_launch((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
   }
   return launch_status("gsa_decode_hier launch");
 }
@@ -1706,9 +1699,7 @@ gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const 
   u.R = pl.R; u.N = pl.N; u.M = pl.M; u.C = pl.C; u.k = pl.k; u.T = pl.T;
   u.scale_log2 = pl.scale * kLog2e; u.score_mul = pl.scale / G;
   prof_begin_call();
-  prof_mark(st);
-  hipLaunchKernelGGL((unit_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
-  prof_mark(st);
+  prof_launch((unit_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
   return launch_status("gsa_decode launch");
 }
 

@@ -719,7 +719,6 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
   int32_t* wsel = reinterpret_cast<int32_t*>(ws);
   const int grid = pl.n_blocks * pl.Hkv;
   prof_begin_call();
-  prof_mark(stream);
   if (pl.k > 0) {
     SelArgs s{};
     s.q = q; s.K = K; s.R = pl.R;
@@ -727,16 +726,14 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
     s.q_start = (int32_t)pl.q_start; s.n_q = (int32_t)pl.n_q;
     s.score_mul = pl.scale / G;
     s.sel_ws = wsel; s.sel_out = sel;
-    hipLaunchKernelGGL((prefill_select<G>), dim3(grid), dim3(kSelThreads), 0, stream, s);
-    prof_mark(stream);
+    prof_launch((prefill_select<G>), dim3(grid), dim3(kSelThreads), 0, stream, s);
   }
   AttArgs t{};
   t.q = q; t.K = K; t.V = V; t.out = out; t.sel = wsel; t.R = pl.R;
   t.M = (int32_t)pl.M; t.C = pl.C; t.k = pl.k; t.W = pl.W; t.Hkv = pl.Hkv; t.n_blocks = pl.n_blocks;
   t.q_start = (int32_t)pl.q_start; t.n_q = (int32_t)pl.n_q;
   t.scale_log2 = pl.scale * kLog2e;
-  hipLaunchKernelGGL((prefill_attend<G>), dim3(grid), dim3(AttShape<G>::NT), 0, stream, t);
-  prof_mark(stream);
+  prof_launch((prefill_attend<G>), dim3(grid), dim3(AttShape<G>::NT), 0, stream, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GSA_ERR_HIP, "gsa_prefill_blocksparse launch: %s", hipGetErrorString(e));
   return GSA_OK;

@@ -1,5 +1,5 @@
 // Timing hook of libgsa (see gsa_profile_events in gsa.h): a per-thread list
-// of caller-owned hipEvent_t handles, recorded in order around the kernel
+// of caller-owned hipEvent_t handles, attached in order to the kernel
 // launches of each later call on that thread.
 #include "gsa_profile.hpp"
 
@@ -11,14 +11,15 @@ namespace {
 constexpr int kMaxEvents = 8;
 thread_local hipEvent_t g_events[kMaxEvents];
 thread_local int g_n = 0;
-thread_local int g_next = 0;
+thread_local int g_launches = 0;   // launches of the current (or last) call
 }  // namespace
 
-void prof_begin_call() { g_next = 0; }
+void prof_begin_call() { g_launches = 0; }
 
-void prof_mark(hipStream_t s) {
-  if (g_next < g_n) (void)hipEventRecord(g_events[g_next], s);
-  ++g_next;
+void prof_launch_events(hipEvent_t* start, hipEvent_t* stop) {
+  *start = (g_launches == 0 && g_n > 0) ? g_events[0] : nullptr;
+  *stop = g_launches + 1 < g_n ? g_events[g_launches + 1] : nullptr;
+  ++g_launches;
 }
 
 }  // namespace gsa
@@ -32,13 +33,12 @@ extern "C" gsa_status_t gsa_profile_events(void* const* events, int32_t n) {
     if (events[i] == nullptr) return gsa::fail(GSA_ERR_INVALID_ARG, "events[%d] is NULL", i);
   for (int i = 0; i < n; ++i) gsa::g_events[i] = reinterpret_cast<hipEvent_t>(events[i]);
   gsa::g_n = n;
-  gsa::g_next = 0;
   return GSA_OK;
 }
 
 extern "C" gsa_status_t gsa_profile_marks(int32_t* n) {
   gsa::clear_error();
   if (n == nullptr) return gsa::fail(GSA_ERR_INVALID_ARG, "n is NULL");
-  *n = gsa::g_next;
+  *n = gsa::g_launches + 1;
   return GSA_OK;
 }

@@ -178,9 +178,9 @@ gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, const void* q,
 /* ------------------------------------------------------------------------
  * Timing hook (not part of the method): arm this thread with n caller-owned
  * hipEvent_t handles (passed as void*). Every later call on this thread
- * records events[0] on its stream before its first kernel launch and
- * events[i] right after its i-th launch, for as many events as there are.
- * Launches per call:
+ * attaches them to its kernel launches (hipExtLaunchKernel): events[0] takes
+ * the start of the call's first kernel and events[i] the end of its i-th
+ * kernel, for as many events as there are. Launches per call:
  *   gsa_decode: one (the whole step of each (batch, kv-head) unit in one
  *     workgroup) for bf16 with D = 128, B*Hkv >= 256, n_gist <= 4096 and
  *     topk <= 64; otherwise a gist pass, then an unfold pass when topk > 0;
