@@ -1,6 +1,6 @@
-// GSA decode on gfx950 in one launch: gist scoring + online softmax over every
-// gist, exact top-k chunk selection, gather of the unfolded chunks and the
-// tail, and a log-sum-exp merge of the partial softmax states.
+// GSA decode on gfx950: gist scoring + online softmax over every gist, exact
+// top-k chunk selection, unfolding of the chosen chunks' raw rows, the tail,
+// and a log-sum-exp merge, per (batch, kv-head) unit.
 //
 // Method: gist.science explainer "Forget, Then Recall", section 2 'Key
 // Concepts' (routing by gist scores, top-k selection, selective unfolding,
@@ -8,30 +8,30 @@
 // entry point (score the meta-gists, then the gists of the chosen groups,
 // then unfold raw chunks).
 //
-// Work is cut into tasks per (batch, kv-head) unit and phase:
-//   gist-like phase  a task streams a contiguous range of gist rows (K and V,
-//                    each row read once), writes each gist's group score and
-//                    one online-softmax partial (m, l, acc[D]) per query head;
-//                    the unit's last task to finish runs the exact top-k over
-//                    the phase's scores and raises the unit's ready flag;
-//   unfold phase     a task waits for its unit's flag, then streams a share of
-//                    the selected chunks' raw rows (each chunk one contiguous
-//                    run; rows the tail owns are skipped) and of the tail; the
-//                    unit's last task merges every partial into out and lse.
-// Single-level decode runs [gist, unfold]; two-level decode runs [level-2
-// gists, level-1 candidate gists, unfold].
+// Two launch shapes:
+//   unit_kernel   (bf16, D = 128, >= 256 units, <= 4096 gists, k <= 64) one
+//                 workgroup runs a unit's whole step: its four waves stream
+//                 the gists and the tail on MFMA through direct-to-LDS rings,
+//                 the group scores stay in LDS, the exact top-k runs in LDS,
+//                 the waves stream the chosen chunks' raw rows and merge their
+//                 four softmax states. Nothing is handed off through memory.
+//   gist_kernel + unfold_kernel (every other shape, and two-level decode)
+//                 split-K over gists: each gist workgroup streams a range of
+//                 gist rows (and a share of the tail), keeps its group scores
+//                 and writes one online-softmax partial (m, l, acc[D]) per
+//                 query head; the unit's last workgroup to finish (an atomic
+//                 counter) selects the unit's top-k from the scores. The
+//                 unfold launch streams the chosen chunks' raw rows (rows the
+//                 tail owns are skipped) and the unit's last workgroup merges
+//                 every partial into out and lse. Two-level decode runs
+//                 level-2 gists, then the candidate level-1 gists, then the
+//                 unfold.
 //
-// Tasks are numbered phase by phase and unit by unit, and a task only ever
-// waits for tasks with lower numbers. The grid is persistent and no larger
-// than the number of workgroups the chip holds at once (occupancy x CUs), so
-// every workgroup is resident; workgroup w runs tasks w, w + P, w + 2P, ... in
-// order. The lowest unfinished task is therefore always running with all its
-// (lower) dependencies finished, so every wait ends. The wait is also bounded;
-// on time-out the task poisons its partial with NaN instead of hanging.
-//
-// Memory-bound work stays on the VALU: 16 lanes cover one 256-byte row with
-// one 16-byte load each, q.k uses v_dot2_f32_bf16, the 16-lane sum uses DPP,
-// and the softmax weights stay fp32.
+// In the split path memory-bound work stays on the VALU: 16 lanes cover one
+// 256-byte row with one 16-byte load each, q.k uses v_dot2_f32_bf16, the
+// 16-lane sum uses DPP, and the softmax weights stay fp32. Hand-off data
+// between workgroups (scores, partials) is written with device-scope stores
+// and read with device-scope loads: the XCDs' L2s are not coherent.
 #include <hip/hip_runtime.h>
 
 #include "gsa.h"
@@ -46,10 +46,7 @@ using namespace dev;
 
 constexpr int kThreads = 256;   // 4 waves per workgroup
 constexpr int kWaves = kThreads / 64;
-#ifndef GSA_ROWS_IN_FLIGHT
-#define GSA_ROWS_IN_FLIGHT 2
-#endif
-constexpr int kU = GSA_ROWS_IN_FLIGHT;   // rows per lane group per batch (two batches in flight)
+constexpr int kU = 2;           // rows per lane group per batch (two batches in flight)
 constexpr int kTaskScores = 1024;        // scores a gist workgroup gathers in LDS
 constexpr int kSelLds = 1024;   // selected chunk ids staged in LDS by unfold tasks
 
@@ -1222,10 +1219,7 @@ constexpr int kUStage = 2 * kUTile;
 constexpr int kUMaxGist = 4096;         // group scores kept in LDS
 constexpr int kUMinUnits = 256;         // units needed to fill the chip
 // cache policy of the row loads: nontemporal (each row is read once per call)
-#ifndef GSA_UNT
-#define GSA_UNT 2
-#endif
-constexpr int kUNt = GSA_UNT;
+constexpr int kUNt = 2;
 static_assert(kUW == kWaves, "the selection helpers assume the workgroup size");
 static_assert(kUW == 4, "the merge combines four wave states");
 static_assert(kUMaxGist / kThreads == 16 && kCandMax == 64, "selection layout: four 16-byte reads per thread");

@@ -24,10 +24,7 @@ constexpr int64_t kMinRows = 64;
 
 // Unfold workgroups get at least this many rows: few rows each keep the
 // latency of the pass short (it starts only after the selection).
-#ifndef GSA_MIN_UNFOLD_ROWS
-#define GSA_MIN_UNFOLD_ROWS 64
-#endif
-constexpr int64_t kMinUnfoldRows = GSA_MIN_UNFOLD_ROWS;
+constexpr int64_t kMinUnfoldRows = 64;
 // A gist workgroup gathers its scores in LDS: at most this many items each.
 constexpr int64_t kMaxTaskItems = 1024;
 
