@@ -6,10 +6,10 @@ heads over 8 kv-heads, head_dim 128, bf16 interleaved cache, 32768-token
 context, chunk 16, top-16 chunks, 64-token tail. One step = one gsa_decode
 call over the whole batch, i.e. every stage of the path: gist scoring +
 attention over all gists and the tail, exact top-k, unfold of the chosen
-chunks and the merge. With its 256 (batch, kv-head) units this is one launch,
-one workgroup per unit (unit_kernel); configurations with fewer units run a
-gist pass (each unit's last workgroup makes the unit's selection) and an
-unfold pass.
+chunks and the merge, in one launch of unit_kernel: one workgroup per
+(batch, kv-head) unit for its 256 units (configurations with fewer units use
+several workgroups per unit that hand their partial states to the unit's
+last one).
 
 `--config prefill_64k` times the causal block-sparse prefill instead (4096
 query positions at the end of a 65536-token sequence, 32/8 heads, k=16, W=64).
@@ -216,28 +216,28 @@ def run_decode_bench(args):
         assert torch.equal(sel.long(), inp.planted), "selection differs from the planted top-k"
     gist_b, unfold_b = decode_bytes(cfg, sel.cpu().numpy() if cfg.topk else [])
     alg_b = gist_b + unfold_b
-    # launch structure of this call: one fused launch (one workgroup per
-    # unit), or a gist pass followed by an unfold pass when topk > 0
-    units = cfg.batch * cfg.n_kv_heads
-    fused = (cfg.dtype == "bf16" and cfg.head_dim == 128 and units >= 256 and cfg.M <= 4096
-             and cfg.topk <= 64)
-    n_marks = 2 if fused or cfg.topk == 0 else 3
-    made = gsa.gsa_profile_marks()
-    assert made == n_marks, f"the call made {made - 1} launches, expected {n_marks - 1}"
+    # launch structure of this call (the timing hook counts the launches):
+    # unit_kernel (bf16, D = 128, k <= 64, at most 16384 gists when k > 0),
+    # followed by unit_unfold_kernel when a unit takes several workgroups and
+    # k > 0; otherwise gist_kernel, then unfold_kernel when k > 0
+    unit_path = (cfg.dtype == "bf16" and cfg.head_dim == 128 and cfg.topk <= 64
+                 and (cfg.topk == 0 or cfg.M <= 16384) and cfg.M + cfg.tail <= 256 * 5120)
+    n_marks = gsa.gsa_profile_marks()
     ms_per_step, per = timed_steps(gsa, step, args, n_marks)
     call_ms = float(per.sum(axis=1).mean())
     qheads = B * Hq
     sha = source_sha("gsa_decode.hip", "gsa_device.hpp")
-    if fused:
-        main, main_b, main_ms = "unit_kernel", alg_b, float(per[:, 0].mean())
-        kernels = {main: {"ms": main_ms, "alg_bytes": main_b, "GB_s": main_b / (main_ms / 1e3) / 1e9}}
+    if unit_path and n_marks == 2:
+        names, nbytes = ["unit_kernel"], [alg_b]
+    elif unit_path:
+        names, nbytes = ["unit_kernel", "unit_unfold_kernel"], [gist_b, unfold_b]
     else:
-        main, main_b, main_ms = "gist_kernel", gist_b, float(per[:, 0].mean())
-        kernels = {main: {"ms": main_ms, "alg_bytes": main_b, "GB_s": main_b / (main_ms / 1e3) / 1e9}}
-        if cfg.topk > 0:
-            unfold_ms = float(per[:, 1].mean())
-            kernels["unfold_kernel"] = {"ms": unfold_ms, "alg_bytes": unfold_b,
-                                        "GB_s": unfold_b / (unfold_ms / 1e3) / 1e9}
+        names, nbytes = ["gist_kernel", "unfold_kernel"][:n_marks - 1], [gist_b, unfold_b][:n_marks - 1]
+    kernels = {}
+    for j, (nm, nb) in enumerate(zip(names, nbytes)):
+        ms = float(per[:, j].mean())
+        kernels[nm] = {"ms": ms, "alg_bytes": nb, "GB_s": nb / (ms / 1e3) / 1e9}
+    main, main_b, main_ms = names[0], nbytes[0], kernels[names[0]]["ms"]
     achieved = main_b / (main_ms / 1e3) / 1e9
     res = {
         "metric": DECODE_METRIC,
@@ -271,6 +271,109 @@ def run_decode_bench(args):
         log("[bench] timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline_decode(inp, cfg, args.cpu_seconds)
     return res
+
+
+# ------------------------------------------------------------- two-level ---
+
+def hier_bytes(cfg, sel1):
+    """Algorithmic bytes per two-level call: every level-2 gist row, the level-1
+    gists of the candidate groups and the orphans, the raw rows of the chosen
+    chunks outside the tail, the tail rows (K + V each), q, and the fp32
+    out/lse and both id lists."""
+    b = cfg.base
+    eb = 2 if b.dtype == "bf16" else 4
+    row = 2 * b.head_dim * eb
+    units = b.batch * b.n_kv_heads
+    n_cand = cfg.topk2 * cfg.fanout + (b.M - cfg.M2 * cfg.fanout)
+    tail0 = b.n_raw - b.tail
+    raw_sel = 0
+    if b.topk:
+        for u_sel in np.asarray(sel1).reshape(units, -1):
+            for m in u_sel:
+                raw_sel += max(0, min(b.chunk, tail0 - int(m) * b.chunk))
+    q = b.batch * b.n_q_heads * b.head_dim * eb
+    out = b.batch * b.n_q_heads * (b.head_dim + 1) * 4 + units * (b.topk + cfg.topk2) * 4
+    return {"l2": units * cfg.M2 * row + units * b.tail * row + q,
+            "cand": units * n_cand * row,
+            "unfold": raw_sel * row + out}
+
+
+def run_hier_bench(args):
+    import torch
+    import decode_gsa_amd as gsa
+    import gsa_inputs as gi
+
+    cfg = gi.CONFIGS[args.config]
+    b = cfg.base
+    dev = torch.device("cuda", 0)
+    log(f"[bench] generating {cfg.name} inputs ...")
+    inp = gi.make_hier(cfg, 1000 + 4, device=dev)
+    eb = 2 if b.dtype == "bf16" else 4
+    per_layer = 2 * b.batch * b.n_kv_heads * (b.R + cfg.M2) * b.head_dim * eb
+    layers = args.layers or 3
+    free = torch.cuda.mem_get_info(dev)[0]
+    layers = max(1, min(layers, int(0.8 * free // per_layer)))
+    caches = [(inp.k_cache, inp.v_cache, inp.k_l2, inp.v_l2)]
+    for _ in range(layers - 1):
+        caches.append(tuple(t.clone() for t in caches[0]))
+    B, Hq, D = inp.q.shape
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    s2 = torch.empty(B, b.n_kv_heads, max(cfg.topk2, 1), dtype=torch.int32, device=dev)
+    s1 = torch.empty(B, b.n_kv_heads, max(b.topk, 1), dtype=torch.int32, device=dev)
+    base = gsa.decode_params(B, Hq, b.n_kv_heads, D, b.n_raw, b.M, b.chunk, b.topk, b.tail, 0.0,
+                             gsa.GSA_BF16 if b.dtype == "bf16" else gsa.GSA_F32)
+    ws = gsa.new_workspace(gsa.hier_workspace_size(gsa.hier_params(base, cfg.fanout, cfg.topk2)), dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        k, v, k2, v2 = caches[i % layers]
+        gsa.gsa_decode_hier(inp.q, k, v, k2, v2, chunk=b.chunk, fanout=cfg.fanout, topk1=b.topk,
+                            topk2=cfg.topk2, tail=b.tail, n_gist=b.M, out=out, lse=lse, sel2=s2,
+                            sel1=s1, workspace=ws, stream=stream)
+
+    step(0)
+    torch.cuda.synchronize()
+    if inp.planted2 is not None:
+        assert torch.equal(s2.long(), inp.planted2), "level-2 selection differs from the planted set"
+        assert torch.equal(s1.long(), inp.planted1), "level-1 selection differs from the planted set"
+    nb = hier_bytes(cfg, s1.cpu().numpy() if b.topk else [])
+    n_marks = gsa.gsa_profile_marks()
+    names = ["gist_kernel (level 2)", "gist_kernel (candidates)", "unfold_kernel"][:n_marks - 1]
+    keys = ["l2", "cand", "unfold"][:n_marks - 1]
+    ms_per_step, per = timed_steps(gsa, step, args, n_marks)
+    kernels = {}
+    for j, (nm, kk) in enumerate(zip(names, keys)):
+        ms = float(per[:, j].mean())
+        kernels[nm] = {"ms": ms, "alg_bytes": nb[kk], "GB_s": nb[kk] / (ms / 1e3) / 1e9}
+    call_ms = float(per.sum(axis=1).mean())
+    alg_b = sum(nb.values())
+    main = max(kernels, key=lambda k: kernels[k]["ms"])
+    qheads = B * Hq
+    return {
+        "metric": "GSA two-level decode query-heads/s + achieved HBM GB/s (1M ctx, C=16, G=16, k2=8, k1=16, bf16)",
+        "value": qheads / (ms_per_step / 1e3),
+        "unit": "query-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b.dtype,
+        "data": "synthetic (seeded Gaussian q/K/V, planted top-k at both levels with margin >= 0.5)",
+        "config": {"workload": f"{cfg.name}: two-level GQA decode step, B={b.batch}, Hq={b.n_q_heads}, "
+                               f"Hkv={b.n_kv_heads}, D={b.head_dim}, N={b.n_raw}, C={b.chunk}, "
+                               f"G={cfg.fanout}, k2={cfg.topk2}, k1={b.topk}, T={b.tail}",
+                   "global_batch": b.batch, "seq_len": b.n_raw, "parallelism": "none (1 GPU)",
+                   "cache_layers_rotated": layers},
+        "roofline": {"bound": "hbm", "achieved": alg_b / (call_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": alg_b / (call_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                     "traffic": None, "kernel": "whole call (three launches)",
+                     "alg_bytes_per_launch": alg_b, "launch_ms_mean": call_ms},
+        "kernels": kernels,
+    }
 
 
 # --------------------------------------------------------------- prefill ---
@@ -428,6 +531,8 @@ def main():
         res = run_decode_bench(args)
     elif isinstance(cfg, gi.PrefillConfig):
         res = run_prefill_bench(args)
+    elif isinstance(cfg, gi.HierConfig):
+        res = run_hier_bench(args)
     else:
         raise SystemExit(f"--config {args.config}: no benchmark for this workload yet")
     print(json.dumps(res), flush=True)

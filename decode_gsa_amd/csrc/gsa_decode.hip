@@ -1216,13 +1216,15 @@ constexpr int kUBR = 16;                // rows per stage
 constexpr int kUNB = 4;                 // stages in a wave's ring
 constexpr int kUTile = kUBR * 256;      // one stage's K (or V) rows
 constexpr int kUStage = 2 * kUTile;
-constexpr int kUMaxGist = 4096;         // group scores kept in LDS
-constexpr int kUMinUnits = 256;         // units needed to fill the chip
+constexpr int kUMaxGist = (int)kUnitMaxGist;   // gists of a unit selected from LDS (one workgroup)
+constexpr int kUWgItems = (int)kUnitWgItems;   // group scores a workgroup keeps in LDS
+constexpr int kUMaxSel = (int)kUnitMaxSel;     // scores one unit's selection reads
 // cache policy of the row loads: nontemporal (each row is read once per call)
 constexpr int kUNt = 2;
 static_assert(kUW == kWaves, "the selection helpers assume the workgroup size");
 static_assert(kUW == 4, "the merge combines four wave states");
-static_assert(kUMaxGist / kThreads == 16 && kCandMax == 64, "selection layout: four 16-byte reads per thread");
+static_assert(kUMaxGist % (16 * kThreads) == 0 && kUMaxSel % (16 * kThreads) == 0 && kCandMax == 64,
+              "selection layout: keys in groups of 16 per thread");
 
 typedef __bf16 bf16x8u __attribute__((ext_vector_type(8)));
 typedef float f32x4u __attribute__((ext_vector_type(4)));
@@ -1293,60 +1295,173 @@ __device__ __forceinline__ void u_v_frag(const uint32_t (&addr)[8], i16x4u (&vf)
 struct UnitSelLds {
   uint32_t tw[kWaves];
   int wsum[kWaves];
+  uint32_t top[kWaves][64];               // each wave's 64 largest of the threads' top-4 keys
+  uint32_t tau;
   // candidates (key << 32 | ~id) in id order; [kCandMax, 2 kCandMax) takes
   // the writes of the other items
   unsigned long long ck[2 * kCandMax];
   int pr[kWaves][kCandMax];               // partial ranks
 };
 
-__device__ __forceinline__ void lds_topk(const float* __restrict__ sc, int n, int k, float* __restrict__ gscratch,
-                                         int unit, int32_t* __restrict__ dst, UnitSelLds& S, TopkLds& T) {
+// One compare-exchange step of a descending bitonic sort of 256 values held
+// four per lane (element 4 lane + r): partners at distance J < 4 are in the
+// same lane, farther ones J/4 lanes away.
+template <int K, int J>
+__device__ __forceinline__ void bitonic4_step(uint32_t (&x)[4]) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (J >= 4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = 4 * lane + r;
+      const uint32_t y = lane_xor<J / 4>(x[r]);
+      const bool keep_max = ((e & J) == 0) == ((e & K) == 0);
+      x[r] = keep_max ? max(x[r], y) : min(x[r], y);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if ((r & J) == 0) {
+        const bool desc = ((4 * lane + r) & K) == 0;
+        const uint32_t a = x[r], b = x[r | J];
+        x[r] = desc ? max(a, b) : min(a, b);
+        x[r | J] = desc ? min(a, b) : max(a, b);
+      }
+    }
+  }
+}
+template <int K, int J>
+__device__ __forceinline__ void bitonic4_stage(uint32_t (&x)[4]) {
+  bitonic4_step<K, J>(x);
+  if constexpr (J > 1) bitonic4_stage<K, J / 2>(x);
+}
+template <int K>
+__device__ __forceinline__ void bitonic4_from(uint32_t (&x)[4]) {
+  bitonic4_stage<K, K / 2>(x);
+  if constexpr (K < 256) bitonic4_from<K * 2>(x);
+}
+// 256 values, four per lane, sorted descending over the wave.
+__device__ __forceinline__ void wave_sort4(uint32_t (&x)[4]) { bitonic4_from<2>(x); }
+
+// k-th largest (k <= 64) of the union of every thread's four largest keys: a
+// lower bound on the workgroup's k-th largest key (they are distinct items),
+// equal to it unless one thread holds more than four of the k largest. Each
+// wave sorts its 256 top-4 keys; wave 0 sorts the four waves' 64 largest.
+template <int PER>
+__device__ __forceinline__ uint32_t tau_top4(const uint32_t (&key)[PER], int k, UnitSelLds& S) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t t[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const uint32_t v = key[j];
+    const uint32_t n1 = max(t[1], min(t[0], v)), n2 = max(t[2], min(t[1], v)), n3 = max(t[3], min(t[2], v));
+    t[0] = max(t[0], v);
+    t[1] = n1;
+    t[2] = n2;
+    t[3] = n3;
+  }
+  wave_sort4(t);
+  if (lane < 16) *reinterpret_cast<uint4*>(&S.top[w][4 * lane]) = make_uint4(t[0], t[1], t[2], t[3]);
+  __syncthreads();
+  if (w == 0) {   // a scalar branch: the whole wave takes it
+    const uint4 v = *reinterpret_cast<const uint4*>(&S.top[lane >> 4][4 * (lane & 15)]);
+    uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    wave_sort4(u);
+    const int r = (k - 1) & 3;
+    const uint32_t pick = r == 0 ? u[0] : r == 1 ? u[1] : r == 2 ? u[2] : u[3];
+    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)pick, (k - 1) >> 2);
+    if (lane == 0) S.tau = tau;
+  }
+  __syncthreads();
+  return S.tau;
+}
+
+// Four 16-byte LDS reads that wait for themselves (the compiler does not see
+// them, so it adds no wait for loads in flight).
+__device__ __forceinline__ void lds_read4x16(const uint32_t (&ad)[4], uint4 (&v)[4]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+      : "memory");
+}
+
+// PER: keys per thread at most (n <= PER * kThreads). FROM_LDS: the scores are
+// an LDS array of PER * kThreads floats; otherwise gscores holds them in
+// device memory, written by other workgroups with device-scope stores.
+template <int PER, bool FROM_LDS>
+__device__ __forceinline__ void unit_select(const float* __restrict__ sc, int n, int k, float* __restrict__ gscores,
+                                            int64_t gstride, int unit, int32_t* __restrict__ dst, UnitSelLds& S,
+                                            TopkLds& T) {
   // Written to keep decisions in vector arithmetic: with one wave per SIMD
   // every vector -> scalar -> vector round trip costs a full pipeline drain.
   typedef unsigned long long u64;
-  constexpr int kPerMax = kUMaxGist / kThreads;
+  constexpr int kPerMax = PER;
+  static_assert(PER % 16 == 0, "keys come in groups of 16");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (k >= n) {
     for (int i = tid; i < n; i += kThreads) dst[i] = i;
     return;
   }
-  const int per = (n + 4 * kThreads - 1) / (4 * kThreads) * 4;   // a multiple of 4, <= 16
+  const int per = (n + 4 * kThreads - 1) / (4 * kThreads) * 4;   // a multiple of 4, <= PER
   const int i0 = tid * per;
   const int nv = max(0, min(per, n - i0));   // this thread's items
-  // 1. keys: four 16-byte reads inside the score array (kUMaxGist floats),
-  // all in flight together; entries past this thread's items are ignored
+  // 1. keys, every read in bounds and in flight with the others of its group
   uint32_t key[kPerMax];
-  {
+  if constexpr (FROM_LDS) {
     const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)sc;
-    uint32_t ad[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ad[q] = base + 16u * (uint32_t)min(i0 / 4 + q, kUMaxGist / 4 - 1);
-    uint4 v0, v1, v2, v3;
-    __asm__ volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
-        : "memory");
-    const uint32_t raw[kPerMax] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w,
-                                   v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+    for (int grp = 0; grp < PER / 16; ++grp) {
+      uint32_t ad[4];
 #pragma unroll
-    for (int j = 0; j < kPerMax; ++j) key[j] = j < nv ? order_key(__uint_as_float(raw[j])) : 0u;
+      for (int q = 0; q < 4; ++q) ad[q] = base + 16u * (uint32_t)min(i0 / 4 + 4 * grp + q, PER * kThreads / 4 - 1);
+      uint4 v[4];
+      lds_read4x16(ad, v);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t raw[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * grp + 4 * q + e;
+          key[j] = j < nv ? order_key(__uint_as_float(raw[e])) : 0u;
+        }
+      }
+    }
+  } else {
+    // 16-byte device-scope loads, all issued together; the buffer covers the
+    // unit's padded score row (gstride floats, a multiple of 4) and a read
+    // past it returns 0 without touching memory: groups past this thread's
+    // `per` items are sent there
+    const CohBuf P(gscores, (uint32_t)gstride * 4u);
+#pragma unroll
+    for (int q = 0; q < kPerMax / 4; ++q) {
+      const uint4 v = P.u128(4 * q < per ? (uint32_t)(i0 + 4 * q) : (uint32_t)gstride);
+      const uint32_t raw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[4 * q + e] = 4 * q + e < nv ? order_key(__uint_as_float(raw[e])) : 0u;
+    }
   }
   uint32_t mx = 0u;
 #pragma unroll
   for (int j = 0; j < kPerMax; ++j) mx = max(mx, key[j]);
-  // (the lane read stays outside any branch: every lane takes part)
-  const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(mx), k - 1);
-  if (lane == 0) S.tw[w] = tw;
-  __syncthreads();
-  uint32_t tau = S.tw[0];
+  uint32_t tau;
+  if (k <= 16) {
+    // (the lane read stays outside any branch: every lane takes part)
+    const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(mx), k - 1);
+    if (lane == 0) S.tw[w] = tw;
+    __syncthreads();
+    tau = S.tw[0];
 #pragma unroll
-  for (int i = 1; i < kWaves; ++i) tau = max(tau, S.tw[i]);
+    for (int i = 1; i < kWaves; ++i) tau = max(tau, S.tw[i]);
+  } else {
+    // a wave's k-th largest thread maximum is a weak bound for large k
+    tau = tau_top4(key, k, S);
+  }
   // Items that are not there have key 0; a real item has key 0 only for a
   // NaN score with every bit set, so tau >= 1 selects exactly the items.
   tau = max(tau, 1u);
@@ -1385,10 +1500,12 @@ __device__ __forceinline__ void lds_topk(const float* __restrict__ sc, int n, in
   }
   __syncthreads();
   if (total > kCandMax) {   // uniform: heavy ties at the threshold
-    for (int i = tid; i < n; i += kThreads) gscratch[i] = sc[i];
-    done_stores();
+    if constexpr (FROM_LDS) {   // the radix select reads device memory
+      for (int i = tid; i < n; i += kThreads) gscores[i] = sc[i];
+      done_stores();
+    }
     __syncthreads();
-    block_topk(gscratch, n, k, IdMap{nullptr, 0, 0, 0, 0}, unit, dst, T);
+    block_topk(gscores, n, k, IdMap{nullptr, 0, 0, 0, 0}, unit, dst, T);
     return;
   }
   // 3. rank of candidate `lane` against candidates 16 w .. 16 w + 15: the
@@ -1430,6 +1547,12 @@ struct UnitArgs {
   int32_t C, k, T;
   float scale_log2;       // softmax logits in log2 units
   float score_mul;        // group score = sum_h(q_h . k) * score_mul
+  // several workgroups per unit (S > 1, and S2 in the unfold launch): partial
+  // states [units][NP][part_stride] and per-unit arrival counters
+  int32_t S, S2, NP;
+  int64_t part_stride;
+  float* part;
+  uint32_t* cnt;
 };
 
 struct UnitLds {
@@ -1444,8 +1567,9 @@ struct UnitLds {
       float o[kUW][16][128];
     } mrg;
   } u;
-  float scores[kUMaxGist];
+  float scores[kUWgItems];
   int32_t sel[kFastSel];
+  uint32_t s_old;
 };
 
 // One wave's running softmax state: lane (h, j) holds head h's max and its
@@ -1461,7 +1585,8 @@ struct UState {
 template <bool FIRST>
 __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const char* __restrict__ Vb, int i0,
                                             int i1, const UnitArgs& a, const bf16x8u (&qf)[4], UState& st,
-                                            char* ring, float* lds_scores, const int32_t* lds_sel) {
+                                            char* ring, float* lds_scores, const int32_t* lds_sel,
+                                            int score_base = 0) {
   const int n = i1 - i0;
   if (n <= 0) return;
   const int lane = threadIdx.x & 63;
@@ -1531,7 +1656,7 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float g = group_sum<16>(s[r]);
-        if (hq == 0 && i_base + r < i1 && i_base + r < M) lds_scores[i_base + r] = g * a.score_mul;
+        if (hq == 0 && i_base + r < i1 && i_base + r < M) lds_scores[i_base + r - score_base] = g * a.score_mul;
       }
     }
     float x[4];
@@ -1593,51 +1718,13 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
   }
 }
 
+// The four waves' softmax states combined: into out/lse (slot == nullptr) or
+// into one partial (m, l, acc[128] per head) written with device-scope stores.
 template <int G>
-__global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
-  __shared__ __attribute__((aligned(16))) UnitLds L;
-  // the wave index as a scalar: each wave's item ranges and trip counts are
-  // then uniform, and the row loops branch on scalars
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+__device__ __forceinline__ void unit_combine(UnitLds& L, const UState& st, int w, float* __restrict__ out,
+                                             float* __restrict__ lse, float* __restrict__ slot) {
+  const int tid = threadIdx.x, lane = tid & 63;
   const int hq = lane & 15, jg = lane >> 4;
-  const int unit = blockIdx.x;
-  const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
-  const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
-  // query fragments: lane (h, j) holds q_h[32 ks + 8 j .. +8], zero past g heads
-  bf16x8u qf[4];
-  {
-    const char* qb = reinterpret_cast<const char*>(a.q) + ((size_t)unit * G + (hq < G ? hq : 0)) * 256 + 16 * jg;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 v = hq < G ? load16(qb + 64 * ks) : make_uint4(0u, 0u, 0u, 0u);
-      qf[ks] = __builtin_bit_cast(bf16x8u, v);
-    }
-    // settle here: a first use inside the row loop would wait for every load
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) __asm__ volatile("" : "+v"(qf[ks]));
-  }
-  UState st;
-  st.m = kMinus;
-  st.l = 0.f;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4u{0.f, 0.f, 0.f, 0.f};
-  char* ring = L.u.ring[w][0];
-  // gists and tail as one item range, split in four consecutive shares
-  const int M = (int)a.M;
-  const int n1 = M + a.T;
-  const int per1 = (n1 + kUW - 1) / kUW;
-  unit_stream<true>(Kb, Vb, min(n1, w * per1), min(n1, (w + 1) * per1), a, qf, st, ring, L.scores, L.sel);
-  if (a.k > 0) {
-    __syncthreads();   // every group score is in LDS, every ring idle
-    float* gs = a.scores + (size_t)unit * a.score_stride;
-    lds_topk(L.scores, M, a.k, gs, unit, L.sel, L.u.sel.s, L.u.sel.t);
-    __syncthreads();
-    const int items = a.k * a.C;
-    const int per2 = (items + kUW - 1) / kUW;
-    unit_stream<false>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
-                       L.sel);
-  }
-  // merge the four waves' states
   __syncthreads();   // LDS changes role: rings -> merge
   float lw = st.l + __uint_as_float(lane_xor<16>(__float_as_uint(st.l)));
   lw += __uint_as_float(lane_xor<32>(__float_as_uint(lw)));
@@ -1668,20 +1755,143 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
       ac.z = fmaf(ov[ww].z, f[ww], ac.z);
       ac.w = fmaf(ov[ww].w, f[ww], ac.w);
     }
-    const float inv = 1.f / Sm;
-    *reinterpret_cast<float4*>(a.out + ((size_t)unit * G + h) * 128 + d4) =
-        make_float4(ac.x * inv, ac.y * inv, ac.z * inv, ac.w * inv);
-    if (d4 == 0 && a.lse) a.lse[(size_t)unit * G + h] = (Mx + log2f(Sm)) * kLn2;
+    if (slot == nullptr) {
+      const float inv = 1.f / Sm;
+      *reinterpret_cast<float4*>(out + h * 128 + d4) = make_float4(ac.x * inv, ac.y * inv, ac.z * inv, ac.w * inv);
+      if (d4 == 0 && lse) lse[h] = (Mx + log2f(Sm)) * kLn2;
+    } else {
+      float* hs = slot + h * (128 + 2);
+      st_coh(hs + 2 + d4, ac.x);
+      st_coh(hs + 3 + d4, ac.y);
+      st_coh(hs + 4 + d4, ac.z);
+      st_coh(hs + 5 + d4, ac.w);
+      if (d4 == 0) {
+        st_coh(hs, Mx);
+        st_coh(hs + 1, Sm);
+      }
+    }
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
+  __shared__ __attribute__((aligned(16))) UnitLds L;
+  // the wave index as a scalar: each wave's item ranges and trip counts are
+  // then uniform, and the row loops branch on scalars
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hq = lane & 15, jg = lane >> 4;
+  const int S = a.S;
+  const int unit = blockIdx.x / S, split = blockIdx.x - unit * S;
+  const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
+  const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
+  // query fragments: lane (h, j) holds q_h[32 ks + 8 j .. +8], zero past g heads
+  bf16x8u qf[4];
+  {
+    const char* qb = reinterpret_cast<const char*>(a.q) + ((size_t)unit * G + (hq < G ? hq : 0)) * 256 + 16 * jg;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 v = hq < G ? load16(qb + 64 * ks) : make_uint4(0u, 0u, 0u, 0u);
+      qf[ks] = __builtin_bit_cast(bf16x8u, v);
+    }
+    // settle here: a first use inside the row loop would wait for every load
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) __asm__ volatile("" : "+v"(qf[ks]));
+  }
+  UState st;
+  st.m = kMinus;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4u{0.f, 0.f, 0.f, 0.f};
+  char* ring = L.u.ring[w][0];
+  // gists and tail as one item range: S consecutive shares, each in four wave shares
+  const int M = (int)a.M;
+  const int n1 = M + a.T;
+  const int perw = (n1 + S - 1) / S;
+  const int w0 = min(n1, split * perw), w1 = min(n1, w0 + perw);
+  const int per1 = (w1 - w0 + kUW - 1) / kUW;
+  unit_stream<true>(Kb, Vb, min(w1, w0 + w * per1), min(w1, w0 + (w + 1) * per1), a, qf, st, ring, L.scores,
+                    L.sel, w0);
+  float* gs = a.scores + (size_t)unit * a.score_stride;
+  const int items = a.k * a.C;
+  const int per2 = (items + kUW - 1) / kUW;
+  if (S == 1) {
+    if (a.k > 0) {
+      __syncthreads();   // every group score is in LDS, every ring idle
+      unit_select<kUMaxGist / kThreads, true>(L.scores, M, a.k, gs, a.score_stride, unit, L.sel, L.u.sel.s,
+                                               L.u.sel.t);
+      __syncthreads();
+      unit_stream<false>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
+                         L.sel);
+    }
+    unit_combine<G>(L, st, w, a.out + (size_t)unit * G * 128, a.lse ? a.lse + (size_t)unit * G : nullptr,
+                    nullptr);
+  } else {
+    // hand the split's partial state (and group scores) on: with k > 0 to the
+    // unfold launch, else to the unit's last workgroup, which merges
+    // (device-scope stores: the XCDs' L2s are not coherent)
+    float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
+    unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)split * a.part_stride);
+    if (a.k > 0) {
+      for (int i = w0 + tid; i < min(w1, M); i += kUW * 64) st_coh(gs + i, L.scores[i - w0]);
+      return;
+    }
+    if (!arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)S, &L.s_old)) return;
+    merge_unit<128, G>(part_u, S, (uint32_t)a.part_stride, a.out + (size_t)unit * G * 128,
+                       a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
+    return;
   }
   if (a.sel)
     for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
 }
 
-// The one-workgroup-per-unit path applies: bf16, D = 128, enough units to
-// fill the chip, the group scores and the selection small enough for LDS.
-bool unit_path_ok(const DecodePlan& pl) {
-  return pl.dtype == GSA_BF16 && pl.D == 128 && pl.units >= kUMinUnits && pl.M <= kUMaxGist &&
-         pl.k <= kFastSel && pl.R < (1ll << 31) && (int64_t)pl.k * pl.C + pl.M + pl.T < (1ll << 31);
+
+// Second launch of the several-workgroups-per-unit path (k > 0): workgroup
+// (unit, p) makes the unit's selection from the group scores the stream
+// launch wrote (every workgroup of the unit makes the same one), streams
+// share p of the chosen chunks' raw rows, and hands its partial state on; the
+// unit's last workgroup merges the S stream and S2 unfold partials.
+template <int G>
+__global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs a) {
+  __shared__ __attribute__((aligned(16))) UnitLds L;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hq = lane & 15, jg = lane >> 4;
+  const int S2 = a.S2;
+  const int unit = blockIdx.x / S2, part = blockIdx.x - unit * S2;
+  const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
+  const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
+  bf16x8u qf[4];
+  {
+    const char* qb = reinterpret_cast<const char*>(a.q) + ((size_t)unit * G + (hq < G ? hq : 0)) * 256 + 16 * jg;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 v = hq < G ? load16(qb + 64 * ks) : make_uint4(0u, 0u, 0u, 0u);
+      qf[ks] = __builtin_bit_cast(bf16x8u, v);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) __asm__ volatile("" : "+v"(qf[ks]));
+  }
+  UState st;
+  st.m = kMinus;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4u{0.f, 0.f, 0.f, 0.f};
+  float* gs = a.scores + (size_t)unit * a.score_stride;
+  unit_select<kUMaxSel / kThreads, false>(nullptr, (int)a.M, a.k, gs, a.score_stride, unit, L.sel, L.u.sel.s,
+                                          L.u.sel.t);
+  __syncthreads();
+  const int items = a.k * a.C;
+  const int perp = (items + S2 - 1) / S2;
+  const int p0 = min(items, part * perp), p1 = min(items, p0 + perp);
+  const int per2 = (p1 - p0 + kUW - 1) / kUW;
+  unit_stream<false>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st, L.u.ring[w][0],
+                     L.scores, L.sel);
+  float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
+  unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)(a.S + part) * a.part_stride);
+  if (!arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)S2, &L.s_old)) return;
+  merge_unit<128, G>(part_u, a.S + S2, (uint32_t)a.part_stride, a.out + (size_t)unit * G * 128,
+                     a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
+  if (a.sel)
+    for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
 }
 
 template <int G>
@@ -1692,8 +1902,12 @@ gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const 
   u.scores = reinterpret_cast<float*>(ws + pl.off_scores); u.score_stride = pl.score_stride;
   u.R = pl.R; u.N = pl.N; u.M = pl.M; u.C = pl.C; u.k = pl.k; u.T = pl.T;
   u.scale_log2 = pl.scale * kLog2e; u.score_mul = pl.scale / G;
+  u.S = pl.unit_S; u.S2 = pl.unit_S2; u.NP = pl.NP; u.part_stride = part_stride(G, 128);
+  u.part = reinterpret_cast<float*>(ws + pl.off_part);
+  u.cnt = ctrl_of(ws, pl.off_ctrl, 0);
   prof_begin_call();
-  prof_launch((unit_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+  prof_launch((unit_kernel<G>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0, st, u);
+  if (pl.unit_S2 > 0) prof_launch((unit_unfold_kernel<G>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st, u);
   return launch_status("gsa_decode launch");
 }
 
@@ -1752,7 +1966,7 @@ extern "C" gsa_status_t gsa_decode(const gsa_decode_params* p, const void* q, co
   if ((s = check_workspace(workspace, workspace_bytes, pl.total)) != GSA_OK) return s;
   char* ws = reinterpret_cast<char*>(workspace);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (unit_path_ok(pl)) {
+  if (pl.unit_S > 0) {
     switch (pl.g) {
       case 1: return run_unit<1>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
       case 2: return run_unit<2>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);

@@ -56,6 +56,12 @@ struct CohBuf {
   __device__ __forceinline__ uint32_t u32(uint32_t word) const {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)(word * 4u), 0, 16 /* sc1 */);
   }
+  // four consecutive words from a multiple of 4
+  __device__ __forceinline__ uint4 u128(uint32_t word) const {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(word * 4u), 0, 16 /* sc1 */);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
 };
 
 // 16-byte global load of raw bits.

@@ -1,6 +1,8 @@
 // Host-side validation and planning for libgsa (no HIP calls in this file).
 #include "gsa_plan.hpp"
 
+#include <algorithm>
+
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -27,6 +29,25 @@ constexpr int64_t kMinRows = 64;
 constexpr int64_t kMinUnfoldRows = 64;
 // A gist workgroup gathers its scores in LDS: at most this many items each.
 constexpr int64_t kMaxTaskItems = 1024;
+
+// Workgroups per unit of the one-workgroup-per-unit path, 0 if it does not
+// apply: bf16, D = 128, k <= kFastSelect, rows addressable in 31 bits; one
+// workgroup per unit when there are enough units, else enough splits to fill
+// the chip; every split's gists fit its LDS and the selection's scores fit
+// kUnitMaxSel.
+static int32_t unit_splits(const DecodePlan& d) {
+  if (d.dtype != GSA_BF16 || d.D != 128 || d.k > kFastSelect) return 0;
+  if (d.R >= ((int64_t)1 << 31) || (int64_t)d.k * d.C + d.M + d.T >= ((int64_t)1 << 31)) return 0;
+  if (d.k > 0 && d.M > kUnitMaxSel) return 0;
+  const int64_t items = d.M + d.T;
+  if (d.units >= kUnitMinWGs && d.M <= kUnitMaxGist) return 1;
+  int64_t s = ceil_div(kUnitMinWGs, d.units);
+  const int64_t need = ceil_div(items, kUnitWgItems);   // gists + tail per split <= LDS scores
+  if (s < need) s = need;
+  if (s > kUnitMaxSplits) return 0;
+  if (ceil_div(items, s) < 64) s = ceil_div(items, 64);
+  return (int32_t)(s < 2 ? 2 : s);
+}
 
 int32_t splits_for(int64_t rows, int64_t units, int64_t min_rows = kMinRows) {
   if (rows <= 0) return 1;
@@ -137,6 +158,13 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   d.S2 = items > 0 ? (int32_t)ceil_div(items, d.items_per_split) : 0;
   d.NP = d.S + d.S2;
   d.score_stride = d.k > 0 ? (d.M + 63) / 64 * 64 : 0;
+  d.unit_S = unit_splits(d);
+  d.unit_S2 = 0;
+  if (d.unit_S > 1) {
+    // the unfold launch: the stream's workgroup count, at least 64 rows each
+    d.unit_S2 = d.k > 0 ? (int32_t)std::min<int64_t>(d.unit_S, ceil_div(items, 64)) : 0;
+    if (d.NP < d.unit_S + d.unit_S2) d.NP = d.unit_S + d.unit_S2;   // stream + unfold partials
+  }
   size_t off = 0;
   d.off_ctrl = off;
   off = align_up(off + ctrl_bytes(units));

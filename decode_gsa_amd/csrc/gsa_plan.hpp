@@ -19,6 +19,15 @@ constexpr size_t kAlign = 256;
 // Selections of at most this many items use wave-level bit-serial selects;
 // larger ones a block-wide radix select.
 constexpr int32_t kFastSelect = 64;
+// One-workgroup-per-unit decode (bf16, D = 128, k <= kFastSelect): a unit is
+// cut into unit_S workgroups, enough of them to fill the chip (kUnitMinWGs);
+// each keeps at most kUnitMaxGist group scores in LDS, and the unit's
+// selection reads at most kUnitMaxSel scores.
+constexpr int32_t kUnitMinWGs = 256;
+constexpr int64_t kUnitMaxGist = 4096;     // one workgroup per unit: gists kept in LDS
+constexpr int64_t kUnitWgItems = 5120;     // several per unit: gist + tail rows per workgroup
+constexpr int64_t kUnitMaxSel = 16384;
+constexpr int32_t kUnitMaxSplits = 256;
 // A two-level call's level-2 selection is staged in LDS: topk2 at most this.
 constexpr int32_t kMaxTopk2 = 1024;
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -74,6 +83,10 @@ struct DecodePlan {
   // byte offsets inside the workspace (control words first)
   size_t off_ctrl, off_scores, off_sel, off_part, total;
   int64_t score_stride; // floats per unit in the score region (read by the unfold pass)
+  // one-workgroup-per-unit path: workgroups per unit, 0 when the shape takes
+  // the gist + unfold passes instead; with unit_S > 1 a second launch of
+  // unit_S2 workgroups per unit selects and unfolds (k > 0)
+  int32_t unit_S, unit_S2;
   int64_t sel_stride;   // ints per unit in the selection region (large k only)
 };
 

@@ -181,9 +181,12 @@ gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, const void* q,
  * attaches them to its kernel launches (hipExtLaunchKernel): events[0] takes
  * the start of the call's first kernel and events[i] the end of its i-th
  * kernel, for as many events as there are. Launches per call:
- *   gsa_decode: one (the whole step of each (batch, kv-head) unit in one
- *     workgroup) for bf16 with D = 128, B*Hkv >= 256, n_gist <= 4096 and
- *     topk <= 64; otherwise a gist pass, then an unfold pass when topk > 0;
+ *   gsa_decode, bf16 with D = 128, topk <= 64, n_gist <= 16384 when topk > 0
+ *     and n_gist + tail <= 256 * 5120: one launch when each (batch, kv-head)
+ *     unit takes one workgroup (B*Hkv >= 256 and n_gist <= 4096) or topk = 0;
+ *     otherwise a stream launch (several workgroups per unit) and a
+ *     select-and-unfold launch;
+ *   gsa_decode, other shapes: a gist pass, then an unfold pass when topk > 0;
  *   gsa_decode_hier: level-2 pass, level-1 candidate pass, unfold pass when
  *     topk1 > 0;
  *   gsa_prefill_blocksparse: selection when topk > 0, then attention.

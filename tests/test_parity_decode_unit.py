@@ -1,7 +1,9 @@
 """GPU parity of gsa_decode in its one-workgroup-per-unit launch (bf16,
-head_dim 128, at least 256 (batch, kv-head) units, at most 4096 gists and
-topk <= 64) against the fp64 oracle: bit-exact selections, outputs and lse
-within the stated tolerance (tests/gpu_util.py).
+head_dim 128, topk <= 64): one workgroup per (batch, kv-head) unit with 256
+or more units and at most 4096 gists, otherwise several workgroups per unit
+that hand their partial states and group scores to the unit's last one.
+Checked against the fp64 oracle: bit-exact selections, outputs and lse within
+the stated tolerance (tests/gpu_util.py).
 """
 import dataclasses
 
@@ -37,13 +39,21 @@ CASES = [
     (cfg_of("gqa_32k", n_q_heads=16, n_raw=2048, tail=5), 64),             # g = 2
     (cfg_of("gqa_32k", n_q_heads=64, n_raw=2048), 64),                     # g = 8
     (cfg_of("gqa_32k", batch=40, n_raw=1500, tail=12), 64),                # 320 units, shortest tail
+    (cfg_of("gqa_32k", n_raw=4096, topk=40), 64),                          # k > 16: top-4 threshold
     (cfg_of("c8_131k", batch=32, n_raw=8192), 48),                         # C = 8, k = 64
     (cfg_of("c32_131k", batch=32, n_raw=8192), 48),                        # C = 32
     (cfg_of("gqa_32k", n_raw=2048, topk=0, plant="none"), 64),             # gists + tail only
     (cfg_of("gqa_32k", n_raw=1024, topk=64, plant="none"), 64),            # every chunk selected
     (cfg_of("gqa_32k", n_raw=12, n_gist=0, topk=0, tail=12, plant="none"), 64),   # no gists
     (cfg_of("gqa_32k", n_raw=65536, tail=300), 12),                        # 4096 gists: the LDS limit
-    (cfg_of("gqa_32k", n_raw=65552, tail=64), 12),                         # 4097 gists: the other path
+    (cfg_of("gqa_32k", n_raw=65552, tail=64), 12),                         # 4097 gists: two workgroups per unit
+    # several workgroups per unit
+    (cfg_of("c8_131k", n_raw=32768), None),                                # 64 units x 4, C = 8, k = 64
+    (cfg_of("c32_131k", n_raw=65536), 32),                                 # 64 units x 4, C = 32
+    (cfg_of("gqa_32k", batch=1, n_kv_heads=1, n_q_heads=4, n_raw=8192, tail=70), None),   # 1 unit x 40
+    (cfg_of("gqa_32k", batch=3, n_kv_heads=2, n_q_heads=16, n_raw=9000, n_gist=562, tail=40), None),  # ragged
+    (cfg_of("gqa_32k", batch=2, n_raw=4096, topk=0, plant="none"), None),  # gists + tail only
+    (cfg_of("gqa_32k", batch=1, n_raw=16384 * 16, tail=64), 8),            # 16384 gists: the selection limit
 ]
 
 
@@ -72,6 +82,22 @@ def test_decode_unit_ties_fall_back_to_radix(gsa):
     torch.cuda.synchronize()
     assert (to_np(sel) == np.arange(k)[None, None, :]).all()
     run_decode(gsa, inp, cfg, units=sample_units(cfg, n=32, seed=1))
+
+
+@pytest.mark.parametrize("batch", [32, 2], ids=["one-wg", "split"])
+def test_decode_unit_ties_radix_any_split(gsa, batch):
+    """All scores equal: the radix select over the scores in the workspace
+    decides, with one workgroup per unit and with several."""
+    C, M, k = 16, 256, 16
+    T = 64
+    cfg = cfg_of("gqa_32k", batch=batch, n_raw=M * C, topk=k, tail=T, plant="none")
+    say(f"decode unit-path ties {cfg}")
+    inp = gi.make_decode(cfg, 3104 + batch, device="cuda")
+    inp.q.zero_()
+    out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=C, topk=k, tail=T)
+    torch.cuda.synchronize()
+    assert (to_np(sel) == np.arange(k)[None, None, :]).all()
+    run_decode(gsa, inp, cfg, units=sample_units(cfg, n=16, seed=4))
 
 
 def test_decode_unit_selects_chunk_inside_tail(gsa):
