@@ -1404,6 +1404,7 @@ __device__ __forceinline__ void unit_select(const float* __restrict__ sc, int n,
   static_assert(PER % 16 == 0, "keys come in groups of 16");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (k <= 0) return;
   if (k >= n) {
     for (int i = tid; i < n; i += kThreads) dst[i] = i;
     return;
@@ -1553,6 +1554,15 @@ struct UnitArgs {
   int64_t part_stride;
   float* part;
   uint32_t* cnt;
+  // two-level decode: level-2 gist arrays [units][M2][D], fanout G2, top-k2,
+  // level-1 candidates (k2 G2 children + orphans), level-2 scores and ids
+  const void* K2;
+  const void* V2;
+  int64_t M2;
+  int32_t G2, k2, n_cand;
+  float* s2;
+  int64_t s2_stride;
+  int32_t* sel2;
 };
 
 struct UnitLds {
@@ -1569,6 +1579,7 @@ struct UnitLds {
   } u;
   float scores[kUWgItems];
   int32_t sel[kFastSel];
+  int32_t sel2[kFastSel];
   uint32_t s_old;
 };
 
@@ -1579,14 +1590,24 @@ struct UState {
   float m, l;
 };
 
-// Stream items [i0, i1) through the wave's state. FIRST: items below M are
-// the gists (group scores kept in LDS), the rest the tail rows; otherwise the
-// raw rows of the selected chunks, skipping those the tail attends.
-template <bool FIRST>
+// What unit_stream streams (the scored kinds keep their items' group scores
+// in LDS):
+//   kUKGists   items below M: the gists; then the tail rows          (scored)
+//   kUKUnfold  the raw rows of the chosen chunks (lds_sel: chunk ids),
+//              skipping those the tail attends
+//   kUKL2      items below M2: level-2 gists (their own arrays); then the
+//              tail rows                                             (scored)
+//   kUKCand    level-1 candidates: the G children of each chosen level-2
+//              group (lds_sel: group ids), then the orphans           (scored)
+enum { kUKGists = 0, kUKUnfold = 1, kUKL2 = 2, kUKCand = 3 };
+
+// Stream items [i0, i1) of one kind through the wave's state.
+template <int KIND>
 __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const char* __restrict__ Vb, int i0,
                                             int i1, const UnitArgs& a, const bf16x8u (&qf)[4], UState& st,
                                             char* ring, float* lds_scores, const int32_t* lds_sel,
-                                            int score_base = 0) {
+                                            int score_base = 0, const char* K2b = nullptr,
+                                            const char* V2b = nullptr) {
   const int n = i1 - i0;
   if (n <= 0) return;
   const int lane = threadIdx.x & 63;
@@ -1594,20 +1615,33 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
   const int nb = (n + kUBR - 1) / kUBR;
   const int C = a.C, M = (int)a.M;
   const unsigned tail0 = (unsigned)(a.N - a.T);   // rows and positions fit in 31 bits here
-  // cache row of item i; -1 when there is no such item or the tail owns it.
-  // Raw position p sits in row p + p / C (p + M past the last gist).
+  constexpr bool kScored = KIND != kUKUnfold;
+  const int n_scored = KIND == kUKGists ? M : KIND == kUKL2 ? (int)a.M2 : i1;
+  // cache row of item i; -1 when there is no such item or the tail owns it,
+  // -2 - j for level-2 gist j. Raw position p sits in row p + p / C (p + M
+  // past the last gist).
   auto row_of = [&](int i) -> int {
     if (i >= i1) return -1;
-    if (FIRST) {
-      if (i < M) return i * (C + 1) + C;
-      const unsigned pos = tail0 + (unsigned)(i - M);
+    if (KIND == kUKGists || KIND == kUKL2) {
+      const int nf = KIND == kUKGists ? M : (int)a.M2;
+      if (i < nf) return KIND == kUKGists ? i * (C + 1) + C : -2 - i;
+      const unsigned pos = tail0 + (unsigned)(i - nf);
       return (int)(pos + min(pos / (unsigned)C, (unsigned)M));
+    }
+    if (KIND == kUKCand) {
+      const int kg = a.k2 * a.G2;
+      const unsigned id = i < kg ? (unsigned)lds_sel[i / a.G2] * (unsigned)a.G2 + (unsigned)(i % a.G2)
+                                 : (unsigned)(a.M2 * a.G2 + (i - kg));
+      return (int)(min(id, (unsigned)(M - 1)) * (unsigned)(C + 1) + (unsigned)C);
     }
     const unsigned ci = (unsigned)i / (unsigned)C, jj = (unsigned)i - ci * (unsigned)C;
     const unsigned m = min((unsigned)lds_sel[ci], (unsigned)(M - 1));   // k <= M, so M >= 1
     const unsigned pos = m * (unsigned)C + jj;
     return pos >= tail0 ? -1 : (int)(pos + m);
   };
+  // the unit's level-2 arrays (K2b, V2b), as offsets from the level-1 bases
+  const int64_t k2off = KIND == kUKL2 ? K2b - Kb : 0;
+  const int64_t v2off = KIND == kUKL2 ? V2b - Vb : 0;
   // stage b -> ring slot b % kUNB: lane i loads 16 bytes of row 4u + i/16 into
   // LDS slot i%16, K and V alike. Items past the end of the last stage read
   // row 0 (in bounds, masked), so that every stage issues the same eight loads.
@@ -1619,9 +1653,13 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     for (int u = 0; u < 4; ++u) {
       const int r = 4 * u + (lane >> 4);
       const int row = row_of(i0 + b * kUBR + r);
-      const int64_t off = (int64_t)(row >= 0 ? row : 0) * 256;
-      __builtin_amdgcn_global_load_lds(Kb + off + uk_slot(sl, r) * 16, kd + u * 1024, 16, 0, kUNt);
-      __builtin_amdgcn_global_load_lds(Vb + off + uv_slot(sl, r) * 16, vd + u * 1024, 16, 0, kUNt);
+      int64_t koffr = (int64_t)(row >= 0 ? row : 0) * 256, voffr = koffr;
+      if (KIND == kUKL2 && row <= -2) {
+        koffr = k2off + (int64_t)(-2 - row) * 256;
+        voffr = v2off + (int64_t)(-2 - row) * 256;
+      }
+      __builtin_amdgcn_global_load_lds(Kb + koffr + uk_slot(sl, r) * 16, kd + u * 1024, 16, 0, kUNt);
+      __builtin_amdgcn_global_load_lds(Vb + voffr + uv_slot(sl, r) * 16, vd + u * 1024, 16, 0, kUNt);
     }
   };
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)ring;
@@ -1651,12 +1689,12 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     const int i_base = i0 + b * kUBR + 4 * jg;
     bool ok[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ok[r] = FIRST ? i_base + r < i1 : row_of(i_base + r) >= 0;
-    if (FIRST) {
+    for (int r = 0; r < 4; ++r) ok[r] = kScored ? i_base + r < i1 : row_of(i_base + r) >= 0;
+    if (kScored) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float g = group_sum<16>(s[r]);
-        if (hq == 0 && i_base + r < i1 && i_base + r < M) lds_scores[i_base + r - score_base] = g * a.score_mul;
+        if (hq == 0 && i_base + r < i1 && i_base + r < n_scored) lds_scores[i_base + r - score_base] = g * a.score_mul;
       }
     }
     float x[4];
@@ -1773,7 +1811,10 @@ __device__ __forceinline__ void unit_combine(UnitLds& L, const UState& st, int w
   }
 }
 
-template <int G>
+// HIER: the first launch of two-level decode -- the level-2 gists (their own
+// arrays) and the tail; every workgroup hands its partial state and level-2
+// scores to unit_hier_kernel.
+template <int G, bool HIER>
 __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
   __shared__ __attribute__((aligned(16))) UnitLds L;
   // the wave index as a scalar: each wave's item ranges and trip counts are
@@ -1805,12 +1846,24 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
   char* ring = L.u.ring[w][0];
   // gists and tail as one item range: S consecutive shares, each in four wave shares
   const int M = (int)a.M;
-  const int n1 = M + a.T;
+  const int nf = HIER ? (int)a.M2 : M;   // scored items ahead of the tail
+  const int n1 = nf + a.T;
   const int perw = (n1 + S - 1) / S;
   const int w0 = min(n1, split * perw), w1 = min(n1, w0 + perw);
   const int per1 = (w1 - w0 + kUW - 1) / kUW;
-  unit_stream<true>(Kb, Vb, min(w1, w0 + w * per1), min(w1, w0 + (w + 1) * per1), a, qf, st, ring, L.scores,
-                    L.sel, w0);
+  if constexpr (HIER) {
+    const char* K2b = reinterpret_cast<const char*>(a.K2) + (size_t)unit * a.M2 * 256;
+    const char* V2b = reinterpret_cast<const char*>(a.V2) + (size_t)unit * a.M2 * 256;
+    unit_stream<kUKL2>(Kb, Vb, min(w1, w0 + w * per1), min(w1, w0 + (w + 1) * per1), a, qf, st, ring, L.scores,
+                       L.sel, w0, K2b, V2b);
+    float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
+    unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)split * a.part_stride);
+    float* s2u = a.s2 + (size_t)unit * a.s2_stride;
+    for (int i = w0 + tid; i < min(w1, nf); i += kUW * 64) st_coh(s2u + i, L.scores[i - w0]);
+    return;
+  }
+  unit_stream<kUKGists>(Kb, Vb, min(w1, w0 + w * per1), min(w1, w0 + (w + 1) * per1), a, qf, st, ring, L.scores,
+                        L.sel, w0);
   float* gs = a.scores + (size_t)unit * a.score_stride;
   const int items = a.k * a.C;
   const int per2 = (items + kUW - 1) / kUW;
@@ -1820,7 +1873,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
       unit_select<kUMaxGist / kThreads, true>(L.scores, M, a.k, gs, a.score_stride, unit, L.sel, L.u.sel.s,
                                                L.u.sel.t);
       __syncthreads();
-      unit_stream<false>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
+      unit_stream<kUKUnfold>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
                          L.sel);
     }
     unit_combine<G>(L, st, w, a.out + (size_t)unit * G * 128, a.lse ? a.lse + (size_t)unit * G : nullptr,
@@ -1883,7 +1936,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs a) {
   const int perp = (items + S2 - 1) / S2;
   const int p0 = min(items, part * perp), p1 = min(items, p0 + perp);
   const int per2 = (p1 - p0 + kUW - 1) / kUW;
-  unit_stream<false>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st, L.u.ring[w][0],
+  unit_stream<kUKUnfold>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st, L.u.ring[w][0],
                      L.scores, L.sel);
   float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
   unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)(a.S + part) * a.part_stride);
@@ -1892,6 +1945,95 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs a) {
                      a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
   if (a.sel)
     for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
+}
+
+// Second launch of two-level decode, one workgroup per unit: the level-2
+// selection from the first launch's scores, the level-1 candidates (group
+// scores kept in LDS), their selection, the chosen chunks' raw rows, and the
+// merge of every partial state.
+template <int G>
+__global__ __launch_bounds__(kUW * 64) void unit_hier_kernel(UnitArgs a) {
+  __shared__ __attribute__((aligned(16))) UnitLds L;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hq = lane & 15, jg = lane >> 4;
+  const int unit = blockIdx.x;
+  const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
+  const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
+  bf16x8u qf[4];
+  {
+    const char* qb = reinterpret_cast<const char*>(a.q) + ((size_t)unit * G + (hq < G ? hq : 0)) * 256 + 16 * jg;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 v = hq < G ? load16(qb + 64 * ks) : make_uint4(0u, 0u, 0u, 0u);
+      qf[ks] = __builtin_bit_cast(bf16x8u, v);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) __asm__ volatile("" : "+v"(qf[ks]));
+  }
+  UState st;
+  st.m = kMinus;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4u{0.f, 0.f, 0.f, 0.f};
+  char* ring = L.u.ring[w][0];
+  // level 2: the chosen groups, ascending
+  float* s2u = a.s2 + (size_t)unit * a.s2_stride;
+  unit_select<kUMaxSel / kThreads, false>(nullptr, (int)a.M2, a.k2, s2u, a.s2_stride, unit, L.sel2, L.u.sel.s,
+                                          L.u.sel.t);
+  __syncthreads();
+  // level 1: every candidate gist (scored), four wave shares
+  const int nc = a.n_cand;
+  const int perc = (nc + kUW - 1) / kUW;
+  unit_stream<kUKCand>(Kb, Vb, min(nc, w * perc), min(nc, (w + 1) * perc), a, qf, st, ring, L.scores, L.sel2);
+  if (a.k > 0) {
+    __syncthreads();   // every candidate score is in LDS, every ring idle
+    float* gsc = a.scores + (size_t)unit * a.score_stride;
+    unit_select<kUMaxGist / kThreads, true>(L.scores, nc, a.k, gsc, a.score_stride, unit, L.sel, L.u.sel.s,
+                                            L.u.sel.t);
+    __syncthreads();
+    // candidate index -> chunk id (candidates are in chunk order)
+    if (tid < a.k) {
+      const int c = L.sel[tid], kg = a.k2 * a.G2;
+      L.sel[tid] = c < kg ? L.sel2[c / a.G2] * a.G2 + c % a.G2 : (int)(a.M2 * a.G2) + (c - kg);
+    }
+    __syncthreads();
+    const int items = a.k * a.C;
+    const int per2 = (items + kUW - 1) / kUW;
+    unit_stream<kUKUnfold>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
+                           L.sel);
+  }
+  float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
+  unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)a.S * a.part_stride);
+  done_stores();
+  __syncthreads();
+  merge_unit<128, G>(part_u, a.S + 1, (uint32_t)a.part_stride, a.out + (size_t)unit * G * 128,
+                     a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
+  if (a.sel2)
+    for (int i = tid; i < a.k2; i += kUW * 64) a.sel2[(size_t)unit * a.k2 + i] = L.sel2[i];
+  if (a.sel)
+    for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
+}
+
+template <int G>
+gsa_status_t run_unit_hier(const HierPlan& hp, const void* q, const void* K, const void* V, const void* K2,
+                           const void* V2, float* out, float* lse, int32_t* sel2, int32_t* sel1, char* ws,
+                           hipStream_t st) {
+  const DecodePlan& pl = hp.base;
+  UnitArgs u{};
+  u.q = q; u.K = K; u.V = V; u.out = out; u.lse = lse; u.sel = pl.k > 0 ? sel1 : nullptr;
+  u.scores = reinterpret_cast<float*>(ws + hp.off_sc); u.score_stride = hp.sc_stride;
+  u.R = pl.R; u.N = pl.N; u.M = pl.M; u.C = pl.C; u.k = pl.k; u.T = pl.T;
+  u.scale_log2 = pl.scale * kLog2e; u.score_mul = pl.scale / G;
+  u.S = hp.unit_S; u.S2 = 0; u.NP = hp.NP; u.part_stride = part_stride(G, 128);
+  u.part = reinterpret_cast<float*>(ws + hp.off_part);
+  u.cnt = nullptr;
+  u.K2 = K2; u.V2 = V2; u.M2 = hp.M2; u.G2 = hp.G; u.k2 = hp.k2; u.n_cand = hp.n_cand;
+  u.s2 = reinterpret_cast<float*>(ws + hp.off_s2); u.s2_stride = hp.s2_stride;
+  u.sel2 = hp.k2 > 0 ? sel2 : nullptr;
+  prof_begin_call();
+  prof_launch((unit_kernel<G, true>), dim3(pl.units * hp.unit_S), dim3(kUW * 64), 0, st, u);
+  prof_launch((unit_hier_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+  return launch_status("gsa_decode_hier launch");
 }
 
 template <int G>
@@ -1906,7 +2048,7 @@ gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const 
   u.part = reinterpret_cast<float*>(ws + pl.off_part);
   u.cnt = ctrl_of(ws, pl.off_ctrl, 0);
   prof_begin_call();
-  prof_launch((unit_kernel<G>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0, st, u);
+  prof_launch((unit_kernel<G, false>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0, st, u);
   if (pl.unit_S2 > 0) prof_launch((unit_unfold_kernel<G>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st, u);
   return launch_status("gsa_decode launch");
 }
@@ -2003,6 +2145,16 @@ extern "C" gsa_status_t gsa_decode_hier(const gsa_hier_params* p, const void* q,
       (s = check_ptr(sel1, "sel1", true)) != GSA_OK)
     return s;
   if ((s = check_workspace(workspace, workspace_bytes, hp.total)) != GSA_OK) return s;
+  if (hp.unit_S > 0) {
+    char* ws = reinterpret_cast<char*>(workspace);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    switch (hp.base.g) {
+      case 1: return run_unit_hier<1>(hp, q, k_cache, v_cache, k_l2, v_l2, out, lse, sel2, sel1, ws, hs);
+      case 2: return run_unit_hier<2>(hp, q, k_cache, v_cache, k_l2, v_l2, out, lse, sel2, sel1, ws, hs);
+      case 4: return run_unit_hier<4>(hp, q, k_cache, v_cache, k_l2, v_l2, out, lse, sel2, sel1, ws, hs);
+      case 8: return run_unit_hier<8>(hp, q, k_cache, v_cache, k_l2, v_l2, out, lse, sel2, sel1, ws, hs);
+    }
+  }
   return dispatch<HierRunner>(hp.base.dtype, hp.base.D, hp.base.g, hp, q, k_cache, v_cache, k_l2, v_l2,
                               out, lse, sel2, sel1, reinterpret_cast<char*>(workspace),
                               reinterpret_cast<hipStream_t>(stream));

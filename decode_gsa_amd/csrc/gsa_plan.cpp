@@ -211,6 +211,20 @@ gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
   h.S_c = h.n_cand > 0 ? (int32_t)ceil_div(h.n_cand, h.cand_per_split) : 1;
   h.tail_per_split = (int32_t)ceil_div(d.T, h.S_l2);
   h.NP = h.S_l2 + h.S_c + d.S2;
+  h.unit_S = 0;
+  if (d.dtype == GSA_BF16 && d.D == 128 && d.k <= kFastSelect && h.k2 <= kFastSelect &&
+      h.M2 <= kUnitMaxSel && h.n_cand <= kUnitMaxGist && d.R < ((int64_t)1 << 31) &&
+      (int64_t)d.k * d.C + h.n_cand + h.M2 + d.T < ((int64_t)1 << 31)) {
+    const int64_t items = h.M2 + d.T;
+    int64_t s = ceil_div(kUnitMinWGs, units);
+    if (s < ceil_div(items, kUnitWgItems)) s = ceil_div(items, kUnitWgItems);
+    if (ceil_div(items, s) < 64) s = ceil_div(items, 64);
+    if (s < 1) s = 1;
+    if (s <= kUnitMaxSplits) {
+      h.unit_S = (int32_t)s;
+      if (h.NP < h.unit_S + 1) h.NP = h.unit_S + 1;   // level-2 stream partials + the rest's
+    }
+  }
   h.s2_stride = (h.M2 + 63) / 64 * 64;
   h.sc_stride = d.k > 0 ? (h.n_cand + 63) / 64 * 64 : 0;
   size_t off = 0;

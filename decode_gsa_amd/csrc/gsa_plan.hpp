@@ -107,6 +107,11 @@ struct HierPlan {
   int32_t NP;           // S_l2 + S_c (+ S2 when k1 > 0)
   size_t off_ctrl, off_s2, off_sc, off_sel2, off_sel1, off_part, total;
   int64_t s2_stride, sc_stride, sel2_stride;
+  // one-workgroup-per-unit path (bf16, D = 128, k1, k2 <= 64, at most 16384
+  // level-2 gists and 4096 candidates): workgroups per unit over the level-2
+  // gists and the tail, then one workgroup per unit for the rest; 0 when the
+  // gist passes run instead
+  int32_t unit_S;
 };
 
 gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* out);

@@ -201,6 +201,9 @@ HIER_CASES = [
          topk=10, plant="none"),                                        # orphans + partial chunk
     dict(batch=1, n_raw=16 * 16 * 8, fanout=16, topk2=8, topk=128, plant="none"),  # all chosen
     dict(batch=1, n_raw=16 * 16 * 8, fanout=16, topk2=0, topk=0, plant="none"),
+    dict(batch=4, n_raw=16 * 8 * 40 + 16 * 5, fanout=8, topk2=6, topk=12),   # 5 orphans, k1 <= 64
+    dict(batch=2, n_raw=16 * 16 * 16, fanout=16, topk2=16, topk=64, plant="none"),  # every group chosen
+    dict(batch=1, n_raw=16 * 4 * 300, fanout=4, topk2=40, topk=20, plant="none"),   # k2 > 16
 ]
 
 
