@@ -700,35 +700,6 @@ struct SelectLds {
   int cnt;
 };
 
-// The value of lane (lane ^ J). Within a 16-lane row the exchange uses DPP
-// (quad permutes, row shifts, row rotate by 8); across rows a permute.
-template <int J>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
-  if constexpr (J == 1) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-  } else if constexpr (J == 2) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-  } else if constexpr (J == 4) {
-    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x104, 0xF, 0xF, false);   // row_shl:4, lane+4
-    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xF, 0xF, false);   // row_shr:4, lane-4
-    return (threadIdx.x & 4) ? dn : up;
-  } else if constexpr (J == 8) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
-  } else if constexpr (J == 16) {
-    // v_permlane16_swap of v with itself: [0] holds rows (0,0,2,2), [1] rows (1,1,3,3)
-    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-    return (threadIdx.x & 16) ? r[0] : r[1];
-  } else {
-    static_assert(J == 32, "lane_xor: distance 1..32");
-    // v_permlane32_swap of v with itself: [0] holds halves (0,0), [1] halves (1,1)
-    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-    return (threadIdx.x & 32) ? r[0] : r[1];
-  }
-}
-template <int J>
-__device__ __forceinline__ unsigned long long lane_xor(unsigned long long v) {
-  return ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
-}
 
 // One compare-exchange step of a bitonic network at distance J within blocks of K.
 template <bool DESC, int K, int J, class T>
@@ -1703,8 +1674,8 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     const float cand = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     if (__ballot(cand > st.m + kLazy) != 0ull) {
       // raise head h's max on its four lanes (j = 0..3) and rescale
-      float c4 = fmaxf(cand, __shfl_xor(cand, 16));
-      c4 = fmaxf(c4, __shfl_xor(c4, 32));
+      float c4 = fmaxf(cand, __uint_as_float(lane_xor<16>(__float_as_uint(cand))));
+      c4 = fmaxf(c4, __uint_as_float(lane_xor<32>(__float_as_uint(c4))));
       const float mn = c4 > st.m + kLazy ? c4 : st.m;
       const float al = fexp2(st.m - mn);
       st.m = mn;
@@ -1729,11 +1700,14 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     for (int dt = 0; dt < 8; ++dt) va[dt] = base + voff[dt];
     i16x4u vf[8];
     u_v_frag(va, vf);
+    // every hi product, then every lo product (no product waits on the one
+    // just issued)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
+    for (int dt = 0; dt < 8; ++dt)
       st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[dt], phi, st.o[dt], 0, 0, 0);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
       st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[dt], plo, st.o[dt], 0, 0, 0);
-    }
   };
   // stages 0..2 in flight; step b issues stage b + 3 (if any) into the slot
   // stage b - 1 left (its reads completed inside their asm blocks) and waits

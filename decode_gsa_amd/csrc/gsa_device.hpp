@@ -155,5 +155,36 @@ __device__ __forceinline__ int block_excl_scan(int v, int* buf) {
   return base + x - v;
 }
 
+// The value of lane (lane ^ J) of the wave. Within a 16-lane row the exchange
+// uses DPP (quad permutes, row shifts, row rotate by 8); across rows the
+// permlane swaps (VALU, no LDS round trip).
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x104, 0xF, 0xF, false);   // row_shl:4, lane+4
+    const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xF, 0xF, false);   // row_shr:4, lane-4
+    return (threadIdx.x & 4) ? dn : up;
+  } else if constexpr (J == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (J == 16) {
+    // v_permlane16_swap of v with itself: [0] holds rows (0,0,2,2), [1] rows (1,1,3,3)
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "lane_xor: distance 1..32");
+    // v_permlane32_swap of v with itself: [0] holds halves (0,0), [1] halves (1,1)
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+template <int J>
+__device__ __forceinline__ unsigned long long lane_xor(unsigned long long v) {
+  return ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
+}
+
 }  // namespace dev
 }  // namespace gsa

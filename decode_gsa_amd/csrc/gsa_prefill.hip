@@ -145,24 +145,28 @@ __device__ __forceinline__ int32_t raw_row(int32_t p, int32_t C, int32_t M) {
 
 // Exclusive prefix and total over the four lanes {i, i+16, i+32, i+48} that
 // share a query (jg = lane / 16 orders them).
+__device__ __forceinline__ int xi16(int v) { return (int)lane_xor<16>((uint32_t)v); }
+__device__ __forceinline__ int xi32(int v) { return (int)lane_xor<32>((uint32_t)v); }
+__device__ __forceinline__ float xf16(float v) { return __uint_as_float(lane_xor<16>(__float_as_uint(v))); }
+__device__ __forceinline__ float xf32(float v) { return __uint_as_float(lane_xor<32>(__float_as_uint(v))); }
 __device__ __forceinline__ int excl4(int c, int jg, int* total) {
-  const int x1 = __shfl_xor(c, 16);
+  const int x1 = xi16(c);
   const int pair = c + x1;
-  const int x2 = __shfl_xor(pair, 32);
+  const int x2 = xi32(pair);
   *total = pair + x2;
   return ((jg & 1) ? x1 : 0) + ((jg & 2) ? x2 : 0);
 }
 __device__ __forceinline__ int sum4(int c) {
-  c += __shfl_xor(c, 16);
-  return c + __shfl_xor(c, 32);
+  c += xi16(c);
+  return c + xi32(c);
 }
 __device__ __forceinline__ float max4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  v = fmaxf(v, xf16(v));
+  return fmaxf(v, xf32(v));
 }
 __device__ __forceinline__ float fsum4(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  v += xf16(v);
+  return v + xf32(v);
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -214,10 +218,11 @@ constexpr int kSelTile = 64;            // gists per tile
 constexpr int kSelNB = 3;               // tiles in the LDS ring
 constexpr int kSelTileBytes = kSelTile * kRowBytes;
 constexpr int kSelPer = kSelTile / 4 / kSelWaves;   // direct loads per wave per tile (4 rows each)
-constexpr int kCap = 48;                // survivor buffer entries per query
+constexpr int kCap = 72;                // survivor buffer entries per query
 constexpr int kCapLane = kCap / 4;      // entries per lane in a compaction
 constexpr int kBufStride = kQB + 4;     // words per buffer entry row (bank spread)
 static_assert(kPrefillMaxK <= kCap - 16, "a compaction must leave room for a 16-gist subtile");
+static_assert(kPrefillMaxGist <= 65536, "survivor ids are 16-bit");
 
 struct SelArgs {
   const void* q;          // [Hq][n_q][D] bf16
@@ -232,7 +237,7 @@ struct SelArgs {
 struct SelLds {
   char ring[kSelNB][kSelTileBytes];
   uint32_t bkey[kCap][kBufStride];   // entry-major: lanes of one entry hit distinct banks
-  uint32_t bid[kCap][kBufStride];
+  uint16_t bid[kCap][kBufStride];   // gist ids < kPrefillMaxGist = 2^16
 };
 
 // Compact every query's survivor buffer of the wave to its exact top-k.
@@ -282,7 +287,7 @@ __device__ __forceinline__ int compact_query(SelLds& L, int qloc, int jg, int cn
   for (int e = 0; e < kCapLane; ++e) {
     if (take[e]) {
       L.bkey[pos][qloc] = kk[e];
-      L.bid[pos][qloc] = ii[e];
+      L.bid[pos][qloc] = (uint16_t)ii[e];
       ++pos;
     }
   }
@@ -344,15 +349,24 @@ __global__ __launch_bounds__(kSelThreads) void prefill_select(SelArgs a) {
     tile_barrier();    // every wave's loads of tile it landed; tile it-1's buffer is free
     if (it + kSelNB - 1 < n_tiles) sel_issue(L.ring[(it + kSelNB - 1) % kSelNB], Kh, it + kSelNB - 1, E, a.C);
     const char* kt = L.ring[it % kSelNB];
+    // the four 16-gist subtiles as four independent MFMA chains (one chain
+    // would wait on each product's latency)
+    f32x4 accs[kSelTile / 16];
+#pragma unroll
+    for (int s = 0; s < kSelTile / 16; ++s) accs[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 kf[kSelTile / 16];
+#pragma unroll
+      for (int s = 0; s < kSelTile / 16; ++s) kf[s] = lds_b128(kt + koff[s][ks]);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int s = 0; s < kSelTile / 16; ++s) accs[s] = mfma(kf[s], qf[h][ks], accs[s]);
+    }
 #pragma unroll
     for (int s = 0; s < kSelTile / 16; ++s) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kf = lds_b128(kt + koff[s][ks]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) acc = mfma(kf, qf[h][ks], acc);
-      }
+      const f32x4 acc = accs[s];
       // acc[r]: gist 64 it + 16 s + 4 jg + r against query qi (heads summed)
       uint32_t key[4];
       bool sv[4];
@@ -371,7 +385,7 @@ __global__ __launch_bounds__(kSelThreads) void prefill_select(SelArgs a) {
         for (int r = 0; r < 4; ++r) {
           if (sv[r]) {
             L.bkey[pos][qloc] = key[r];
-            L.bid[pos][qloc] = (uint32_t)(it * kSelTile + 16 * s + 4 * jg + r);
+            L.bid[pos][qloc] = (uint16_t)(it * kSelTile + 16 * s + 4 * jg + r);
             ++pos;
           }
         }
@@ -499,14 +513,18 @@ __device__ __forceinline__ void att_tile(const char* kt, const char* vt, const A
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int h = 0; h < H; ++h) s[sb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // 2 H independent MFMA chains, interleaved so that no product waits on the
+  // one just issued
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
+  for (int ks = 0; ks < 4; ++ks) {
+    bf16x8 kf[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 kf = lds_b128(kt + (16 * sb + qi) * kRowBytes + k_slot(4 * ks + jg, qi) * 16);
+    for (int sb = 0; sb < 2; ++sb) kf[sb] = lds_b128(kt + (16 * sb + qi) * kRowBytes + k_slot(4 * ks + jg, qi) * 16);
 #pragma unroll
-      for (int h = 0; h < H; ++h) s[sb][h] = mfma(kf, qf[h][ks], s[sb][h]);
-    }
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int h = 0; h < H; ++h) s[sb][h] = mfma(kf[sb], qf[h][ks], s[sb][h]);
+  }
   // s[sb][h][r]: row i0 + 16sb + 4jg + r against the lane's query, head h
   if (masked) {
 #pragma unroll
@@ -558,13 +576,16 @@ __device__ __forceinline__ void att_tile(const char* kt, const char* vt, const A
   for (int dt = 0; dt < 8; ++dt) va[dt] = vrow + v_slot(2 * dt + ((s16 & 3) >> 1), R) * 16;
   bf16x8 vf[8];
   lds_tr_tile(va, vf);
+  // every hi product, then every lo product: 8 H independent accumulators
+  // between the two products of one
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int h = 0; h < H; ++h) {
-      st.o[h][dt] = mfma(vf[dt], phi[h], st.o[h][dt]);
-      st.o[h][dt] = mfma(vf[dt], plo[h], st.o[h][dt]);
-    }
+    for (int h = 0; h < H; ++h) st.o[h][dt] = mfma(vf[dt], phi[h], st.o[h][dt]);
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int h = 0; h < H; ++h) st.o[h][dt] = mfma(vf[dt], plo[h], st.o[h][dt]);
 }
 
 // One phase: rows [0, n) of kind KIND, kAttTile rows per tile, kAttNB tiles
