@@ -164,6 +164,10 @@ __device__ __forceinline__ float max4(float v) {
   v = fmaxf(v, xf16(v));
   return fmaxf(v, xf32(v));
 }
+__device__ __forceinline__ float min4(float v) {
+  v = fminf(v, xf16(v));
+  return fminf(v, xf32(v));
+}
 __device__ __forceinline__ float fsum4(float v) {
   v += xf16(v);
   return v + xf32(v);
@@ -214,15 +218,15 @@ __device__ __forceinline__ void load_qfrag(const char* qbase, int64_t n_q, int64
 
 constexpr int kSelThreads = 256;        // 4 waves, one 16-query tile each
 constexpr int kSelWaves = 4;
-constexpr int kSelTile = 64;            // gists per tile
-constexpr int kSelNB = 3;               // tiles in the LDS ring
+constexpr int kSelTile = 32;            // gists per tile
+constexpr int kSelSub = kSelTile / 16;  // 16-gist subtiles per tile
+constexpr int kSelNB = 4;               // tiles in the LDS ring
 constexpr int kSelTileBytes = kSelTile * kRowBytes;
 constexpr int kSelPer = kSelTile / 4 / kSelWaves;   // direct loads per wave per tile (4 rows each)
-constexpr int kCap = 72;                // survivor buffer entries per query
-constexpr int kCapLane = kCap / 4;      // entries per lane in a compaction
-constexpr int kBufStride = kQB + 4;     // words per buffer entry row (bank spread)
-static_assert(kPrefillMaxK <= kCap - 16, "a compaction must leave room for a 16-gist subtile");
-static_assert(kPrefillMaxGist <= 65536, "survivor ids are 16-bit");
+constexpr int kLaneCand = kSelTile / 4;             // scores one lane sees per tile
+constexpr int kListCap = 24;            // entries of a lane's candidate list
+static_assert(kListCap % 8 == 0, "lists are read in groups of 8 entries");
+static_assert(kPrefillMaxGist <= 65536, "candidate ids fit the id field");
 
 struct SelArgs {
   const void* q;          // [Hq][n_q][D] bf16
@@ -234,70 +238,189 @@ struct SelArgs {
   int32_t* sel_out;       // [Hkv][n_q][k] or null
 };
 
+// Each lane keeps a list of candidate entries of its query: entry e of lane
+// tid is ent[e][tid] = (score bits, gist id).
 struct SelLds {
   char ring[kSelNB][kSelTileBytes];
-  uint32_t bkey[kCap][kBufStride];   // entry-major: lanes of one entry hit distinct banks
-  uint16_t bid[kCap][kBufStride];   // gist ids < kPrefillMaxGist = 2^16
+  uint2 ent[kListCap][kSelThreads];
 };
+static_assert(sizeof(SelLds) <= 80 * 1024, "two workgroups per CU");
 
-// Compact every query's survivor buffer of the wave to its exact top-k.
-// Lanes (qi, jg) own entries [kCapLane*jg, kCapLane*(jg+1)) of query qloc's
-// buffer (in gist order). Returns the new count; tau gets the k-th best key
-// (0 if fewer than k entries: then every later eligible gist still enters).
-__device__ __forceinline__ int compact_query(SelLds& L, int qloc, int jg, int cnt, int k, uint32_t* tau) {
-  uint32_t kk[kCapLane];
-  const int e0 = kCapLane * jg;
+// Score of an order key (inverse of order_key on canonical values).
+__device__ __forceinline__ float key_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// The candidates of a query are the entries of the four lists of the lanes
+// (qi, jg = 0..3) that share it. Compactions rewrite the lists with a subset
+// of them that still holds the query's top-k, dealt round-robin over the
+// four lists (kept entry p goes to list p % 4, slot p / 4). The last slot of
+// every list is a spare that takes the writes of dropped entries.
+constexpr int kKeepMax = 4 * (kListCap - 1 - kLaneCand);   // entries a compaction may keep
+constexpr int kPruneSlack = 8;          // a prune stops once at most k + this many remain
+static_assert(kPrefillMaxK + kPruneSlack <= kKeepMax, "a prune can always keep k + slack entries");
+
+template <int NE>
+__device__ __forceinline__ void sel_load(const SelLds& L, int tid, float (&v)[NE], uint32_t (&id)[NE]) {
 #pragma unroll
-  for (int e = 0; e < kCapLane; ++e) kk[e] = e0 + e < cnt ? L.bkey[e0 + e][qloc] : 0u;
+  for (int e = 0; e < NE; ++e) {
+    const uint2 x = L.ent[e][tid];
+    v[e] = __uint_as_float(x.x);
+    id[e] = x.y;
+  }
+}
+
+// Rewrite the lists with the entries marked `take`; returns this lane's new
+// list length and the query's kept count in *tot.
+template <int NE>
+__device__ __forceinline__ int sel_deal(SelLds& L, int w, int lane, const float (&v)[NE],
+                                        const uint32_t (&id)[NE], const bool (&take)[NE], int* tot) {
+  const int qi = lane & 15, jg = lane >> 4;
+  int ct = 0;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) ct += take[e] ? 1 : 0;
+  int p = excl4(ct, jg, tot);
+  wave_lds_sync();   // every lane has read its list
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int jt = take[e] ? (p & 3) : jg;
+    const int slot = take[e] ? (p >> 2) : kListCap - 1;
+    L.ent[slot][64 * w + qi + 16 * jt] = make_uint2(__float_as_uint(v[e]), id[e]);
+    p += take[e] ? 1 : 0;
+  }
+  wave_lds_sync();
+  return (*tot + 3 - jg) >> 2;
+}
+
+// Exact top-k: the k-th best order key P by a bit-serial radix select over
+// the four lists; entries above P are kept and, of those equal to P, the ones
+// with the smallest ids (ties go to the smaller gist index). *tau becomes the
+// k-th best score, or -inf while the query has fewer than k candidates.
+// NE: list entries that may be in use (wave-uniform).
+template <int NE>
+__device__ __forceinline__ int sel_exact_n(SelLds& L, int w, int lane, int pos, int k, float* tau) {
+  float v[NE];
+  uint32_t id[NE], key[NE];
+  sel_load<NE>(L, 64 * w + lane, v, id);
+#pragma unroll
+  for (int e = 0; e < NE; ++e) key[e] = e < pos ? order_key(v[e]) : 0u;
   uint32_t P = 0u;
   for (int b = 31; b >= 0; --b) {
     const uint32_t c = P | (1u << b);
     int n = 0;
 #pragma unroll
-    for (int e = 0; e < kCapLane; ++e) n += kk[e] >= c ? 1 : 0;
+    for (int e = 0; e < NE; ++e) n += key[e] >= c ? 1 : 0;
     n = sum4(n);
     P = n >= k ? c : P;
   }
   int gt = 0, ce = 0;
 #pragma unroll
-  for (int e = 0; e < kCapLane; ++e) {
-    gt += kk[e] > P ? 1 : 0;
-    ce += (kk[e] == P && kk[e] != 0u) ? 1 : 0;
+  for (int e = 0; e < NE; ++e) {
+    gt += key[e] > P ? 1 : 0;
+    ce += (key[e] == P && key[e] != 0u) ? 1 : 0;
   }
   gt = sum4(gt);
-  const int need = k - gt;
-  int ce_tot;
-  int eqb = excl4(ce, jg, &ce_tot);
-  bool take[kCapLane];
-  int ct = 0;
+  const int ce_tot = sum4(ce);
+  const int need = k - gt;        // entries equal to P that are kept (>= 1 when P > 0)
+  uint32_t I = 0xffffffffu;       // of those, the ones with id <= I
+  if (__ballot(ce_tot > need) != 0ull) {
+    // need-th smallest id among the entries equal to P (ids are distinct)
+    uint32_t lo = 0u;
+    for (int b = 15; b >= 0; --b) {
+      const uint32_t trial = lo + (1u << b);
+      int n = 0;
 #pragma unroll
-  for (int e = 0; e < kCapLane; ++e) {
-    const bool eq = kk[e] == P && kk[e] != 0u;
-    take[e] = kk[e] > P || (eq && eqb < need);
-    eqb += eq ? 1 : 0;
-    ct += take[e] ? 1 : 0;
-  }
-  int tot;
-  int pos = excl4(ct, jg, &tot);
-  uint32_t ii[kCapLane];
-#pragma unroll
-  for (int e = 0; e < kCapLane; ++e) ii[e] = take[e] ? L.bid[e0 + e][qloc] : 0u;
-  wave_lds_sync();
-#pragma unroll
-  for (int e = 0; e < kCapLane; ++e) {
-    if (take[e]) {
-      L.bkey[pos][qloc] = kk[e];
-      L.bid[pos][qloc] = (uint16_t)ii[e];
-      ++pos;
+      for (int e = 0; e < NE; ++e) n += (key[e] == P && key[e] != 0u && id[e] < trial) ? 1 : 0;
+      n = sum4(n);
+      lo = n < need ? trial : lo;
     }
+    if (ce_tot > need) I = lo;
   }
-  wave_lds_sync();
-  *tau = tot >= k ? P : 0u;
-  return tot;
+  bool take[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) take[e] = key[e] > P || (key[e] == P && key[e] != 0u && id[e] <= I);
+  int tot;
+  const int n = sel_deal<NE>(L, w, lane, v, id, take, &tot);
+  *tau = tot >= k ? key_score(P) : -INFINITY;
+  return n;
 }
 
-// Direct loads of gist tile `it` (rows m = 64 it + r; rows past E read gist 0,
-// whose scores the eligibility mask drops).
+// Prune: a bisection of the query's score range finds lo with at least k
+// entries >= lo, and the entries below lo are dropped (k entries beat each of
+// them). lo becomes *tau: a later gist scoring <= lo has k earlier entries at
+// least as good. The bisection stops once at most k + kPruneSlack entries are
+// >= lo. Returns -1 (lists untouched) if some query would keep more than
+// kKeepMax entries (scores tied over a wide range); an exact compaction
+// follows then.
+template <int NE>
+__device__ __forceinline__ int sel_prune_n(SelLds& L, int w, int lane, int pos, int k, float* tau) {
+  float v[NE];
+  uint32_t id[NE];
+  sel_load<NE>(L, 64 * w + lane, v, id);
+  float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    if (e >= pos) v[e] = -INFINITY;     // unused slots count nowhere
+    mx = e < pos ? fmaxf(mx, v[e]) : mx;
+    mn = e < pos ? fminf(mn, v[e]) : mn;
+  }
+  mx = max4(mx);
+  mn = min4(mn);
+  const int total = sum4(pos);
+  const bool full = total >= k;
+  float lo = mn, hi = mx;
+  int n_lo = total;
+  for (int s = 0; s < 16; ++s) {
+    if (__ballot(full && n_lo > k + kPruneSlack) == 0ull) break;
+    const float mid = 0.5f * lo + 0.5f * hi;
+    int n = 0;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) n += v[e] >= mid ? 1 : 0;
+    n = sum4(n);
+    if (n >= k) {
+      lo = mid;
+      n_lo = n;
+    } else {
+      hi = mid;
+    }
+  }
+  if (__ballot(n_lo > kKeepMax) != 0ull) return -1;
+  bool take[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) take[e] = e < pos && (!full || v[e] >= lo);
+  int tot;
+  const int n = sel_deal<NE>(L, w, lane, v, id, take, &tot);
+  if (full) *tau = lo;
+  return n;
+}
+
+// Entries per list in use, rounded up to groups of 8 (wave-uniform).
+__device__ __forceinline__ int list_groups(int pos) {
+  static_assert(kListCap == 24, "three groups");
+  return __ballot(pos > 16) ? 3 : __ballot(pos > 8) ? 2 : 1;
+}
+
+__device__ __forceinline__ int sel_exact(SelLds& L, int w, int lane, int pos, int k, float* tau) {
+  switch (list_groups(pos)) {
+    case 1: return sel_exact_n<8>(L, w, lane, pos, k, tau);
+    case 2: return sel_exact_n<16>(L, w, lane, pos, k, tau);
+    default: return sel_exact_n<24>(L, w, lane, pos, k, tau);
+  }
+}
+
+// Make room in the lists: prune, or compact exactly if a prune cannot.
+__device__ __forceinline__ int sel_compact(SelLds& L, int w, int lane, int pos, int k, float* tau) {
+  int n;
+  switch (list_groups(pos)) {
+    case 1: n = sel_prune_n<8>(L, w, lane, pos, k, tau); break;
+    case 2: n = sel_prune_n<16>(L, w, lane, pos, k, tau); break;
+    default: n = sel_prune_n<24>(L, w, lane, pos, k, tau); break;
+  }
+  return n >= 0 ? n : sel_exact(L, w, lane, pos, k, tau);
+}
+
+// Direct loads of gist tile `it` (rows m = kSelTile it + r; rows past E read
+// gist 0, whose scores the eligibility mask drops).
 __device__ __forceinline__ void sel_issue(char* buf, const char* Kh, int it, int E, int C) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -310,12 +433,64 @@ __device__ __forceinline__ void sel_issue(char* buf, const char* Kh, int it, int
   }
 }
 
+// The query summed over its group's heads, qbar = sum_h q_h (fp32, exact for
+// bf16 heads of similar magnitude), as two bf16 parts hi + lo: the group
+// score (scale/g) sum_h q_h . k = (scale/g) qbar . k then takes two MFMA
+// chains instead of one per head, with qbar kept to about 16 bits (all of it
+// for g = 1, where lo is zero).
 template <int G>
-__global__ __launch_bounds__(kSelThreads) void prefill_select(SelArgs a) {
+__device__ __forceinline__ void load_qbar(const char* qbase, int64_t n_q, int64_t t_idx, bool valid, int jg,
+                                          bf16x8 (&qh)[4], bf16x8 (&ql)[4]) {
+  bf16x8 qf[G][4];
+  load_qfrag<G>(qbase, n_q, t_idx, valid, 0, jg, qf);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float s = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) s += (float)qf[h][ks][e];
+      const __bf16 hi = (__bf16)s;
+      qh[ks][e] = hi;
+      ql[ks][e] = (__bf16)(s - (float)hi);
+    }
+}
+
+// Append the candidates of one 16-gist subtile (score[r]: gist m0 + r) that
+// beat tau. Every score is written at the list's end, and the end advances
+// past the ones that beat tau: no branch per score.
+template <bool MASK>
+__device__ __forceinline__ void sel_append(SelLds& L, int tid, const float (&score)[4], int m0, int elig,
+                                           float tau, int* pos) {
+  float v[4];
+  bool ok[4];
+  bool any = false;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    v[r] = MASK && m0 + r >= elig ? -INFINITY : score[r];
+    ok[r] = v[r] > tau;
+    any |= ok[r];
+  }
+  if (__ballot(any) == 0ull) return;
+  int p = *pos;
+  const uint32_t base = lds_addr(reinterpret_cast<const char*>(&L.ent[0][tid]));
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    // written as asm: the compiler would otherwise wait for every direct-to-
+    // LDS load in flight (the K tiles ahead) before a list write
+    const uint2 x = make_uint2(__float_as_uint(v[r]), (uint32_t)(m0 + r));
+    __asm__ volatile("ds_write_b64 %0, %1" ::"v"(base + (uint32_t)p * (kSelThreads * 8)), "v"(x) : "memory");
+    p += ok[r] ? 1 : 0;
+  }
+  *pos = p;
+}
+
+template <int G>
+__global__ __launch_bounds__(kSelThreads, 2) void prefill_select(SelArgs a) {
   __shared__ __attribute__((aligned(16))) SelLds L;
   int kvh, blk;
   wg_coords(a.n_blocks, a.Hkv, &kvh, &blk);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int qi = lane & 15, jg = lane >> 4;
   const int qloc = 16 * w + qi;
   const int t_idx = blk * kQB + qloc;
@@ -324,19 +499,21 @@ __global__ __launch_bounds__(kSelThreads) void prefill_select(SelArgs a) {
   const int elig = valid ? min(a.M, t / a.C) : 0;
   const int t_last = a.q_start + min(a.n_q, (blk + 1) * kQB) - 1;
   const int E = min(a.M, t_last / a.C);     // gists any query of the block may use
+  // gists every valid query of this wave may use (its first query's)
+  const int e_lo = min(a.M, (a.q_start + blk * kQB + 16 * w) / a.C);
 
-  bf16x8 qf[G][4];
-  load_qfrag<G>(reinterpret_cast<const char*>(a.q) + (int64_t)kvh * G * a.n_q * kRowBytes, a.n_q, t_idx,
-                valid, 0, jg, qf);
+  bf16x8 qh[4], ql[4];
+  load_qbar<G>(reinterpret_cast<const char*>(a.q) + (int64_t)kvh * G * a.n_q * kRowBytes, a.n_q, t_idx, valid,
+               jg, qh, ql);
   const char* Kh = reinterpret_cast<const char*>(a.K) + (int64_t)kvh * a.R * kRowBytes;
 
-  int cnt = 0;
-  uint32_t tau = 0u;
+  int pos = 0;
+  float tau = valid ? -INFINITY : INFINITY;   // a query past n_q takes nothing
   const int n_tiles = (E + kSelTile - 1) / kSelTile;
   // this lane's operand offsets inside a tile: row 16s + qi, chunk 4ks + jg
-  int koff[4][4];
+  int koff[kSelSub][4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
+  for (int s = 0; s < kSelSub; ++s)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) koff[s][ks] = (16 * s + qi) * kRowBytes + k_slot(4 * ks + jg, qi) * 16;
 
@@ -344,67 +521,70 @@ __global__ __launch_bounds__(kSelThreads) void prefill_select(SelArgs a) {
   for (int it = 0; it < n_tiles; ++it) {
     // this wave's loads of tile `it` are done once at most (tiles issued
     // after it) x kSelPer loads are outstanding
-    if (it + 1 < n_tiles) wait_vm<kSelPer * (kSelNB - 2)>();
+    const int ahead = min(kSelNB - 2, n_tiles - 1 - it);
+    if (ahead >= 2) wait_vm<2 * kSelPer>();
+    else if (ahead == 1) wait_vm<kSelPer>();
     else wait_vm<0>();
     tile_barrier();    // every wave's loads of tile it landed; tile it-1's buffer is free
     if (it + kSelNB - 1 < n_tiles) sel_issue(L.ring[(it + kSelNB - 1) % kSelNB], Kh, it + kSelNB - 1, E, a.C);
     const char* kt = L.ring[it % kSelNB];
-    // the four 16-gist subtiles as four independent MFMA chains (one chain
-    // would wait on each product's latency)
-    f32x4 accs[kSelTile / 16];
+    // per subtile two independent chains: qbar's hi and lo parts
+    f32x4 acc[kSelSub][2];
 #pragma unroll
-    for (int s = 0; s < kSelTile / 16; ++s) accs[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < kSelSub; ++s) acc[s][0] = acc[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 kf[kSelTile / 16];
+      bf16x8 kf[kSelSub];
 #pragma unroll
-      for (int s = 0; s < kSelTile / 16; ++s) kf[s] = lds_b128(kt + koff[s][ks]);
+      for (int s = 0; s < kSelSub; ++s) kf[s] = lds_b128(kt + koff[s][ks]);
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int s = 0; s < kSelTile / 16; ++s) accs[s] = mfma(kf[s], qf[h][ks], accs[s]);
+      for (int s = 0; s < kSelSub; ++s) {
+        acc[s][0] = mfma(kf[s], qh[ks], acc[s][0]);
+        if (G > 1) acc[s][1] = mfma(kf[s], ql[ks], acc[s][1]);   // g = 1: lo is zero
+      }
     }
+    // score of gist kSelTile it + 16 s + 4 jg + r against query qi
+    const int m0 = it * kSelTile + 4 * jg;
+    const bool masked = (it + 1) * kSelTile > e_lo;
 #pragma unroll
-    for (int s = 0; s < kSelTile / 16; ++s) {
-      const f32x4 acc = accs[s];
-      // acc[r]: gist 64 it + 16 s + 4 jg + r against query qi (heads summed)
-      uint32_t key[4];
-      bool sv[4];
-      int c = 0;
+    for (int s = 0; s < kSelSub; ++s) {
+      float sc[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = it * kSelTile + 16 * s + 4 * jg + r;
-        key[r] = m < elig ? order_key(acc[r] * a.score_mul) : 0u;
-        sv[r] = key[r] > tau;
-        c += sv[r] ? 1 : 0;
-      }
-      if (__ballot(c > 0) != 0ull) {
-        int tot;
-        int pos = cnt + excl4(c, jg, &tot);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (sv[r]) {
-            L.bkey[pos][qloc] = key[r];
-            L.bid[pos][qloc] = (uint16_t)(it * kSelTile + 16 * s + 4 * jg + r);
-            ++pos;
-          }
-        }
-        cnt += tot;
-        wave_lds_sync();
-        if (__ballot(cnt > kCap - 16) != 0ull) cnt = compact_query(L, qloc, jg, cnt, a.k, &tau);
-      }
+      for (int r = 0; r < 4; ++r) sc[r] = (acc[s][0][r] + acc[s][1][r]) * a.score_mul;
+      if (masked) sel_append<true>(L, tid, sc, m0 + 16 * s, elig, tau, &pos);
+      else sel_append<false>(L, tid, sc, m0 + 16 * s, elig, tau, &pos);
+    }
+    if (__ballot(pos > kListCap - 1 - kLaneCand) != 0ull) {
+      wave_lds_sync();
+      pos = sel_compact(L, w, lane, pos, a.k, &tau);
     }
   }
-  cnt = compact_query(L, qloc, jg, cnt, a.k, &tau);
+  wave_lds_sync();
+  pos = sel_compact(L, w, lane, pos, a.k, &tau);
+  pos = sel_exact(L, w, lane, pos, a.k, &tau);
+  // the query's kept entries in ascending id order: each lane ranks its own
+  // entries among all of the query's (at most k, dealt round-robin)
+  const int tot = sum4(pos);
+  uint32_t ids[kPrefillMaxK];
+#pragma unroll
+  for (int p = 0; p < kPrefillMaxK; ++p)
+    ids[p] = p < tot ? L.ent[p >> 2][64 * w + qi + 16 * (p & 3)].y : 0xffffffffu;
   if (valid) {
     const int64_t o = ((int64_t)kvh * a.n_q + t_idx) * a.k;
 #pragma unroll
-    for (int e = 0; e < kCapLane; ++e) {
-      const int i = kCapLane * jg + e;
+    for (int e = 0; e < (kPrefillMaxK + 3) / 4; ++e) {
+      if (e < pos) {
+        const uint32_t mine = ids[4 * e + jg];
+        int rank = 0;
+#pragma unroll
+        for (int p = 0; p < kPrefillMaxK; ++p) rank += ids[p] < mine ? 1 : 0;
+        a.sel_ws[o + rank] = (int32_t)mine;
+        if (a.sel_out) a.sel_out[o + rank] = (int32_t)mine;
+      }
+      const int i = tot + 4 * e + jg;   // slots past the kept entries
       if (i < a.k) {
-        const int32_t v = i < cnt ? (int32_t)L.bid[i][qloc] : -1;
-        a.sel_ws[o + i] = v;
-        if (a.sel_out) a.sel_out[o + i] = v;
+        a.sel_ws[o + i] = -1;
+        if (a.sel_out) a.sel_out[o + i] = -1;
       }
     }
   }

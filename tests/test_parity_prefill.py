@@ -115,3 +115,21 @@ def test_prefill_full_size_sampled(gsa):
     blk = torch.arange(cfg.n_q, device=sel.device) // cfg.q_block
     assert torch.equal(sel.permute(1, 0, 2).long(), inp.planted[blk])
     say(f"  max err / rms = {err:.2e}")
+
+
+@pytest.mark.parametrize("topk", [16, 32])
+def test_prefill_all_scores_tied(gsa, topk):
+    """q = 0: every group score is 0, so a query keeps the topk smallest
+    eligible gist indices. More tied candidates than the candidate lists can
+    hold after a bisection prune, so the exact radix selection (ties by
+    index) decides."""
+    cfg = small(n_raw=4096, n_q=192, n_kv_heads=2, n_q_heads=8, topk=topk, chunk=8, window=24)
+    say(f"prefill all scores tied {cfg}")
+    inp = gi.make_prefill(cfg, 4100 + topk, device="cuda")
+    inp.q.zero_()
+    err, _, sel = run_prefill(gsa, inp, cfg, queries=[(i, j) for i in range(0, cfg.n_q, 7) for j in (0, 1)])
+    t = cfg.q_start + np.arange(cfg.n_q)
+    elig = np.minimum(t // cfg.chunk, cfg.M)
+    want = np.where(np.arange(topk)[None, :] < elig[:, None], np.arange(topk)[None, :], -1)
+    np.testing.assert_array_equal(to_np(sel), np.broadcast_to(want, (cfg.n_kv_heads,) + want.shape))
+    say(f"  max err / rms = {err:.2e}")
