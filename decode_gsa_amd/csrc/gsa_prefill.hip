@@ -173,6 +173,22 @@ __device__ __forceinline__ float fsum4(float v) {
   return v + xf32(v);
 }
 
+// Maximum of the 8 scores of two accumulators, with v_max3 (the compiler's
+// fmaxf adds NaN-quieting instructions; the scores are never NaN).
+__device__ __forceinline__ float max8(const f32x4& a, const f32x4& b) {
+  float m;
+  __asm__("v_max3_f32 %0, %1, %2, %3\n\t"
+          "v_max3_f32 %0, %0, %4, %5\n\t"
+          "v_max3_f32 %0, %0, %6, %7\n\t"
+          "v_max_f32 %0, %0, %8"
+          : "=&v"(m)
+          : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
+  return m;
+}
+
+// This thread's wave in the workgroup, known to the compiler as wave-uniform.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -422,7 +438,7 @@ __device__ __forceinline__ int sel_compact(SelLds& L, int w, int lane, int pos, 
 // Direct loads of gist tile `it` (rows m = kSelTile it + r; rows past E read
 // gist 0, whose scores the eligibility mask drops).
 __device__ __forceinline__ void sel_issue(char* buf, const char* Kh, int it, int E, int C) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
 #pragma unroll
   for (int u = 0; u < kSelPer; ++u) {
     const int rb = 4 * (w + kSelWaves * u);
@@ -594,7 +610,9 @@ __global__ __launch_bounds__(kSelThreads, 2) void prefill_select(SelArgs a) {
 
 constexpr int kMaxChunkWords = kPrefillMaxGist / 32;   // bitmap of selectable chunks
 constexpr int kMaxUnion = kQB * kPrefillMaxK;           // distinct chunks a block can select
-constexpr int kAttTile = 32;            // rows per tile (the K of the P.V MFMA)
+constexpr int kAttTile = 32;            // rows per ring tile (the K of the P.V MFMA)
+constexpr int kAttSub = 32;             // rows per MFMA subtile
+constexpr int kAttGroups = kAttTile / 4;                 // 4-row load groups of the K (or V) rows
 constexpr int kAttNB = 4;               // tiles in the LDS ring
 constexpr int kHalfTile = kAttTile * kRowBytes;          // K or V part of a tile (8 KB)
 
@@ -604,7 +622,7 @@ template <int G> struct AttShape {
   static constexpr int HPW = G / WPQ;
   static constexpr int NW = 4 * WPQ;          // waves per workgroup
   static constexpr int NT = 64 * NW;          // threads per workgroup
-  static constexpr int PER = 16 / NW;         // direct loads (4 rows each) per wave per tile
+  static constexpr int PER = 2 * kAttGroups / NW;   // direct loads (4 rows each) per wave per tile
 };
 
 struct AttArgs {
@@ -643,14 +661,33 @@ __device__ __forceinline__ int64_t phase_row(const AttLds& L, int i, int n, int 
 template <int NW, int KIND>
 __device__ __forceinline__ void att_issue(char* buf, const char* Kh, const char* Vh, const AttLds& L,
                                           int i0, int n, int lo, int C, int M) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  if (KIND == kGist && i0 + kAttTile <= n) {
+    // gist rows i0 + r sit (C+1) rows apart: a wave-uniform base for the
+    // tile and a per-lane 32-bit offset
+    const int64_t step = (int64_t)i0 * (C + 1) * kRowBytes;
+    const char* kb = Kh + step;
+    const char* vb = Vh + step;
 #pragma unroll
-  for (int u = 0; u < 16 / NW; ++u) {
-    const int j = w + NW * u;                 // wave-uniform: K rows for j < 8, V rows after
-    const int rb = 4 * (j & 7);
+    for (int u = 0; u < 2 * kAttGroups / NW; ++u) {
+      const int j = w + NW * u;
+      const int rb = 4 * (j % kAttGroups);
+      const int r = rb + (lane >> 4);
+      const uint32_t roff = (uint32_t)(r * (C + 1) + C) * kRowBytes;
+      if (j < kAttGroups)
+        dma16(kb + (roff + k_slot(lane & 15, r) * 16), buf + rb * kRowBytes);
+      else
+        dma16(vb + (roff + v_slot(lane & 15, r) * 16), buf + kHalfTile + rb * kRowBytes);
+    }
+    return;
+  }
+#pragma unroll
+  for (int u = 0; u < 2 * kAttGroups / NW; ++u) {
+    const int j = w + NW * u;                 // wave-uniform: K rows for j < kAttGroups, V rows after
+    const int rb = 4 * (j % kAttGroups);
     const int r = rb + (lane >> 4);
     const int64_t row = phase_row<KIND>(L, i0 + r, n, lo, C, M);
-    if (j < 8)
+    if (j < kAttGroups)
       dma16(Kh + row * kRowBytes + k_slot(lane & 15, r) * 16, buf + rb * kRowBytes);
     else
       dma16(Vh + row * kRowBytes + v_slot(lane & 15, r) * 16, buf + kHalfTile + rb * kRowBytes);
@@ -719,9 +756,7 @@ __device__ __forceinline__ void att_tile(const char* kt, const char* vt, const A
   bf16x8 phi[H], plo[H];
 #pragma unroll
   for (int h = 0; h < H; ++h) {
-    float mx = s[0][h][0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e >> 2][h][e & 3]);
+    const float mx = max8(s[0][h], s[1][h]);
     const float cand = mx * x.c;
     if (__ballot(cand > st.m[h] + kPLazy) != 0ull) {
       // raise the row's max (the same on the row's four lanes) and rescale
@@ -736,16 +771,25 @@ __device__ __forceinline__ void att_tile(const char* kt, const char* vt, const A
         for (int r = 0; r < 4; ++r) st.o[h][dt][r] *= al;
     }
     const float nm = -st.m[h];
-    float ps = 0.f;
+    float p[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = fexp2(fmaf(s[e >> 2][h][e & 3], x.c, nm));
-      ps += p;
-      const __bf16 hi = (__bf16)p;
-      phi[h][e] = hi;
-      plo[h][e] = (__bf16)(p - (float)hi);
-    }
+    for (int e = 0; e < 8; ++e) p[e] = fexp2(fmaf(s[e >> 2][h][e & 3], x.c, nm));
+    float ps = p[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) ps += p[e];
     st.l[h] += ps;
+    // p = hi + lo: hi is p truncated to bf16 (its top 16 bits), lo = p - hi
+    // (exact in fp32, below 2^-7 p) rounded to bf16
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 hp;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t b0 = __float_as_uint(p[e]), b1 = __float_as_uint(p[e + 1]);
+      hp[e >> 1] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+      plo[h][e] = (__bf16)(p[e] - __uint_as_float(b0 & 0xffff0000u));
+      plo[h][e + 1] = (__bf16)(p[e + 1] - __uint_as_float(b1 & 0xffff0000u));
+    }
+    phi[h] = __builtin_bit_cast(bf16x8, hp);
   }
   // O^T += V^T P^T; the V^T operand comes transposed out of LDS
   const int s16 = lane & 15;
@@ -782,6 +826,7 @@ __device__ __forceinline__ void att_phase(AttLds& L, const char* Kh, const char*
     att_issue<NW, KIND>(L.ring[t], Kh, Vh, L, t * kAttTile, n, x.lo, x.C, M);
   for (int t = 0; t < nt; ++t) {
     const int ahead = min(kAttNB - 2, nt - 1 - t);   // tiles issued after tile t
+    static_assert(kAttNB <= 4, "at most two tiles ahead");
     if (ahead >= 2) wait_vm<2 * PER>();
     else if (ahead == 1) wait_vm<PER>();
     else wait_vm<0>();
@@ -790,6 +835,7 @@ __device__ __forceinline__ void att_phase(AttLds& L, const char* Kh, const char*
       att_issue<NW, KIND>(L.ring[(t + kAttNB - 1) % kAttNB], Kh, Vh, L, (t + kAttNB - 1) * kAttTile, n, x.lo,
                           x.C, M);
     const char* buf = L.ring[t % kAttNB];
+    static_assert(kAttTile == kAttSub, "one MFMA subtile per ring tile");
     const bool masked = KIND != kGist || (t + 1) * kAttTile > all_ok;
     att_tile<H, KIND>(buf, buf + kHalfTile, L, x, t * kAttTile, n, masked, qf, st);
   }
