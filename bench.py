@@ -20,10 +20,15 @@ last touched L-1 steps (>= 0.9 GB of other traffic) earlier and is no longer in
 the 256 MB Infinity Cache -- as in a real model, where each layer has its own
 cache. Inputs are resident in HBM before timing starts.
 
-Per-kernel times come from HIP events that the library attaches to its
+Timing: `value` and `ms_per_step` come from the wall clock around K
+uninstrumented steps (device synchronizations on both sides). Per-kernel
+times come from K more steps in which the library attaches HIP events to its
 kernel launches (gsa_profile_events: the runtime stamps them with each
 kernel's start and end), so the roofline of the dominant kernel is measured
-live in the timed region.
+live in bench.py (mean, median, p10, p90 per launch). Instrumented launches
+do not overlap their neighbours and cost a few microseconds each, which is
+why they are kept out of the throughput figure. The decode line also carries
+the machine's practical streaming rate (plain 1 GiB device copies).
 
 Prints one JSON line.
 """
@@ -85,21 +90,29 @@ class HipEvents:
 
 
 def timed_steps(gsa, step, args, n_marks):
-    """Warm up, then time exactly args.steps steps; the library records
-    n_marks events per step. Returns (wall ms per step, [steps, n_marks-1] ms)."""
+    """Warm up, then time exactly args.steps steps (wall clock between two
+    device synchronizations, no instrumentation). Then the same number of
+    steps again with the library recording n_marks events per step (one
+    before the first launch, one after each): a launch that records events
+    starts only after the previous one has finished and costs a few
+    microseconds more, so the instrumented steps give each kernel's own
+    duration but not the throughput. Returns (wall ms per step of the first
+    region, [steps, n_marks-1] ms per launch of the second)."""
     import torch
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     ev = HipEvents(args.steps * n_marks)
     try:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for i in range(args.steps):
             gsa.gsa_profile_events(ev.ev[i * n_marks:(i + 1) * n_marks])
-            step(args.warmup + i)
+            step(args.warmup + args.steps + i)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         gsa.gsa_profile_events([])
         per = np.array([[ev.ms(i * n_marks + j, i * n_marks + j + 1) for j in range(n_marks - 1)]
                         for i in range(args.steps)])
@@ -107,6 +120,13 @@ def timed_steps(gsa, step, args, n_marks):
         gsa.gsa_profile_events([])
         ev.close()
     return 1e3 * wall / args.steps, per
+
+
+def pcts(x) -> dict:
+    """Median, p10 and p90 of per-launch times (ms)."""
+    x = np.asarray(x, dtype=np.float64)
+    return {"ms_p50": float(np.percentile(x, 50)), "ms_p10": float(np.percentile(x, 10)),
+            "ms_p90": float(np.percentile(x, 90))}
 
 
 def source_sha(*names) -> str:
@@ -236,7 +256,7 @@ def run_decode_bench(args):
     kernels = {}
     for j, (nm, nb) in enumerate(zip(names, nbytes)):
         ms = float(per[:, j].mean())
-        kernels[nm] = {"ms": ms, "alg_bytes": nb, "GB_s": nb / (ms / 1e3) / 1e9}
+        kernels[nm] = {"ms": ms, "alg_bytes": nb, "GB_s": nb / (ms / 1e3) / 1e9, **pcts(per[:, j])}
     main, main_b, main_ms = names[0], nbytes[0], kernels[names[0]]["ms"]
     achieved = main_b / (main_ms / 1e3) / 1e9
     res = {
@@ -267,6 +287,7 @@ def run_decode_bench(args):
         "kernels": kernels,
         "source_sha": sha,
     }
+    res["roofline"]["machine_stream_rates"] = hbm_stream_rates()
     if not args.no_cpu:
         log("[bench] timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline_decode(inp, cfg, args.cpu_seconds)
@@ -349,7 +370,7 @@ def run_hier_bench(args):
     kernels = {}
     for j, (nm, b_) in enumerate(zip(names, nbytes)):
         ms = float(per[:, j].mean())
-        kernels[nm] = {"ms": ms, "alg_bytes": b_, "GB_s": b_ / (ms / 1e3) / 1e9}
+        kernels[nm] = {"ms": ms, "alg_bytes": b_, "GB_s": b_ / (ms / 1e3) / 1e9, **pcts(per[:, j])}
     call_ms = float(per.sum(axis=1).mean())
     alg_b = sum(nb.values())
     main = max(kernels, key=lambda k: kernels[k]["ms"])
@@ -455,11 +476,11 @@ def run_prefill_bench(args):
     achieved = total_fl / (att_ms / 1e3) / 1e12
     call_ms = float(per.sum(axis=1).mean())
     kernels = {"prefill_attend": {"ms": att_ms, "alg_flops": total_fl,
-                                  "TFLOP_s": total_fl / (att_ms / 1e3) / 1e12}}
+                                  "TFLOP_s": total_fl / (att_ms / 1e3) / 1e12, **pcts(per[:, -1])}}
     if cfg.topk > 0:
         sel_ms = float(per[:, 0].mean())
         kernels["prefill_select"] = {"ms": sel_ms, "alg_flops": sel_fl,
-                                     "TFLOP_s": sel_fl / (sel_ms / 1e3) / 1e12}
+                                     "TFLOP_s": sel_fl / (sel_ms / 1e3) / 1e12, **pcts(per[:, 0])}
     res = {
         "metric": PREFILL_METRIC,
         "value": cfg.n_q / (ms_per_step / 1e3),
@@ -491,6 +512,33 @@ def run_prefill_bench(args):
         log("[bench] timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline_prefill(inp, cfg, args.cpu_seconds)
     return res
+
+
+def hbm_stream_rates(reps: int = 8) -> dict:
+    """Practical bandwidth of plain torch kernels over 1 GiB: a device copy
+    (bytes read + written) and a full reduction (bytes read): the machine's
+    streaming rates next to the 8 TB/s specification."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n // 4, dtype=torch.int32, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def rate(fn, nbytes):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return nbytes / (e0.elapsed_time(e1) / reps / 1e3) / 1e9
+
+    copy = rate(lambda: b.copy_(a), 2 * n)
+    red = rate(lambda: a.sum(), n)
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_1GiB_GB_s": copy, "sum_1GiB_read_GB_s": red}
 
 
 def run_copy_calibration():

@@ -1,7 +1,9 @@
 """GPU parity of gsa_decode in its one-workgroup-per-unit launch (bf16,
 head_dim 128, topk <= 64): one workgroup per (batch, kv-head) unit with 256
 or more units and at most 4096 gists, otherwise several workgroups per unit
-that hand their partial states and group scores to the unit's last one.
+(with topk > 0 they hand their partial states and group scores to a second
+launch that selects, unfolds and merges; with topk = 0 the unit's last
+workgroup merges).
 Checked against the fp64 oracle: bit-exact selections, outputs and lse within
 the stated tolerance (tests/gpu_util.py).
 """
@@ -54,6 +56,7 @@ CASES = [
     (cfg_of("gqa_32k", batch=3, n_kv_heads=2, n_q_heads=16, n_raw=9000, n_gist=562, tail=40), None),  # ragged
     (cfg_of("gqa_32k", batch=2, n_raw=4096, topk=0, plant="none"), None),  # gists + tail only
     (cfg_of("gqa_32k", batch=1, n_raw=16384 * 16, tail=64), 8),            # 16384 gists: the selection limit
+    (cfg_of("gqa_32k", batch=1, n_kv_heads=1, n_q_heads=4, n_raw=65536, topk=64, tail=64), None),  # 1 unit x 65, k = 64
 ]
 
 
