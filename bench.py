@@ -515,30 +515,25 @@ def run_prefill_bench(args):
 
 
 def hbm_stream_rates(reps: int = 8) -> dict:
-    """Practical bandwidth of plain torch kernels over 1 GiB: a device copy
-    (bytes read + written) and a full reduction (bytes read): the machine's
-    streaming rates next to the 8 TB/s specification."""
+    """Bandwidth of a plain torch device copy of 1 GiB (bytes read + written),
+    reported next to the 8 TB/s specification as what a generic streaming
+    kernel reaches on this machine."""
     import torch
     n = 1 << 30
-    a = torch.empty(n // 4, dtype=torch.int32, device="cuda").fill_(1)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     b = torch.empty_like(a)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def rate(fn, nbytes):
-        fn()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return nbytes / (e0.elapsed_time(e1) / reps / 1e3) / 1e9
-
-    copy = rate(lambda: b.copy_(a), 2 * n)
-    red = rate(lambda: a.sum(), n)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n / (e0.elapsed_time(e1) / reps / 1e3) / 1e9
     del a, b
     torch.cuda.empty_cache()
-    return {"copy_1GiB_GB_s": copy, "sum_1GiB_read_GB_s": red}
+    return {"torch_copy_1GiB_GB_s": gbs}
 
 
 def run_copy_calibration():
