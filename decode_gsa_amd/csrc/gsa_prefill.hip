@@ -236,7 +236,7 @@ constexpr int kSelThreads = 256;        // 4 waves, one 16-query tile each
 constexpr int kSelWaves = 4;
 constexpr int kSelTile = 32;            // gists per tile
 constexpr int kSelSub = kSelTile / 16;  // 16-gist subtiles per tile
-constexpr int kSelNB = 4;               // tiles in the LDS ring
+constexpr int kSelNB = 3;               // tiles in the LDS ring
 constexpr int kSelTileBytes = kSelTile * kRowBytes;
 constexpr int kSelPer = kSelTile / 4 / kSelWaves;   // direct loads per wave per tile (4 rows each)
 constexpr int kLaneCand = kSelTile / 4;             // scores one lane sees per tile
@@ -259,6 +259,7 @@ struct SelArgs {
 struct SelLds {
   char ring[kSelNB][kSelTileBytes];
   uint2 ent[kListCap][kSelThreads];
+  uint32_t full[2][kSelWaves];   // per tile parity: a wave's lists need a compaction
 };
 static_assert(sizeof(SelLds) <= 80 * 1024, "two workgroups per CU");
 
@@ -542,6 +543,15 @@ __global__ __launch_bounds__(kSelThreads, 2) void prefill_select(SelArgs a) {
     else if (ahead == 1) wait_vm<kSelPer>();
     else wait_vm<0>();
     tile_barrier();    // every wave's loads of tile it landed; tile it-1's buffer is free
+    if (it > 0) {
+      // every wave compacts when one needs to: one wave alone would hold the
+      // others at the next barrier
+      const uint32_t* f = L.full[(it - 1) & 1];
+      if (__builtin_amdgcn_readfirstlane(f[0] | f[1] | f[2] | f[3]) != 0u) {
+        wave_lds_sync();
+        pos = sel_compact(L, w, lane, pos, a.k, &tau);
+      }
+    }
     if (it + kSelNB - 1 < n_tiles) sel_issue(L.ring[(it + kSelNB - 1) % kSelNB], Kh, it + kSelNB - 1, E, a.C);
     const char* kt = L.ring[it % kSelNB];
     // per subtile two independent chains: qbar's hi and lo parts
@@ -570,10 +580,8 @@ __global__ __launch_bounds__(kSelThreads, 2) void prefill_select(SelArgs a) {
       if (masked) sel_append<true>(L, tid, sc, m0 + 16 * s, elig, tau, &pos);
       else sel_append<false>(L, tid, sc, m0 + 16 * s, elig, tau, &pos);
     }
-    if (__ballot(pos > kListCap - 1 - kLaneCand) != 0ull) {
-      wave_lds_sync();
-      pos = sel_compact(L, w, lane, pos, a.k, &tau);
-    }
+    const bool full = __ballot(pos > kListCap - 1 - kLaneCand) != 0ull;
+    if (lane == 0) L.full[it & 1][w] = full ? 1u : 0u;
   }
   wave_lds_sync();
   pos = sel_compact(L, w, lane, pos, a.k, &tau);
