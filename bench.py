@@ -8,8 +8,8 @@ call over the whole batch, i.e. every stage of the path: gist scoring +
 attention over all gists and the tail, exact top-k, unfold of the chosen
 chunks and the merge, in one launch of unit_kernel: one workgroup per
 (batch, kv-head) unit for its 256 units (configurations with fewer units use
-several workgroups per unit that hand their partial states to the unit's
-last one).
+several workgroups per unit and a second launch, unit_unfold_kernel, that
+selects, unfolds and merges).
 
 `--config prefill_64k` times the causal block-sparse prefill instead (4096
 query positions at the end of a 65536-token sequence, 32/8 heads, k=16, W=64).

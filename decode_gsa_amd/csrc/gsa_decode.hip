@@ -8,14 +8,26 @@
 // entry point (score the meta-gists, then the gists of the chosen groups,
 // then unfold raw chunks).
 //
-// Two launch shapes:
-//   unit_kernel   (bf16, D = 128, >= 256 units, <= 4096 gists, k <= 64) one
-//                 workgroup runs a unit's whole step: its four waves stream
-//                 the gists and the tail on MFMA through direct-to-LDS rings,
-//                 the group scores stay in LDS, the exact top-k runs in LDS,
-//                 the waves stream the chosen chunks' raw rows and merge their
-//                 four softmax states. Nothing is handed off through memory.
-//   gist_kernel + unfold_kernel (every other shape, and two-level decode)
+// Launch shapes:
+//   unit path (bf16, D = 128, k <= 64): a workgroup's four waves stream rows
+//                 on MFMA through direct-to-LDS rings, keep the group scores
+//                 in LDS and run an exact top-k in LDS.
+//     unit_kernel alone (>= 256 units, <= 4096 gists): one workgroup runs a
+//                 unit's whole step -- gists and tail, the top-k, the chosen
+//                 chunks' raw rows, the merge of its four waves' softmax
+//                 states. Nothing is handed off through memory.
+//     unit_kernel + unit_unfold_kernel (fewer units or more gists): S
+//                 workgroups per unit stream shares of the gists and tail and
+//                 hand their partial states and group scores on; S2
+//                 workgroups per unit then each make the unit's selection,
+//                 stream a share of the chosen raw rows, and the last one
+//                 merges every partial (k = 0: the stream launch's last
+//                 workgroup merges).
+//     unit_kernel<HIER> + unit_hier_kernel (two-level decode): the level-2
+//                 gists and the tail, then one workgroup per unit for the
+//                 level-2 selection, the candidate level-1 gists, the
+//                 level-1 selection, the unfold and the merge.
+//   gist_kernel + unfold_kernel (every other shape: fp32, D = 64, k > 64, ...)
 //                 split-K over gists: each gist workgroup streams a range of
 //                 gist rows (and a share of the tail), keeps its group scores
 //                 and writes one online-softmax partial (m, l, acc[D]) per

@@ -13,12 +13,16 @@
 //
 //   prefill_select  group score S[t][m] = (scale/g) * sum_h q_h(t) . k(gist m)
 //                   for eligible gists, per query the exact top-k (ties to the
-//                   smaller m) -> sel. The g heads of a query form one
-//                   contraction of length g*D, so one MFMA chain gives the
-//                   group score. Top-k is a streaming filter: a per-query LDS
-//                   buffer of survivors (in gist order) is compacted to the
-//                   exact top-k by a bit-serial radix select whenever it fills;
-//                   afterwards only scores above the k-th best can enter.
+//                   smaller m) -> sel. The sum over heads is taken on the
+//                   query side (qbar = sum_h q_h, kept as bf16 hi + lo), so
+//                   two MFMA chains give the group score. Top-k is a
+//                   streaming filter: the four lanes that hold a query's
+//                   scores keep candidate lists in LDS; a score enters when it
+//                   beats the query's running bound tau; when a list fills,
+//                   the workgroup prunes every list (a bisection finds a
+//                   value with at least k entries at or above it) and the
+//                   bound rises; the end is an exact radix selection.
+//                   In a 32-gist tile a lane sees eight scores.
 //   prefill_attend  softmax attention over every eligible gist, the raw rows of
 //                   the union of the block's selected chunks (a query sees a
 //                   chunk only if it selected it) and the causal window
@@ -27,7 +31,8 @@
 //                   results keep one query row per lane; V^T comes from the
 //                   row-major V tile through the transposing LDS read
 //                   (ds_read_b64_tr_b16). P is split into bf16 hi + lo parts so
-//                   that P.V keeps about 16 bits of the fp32 weights. With g = 4
+//                   that P.V keeps about 16 bits of the fp32 weights (hi is p
+//                   truncated to bf16, lo = p - hi rounded). With g = 4
 //                   two waves share a query tile (two heads each), so each SIMD
 //                   runs two waves.
 //
