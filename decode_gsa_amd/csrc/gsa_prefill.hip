@@ -138,6 +138,25 @@ __device__ __forceinline__ void lds_tr_tile(const uint32_t (&addr)[8], bf16x8 (&
   for (int dt = 0; dt < 8; ++dt) vf[dt] = cat8(a[dt], b[dt]);
 }
 
+// Eight 16-byte LDS reads issued together in one asm block that also waits
+// for them (the builtin reads would get a wait after every pair).
+__device__ __forceinline__ void lds_read8x16(const uint32_t (&addr)[8], uint4 (&r)[8]) {
+  __asm__ volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+        "v"(addr[7])
+      : "memory");
+}
+
 // LDS slot of chunk c of tile row r.
 __device__ __forceinline__ int k_slot(int c, int r) { return c ^ (r & 15); }
 __device__ __forceinline__ int v_slot(int c, int r) { return c ^ (2 * (r & 7)); }
@@ -563,15 +582,30 @@ __global__ __launch_bounds__(kSelThreads, 2) void prefill_select(SelArgs a) {
     f32x4 acc[kSelSub][2];
 #pragma unroll
     for (int s = 0; s < kSelSub; ++s) acc[s][0] = acc[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // every K operand read of the tile in one asm block: one LDS round trip,
+    // not four (the compiler would wait after each pair)
+    static_assert(kSelSub == 2, "eight operand reads per tile");
+    bf16x8 kf[4][kSelSub];
+    {
+      const uint32_t kb = lds_addr(kt);
+      uint32_t ad[8];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int sb = 0; sb < kSelSub; ++sb) ad[2 * ks + sb] = kb + koff[sb][ks];
+      uint4 r[8];
+      lds_read8x16(ad, r);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int s = 0; s < kSelSub; ++s) kf[ks][s] = __builtin_bit_cast(bf16x8, r[2 * ks + s]);
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 kf[kSelSub];
-#pragma unroll
-      for (int s = 0; s < kSelSub; ++s) kf[s] = lds_b128(kt + koff[s][ks]);
 #pragma unroll
       for (int s = 0; s < kSelSub; ++s) {
-        acc[s][0] = mfma(kf[s], qh[ks], acc[s][0]);
-        if (G > 1) acc[s][1] = mfma(kf[s], ql[ks], acc[s][1]);   // g = 1: lo is zero
+        acc[s][0] = mfma(kf[ks][s], qh[ks], acc[s][0]);
+        if (G > 1) acc[s][1] = mfma(kf[ks][s], ql[ks], acc[s][1]);   // g = 1: lo is zero
       }
     }
     // score of gist kSelTile it + 16 s + 4 jg + r against query qi
@@ -743,18 +777,29 @@ __device__ __forceinline__ void att_tile(const char* kt, const char* vt, const A
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int h = 0; h < H; ++h) s[sb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // 2 H independent MFMA chains, interleaved so that no product waits on the
-  // one just issued
+  // the tile's eight K operand reads in one round trip, then 2 H independent
+  // MFMA chains, interleaved so that no product waits on the one just issued
+  bf16x8 kf[4][2];
+  {
+    uint32_t ad[8];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    bf16x8 kf[2];
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) kf[sb] = lds_b128(kt + (16 * sb + qi) * kRowBytes + k_slot(4 * ks + jg, qi) * 16);
+      for (int sb = 0; sb < 2; ++sb)
+        ad[2 * ks + sb] = lds_addr(kt) + (16 * sb + qi) * kRowBytes + k_slot(4 * ks + jg, qi) * 16;
+    uint4 r[8];
+    lds_read8x16(ad, r);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) kf[ks][sb] = __builtin_bit_cast(bf16x8, r[2 * ks + sb]);
+  }
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int h = 0; h < H; ++h) s[sb][h] = mfma(kf[sb], qf[h][ks], s[sb][h]);
-  }
+      for (int h = 0; h < H; ++h) s[sb][h] = mfma(kf[ks][sb], qf[h][ks], s[sb][h]);
   // s[sb][h][r]: row i0 + 16sb + 4jg + r against the lane's query, head h
   if (masked) {
 #pragma unroll
