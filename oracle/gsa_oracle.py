@@ -22,6 +22,10 @@ in float64 on the exact input values (bf16 inputs are widened exactly):
     (same section, 'Hybrid Attention'), plus the trailing raw tokens that
     have no gist yet or that form the uncompressed suffix (slide deck,
     slide 9, prefix/suffix split);
+  * selection-rule variants -- the slide deck's slide 17 ('Selective Rules
+    Comparison') compares the set above (all gists + selected raw tokens)
+    with the selected chunks' gists + their raw tokens, and with the selected
+    raw tokens alone; ``gist_set`` picks one of the three;
   * two-level variant -- meta-gists are scored first, then the gists inside
     the chosen meta-gist groups, then raw chunks are unfolded (gist.science
     explainer, 'Hierarchical Extension (H-GSA)', 'Coarse-to-Fine Selection');
@@ -148,15 +152,21 @@ def _check_common(n_raw: int, n_gist: int, C: int, R: int) -> None:
 
 # ---------------------------------------------------------------- decode ---
 
+GIST_SETS = ("all", "selected", "none")
+
+
 def decode_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, *, n_raw: int,
                 n_gist: int, chunk: int, topk: int, tail: int,
-                scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+                scale: Optional[float] = None, gist_set: str = "all") -> Dict[str, np.ndarray]:
     """One (batch, kv-head) unit of single-level GSA decode.
 
     qg: [g, D] query heads sharing this kv-head.  K, V: [R, D] interleaved
-    cache of the unit, R = n_raw + n_gist.  Returns out [g, D], lse [g],
-    wsum [g], sel [k] (ascending chunk ids), rows (sorted attention-set rows)
-    and scores [M] (group scores of every gist).
+    cache of the unit, R = n_raw + n_gist.  gist_set: which gist rows join
+    the attention set -- "all" (every gist; the hybrid attention of section 2),
+    "selected" (the selected chunks' gists) or "none" (raw tokens only); the
+    last two are slide 17's SG+SR and SR-only rules.  Returns out [g, D],
+    lse [g], wsum [g], sel [k] (ascending chunk ids), rows (sorted
+    attention-set rows) and scores [M] (group scores of every gist).
     """
     qg = _f64(qg)
     g, D = qg.shape
@@ -166,6 +176,10 @@ def decode_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, *, n_raw: int,
         raise ValueError("need 0 <= topk <= n_gist")
     if not (N - M * C <= T <= N):
         raise ValueError("tail must cover the raw tokens after the last gist")
+    if gist_set not in GIST_SETS:
+        raise ValueError(f"gist_set must be one of {GIST_SETS}")
+    if gist_set != "all" and topk == 0 and T == 0:
+        raise ValueError("the attention set would be empty")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
 
     # 1. routing: score every gist
@@ -173,8 +187,14 @@ def decode_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, *, n_raw: int,
     S = _group_scores(qg, _f64(K[gist_rows]), scale) if M else np.zeros(0)
     # 2. top-k chunks
     sel = topk_ascending(S, list(range(M)), topk)
-    # 3. unfold: attention set = all gists + raw of selected chunks + tail
-    A = set(gist_rows)
+    # 3. unfold: attention set = the gists of the rule + raw of selected
+    #    chunks + tail
+    if gist_set == "all":
+        A = set(gist_rows)
+    elif gist_set == "selected":
+        A = {gist_rows[m] for m in sel}
+    else:
+        A = set()
     for m in sel:
         for j in range(C):
             A.add(raw_row_index(m * C + j, C, M))
@@ -196,7 +216,7 @@ def _units(B: int, Hkv: int, units: Optional[Iterable[Tuple[int, int]]]):
 def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, *, chunk: int,
            topk: int, tail: int, n_gist: Optional[int] = None,
            scale: Optional[float] = None,
-           units: Optional[Iterable[Tuple[int, int]]] = None):
+           units: Optional[Iterable[Tuple[int, int]]] = None, gist_set: str = "all"):
     """Batched single-level decode. q [B, Hq, D]; caches [B, Hkv, R, D].
 
     Returns out [B, Hq, D], lse [B, Hq], sel [B, Hkv, k] (units not listed in
@@ -214,7 +234,7 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, *, chunk: in
     for b, j in _units(B, Hkv, units):
         r = decode_unit(q[b, j * g:(j + 1) * g], k_cache[b, j], v_cache[b, j],
                         n_raw=n_raw, n_gist=n_gist, chunk=chunk, topk=topk, tail=tail,
-                        scale=scale)
+                        scale=scale, gist_set=gist_set)
         out[b, j * g:(j + 1) * g] = r["out"]
         lse[b, j * g:(j + 1) * g] = r["lse"]
         sel[b, j] = r["sel"]

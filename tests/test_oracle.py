@@ -437,3 +437,66 @@ def test_prefill_window_rows_literal():
     p = oracle.prefill_query(rng.standard_normal((1, D)), K, V, t=10, n_raw=N, n_gist=M,
                              chunk=C, topk=0, window=3)
     assert list(p["rows"]) == [4, 9, 10, 11, 12]
+
+
+# ----------------------------------------- selection-rule variants (slide 17) ---
+
+def _variant_mask(sel, C, M, N, T, R, gist_set):
+    """Attention-set mask built from row kinds (independent of the oracle's
+    position-to-row map): the rule's gists, raw rows of selected chunks, tail."""
+    mask = np.zeros(R, bool)
+    for r in range(R):
+        kind, v = row_kind(r, C, M)
+        if kind == "gist":
+            mask[r] = gist_set == "all" or (gist_set == "selected" and v in sel)
+        else:
+            mask[r] = v >= N - T or (v // C < M and v // C in sel)
+    return mask
+
+
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+@pytest.mark.parametrize("C,M,r,k,T", [(4, 12, 0, 3, 5), (8, 9, 3, 4, 3), (16, 6, 16, 2, 20), (3, 11, 1, 5, 1)])
+def test_gist_set_variants_match_masked_sdpa(gist_set, C, M, r, k, T):
+    rng = np.random.default_rng(C * 1000 + M * 10 + k)
+    g, D = 3, 16
+    N = M * C + r
+    R = N + M
+    qg, K, V = rng.standard_normal((g, D)), rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    base = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=k, tail=T)
+    res = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=k, tail=T, gist_set=gist_set)
+    np.testing.assert_array_equal(res["sel"], base["sel"])       # the rule changes the set, not the choice
+    mask = _variant_mask(set(res["sel"].tolist()), C, M, N, T, R, gist_set)
+    assert len(res["rows"]) == mask.sum()
+    ref = sdpa(qg, K, V, mask, 1 / math.sqrt(D))
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res["wsum"], 1.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,M,r", [(4, 12, 0), (8, 5, 3)])
+def test_gist_set_with_k_equals_M(C, M, r):
+    """Every chunk selected: the selected-gist rule is full attention, the
+    raw-only rule is full attention over the raw rows."""
+    rng = np.random.default_rng(C + M)
+    g, D = 2, 8
+    N = M * C + r
+    R = N + M
+    qg, K, V = rng.standard_normal((g, D)), rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    sg = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=M, tail=r, gist_set="selected")
+    np.testing.assert_allclose(sg["out"], sdpa(qg, K, V, np.ones(R, bool), 1 / math.sqrt(D)), rtol=0, atol=1e-12)
+    sr = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=M, tail=r, gist_set="none")
+    raw = np.array([row_kind(i, C, M)[0] == "raw" for i in range(R)])
+    np.testing.assert_allclose(sr["out"], sdpa(qg, K, V, raw, 1 / math.sqrt(D)), rtol=0, atol=1e-12)
+
+
+def test_gist_set_k_zero_is_tail_only_and_empty_set_is_rejected():
+    rng = np.random.default_rng(3)
+    g, D, C, M, T = 2, 8, 4, 6, 5
+    N = M * C
+    R = N + M
+    qg, K, V = rng.standard_normal((g, D)), rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    res = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=0, tail=T, gist_set="selected")
+    tail = np.array([row_kind(i, C, M) == ("raw", row_kind(i, C, M)[1]) and row_kind(i, C, M)[1] >= N - T
+                     for i in range(R)])
+    np.testing.assert_allclose(res["out"], sdpa(qg, K, V, tail, 1 / math.sqrt(D)), rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=0, tail=0, gist_set="none")
