@@ -53,6 +53,8 @@ PREFILL_METRIC = "GSA block-sparse prefill query-positions/s + MFMA utilisation 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GIST_SET_NAMES = {"selected": "selected chunks' gists + raw + tail (SG+SR)",
+                  "none": "selected raw + tail (SR-only)"}
 
 
 def log(*a):
@@ -152,11 +154,13 @@ def measured_traffic(key: str, sha: str):
 
 # ---------------------------------------------------------------- decode ---
 
-def decode_bytes(cfg, sel):
+def decode_bytes(cfg, sel, gist_set="all"):
     """Algorithmic bytes per call: (gist pass, unfold pass). Gist pass: every
     gist row and every tail row (K + V), q. Unfold pass: the raw rows of the
     selected chunks not in the tail (K + V), the fp32 output, lse and the
-    selected ids."""
+    selected ids. With gist_set "selected" / "none" the gist pass reads the
+    gists' K rows only (scores), and "selected" adds the chosen gists' V
+    rows to the unfold pass."""
     eb = 2 if cfg.dtype == "bf16" else 4
     row = 2 * cfg.head_dim * eb
     units = cfg.batch * cfg.n_kv_heads
@@ -168,13 +172,17 @@ def decode_bytes(cfg, sel):
             for m in sel[u]:
                 raw_sel += max(0, min(cfg.chunk, tail0 - int(m) * cfg.chunk))
     q = cfg.batch * cfg.n_q_heads * cfg.head_dim * eb
-    gist = units * (cfg.M + cfg.tail) * row + q
     out = cfg.batch * cfg.n_q_heads * (cfg.head_dim + 1) * 4 + units * cfg.topk * 4
-    unfold = raw_sel * row + out
+    if gist_set == "all":
+        gist = units * (cfg.M + cfg.tail) * row + q
+        unfold = raw_sel * row + out
+    else:
+        gist = units * cfg.M * (row // 2) + units * cfg.tail * row + q
+        unfold = raw_sel * row + (units * cfg.topk * (row // 2) if gist_set == "selected" else 0) + out
     return gist, unfold
 
 
-def cpu_baseline_decode(inp, cfg, budget_s: float):
+def cpu_baseline_decode(inp, cfg, budget_s: float, gist_set: str = "all"):
     """The fp64 oracle (as it stands) on whole decode units, one thread."""
     import oracle
     from threadpoolctl import threadpool_limits
@@ -189,7 +197,7 @@ def cpu_baseline_decode(inp, cfg, budget_s: float):
                 V = inp.v_cache[b, j].float().cpu().numpy()
                 t0 = time.perf_counter()
                 oracle.decode_unit(q[b, j * g:(j + 1) * g], K, V, n_raw=cfg.n_raw, n_gist=cfg.M,
-                                   chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail)
+                                   chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail, gist_set=gist_set)
                 t_total += time.perf_counter() - t0
                 n_qh += g
                 if t_total >= budget_s:
@@ -227,14 +235,15 @@ def run_decode_bench(args):
     def step(i):
         l = i % layers
         gsa.gsa_decode(inp.q, ks[l], vs[l], chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail,
-                       n_gist=cfg.M, out=out, lse=lse, sel_idx=sel, workspace=ws, stream=stream)
+                       n_gist=cfg.M, out=out, lse=lse, sel_idx=sel, workspace=ws, stream=stream,
+                       gist_set=args.gist_set)
 
     # parity spot check of this exact launch configuration (selection = planted set)
     step(0)
     torch.cuda.synchronize()
     if cfg.topk > 0 and inp.planted is not None:
         assert torch.equal(sel.long(), inp.planted), "selection differs from the planted top-k"
-    gist_b, unfold_b = decode_bytes(cfg, sel.cpu().numpy() if cfg.topk else [])
+    gist_b, unfold_b = decode_bytes(cfg, sel.cpu().numpy() if cfg.topk else [], args.gist_set)
     alg_b = gist_b + unfold_b
     # launch structure of this call (the timing hook counts the launches):
     # unit_kernel (bf16, D = 128, k <= 64, at most 16384 gists when k > 0),
@@ -274,13 +283,16 @@ def run_decode_bench(args):
         "data": "synthetic (seeded Gaussian q/K/V, planted top-k with margin >= 0.5)",
         "config": {"workload": f"{cfg.name}: GQA decode step, B={cfg.batch}, Hq={cfg.n_q_heads}, "
                                f"Hkv={cfg.n_kv_heads}, D={cfg.head_dim}, N={cfg.n_raw}, "
-                               f"C={cfg.chunk}, k={cfg.topk}, T={cfg.tail}, {cfg.dtype} cache",
+                               f"C={cfg.chunk}, k={cfg.topk}, T={cfg.tail}, {cfg.dtype} cache"
+                               + ("" if args.gist_set == "all" else
+                                  f", attention set: {GIST_SET_NAMES[args.gist_set]}"),
                    "global_batch": cfg.batch, "seq_len": cfg.n_raw, "parallelism": "none (1 GPU)",
                    "cache_layers_rotated": layers},
         "tokens_per_s": cfg.batch / (ms_per_step / 1e3),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(f"{main}/{cfg.name}", sha),
+                     "traffic": measured_traffic(f"{main}/{cfg.name}"
+                                                 + ("" if args.gist_set == "all" else f"/{args.gist_set}"), sha),
                      "kernel": main, "alg_bytes_per_launch": main_b,
                      "launch_ms_mean": main_ms},
         "call": {"ms_mean": call_ms, "alg_bytes": alg_b, "GB_s": alg_b / (call_ms / 1e3) / 1e9},
@@ -290,7 +302,7 @@ def run_decode_bench(args):
     res["roofline"]["machine_stream_rates"] = hbm_stream_rates()
     if not args.no_cpu:
         log("[bench] timing the CPU oracle ...")
-        res["cpu_baseline"] = cpu_baseline_decode(inp, cfg, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline_decode(inp, cfg, args.cpu_seconds, args.gist_set)
     return res
 
 
@@ -559,6 +571,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--gist-set", default="all", choices=["all", "selected", "none"],
+                    help="decode attention-set rule (slide 17 variants)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "

@@ -27,6 +27,8 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
 GSA_F32, GSA_BF16 = 0, 1
+# gsa_status_t
+GSA_OK, GSA_ERR_INVALID_ARG, GSA_ERR_UNSUPPORTED, GSA_ERR_WORKSPACE, GSA_ERR_HIP = 0, 1, 2, 3, 4
 EXPORTED_SYMBOLS = (
     "gsa_decode_workspace_size", "gsa_decode",
     "gsa_decode_hier_workspace_size", "gsa_decode_hier",
@@ -42,7 +44,7 @@ class DecodeParams(ctypes.Structure):
     _fields_ = [("batch", _c_i32), ("n_q_heads", _c_i32), ("n_kv_heads", _c_i32),
                 ("head_dim", _c_i32), ("n_raw", _c_i64), ("n_gist", _c_i64),
                 ("chunk", _c_i32), ("topk", _c_i32), ("tail", _c_i32), ("scale", _c_f32),
-                ("dtype", _c_i32)]
+                ("dtype", _c_i32), ("gist_set", _c_i32)]
 
 
 class HierParams(ctypes.Structure):
@@ -128,9 +130,9 @@ def _dtype_code(t) -> int:
 
 
 def decode_params(batch, n_q_heads, n_kv_heads, head_dim, n_raw, n_gist, chunk, topk, tail,
-                  scale=0.0, dtype=GSA_BF16) -> DecodeParams:
+                  scale=0.0, dtype=GSA_BF16, gist_set=0) -> DecodeParams:
     return DecodeParams(batch, n_q_heads, n_kv_heads, head_dim, n_raw, n_gist, chunk, topk,
-                        tail, scale, dtype)
+                        tail, scale, dtype, gist_set)
 
 
 def hier_params(base: DecodeParams, fanout: int, topk2: int) -> HierParams:
@@ -201,11 +203,16 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
+GIST_SETS = {"all": 0, "selected": 1, "none": 2}
+
+
 def gsa_decode(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int,
                n_gist: Optional[int] = None, scale: float = 0.0, out=None, lse=None,
                sel_idx=None, workspace=None, stream=None, want_lse: bool = True,
-               want_sel: bool = True):
+               want_sel: bool = True, gist_set: str = "all"):
     """Single-level GSA decode. q [B,Hq,D]; caches [B,Hkv,R,D] (bf16 or fp32).
+    gist_set: "all" (every gist), "selected" (the chosen chunks' gists) or
+    "none" -- which gist rows the attention set holds.
 
     Returns (out [B,Hq,D] fp32, lse [B,Hq] fp32 or None, sel [B,Hkv,k] int32 or None).
     """
@@ -213,7 +220,10 @@ def gsa_decode(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int,
     B, Hq, D = q.shape
     Hkv, R = k_cache.shape[1], k_cache.shape[2]
     M = R // (chunk + 1) if n_gist is None else n_gist
-    p = decode_params(B, Hq, Hkv, D, R - M, M, chunk, topk, tail, scale, _dtype_code(q))
+    if gist_set not in GIST_SETS:
+        raise ValueError(f"gist_set must be one of {tuple(GIST_SETS)}")
+    p = decode_params(B, Hq, Hkv, D, R - M, M, chunk, topk, tail, scale, _dtype_code(q),
+                      GIST_SETS[gist_set])
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q, k_cache, v_cache must share one dtype")
     if tuple(k_cache.shape) != (B, Hkv, R, D) or tuple(v_cache.shape) != (B, Hkv, R, D):

@@ -1546,6 +1546,8 @@ struct UnitArgs {
   float* s2;
   int64_t s2_stride;
   int32_t* sel2;
+  // which gists the attention set holds: 0 all, 1 the selected chunks', 2 none
+  int32_t gist_set;
 };
 
 struct UnitLds {
@@ -1582,7 +1584,12 @@ struct UState {
 //              tail rows                                             (scored)
 //   kUKCand    level-1 candidates: the G children of each chosen level-2
 //              group (lds_sel: group ids), then the orphans           (scored)
-enum { kUKGists = 0, kUKUnfold = 1, kUKL2 = 2, kUKCand = 3 };
+//   kUKScore   items below M: the gists' K rows only, 32 per stage; group
+//              scores, no attention                                   (scored)
+//   kUKSet     the raw rows of the chosen chunks (skipping those the tail
+//              attends), then the chosen chunks' gists when the set keeps
+//              them (gist_set 1), then the tail rows
+enum { kUKGists = 0, kUKUnfold = 1, kUKL2 = 2, kUKCand = 3, kUKScore = 4, kUKSet = 5 };
 
 // Stream items [i0, i1) of one kind through the wave's state.
 template <int KIND>
@@ -1595,16 +1602,25 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
   if (n <= 0) return;
   const int lane = threadIdx.x & 63;
   const int hq = lane & 15, jg = lane >> 4;
-  const int nb = (n + kUBR - 1) / kUBR;
+  constexpr int kRows = KIND == kUKScore ? 2 * kUBR : kUBR;   // rows per stage (K only: twice as many)
+  const int nb = (n + kRows - 1) / kRows;
   const int C = a.C, M = (int)a.M;
   const unsigned tail0 = (unsigned)(a.N - a.T);   // rows and positions fit in 31 bits here
-  constexpr bool kScored = KIND != kUKUnfold;
-  const int n_scored = KIND == kUKGists ? M : KIND == kUKL2 ? (int)a.M2 : i1;
+  constexpr bool kScored = KIND != kUKUnfold && KIND != kUKSet;
+  const int n_scored = KIND == kUKGists || KIND == kUKScore ? M : KIND == kUKL2 ? (int)a.M2 : i1;
+  const int kC = a.k * C;                              // kUKSet: raw items, then gists, then tail
+  const int kg = KIND == kUKSet && a.gist_set == 1 ? a.k : 0;
   // cache row of item i; -1 when there is no such item or the tail owns it,
   // -2 - j for level-2 gist j. Raw position p sits in row p + p / C (p + M
   // past the last gist).
   auto row_of = [&](int i) -> int {
     if (i >= i1) return -1;
+    if (KIND == kUKScore) return i * (C + 1) + C;
+    if (KIND == kUKSet && i >= kC) {
+      if (i < kC + kg) return (int)(min((unsigned)lds_sel[i - kC], (unsigned)(M - 1)) * (unsigned)(C + 1) + (unsigned)C);
+      const unsigned pos = tail0 + (unsigned)(i - kC - kg);
+      return (int)(pos + min(pos / (unsigned)C, (unsigned)M));
+    }
     if (KIND == kUKGists || KIND == kUKL2) {
       const int nf = KIND == kUKGists ? M : (int)a.M2;
       if (i < nf) return KIND == kUKGists ? i * (C + 1) + C : -2 - i;
@@ -1632,10 +1648,22 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     char* kd = ring + (b % kUNB) * kUStage;
     char* vd = kd + kUTile;
     const int sl = lane & 15;
+    if constexpr (KIND == kUKScore) {
+      // rows 0..15 of the stage into the K tile, rows 16..31 into the V tile's place
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = 4 * (u & 3) + (lane >> 4);
+        const int row = row_of(i0 + b * kRows + 16 * (u >> 2) + r);
+        const int64_t koffr = (int64_t)(row >= 0 ? row : 0) * 256;
+        __builtin_amdgcn_global_load_lds(Kb + koffr + uk_slot(sl, r) * 16, kd + (u >> 2) * kUTile + (u & 3) * 1024, 16,
+                                         0, kUNt);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int r = 4 * u + (lane >> 4);
-      const int row = row_of(i0 + b * kUBR + r);
+      const int row = row_of(i0 + b * kRows + r);
       int64_t koffr = (int64_t)(row >= 0 ? row : 0) * 256, voffr = koffr;
       if (KIND == kUKL2 && row <= -2) {
         koffr = k2off + (int64_t)(-2 - row) * 256;
@@ -1660,6 +1688,27 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
   }
   auto compute = [&](int b) {
     const uint32_t base = ring_lds + (b % kUNB) * kUStage;
+    if constexpr (KIND == kUKScore) {
+      // two 16-row halves: group scores only
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t ka[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) ka[ks] = base + h * kUTile + koff[ks];
+        bf16x8u kf[4];
+        u_k_frag(ka, kf);
+        f32x4u s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+        const int i_base = i0 + b * kRows + 16 * h + 4 * jg;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gsum = group_sum<16>(s[r]);
+          if (hq == 0 && i_base + r < i1) lds_scores[i_base + r - score_base] = gsum * a.score_mul;
+        }
+      }
+      return;
+    }
     uint32_t ka[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) ka[ks] = base + koff[ks];
@@ -1669,7 +1718,7 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], s, 0, 0, 0);
     // s[r]: head hq against stage row 4 jg + r
-    const int i_base = i0 + b * kUBR + 4 * jg;
+    const int i_base = i0 + b * kRows + 4 * jg;
     bool ok[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) ok[r] = kScored ? i_base + r < i1 : row_of(i_base + r) >= 0;
@@ -1800,7 +1849,7 @@ __device__ __forceinline__ void unit_combine(UnitLds& L, const UState& st, int w
 // HIER: the first launch of two-level decode -- the level-2 gists (their own
 // arrays) and the tail; every workgroup hands its partial state and level-2
 // scores to unit_hier_kernel.
-template <int G, bool HIER>
+template <int G, bool HIER, bool SETS = false>
 __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
   __shared__ __attribute__((aligned(16))) UnitLds L;
   // the wave index as a scalar: each wave's item ranges and trip counts are
@@ -1846,6 +1895,27 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
     unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)split * a.part_stride);
     float* s2u = a.s2 + (size_t)unit * a.s2_stride;
     for (int i = w0 + tid; i < min(w1, nf); i += kUW * 64) st_coh(s2u + i, L.scores[i - w0]);
+    return;
+  }
+  if constexpr (SETS) {
+    // selection-rule variants (one workgroup per unit): the gists' K rows for
+    // the scores only; then the chosen chunks' raw rows, their gists if the
+    // set keeps them, and the tail, all attended
+    const int perg = (M + kUW - 1) / kUW;
+    unit_stream<kUKScore>(Kb, Vb, min(M, w * perg), min(M, (w + 1) * perg), a, qf, st, ring, L.scores, L.sel);
+    __syncthreads();   // every group score is in LDS, every ring idle
+    float* gsv = a.scores + (size_t)unit * a.score_stride;
+    if (a.k > 0) {
+      unit_select<kUMaxGist / kThreads, true>(L.scores, M, a.k, gsv, a.score_stride, unit, L.sel, L.u.sel.s,
+                                               L.u.sel.t);
+      __syncthreads();
+    }
+    const int n3 = a.k * a.C + (a.gist_set == 1 ? a.k : 0) + a.T;
+    const int per3 = (n3 + kUW - 1) / kUW;
+    unit_stream<kUKSet>(Kb, Vb, min(n3, w * per3), min(n3, (w + 1) * per3), a, qf, st, ring, L.scores, L.sel);
+    unit_combine<G>(L, st, w, a.out + (size_t)unit * G * 128, a.lse ? a.lse + (size_t)unit * G : nullptr, nullptr);
+    if (a.sel)
+      for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
     return;
   }
   unit_stream<kUKGists>(Kb, Vb, min(w1, w0 + w * per1), min(w1, w0 + (w + 1) * per1), a, qf, st, ring, L.scores,
@@ -2031,10 +2101,14 @@ gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const 
   u.R = pl.R; u.N = pl.N; u.M = pl.M; u.C = pl.C; u.k = pl.k; u.T = pl.T;
   u.scale_log2 = pl.scale * kLog2e; u.score_mul = pl.scale / G;
   u.S = pl.unit_S; u.S2 = pl.unit_S2; u.NP = pl.NP; u.part_stride = part_stride(G, 128);
+  u.gist_set = pl.gist_set;
   u.part = reinterpret_cast<float*>(ws + pl.off_part);
   u.cnt = ctrl_of(ws, pl.off_ctrl, 0);
   prof_begin_call();
-  prof_launch((unit_kernel<G, false>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0, st, u);
+  if (pl.gist_set != GSA_GISTS_ALL)
+    prof_launch((unit_kernel<G, false, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+  else
+    prof_launch((unit_kernel<G, false>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0, st, u);
   if (pl.unit_S2 > 0) prof_launch((unit_unfold_kernel<G>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st, u);
   return launch_status("gsa_decode launch");
 }

@@ -147,6 +147,12 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   d.T = p->tail;
   d.scale = resolve_scale(p->scale, p->head_dim);
   d.dtype = p->dtype;
+  if (p->gist_set < GSA_GISTS_ALL || p->gist_set > GSA_GISTS_NONE)
+    return fail(GSA_ERR_INVALID_ARG, "gist_set=%d not in {0, 1, 2}", p->gist_set);
+  if (p->gist_set != GSA_GISTS_ALL && p->topk == 0 && p->tail == 0)
+    return fail(GSA_ERR_INVALID_ARG, "gist_set=%d with topk = 0 and tail = 0 leaves nothing to attend",
+                p->gist_set);
+  d.gist_set = p->gist_set;
   d.S = splits_for(d.M, units);
   if (ceil_div(d.M, d.S) > kMaxTaskItems) d.S = (int32_t)ceil_div(d.M, kMaxTaskItems);
   d.gists_per_split = d.M > 0 ? ceil_div(d.M, d.S) : 0;
@@ -159,6 +165,10 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   d.NP = d.S + d.S2;
   d.score_stride = d.k > 0 ? (d.M + 63) / 64 * 64 : 0;
   d.unit_S = unit_splits(d);
+  if (d.gist_set != GSA_GISTS_ALL && d.unit_S != 1)
+    return fail(GSA_ERR_UNSUPPORTED,
+                "gist_set=%d runs on the one-workgroup-per-unit launch only (bf16, D = 128, topk <= 64, "
+                ">= 256 units, <= 4096 gists)", d.gist_set);
   d.unit_S2 = 0;
   if (d.unit_S > 1) {
     // the unfold launch: the stream's workgroup count, at least 64 rows each
@@ -182,6 +192,8 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
 
 gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
   if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->base.gist_set != GSA_GISTS_ALL)
+    return fail(GSA_ERR_UNSUPPORTED, "two-level decode attends every gist: base.gist_set must be 0");
   gsa_status_t s = plan_decode(&p->base, &o->base);
   if (s != GSA_OK) return s;
   HierPlan h{};

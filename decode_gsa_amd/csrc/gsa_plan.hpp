@@ -70,6 +70,7 @@ struct DecodePlan {
   int32_t C, k, T;
   float scale;          // resolved (> 0)
   int32_t dtype;
+  int32_t gist_set;     // GSA_GISTS_*
   // gist pass: S workgroups per unit, each over a contiguous gist range
   int32_t S;
   int64_t gists_per_split;

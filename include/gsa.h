@@ -77,7 +77,20 @@ typedef struct {
                           N - M*C <= T <= N */
   float scale;         /* <= 0: 1/sqrt(D) */
   int32_t dtype;       /* gsa_dtype_t of q, K, V */
+  int32_t gist_set;    /* which gist rows the attention set holds (the slide
+                          deck's slide 17, 'Selective Rules Comparison'):
+                          GSA_GISTS_ALL (0, the default: every gist, the
+                          explainer's hybrid attention), GSA_GISTS_SELECTED
+                          (1, the chosen chunks' gists: SG+SR) or
+                          GSA_GISTS_NONE (2, raw tokens only: SR-only).
+                          1 and 2 need k > 0 or T > 0 (a non-empty set) and
+                          run on the one-workgroup-per-unit launch only (bf16,
+                          D = 128, k <= 64, >= 256 units, <= 4096 gists);
+                          other shapes return GSA_ERR_UNSUPPORTED.
+                          gsa_decode_hier requires 0. */
 } gsa_decode_params;
+
+enum { GSA_GISTS_ALL = 0, GSA_GISTS_SELECTED = 1, GSA_GISTS_NONE = 2 };
 
 /* Bytes of device workspace gsa_decode needs for these parameters. */
 gsa_status_t gsa_decode_workspace_size(const gsa_decode_params* p, size_t* bytes);

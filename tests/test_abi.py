@@ -47,7 +47,9 @@ int main(void) {
   printf("gsa_hier_params %zu\n", sizeof(gsa_hier_params));
   printf("gsa_prefill_params %zu\n", sizeof(gsa_prefill_params));
   F(gsa_decode_params, n_raw); F(gsa_decode_params, n_gist); F(gsa_decode_params, chunk);
-  F(gsa_decode_params, scale); F(gsa_decode_params, dtype);
+  F(gsa_decode_params, scale); F(gsa_decode_params, dtype); F(gsa_decode_params, gist_set);
+  printf("GSA_GISTS_ALL %d\nGSA_GISTS_SELECTED %d\nGSA_GISTS_NONE %d\n", GSA_GISTS_ALL,
+         GSA_GISTS_SELECTED, GSA_GISTS_NONE);
   F(gsa_hier_params, fanout); F(gsa_hier_params, topk2);
   F(gsa_prefill_params, n_raw); F(gsa_prefill_params, q_start); F(gsa_prefill_params, n_q);
   F(gsa_prefill_params, scale); F(gsa_prefill_params, dtype);
@@ -61,8 +63,10 @@ int main(void) {
     assert int(got["gsa_decode_params"]) == ctypes.sizeof(gsa.DecodeParams)
     assert int(got["gsa_hier_params"]) == ctypes.sizeof(gsa.HierParams)
     assert int(got["gsa_prefill_params"]) == ctypes.sizeof(gsa.PrefillParams)
+    assert [int(got[f"GSA_GISTS_{n}"]) for n in ("ALL", "SELECTED", "NONE")] == \
+        [gsa.GIST_SETS[n] for n in ("all", "selected", "none")]
     for key, val in got.items():
-        if "." in key:
+        if "." in key and not key.startswith("GSA_"):
             t, m = key.split(".")
             cls = {"gsa_decode_params": gsa.DecodeParams, "gsa_hier_params": gsa.HierParams,
                    "gsa_prefill_params": gsa.PrefillParams}[t]
@@ -102,6 +106,12 @@ def ws_size(L, p):
     ({"n_raw": 1030, "tail": 6}, OK),
     ({"tail": 1025}, INVALID),                # tail > n_raw
     ({"scale": float("nan")}, INVALID),
+    ({"gist_set": 3}, INVALID),
+    ({"gist_set": -1}, INVALID),
+    ({"gist_set": 1}, UNSUPPORTED),           # 4 units: not the one-workgroup-per-unit launch
+    ({"gist_set": 2, "batch": 128}, OK),      # 256 units
+    ({"gist_set": 1, "batch": 128, "topk": 0, "tail": 0}, INVALID),   # nothing to attend
+    ({"gist_set": 2, "batch": 128, "dtype": gsa.GSA_F32}, UNSUPPORTED),
 ])
 def test_decode_param_validation(L, kw, status):
     st, n = ws_size(L, good_decode(**kw))

@@ -28,11 +28,11 @@ def gsa():
     return decode_gsa_amd
 
 
-def run_decode(gsa, inp, cfg, units=None):
+def run_decode(gsa, inp, cfg, units=None, gist_set="all"):
     """Run the GPU path once, then compare the listed units (default: all) with
     the oracle, copying only those units' cache slabs to the host."""
     out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=cfg.chunk,
-                                   topk=cfg.topk, tail=cfg.tail, n_gist=cfg.M)
+                                   topk=cfg.topk, tail=cfg.tail, n_gist=cfg.M, gist_set=gist_set)
     torch.cuda.synchronize()
     g = cfg.n_q_heads // cfg.n_kv_heads
     us = [(b, j) for b in range(cfg.batch) for j in range(cfg.n_kv_heads)] if units is None else units
@@ -40,7 +40,7 @@ def run_decode(gsa, inp, cfg, units=None):
     for b, j in us:
         r = oracle.decode_unit(to_np(inp.q[b, j * g:(j + 1) * g]), to_np(inp.k_cache[b, j]),
                                to_np(inp.v_cache[b, j]), n_raw=cfg.n_raw, n_gist=cfg.M,
-                               chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail)
+                               chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail, gist_set=gist_set)
         if cfg.topk > 0:
             np.testing.assert_array_equal(to_np(sel[b, j]), r["sel"], err_msg=f"unit {(b, j)}")
         got.append(to_np(out[b, j * g:(j + 1) * g]))

@@ -1,0 +1,92 @@
+"""GPU parity of gsa_decode's selection-rule variants (slide deck, slide 17
+'Selective Rules Comparison'): the attention set keeps the selected chunks'
+gists with their raw tokens (gist_set "selected", SG+SR) or the selected raw
+tokens alone ("none", SR-only), plus the tail. They run on the
+one-workgroup-per-unit launch (256 or more units, at most 4096 gists):
+gist keys are read for the scores only, then the chosen chunks' rows, their
+gists and the tail are attended. Checked against the fp64 oracle with the
+same rule: bit-exact selections, outputs and lse within the stated
+tolerance (tests/gpu_util.py).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gsa_inputs as gi
+from conftest import to_np
+from gpu_util import say
+from test_parity_decode import run_decode, sample_units
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_gsa_amd
+    decode_gsa_amd.lib()          # raises if the library is missing: no fallback
+    return decode_gsa_amd
+
+
+def cfg_of(name, **kw):
+    return dataclasses.replace(gi.CONFIGS[name], **kw)
+
+
+# (config, units compared: None = every unit, else that many sampled)
+CASES = [
+    (cfg_of("gqa_32k", n_raw=4096), None),                                  # 256 units, g = 4, k = 16
+    (cfg_of("gqa_32k", n_q_heads=8, n_raw=3000, n_gist=187, tail=40), 64),  # g = 1, ragged, partial chunk
+    (cfg_of("gqa_32k", n_q_heads=64, n_raw=2048), 64),                      # g = 8
+    (cfg_of("c8_131k", batch=32, n_raw=8192), 48),                          # C = 8, k = 64
+    (cfg_of("c32_131k", batch=32, n_raw=8192, tail=5), 48),                 # C = 32, short tail
+    (cfg_of("gqa_32k", n_raw=2048, topk=0, plant="none"), 64),              # k = 0: the tail alone
+    (cfg_of("gqa_32k", n_raw=1024, topk=64, plant="none"), 64),             # every chunk selected
+    (cfg_of("gqa_32k", n_raw=65536, tail=300), 12),                         # 4096 gists
+]
+
+
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+@pytest.mark.parametrize("case", range(len(CASES)), ids=[f"set{i}" for i in range(len(CASES))])
+def test_decode_gist_set(gsa, case, gist_set):
+    cfg, n = CASES[case]
+    say(f"decode gist_set={gist_set} {cfg} units={'all' if n is None else n}")
+    inp = gi.make_decode(cfg, 5000 + case, device="cuda")
+    units = None if n is None else sample_units(cfg, n=n, seed=case)
+    err = run_decode(gsa, inp, cfg, units=units, gist_set=gist_set)
+    say(f"  max err / rms = {err:.2e}")
+
+
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+def test_decode_gist_set_ties_and_tail_overlap(gsa, gist_set):
+    """q = 0: every score ties, so chunks 0..k-1 are chosen; the tail starts
+    inside chunk k-1, whose rows (and, for "selected", gist) are attended
+    once."""
+    C, M, k = 16, 128, 16
+    T = M * C - ((k - 1) * C + 8)
+    cfg = cfg_of("gqa_32k", n_raw=M * C, topk=k, tail=T, plant="none")
+    say(f"decode gist_set={gist_set} ties {cfg}")
+    inp = gi.make_decode(cfg, 5100, device="cuda")
+    inp.q.zero_()
+    out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=C, topk=k, tail=T,
+                                   gist_set=gist_set)
+    torch.cuda.synchronize()
+    assert (to_np(sel) == np.arange(k)[None, None, :]).all()
+    run_decode(gsa, inp, cfg, units=sample_units(cfg, n=16, seed=5), gist_set=gist_set)
+
+
+def test_decode_gist_set_rejections(gsa):
+    """Shapes off the one-workgroup-per-unit launch, an empty set and the
+    two-level entry point are refused before any launch."""
+    cfg = cfg_of("gqa_32k", batch=2, n_raw=4096)        # 16 units: several workgroups per unit
+    inp = gi.make_decode(cfg, 5200, device="cuda")
+    with pytest.raises(gsa.GsaError) as e:
+        gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=16, tail=64, gist_set="selected")
+    assert e.value.status == gsa.GSA_ERR_UNSUPPORTED
+    cfg = cfg_of("gqa_32k", n_raw=1024)
+    inp = gi.make_decode(cfg, 5201, device="cuda")
+    with pytest.raises(gsa.GsaError) as e:
+        gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=0, tail=0, gist_set="none")
+    assert e.value.status == gsa.GSA_ERR_INVALID_ARG
