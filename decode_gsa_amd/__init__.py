@@ -22,7 +22,7 @@ __all__ = [
     "decode_params", "hier_params", "prefill_params",
     "decode_workspace_size", "hier_workspace_size", "prefill_workspace_size", "new_workspace",
     "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse", "gsa_profile_events",
-    "gsa_profile_marks",
+    "gsa_profile_marks", "topk_for_budget", "GIST_SETS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -34,6 +34,7 @@ EXPORTED_SYMBOLS = (
     "gsa_decode_hier_workspace_size", "gsa_decode_hier",
     "gsa_prefill_workspace_size", "gsa_prefill_blocksparse",
     "gsa_profile_events", "gsa_profile_marks", "gsa_status_string", "gsa_last_error",
+    "gsa_topk_for_budget",
 )
 
 _c_i32, _c_i64, _c_f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -90,6 +91,8 @@ def lib() -> ctypes.CDLL:
                   "gsa_decode_hier", "gsa_prefill_workspace_size", "gsa_prefill_blocksparse",
                   "gsa_profile_events", "gsa_profile_marks"):
             getattr(L, f).restype = _c_i32
+        L.gsa_topk_for_budget.argtypes = [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32, P(_c_i32)]
+        L.gsa_topk_for_budget.restype = _c_i32
         L.gsa_status_string.argtypes = [_c_i32]
         L.gsa_status_string.restype = ctypes.c_char_p
         L.gsa_last_error.argtypes = []
@@ -204,6 +207,15 @@ def _nbytes(t) -> int:
 
 
 GIST_SETS = {"all": 0, "selected": 1, "none": 2}
+
+
+def topk_for_budget(budget: int, n_gist: int, chunk: int, tail: int, gist_set: str = "all") -> int:
+    """Fixed-token-budget mode: the largest top-k whose attention set fits
+    `budget` tokens (see gsa_topk_for_budget in include/gsa.h)."""
+    k = _c_i32(0)
+    _check(lib().gsa_topk_for_budget(budget, n_gist, chunk, tail, GIST_SETS[gist_set], ctypes.byref(k)),
+           "gsa_topk_for_budget")
+    return k.value
 
 
 def gsa_decode(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int,

@@ -304,6 +304,24 @@ gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* o) {
 
 }  // namespace gsa
 
+extern "C" gsa_status_t gsa_topk_for_budget(int64_t budget, int64_t n_gist, int32_t chunk, int32_t tail,
+                                            int32_t gist_set, int32_t* topk) {
+  gsa::clear_error();
+  if (!topk) return gsa::fail(GSA_ERR_INVALID_ARG, "topk is NULL");
+  if (n_gist < 0 || n_gist > (1 << 30) || chunk < 1 || tail < 0)
+    return gsa::fail(GSA_ERR_INVALID_ARG, "need n_gist >= 0, chunk >= 1, tail >= 0");
+  if (gist_set < GSA_GISTS_ALL || gist_set > GSA_GISTS_NONE)
+    return gsa::fail(GSA_ERR_INVALID_ARG, "gist_set=%d not in {0, 1, 2}", gist_set);
+  const int64_t fixed = (gist_set == GSA_GISTS_ALL ? n_gist : 0) + tail;   // tokens with k = 0
+  const int64_t per = chunk + (gist_set == GSA_GISTS_SELECTED ? 1 : 0);     // tokens per chosen chunk
+  if (budget < fixed)
+    return gsa::fail(GSA_ERR_INVALID_ARG, "budget %lld is below the %lld tokens of the set with k = 0",
+                     (long long)budget, (long long)fixed);
+  const int64_t k = (budget - fixed) / per;
+  *topk = (int32_t)(k < n_gist ? k : n_gist);
+  return GSA_OK;
+}
+
 extern "C" const char* gsa_status_string(gsa_status_t s) {
   switch (s) {
     case GSA_OK: return "GSA_OK";

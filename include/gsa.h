@@ -212,6 +212,21 @@ gsa_status_t gsa_profile_events(void* const* events, int32_t n);
  * armed or not; 0 before any call. GSA_ERR_INVALID_ARG for a NULL n. */
 gsa_status_t gsa_profile_marks(int32_t* n);
 
+/* ------------------------------------------------------------------------
+ * Fixed-token-budget mode (slide deck, slide 17: under one token budget,
+ * leaving out the unselected chunks' gists leaves room for more unfolded
+ * chunks). Host only.
+ * *topk = the largest k <= n_gist whose attention set under gist_set holds at
+ * most `budget` tokens, counting n_gist gists (GSA_GISTS_ALL) or k gists
+ * (GSA_GISTS_SELECTED) or none, plus k * chunk raw tokens and `tail` tail
+ * tokens with no overlap (k is fixed before the selection, so this is the
+ * most the set can hold).
+ * GSA_ERR_INVALID_ARG for n_gist < 0, chunk < 1, tail < 0, an unknown
+ * gist_set, a NULL topk, or a budget below the k = 0 set.
+ * ---------------------------------------------------------------------- */
+gsa_status_t gsa_topk_for_budget(int64_t budget, int64_t n_gist, int32_t chunk, int32_t tail,
+                                 int32_t gist_set, int32_t* topk);
+
 /* Static description of a status code. */
 const char* gsa_status_string(gsa_status_t s);
 

@@ -62,7 +62,7 @@ import numpy as np
 
 __all__ = [
     "gist_row_index", "raw_row_index", "topk_ascending",
-    "decode_unit", "decode", "decode_hier_unit", "decode_hier",
+    "decode_unit", "decode", "decode_hier_unit", "decode_hier", "topk_for_budget", "GIST_SETS",
     "prefill_query", "prefill",
 ]
 
@@ -153,6 +153,24 @@ def _check_common(n_raw: int, n_gist: int, C: int, R: int) -> None:
 # ---------------------------------------------------------------- decode ---
 
 GIST_SETS = ("all", "selected", "none")
+
+
+def topk_for_budget(budget: int, n_gist: int, chunk: int, tail: int, gist_set: str = "all") -> int:
+    """Fixed-token-budget mode (slide deck, slide 17: under one token budget,
+    leaving out the unselected chunks' gists frees room for more unfolded
+    chunks): the largest k <= n_gist whose attention set holds at most
+    ``budget`` tokens, counting every kept gist, C raw tokens per selected
+    chunk and the T tail tokens with no overlap (k is fixed before the
+    selection, so the count is the most the set can hold). -1 if even k = 0
+    exceeds the budget."""
+    if gist_set not in GIST_SETS:
+        raise ValueError(f"gist_set must be one of {GIST_SETS}")
+    best = -1
+    for k in range(n_gist + 1):
+        gists = n_gist if gist_set == "all" else (k if gist_set == "selected" else 0)
+        if gists + k * chunk + tail <= budget:
+            best = k
+    return best
 
 
 def decode_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, *, n_raw: int,

@@ -228,3 +228,23 @@ def test_python_binding_raises_without_gpu_tensors():
         q = torch.zeros(1, 1, 64)
         k = torch.zeros(1, 1, 17, 64)
         gsa.gsa_decode(q, k, k, chunk=16, topk=1, tail=0)
+
+
+@pytest.mark.parametrize("gist_set", ["all", "selected", "none"])
+def test_topk_for_budget_matches_the_oracle(L, gist_set):
+    """Host-only budget mode: the library's k equals the oracle's for a grid of
+    budgets and shapes; a budget below the k = 0 set is rejected."""
+    import oracle
+    for M, C, T in [(10, 4, 6), (0, 16, 3), (7, 1, 0), (100, 32, 64)]:
+        for budget in list(range(0, 60)) + [M * (C + 1) + T, 10 ** 7]:
+            want = oracle.topk_for_budget(budget, M, C, T, gist_set)
+            k = ctypes.c_int32(-5)
+            st = L.gsa_topk_for_budget(budget, M, C, T, gsa.GIST_SETS[gist_set], ctypes.byref(k))
+            if want < 0:
+                assert st == INVALID
+            else:
+                assert st == OK and k.value == want, (M, C, T, budget)
+    k = ctypes.c_int32(0)
+    assert L.gsa_topk_for_budget(100, 10, 0, 0, 0, ctypes.byref(k)) == INVALID    # chunk < 1
+    assert L.gsa_topk_for_budget(100, 10, 4, 0, 3, ctypes.byref(k)) == INVALID    # gist_set
+    assert L.gsa_topk_for_budget(100, 10, 4, 0, 0, None) == INVALID

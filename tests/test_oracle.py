@@ -500,3 +500,33 @@ def test_gist_set_k_zero_is_tail_only_and_empty_set_is_rejected():
     np.testing.assert_allclose(res["out"], sdpa(qg, K, V, tail, 1 / math.sqrt(D)), rtol=0, atol=1e-12)
     with pytest.raises(ValueError):
         oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=0, tail=0, gist_set="none")
+
+
+@pytest.mark.parametrize("gist_set", ["all", "selected", "none"])
+def test_topk_for_budget_is_the_largest_fitting_k(gist_set):
+    """The chosen k's attention set (the oracle's own rows, tail placed so it
+    overlaps no selected chunk) fits the budget and k + 1 would not; every
+    chunk selected when the budget holds them all."""
+    rng = np.random.default_rng(11)
+    g, D, C, M, T = 2, 8, 4, 10, 6
+    N = M * C
+    R = N + M
+    qg, K, V = rng.standard_normal((g, D)), rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    # planted: chunks 0.. score highest, so the selection stays clear of the tail
+    for m in range(M):
+        K[m * (C + 1) + C] = qg.mean(0) * (M - m)
+    for budget in range(0, R + 5):
+        k = oracle.topk_for_budget(budget, M, C, T, gist_set)
+        if k < 0:
+            assert (M if gist_set == "all" else 0) + T > budget
+            continue
+        if k == 0 and T == 0 and gist_set != "all":
+            continue
+        rows = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=k, tail=T,
+                                  gist_set=gist_set)["rows"]
+        assert len(rows) <= budget
+        if k < M - -(-T // C):   # k + 1 chunks that stay clear of the tail: no overlap to shrink the set
+            rows1 = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=k + 1, tail=T,
+                                       gist_set=gist_set)["rows"]
+            assert len(rows1) > budget
+    assert oracle.topk_for_budget(10 ** 6, M, C, T, gist_set) == M

@@ -90,3 +90,20 @@ def test_decode_gist_set_rejections(gsa):
     with pytest.raises(gsa.GsaError) as e:
         gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=0, tail=0, gist_set="none")
     assert e.value.status == gsa.GSA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("gist_set,want_k", [("all", 10), ("selected", 40), ("none", 42)])
+def test_decode_token_budget(gsa, gist_set, want_k):
+    """Fixed-token-budget mode: one budget of 744 tokens over 512 gists, C = 16,
+    T = 64 unfolds 10 chunks when every gist stays in the set, 40 with only
+    the chosen gists and 42 with none (slide 17's argument for dropping the
+    unselected gists); each k then runs through gsa_decode and matches the
+    oracle."""
+    budget = 744
+    cfg = cfg_of("gqa_32k", n_raw=8192, plant="none")
+    k = gsa.topk_for_budget(budget, cfg.M, cfg.chunk, cfg.tail, gist_set)
+    assert k == want_k
+    cfg = dataclasses.replace(cfg, topk=k)
+    say(f"decode budget {budget} gist_set={gist_set} -> k={k}")
+    inp = gi.make_decode(cfg, 5300, device="cuda")
+    run_decode(gsa, inp, cfg, units=sample_units(cfg, n=16, seed=6), gist_set=gist_set)
