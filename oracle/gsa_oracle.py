@@ -31,7 +31,12 @@ in float64 on the exact input values (bf16 inputs are widened exactly):
     explainer, 'Hierarchical Extension (H-GSA)', 'Coarse-to-Fine Selection');
   * prefill -- the same rule applied per query position under causality, i.e.
     the forward pass of the top-k attention mask of selective finetuning
-    (gist.science explainer, 'Training Procedure: Selective Finetuning').
+    (gist.science explainer, 'Training Procedure: Selective Finetuning');
+  * gist tokens -- the gist token of chunk m attends to its own chunk's raw
+    tokens and to the gist tokens before it (the gist causal mask: explainer
+    section 2 'Interleaved Gist Tokens'; slide deck, slide 7), and the cache
+    grows by one row per token, the gist row following its chunk
+    (``cache_row``).
 
 Readings where the pages are silent (each also listed in the design notes):
   R1 score = scale * (q . k_gist), scale = 1/sqrt(D) unless given;
@@ -46,6 +51,9 @@ Readings where the pages are silent (each also listed in the design notes):
      (0..C of them) must lie inside the tail;
   R6 prefill eligibility: query t may use gist m only if m < floor(t / C);
      the window is raw positions [t - W + 1, t];
+  R8 gist causal mask: the listed rows are the chunk's C raw tokens and the
+     earlier gists; the gist token's own key is not among them (slide 7
+     lists g1 -> x1, x2 and g2 -> g1, x3, x4);
   R7 two-level: level-2 gists live in their own array; group i covers chunks
      [i G, (i + 1) G); the level-1 gists that no full group covers are always
      candidates; the attention set holds every level-2 gist, every candidate
@@ -63,7 +71,7 @@ import numpy as np
 __all__ = [
     "gist_row_index", "raw_row_index", "topk_ascending",
     "decode_unit", "decode", "decode_hier_unit", "decode_hier", "topk_for_budget", "GIST_SETS",
-    "prefill_query", "prefill",
+    "prefill_query", "prefill", "cache_row", "gist_query", "gist_prefill",
 ]
 
 
@@ -403,3 +411,63 @@ def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, *, chunk: i
         out[j * g:(j + 1) * g, i] = r["out"]
         sel[j, i] = r["sel"]
     return out, sel
+
+
+# ------------------------------------------------ gist tokens, cache rows ---
+
+def cache_row(position: int, chunk: int, is_gist: bool) -> int:
+    """Row written when the cache grows by one token (explainer section 2
+    'Interleaved Gist Tokens': a gist token follows every chunk): raw token
+    ``position`` goes to its chunk's slot, the gist of chunk ``position`` to
+    the slot after the chunk's C raw tokens."""
+    if position < 0 or chunk <= 0:
+        raise ValueError("need position >= 0 and chunk >= 1")
+    if is_gist:
+        return gist_row_index(position, chunk)
+    m, j = divmod(position, chunk)
+    return m * (chunk + 1) + j
+
+
+def gist_query(qg: np.ndarray, K: np.ndarray, V: np.ndarray, *, m: int, n_raw: int,
+               n_gist: int, chunk: int, scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Attention of chunk m's gist token under the gist causal mask (R8): its
+    own chunk's C raw tokens and the gists of chunks 0..m-1.
+
+    qg: [g, D] the gist token's query heads of one kv-group.  K, V: [R, D].
+    Needs chunk m complete ((m + 1) C <= n_raw) and the gists before it in
+    the cache (m <= n_gist).  Returns out [g, D], lse [g], wsum [g], rows.
+    """
+    qg = _f64(qg)
+    g, D = qg.shape
+    C, M, N = chunk, n_gist, n_raw
+    _check_common(N, M, C, K.shape[0])
+    if not (0 <= m and (m + 1) * C <= N and m <= M):
+        raise ValueError("chunk m must be complete and the gists before it present")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rows = [raw_row_index(m * C + j, C, M) for j in range(C)]
+    rows += [gist_row_index(mm, C) for mm in range(m)]
+    rows = np.array(sorted(rows), dtype=np.int64)
+    out, lse, wsum = _softmax_attend(qg, _f64(K[rows]), _f64(V[rows]), scale)
+    return {"out": out, "lse": lse, "wsum": wsum, "rows": rows}
+
+
+def gist_prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, *, chunk: int,
+                 m_start: int, n_gist: Optional[int] = None, scale: Optional[float] = None,
+                 queries: Optional[Iterable[Tuple[int, int]]] = None):
+    """Gist tokens of chunks [m_start, m_start + n) for one sequence.
+    q [Hq, n, D]; caches [Hkv, R, D]. Returns out [Hq, n, D] (entries not in
+    ``queries`` -- (i, kv-head) pairs -- are NaN)."""
+    Hq, n, D = q.shape
+    Hkv, R = k_cache.shape[0], k_cache.shape[1]
+    g = Hq // Hkv
+    if n_gist is None:
+        n_gist = R // (chunk + 1)
+    n_raw = R - n_gist
+    out = np.full((Hq, n, D), np.nan)
+    todo = [(i, j) for i in range(n) for j in range(Hkv)] if queries is None else queries
+    for i, j in todo:
+        r = gist_query(q[j * g:(j + 1) * g, i], k_cache[j], v_cache[j], m=m_start + i, n_raw=n_raw,
+                       n_gist=n_gist, chunk=chunk, scale=scale)
+        out[j * g:(j + 1) * g, i] = r["out"]
+    return out
+

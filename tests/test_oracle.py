@@ -530,3 +530,66 @@ def test_topk_for_budget_is_the_largest_fitting_k(gist_set):
                                        gist_set=gist_set)["rows"]
             assert len(rows1) > budget
     assert oracle.topk_for_budget(10 ** 6, M, C, T, gist_set) == M
+
+
+# ------------------------------------------------ gist tokens, cache rows ---
+
+def test_cache_rows_are_appended_in_time_order():
+    """Tokens in time order (x_0 .. x_{C-1}, g_0, x_C, ...) land on rows
+    0, 1, 2, ... with no gap: the interleaved cache only ever grows at its end;
+    the rows agree with the layout's own row kinds."""
+    for C in (1, 3, 16):
+        row = 0
+        for p in range(5 * C + 2):
+            assert oracle.cache_row(p, C, False) == row
+            assert row_kind(row, C, 10 ** 6) == ("raw", p)
+            row += 1
+            if p % C == C - 1:
+                m = p // C
+                assert oracle.cache_row(m, C, True) == row
+                assert row_kind(row, C, 10 ** 6) == ("gist", m)
+                row += 1
+
+
+@pytest.mark.parametrize("C,M,r,m", [(4, 12, 0, 0), (4, 12, 0, 7), (8, 5, 3, 4), (16, 6, 16, 6), (3, 9, 2, 9)])
+def test_gist_query_is_masked_sdpa(C, M, r, m):
+    """Gist causal mask: the chunk's raw rows and the earlier gists only
+    (mask built from row kinds), against float64 SDPA."""
+    rng = np.random.default_rng(C * 31 + M + m)
+    g, D = 2, 16
+    N = M * C + r
+    R = N + M
+    if (m + 1) * C > N:
+        pytest.skip("chunk m incomplete")
+    qg, K, V = rng.standard_normal((g, D)), rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    res = oracle.gist_query(qg, K, V, m=m, n_raw=N, n_gist=M, chunk=C)
+    mask = np.array([(lambda k, v: (k == "gist" and v < m) or (k == "raw" and v // C == m))(*row_kind(i, C, M))
+                     for i in range(R)])
+    assert len(res["rows"]) == mask.sum() == C + m
+    np.testing.assert_allclose(res["out"], sdpa(qg, K, V, mask, 1 / math.sqrt(D)), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("m", [0, 1, 5, 11])
+def test_gist_query_is_prefill_at_the_chunks_last_token(m):
+    """Reduction: the gist token of chunk m sees what a prefill query at the
+    chunk's last raw position sees with k = 0 and a window of C."""
+    rng = np.random.default_rng(m)
+    g, D, C, M = 4, 8, 4, 12
+    N = M * C
+    R = N + M
+    qg, K, V = rng.standard_normal((g, D)), rng.standard_normal((R, D)), rng.standard_normal((R, D))
+    a = oracle.gist_query(qg, K, V, m=m, n_raw=N, n_gist=M, chunk=C)
+    b = oracle.prefill_query(qg, K, V, t=m * C + C - 1, n_raw=N, n_gist=M, chunk=C, topk=0, window=C)
+    np.testing.assert_array_equal(a["rows"], b["rows"])
+    np.testing.assert_allclose(a["out"], b["out"], rtol=0, atol=1e-13)
+
+
+def test_gist_query_needs_a_complete_chunk_and_its_predecessors():
+    rng = np.random.default_rng(0)
+    C, M = 4, 3
+    N = M * C + 2
+    R = N + M
+    qg, K, V = rng.standard_normal((1, 8)), rng.standard_normal((R, 8)), rng.standard_normal((R, 8))
+    with pytest.raises(ValueError):
+        oracle.gist_query(qg, K, V, m=3, n_raw=N, n_gist=M, chunk=C)   # chunk 3 has 2 of 4 tokens
+    oracle.gist_query(qg, K, V, m=2, n_raw=N, n_gist=M, chunk=C)
