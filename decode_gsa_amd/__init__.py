@@ -9,6 +9,12 @@ Entry points (same names as the C ABI):
   gsa_decode(q, k_cache, v_cache, chunk=, topk=, tail=, ...)
   gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, chunk=, fanout=, topk1=, topk2=, tail=, ...)
   gsa_prefill_blocksparse(q, k_cache, v_cache, chunk=, topk=, window=, q_start=, ...)
+  gsa_gist_prefill(q, k_cache, v_cache, chunk=, m_start=, ...)
+  gsa_cache_append(k_cache, v_cache, chunk=, n_raw=, n_gist=, k_raw=, v_raw=, k_gist=, v_gist=)
+
+Caches sized for more rows than they hold (to grow in place with
+gsa_cache_append) take n_raw= and n_gist= explicitly; their row count is then
+the capacity (row_capacity in the C structs).
 """
 from __future__ import annotations
 
@@ -17,12 +23,12 @@ import os
 from typing import Optional
 
 __all__ = [
-    "GsaError", "lib", "LIB_PATH", "DecodeParams", "HierParams", "PrefillParams",
-    "GSA_F32", "GSA_BF16", "EXPORTED_SYMBOLS",
-    "decode_params", "hier_params", "prefill_params",
+    "GsaError", "lib", "LIB_PATH", "DecodeParams", "HierParams", "PrefillParams", "GistParams",
+    "AppendParams", "GSA_F32", "GSA_BF16", "EXPORTED_SYMBOLS",
+    "decode_params", "hier_params", "prefill_params", "gist_params", "append_params",
     "decode_workspace_size", "hier_workspace_size", "prefill_workspace_size", "new_workspace",
     "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse", "gsa_profile_events",
-    "gsa_profile_marks", "topk_for_budget", "GIST_SETS",
+    "gsa_profile_marks", "topk_for_budget", "GIST_SETS", "gsa_gist_prefill", "gsa_cache_append",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -34,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "gsa_decode_hier_workspace_size", "gsa_decode_hier",
     "gsa_prefill_workspace_size", "gsa_prefill_blocksparse",
     "gsa_profile_events", "gsa_profile_marks", "gsa_status_string", "gsa_last_error",
-    "gsa_topk_for_budget",
+    "gsa_topk_for_budget", "gsa_gist_prefill", "gsa_cache_append",
 )
 
 _c_i32, _c_i64, _c_f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -45,7 +51,7 @@ class DecodeParams(ctypes.Structure):
     _fields_ = [("batch", _c_i32), ("n_q_heads", _c_i32), ("n_kv_heads", _c_i32),
                 ("head_dim", _c_i32), ("n_raw", _c_i64), ("n_gist", _c_i64),
                 ("chunk", _c_i32), ("topk", _c_i32), ("tail", _c_i32), ("scale", _c_f32),
-                ("dtype", _c_i32), ("gist_set", _c_i32)]
+                ("dtype", _c_i32), ("gist_set", _c_i32), ("row_capacity", _c_i64)]
 
 
 class HierParams(ctypes.Structure):
@@ -56,7 +62,19 @@ class PrefillParams(ctypes.Structure):
     _fields_ = [("n_q_heads", _c_i32), ("n_kv_heads", _c_i32), ("head_dim", _c_i32),
                 ("chunk", _c_i32), ("topk", _c_i32), ("window", _c_i32), ("n_raw", _c_i64),
                 ("n_gist", _c_i64), ("q_start", _c_i64), ("n_q", _c_i64), ("scale", _c_f32),
-                ("dtype", _c_i32)]
+                ("dtype", _c_i32), ("row_capacity", _c_i64)]
+
+
+class GistParams(ctypes.Structure):
+    _fields_ = [("n_q_heads", _c_i32), ("n_kv_heads", _c_i32), ("head_dim", _c_i32),
+                ("chunk", _c_i32), ("n_raw", _c_i64), ("n_gist", _c_i64), ("m_start", _c_i64),
+                ("n_q", _c_i64), ("scale", _c_f32), ("dtype", _c_i32), ("row_capacity", _c_i64)]
+
+
+class AppendParams(ctypes.Structure):
+    _fields_ = [("batch", _c_i32), ("n_kv_heads", _c_i32), ("head_dim", _c_i32),
+                ("chunk", _c_i32), ("n_raw", _c_i64), ("n_gist", _c_i64), ("raw_new", _c_i64),
+                ("gist_new", _c_i64), ("row_capacity", _c_i64), ("dtype", _c_i32)]
 
 
 class GsaError(RuntimeError):
@@ -85,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.gsa_prefill_workspace_size.argtypes = [P(PrefillParams), P(_sz)]
         L.gsa_prefill_blocksparse.argtypes = [P(PrefillParams), _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                               _vp]
+        L.gsa_gist_prefill.argtypes = [P(GistParams), _vp, _vp, _vp, _vp, _vp]
+        L.gsa_cache_append.argtypes = [P(AppendParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.gsa_profile_events.argtypes = [P(_vp), _c_i32]
         L.gsa_profile_marks.argtypes = [P(_c_i32)]
         for f in ("gsa_decode_workspace_size", "gsa_decode", "gsa_decode_hier_workspace_size",
@@ -133,9 +153,9 @@ def _dtype_code(t) -> int:
 
 
 def decode_params(batch, n_q_heads, n_kv_heads, head_dim, n_raw, n_gist, chunk, topk, tail,
-                  scale=0.0, dtype=GSA_BF16, gist_set=0) -> DecodeParams:
+                  scale=0.0, dtype=GSA_BF16, gist_set=0, row_capacity=0) -> DecodeParams:
     return DecodeParams(batch, n_q_heads, n_kv_heads, head_dim, n_raw, n_gist, chunk, topk,
-                        tail, scale, dtype, gist_set)
+                        tail, scale, dtype, gist_set, row_capacity)
 
 
 def hier_params(base: DecodeParams, fanout: int, topk2: int) -> HierParams:
@@ -143,9 +163,21 @@ def hier_params(base: DecodeParams, fanout: int, topk2: int) -> HierParams:
 
 
 def prefill_params(n_q_heads, n_kv_heads, head_dim, chunk, topk, window, n_raw, n_gist, q_start,
-                   n_q, scale=0.0, dtype=GSA_BF16) -> PrefillParams:
+                   n_q, scale=0.0, dtype=GSA_BF16, row_capacity=0) -> PrefillParams:
     return PrefillParams(n_q_heads, n_kv_heads, head_dim, chunk, topk, window, n_raw, n_gist,
-                         q_start, n_q, scale, dtype)
+                         q_start, n_q, scale, dtype, row_capacity)
+
+
+def gist_params(n_q_heads, n_kv_heads, head_dim, chunk, n_raw, n_gist, m_start, n_q, scale=0.0,
+                dtype=GSA_BF16, row_capacity=0) -> GistParams:
+    return GistParams(n_q_heads, n_kv_heads, head_dim, chunk, n_raw, n_gist, m_start, n_q, scale,
+                      dtype, row_capacity)
+
+
+def append_params(batch, n_kv_heads, head_dim, chunk, n_raw, n_gist, raw_new, gist_new,
+                  row_capacity, dtype=GSA_BF16) -> AppendParams:
+    return AppendParams(batch, n_kv_heads, head_dim, chunk, n_raw, n_gist, raw_new, gist_new,
+                        row_capacity, dtype)
 
 
 def decode_workspace_size(p: DecodeParams) -> int:
@@ -206,6 +238,17 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
+def _geometry(rows: int, chunk: int, n_gist: Optional[int], n_raw: Optional[int]):
+    """(N, M, row_capacity) of a cache whose row dimension is `rows`: all rows
+    in use unless n_raw is given, in which case `rows` is the capacity."""
+    if n_raw is None:
+        M = rows // (chunk + 1) if n_gist is None else n_gist
+        return rows - M, M, 0
+    if n_gist is None:
+        raise ValueError("n_raw= needs n_gist= as well")
+    return n_raw, n_gist, rows
+
+
 GIST_SETS = {"all": 0, "selected": 1, "none": 2}
 
 
@@ -221,7 +264,7 @@ def topk_for_budget(budget: int, n_gist: int, chunk: int, tail: int, gist_set: s
 def gsa_decode(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int,
                n_gist: Optional[int] = None, scale: float = 0.0, out=None, lse=None,
                sel_idx=None, workspace=None, stream=None, want_lse: bool = True,
-               want_sel: bool = True, gist_set: str = "all"):
+               want_sel: bool = True, gist_set: str = "all", n_raw: Optional[int] = None):
     """Single-level GSA decode. q [B,Hq,D]; caches [B,Hkv,R,D] (bf16 or fp32).
     gist_set: "all" (every gist), "selected" (the chosen chunks' gists) or
     "none" -- which gist rows the attention set holds.
@@ -231,11 +274,11 @@ def gsa_decode(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int,
     import torch
     B, Hq, D = q.shape
     Hkv, R = k_cache.shape[1], k_cache.shape[2]
-    M = R // (chunk + 1) if n_gist is None else n_gist
+    N, M, cap = _geometry(R, chunk, n_gist, n_raw)
     if gist_set not in GIST_SETS:
         raise ValueError(f"gist_set must be one of {tuple(GIST_SETS)}")
-    p = decode_params(B, Hq, Hkv, D, R - M, M, chunk, topk, tail, scale, _dtype_code(q),
-                      GIST_SETS[gist_set])
+    p = decode_params(B, Hq, Hkv, D, N, M, chunk, topk, tail, scale, _dtype_code(q),
+                      GIST_SETS[gist_set], cap)
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q, k_cache, v_cache must share one dtype")
     if tuple(k_cache.shape) != (B, Hkv, R, D) or tuple(v_cache.shape) != (B, Hkv, R, D):
@@ -257,7 +300,7 @@ def gsa_decode(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int,
 def gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int, topk1: int,
                     topk2: int, tail: int, n_gist: Optional[int] = None, scale: float = 0.0,
                     out=None, lse=None, sel2=None, sel1=None, workspace=None, stream=None,
-                    want_lse: bool = True, want_sel: bool = True):
+                    want_lse: bool = True, want_sel: bool = True, n_raw: Optional[int] = None):
     """Two-level (gist-of-gist) decode. k_l2, v_l2 [B,Hkv,M2,D].
 
     Returns (out, lse, sel2 [B,Hkv,k2], sel1 [B,Hkv,k1]).
@@ -265,8 +308,9 @@ def gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int,
     import torch
     B, Hq, D = q.shape
     Hkv, R = k_cache.shape[1], k_cache.shape[2]
-    M = R // (chunk + 1) if n_gist is None else n_gist
-    base = decode_params(B, Hq, Hkv, D, R - M, M, chunk, topk1, tail, scale, _dtype_code(q))
+    N, M, cap = _geometry(R, chunk, n_gist, n_raw)
+    base = decode_params(B, Hq, Hkv, D, N, M, chunk, topk1, tail, scale, _dtype_code(q),
+                         row_capacity=cap)
     p = hier_params(base, fanout, topk2)
     dev = q.device
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
@@ -290,7 +334,7 @@ def gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int,
 def gsa_prefill_blocksparse(q, k_cache, v_cache, *, chunk: int, topk: int, window: int,
                             q_start: int, n_gist: Optional[int] = None, scale: float = 0.0,
                             out=None, sel=None, workspace=None, stream=None,
-                            want_sel: bool = True):
+                            want_sel: bool = True, n_raw: Optional[int] = None):
     """Causal block-sparse prefill. q [Hq,n_q,D]; caches [Hkv,R,D] (bf16).
 
     Returns (out [Hq,n_q,D] fp32, sel [Hkv,n_q,k] int32 or None).
@@ -298,9 +342,9 @@ def gsa_prefill_blocksparse(q, k_cache, v_cache, *, chunk: int, topk: int, windo
     import torch
     Hq, n_q, D = q.shape
     Hkv, R = k_cache.shape[0], k_cache.shape[1]
-    M = R // (chunk + 1) if n_gist is None else n_gist
-    p = prefill_params(Hq, Hkv, D, chunk, topk, window, R - M, M, q_start, n_q, scale,
-                       _dtype_code(q))
+    N, M, cap = _geometry(R, chunk, n_gist, n_raw)
+    p = prefill_params(Hq, Hkv, D, chunk, topk, window, N, M, q_start, n_q, scale,
+                       _dtype_code(q), cap)
     dev = q.device
     out = torch.empty(Hq, n_q, D, dtype=torch.float32, device=dev) if out is None else out
     if sel is None and want_sel:
@@ -312,3 +356,58 @@ def gsa_prefill_blocksparse(q, k_cache, v_cache, *, chunk: int, topk: int, windo
                                          _nbytes(ws), _stream(stream, dev)),
            "gsa_prefill_blocksparse")
     return out, sel
+
+
+def gsa_gist_prefill(q, k_cache, v_cache, *, chunk: int, m_start: int,
+                     n_gist: Optional[int] = None, n_raw: Optional[int] = None, scale: float = 0.0,
+                     out=None, stream=None):
+    """Gist tokens of chunks [m_start, m_start + n_q) of one sequence under the
+    gist causal mask. q [Hq,n_q,D]; caches [Hkv,R,D] (bf16).
+
+    Returns out [Hq,n_q,D] fp32.
+    """
+    import torch
+    Hq, n_q, D = q.shape
+    Hkv, R = k_cache.shape[0], k_cache.shape[1]
+    N, M, cap = _geometry(R, chunk, n_gist, n_raw)
+    p = gist_params(Hq, Hkv, D, chunk, N, M, m_start, n_q, scale, _dtype_code(q), cap)
+    dev = q.device
+    out = torch.empty(Hq, n_q, D, dtype=torch.float32, device=dev) if out is None else out
+    _check(lib().gsa_gist_prefill(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                  _stream(stream, dev)), "gsa_gist_prefill")
+    return out
+
+
+def gsa_cache_append(k_cache, v_cache, *, chunk: int, n_raw: int, n_gist: int, k_raw=None,
+                     v_raw=None, k_gist=None, v_gist=None, stream=None) -> None:
+    """Write new raw rows (positions n_raw, n_raw + 1, ...) and new gist rows
+    (chunks n_gist, n_gist + 1, ...) into their interleaved slots.
+
+    Caches [B,Hkv,cap,D] or [Hkv,cap,D] (one sequence); k_raw, v_raw
+    [..., n_new, D] and k_gist, v_gist [..., g_new, D] with the caches' leading
+    dimensions and dtype (None: nothing of that kind).
+    """
+    lead = tuple(k_cache.shape[:-2])
+    cap, D = k_cache.shape[-2], k_cache.shape[-1]
+    if len(lead) not in (1, 2) or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("caches must be [B,Hkv,cap,D] or [Hkv,cap,D], K and V alike")
+    B, Hkv = (1, lead[0]) if len(lead) == 1 else lead
+
+    def rows(a, b, what):
+        if (a is None) != (b is None):
+            raise ValueError(f"give both k_{what} and v_{what} or neither")
+        if a is None:
+            return 0
+        if tuple(a.shape[:-2]) != lead or a.shape[-1] != D or tuple(b.shape) != tuple(a.shape):
+            raise ValueError(f"k_{what} / v_{what} shape mismatch with the caches")
+        if a.dtype != k_cache.dtype or b.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+            raise TypeError("all rows and caches must share one dtype")
+        return a.shape[-2]
+
+    n_new, g_new = rows(k_raw, v_raw, "raw"), rows(k_gist, v_gist, "gist")
+    p = append_params(B, Hkv, D, chunk, n_raw, n_gist, n_new, g_new, cap, _dtype_code(k_cache))
+    _check(lib().gsa_cache_append(ctypes.byref(p), _ptr(k_raw) if n_new else None,
+                                  _ptr(v_raw) if n_new else None, _ptr(k_gist) if g_new else None,
+                                  _ptr(v_gist) if g_new else None, _ptr(k_cache), _ptr(v_cache),
+                                  _stream(stream, k_cache.device)), "gsa_cache_append")
+

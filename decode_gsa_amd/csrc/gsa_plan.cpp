@@ -112,6 +112,17 @@ static gsa_status_t check_heads(int32_t hq, int32_t hkv, int32_t d, int32_t dtyp
   return GSA_OK;
 }
 
+// Stride in rows between the [rows, D] cache blocks of consecutive
+// (sequence, kv-head) pairs: the rows in use, or the caller's capacity.
+static gsa_status_t resolve_rows(int64_t rows, int64_t capacity, int64_t* R) {
+  if (capacity < 0 || (capacity > 0 && capacity < rows))
+    return fail(GSA_ERR_INVALID_ARG, "row_capacity=%lld below the %lld rows of the cache", (long long)capacity,
+                (long long)rows);
+  if (capacity > ((int64_t)1 << 41)) return fail(GSA_ERR_UNSUPPORTED, "row_capacity too large");
+  *R = capacity > 0 ? capacity : rows;
+  return GSA_OK;
+}
+
 static float resolve_scale(float s, int32_t d) {
   return (s > 0.f && isfinite(s)) ? s : 1.0f / sqrtf((float)d);
 }
@@ -141,7 +152,7 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   d.D = p->head_dim;
   d.M = p->n_gist;
   d.N = p->n_raw;
-  d.R = cache_rows(p->n_raw, p->n_gist);
+  if ((s = resolve_rows(cache_rows(p->n_raw, p->n_gist), p->row_capacity, &d.R)) != GSA_OK) return s;
   d.C = p->chunk;
   d.k = p->topk;
   d.T = p->tail;
@@ -290,14 +301,99 @@ gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* o) {
   d.W = p->window;
   d.N = p->n_raw;
   d.M = p->n_gist;
-  d.R = cache_rows(d.N, d.M);
+  if ((s = resolve_rows(cache_rows(d.N, d.M), p->row_capacity, &d.R)) != GSA_OK) return s;
   d.q_start = p->q_start;
+  d.q_stride = 1;
   d.n_q = p->n_q;
   d.scale = resolve_scale(p->scale, p->head_dim);
   d.n_blocks = (int32_t)ceil_div(d.n_q, kQBlock);
   if ((int64_t)d.n_blocks * d.Hkv > (1 << 30)) return fail(GSA_ERR_UNSUPPORTED, "prefill: too many blocks");
   // workspace: the selection [Hkv][n_q][k] handed from the select to the attend kernel
   d.total = align_up(sizeof(int32_t) * (size_t)d.Hkv * (size_t)d.n_q * (size_t)d.k);
+  *o = d;
+  return GSA_OK;
+}
+
+gsa_status_t plan_gist(const gsa_gist_params* p, PrefillPlan* o) {
+  if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->chunk < 1) return fail(GSA_ERR_INVALID_ARG, "chunk=%d must be >= 1", p->chunk);
+  if (p->m_start < 0 || p->n_q < 0 || p->m_start > p->n_raw || p->n_q > p->n_raw)
+    return fail(GSA_ERR_INVALID_ARG, "gist queries [%lld, +%lld) outside the sequence", (long long)p->m_start,
+                (long long)p->n_q);
+  const int64_t m_end = p->m_start + p->n_q;
+  if (p->n_q > 0 && m_end * p->chunk > p->n_raw)
+    return fail(GSA_ERR_INVALID_ARG, "chunk %lld is not complete (n_raw=%lld, chunk=%d)", (long long)(m_end - 1),
+                (long long)p->n_raw, p->chunk);
+  if (p->n_q > 0 && m_end - 1 > p->n_gist)
+    return fail(GSA_ERR_INVALID_ARG, "the gist of chunk %lld needs gists 0..%lld, the cache holds %lld",
+                (long long)(m_end - 1), (long long)(m_end - 2), (long long)p->n_gist);
+  // The attention of a raw query at the chunk's last position, k = 0, W = C,
+  // one query every C positions.
+  gsa_prefill_params pp{};
+  pp.n_q_heads = p->n_q_heads;
+  pp.n_kv_heads = p->n_kv_heads;
+  pp.head_dim = p->head_dim;
+  pp.chunk = p->chunk;
+  pp.topk = 0;
+  pp.window = p->chunk;
+  pp.n_raw = p->n_raw;
+  pp.n_gist = p->n_gist;
+  pp.q_start = p->n_q > 0 ? p->m_start * p->chunk + p->chunk - 1 : 0;
+  pp.n_q = p->n_q > 0 ? 1 : 0;
+  pp.scale = p->scale;
+  pp.dtype = p->dtype;
+  pp.row_capacity = p->row_capacity;
+  gsa_status_t s = plan_prefill(&pp, o);
+  if (s != GSA_OK) return s;
+  // positions of the last block's padding queries stay in 32 bits
+  if (p->n_raw + (int64_t)kQBlock * p->chunk >= ((int64_t)1 << 31))
+    return fail(GSA_ERR_UNSUPPORTED, "gist prefill: sequence too long for 32-bit positions");
+  o->n_q = p->n_q;
+  o->q_stride = p->chunk;
+  o->n_blocks = (int32_t)ceil_div(p->n_q, kQBlock);
+  if ((int64_t)o->n_blocks * o->Hkv > (1 << 30)) return fail(GSA_ERR_UNSUPPORTED, "gist prefill: too many blocks");
+  o->total = 0;
+  return GSA_OK;
+}
+
+gsa_status_t plan_append(const gsa_append_params* p, AppendPlan* o) {
+  if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 1 || p->n_kv_heads < 1)
+    return fail(GSA_ERR_INVALID_ARG, "batch=%d and n_kv_heads=%d must be >= 1", p->batch, p->n_kv_heads);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(GSA_ERR_UNSUPPORTED, "head_dim=%d not in {64,128}", p->head_dim);
+  if (p->dtype != GSA_F32 && p->dtype != GSA_BF16) return fail(GSA_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+  if (p->chunk < 1 || p->chunk > 4096) return fail(GSA_ERR_INVALID_ARG, "chunk=%d outside [1, 4096]", p->chunk);
+  if (p->n_raw < 0 || p->n_gist < 0 || p->raw_new < 0 || p->gist_new < 0 || p->n_raw > ((int64_t)1 << 40) ||
+      p->raw_new > ((int64_t)1 << 40) || p->n_gist > p->n_raw || p->gist_new > p->raw_new + p->n_raw)
+    return fail(GSA_ERR_INVALID_ARG, "token counts must be >= 0 and within range");
+  const int64_t C = p->chunk;
+  // a gist exists only for a complete chunk; raw rows may run ahead of the
+  // gists (their slots are fixed), the readers need the gists caught up
+  if (p->n_gist * C > p->n_raw)
+    return fail(GSA_ERR_INVALID_ARG, "cache state n_gist=%lld has gists of incomplete chunks (n_raw=%lld)",
+                (long long)p->n_gist, (long long)p->n_raw);
+  const int64_t N1 = p->n_raw + p->raw_new, M1 = p->n_gist + p->gist_new;
+  if (M1 * C > N1)
+    return fail(GSA_ERR_INVALID_ARG, "the append adds gists of incomplete chunks (n_raw=%lld, n_gist=%lld after it)",
+                (long long)N1, (long long)M1);
+  // one past the highest slot written: the last raw row, or the last gist row
+  const int64_t raw_end = N1 > 0 ? (N1 - 1) / C * (C + 1) + (N1 - 1) % C + 1 : 0;
+  const int64_t need = raw_end > M1 * (C + 1) ? raw_end : M1 * (C + 1);
+  if (p->row_capacity < need)
+    return fail(GSA_ERR_INVALID_ARG, "row_capacity=%lld below the %lld rows the append reaches",
+                (long long)p->row_capacity, (long long)need);
+  const int64_t units = (int64_t)p->batch * p->n_kv_heads;
+  if (units > (1 << 24)) return fail(GSA_ERR_UNSUPPORTED, "too many (batch, kv-head) units");
+  AppendPlan d{};
+  d.units = units;
+  d.C = p->chunk;
+  d.N = p->n_raw;
+  d.M = p->n_gist;
+  d.raw_new = p->raw_new;
+  d.gist_new = p->gist_new;
+  d.R = p->row_capacity;
+  d.row_bytes = (int32_t)(p->head_dim * (p->dtype == GSA_BF16 ? 2 : 4));
   *o = d;
   return GSA_OK;
 }

@@ -66,7 +66,7 @@ struct DecodePlan {
   int32_t units;        // B * Hkv
   int32_t g;            // query heads per kv-head
   int32_t D;
-  int64_t M, R, N;
+  int64_t M, R, N;      // R: rows between (sequence, kv-head) blocks (>= N + M)
   int32_t C, k, T;
   float scale;          // resolved (> 0)
   int32_t dtype;
@@ -120,7 +120,8 @@ gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* out);
 // Prefill plan.
 struct PrefillPlan {
   int32_t Hq, Hkv, g, D, C, k, W;
-  int64_t N, M, R, q_start, n_q;
+  int64_t N, M, R, q_start, n_q;   // R: rows between kv-head blocks (>= N + M)
+  int32_t q_stride;     // positions between consecutive queries (1; C for gist tokens)
   float scale;
   int32_t n_blocks;     // query blocks of kQBlock queries
   size_t total;
@@ -134,6 +135,16 @@ constexpr int32_t kPrefillMaxGist = 65536;
 constexpr int32_t kPrefillMaxK = 32;
 
 gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* out);
+// Gist-token queries as prefill queries at positions mC + C - 1 (stride C),
+// k = 0, W = C.
+gsa_status_t plan_gist(const gsa_gist_params* p, PrefillPlan* out);
+
+struct AppendPlan {
+  int64_t units;        // B * Hkv
+  int32_t C, row_bytes;
+  int64_t N, M, raw_new, gist_new, R;
+};
+gsa_status_t plan_append(const gsa_append_params* p, AppendPlan* out);
 
 // Pointer checks shared by the entry points.
 gsa_status_t check_ptr(const void* p, const char* name, bool allow_null = false);

@@ -36,6 +36,12 @@
 //                   two waves share a query tile (two heads each), so each SIMD
 //                   runs two waves.
 //
+// Gist tokens (gsa_gist_prefill): the gist of chunk m sees the chunk's C raw
+// tokens and the gists before it (the gist causal mask, section 2 and slide
+// 7), which is the attention of a raw query at position mC + C - 1 with k = 0
+// and W = C. The attention kernel runs them as such, its queries C positions
+// apart (AttArgs::q_stride).
+//
 // K/V tiles reach LDS by direct-to-LDS loads (global_load_lds_dwordx4) into a
 // ring of tiles, several tiles in flight. Such a load writes lane i's 16 bytes
 // at LDS base + 16 i, so the layout is made conflict-free by choosing which
@@ -680,6 +686,7 @@ struct AttArgs {
   const int32_t* sel;     // [Hkv][n_q][k]
   int64_t R;
   int32_t M, C, k, W, Hkv, n_blocks, q_start, n_q;
+  int32_t q_stride;       // query i sits at position q_start + i * q_stride
   float scale_log2;
 };
 
@@ -913,10 +920,10 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
   const int qloc = 16 * qt + qi;
   const int t_idx = blk * kQB + qloc;
   const bool valid = t_idx < a.n_q;
-  const int t = a.q_start + t_idx;
+  const int t = a.q_start + t_idx * a.q_stride;
   const int nq_blk = min(kQB, a.n_q - blk * kQB);
-  const int t_first = a.q_start + blk * kQB;
-  const int t_last = t_first + nq_blk - 1;
+  const int t_first = a.q_start + blk * kQB * a.q_stride;
+  const int t_last = t_first + (nq_blk - 1) * a.q_stride;
   const int E = min(a.M, t_last / a.C);
   const int E0 = min(a.M, t_first / a.C);   // gists every query of the block may use
 
@@ -1036,11 +1043,13 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
   AttArgs t{};
   t.q = q; t.K = K; t.V = V; t.out = out; t.sel = wsel; t.R = pl.R;
   t.M = (int32_t)pl.M; t.C = pl.C; t.k = pl.k; t.W = pl.W; t.Hkv = pl.Hkv; t.n_blocks = pl.n_blocks;
-  t.q_start = (int32_t)pl.q_start; t.n_q = (int32_t)pl.n_q;
+  t.q_start = (int32_t)pl.q_start; t.n_q = (int32_t)pl.n_q; t.q_stride = pl.q_stride;
   t.scale_log2 = pl.scale * kLog2e;
   prof_launch((prefill_attend<G>), dim3(grid), dim3(AttShape<G>::NT), 0, stream, t);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(GSA_ERR_HIP, "gsa_prefill_blocksparse launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess)
+    return fail(GSA_ERR_HIP, "%s launch: %s", pl.q_stride == 1 ? "gsa_prefill_blocksparse" : "gsa_gist_prefill",
+                hipGetErrorString(e));
   return GSA_OK;
 }
 
@@ -1080,4 +1089,23 @@ extern "C" gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, con
     case 4: return run_prefill<4>(pl, q, k_cache, v_cache, out, sel, ws, st);
   }
   return fail(GSA_ERR_UNSUPPORTED, "prefill: %d query heads per kv-head not in {1, 2, 4}", pl.g);
+}
+
+extern "C" gsa_status_t gsa_gist_prefill(const gsa_gist_params* p, const void* q, const void* k_cache,
+                                         const void* v_cache, float* out, void* stream) {
+  clear_error();
+  PrefillPlan pl;
+  gsa_status_t s = plan_gist(p, &pl);
+  if (s != GSA_OK) return s;
+  if ((s = check_ptr(q, "q")) != GSA_OK || (s = check_ptr(k_cache, "k_cache")) != GSA_OK ||
+      (s = check_ptr(v_cache, "v_cache")) != GSA_OK || (s = check_ptr(out, "out")) != GSA_OK)
+    return s;
+  // k = 0: no selection launch, no workspace
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  switch (pl.g) {
+    case 1: return run_prefill<1>(pl, q, k_cache, v_cache, out, nullptr, nullptr, st);
+    case 2: return run_prefill<2>(pl, q, k_cache, v_cache, out, nullptr, nullptr, st);
+    case 4: return run_prefill<4>(pl, q, k_cache, v_cache, out, nullptr, nullptr, st);
+  }
+  return fail(GSA_ERR_UNSUPPORTED, "gist prefill: %d query heads per kv-head not in {1, 2, 4}", pl.g);
 }

@@ -28,7 +28,7 @@ import torch
 __all__ = [
     "DecodeConfig", "HierConfig", "PrefillConfig", "CONFIGS",
     "DecodeInputs", "HierInputs", "PrefillInputs",
-    "make_decode", "make_hier", "make_prefill",
+    "make_decode", "make_hier", "make_prefill", "make_gist", "TokenStream", "make_token_stream",
     "raw_row", "gist_row", "n_rows",
 ]
 
@@ -482,3 +482,43 @@ def make_prefill(cfg: PrefillConfig, seed: int, device="cpu", max_tries: int = 1
         if inp.planted is None or not check or inp.min_gap >= cfg.margin:
             return inp
     raise RuntimeError(f"{cfg.name}: no seed reached the planted gap")
+
+
+# --------------------------------------------------------------------------
+# gist-token queries and token streams (plain Gaussian values)
+# --------------------------------------------------------------------------
+
+def make_gist(n_q_heads: int, n_kv_heads: int, head_dim: int, n_raw: int, n_gist: int,
+              n_q: int, seed: int, device="cpu", dtype: str = "bf16"):
+    """Gist-token queries q [Hq, n_q, D] and a one-sequence interleaved cache
+    k, v [Hkv, N + M, D], all i.i.d. standard normal, rounded to `dtype`."""
+    g = _gen(device, seed)
+    R = n_raw + n_gist
+    q = torch.randn(n_q_heads, n_q, head_dim, generator=g, device=device)
+    k = torch.randn(n_kv_heads, R, head_dim, generator=g, device=device)
+    v = torch.randn(n_kv_heads, R, head_dim, generator=g, device=device)
+    return _store(q, dtype), _store(k, dtype), _store(v, dtype)
+
+
+@dataclasses.dataclass
+class TokenStream:
+    """K/V rows of a batch of sequences generated token by token."""
+    raw_k: torch.Tensor      # [steps, B, Hkv, D] row of raw token p at [p]
+    raw_v: torch.Tensor
+    gist_k: torch.Tensor     # [n_chunks, B, Hkv, D] row of the gist of chunk m at [m]
+    gist_v: torch.Tensor
+    gist_q: torch.Tensor     # [n_chunks, B, Hq, D] query of the gist token of chunk m
+    q: torch.Tensor          # [B, Hq, D] query of the token after the stream
+
+
+def make_token_stream(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, steps: int,
+                      chunk: int, seed: int, device="cpu", dtype: str = "bf16") -> TokenStream:
+    g = _gen(device, seed)
+    nc = steps // chunk
+
+    def r(*shape):
+        return _store(torch.randn(*shape, head_dim, generator=g, device=device), dtype)
+    return TokenStream(r(steps, batch, n_kv_heads), r(steps, batch, n_kv_heads),
+                       r(nc, batch, n_kv_heads), r(nc, batch, n_kv_heads),
+                       r(nc, batch, n_q_heads), r(batch, n_q_heads))
+

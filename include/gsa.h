@@ -88,6 +88,11 @@ typedef struct {
                           D = 128, k <= 64, >= 256 units, <= 4096 gists);
                           other shapes return GSA_ERR_UNSUPPORTED.
                           gsa_decode_hier requires 0. */
+  int64_t row_capacity; /* rows allocated per (sequence, kv-head) in the
+                          caches, the stride between their [R, D] blocks:
+                          0 means exactly R = N + M; else it must be
+                          >= N + M, so a cache sized once for its final
+                          length grows in place (gsa_cache_append) */
 } gsa_decode_params;
 
 enum { GSA_GISTS_ALL = 0, GSA_GISTS_SELECTED = 1, GSA_GISTS_NONE = 2 };
@@ -97,7 +102,9 @@ gsa_status_t gsa_decode_workspace_size(const gsa_decode_params* p, size_t* bytes
 
 /*
  * q        [B, Hq, D]        query of the new token, per head
- * k_cache  [B, Hkv, R, D]    interleaved key cache, R = N + M
+ * k_cache  [B, Hkv, R, D]    interleaved key cache, R = N + M (R =
+ *                            row_capacity when that is set; rows past N + M
+ *                            are never read)
  * v_cache  [B, Hkv, R, D]    interleaved value cache
  * out      [B, Hq, D] fp32   attention output (written)
  * lse      [B, Hq]    fp32   natural-log sum-exp of the attended logits, or NULL
@@ -171,6 +178,8 @@ typedef struct {
   int64_t n_q;         /* queries; q_start + n_q <= N */
   float scale;         /* <= 0: 1/sqrt(D) */
   int32_t dtype;       /* GSA_BF16 */
+  int64_t row_capacity; /* rows per kv-head in the caches (their stride);
+                           0: R = N + M, else >= N + M */
 } gsa_prefill_params;
 
 gsa_status_t gsa_prefill_workspace_size(const gsa_prefill_params* p, size_t* bytes);
@@ -178,6 +187,7 @@ gsa_status_t gsa_prefill_workspace_size(const gsa_prefill_params* p, size_t* byt
 /*
  * q       [Hq, n_q, D]        queries (row i is position q_start + i)
  * k_cache [Hkv, R, D]         interleaved cache of the sequence, R = N + M
+ *                             (R = row_capacity when that is set)
  * v_cache [Hkv, R, D]
  * out     [Hq, n_q, D] fp32   attention output (written)
  * sel     [Hkv, n_q, k] int32 chosen chunks per query, ascending, -1 padded,
@@ -187,6 +197,87 @@ gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, const void* q,
                                      const void* k_cache, const void* v_cache, float* out,
                                      int32_t* sel, void* workspace, size_t workspace_bytes,
                                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * Gist-token attention of one sequence (the step that builds the cache).
+ * Source: gist.science explainer, section 2 'Key Concepts: Interleaved Gist
+ * Tokens' and 'Technical Innovations' (the gist causal mask), slide deck
+ * slide 7: the gist token of chunk m attends to the C raw tokens of chunk m
+ * and to the gists of chunks 0..m-1 (not to its own key). This is what a
+ * raw query at position mC + C - 1 of gsa_prefill_blocksparse sees with
+ * topk = 0 and window = C, and it runs on the same attention kernel.
+ * One gist token at decode time (batch of sequences, chunk M just complete,
+ * gist M not yet appended) is gsa_decode with topk = 0 and tail = C.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t n_q_heads;   /* Hq, multiple of n_kv_heads; g in {1, 2, 4} */
+  int32_t n_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;    /* D: 128 */
+  int32_t chunk;       /* C >= 1 */
+  int64_t n_raw;       /* N raw tokens in the cache */
+  int64_t n_gist;      /* M gists in the cache; 0 <= N - M*C <= C */
+  int64_t m_start;     /* first query's chunk */
+  int64_t n_q;         /* gist queries, chunks [m_start, m_start + n_q):
+                          each chunk complete ((m_start + n_q) * C <= N) and
+                          the gists before it present (m_start + n_q - 1 <= M) */
+  float scale;         /* <= 0: 1/sqrt(D) */
+  int32_t dtype;       /* GSA_BF16 */
+  int64_t row_capacity; /* rows per kv-head in the caches; 0: R = N + M */
+} gsa_gist_params;
+
+/*
+ * q       [Hq, n_q, D]        gist-token queries (row i is chunk m_start + i)
+ * k_cache [Hkv, R, D]         interleaved cache of the sequence
+ * v_cache [Hkv, R, D]
+ * out     [Hq, n_q, D] fp32   attention output (written)
+ * No workspace. GSA_ERR_INVALID_ARG for a NULL pointer or a query range the
+ * cache cannot serve; GSA_ERR_UNSUPPORTED for shapes the kernel does not
+ * run (as gsa_prefill_blocksparse: bf16, D = 128, g in {1, 2, 4},
+ * M <= 65536, N + M < 2^31).
+ */
+gsa_status_t gsa_gist_prefill(const gsa_gist_params* p, const void* q, const void* k_cache,
+                              const void* v_cache, float* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Cache append: place new tokens' K and V rows at their interleaved slots.
+ * Source: gist.science explainer, section 2 'Interleaved Gist Tokens' (a
+ * gist token follows every C raw tokens); slide deck slide 7. Raw token p
+ * goes to row (p / C) * (C + 1) + p % C, the gist of chunk m to row
+ * m * (C + 1) + C, in every (sequence, kv-head) block of row_capacity rows.
+ * In time order the tokens fill rows N + M, N + M + 1, ... (a decode step
+ * appends one raw row, and one gist row every C steps), but raw and gist
+ * rows are given apart and may be appended in any split, e.g. a whole
+ * prompt's raw rows and then its gists.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;        /* B >= 1 sequences */
+  int32_t n_kv_heads;   /* Hkv >= 1 */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int32_t chunk;        /* C >= 1 */
+  int64_t n_raw;        /* N raw tokens already in the cache */
+  int64_t n_gist;       /* M gists already in the cache */
+  int64_t raw_new;      /* raw tokens appended: positions [N, N + raw_new) */
+  int64_t gist_new;     /* gists appended: chunks [M, M + gist_new) */
+  int64_t row_capacity; /* rows per (sequence, kv-head) block, past the
+                           highest slot written */
+  int32_t dtype;        /* gsa_dtype_t of all rows */
+} gsa_append_params;
+
+/*
+ * k_raw, v_raw     [B, Hkv, raw_new, D]    rows of the new raw tokens
+ * k_gist, v_gist   [B, Hkv, gist_new, D]   rows of the new gists
+ * k_cache, v_cache [B, Hkv, row_capacity, D]   written at the new slots only
+ * Inputs and caches are device memory and must not overlap (checked).
+ * Gists only of complete chunks: M * C <= N before and M' * C <= N' after,
+ * with N' = N + raw_new, M' = M + gist_new; raw rows may run ahead of the
+ * gists, their slots waiting. row_capacity must reach the highest slot
+ * written. Else GSA_ERR_INVALID_ARG. The readers (gsa_decode, the prefills)
+ * need the gists caught up, 0 <= N - M*C <= C. Empty appends return
+ * GSA_OK; pointers of an empty side may be NULL.
+ */
+gsa_status_t gsa_cache_append(const gsa_append_params* p, const void* k_raw, const void* v_raw,
+                              const void* k_gist, const void* v_gist, void* k_cache, void* v_cache,
+                              void* stream);
 
 /* ------------------------------------------------------------------------
  * Timing hook (not part of the method): arm this thread with n caller-owned
@@ -203,6 +294,7 @@ gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, const void* q,
  *   gsa_decode_hier: level-2 pass, level-1 candidate pass, unfold pass when
  *     topk1 > 0;
  *   gsa_prefill_blocksparse: selection when topk > 0, then attention.
+ *   gsa_gist_prefill: attention; gsa_cache_append: one copy launch.
  * The library never creates, waits on or destroys the events. n = 0 disarms.
  * Returns GSA_ERR_INVALID_ARG for n outside [0, 8] or a NULL handle.
  * ---------------------------------------------------------------------- */

@@ -46,6 +46,15 @@ int main(void) {
   printf("gsa_decode_params %zu\n", sizeof(gsa_decode_params));
   printf("gsa_hier_params %zu\n", sizeof(gsa_hier_params));
   printf("gsa_prefill_params %zu\n", sizeof(gsa_prefill_params));
+  printf("gsa_gist_params %zu\n", sizeof(gsa_gist_params));
+  printf("gsa_append_params %zu\n", sizeof(gsa_append_params));
+  F(gsa_decode_params, row_capacity); F(gsa_prefill_params, row_capacity);
+  F(gsa_gist_params, n_raw); F(gsa_gist_params, n_gist); F(gsa_gist_params, m_start);
+  F(gsa_gist_params, n_q); F(gsa_gist_params, scale); F(gsa_gist_params, dtype);
+  F(gsa_gist_params, row_capacity);
+  F(gsa_append_params, chunk); F(gsa_append_params, n_raw); F(gsa_append_params, n_gist);
+  F(gsa_append_params, raw_new); F(gsa_append_params, gist_new);
+  F(gsa_append_params, row_capacity); F(gsa_append_params, dtype);
   F(gsa_decode_params, n_raw); F(gsa_decode_params, n_gist); F(gsa_decode_params, chunk);
   F(gsa_decode_params, scale); F(gsa_decode_params, dtype); F(gsa_decode_params, gist_set);
   printf("GSA_GISTS_ALL %d\nGSA_GISTS_SELECTED %d\nGSA_GISTS_NONE %d\n", GSA_GISTS_ALL,
@@ -63,13 +72,16 @@ int main(void) {
     assert int(got["gsa_decode_params"]) == ctypes.sizeof(gsa.DecodeParams)
     assert int(got["gsa_hier_params"]) == ctypes.sizeof(gsa.HierParams)
     assert int(got["gsa_prefill_params"]) == ctypes.sizeof(gsa.PrefillParams)
+    assert int(got["gsa_gist_params"]) == ctypes.sizeof(gsa.GistParams)
+    assert int(got["gsa_append_params"]) == ctypes.sizeof(gsa.AppendParams)
     assert [int(got[f"GSA_GISTS_{n}"]) for n in ("ALL", "SELECTED", "NONE")] == \
         [gsa.GIST_SETS[n] for n in ("all", "selected", "none")]
     for key, val in got.items():
         if "." in key and not key.startswith("GSA_"):
             t, m = key.split(".")
             cls = {"gsa_decode_params": gsa.DecodeParams, "gsa_hier_params": gsa.HierParams,
-                   "gsa_prefill_params": gsa.PrefillParams}[t]
+                   "gsa_prefill_params": gsa.PrefillParams, "gsa_gist_params": gsa.GistParams,
+                   "gsa_append_params": gsa.AppendParams}[t]
             assert getattr(cls, m).offset == int(val), key
 
 
@@ -112,6 +124,10 @@ def ws_size(L, p):
     ({"gist_set": 2, "batch": 128}, OK),      # 256 units
     ({"gist_set": 1, "batch": 128, "topk": 0, "tail": 0}, INVALID),   # nothing to attend
     ({"gist_set": 2, "batch": 128, "dtype": gsa.GSA_F32}, UNSUPPORTED),
+    ({"row_capacity": 1088}, OK),              # exactly N + M
+    ({"row_capacity": 4096}, OK),
+    ({"row_capacity": 1087}, INVALID),         # below N + M
+    ({"row_capacity": -1}, INVALID),
 ])
 def test_decode_param_validation(L, kw, status):
     st, n = ws_size(L, good_decode(**kw))
@@ -185,6 +201,9 @@ def good_prefill(**kw):
     ({"topk": 33}, UNSUPPORTED),                  # above the per-block union bound
     ({"n_raw": 16 * 65537, "n_gist": 65537, "q_start": 0, "n_q": 64}, UNSUPPORTED),
     ({"n_q": 0}, OK),
+    ({"row_capacity": 4352}, OK),              # exactly N + M
+    ({"row_capacity": 8192}, OK),
+    ({"row_capacity": 4351}, INVALID),
 ])
 def test_prefill_param_validation(L, kw, status):
     n = ctypes.c_size_t(0)
@@ -248,3 +267,91 @@ def test_topk_for_budget_matches_the_oracle(L, gist_set):
     assert L.gsa_topk_for_budget(100, 10, 0, 0, 0, ctypes.byref(k)) == INVALID    # chunk < 1
     assert L.gsa_topk_for_budget(100, 10, 4, 0, 3, ctypes.byref(k)) == INVALID    # gist_set
     assert L.gsa_topk_for_budget(100, 10, 4, 0, 0, None) == INVALID
+
+
+# ------------------------------------------------ gist prefill, cache append ---
+
+def good_gist(**kw):
+    p = dict(n_q_heads=8, n_kv_heads=2, head_dim=128, chunk=16, n_raw=1024, n_gist=64, m_start=0,
+             n_q=64, scale=0.0, dtype=gsa.GSA_BF16)
+    p.update(kw)
+    return gsa.GistParams(**p)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, "ok"),
+    ({"m_start": -1}, INVALID),
+    ({"n_q": -1}, INVALID),
+    ({"m_start": 1}, INVALID),                  # chunk 64 does not exist (1024 = 64 chunks)
+    ({"n_raw": 1030, "m_start": 1}, INVALID),   # chunk 64 incomplete (6 of 16 tokens)
+    ({"n_raw": 1040, "n_gist": 64, "m_start": 1}, "ok"),   # chunk 64 complete, gists 0..63 present
+    ({"n_raw": 1040, "n_gist": 64, "m_start": 2}, INVALID),
+    ({"n_gist": 62, "n_raw": 1008, "n_q": 63}, "ok"),    # 63 complete chunks, gist 62 is the last needed
+    ({"n_gist": 61, "n_raw": 992, "n_q": 62}, "ok"),
+    ({"head_dim": 64}, UNSUPPORTED),
+    ({"dtype": gsa.GSA_F32}, UNSUPPORTED),
+    ({"n_q_heads": 16, "n_kv_heads": 2}, UNSUPPORTED),
+    ({"chunk": 0}, INVALID),
+    ({"row_capacity": 1000}, INVALID),
+    ({"n_q": 0}, "ok"),
+])
+def test_gist_prefill_validation(L, kw, status):
+    """Shape errors come back with their status; shapes that pass validation
+    fail on the NULL q instead, so nothing launches."""
+    st = L.gsa_gist_prefill(ctypes.byref(good_gist(**kw)), None, FAKE, FAKE, FAKE, None)
+    msg = L.gsa_last_error().decode()
+    if status == "ok":
+        assert st == INVALID and msg.startswith("q "), msg
+    else:
+        assert st == status and not msg.startswith("q "), msg
+
+
+def good_append(**kw):
+    p = dict(batch=2, n_kv_heads=4, head_dim=128, chunk=16, n_raw=32, n_gist=2, raw_new=1,
+             gist_new=0, row_capacity=4096, dtype=gsa.GSA_BF16)
+    p.update(kw)
+    return gsa.AppendParams(**p)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"n_raw": 32, "n_gist": 2, "raw_new": 0}, OK),      # empty append: nothing to do
+    ({"n_raw": 0, "n_gist": 0, "raw_new": 0}, OK),
+    ({"batch": 0}, INVALID),
+    ({"head_dim": 96}, UNSUPPORTED),
+    ({"dtype": 5}, INVALID),
+    ({"chunk": 0}, INVALID),
+    ({"raw_new": -1}, INVALID),
+    ({"n_raw": 32, "n_gist": 3}, INVALID),       # start state: gist 2 of an incomplete chunk
+    ({"n_raw": 32, "n_gist": 2, "gist_new": 1, "raw_new": 0}, INVALID),   # gist 2 before chunk 2
+    ({"n_raw": 32, "n_gist": 2, "gist_new": 1, "raw_new": 15}, INVALID),  # chunk 2 one token short
+    ({"n_raw": 32, "n_gist": 2, "gist_new": 1, "raw_new": 16}, "ok"),
+    ({"n_raw": 48, "n_gist": 1}, "ok"),          # raw rows ahead of the gists: slots wait
+    ({"n_raw": 0, "n_gist": 0, "raw_new": 50, "row_capacity": 53}, "ok"),   # raw 49 -> row 3 * 17 + 1
+    ({"n_raw": 0, "n_gist": 0, "raw_new": 50, "row_capacity": 52}, INVALID),
+    ({"n_raw": 32, "n_gist": 0, "gist_new": 2, "raw_new": 0, "row_capacity": 34}, "ok"),  # gist 1 -> row 33
+    ({"n_raw": 32, "n_gist": 0, "gist_new": 2, "raw_new": 0, "row_capacity": 33}, INVALID),
+    ({"row_capacity": 35}, "ok"),                # raw 32 -> row 34
+    ({"row_capacity": 34}, INVALID),
+])
+def test_cache_append_validation(L, kw, status):
+    p = good_append(**kw)
+    st = L.gsa_cache_append(ctypes.byref(p), None, None, None, None, None, None, None)
+    msg = L.gsa_last_error().decode()
+    if status == "ok":
+        assert st == INVALID and msg.startswith("k_cache"), msg   # shape fine, NULL cache
+    else:
+        assert st == status and not msg.startswith("k_cache"), msg
+
+
+def test_cache_append_rejects_overlap(L):
+    """A source inside a cache, and K and V caches that overlap, are refused
+    before any launch."""
+    p = good_append()
+    cache = 2 * 4 * 4096 * 256
+    assert L.gsa_cache_append(ctypes.byref(p), FAKE + 256, FAKE + cache + 4096, None, None, FAKE,
+                              FAKE + cache, None) == INVALID
+    assert "overlap" in L.gsa_last_error().decode()
+    assert L.gsa_cache_append(ctypes.byref(p), FAKE + 3 * cache, FAKE + 4 * cache, None, None, FAKE,
+                              FAKE + 256, None) == INVALID
+    assert "overlap" in L.gsa_last_error().decode()
+
