@@ -13,6 +13,9 @@ selects, unfolds and merges).
 
 `--config prefill_64k` times the causal block-sparse prefill instead (4096
 query positions at the end of a 65536-token sequence, 32/8 heads, k=16, W=64).
+`--config gist_64k` times the cache-building step of a 65536-token prompt:
+gsa_cache_append of its raw and gist rows into an empty cache, then
+gsa_gist_prefill of its 4096 gist tokens.
 
 Cold-cache protocol without flushes: the benchmark keeps several copies
 ("layers") of the KV cache and step i reads layer i mod L, so a step's data was
@@ -50,6 +53,7 @@ sys.path.insert(0, ROOT)
 
 DECODE_METRIC = "GSA decode query-heads/s + achieved HBM GB/s (32K ctx, C=16, k=16, bf16)"
 PREFILL_METRIC = "GSA block-sparse prefill query-positions/s + MFMA utilisation (64K ctx, 4096 queries)"
+GIST_METRIC = "GSA cache build (append + gist-token attention) prompt tokens/s (64K prompt, C=16)"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -526,6 +530,140 @@ def run_prefill_bench(args):
     return res
 
 
+# ------------------------------------------------------------ cache build ---
+
+def gist_flops(cfg):
+    """Algorithmic FLOPs of the gist tokens: 2 * D for q.k and 2 * D for p.v
+    per (query head, row); gist m attends its C raw rows and m gists."""
+    rows = cfg.M * cfg.chunk + cfg.M * (cfg.M - 1) // 2
+    return float(rows) * cfg.n_q_heads * cfg.head_dim * 4
+
+
+def cpu_baseline_gist(q, k, v, cfg, budget_s: float):
+    import oracle
+    from threadpoolctl import threadpool_limits
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    qn = q.float().cpu().numpy()
+    K = [k[j].float().cpu().numpy() for j in range(cfg.n_kv_heads)]
+    V = [v[j].float().cpu().numpy() for j in range(cfg.n_kv_heads)]
+    rng = np.random.default_rng(6)
+    t_total, n, rows = 0.0, 0, 0
+    with threadpool_limits(1):
+        while t_total < budget_s and n < 100000:
+            m, j = int(rng.integers(cfg.M)), int(rng.integers(cfg.n_kv_heads))
+            t0 = time.perf_counter()
+            oracle.gist_query(qn[j * g:(j + 1) * g, m], K[j], V[j], m=m, n_raw=cfg.n_raw, n_gist=cfg.M,
+                              chunk=cfg.chunk)
+            t_total += time.perf_counter() - t0
+            n += 1
+            rows += cfg.chunk + m
+    # scaled to whole gist tokens (all kv-heads) of the average length, then
+    # to prompt tokens (C per gist)
+    mean_rows = cfg.chunk + (cfg.M - 1) / 2
+    per_token_s = t_total / n * cfg.n_kv_heads * (mean_rows / (rows / n))
+    return {"value": cfg.chunk / per_token_s, "unit": "prompt-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} random (gist token, kv-head) pairs of the same prompt, fp64 numpy, 1 thread, "
+                      f"{t_total:.1f} s; the append is not timed on the CPU"}
+
+
+def run_gist_bench(args):
+    import torch
+    import decode_gsa_amd as gsa
+    import gsa_inputs as gi
+    import oracle
+
+    cfg = gi.CONFIGS[args.config]
+    dev = torch.device("cuda", 0)
+    C, M, N, D = cfg.chunk, cfg.M, cfg.n_raw, cfg.head_dim
+    log(f"[bench] generating {cfg.name} inputs ...")
+    q, k, v = gi.make_gist(cfg.n_q_heads, cfg.n_kv_heads, D, N, M, M, 2000 + 7, device=dev)
+    raw_rows = torch.tensor([gi.raw_row(p, C, M) for p in range(N)], device=dev)
+    gist_rows = torch.arange(M, device=dev) * (C + 1) + C
+    k_raw, v_raw = k[:, raw_rows].contiguous(), v[:, raw_rows].contiguous()
+    k_gist, v_gist = k[:, gist_rows].contiguous(), v[:, gist_rows].contiguous()
+    kc, vc = torch.zeros_like(k), torch.zeros_like(v)
+    out = torch.empty(cfg.n_q_heads, M, D, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        gsa.gsa_cache_append(kc, vc, chunk=C, n_raw=0, n_gist=0, k_raw=k_raw, v_raw=v_raw, k_gist=k_gist,
+                             v_gist=v_gist, stream=stream)
+        gsa.gsa_gist_prefill(q, kc, vc, chunk=C, m_start=0, n_gist=M, out=out, stream=stream)
+
+    step(0)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, k) and torch.equal(vc, v), "appended cache differs from the interleaved layout"
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    for m, j in ((0, 0), (M // 2 + 3, 5), (M - 1, cfg.n_kv_heads - 1)):
+        r = oracle.gist_query(q[j * g:(j + 1) * g, m].float().cpu().numpy(), k[j].float().cpu().numpy(),
+                              v[j].float().cpu().numpy(), m=m, n_raw=N, n_gist=M, chunk=C)
+        got = out[j * g:(j + 1) * g, m].double().cpu().numpy()
+        rms = float(np.sqrt(np.mean(r["out"] ** 2)))
+        assert float(np.abs(got - r["out"]).max()) <= 2e-3 * rms, f"gist token {m} differs from the oracle"
+    # wall clock of uninstrumented steps, then per-call kernel times: the
+    # event hook is armed per library call, so each call gets its own pair
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    ev = HipEvents(4 * args.steps)
+    try:
+        for i in range(args.steps):
+            gsa.gsa_profile_events(ev.ev[4 * i:4 * i + 2])
+            gsa.gsa_cache_append(kc, vc, chunk=C, n_raw=0, n_gist=0, k_raw=k_raw, v_raw=v_raw,
+                                 k_gist=k_gist, v_gist=v_gist, stream=stream)
+            gsa.gsa_profile_events(ev.ev[4 * i + 2:4 * i + 4])
+            gsa.gsa_gist_prefill(q, kc, vc, chunk=C, m_start=0, n_gist=M, out=out, stream=stream)
+            gsa.gsa_profile_events([])
+        torch.cuda.synchronize()
+        app_per = np.array([ev.ms(4 * i, 4 * i + 1) for i in range(args.steps)])
+        att_per = np.array([ev.ms(4 * i + 2, 4 * i + 3) for i in range(args.steps)])
+    finally:
+        gsa.gsa_profile_events([])
+        ev.close()
+    app_ms = float(app_per.mean())
+    att_ms = float(att_per.mean())
+    fl = gist_flops(cfg)
+    achieved = fl / (att_ms / 1e3) / 1e12
+    row_b = D * 2
+    app_bytes = 2.0 * cfg.n_kv_heads * (N + M) * row_b * 2     # K and V rows read and written
+    res = {
+        "metric": GIST_METRIC,
+        "value": N / (ms_per_step / 1e3),
+        "unit": "prompt-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian q/K/V rows)",
+        "config": {"workload": f"{cfg.name}: cache build of a {N}-token prompt, append of {N} raw + {M} "
+                               f"gist rows then attention of its {M} gist tokens, Hq={cfg.n_q_heads}, "
+                               f"Hkv={cfg.n_kv_heads}, D={D}, C={C}, bf16",
+                   "seq_len": N, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                     "traffic": measured_traffic(f"prefill_attend/{cfg.name}", source_sha("gsa_prefill.hip")),
+                     "kernel": "prefill_attend (gist queries)", "alg_flops_per_launch": fl,
+                     "launch_ms_mean": att_ms},
+        "kernels": {"prefill_attend": {"ms": att_ms, "alg_flops": fl, "TFLOP_s": achieved, **pcts(att_per)},
+                    "cache_append": {"ms": app_ms, "alg_bytes": app_bytes,
+                                     "GB_s": app_bytes / (app_ms / 1e3) / 1e9, **pcts(app_per)}},
+        "source_sha": source_sha("gsa_prefill.hip", "gsa_cache.hip"),
+    }
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline_gist(q, k, v, cfg, args.cpu_seconds)
+    return res
+
+
 def hbm_stream_rates(reps: int = 8) -> dict:
     """Bandwidth of a plain torch device copy of 1 GiB (bytes read + written),
     reported next to the 8 TB/s specification as what a generic streaming
@@ -594,6 +732,8 @@ def main():
         res = run_prefill_bench(args)
     elif isinstance(cfg, gi.HierConfig):
         res = run_hier_bench(args)
+    elif isinstance(cfg, gi.GistConfig):
+        res = run_gist_bench(args)
     else:
         raise SystemExit(f"--config {args.config}: no benchmark for this workload yet")
     print(json.dumps(res), flush=True)

@@ -228,12 +228,15 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Workgroup -> (kv-head, query block). Consecutive linear ids share a kv-head
 // (its K/V rows); with 8 XCDs taking workgroups round-robin, the linear id
 // groups each XCD's workgroups together so one XCD's L2 serves one kv-head.
+// Blocks go out last first: under the causal order a later block sees more
+// gists, so the longest workgroups start first and the short ones fill in
+// behind them (a CU that ends a long block early takes a short one).
 __device__ __forceinline__ void wg_coords(int n_blocks, int Hkv, int* kvh, int* blk) {
   const int total = n_blocks * Hkv;
   int x = (int)blockIdx.x;
   if (total % 8 == 0) x = (x % 8) * (total / 8) + x / 8;
   *kvh = x / n_blocks;
-  *blk = x % n_blocks;
+  *blk = n_blocks - 1 - x % n_blocks;
 }
 
 // Query fragments (B operand of S^T = K Q^T) of heads h0..h0+H-1: lane holds

@@ -26,7 +26,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "DecodeConfig", "HierConfig", "PrefillConfig", "CONFIGS",
+    "DecodeConfig", "HierConfig", "PrefillConfig", "GistConfig", "CONFIGS",
     "DecodeInputs", "HierInputs", "PrefillInputs",
     "make_decode", "make_hier", "make_prefill", "make_gist", "TokenStream", "make_token_stream",
     "raw_row", "gist_row", "n_rows",
@@ -108,6 +108,27 @@ class PrefillConfig:
         return self.n_raw - self.n_q
 
 
+@dataclasses.dataclass(frozen=True)
+class GistConfig:
+    """Cache-building step of one prompt: every raw and gist row appended to an
+    empty cache, then the attention of every gist token."""
+    name: str
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str
+    n_raw: int
+    chunk: int
+
+    @property
+    def M(self) -> int:
+        return self.n_raw // self.chunk
+
+    @property
+    def R(self) -> int:
+        return self.n_raw + self.M
+
+
 CONFIGS = {
     # tiny single-query decode, fp32, D=64: parity config
     "tiny_f32": DecodeConfig("tiny_f32", 1, 1, 1, 64, "f32", 4096, 16, 8, 16,
@@ -123,6 +144,8 @@ CONFIGS = {
     # causal block-sparse prefill of the last 4096 positions of a 64K sequence
     "prefill_64k": PrefillConfig("prefill_64k", 32, 8, 128, "bf16", 65536, 16, 16,
                                  64, 4096),
+    # cache append + gist-token attention of a 64K-token prompt (4096 gists)
+    "gist_64k": GistConfig("gist_64k", 32, 8, 128, "bf16", 65536, 16),
 }
 
 
