@@ -29,6 +29,7 @@ in float64 on the exact input values (bf16 inputs are widened exactly):
   * two-level variant -- meta-gists are scored first, then the gists inside
     the chosen meta-gist groups, then raw chunks are unfolded (gist.science
     explainer, 'Hierarchical Extension (H-GSA)', 'Coarse-to-Fine Selection');
+    the same descent over L levels of gists-of-gists (``decode_levels_unit``);
   * prefill -- the same rule applied per query position under causality, i.e.
     the forward pass of the top-k attention mask of selective finetuning
     (gist.science explainer, 'Training Procedure: Selective Finetuning');
@@ -58,6 +59,13 @@ Readings where the pages are silent (each also listed in the design notes):
      [i G, (i + 1) G); the level-1 gists that no full group covers are always
      candidates; the attention set holds every level-2 gist, every candidate
      level-1 gist, the raw rows of the selected chunks and the tail.
+  R9 L levels: level l >= 2 has M_l = floor(M_{l-1} / G) gists in its own
+     array, gist i of level l summarising gists [i G, (i + 1) G) of level
+     l - 1; top-down, every level's candidates are the children of the
+     level above's selection plus that level's ungrouped gists (every gist at
+     the top); the set holds every top-level gist, every candidate of the
+     levels below, the raw rows of the selected chunks and the tail. L = 2 is
+     R7.
 
 Parity pins for every function here live in tests/test_oracle.py.
 """
@@ -70,7 +78,7 @@ import numpy as np
 
 __all__ = [
     "gist_row_index", "raw_row_index", "topk_ascending",
-    "decode_unit", "decode", "decode_hier_unit", "decode_hier", "topk_for_budget", "GIST_SETS",
+    "decode_unit", "decode", "decode_hier_unit", "decode_hier", "decode_levels_unit", "decode_levels", "topk_for_budget", "GIST_SETS",
     "prefill_query", "prefill", "cache_row", "gist_query", "gist_prefill",
 ]
 
@@ -344,6 +352,93 @@ def decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int, top
         sel2[b, j] = r["sel2"]
         sel1[b, j, :len(r["sel1"])] = r["sel1"]
     return out, lse, sel2, sel1
+
+
+def decode_levels_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, upper, *, n_raw: int,
+                       n_gist: int, chunk: int, fanout: int, topks, tail: int,
+                       scale: Optional[float] = None) -> Dict[str, object]:
+    """One unit of L-level decode (R9; explainer 'Hierarchical Extension
+    (H-GSA)' and 'Coarse-to-Fine Selection', slide 11).
+
+    upper: [(K_2, V_2), ..., (K_L, V_L)], K_l: [M_l, D] with
+    M_l = floor(M_{l-1} / G), M_1 = n_gist.  topks: [k_1, ..., k_L], k_1 the
+    chunks unfolded.  Returns out, lse, wsum, sels [sel_1 .. sel_L]
+    (ascending ids), cands [cand_1 .. cand_L] (sorted candidate ids of every
+    level; all ids at the top) and rows (level-1 cache rows attended).
+    """
+    qg = _f64(qg)
+    g, D = qg.shape
+    C, M, N, T, G = chunk, n_gist, n_raw, tail, fanout
+    _check_common(N, M, C, K.shape[0])
+    L = len(upper) + 1
+    if G <= 0 or L < 2 or len(topks) != L:
+        raise ValueError("need fanout > 0, at least two levels and one k per level")
+    sizes = [M]
+    for l in range(2, L + 1):
+        sizes.append(sizes[-1] // G)
+        if upper[l - 2][0].shape[0] != sizes[-1]:
+            raise ValueError(f"level {l} array has {upper[l - 2][0].shape[0]} rows, expected {sizes[-1]}")
+    if not (N - M * C <= T <= N):
+        raise ValueError("tail must cover the raw tokens after the last gist")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+    def keys_of(l, ids):           # key rows of gists `ids` at level l (1-based)
+        if l == 1:
+            return _f64(K[[gist_row_index(m, C) for m in ids]])
+        return _f64(upper[l - 2][0][list(ids)])
+
+    sels, cands = [None] * (L + 1), [None] * (L + 1)
+    cands[L] = list(range(sizes[L - 1]))
+    for l in range(L, 0, -1):
+        if l < L:
+            above = sels[l + 1]
+            grouped = sizes[l] * G
+            cands[l] = sorted({i * G + c for i in above for c in range(G)} | set(range(grouped, sizes[l - 1])))
+        k = topks[l - 1]
+        if not (0 <= k <= len(cands[l])):
+            raise ValueError(f"k at level {l} exceeds its {len(cands[l])} candidates")
+        S = _group_scores(qg, keys_of(l, cands[l]), scale) if cands[l] else np.zeros(0)
+        sels[l] = topk_ascending(S, cands[l], k)
+    # attention set: the top level, every lower level's candidates, the raw
+    # rows of the chosen chunks and the tail (rows of the level-1 cache)
+    A = {gist_row_index(m, C) for m in cands[1]}
+    for m in sels[1]:
+        for j in range(C):
+            A.add(raw_row_index(m * C + j, C, M))
+    for p in range(N - T, N):
+        A.add(raw_row_index(p, C, M))
+    rows = np.array(sorted(A), dtype=np.int64)
+    keys = [_f64(upper[l - 2][0][cands[l]]) for l in range(L, 1, -1)] + [_f64(K[rows])]
+    vals = [_f64(upper[l - 2][1][cands[l]]) for l in range(L, 1, -1)] + [_f64(V[rows])]
+    out, lse, wsum = _softmax_attend(qg, np.concatenate(keys), np.concatenate(vals), scale)
+    return {"out": out, "lse": lse, "wsum": wsum,
+            "sels": [np.array(sels[l], dtype=np.int64) for l in range(1, L + 1)],
+            "cands": [np.array(cands[l], dtype=np.int64) for l in range(1, L + 1)], "rows": rows}
+
+
+def decode_levels(q, k_cache, v_cache, upper, *, chunk: int, fanout: int, topks, tail: int,
+                  n_gist: Optional[int] = None, scale: Optional[float] = None, units=None):
+    """Batched L-level decode. upper: [(K_2, V_2), ...] each [B, Hkv, M_l, D].
+    Returns out [B, Hq, D], lse [B, Hq], sels [[B, Hkv, k_l] for l = 1..L]."""
+    B, Hq, D = q.shape
+    Hkv, R = k_cache.shape[1], k_cache.shape[2]
+    g = Hq // Hkv
+    if n_gist is None:
+        n_gist = R // (chunk + 1)
+    n_raw = R - n_gist
+    out = np.full((B, Hq, D), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    sels = [np.full((B, Hkv, k), -1, dtype=np.int64) for k in topks]
+    todo = [(b, j) for b in range(B) for j in range(Hkv)] if units is None else units
+    for b, j in todo:
+        r = decode_levels_unit(q[b, j * g:(j + 1) * g], k_cache[b, j], v_cache[b, j],
+                               [(Ku[b, j], Vu[b, j]) for Ku, Vu in upper], n_raw=n_raw, n_gist=n_gist,
+                               chunk=chunk, fanout=fanout, topks=topks, tail=tail, scale=scale)
+        out[b, j * g:(j + 1) * g] = r["out"]
+        lse[b, j * g:(j + 1) * g] = r["lse"]
+        for l, sl in enumerate(r["sels"]):
+            sels[l][b, j] = sl
+    return out, lse, sels
 
 
 # --------------------------------------------------------------- prefill ---

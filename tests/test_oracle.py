@@ -593,3 +593,104 @@ def test_gist_query_needs_a_complete_chunk_and_its_predecessors():
     with pytest.raises(ValueError):
         oracle.gist_query(qg, K, V, m=3, n_raw=N, n_gist=M, chunk=C)   # chunk 3 has 2 of 4 tokens
     oracle.gist_query(qg, K, V, m=2, n_raw=N, n_gist=M, chunk=C)
+
+
+# ---------------------------------------------------------------- L levels --
+
+def _levels_inputs(rng, g, D, C, M, G, L, r=0):
+    N = M * C + r
+    R = N + M
+    sizes = [M]
+    for _ in range(2, L + 1):
+        sizes.append(sizes[-1] // G)
+    upper = [(rng.standard_normal((n, D)), rng.standard_normal((n, D))) for n in sizes[1:]]
+    return rng.standard_normal((g, D)), rng.standard_normal((R, D)), rng.standard_normal((R, D)), upper, N, sizes
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_levels_two_is_the_two_level_decode(seed):
+    """L = 2 is the two-level rule (pinned above on its own)."""
+    rng = np.random.default_rng(500 + seed)
+    g, D, C, G = 2, 8, 4, int(rng.integers(2, 5))
+    M = int(rng.integers(G, 40))
+    r = int(rng.integers(0, C + 1))
+    qg, K, V, upper, N, sizes = _levels_inputs(rng, g, D, C, M, G, 2, r)
+    k2 = int(rng.integers(0, sizes[1] + 1))
+    k1 = int(rng.integers(0, k2 * G + (M - sizes[1] * G) + 1))
+    T = int(rng.integers(r, N + 1))
+    a = oracle.decode_levels_unit(qg, K, V, upper, n_raw=N, n_gist=M, chunk=C, fanout=G, topks=[k1, k2], tail=T)
+    b = oracle.decode_hier_unit(qg, K, V, upper[0][0], upper[0][1], n_raw=N, n_gist=M, chunk=C, fanout=G,
+                                topk1=k1, topk2=k2, tail=T)
+    assert list(a["sels"][0]) == list(b["sel1"]) and list(a["sels"][1]) == list(b["sel2"])
+    np.testing.assert_array_equal(a["rows"], b["rows"])
+    np.testing.assert_allclose(a["out"], b["out"], rtol=0, atol=1e-13)
+
+
+def test_levels_everything_selected_is_full_attention_over_every_level():
+    rng = np.random.default_rng(510)
+    g, D, C, M, G, L = 2, 16, 3, 29, 3, 4      # sizes 29, 9, 3, 1: orphans at levels 1 and 2
+    qg, K, V, upper, N, sizes = _levels_inputs(rng, g, D, C, M, G, L)
+    topks = [sizes[l] for l in range(L)]      # every candidate at every level is every gist
+    res = oracle.decode_levels_unit(qg, K, V, upper, n_raw=N, n_gist=M, chunk=C, fanout=G, topks=topks, tail=0)
+    keys = np.concatenate([u[0] for u in upper[::-1]] + [K])
+    vals = np.concatenate([u[1] for u in upper[::-1]] + [V])
+    ref = sdpa(qg, keys, vals, np.ones(len(keys), bool), 1 / math.sqrt(D))
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_levels_coarse_to_fine_bruteforce_dense_masks(seed):
+    """Three and four levels: at every level the best subset of the
+    candidates by brute force, candidates from a dense mask over the level
+    (parent chosen, or no full group above), and the attention set from those
+    masks against float64 SDPA."""
+    rng = np.random.default_rng(520 + seed)
+    g, D, C, G = 2, 6, 2, 2
+    L = 3 + seed % 2
+    M = int(rng.integers(G ** (L - 1), 22))
+    qg, K, V, upper, N, sizes = _levels_inputs(rng, g, D, C, M, G, L)
+    keys_at = [np.array([K[m * (C + 1) + C] for m in range(M)])] + [u[0] for u in upper]
+    vals_at = [np.array([V[m * (C + 1) + C] for m in range(M)])] + [u[1] for u in upper]
+    # choose k per level top-down so that each is feasible
+    topks, masks, chosen = [0] * L, [None] * L, [None] * L
+    for l in range(L - 1, -1, -1):
+        n = sizes[l]
+        if l == L - 1:
+            mask = np.ones(n, bool)
+        else:
+            par = np.arange(n) // G
+            mask = (par >= sizes[l + 1]) | np.isin(par, list(chosen[l + 1]))
+        ids = list(np.nonzero(mask)[0])
+        k = int(rng.integers(0, len(ids) + 1))
+        s = (keys_at[l] @ qg.T).mean(1)
+        best = max(itertools.combinations(ids, k), key=lambda c: (sum(s[list(c)]), [-i for i in c]))
+        topks[l], masks[l], chosen[l] = k, mask, set(best)
+    res = oracle.decode_levels_unit(qg, K, V, upper, n_raw=N, n_gist=M, chunk=C, fanout=G, topks=topks, tail=0)
+    for l in range(L):
+        assert list(res["sels"][l]) == sorted(chosen[l]), f"level {l + 1}"
+        assert list(res["cands"][l]) == list(np.nonzero(masks[l])[0]), f"level {l + 1}"
+    # dense attention mask over [level L .. level 2 arrays, level-1 cache]
+    keys = np.concatenate([keys_at[l] for l in range(L - 1, 0, -1)] + [K])
+    vals = np.concatenate([vals_at[l] for l in range(L - 1, 0, -1)] + [V])
+    m1 = np.zeros(len(K), bool)
+    for x in range(len(K)):
+        kind, v = row_kind(x, C, M)
+        m1[x] = masks[0][v] if kind == "gist" else (v // C < M and v // C in chosen[0])
+    mask = np.concatenate([masks[l] for l in range(L - 1, 0, -1)] + [m1])
+    np.testing.assert_allclose(res["out"], sdpa(qg, keys, vals, mask, 1 / math.sqrt(D)), rtol=0, atol=1e-12)
+
+
+def test_levels_middle_orphan_is_always_a_candidate():
+    """A level-2 gist that no level-3 group covers is a candidate whatever
+    level 3 chooses, and its children follow it down."""
+    rng = np.random.default_rng(530)
+    g, D, C, M, G, L = 1, 4, 2, 14, 3, 3     # sizes 14, 4, 1: level-2 gist 3 is ungrouped
+    qg, K, V, upper, N, sizes = _levels_inputs(rng, g, D, C, M, G, L)
+    qg = np.array([[1.0, 0, 0, 0]])
+    upper[1][0][0, 0] = 5.0                   # the one level-3 group: children 0, 1, 2
+    upper[0][0][:, 0] = [1.0, 0.0, 0.0, 40.0]  # orphan 3 is the best level-2 gist
+    res = oracle.decode_levels_unit(qg, K, V, upper, n_raw=N, n_gist=M, chunk=C, fanout=G, topks=[1, 1, 1],
+                                    tail=0, scale=1.0)
+    assert list(res["cands"][1]) == [0, 1, 2, 3]
+    assert list(res["sels"][1]) == [3]
+    assert list(res["cands"][0]) == [9, 10, 11, 12, 13]   # children of 3, then level-1 orphans 12, 13
