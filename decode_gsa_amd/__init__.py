@@ -8,6 +8,7 @@ built, every call raises (there is no fallback path).
 Entry points (same names as the C ABI):
   gsa_decode(q, k_cache, v_cache, chunk=, topk=, tail=, ...)
   gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, chunk=, fanout=, topk1=, topk2=, tail=, ...)
+  gsa_decode_levels(q, k_cache, v_cache, k_up, v_up, chunk=, fanout=, topks=, tail=, ...)
   gsa_prefill_blocksparse(q, k_cache, v_cache, chunk=, topk=, window=, q_start=, ...)
   gsa_gist_prefill(q, k_cache, v_cache, chunk=, m_start=, ...)
   gsa_cache_append(k_cache, v_cache, chunk=, n_raw=, n_gist=, k_raw=, v_raw=, k_gist=, v_gist=)
@@ -24,11 +25,12 @@ from typing import Optional
 
 __all__ = [
     "GsaError", "lib", "LIB_PATH", "DecodeParams", "HierParams", "PrefillParams", "GistParams",
-    "AppendParams", "GSA_F32", "GSA_BF16", "EXPORTED_SYMBOLS",
-    "decode_params", "hier_params", "prefill_params", "gist_params", "append_params",
+    "AppendParams", "LevelsParams", "MAX_LEVELS", "GSA_F32", "GSA_BF16", "EXPORTED_SYMBOLS",
+    "decode_params", "hier_params", "prefill_params", "gist_params", "append_params", "levels_params",
     "decode_workspace_size", "hier_workspace_size", "prefill_workspace_size", "new_workspace",
     "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse", "gsa_profile_events",
     "gsa_profile_marks", "topk_for_budget", "GIST_SETS", "gsa_gist_prefill", "gsa_cache_append",
+    "gsa_decode_levels", "levels_workspace_size",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -41,7 +43,9 @@ EXPORTED_SYMBOLS = (
     "gsa_prefill_workspace_size", "gsa_prefill_blocksparse",
     "gsa_profile_events", "gsa_profile_marks", "gsa_status_string", "gsa_last_error",
     "gsa_topk_for_budget", "gsa_gist_prefill", "gsa_cache_append",
+    "gsa_decode_levels_workspace_size", "gsa_decode_levels",
 )
+MAX_LEVELS = 6
 
 _c_i32, _c_i64, _c_f32, _vp, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                     ctypes.c_void_p, ctypes.c_size_t)
@@ -56,6 +60,11 @@ class DecodeParams(ctypes.Structure):
 
 class HierParams(ctypes.Structure):
     _fields_ = [("base", DecodeParams), ("fanout", _c_i32), ("topk2", _c_i32)]
+
+
+class LevelsParams(ctypes.Structure):
+    _fields_ = [("base", DecodeParams), ("n_levels", _c_i32), ("fanout", _c_i32),
+                ("topk_up", _c_i32 * (MAX_LEVELS - 1))]
 
 
 class PrefillParams(ctypes.Structure):
@@ -103,6 +112,9 @@ def lib() -> ctypes.CDLL:
         L.gsa_prefill_workspace_size.argtypes = [P(PrefillParams), P(_sz)]
         L.gsa_prefill_blocksparse.argtypes = [P(PrefillParams), _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                                               _vp]
+        L.gsa_decode_levels_workspace_size.argtypes = [P(LevelsParams), P(_sz)]
+        L.gsa_decode_levels.argtypes = [P(LevelsParams), _vp, _vp, _vp, P(_vp), P(_vp), _vp, _vp,
+                                         P(_vp), _vp, _vp, _sz, _vp]
         L.gsa_gist_prefill.argtypes = [P(GistParams), _vp, _vp, _vp, _vp, _vp]
         L.gsa_cache_append.argtypes = [P(AppendParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.gsa_profile_events.argtypes = [P(_vp), _c_i32]
@@ -162,6 +174,14 @@ def hier_params(base: DecodeParams, fanout: int, topk2: int) -> HierParams:
     return HierParams(base, fanout, topk2)
 
 
+def levels_params(base: DecodeParams, fanout: int, topk_up) -> LevelsParams:
+    """topk_up = [k_2, ..., k_L] (base.topk is k_1)."""
+    if not 1 <= len(topk_up) <= MAX_LEVELS - 1:
+        raise ValueError(f"2 to {MAX_LEVELS} levels")
+    arr = (_c_i32 * (MAX_LEVELS - 1))(*([int(k) for k in topk_up] + [0] * (MAX_LEVELS - 1 - len(topk_up))))
+    return LevelsParams(base, len(topk_up) + 1, fanout, arr)
+
+
 def prefill_params(n_q_heads, n_kv_heads, head_dim, chunk, topk, window, n_raw, n_gist, q_start,
                    n_q, scale=0.0, dtype=GSA_BF16, row_capacity=0) -> PrefillParams:
     return PrefillParams(n_q_heads, n_kv_heads, head_dim, chunk, topk, window, n_raw, n_gist,
@@ -191,6 +211,13 @@ def hier_workspace_size(p: HierParams) -> int:
     n = _sz(0)
     _check(lib().gsa_decode_hier_workspace_size(ctypes.byref(p), ctypes.byref(n)),
            "gsa_decode_hier_workspace_size")
+    return n.value
+
+
+def levels_workspace_size(p: LevelsParams) -> int:
+    n = _sz(0)
+    _check(lib().gsa_decode_levels_workspace_size(ctypes.byref(p), ctypes.byref(n)),
+           "gsa_decode_levels_workspace_size")
     return n.value
 
 
@@ -329,6 +356,45 @@ def gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int,
                                  _ptr(sel1) if topk1 > 0 else None, _ptr(ws), _nbytes(ws),
                                  _stream(stream, dev)), "gsa_decode_hier")
     return out, lse, sel2, sel1
+
+
+def gsa_decode_levels(q, k_cache, v_cache, k_up, v_up, *, chunk: int, fanout: int, topks,
+                      tail: int, n_gist: Optional[int] = None, n_raw: Optional[int] = None,
+                      scale: float = 0.0, out=None, lse=None, workspace=None, stream=None,
+                      want_lse: bool = True, want_sel: bool = True):
+    """L-level decode. k_up, v_up: [level 2, ..., level L] arrays [B,Hkv,M_l,D];
+    topks = [k_1, ..., k_L].
+
+    Returns (out [B,Hq,D] fp32, lse [B,Hq] or None, sels [sel_1 [B,Hkv,k_1], ...,
+    sel_L] or None).
+    """
+    import torch
+    B, Hq, D = q.shape
+    Hkv, R = k_cache.shape[1], k_cache.shape[2]
+    N, M, cap = _geometry(R, chunk, n_gist, n_raw)
+    topks = [int(k) for k in topks]
+    if len(k_up) != len(topks) - 1 or len(v_up) != len(topks) - 1:
+        raise ValueError("one k per level and one array pair per level above the first")
+    base = decode_params(B, Hq, Hkv, D, N, M, chunk, topks[0], tail, scale, _dtype_code(q),
+                         row_capacity=cap)
+    p = levels_params(base, fanout, topks[1:])
+    dev = q.device
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    sels = ([torch.empty(B, Hkv, max(k, 0), dtype=torch.int32, device=dev) for k in topks]
+            if want_sel else None)
+    n_up = len(k_up)
+    kp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in k_up])
+    vp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in v_up])
+    sp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in sels[1:]]) if want_sel else None
+    nbytes = levels_workspace_size(p)
+    ws = _workspace(workspace, nbytes, dev)
+    _check(lib().gsa_decode_levels(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), kp, vp,
+                                   _ptr(out), _ptr(lse), sp,
+                                   _ptr(sels[0]) if want_sel and topks[0] > 0 else None, _ptr(ws),
+                                   _nbytes(ws), _stream(stream, dev)), "gsa_decode_levels")
+    return out, lse, sels
 
 
 def gsa_prefill_blocksparse(q, k_cache, v_cache, *, chunk: int, topk: int, window: int,

@@ -867,6 +867,7 @@ struct GistArgs {
   const float* prev_scores;
   int64_t prev_stride;
   int32_t prev_n, prev_k;
+  IdMap prev_im;          // previous pass' score index -> id (identity when it scored every gist)
   int32_t* sel2_ws;       // [units][sel2_stride] (for the unfold pass' ids)
   int64_t sel2_stride;
   int32_t* sel2_out;      // [units][prev_k] or null
@@ -913,8 +914,8 @@ void gist_kernel(GistArgs a) {
   RowMap rm = a.rm;
   if (rm.kind == 2) {
     // the unit's level-2 groups (every workgroup of the unit makes the same selection)
-    unit_topk(a.prev_scores + (size_t)unit * a.prev_stride, a.prev_n, a.prev_k, IdMap{nullptr, 0, 0, 0, 0},
-              unit, lds.sel2, lds.u.sel.s, lds.u.sel.t);
+    unit_topk(a.prev_scores + (size_t)unit * a.prev_stride, a.prev_n, a.prev_k, a.prev_im, unit, lds.sel2,
+              lds.u.sel.s, lds.u.sel.t);
     __syncthreads();
     if (split == 0)
       for (int i = tid; i < a.prev_k; i += kThreads) {
@@ -1153,6 +1154,7 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   c.T = 0; c.tail_per_task = 0;
   c.scores = pl.k > 0 ? sc : nullptr; c.score_stride = hp.sc_stride;
   c.prev_scores = s2; c.prev_stride = hp.s2_stride; c.prev_n = (int32_t)hp.M2; c.prev_k = hp.k2;
+  c.prev_im = IdMap{nullptr, 0, 0, 0, 0};
   c.sel2_ws = wsel2; c.sel2_stride = hp.sel2_stride; c.sel2_out = sel2;
   c.part_base = hp.S_l2;
   c.out = pl.k > 0 ? nullptr : out; c.lse = pl.k > 0 ? nullptr : lse;
@@ -2139,6 +2141,84 @@ struct HierRunner {
   static gsa_status_t run(A&&... a) { return run_hier<B, D, G>(a...); }
 };
 
+// L levels: the top pass scores and attends every top-level gist and the
+// tail; the pass of each lower level l first selects the top k_{l+1} of the
+// level above from that pass' scores (mapped to ids), then scores and attends
+// its candidates (the chosen gists' children and the ungrouped gists, dense
+// rows of the level's array; level 1: gist rows of the interleaved cache);
+// the unfold pass selects k_1 chunks among the level-1 candidates and merges.
+template <bool BF16, int D, int G>
+gsa_status_t run_levels(const LevelsPlan& lp, const void* q, const void* K, const void* V,
+                        const void* const* Ku, const void* const* Vu, float* out, float* lse,
+                        int32_t* const* sel_up, int32_t* sel1, char* ws, hipStream_t st) {
+  const DecodePlan& pl = lp.base;
+  const int L = lp.L;
+  float* part = reinterpret_cast<float*>(ws + lp.off_part);
+  const int64_t ps = part_stride(G, D);
+  auto scores = [&](int l) { return reinterpret_cast<float*>(ws + lp.off_scores[l]); };
+  auto selws = [&](int l) { return reinterpret_cast<int32_t*>(ws + lp.off_sel[l]); };
+  GistArgs g{};
+  g.q = q; g.K = Ku[L - 2]; g.V = Vu[L - 2];
+  g.unit_rows = lp.Ml[L]; g.n_items = lp.items[L]; g.per_task = lp.per_split[L]; g.tasks = lp.S[L];
+  g.rm = RowMap{1, pl.C, nullptr, 0, 0, 0, 0};
+  g.Kt = K; g.Vt = V; g.tail_unit_rows = pl.R;
+  g.N = pl.N; g.M = pl.M; g.C = pl.C; g.T = pl.T; g.tail_per_task = lp.tail_per_split;
+  g.scores = scores(L); g.score_stride = lp.score_stride[L];
+  g.part = part; g.part_stride = ps; g.NP = lp.NP; g.part_base = 0;
+  g.out = nullptr; g.lse = nullptr;
+  g.cnt = ctrl_of(ws, lp.off_ctrl, 0);
+  g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
+  g.fuse_k = 0;
+  prof_begin_call();
+  prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * lp.S[L]), dim3(kThreads), 0, st, g);
+  int32_t base = lp.S[L];
+  for (int l = L - 1; l >= 1; --l) {
+    GistArgs c = g;
+    c.K = l >= 2 ? Ku[l - 2] : K;
+    c.V = l >= 2 ? Vu[l - 2] : V;
+    c.unit_rows = l >= 2 ? lp.Ml[l] : pl.R;
+    c.n_items = lp.items[l]; c.per_task = lp.per_split[l]; c.tasks = lp.S[l];
+    // kind 2 with C = 0 gives dense rows of a level array
+    c.rm = RowMap{2, l >= 2 ? 0 : pl.C, nullptr, lp.G, lp.kl[l + 1], lp.orphan0[l], 0};
+    c.T = 0; c.tail_per_task = 0;
+    const bool last = l == 1 && pl.k == 0;
+    c.scores = last ? nullptr : scores(l); c.score_stride = lp.score_stride[l];
+    c.prev_scores = scores(l + 1); c.prev_stride = lp.score_stride[l + 1];
+    c.prev_n = (int32_t)lp.items[l + 1]; c.prev_k = lp.kl[l + 1];
+    c.prev_im = l + 1 == L ? IdMap{nullptr, 0, 0, 0, 0}
+                           : IdMap{selws(l + 2), lp.G, lp.kl[l + 2], lp.orphan0[l + 1], lp.sel_stride[l + 2]};
+    c.sel2_ws = selws(l + 1); c.sel2_stride = lp.sel_stride[l + 1];
+    c.sel2_out = sel_up ? sel_up[l - 1] : nullptr;
+    c.part_base = base;
+    c.out = last ? out : nullptr; c.lse = last ? lse : nullptr;
+    c.cnt = ctrl_of(ws, lp.off_ctrl, L - l);
+    prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * lp.S[l]), dim3(kThreads), 0, st, c);
+    base += lp.S[l];
+  }
+  if (pl.k > 0) {
+    UnfoldArgs u{};
+    u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
+    u.scores = scores(1); u.score_stride = lp.score_stride[1]; u.n_cand = (int32_t)lp.items[1];
+    u.im = IdMap{selws(2), lp.G, lp.kl[2], lp.orphan0[1], lp.sel_stride[2]};
+    u.sel_ws = reinterpret_cast<int32_t*>(ws + lp.off_sel1); u.sel_stride = pl.sel_stride;
+    u.sel_out = sel1; u.k = pl.k;
+    u.C = pl.C; u.T = pl.T; u.M = pl.M; u.N = pl.N;
+    u.n_items = pl.n_items; u.per_task = pl.items_per_split; u.tasks = pl.S2;
+    u.part = part; u.part_stride = ps; u.NP = lp.NP; u.part_base = base;
+    u.out = out; u.lse = lse;
+    u.cnt = ctrl_of(ws, lp.off_ctrl, L);
+    u.scale_log2 = pl.scale * kLog2e;
+    prof_launch((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
+  }
+  return launch_status("gsa_decode_levels launch");
+}
+
+template <bool B, int D, int G>
+struct LevelsRunner {
+  template <class... A>
+  static gsa_status_t run(A&&... a) { return run_levels<B, D, G>(a...); }
+};
+
 }  // namespace
 }  // namespace gsa
 
@@ -2219,3 +2299,43 @@ extern "C" gsa_status_t gsa_decode_hier(const gsa_hier_params* p, const void* q,
                               out, lse, sel2, sel1, reinterpret_cast<char*>(workspace),
                               reinterpret_cast<hipStream_t>(stream));
 }
+
+extern "C" gsa_status_t gsa_decode_levels_workspace_size(const gsa_levels_params* p, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(GSA_ERR_INVALID_ARG, "bytes is NULL");
+  LevelsPlan lp;
+  gsa_status_t s = plan_levels(p, &lp);
+  if (s != GSA_OK) return s;
+  *bytes = lp.total;
+  return GSA_OK;
+}
+
+extern "C" gsa_status_t gsa_decode_levels(const gsa_levels_params* p, const void* q, const void* k_cache,
+                                          const void* v_cache, const void* const* k_up,
+                                          const void* const* v_up, float* out, float* lse,
+                                          int32_t* const* sel_up, int32_t* sel1, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+  clear_error();
+  LevelsPlan lp;
+  gsa_status_t s = plan_levels(p, &lp);
+  if (s != GSA_OK) return s;
+  if ((s = check_ptr(q, "q")) != GSA_OK || (s = check_ptr(k_cache, "k_cache")) != GSA_OK ||
+      (s = check_ptr(v_cache, "v_cache")) != GSA_OK || (s = check_ptr(out, "out")) != GSA_OK ||
+      (s = check_ptr(lse, "lse", true)) != GSA_OK || (s = check_ptr(sel1, "sel1", true)) != GSA_OK)
+    return s;
+  if (!k_up || !v_up) return fail(GSA_ERR_INVALID_ARG, "k_up / v_up is NULL");
+  static const char* kNames[] = {"k_up[0]", "k_up[1]", "k_up[2]", "k_up[3]", "k_up[4]"};
+  static const char* vNames[] = {"v_up[0]", "v_up[1]", "v_up[2]", "v_up[3]", "v_up[4]"};
+  static const char* sNames[] = {"sel_up[0]", "sel_up[1]", "sel_up[2]", "sel_up[3]", "sel_up[4]"};
+  for (int i = 0; i + 2 <= lp.L; ++i) {
+    const bool need = lp.Ml[i + 2] > 0;
+    if ((s = check_ptr(k_up[i], kNames[i], !need)) != GSA_OK || (s = check_ptr(v_up[i], vNames[i], !need)) != GSA_OK)
+      return s;
+    if (sel_up && (s = check_ptr(sel_up[i], sNames[i], true)) != GSA_OK) return s;
+  }
+  if ((s = check_workspace(workspace, workspace_bytes, lp.total)) != GSA_OK) return s;
+  return dispatch<LevelsRunner>(lp.base.dtype, lp.base.D, lp.base.g, lp, q, k_cache, v_cache, k_up, v_up, out,
+                                lse, sel_up, sel1, reinterpret_cast<char*>(workspace),
+                                reinterpret_cast<hipStream_t>(stream));
+}
+

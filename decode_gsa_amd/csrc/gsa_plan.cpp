@@ -314,6 +314,74 @@ gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* o) {
   return GSA_OK;
 }
 
+gsa_status_t plan_levels(const gsa_levels_params* p, LevelsPlan* o) {
+  if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->base.gist_set != GSA_GISTS_ALL)
+    return fail(GSA_ERR_UNSUPPORTED, "L-level decode attends every gist: base.gist_set must be 0");
+  if (p->n_levels < 2 || p->n_levels > GSA_MAX_LEVELS)
+    return fail(GSA_ERR_INVALID_ARG, "n_levels=%d outside [2, %d]", p->n_levels, GSA_MAX_LEVELS);
+  if (p->fanout < 2) return fail(GSA_ERR_INVALID_ARG, "fanout=%d must be >= 2", p->fanout);
+  gsa_status_t s = plan_decode(&p->base, &o->base);
+  if (s != GSA_OK) return s;
+  LevelsPlan h{};
+  h.base = o->base;
+  const DecodePlan& d = h.base;
+  const int L = p->n_levels, G = p->fanout;
+  h.L = L;
+  h.G = G;
+  h.Ml[1] = d.M;
+  h.kl[1] = d.k;
+  for (int l = 2; l <= L; ++l) {
+    h.Ml[l] = h.Ml[l - 1] / G;
+    h.kl[l] = p->topk_up[l - 2];
+  }
+  // candidates top-down
+  h.items[L] = h.Ml[L];
+  for (int l = L; l >= 1; --l) {
+    if (l < L) {
+      h.orphan0[l] = h.Ml[l + 1] * G;
+      h.items[l] = (int64_t)h.kl[l + 1] * G + (h.Ml[l] - h.orphan0[l]);
+    }
+    if (h.kl[l] < 0 || h.kl[l] > h.items[l])
+      return fail(GSA_ERR_INVALID_ARG, "k at level %d is %d, outside [0, %lld candidates]", l, h.kl[l],
+                  (long long)h.items[l]);
+    if (l >= 2 && h.kl[l] > kMaxTopk2)
+      return fail(GSA_ERR_UNSUPPORTED, "k at level %d is %d, above %d", l, h.kl[l], kMaxTopk2);
+    if (h.items[l] > (1 << 30)) return fail(GSA_ERR_UNSUPPORTED, "too many candidates at level %d", l);
+  }
+  const int64_t units = d.units;
+  h.NP = 0;
+  for (int l = L; l >= 1; --l) {
+    int32_t S = splits_for(h.items[l], units);
+    if (ceil_div(h.items[l], S) > kMaxTaskItems) S = (int32_t)ceil_div(h.items[l], kMaxTaskItems);
+    h.per_split[l] = h.items[l] > 0 ? ceil_div(h.items[l], S) : 0;
+    h.S[l] = h.items[l] > 0 ? (int32_t)ceil_div(h.items[l], h.per_split[l]) : 1;
+    h.NP += h.S[l];
+  }
+  h.tail_per_split = (int32_t)ceil_div(d.T, h.S[L]);
+  h.NP += d.S2;
+  size_t off = 0;
+  h.off_ctrl = off;
+  off = align_up(off + ctrl_bytes(units));
+  for (int l = 1; l <= L; ++l) {
+    h.score_stride[l] = (h.items[l] + 63) / 64 * 64;
+    h.off_scores[l] = off;
+    off = align_up(off + sizeof(float) * (size_t)units * (size_t)h.score_stride[l]);
+    if (l >= 2) {
+      h.sel_stride[l] = line_pad(h.kl[l] > 0 ? h.kl[l] : 1);
+      h.off_sel[l] = off;
+      off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)h.sel_stride[l]);
+    }
+  }
+  h.off_sel1 = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)d.sel_stride);
+  h.off_part = off;
+  off = align_up(off + sizeof(float) * (size_t)units * h.NP * (size_t)part_stride(d.g, d.D));
+  h.total = off;
+  *o = h;
+  return GSA_OK;
+}
+
 gsa_status_t plan_gist(const gsa_gist_params* p, PrefillPlan* o) {
   if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
   if (p->chunk < 1) return fail(GSA_ERR_INVALID_ARG, "chunk=%d must be >= 1", p->chunk);

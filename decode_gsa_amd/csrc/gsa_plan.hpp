@@ -117,6 +117,28 @@ struct HierPlan {
 
 gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* out);
 
+// L-level plan (split path only): pass L over the top level + tail, one
+// candidate pass per lower level, unfold. Index l = 1..L.
+struct LevelsPlan {
+  DecodePlan base;      // level 1 (k = k_1); base.S unused
+  int32_t L, G;
+  int64_t Ml[GSA_MAX_LEVELS + 1];        // gists at level l
+  int32_t kl[GSA_MAX_LEVELS + 1];        // chosen at level l
+  int64_t items[GSA_MAX_LEVELS + 1];     // items of pass l: M_L at the top, candidates below
+  int64_t orphan0[GSA_MAX_LEVELS + 1];   // l < L: first level-l gist no group covers (M_{l+1} G)
+  int32_t S[GSA_MAX_LEVELS + 1];         // workgroups per unit of pass l
+  int64_t per_split[GSA_MAX_LEVELS + 1];
+  int32_t tail_per_split;                // tail rows per top-level workgroup
+  int32_t NP;                            // sum of S + S2 (k_1 > 0)
+  size_t off_ctrl, off_part, off_sel1, total;
+  size_t off_scores[GSA_MAX_LEVELS + 1]; // scores of pass l (read by the pass below)
+  int64_t score_stride[GSA_MAX_LEVELS + 1];
+  size_t off_sel[GSA_MAX_LEVELS + 1];    // l >= 2: chosen ids of level l
+  int64_t sel_stride[GSA_MAX_LEVELS + 1];
+};
+
+gsa_status_t plan_levels(const gsa_levels_params* p, LevelsPlan* out);
+
 // Prefill plan.
 struct PrefillPlan {
   int32_t Hq, Hkv, g, D, C, k, W;

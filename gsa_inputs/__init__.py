@@ -29,6 +29,7 @@ __all__ = [
     "DecodeConfig", "HierConfig", "PrefillConfig", "GistConfig", "CONFIGS",
     "DecodeInputs", "HierInputs", "PrefillInputs",
     "make_decode", "make_hier", "make_prefill", "make_gist", "TokenStream", "make_token_stream",
+    "make_levels", "level_sizes",
     "raw_row", "gist_row", "n_rows",
 ]
 
@@ -544,4 +545,48 @@ def make_token_stream(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int
     return TokenStream(r(steps, batch, n_kv_heads), r(steps, batch, n_kv_heads),
                        r(nc, batch, n_kv_heads), r(nc, batch, n_kv_heads),
                        r(nc, batch, n_q_heads), r(batch, n_q_heads))
+
+
+# --------------------------------------------------------------------------
+# L-level decode inputs
+# --------------------------------------------------------------------------
+
+def level_sizes(n_gist: int, fanout: int, n_levels: int):
+    """[M_1, ..., M_L], M_l = floor(M_{l-1} / G)."""
+    sizes = [n_gist]
+    for _ in range(n_levels - 1):
+        sizes.append(sizes[-1] // fanout)
+    return sizes
+
+
+def make_levels(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_raw: int, n_gist: int,
+                chunk: int, fanout: int, n_levels: int, seed: int, device="cpu", dtype: str = "bf16",
+                values: str = "int"):
+    """q [B, Hq, D], the interleaved cache [B, Hkv, N + M, D] and the level
+    arrays [B, Hkv, M_l, D] for l = 2..L. values="int": entries uniform in
+    {-2..2} (exact group scores, many ties); "gauss": N(0, 1). Built in
+    slices so that long caches need no full-size float32 temporaries."""
+    g = _gen(device, seed)
+    D = head_dim
+
+    def draw(*shape):
+        out = torch.empty(*shape, D, dtype=_TORCH_DT[dtype], device=device)
+        flat = out.view(-1, D)
+        step = 1 << 20
+        for i in range(0, flat.shape[0], step):
+            n = min(step, flat.shape[0] - i)
+            if values == "int":
+                x = torch.randint(-2, 3, (n, D), generator=g, device=device).float()
+            else:
+                x = torch.randn(n, D, generator=g, device=device)
+            flat[i:i + n] = x.to(out.dtype)
+        return out
+    R = n_raw + n_gist
+    q = draw(batch, n_q_heads)
+    k = draw(batch, n_kv_heads, R)
+    v = draw(batch, n_kv_heads, R)
+    sizes = level_sizes(n_gist, fanout, n_levels)
+    k_up = [draw(batch, n_kv_heads, m) for m in sizes[1:]]
+    v_up = [draw(batch, n_kv_heads, m) for m in sizes[1:]]
+    return q, k, v, k_up, v_up
 

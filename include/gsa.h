@@ -153,6 +153,57 @@ gsa_status_t gsa_decode_hier(const gsa_hier_params* p, const void* q, const void
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * L-level decode (gists of gists of gists ...).
+ * Source: gist.science explainer, 'Hierarchical Extension (H-GSA)' and
+ * 'Coarse-to-Fine Selection' (multi-resolution access: the selection walks
+ * down from the coarsest summaries), slide deck slide 11.
+ * Level 1 is the interleaved cache's M gists; level l >= 2 holds
+ * M_l = floor(M_{l-1} / G) gists in its own [B, Hkv, M_l, D] array, gist i
+ * of level l summarising gists [i*G, (i+1)*G) of level l - 1. Top-down: the
+ * top level's gists are all candidates; each level's top-k_l candidates (by
+ * group score, ties to the smaller id) make their G children candidates of
+ * the level below, together with that level's M_l - M_{l+1}*G gists no group
+ * covers. Attention set: every top-level gist, every candidate of the
+ * levels below, the raw rows of the k_1 chosen chunks and the tail.
+ * L = 2 is gsa_decode_hier's rule.
+ * ---------------------------------------------------------------------- */
+#define GSA_MAX_LEVELS 6
+
+typedef struct {
+  gsa_decode_params base; /* level 1 and the step: base.topk = k_1 chunks
+                             unfolded; base.gist_set must be 0 */
+  int32_t n_levels;       /* L, 2 <= L <= GSA_MAX_LEVELS */
+  int32_t fanout;         /* G >= 2 */
+  int32_t topk_up[GSA_MAX_LEVELS - 1]; /* topk_up[i] = k_{i+2}, for levels
+                             2..L: 0 <= k_L <= M_L, and k_l at most the
+                             candidates of level l (k_{l+1}*G + M_l -
+                             M_{l+1}*G), k_l <= 1024; k_1 likewise */
+} gsa_levels_params;
+
+gsa_status_t gsa_decode_levels_workspace_size(const gsa_levels_params* p, size_t* bytes);
+
+/*
+ * q, k_cache, v_cache, out, lse: as gsa_decode (row_capacity honoured).
+ * k_up, v_up   host arrays of L - 1 device pointers: k_up[i] is level i+2's
+ *              [B, Hkv, M_{i+2}, D] key array (v_up its values), dense rows
+ * sel_up       host array of L - 1 device pointers or NULL: sel_up[i]
+ *              [B, Hkv, k_{i+2}] int32 gets level i+2's chosen ids
+ *              (ascending); an entry may be NULL
+ * sel1         [B, Hkv, k_1] int32 chosen chunk ids (ascending) or NULL
+ * workspace    as gsa_decode (zero-filled once; left zero by each call)
+ * Runs a pass over the top level and the tail, one pass per lower level
+ * (scoring and attending its candidates, selecting among the level above's
+ * scores), and the unfold: L + 1 launches (L when k_1 = 0).
+ * GSA_ERR_INVALID_ARG for out-of-range sizes or NULL arrays;
+ * GSA_ERR_UNSUPPORTED for g outside {1, 2, 4, 8}, D outside {64, 128}.
+ */
+gsa_status_t gsa_decode_levels(const gsa_levels_params* p, const void* q, const void* k_cache,
+                               const void* v_cache, const void* const* k_up,
+                               const void* const* v_up, float* out, float* lse,
+                               int32_t* const* sel_up, int32_t* sel1, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Causal block-sparse prefill of query positions [q_start, q_start + n_q)
  * of one sequence.
  * Source: gist.science explainer, 'Training Procedure: Selective Finetuning'
@@ -293,6 +344,8 @@ gsa_status_t gsa_cache_append(const gsa_append_params* p, const void* k_raw, con
  *   gsa_decode, other shapes: a gist pass, then an unfold pass when topk > 0;
  *   gsa_decode_hier: level-2 pass, level-1 candidate pass, unfold pass when
  *     topk1 > 0;
+ *   gsa_decode_levels: top-level pass, one pass per lower level, unfold pass
+ *     when k_1 > 0;
  *   gsa_prefill_blocksparse: selection when topk > 0, then attention.
  *   gsa_gist_prefill: attention; gsa_cache_append: one copy launch.
  * The library never creates, waits on or destroys the events. n = 0 disarms.

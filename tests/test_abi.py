@@ -47,6 +47,9 @@ int main(void) {
   printf("gsa_hier_params %zu\n", sizeof(gsa_hier_params));
   printf("gsa_prefill_params %zu\n", sizeof(gsa_prefill_params));
   printf("gsa_gist_params %zu\n", sizeof(gsa_gist_params));
+  printf("gsa_levels_params %zu\n", sizeof(gsa_levels_params));
+  printf("GSA_MAX_LEVELS %d\n", GSA_MAX_LEVELS);
+  F(gsa_levels_params, n_levels); F(gsa_levels_params, fanout); F(gsa_levels_params, topk_up);
   printf("gsa_append_params %zu\n", sizeof(gsa_append_params));
   F(gsa_decode_params, row_capacity); F(gsa_prefill_params, row_capacity);
   F(gsa_gist_params, n_raw); F(gsa_gist_params, n_gist); F(gsa_gist_params, m_start);
@@ -73,6 +76,8 @@ int main(void) {
     assert int(got["gsa_hier_params"]) == ctypes.sizeof(gsa.HierParams)
     assert int(got["gsa_prefill_params"]) == ctypes.sizeof(gsa.PrefillParams)
     assert int(got["gsa_gist_params"]) == ctypes.sizeof(gsa.GistParams)
+    assert int(got["gsa_levels_params"]) == ctypes.sizeof(gsa.LevelsParams)
+    assert int(got["GSA_MAX_LEVELS"]) == gsa.MAX_LEVELS
     assert int(got["gsa_append_params"]) == ctypes.sizeof(gsa.AppendParams)
     assert [int(got[f"GSA_GISTS_{n}"]) for n in ("ALL", "SELECTED", "NONE")] == \
         [gsa.GIST_SETS[n] for n in ("all", "selected", "none")]
@@ -81,7 +86,7 @@ int main(void) {
             t, m = key.split(".")
             cls = {"gsa_decode_params": gsa.DecodeParams, "gsa_hier_params": gsa.HierParams,
                    "gsa_prefill_params": gsa.PrefillParams, "gsa_gist_params": gsa.GistParams,
-                   "gsa_append_params": gsa.AppendParams}[t]
+                   "gsa_append_params": gsa.AppendParams, "gsa_levels_params": gsa.LevelsParams}[t]
             assert getattr(cls, m).offset == int(val), key
 
 
@@ -354,4 +359,55 @@ def test_cache_append_rejects_overlap(L):
     assert L.gsa_cache_append(ctypes.byref(p), FAKE + 3 * cache, FAKE + 4 * cache, None, None, FAKE,
                               FAKE + 256, None) == INVALID
     assert "overlap" in L.gsa_last_error().decode()
+
+
+# ---------------------------------------------------------------- L levels ---
+
+def good_levels(n_levels=3, fanout=4, topk_up=(6, 4), **kw):
+    # M = 640 gists: level sizes 640, 160, 40 (L = 3)
+    base = good_decode(n_raw=16 * 640, n_gist=640, topk=8, tail=64, **kw)
+    return gsa.levels_params(base, fanout, list(topk_up)[:n_levels - 1]) if n_levels >= 2 else None
+
+
+def levels_ws(L, p):
+    n = ctypes.c_size_t(0)
+    return L.gsa_decode_levels_workspace_size(ctypes.byref(p), ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("make,status", [
+    (lambda: good_levels(), OK),
+    (lambda: good_levels(n_levels=2, topk_up=(6,)), OK),
+    (lambda: good_levels(topk_up=(40, 40)), OK),                 # k_3 = M_3 = 40, k_2 = 160 candidates max
+    (lambda: good_levels(topk_up=(6, 41)), INVALID),             # k_3 > M_3
+    (lambda: good_levels(topk_up=(25, 6)), INVALID),             # 6 groups of 4 = 24 level-2 candidates
+    (lambda: good_levels(topk_up=(24, 6)), OK),
+    (lambda: good_levels(topk_up=(1, 6)), INVALID),              # k_1 = 8 > 4 level-1 candidates
+    (lambda: good_levels(topk_up=(2, 6)), OK),
+    (lambda: good_levels(fanout=1), INVALID),
+    (lambda: good_levels(gist_set=2, batch=128), UNSUPPORTED),
+    (lambda: gsa.LevelsParams(good_decode(), 1, 4), INVALID),    # one level
+    (lambda: gsa.LevelsParams(good_decode(), 7, 4), INVALID),    # above GSA_MAX_LEVELS
+    (lambda: gsa.levels_params(good_decode(n_raw=16 * 4096, n_gist=4096, topk=8, tail=64), 2,
+                               [1025]), UNSUPPORTED),            # k_2 above 1024
+    (lambda: gsa.levels_params(good_decode(n_raw=16 * 4096, n_gist=4096, topk=8, tail=64), 2,
+                               [30, 30, 30, 30, 30]), OK),       # six levels
+])
+def test_levels_param_validation(L, make, status):
+    st, n = levels_ws(L, make())
+    assert st == status, L.gsa_last_error()
+    if status == OK:
+        assert n > 0 and n % 256 == 0
+
+
+def test_levels_rejects_null_arrays(L):
+    p = good_levels()
+    st, need = levels_ws(L, p)
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    nul = (ctypes.c_void_p * 2)(FAKE, None)
+    call = lambda k, v: L.gsa_decode_levels(ctypes.byref(p), FAKE, FAKE, FAKE, k, v, FAKE, None, None, None,
+                                            FAKE, need, None)
+    assert call(None, arr) == INVALID
+    assert call(arr, nul) == INVALID and "v_up[1]" in L.gsa_last_error().decode()
+    assert L.gsa_decode_levels(ctypes.byref(p), FAKE, FAKE, FAKE, arr, arr, FAKE, None, None, None, FAKE,
+                               need - 256, None) == WORKSPACE
 
