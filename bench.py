@@ -16,6 +16,10 @@ query positions at the end of a 65536-token sequence, 32/8 heads, k=16, W=64).
 `--config gist_64k` times the cache-building step of a 65536-token prompt:
 gsa_cache_append of its raw and gist rows into an empty cache, then
 gsa_gist_prefill of its 4096 gist tokens.
+`--scaling` sweeps the context from 32K to 16M tokens (one sequence, Hq 32 /
+Hkv 8, C 16, k 16, T 64) over single-level, two-level and L-level decode
+(fanout 16, levels added until the top holds at most 256 gists) and prints
+one JSON line per (context, variant): time and algorithmic bytes per step.
 
 Cold-cache protocol without flushes: the benchmark keeps several copies
 ("layers") of the KV cache and step i reads layer i mod L, so a step's data was
@@ -664,6 +668,127 @@ def run_gist_bench(args):
     return res
 
 
+# --------------------------------------------------------------- scaling ---
+
+SCALING_N = [1 << 15, 1 << 17, 1 << 19, 1 << 21, 1 << 23, 1 << 24]
+
+
+def scaling_levels(M: int, G: int = 16, top: int = 256):
+    """Level sizes [M_1, ..., M_L]: levels are added until the top holds at
+    most `top` gists (at least two levels)."""
+    sizes = [M, M // G]
+    while sizes[-1] > top:
+        sizes.append(sizes[-1] // G)
+    return sizes
+
+
+def tail_free_rows(sel1, n_raw: int, tail: int, chunk: int) -> int:
+    """Raw rows of the chosen chunks that the tail does not already hold."""
+    tail0 = n_raw - tail
+    return int(sum(max(0, min(chunk, tail0 - int(m) * chunk)) for m in np.asarray(sel1).ravel()))
+
+
+def run_scaling(args):
+    import torch
+    import decode_gsa_amd as gsa
+    import gsa_inputs as gi
+    import oracle
+
+    dev = torch.device("cuda", 0)
+    B, Hq, Hkv, D, C, T, G = 1, 32, 8, 128, 16, 64, 16
+    units, row = B * Hkv, 2 * D * 2
+    k1, k_mid, k_top = 16, 8, 4
+    ns = [n for n in SCALING_N if n <= args.scaling_max]
+    for N in ns:
+        M = N // C
+        sizes = scaling_levels(M, G)
+        L = len(sizes)
+        topks = [k1] + [k_mid] * (L - 2) + [k_top]
+        cache_b = units * (N + M) * row
+        step_b = units * (M + T) * row
+        copies = int(max(1, min(16, math.ceil(2e9 / step_b), 100e9 // cache_b)))
+        log(f"[scaling] N={N}: levels {sizes}, {copies} cache copies ...")
+        sets = [gi.make_levels(B, Hq, Hkv, D, N, M, C, G, L, 7000 + N % 997 + i, device=dev, values="gauss")
+                for i in range(copies)]
+        base = gsa.decode_params(B, Hq, Hkv, D, N, M, C, k1, T)
+        ws = gsa.new_workspace(max(gsa.decode_workspace_size(base),
+                                   gsa.hier_workspace_size(gsa.hier_params(base, G, k_mid)),
+                                   gsa.levels_workspace_size(gsa.levels_params(base, G, topks[1:]))), dev)
+        stream = torch.cuda.current_stream(dev)
+        # unit (0, 0) on the host for the oracle spot checks
+        x0 = sets[0]
+        g = Hq // Hkv
+        qn = x0[0][0, :g].float().cpu().numpy()
+        Kn, Vn = x0[1][0, 0].float().cpu().numpy(), x0[2][0, 0].float().cpu().numpy()
+        upn = [(a[0, 0].float().cpu().numpy(), b[0, 0].float().cpu().numpy()) for a, b in zip(x0[3], x0[4])]
+
+        def flat(x):
+            return gsa.gsa_decode(x[0], x[1], x[2], chunk=C, topk=k1, tail=T, n_gist=M, workspace=ws,
+                                  stream=stream)
+
+        def two(x):
+            return gsa.gsa_decode_hier(x[0], x[1], x[2], x[3][0], x[4][0], chunk=C, fanout=G, topk1=k1,
+                                       topk2=k_mid, tail=T, n_gist=M, workspace=ws, stream=stream)
+
+        def many(x):
+            return gsa.gsa_decode_levels(x[0], x[1], x[2], x[3], x[4], chunk=C, fanout=G, topks=topks, tail=T,
+                                         n_gist=M, workspace=ws, stream=stream)
+
+        for name, fn in (("single-level", flat), ("two-level", two), (f"{L}-level", many)):
+            if name == "two-level" and L == 2:
+                continue
+            res0 = fn(sets[0])
+            torch.cuda.synchronize()
+            if name == "single-level":
+                sel1 = res0[2]
+                nb = units * (M + T) * row
+            elif name == "two-level":
+                sel1 = res0[3]
+                n_cand = k_mid * G + (M - (M // G) * G)
+                nb = units * ((M // G) + T + n_cand) * row
+            else:
+                sel1 = res0[2][0]
+                n_items = [k_mid * G + (sizes[l] - sizes[l + 1] * G) if l + 2 < L else
+                           k_top * G + (sizes[l] - sizes[l + 1] * G) for l in range(L - 1)]
+                nb = units * (sizes[-1] + T + sum(n_items)) * row
+            nb += tail_free_rows(to_cpu(sel1), N, T, C) * row
+            # oracle spot check on unit (0, 0)
+            if name == "single-level":
+                r = oracle.decode_unit(qn, Kn, Vn, n_raw=N, n_gist=M, chunk=C, topk=k1, tail=T)
+                ok_sel = np.array_equal(to_cpu(sel1)[0, 0], r["sel"])
+            elif name == "two-level":
+                r = oracle.decode_hier_unit(qn, Kn, Vn, upn[0][0], upn[0][1], n_raw=N, n_gist=M, chunk=C,
+                                            fanout=G, topk1=k1, topk2=k_mid, tail=T)
+                ok_sel = np.array_equal(to_cpu(sel1)[0, 0], r["sel1"])
+            else:
+                r = oracle.decode_levels_unit(qn, Kn, Vn, upn, n_raw=N, n_gist=M, chunk=C, fanout=G, topks=topks,
+                                              tail=T)
+                ok_sel = np.array_equal(to_cpu(sel1)[0, 0], r["sels"][0])
+            got = res0[0][0, :g].double().cpu().numpy()
+            rms = float(np.sqrt(np.mean(r["out"] ** 2)))
+            if not ok_sel or float(np.abs(got - r["out"]).max()) > 2e-3 * rms:
+                raise SystemExit(f"[scaling] N={N} {name}: differs from the oracle")
+            for i in range(3):
+                fn(sets[i % copies])
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                fn(sets[i % copies])
+            torch.cuda.synchronize()
+            ms = 1e3 * (time.perf_counter() - t0) / args.steps
+            lv, tk = {"single-level": ([M], [k1]), "two-level": ([M, M // G], [k1, k_mid])}.get(name, (sizes, topks))
+            line = {"context": N, "variant": name, "levels": lv, "topks": tk,
+                    "ms_per_step": ms, "alg_bytes_per_step": nb, "GB_s": nb / (ms / 1e3) / 1e9,
+                    "cache_copies": copies, "oracle_checked_unit": [0, 0]}
+            print(json.dumps(line), flush=True)
+        del sets, x0, Kn, Vn, upn
+        torch.cuda.empty_cache()
+
+
+def to_cpu(t):
+    return t.cpu().numpy()
+
+
 def hbm_stream_rates(reps: int = 8) -> dict:
     """Bandwidth of a plain torch device copy of 1 GiB (bytes read + written),
     reported next to the 8 TB/s specification as what a generic streaming
@@ -709,6 +834,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--scaling", action="store_true", help="decode time and bytes per step vs context length")
+    ap.add_argument("--scaling-max", type=int, default=1 << 24)
     ap.add_argument("--gist-set", default="all", choices=["all", "selected", "none"],
                     help="decode attention-set rule (slide 17 variants)")
     args = ap.parse_args()
@@ -723,6 +850,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         run_copy_calibration()
+        return
+    if args.scaling:
+        run_scaling(args)
         return
     import gsa_inputs as gi
     cfg = gi.CONFIGS[args.config]
