@@ -2072,6 +2072,156 @@ __global__ __launch_bounds__(kUW * 64) void unit_hier_kernel(UnitArgs a) {
     for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
 }
 
+// L-level decode, one workgroup per unit after the top level's stream launch:
+// choose among the top level's scores, then for each level below stream its
+// candidates (the chosen gists' children and the ungrouped gists: dense rows
+// of the level's array, gist rows of the interleaved cache at level 1) into
+// the wave states with their scores in LDS, choose among them, and finally
+// unfold the chosen chunks and merge. The level-1 part is unit_hier_kernel's.
+struct LevelArgs {
+  int32_t L, G;
+  const void* K[GSA_MAX_LEVELS + 1];     // l >= 2: [units][Ml[l]][D]
+  const void* V[GSA_MAX_LEVELS + 1];
+  int64_t Ml[GSA_MAX_LEVELS + 1];
+  int32_t kl[GSA_MAX_LEVELS + 1];
+  int32_t items[GSA_MAX_LEVELS + 1];     // candidates of level l < L
+  int32_t* sel_out[GSA_MAX_LEVELS + 1];  // l >= 2: [units][kl[l]] chosen ids, or null
+};
+
+template <int G>
+__global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, LevelArgs lv) {
+  __shared__ __attribute__((aligned(16))) UnitLds L;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hq = lane & 15, jg = lane >> 4;
+  const int unit = blockIdx.x;
+  const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
+  const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
+  bf16x8u qf[4];
+  {
+    const char* qb = reinterpret_cast<const char*>(a.q) + ((size_t)unit * G + (hq < G ? hq : 0)) * 256 + 16 * jg;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 v = hq < G ? load16(qb + 64 * ks) : make_uint4(0u, 0u, 0u, 0u);
+      qf[ks] = __builtin_bit_cast(bf16x8u, v);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) __asm__ volatile("" : "+v"(qf[ks]));
+  }
+  UState st;
+  st.m = kMinus;
+  st.l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4u{0.f, 0.f, 0.f, 0.f};
+  char* ring = L.u.ring[w][0];
+  const int Lv = lv.L, Gf = lv.G;
+  float* gsc = a.scores + (size_t)unit * a.score_stride;
+  // the top level: its chosen gists, ascending
+  unit_select<kUMaxSel / kThreads, false>(nullptr, (int)lv.Ml[Lv], lv.kl[Lv], a.s2 + (size_t)unit * a.s2_stride,
+                                          a.s2_stride, unit, L.sel2, L.u.sel.s, L.u.sel.t);
+  __syncthreads();
+  if (lv.sel_out[Lv])
+    for (int i = tid; i < lv.kl[Lv]; i += kUW * 64) lv.sel_out[Lv][(size_t)unit * lv.kl[Lv] + i] = L.sel2[i];
+  // the levels between: dense rows of each level's array
+  for (int l = Lv - 1; l >= 2; --l) {
+    UnitArgs b = a;
+    b.C = 0;                 // row of gist id = id
+    b.M = lv.Ml[l];
+    b.M2 = lv.Ml[l + 1];
+    b.k2 = lv.kl[l + 1];
+    b.G2 = Gf;
+    const char* Kl = reinterpret_cast<const char*>(lv.K[l]) + (size_t)unit * lv.Ml[l] * 256;
+    const char* Vl = reinterpret_cast<const char*>(lv.V[l]) + (size_t)unit * lv.Ml[l] * 256;
+    const int nc = lv.items[l];
+    const int perc = (nc + kUW - 1) / kUW;
+    unit_stream<kUKCand>(Kl, Vl, min(nc, w * perc), min(nc, (w + 1) * perc), b, qf, st, ring, L.scores, L.sel2);
+    __syncthreads();   // every candidate score is in LDS, every ring idle
+    const int k = lv.kl[l];
+    unit_select<kUMaxGist / kThreads, true>(L.scores, nc, k, gsc, a.score_stride, unit, L.sel, L.u.sel.s,
+                                            L.u.sel.t);
+    __syncthreads();
+    // candidate index -> id (candidates are in id order), then it is the
+    // parent list of the level below
+    int id = 0;
+    if (tid < k) {
+      const int c = L.sel[tid], kg = lv.kl[l + 1] * Gf;
+      id = c < kg ? L.sel2[c / Gf] * Gf + c % Gf : (int)(lv.Ml[l + 1] * Gf) + (c - kg);
+    }
+    __syncthreads();
+    if (tid < k) {
+      L.sel2[tid] = id;
+      if (lv.sel_out[l]) lv.sel_out[l][(size_t)unit * k + tid] = id;
+    }
+    __syncthreads();
+  }
+  // level 1: gist rows of the interleaved cache, then the chunks
+  UnitArgs b = a;
+  b.M2 = lv.Ml[2];
+  b.k2 = lv.kl[2];
+  b.G2 = Gf;
+  const int nc = lv.items[1];
+  const int perc = (nc + kUW - 1) / kUW;
+  unit_stream<kUKCand>(Kb, Vb, min(nc, w * perc), min(nc, (w + 1) * perc), b, qf, st, ring, L.scores, L.sel2);
+  if (a.k > 0) {
+    __syncthreads();
+    unit_select<kUMaxGist / kThreads, true>(L.scores, nc, a.k, gsc, a.score_stride, unit, L.sel, L.u.sel.s,
+                                            L.u.sel.t);
+    __syncthreads();
+    if (tid < a.k) {
+      const int c = L.sel[tid], kg = b.k2 * Gf;
+      L.sel[tid] = c < kg ? L.sel2[c / Gf] * Gf + c % Gf : (int)(b.M2 * Gf) + (c - kg);
+    }
+    __syncthreads();
+    const int items = a.k * a.C;
+    const int per2 = (items + kUW - 1) / kUW;
+    unit_stream<kUKUnfold>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
+                           L.sel);
+  }
+  float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
+  unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)a.S * a.part_stride);
+  done_stores();
+  __syncthreads();
+  merge_unit<128, G>(part_u, a.S + 1, (uint32_t)a.part_stride, a.out + (size_t)unit * G * 128,
+                     a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
+  if (a.sel)
+    for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
+}
+
+template <int G>
+gsa_status_t run_unit_levels(const LevelsPlan& lp, const void* q, const void* K, const void* V,
+                             const void* const* Ku, const void* const* Vu, float* out, float* lse,
+                             int32_t* const* sel_up, int32_t* sel1, char* ws, hipStream_t st) {
+  const DecodePlan& pl = lp.base;
+  const int Lv = lp.L;
+  UnitArgs u{};
+  u.q = q; u.K = K; u.V = V; u.out = out; u.lse = lse; u.sel = pl.k > 0 ? sel1 : nullptr;
+  u.scores = reinterpret_cast<float*>(ws + lp.off_scores[1]); u.score_stride = lp.score_stride[1];
+  u.R = pl.R; u.N = pl.N; u.M = pl.M; u.C = pl.C; u.k = pl.k; u.T = pl.T;
+  u.scale_log2 = pl.scale * kLog2e; u.score_mul = pl.scale / G;
+  u.S = lp.unit_S; u.S2 = 0; u.NP = lp.NP; u.part_stride = part_stride(G, 128);
+  u.part = reinterpret_cast<float*>(ws + lp.off_part);
+  u.cnt = nullptr;
+  // the stream launch sees the top level as its "level 2"
+  u.K2 = Ku[Lv - 2]; u.V2 = Vu[Lv - 2]; u.M2 = lp.Ml[Lv]; u.G2 = lp.G; u.k2 = lp.kl[Lv]; u.n_cand = 0;
+  u.s2 = reinterpret_cast<float*>(ws + lp.off_scores[Lv]); u.s2_stride = lp.score_stride[Lv];
+  u.sel2 = nullptr;
+  LevelArgs lv{};
+  lv.L = Lv; lv.G = lp.G;
+  for (int l = 1; l <= Lv; ++l) {
+    lv.Ml[l] = lp.Ml[l];
+    lv.kl[l] = lp.kl[l];
+    lv.items[l] = (int32_t)lp.items[l];
+    if (l >= 2) {
+      lv.K[l] = Ku[l - 2];
+      lv.V[l] = Vu[l - 2];
+      lv.sel_out[l] = sel_up && lp.kl[l] > 0 ? sel_up[l - 2] : nullptr;
+    }
+  }
+  prof_begin_call();
+  prof_launch((unit_kernel<G, true>), dim3(pl.units * lp.unit_S), dim3(kUW * 64), 0, st, u);
+  prof_launch((unit_levels_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
+  return launch_status("gsa_decode_levels launch");
+}
+
 template <int G>
 gsa_status_t run_unit_hier(const HierPlan& hp, const void* q, const void* K, const void* V, const void* K2,
                            const void* V2, float* out, float* lse, int32_t* sel2, int32_t* sel1, char* ws,
@@ -2334,6 +2484,16 @@ extern "C" gsa_status_t gsa_decode_levels(const gsa_levels_params* p, const void
     if (sel_up && (s = check_ptr(sel_up[i], sNames[i], true)) != GSA_OK) return s;
   }
   if ((s = check_workspace(workspace, workspace_bytes, lp.total)) != GSA_OK) return s;
+  if (lp.unit_S > 0) {
+    char* ws = reinterpret_cast<char*>(workspace);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    switch (lp.base.g) {
+      case 1: return run_unit_levels<1>(lp, q, k_cache, v_cache, k_up, v_up, out, lse, sel_up, sel1, ws, hs);
+      case 2: return run_unit_levels<2>(lp, q, k_cache, v_cache, k_up, v_up, out, lse, sel_up, sel1, ws, hs);
+      case 4: return run_unit_levels<4>(lp, q, k_cache, v_cache, k_up, v_up, out, lse, sel_up, sel1, ws, hs);
+      case 8: return run_unit_levels<8>(lp, q, k_cache, v_cache, k_up, v_up, out, lse, sel_up, sel1, ws, hs);
+    }
+  }
   return dispatch<LevelsRunner>(lp.base.dtype, lp.base.D, lp.base.g, lp, q, k_cache, v_cache, k_up, v_up, out,
                                 lse, sel_up, sel1, reinterpret_cast<char*>(workspace),
                                 reinterpret_cast<hipStream_t>(stream));

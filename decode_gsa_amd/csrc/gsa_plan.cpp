@@ -360,11 +360,37 @@ gsa_status_t plan_levels(const gsa_levels_params* p, LevelsPlan* o) {
   }
   h.tail_per_split = (int32_t)ceil_div(d.T, h.S[L]);
   h.NP += d.S2;
+  h.unit_S = 0;
+  {
+    bool ok = d.dtype == GSA_BF16 && d.D == 128 && d.k <= kFastSelect && h.Ml[L] >= 1 && h.Ml[L] <= kUnitMaxSel &&
+              d.R < ((int64_t)1 << 31);
+    int64_t rows = (int64_t)d.k * d.C + h.Ml[L] + d.T;
+    for (int l = 1; l < L; ++l) {
+      ok = ok && h.kl[l + 1] <= kFastSelect && h.items[l] <= kUnitMaxGist;
+      rows += h.items[l];
+    }
+    ok = ok && rows < ((int64_t)1 << 31);
+    if (ok) {
+      const int64_t items = h.Ml[L] + d.T;
+      int64_t s = ceil_div(kUnitMinWGs, units);
+      if (s < ceil_div(items, kUnitWgItems)) s = ceil_div(items, kUnitWgItems);
+      if (ceil_div(items, s) < 64) s = ceil_div(items, 64);
+      if (s < 1) s = 1;
+      if (s <= kUnitMaxSplits) {
+        h.unit_S = (int32_t)s;
+        if (h.NP < h.unit_S + 1) h.NP = h.unit_S + 1;   // top-level stream partials + the descent's
+      }
+    }
+  }
   size_t off = 0;
   h.off_ctrl = off;
   off = align_up(off + ctrl_bytes(units));
   for (int l = 1; l <= L; ++l) {
     h.score_stride[l] = (h.items[l] + 63) / 64 * 64;
+    // the one-workgroup-per-unit descent reuses level 1's region for every
+    // lower level's selection fallback
+    if (l == 1)
+      for (int j = 2; j < L; ++j) h.score_stride[1] = std::max(h.score_stride[1], (h.items[j] + 63) / 64 * 64);
     h.off_scores[l] = off;
     off = align_up(off + sizeof(float) * (size_t)units * (size_t)h.score_stride[l]);
     if (l >= 2) {

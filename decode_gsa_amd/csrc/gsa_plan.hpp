@@ -135,6 +135,11 @@ struct LevelsPlan {
   int64_t score_stride[GSA_MAX_LEVELS + 1];
   size_t off_sel[GSA_MAX_LEVELS + 1];    // l >= 2: chosen ids of level l
   int64_t sel_stride[GSA_MAX_LEVELS + 1];
+  // one-workgroup-per-unit path (bf16, D = 128, every k <= 64, at most 16384
+  // top-level gists and 4096 candidates per lower level): workgroups per unit
+  // over the top level and the tail, then one workgroup per unit for the
+  // descent; 0 when the per-level passes run instead
+  int32_t unit_S;
 };
 
 gsa_status_t plan_levels(const gsa_levels_params* p, LevelsPlan* out);

@@ -36,6 +36,7 @@ def run_levels(gsa, c, seed, units=None, values="int"):
                                      values=values)
     out, lse, sels = gsa.gsa_decode_levels(q, k, v, ku, vu, chunk=C, fanout=G, topks=topks, tail=T, n_gist=M)
     torch.cuda.synchronize()
+    c["_launches"] = gsa.gsa_profile_marks() - 1
     g = Hq // Hkv
     us = [(b, j) for b in range(B) for j in range(Hkv)] if units is None else units
     got, ref, got_l, ref_l = [], [], [], []
@@ -71,14 +72,25 @@ CASES = [
     dict(B=1, Hq=8, Hkv=2, D=128, C=16, M=650, r=9, G=4, topks=[2, 2, 0], T=9),
     # every candidate chosen at every level
     dict(B=1, Hq=4, Hkv=1, D=128, C=4, M=100, r=0, G=3, topks=[100, 33, 11], T=0),
+    # bf16 with k_1 > 64: the per-level passes
+    dict(B=2, Hq=8, Hkv=2, D=128, C=16, M=640, r=5, G=4, topks=[70, 20, 8], T=64),
 ]
 
 
-@pytest.mark.parametrize("c", CASES, ids=[f"case{i}" for i in range(len(CASES))])
-def test_levels_small(gsa, c):
+# bf16, D = 128, every k <= 64: the top-level stream launch + one workgroup
+# per unit for the descent (2 launches); otherwise one pass per level + unfold
+FUSED = {0, 2, 3, 4, 5}
+
+
+@pytest.mark.parametrize("i", range(len(CASES)), ids=[f"case{i}" for i in range(len(CASES))])
+def test_levels_small(gsa, i):
+    c = dict(CASES[i])
     say(f"levels {c}")
-    err, _ = run_levels(gsa, c, 6000 + CASES.index(c))
-    say(f"  max err / rms = {err:.2e}")
+    err, _ = run_levels(gsa, c, 6000 + i)
+    L = len(c["topks"])
+    want = 2 if i in FUSED else L + (1 if c["topks"][0] > 0 else 0)
+    say(f"  max err / rms = {err:.2e}, {c['_launches']} launches")
+    assert c["_launches"] == want
 
 
 def test_levels_gaussian_values(gsa):
@@ -92,7 +104,7 @@ def test_levels_gaussian_values(gsa):
 def test_levels_capacity_and_repeat(gsa):
     """A cache with spare rows gives bit-identical results; so does a second
     call with the same (reused) workspace."""
-    c = CASES[0]
+    c = dict(CASES[0])
     say("levels capacity")
     _, (q, k, v, ku, vu, out, lse, sels, N) = run_levels(gsa, c, 6200)
     big_k = torch.zeros(c["B"], c["Hkv"], k.shape[2] + 19, c["D"], dtype=k.dtype, device="cuda")
