@@ -19,7 +19,9 @@ gsa_gist_prefill of its 4096 gist tokens.
 `--scaling` sweeps the context from 32K to 16M tokens (one sequence, Hq 32 /
 Hkv 8, C 16, k 16, T 64) over single-level, two-level and L-level decode
 (fanout 16, levels added until the top holds at most 256 gists) and prints
-one JSON line per (context, variant): time and algorithmic bytes per step.
+one JSON line per (context, variant): wall time per step, the device time of
+a call (event hook: first kernel's start to last kernel's end) and the
+algorithmic bytes per step.
 
 Cold-cache protocol without flushes: the benchmark keeps several copies
 ("layers") of the KV cache and step i reads layer i mod L, so a step's data was
@@ -776,9 +778,24 @@ def run_scaling(args):
                 fn(sets[i % copies])
             torch.cuda.synchronize()
             ms = 1e3 * (time.perf_counter() - t0) / args.steps
+            # device time of a call: the library's event hook, first kernel's
+            # start to last kernel's end
+            n_marks = gsa.gsa_profile_marks()
+            ev = HipEvents(n_marks * args.steps)
+            try:
+                for i in range(args.steps):
+                    gsa.gsa_profile_events(ev.ev[i * n_marks:(i + 1) * n_marks])
+                    fn(sets[i % copies])
+                gsa.gsa_profile_events([])
+                torch.cuda.synchronize()
+                dev_ms = float(np.mean([ev.ms(i * n_marks, (i + 1) * n_marks - 1) for i in range(args.steps)]))
+            finally:
+                gsa.gsa_profile_events([])
+                ev.close()
             lv, tk = {"single-level": ([M], [k1]), "two-level": ([M, M // G], [k1, k_mid])}.get(name, (sizes, topks))
             line = {"context": N, "variant": name, "levels": lv, "topks": tk,
-                    "ms_per_step": ms, "alg_bytes_per_step": nb, "GB_s": nb / (ms / 1e3) / 1e9,
+                    "ms_per_step": ms, "device_ms_per_call": dev_ms, "launches": n_marks - 1,
+                    "alg_bytes_per_step": nb, "GB_s": nb / (ms / 1e3) / 1e9,
                     "cache_copies": copies, "oracle_checked_unit": [0, 0]}
             print(json.dumps(line), flush=True)
         del sets, x0, Kn, Vn, upn
