@@ -7,6 +7,7 @@ built, every call raises (there is no fallback path).
 
 Entry points (same names as the C ABI):
   gsa_decode(q, k_cache, v_cache, chunk=, topk=, tail=, ...)
+  gsa_decode_varlen(q, k_cache, v_cache, seq_n_raw=, seq_n_gist=, chunk=, topk=, tail=, ...)
   gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, chunk=, fanout=, topk1=, topk2=, tail=, ...)
   gsa_decode_levels(q, k_cache, v_cache, k_up, v_up, chunk=, fanout=, topks=, tail=, ...)
   gsa_prefill_blocksparse(q, k_cache, v_cache, chunk=, topk=, window=, q_start=, ...)
@@ -30,7 +31,7 @@ __all__ = [
     "decode_workspace_size", "hier_workspace_size", "prefill_workspace_size", "new_workspace",
     "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse", "gsa_profile_events",
     "gsa_profile_marks", "topk_for_budget", "GIST_SETS", "gsa_gist_prefill", "gsa_cache_append",
-    "gsa_decode_levels", "levels_workspace_size",
+    "gsa_decode_levels", "levels_workspace_size", "gsa_decode_varlen", "check_seq_lens",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -43,7 +44,7 @@ EXPORTED_SYMBOLS = (
     "gsa_prefill_workspace_size", "gsa_prefill_blocksparse",
     "gsa_profile_events", "gsa_profile_marks", "gsa_status_string", "gsa_last_error",
     "gsa_topk_for_budget", "gsa_gist_prefill", "gsa_cache_append",
-    "gsa_decode_levels_workspace_size", "gsa_decode_levels",
+    "gsa_decode_levels_workspace_size", "gsa_decode_levels", "gsa_decode_varlen", "gsa_check_seq_lens",
 )
 MAX_LEVELS = 6
 
@@ -115,6 +116,9 @@ def lib() -> ctypes.CDLL:
         L.gsa_decode_levels_workspace_size.argtypes = [P(LevelsParams), P(_sz)]
         L.gsa_decode_levels.argtypes = [P(LevelsParams), _vp, _vp, _vp, P(_vp), P(_vp), _vp, _vp,
                                          P(_vp), _vp, _vp, _sz, _vp]
+        L.gsa_decode_varlen.argtypes = [P(DecodeParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _sz, _vp]
+        L.gsa_check_seq_lens.argtypes = [P(DecodeParams), P(_c_i32), P(_c_i32)]
         L.gsa_gist_prefill.argtypes = [P(GistParams), _vp, _vp, _vp, _vp, _vp]
         L.gsa_cache_append.argtypes = [P(AppendParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.gsa_profile_events.argtypes = [P(_vp), _c_i32]
@@ -321,6 +325,60 @@ def gsa_decode(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int,
     _check(lib().gsa_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
                             _ptr(lse), _ptr(sel_idx) if topk > 0 else None, _ptr(ws),
                             _nbytes(ws), _stream(stream, dev)), "gsa_decode")
+    return out, lse, sel_idx
+
+
+def check_seq_lens(p: DecodeParams, seq_n_raw, seq_n_gist) -> None:
+    """Host check of per-sequence lengths against a call's parameters."""
+    n = (_c_i32 * p.batch)(*[int(x) for x in seq_n_raw])
+    m = (_c_i32 * p.batch)(*[int(x) for x in seq_n_gist])
+    _check(lib().gsa_check_seq_lens(ctypes.byref(p), n, m), "gsa_check_seq_lens")
+
+
+def gsa_decode_varlen(q, k_cache, v_cache, *, seq_n_raw, seq_n_gist, chunk: int, topk: int,
+                      tail: int, n_raw: Optional[int] = None, n_gist: Optional[int] = None,
+                      scale: float = 0.0, out=None, lse=None, sel_idx=None, workspace=None,
+                      stream=None, want_lse: bool = True, want_sel: bool = True):
+    """Single-level decode of sequences of different lengths. Caches
+    [B,Hkv,cap,D]: sequence b uses its first seq_n_raw[b] + seq_n_gist[b] rows.
+
+    seq_n_raw / seq_n_gist: host sequences (checked with gsa_check_seq_lens,
+    then copied to the device) or device int32 tensors [B], used as given
+    (then n_raw= and n_gist=, the batch's largest values, are required).
+    Returns (out, lse, sel) as gsa_decode.
+    """
+    import torch
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    on_dev = isinstance(seq_n_raw, torch.Tensor) and seq_n_raw.is_cuda
+    if on_dev:
+        if n_raw is None or n_gist is None:
+            raise ValueError("device length arrays need n_raw= and n_gist= (the batch's largest)")
+        sn, sm = seq_n_raw, seq_n_gist
+    else:
+        hn = [int(x) for x in (seq_n_raw.tolist() if hasattr(seq_n_raw, "tolist") else seq_n_raw)]
+        hm = [int(x) for x in (seq_n_gist.tolist() if hasattr(seq_n_gist, "tolist") else seq_n_gist)]
+        if len(hn) != B or len(hm) != B:
+            raise ValueError("one length per sequence")
+        n_raw = max(hn) if n_raw is None else n_raw
+        n_gist = max(hm) if n_gist is None else n_gist
+    p = decode_params(B, Hq, Hkv, D, n_raw, n_gist, chunk, topk, tail, scale, _dtype_code(q),
+                      0, cap)
+    if not on_dev:
+        check_seq_lens(p, hn, hm)
+        sn = torch.tensor(hn, dtype=torch.int32, device=dev)
+        sm = torch.tensor(hm, dtype=torch.int32, device=dev)
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    if sel_idx is None and want_sel:
+        sel_idx = torch.empty(B, Hkv, max(topk, 0), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace, decode_workspace_size(p), dev)
+    _check(lib().gsa_decode_varlen(ctypes.byref(p), _ptr(sn), _ptr(sm), _ptr(q), _ptr(k_cache),
+                                   _ptr(v_cache), _ptr(out), _ptr(lse),
+                                   _ptr(sel_idx) if topk > 0 else None, _ptr(ws), _nbytes(ws),
+                                   _stream(stream, dev)), "gsa_decode_varlen")
     return out, lse, sel_idx
 
 

@@ -120,6 +120,33 @@ __device__ __forceinline__ int32_t map_id(const IdMap& im, int unit, int32_t i) 
                 : (int32_t)(im.orphan0 + (i - kg));
 }
 
+// Variable-length batches: sequence b holds seq_n[b] raw tokens and
+// seq_m[b] gists (device arrays); N and M of the call are the batch's
+// largest. A sequence whose pair breaks the rules a call checks for uniform
+// lengths (1 <= n <= N, k <= m <= M, m C <= n <= m C + C, n - m C <= T <= n)
+// is run with (N, M) instead: every row read stays inside its slab.
+struct SeqLens {
+  const int32_t* n;       // [B] or null (every sequence has N, M)
+  const int32_t* m;
+  int32_t Hkv;
+  int32_t k;              // the call's top-k (a sequence needs k <= m)
+};
+
+__device__ __forceinline__ void unit_lengths(const SeqLens& sl, int unit, int64_t N, int64_t M, int32_t C,
+                                             int32_t T, int64_t* n_out, int64_t* m_out) {
+  *n_out = N;
+  *m_out = M;
+  if (sl.n == nullptr) return;
+  const int k = sl.k;
+  const int b = unit / sl.Hkv;
+  const int64_t n = sl.n[b], m = sl.m[b];
+  const bool ok = n >= 1 && n <= N && m >= k && m <= M && m * C <= n && n <= m * C + C && n - m * C <= T && T <= n;
+  if (ok) {
+    *n_out = n;
+    *m_out = m;
+  }
+}
+
 // Stream items [i0, i1) of one unit through the online softmax. row_of(i)
 // gives the cache row of item i; with CAN_SKIP it may return -1 to skip the
 // item. When score_out is set (LDS), the group score of item i goes to
@@ -886,6 +913,7 @@ struct GistArgs {
   int32_t* sel_ws;        // [units][sel_stride] (k > kSelLdsMax: the selection lives here)
   int64_t sel_stride;
   int32_t* sel_out;       // [units][k] or null
+  SeqLens seq;            // single-level decode: per-sequence lengths
 };
 
 template <int D, int G>
@@ -930,9 +958,15 @@ void gist_kernel(GistArgs a) {
   load_q<BF16, D, G>(a.q, unit, qv);
   State<BF16, G> st;
   init_state<BF16, G>(st);
+  // this unit's lengths (single-level decode: the items are its gists)
+  int64_t uN = a.N, uM = a.M, n_items = a.n_items;
+  if (a.seq.n != nullptr) {
+    unit_lengths(a.seq, unit, a.N, a.M, a.C, a.T, &uN, &uM);
+    n_items = uM;
+  }
   const size_t ub = (size_t)unit * (size_t)a.unit_rows * Gm::ROW_BYTES;
   const int64_t i0 = (int64_t)split * a.per_task;
-  const int64_t i1 = i0 + a.per_task < a.n_items ? i0 + a.per_task : a.n_items;
+  const int64_t i1 = i0 + a.per_task < n_items ? i0 + a.per_task : (i0 < n_items ? n_items : i0);
   stream_rows<BF16, D, G, false>(reinterpret_cast<const char*>(a.K) + ub,
                                  reinterpret_cast<const char*>(a.V) + ub, i0, i1,
                                  [&](int64_t i) { return map_row(rm, 0, i); }, qv, st,
@@ -942,7 +976,7 @@ void gist_kernel(GistArgs a) {
   const int64_t t1 = t0 + a.tail_per_task < a.T ? t0 + a.tail_per_task : a.T;
   if (t0 < t1) {
     const size_t tb = (size_t)unit * (size_t)a.tail_unit_rows * Gm::ROW_BYTES;
-    const int64_t N = a.N, M = a.M;
+    const int64_t N = uN, M = uM;
     const int32_t C = a.C, T = a.T;
     stream_rows<BF16, D, G, false>(reinterpret_cast<const char*>(a.Kt) + tb,
                                    reinterpret_cast<const char*>(a.Vt) + tb, t0, t1,
@@ -955,6 +989,7 @@ void gist_kernel(GistArgs a) {
     // workgroup or the next launch reads them)
     float* so = a.scores + (size_t)unit * a.score_stride + i0;
     for (int64_t i = tid; i < i1 - i0; i += kThreads) st_coh(so + i, lds.scores[i]);
+
   }
   float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
   write_partial<BF16, D, G>(st, part_u + (size_t)(a.part_base + split) * a.part_stride, lds.u.part, false);
@@ -965,7 +1000,7 @@ void gist_kernel(GistArgs a) {
     __syncthreads();   // LDS changes role: partial merge -> selection
     const int k = a.fuse_k;
     int32_t* us = a.sel_ws + (size_t)unit * a.sel_stride;
-    unit_topk(a.scores + (size_t)unit * a.score_stride, (int)a.n_items, k, IdMap{nullptr, 0, 0, 0, 0}, unit, us,
+    unit_topk(a.scores + (size_t)unit * a.score_stride, (int)n_items, k, IdMap{nullptr, 0, 0, 0, 0}, unit, us,
               lds.u.sel.s, lds.u.sel.t);
     __syncthreads();
     if (a.sel_out)
@@ -1004,6 +1039,7 @@ struct UnfoldArgs {
   float* lse;
   uint32_t* cnt;
   float scale_log2;
+  SeqLens seq;            // per-sequence lengths (single-level decode)
 };
 
 template <int D, int G>
@@ -1027,9 +1063,12 @@ __global__ __launch_bounds__(kThreads) void unfold_kernel(UnfoldArgs a) {
   const int unit = blockIdx.x / a.tasks, split = blockIdx.x % a.tasks;
   const bool in_lds = a.k <= kSelLdsMax;
   int32_t* us = in_lds ? lds.sel : a.sel_ws + (size_t)unit * a.sel_stride;
+  int64_t uN = a.N, uM = a.M;
+  unit_lengths(a.seq, unit, a.N, a.M, a.C, a.T, &uN, &uM);
   if (a.scores != nullptr) {
     // make the unit's selection from the previous pass's scores
-    unit_topk(a.scores + (size_t)unit * a.score_stride, a.n_cand, a.k, a.im, unit, us, lds.u.sel.s, lds.u.sel.t);
+    const int n_cand = a.seq.n != nullptr ? (int)uM : a.n_cand;
+    unit_topk(a.scores + (size_t)unit * a.score_stride, n_cand, a.k, a.im, unit, us, lds.u.sel.s, lds.u.sel.t);
     __syncthreads();
     if (split == 0 && a.sel_out)
       for (int i = tid; i < a.k; i += kThreads) a.sel_out[(size_t)unit * a.k + i] = us[i];
@@ -1048,7 +1087,7 @@ __global__ __launch_bounds__(kThreads) void unfold_kernel(UnfoldArgs a) {
   const int64_t i1 = i0 + a.per_task < a.n_items ? i0 + a.per_task : a.n_items;
   // 32-bit index math: items < 2^30
   const uint32_t C = (uint32_t)a.C;
-  const int64_t M = a.M, tail0 = a.N - a.T;
+  const int64_t M = uM, tail0 = uN - a.T;
   auto row_of = [&](int64_t i64) -> int64_t {
     const uint32_t i = (uint32_t)i64;
     const uint32_t ci = i / C, j = i - ci * C;
@@ -1101,6 +1140,7 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
   g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
   g.fuse_k = pl.k;
   g.sel_ws = wsel; g.sel_stride = pl.sel_stride; g.sel_out = sel_idx;
+  g.seq = SeqLens{pl.seq_n, pl.seq_m, pl.Hkv, pl.k};
   prof_begin_call();
   prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st, g);
   if (pl.k > 0) {
@@ -1114,6 +1154,7 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
     u.out = out; u.lse = lse;
     u.cnt = ctrl_of(ws, pl.off_ctrl, 2);
     u.scale_log2 = pl.scale * kLog2e;
+    u.seq = g.seq;
     prof_launch((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
   }
   return launch_status("gsa_decode launch");
@@ -1550,6 +1591,7 @@ struct UnitArgs {
   int32_t* sel2;
   // which gists the attention set holds: 0 all, 1 the selected chunks', 2 none
   int32_t gist_set;
+  SeqLens seq;            // per-sequence lengths (single-level decode)
 };
 
 struct UnitLds {
@@ -1851,15 +1893,17 @@ __device__ __forceinline__ void unit_combine(UnitLds& L, const UState& st, int w
 // HIER: the first launch of two-level decode -- the level-2 gists (their own
 // arrays) and the tail; every workgroup hands its partial state and level-2
 // scores to unit_hier_kernel.
-template <int G, bool HIER, bool SETS = false>
-__global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
+template <int G, bool HIER, bool SETS = false, bool VARLEN = false>
+__global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
   __shared__ __attribute__((aligned(16))) UnitLds L;
+  UnitArgs a = args;
   // the wave index as a scalar: each wave's item ranges and trip counts are
   // then uniform, and the row loops branch on scalars
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq = lane & 15, jg = lane >> 4;
   const int S = a.S;
   const int unit = blockIdx.x / S, split = blockIdx.x - unit * S;
+  if constexpr (VARLEN) unit_lengths(args.seq, unit, args.N, args.M, args.C, args.T, &a.N, &a.M);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
   const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
   // query fragments: lane (h, j) holds q_h[32 ks + 8 j .. +8], zero past g heads
@@ -1961,13 +2005,15 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs a) {
 // launch wrote (every workgroup of the unit makes the same one), streams
 // share p of the chosen chunks' raw rows, and hands its partial state on; the
 // unit's last workgroup merges the S stream and S2 unfold partials.
-template <int G>
-__global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs a) {
+template <int G, bool VARLEN = false>
+__global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   __shared__ __attribute__((aligned(16))) UnitLds L;
+  UnitArgs a = args;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq = lane & 15, jg = lane >> 4;
   const int S2 = a.S2;
   const int unit = blockIdx.x / S2, part = blockIdx.x - unit * S2;
+  if constexpr (VARLEN) unit_lengths(args.seq, unit, args.N, args.M, args.C, args.T, &a.N, &a.M);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
   const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
   bf16x8u qf[4];
@@ -2256,12 +2302,21 @@ gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const 
   u.gist_set = pl.gist_set;
   u.part = reinterpret_cast<float*>(ws + pl.off_part);
   u.cnt = ctrl_of(ws, pl.off_ctrl, 0);
+  u.seq = SeqLens{pl.seq_n, pl.seq_m, pl.Hkv, pl.k};
   prof_begin_call();
+  const bool varlen = pl.seq_n != nullptr;
   if (pl.gist_set != GSA_GISTS_ALL)
     prof_launch((unit_kernel<G, false, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+  else if (varlen)
+    prof_launch((unit_kernel<G, false, false, true>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0, st, u);
   else
     prof_launch((unit_kernel<G, false>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0, st, u);
-  if (pl.unit_S2 > 0) prof_launch((unit_unfold_kernel<G>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st, u);
+  if (pl.unit_S2 > 0) {
+    if (varlen)
+      prof_launch((unit_unfold_kernel<G, true>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st, u);
+    else
+      prof_launch((unit_unfold_kernel<G>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st, u);
+  }
   return launch_status("gsa_decode launch");
 }
 
@@ -2497,5 +2552,36 @@ extern "C" gsa_status_t gsa_decode_levels(const gsa_levels_params* p, const void
   return dispatch<LevelsRunner>(lp.base.dtype, lp.base.D, lp.base.g, lp, q, k_cache, v_cache, k_up, v_up, out,
                                 lse, sel_up, sel1, reinterpret_cast<char*>(workspace),
                                 reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" gsa_status_t gsa_decode_varlen(const gsa_decode_params* p, const int32_t* seq_n_raw,
+                                          const int32_t* seq_n_gist, const void* q, const void* k_cache,
+                                          const void* v_cache, float* out, float* lse, int32_t* sel_idx,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  DecodePlan pl;
+  gsa_status_t s = plan_decode(p, &pl);
+  if (s != GSA_OK) return s;
+  if (pl.gist_set != GSA_GISTS_ALL)
+    return fail(GSA_ERR_UNSUPPORTED, "variable-length decode attends every gist: gist_set must be 0");
+  if ((s = check_ptr(seq_n_raw, "seq_n_raw")) != GSA_OK || (s = check_ptr(seq_n_gist, "seq_n_gist")) != GSA_OK ||
+      (s = check_ptr(q, "q")) != GSA_OK || (s = check_ptr(k_cache, "k_cache")) != GSA_OK ||
+      (s = check_ptr(v_cache, "v_cache")) != GSA_OK || (s = check_ptr(out, "out")) != GSA_OK ||
+      (s = check_ptr(lse, "lse", true)) != GSA_OK || (s = check_ptr(sel_idx, "sel_idx", true)) != GSA_OK)
+    return s;
+  if ((s = check_workspace(workspace, workspace_bytes, pl.total)) != GSA_OK) return s;
+  pl.seq_n = seq_n_raw;
+  pl.seq_m = seq_n_gist;
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (pl.unit_S > 0) {
+    switch (pl.g) {
+      case 1: return run_unit<1>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
+      case 2: return run_unit<2>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
+      case 4: return run_unit<4>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
+      case 8: return run_unit<8>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
+    }
+  }
+  return dispatch<DecodeRunner>(pl.dtype, pl.D, pl.g, pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
 }
 

@@ -148,6 +148,7 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
 
   DecodePlan d{};
   d.units = (int32_t)units;
+  d.Hkv = p->n_kv_heads;
   d.g = p->n_q_heads / p->n_kv_heads;
   d.D = p->head_dim;
   d.M = p->n_gist;
@@ -493,6 +494,27 @@ gsa_status_t plan_append(const gsa_append_params* p, AppendPlan* o) {
 }
 
 }  // namespace gsa
+
+extern "C" gsa_status_t gsa_check_seq_lens(const gsa_decode_params* p, const int32_t* seq_n_raw,
+                                           const int32_t* seq_n_gist) {
+  gsa::clear_error();
+  gsa::DecodePlan d;
+  gsa_status_t s = gsa::plan_decode(p, &d);
+  if (s != GSA_OK) return s;
+  if (!seq_n_raw || !seq_n_gist) return gsa::fail(GSA_ERR_INVALID_ARG, "length arrays are NULL");
+  const int64_t C = p->chunk;
+  for (int32_t b = 0; b < p->batch; ++b) {
+    const int64_t n = seq_n_raw[b], m = seq_n_gist[b];
+    const bool ok = n >= 1 && n <= p->n_raw && m >= p->topk && m <= p->n_gist && m * C <= n && n <= m * C + C &&
+                    n - m * C <= p->tail && p->tail <= n;
+    if (!ok)
+      return gsa::fail(GSA_ERR_INVALID_ARG,
+                       "sequence %d: n_raw=%lld, n_gist=%lld break 1 <= n <= %lld, %d <= m <= %lld, "
+                       "0 <= n - m*C <= C, n - m*C <= tail=%d <= n",
+                       b, (long long)n, (long long)m, (long long)p->n_raw, p->topk, (long long)p->n_gist, p->tail);
+  }
+  return GSA_OK;
+}
 
 extern "C" gsa_status_t gsa_topk_for_budget(int64_t budget, int64_t n_gist, int32_t chunk, int32_t tail,
                                             int32_t gist_set, int32_t* topk) {

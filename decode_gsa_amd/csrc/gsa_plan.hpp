@@ -89,6 +89,11 @@ struct DecodePlan {
   // unit_S2 workgroups per unit selects and unfolds (k > 0)
   int32_t unit_S, unit_S2;
   int64_t sel_stride;   // ints per unit in the selection region (large k only)
+  int32_t Hkv;
+  // variable-length batches (gsa_decode_varlen): device arrays of each
+  // sequence's raw tokens and gists, null for uniform lengths
+  const int32_t* seq_n;
+  const int32_t* seq_m;
 };
 
 gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* out);

@@ -23,13 +23,14 @@ import dataclasses
 import math
 from typing import Optional
 
+import numpy as np
 import torch
 
 __all__ = [
     "DecodeConfig", "HierConfig", "PrefillConfig", "GistConfig", "CONFIGS",
     "DecodeInputs", "HierInputs", "PrefillInputs",
     "make_decode", "make_hier", "make_prefill", "make_gist", "TokenStream", "make_token_stream",
-    "make_levels", "level_sizes",
+    "make_levels", "level_sizes", "varlen_lengths",
     "raw_row", "gist_row", "n_rows",
 ]
 
@@ -589,4 +590,17 @@ def make_levels(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_ra
     k_up = [draw(batch, n_kv_heads, m) for m in sizes[1:]]
     v_up = [draw(batch, n_kv_heads, m) for m in sizes[1:]]
     return q, k, v, k_up, v_up
+
+
+def varlen_lengths(batch: int, n_min: int, n_max: int, chunk: int, seed: int):
+    """Per-sequence (n_raw, n_gist) with n_raw uniform in [n_min, n_max] and
+    every complete chunk gisted, except that a sequence ending on a chunk
+    boundary leaves its last chunk's gist out half of the time (a full chunk
+    waiting for its gist)."""
+    rng = np.random.default_rng(seed)
+    n = rng.integers(n_min, n_max + 1, size=batch)
+    m = n // chunk
+    drop = (n % chunk == 0) & (rng.random(batch) < 0.5) & (m > 0)
+    m = m - drop.astype(n.dtype)
+    return [int(x) for x in n], [int(x) for x in m]
 

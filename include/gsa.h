@@ -122,6 +122,34 @@ gsa_status_t gsa_decode(const gsa_decode_params* p, const void* q, const void* k
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Variable-length batch: the same step as gsa_decode, for sequences of
+ * different lengths (each (sequence, kv-head) block holds its own raw tokens
+ * and gists, read only up to its own N_b + M_b rows).
+ * Source: the decode rule of gsa_decode (explainer section 2 'Key
+ * Concepts'), applied per sequence; serving batches of documents of several
+ * lengths is the use the explainer's reuse of cached documents implies.
+ * p->n_raw and p->n_gist are the batch's largest values (they size the
+ * workspace and the launch: gsa_decode_workspace_size(p) applies);
+ * p->row_capacity (or N + M of those maxima) is the slab stride.
+ * seq_n_raw, seq_n_gist: device arrays [B] int32, 16-byte aligned: sequence
+ * b holds N_b raw tokens and M_b gists with 1 <= N_b <= N, topk <= M_b <= M,
+ * 0 <= N_b - M_b*C <= C and N_b - M_b*C <= tail <= N_b. They stay on the
+ * device (read by the kernels); gsa_check_seq_lens validates a host copy.
+ * A sequence that breaks these rules is run with (N, M) instead, so no read
+ * leaves its slab. gist_set must be 0 (else GSA_ERR_UNSUPPORTED).
+ * ---------------------------------------------------------------------- */
+gsa_status_t gsa_decode_varlen(const gsa_decode_params* p, const int32_t* seq_n_raw,
+                               const int32_t* seq_n_gist, const void* q, const void* k_cache,
+                               const void* v_cache, float* out, float* lse, int32_t* sel_idx,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host check of per-sequence lengths (host arrays [p->batch]) against the
+ * rules above: GSA_OK, or GSA_ERR_INVALID_ARG naming the first sequence that
+ * breaks one (gsa_last_error). */
+gsa_status_t gsa_check_seq_lens(const gsa_decode_params* p, const int32_t* seq_n_raw,
+                                const int32_t* seq_n_gist);
+
+/* ------------------------------------------------------------------------
  * Two-level (gist-of-gist) decode.
  * Source: gist.science explainer, 'Hierarchical Extension (H-GSA)': meta-gists
  * summarise groups of gists; selection scores the meta-gists, then the gists
@@ -342,6 +370,7 @@ gsa_status_t gsa_cache_append(const gsa_append_params* p, const void* k_raw, con
  *     otherwise a stream launch (several workgroups per unit) and a
  *     select-and-unfold launch;
  *   gsa_decode, other shapes: a gist pass, then an unfold pass when topk > 0;
+ *   gsa_decode_varlen: as gsa_decode for the same parameters;
  *   gsa_decode_hier: level-2 pass, level-1 candidate pass, unfold pass when
  *     topk1 > 0;
  *   gsa_decode_levels: top-level pass, one pass per lower level, unfold pass

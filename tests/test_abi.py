@@ -411,3 +411,42 @@ def test_levels_rejects_null_arrays(L):
     assert L.gsa_decode_levels(ctypes.byref(p), FAKE, FAKE, FAKE, arr, arr, FAKE, None, None, None, FAKE,
                                need - 256, None) == WORKSPACE
 
+
+# ------------------------------------------------------- variable lengths ---
+
+def varlen_params(**kw):
+    p = dict(batch=3, n_raw=1024, n_gist=64, topk=2, tail=32)
+    p.update(kw)
+    return good_decode(**p)
+
+
+# C = 16, k = 2, tail = 32: 1 <= n <= 1024, 2 <= m <= 64, 16 m <= n <= 16 m + 16, 32 <= n
+@pytest.mark.parametrize("n,m,status", [
+    ([1024, 500, 40], [64, 31, 2], OK),
+    ([1024, 512, 48], [64, 32, 3], OK),
+    ([1024, 512, 48], [64, 31, 3], OK),           # 512 - 31*16 = 16: a full chunk without its gist
+    ([1024, 512, 48], [64, 33, 3], INVALID),      # gist 32 of an incomplete chunk
+    ([1024, 500, 31], [64, 31, 1], INVALID),      # n = 31 below the tail
+    ([1024, 500, 40], [64, 31, 3], INVALID),      # 3 gists need 48 raw tokens
+    ([1024, 500, 40], [64, 30, 2], INVALID),      # 500 - 30*16 = 20 > C
+    ([1025, 500, 40], [64, 31, 2], INVALID),      # above the call's n_raw
+    ([1024, 500, 40], [65, 31, 2], INVALID),      # above the call's n_gist
+    ([1024, 500, 40], [64, 31, 1], INVALID),      # m = 1 below topk = 2
+    ([1024, 500, 36], [64, 31, 2], OK),
+])
+def test_check_seq_lens(L, n, m, status):
+    p = varlen_params()
+    arr = lambda v: (ctypes.c_int32 * 3)(*v)
+    st = L.gsa_check_seq_lens(ctypes.byref(p), arr(n), arr(m))
+    assert st == status, L.gsa_last_error()
+
+
+def test_decode_varlen_rejections(L):
+    p = varlen_params()
+    st, need = ws_size(L, p)
+    call = lambda pp, sn, sm: L.gsa_decode_varlen(ctypes.byref(pp), sn, sm, FAKE, FAKE, FAKE, FAKE, None, None,
+                                                  FAKE, need, None)
+    assert call(p, None, FAKE) == INVALID and "seq_n_raw" in L.gsa_last_error().decode()
+    assert call(p, FAKE, FAKE + 4) == INVALID                       # misaligned
+    assert call(varlen_params(gist_set=1, batch=128), FAKE, FAKE) == UNSUPPORTED
+
