@@ -16,6 +16,9 @@ query positions at the end of a 65536-token sequence, 32/8 heads, k=16, W=64).
 `--config gist_64k` times the cache-building step of a 65536-token prompt:
 gsa_cache_append of its raw and gist rows into an empty cache, then
 gsa_gist_prefill of its 4096 gist tokens.
+`--config varlen_32k` times gsa_decode_varlen on the same batch shape with
+sequence lengths uniform in [4K, 32K] (one workgroup per unit: a step lasts
+as long as its longest sequence).
 `--scaling` sweeps the context from 32K to 16M tokens (one sequence, Hq 32 /
 Hkv 8, C 16, k 16, T 64) over single-level, two-level and L-level decode
 (fanout 16, levels added until the top holds at most 256 gists) and prints
@@ -59,6 +62,7 @@ sys.path.insert(0, ROOT)
 
 DECODE_METRIC = "GSA decode query-heads/s + achieved HBM GB/s (32K ctx, C=16, k=16, bf16)"
 PREFILL_METRIC = "GSA block-sparse prefill query-positions/s + MFMA utilisation (64K ctx, 4096 queries)"
+VARLEN_METRIC = "GSA variable-length decode query-heads/s + achieved HBM GB/s (4K-32K ctx, C=16, k=16, bf16)"
 GIST_METRIC = "GSA cache build (append + gist-token attention) prompt tokens/s (64K prompt, C=16)"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
@@ -536,6 +540,95 @@ def run_prefill_bench(args):
     return res
 
 
+# -------------------------------------------------------- variable length ---
+
+def run_varlen_bench(args):
+    import torch
+    import decode_gsa_amd as gsa
+    import gsa_inputs as gi
+    import oracle
+
+    cfg = gi.CONFIGS[args.config]
+    dev = torch.device("cuda", 0)
+    B, Hq, Hkv, D, C, k, T = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.chunk, cfg.topk, cfg.tail
+    n, m = gi.varlen_lengths(B, cfg.n_min, cfg.n_max, C, 2000 + 9)
+    N, M = max(n), max(m)
+    cap = N + M
+    log(f"[bench] generating {cfg.name} inputs (lengths {min(n)}..{N}) ...")
+    q, kc, vc, _, _ = gi.make_levels(B, Hq, Hkv, D, N, M, C, 2, 2, 2000 + 9, device=dev, values="gauss")
+    sn = torch.tensor(n, dtype=torch.int32, device=dev)
+    sm = torch.tensor(m, dtype=torch.int32, device=dev)
+    p = gsa.decode_params(B, Hq, Hkv, D, N, M, C, k, T, row_capacity=cap)
+    gsa.check_seq_lens(p, n, m)
+    ws = gsa.new_workspace(gsa.decode_workspace_size(p), dev)
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    sel = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        gsa.gsa_decode_varlen(q, kc, vc, seq_n_raw=sn, seq_n_gist=sm, n_raw=N, n_gist=M, chunk=C, topk=k, tail=T,
+                              out=out, lse=lse, sel_idx=sel, workspace=ws, stream=stream)
+
+    step(0)
+    torch.cuda.synchronize()
+    g = Hq // Hkv
+    for b, j in ((int(np.argmin(n)), 0), (int(np.argmax(n)), Hkv - 1)):
+        R = n[b] + m[b]
+        r = oracle.decode_unit(q[b, j * g:(j + 1) * g].float().cpu().numpy(), kc[b, j, :R].float().cpu().numpy(),
+                               vc[b, j, :R].float().cpu().numpy(), n_raw=n[b], n_gist=m[b], chunk=C, topk=k, tail=T)
+        got = out[b, j * g:(j + 1) * g].double().cpu().numpy()
+        rms = float(np.sqrt(np.mean(r["out"] ** 2)))
+        if not np.array_equal(sel[b, j].cpu().numpy(), r["sel"]) or float(np.abs(got - r["out"]).max()) > 2e-3 * rms:
+            raise SystemExit(f"varlen: sequence {b} kv-head {j} differs from the oracle")
+    ms_per_step, per = timed_steps(gsa, step, args, 2)
+    k_ms = float(per[:, 0].mean())
+    row = 2 * D * 2
+    sel_np = sel.cpu().numpy()
+    raw_sel = sum(tail_free_rows(sel_np[b], n[b], T, C) for b in range(B))
+    nb = Hkv * sum((mb + T) for mb in m) * row + raw_sel * row + B * Hq * D * 2 + B * Hq * (D + 1) * 4 + B * Hkv * k * 4
+    achieved = nb / (k_ms / 1e3) / 1e9
+    mean_n = float(np.mean(n))
+    res = {
+        "metric": VARLEN_METRIC,
+        "value": B * Hq / (ms_per_step / 1e3),
+        "unit": "query-heads/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian q/K/V, seeded lengths)",
+        "config": {"workload": f"{cfg.name}: decode step of {B} sequences of {min(n)}..{N} tokens (mean "
+                               f"{mean_n:.0f}), Hq={Hq}, Hkv={Hkv}, D={D}, C={C}, k={k}, T={T}, bf16 cache",
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "unit_kernel (VARLEN)",
+                     "alg_bytes_per_launch": nb, "launch_ms_mean": k_ms,
+                     "longest_share": float(max(n)) / mean_n},
+        "kernels": {"unit_kernel": {"ms": k_ms, "alg_bytes": nb, "GB_s": achieved, **pcts(per[:, 0])}},
+        "source_sha": source_sha("gsa_decode.hip", "gsa_device.hpp"),
+    }
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle ...")
+        from threadpoolctl import threadpool_limits
+        rng = np.random.default_rng(9)
+        t_total, cnt, host = 0.0, 0, {}
+        with threadpool_limits(1):
+            while t_total < args.cpu_seconds and cnt < 100000:
+                b, j = int(rng.integers(B)), int(rng.integers(Hkv))
+                if (b, j) not in host:
+                    R = n[b] + m[b]
+                    host[(b, j)] = (q[b, j * g:(j + 1) * g].float().cpu().numpy(), kc[b, j, :R].float().cpu().numpy(),
+                                    vc[b, j, :R].float().cpu().numpy())
+                qh, Kh, Vh = host[(b, j)]
+                t0 = time.perf_counter()
+                oracle.decode_unit(qh, Kh, Vh, n_raw=n[b], n_gist=m[b], chunk=C, topk=k, tail=T)
+                t_total += time.perf_counter() - t0
+                cnt += 1
+        res["cpu_baseline"] = {"value": cnt * g / t_total, "unit": "query-heads/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{cnt} random (sequence, kv-head) units of the same batch, fp64 numpy, "
+                                         f"1 thread, {t_total:.1f} s"}
+    return res
+
+
 # ------------------------------------------------------------ cache build ---
 
 def gist_flops(cfg):
@@ -881,6 +974,8 @@ def main():
         res = run_hier_bench(args)
     elif isinstance(cfg, gi.GistConfig):
         res = run_gist_bench(args)
+    elif isinstance(cfg, gi.VarlenConfig):
+        res = run_varlen_bench(args)
     else:
         raise SystemExit(f"--config {args.config}: no benchmark for this workload yet")
     print(json.dumps(res), flush=True)

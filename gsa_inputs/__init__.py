@@ -27,7 +27,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "DecodeConfig", "HierConfig", "PrefillConfig", "GistConfig", "CONFIGS",
+    "DecodeConfig", "HierConfig", "PrefillConfig", "GistConfig", "VarlenConfig", "CONFIGS",
     "DecodeInputs", "HierInputs", "PrefillInputs",
     "make_decode", "make_hier", "make_prefill", "make_gist", "TokenStream", "make_token_stream",
     "make_levels", "level_sizes", "varlen_lengths",
@@ -111,6 +111,23 @@ class PrefillConfig:
 
 
 @dataclasses.dataclass(frozen=True)
+class VarlenConfig:
+    """A decode step over sequences of different lengths (uniform in
+    [n_min, n_max] raw tokens)."""
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str
+    n_min: int
+    n_max: int
+    chunk: int
+    topk: int
+    tail: int
+
+
+@dataclasses.dataclass(frozen=True)
 class GistConfig:
     """Cache-building step of one prompt: every raw and gist row appended to an
     empty cache, then the attention of every gist token."""
@@ -148,6 +165,8 @@ CONFIGS = {
                                  64, 4096),
     # cache append + gist-token attention of a 64K-token prompt (4096 gists)
     "gist_64k": GistConfig("gist_64k", 32, 8, 128, "bf16", 65536, 16),
+    # the batched GQA decode step with sequence lengths uniform in [4K, 32K]
+    "varlen_32k": VarlenConfig("varlen_32k", 32, 32, 8, 128, "bf16", 4096, 32768, 16, 16, 64),
 }
 
 
