@@ -600,7 +600,9 @@ def run_varlen_bench(args):
                                f"{mean_n:.0f}), Hq={Hq}, Hkv={Hkv}, D={D}, C={C}, k={k}, T={T}, bf16 cache",
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "unit_kernel (VARLEN)",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(f"unit_kernel/{cfg.name}", source_sha("gsa_decode.hip", "gsa_device.hpp")),
+                     "kernel": "unit_kernel (VARLEN)",
                      "alg_bytes_per_launch": nb, "launch_ms_mean": k_ms,
                      "longest_share": float(max(n)) / mean_n},
         "kernels": {"unit_kernel": {"ms": k_ms, "alg_bytes": nb, "GB_s": achieved, **pcts(per[:, 0])}},
