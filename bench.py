@@ -795,7 +795,7 @@ def run_scaling(args):
     B, Hq, Hkv, D, C, T, G = 1, 32, 8, 128, 16, 64, 16
     units, row = B * Hkv, 2 * D * 2
     k1, k_mid, k_top = 16, 8, 4
-    ns = [n for n in SCALING_N if n <= args.scaling_max]
+    ns = [n for n in SCALING_N if args.scaling_min <= n <= args.scaling_max]
     for N in ns:
         M = N // C
         sizes = scaling_levels(M, G)
@@ -884,12 +884,16 @@ def run_scaling(args):
                 gsa.gsa_profile_events([])
                 torch.cuda.synchronize()
                 dev_ms = float(np.mean([ev.ms(i * n_marks, (i + 1) * n_marks - 1) for i in range(args.steps)]))
+                # per launch: launch 0 from the call's start, launch j > 0 from the end of launch j - 1
+                per_launch = [float(np.mean([ev.ms(i * n_marks + j, i * n_marks + j + 1) for i in range(args.steps)]))
+                              for j in range(n_marks - 1)]
             finally:
                 gsa.gsa_profile_events([])
                 ev.close()
             lv, tk = {"single-level": ([M], [k1]), "two-level": ([M, M // G], [k1, k_mid])}.get(name, (sizes, topks))
             line = {"context": N, "variant": name, "levels": lv, "topks": tk,
                     "ms_per_step": ms, "device_ms_per_call": dev_ms, "launches": n_marks - 1,
+                    "launch_ms": per_launch,
                     "alg_bytes_per_step": nb, "GB_s": nb / (ms / 1e3) / 1e9,
                     "cache_copies": copies, "oracle_checked_unit": [0, 0]}
             print(json.dumps(line), flush=True)
@@ -948,6 +952,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--scaling", action="store_true", help="decode time and bytes per step vs context length")
     ap.add_argument("--scaling-max", type=int, default=1 << 24)
+    ap.add_argument("--scaling-min", type=int, default=0)
     ap.add_argument("--gist-set", default="all", choices=["all", "selected", "none"],
                     help="decode attention-set rule (slide 17 variants)")
     args = ap.parse_args()

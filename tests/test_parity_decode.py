@@ -121,6 +121,24 @@ def test_decode_selects_chunk_inside_tail(gsa):
     run_decode(gsa, inp, cfg)
 
 
+@pytest.mark.parametrize("kw", [
+    # more gists than one workgroup per unit keeps (split path, one unit per
+    # kv-head): the unit's last workgroup selects among 20000 scores
+    dict(batch=1, n_kv_heads=2, n_q_heads=8, n_raw=16 * 20000 + 7, topk=16, tail=64),
+    # fp32, D = 64: 5000 scores, several rounds of loads per thread
+    dict(batch=1, n_kv_heads=2, n_q_heads=4, head_dim=64, dtype="f32", n_raw=8 * 5000, chunk=8, topk=8, tail=8),
+    # just above and at the single-round bound (4096 scores)
+    dict(batch=2, n_kv_heads=1, n_q_heads=2, dtype="f32", head_dim=64, n_raw=16 * 4097, topk=12, tail=16),
+    dict(batch=2, n_kv_heads=1, n_q_heads=2, dtype="f32", head_dim=64, n_raw=16 * 4096, topk=12, tail=16),
+])
+def test_decode_split_path_many_gists(gsa, kw):
+    cfg = small("gqa_32k", **kw)
+    say(f"split path {kw}")
+    inp = gi.make_decode(cfg, 2100, device="cuda")
+    err = run_decode(gsa, inp, cfg)
+    say(f"  max err / rms = {err:.2e}, {gsa.gsa_profile_marks() - 1} launches")
+
+
 def test_decode_no_gists(gsa):
     cfg = small("gqa_32k", batch=2, n_raw=12, n_gist=0, topk=0, tail=12, plant="none")
     inp = gi.make_decode(cfg, 2004, device="cuda")
