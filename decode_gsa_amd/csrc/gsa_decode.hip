@@ -1011,6 +1011,49 @@ void gist_kernel(GistArgs a) {
                      a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
 }
 
+// Split path with many gists per unit: workgroup (unit, split) takes the top-k
+// of the split's scores (written by the gist pass) and writes them as (score,
+// id) candidates, padded with scores that never win. The unit's top-k (ties to
+// the smaller id) lies within the candidates of its splits, so the unfold
+// pass selects among S k of them instead of all M scores.
+struct CandArgs {
+  const float* scores;    // [units][score_stride]
+  int64_t score_stride;
+  int64_t n_items, per_task;
+  int32_t tasks, k;
+  int64_t N, M;
+  int32_t C, T;
+  SeqLens seq;
+  float* cand_scores;     // [units][cand_stride]
+  int32_t* cand_ids;
+  int64_t cand_stride;
+};
+
+__global__ __launch_bounds__(kThreads) void cand_kernel(CandArgs a) {
+  __shared__ SelectLds sl;
+  __shared__ TopkLds tl;
+  __shared__ int32_t loc[kFastSel];
+  const int tid = threadIdx.x;
+  const int unit = blockIdx.x / a.tasks, split = blockIdx.x % a.tasks;
+  int64_t uN = a.N, uM = a.M;
+  unit_lengths(a.seq, unit, a.N, a.M, a.C, a.T, &uN, &uM);
+  const int64_t n_items = a.seq.n != nullptr ? uM : a.n_items;
+  const int64_t i0 = (int64_t)split * a.per_task;
+  const int64_t i1 = i0 + a.per_task < n_items ? i0 + a.per_task : n_items;
+  const int nl = i1 > i0 ? (int)(i1 - i0) : 0;
+  const float* su = a.scores + (size_t)unit * a.score_stride;
+  unit_topk(su + i0, nl, a.k, IdMap{nullptr, 0, 0, 0, 0}, unit, loc, sl, tl);
+  __syncthreads();
+  float* cs = a.cand_scores + (size_t)unit * a.cand_stride + (size_t)split * a.k;
+  int32_t* ci = a.cand_ids + (size_t)unit * a.cand_stride + (size_t)split * a.k;
+  for (int j = tid; j < a.k; j += kThreads) {
+    const bool real = j < nl;
+    const int li = real ? loc[j] : 0;
+    cs[j] = real ? su[i0 + li] : -INFINITY;
+    ci[j] = real ? (int32_t)(i0 + li) : 0;
+  }
+}
+
 // Raw rows of the selected chunks (minus rows the tail owns); every workgroup
 // first makes the unit's selection from the previous pass's scores, and the
 // unit's last workgroup merges every partial into out and lse.
@@ -1067,7 +1110,8 @@ __global__ __launch_bounds__(kThreads) void unfold_kernel(UnfoldArgs a) {
   unit_lengths(a.seq, unit, a.N, a.M, a.C, a.T, &uN, &uM);
   if (a.scores != nullptr) {
     // make the unit's selection from the previous pass's scores
-    const int n_cand = a.seq.n != nullptr ? (int)uM : a.n_cand;
+    // a variable-length unit's own gist scores (identity ids); candidate lists keep their size
+    const int n_cand = a.seq.n != nullptr && a.im.sel2 == nullptr ? (int)uM : a.n_cand;
     unit_topk(a.scores + (size_t)unit * a.score_stride, n_cand, a.k, a.im, unit, us, lds.u.sel.s, lds.u.sel.t);
     __syncthreads();
     if (split == 0 && a.sel_out)
@@ -1138,16 +1182,33 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
   g.out = pl.k > 0 ? nullptr : out; g.lse = pl.k > 0 ? nullptr : lse;
   g.cnt = ctrl_of(ws, pl.off_ctrl, 0);
   g.scale_log2 = pl.scale * kLog2e; g.score_mul = pl.scale / G;
-  g.fuse_k = pl.k;
+  const bool cand = pl.cand_stride > 0;
+  g.fuse_k = cand ? 0 : pl.k;   // with candidates the unfold pass selects
   g.sel_ws = wsel; g.sel_stride = pl.sel_stride; g.sel_out = sel_idx;
   g.seq = SeqLens{pl.seq_n, pl.seq_m, pl.Hkv, pl.k};
   prof_begin_call();
   prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st, g);
+  float* cand_s = reinterpret_cast<float*>(ws + pl.off_cand);
+  int32_t* cand_i = reinterpret_cast<int32_t*>(ws + pl.off_cand_ids);
+  if (cand) {
+    CandArgs c{};
+    c.scores = scores; c.score_stride = pl.score_stride;
+    c.n_items = pl.M; c.per_task = pl.gists_per_split; c.tasks = pl.S; c.k = pl.k;
+    c.N = pl.N; c.M = pl.M; c.C = pl.C; c.T = pl.T; c.seq = g.seq;
+    c.cand_scores = cand_s; c.cand_ids = cand_i; c.cand_stride = pl.cand_stride;
+    prof_launch(cand_kernel, dim3(pl.units * pl.S), dim3(kThreads), 0, st, c);
+  }
   if (pl.k > 0) {
     UnfoldArgs u{};
     u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
     u.scores = nullptr;
-    u.sel_ws = wsel; u.sel_stride = pl.sel_stride; u.sel_out = nullptr; u.k = pl.k;
+    if (cand) {
+      u.scores = cand_s; u.score_stride = pl.cand_stride; u.n_cand = pl.S * pl.k;
+      u.im = IdMap{cand_i, 1, pl.S * pl.k, 0, pl.cand_stride};
+      u.sel_out = sel_idx;
+    }
+    u.sel_ws = wsel; u.sel_stride = pl.sel_stride; u.k = pl.k;
+    if (!cand) u.sel_out = nullptr;
     u.C = pl.C; u.T = pl.T; u.M = pl.M; u.N = pl.N;
     u.n_items = pl.n_items; u.per_task = pl.items_per_split; u.tasks = pl.S2;
     u.part = part; u.part_stride = ps; u.NP = pl.NP; u.part_base = pl.S;

@@ -197,6 +197,14 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)d.sel_stride);
   d.off_part = off;
   off = align_up(off + sizeof(float) * (size_t)units * d.NP * (size_t)part_stride(d.g, d.D));
+  d.cand_stride = 0;
+  if (d.unit_S == 0 && d.k > 0 && d.k <= kFastSelect && d.S >= 4 && (int64_t)d.S * d.k * 2 <= d.M) {
+    d.cand_stride = line_pad((int64_t)d.S * d.k);
+    d.off_cand = off;
+    off = align_up(off + sizeof(float) * (size_t)units * (size_t)d.cand_stride);
+    d.off_cand_ids = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)d.cand_stride);
+  }
   d.total = off;
   *o = d;
   return GSA_OK;

@@ -90,6 +90,11 @@ struct DecodePlan {
   int32_t unit_S, unit_S2;
   int64_t sel_stride;   // ints per unit in the selection region (large k only)
   int32_t Hkv;
+  // split path with many gists per unit (k <= 64): each gist workgroup hands
+  // its own top-k (score, id) candidates on, and the unit's last workgroup
+  // selects among S k of them; cand_stride = 0 when it selects among all M
+  int64_t cand_stride;
+  size_t off_cand, off_cand_ids;
   // variable-length batches (gsa_decode_varlen): device arrays of each
   // sequence's raw tokens and gists, null for uniform lengths
   const int32_t* seq_n;
