@@ -1257,6 +1257,19 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   c.scores = pl.k > 0 ? sc : nullptr; c.score_stride = hp.sc_stride;
   c.prev_scores = s2; c.prev_stride = hp.s2_stride; c.prev_n = (int32_t)hp.M2; c.prev_k = hp.k2;
   c.prev_im = IdMap{nullptr, 0, 0, 0, 0};
+  if (hp.cand2_stride > 0) {
+    // the level-2 workgroups' own top-k2, then the selection among those
+    float* cs = reinterpret_cast<float*>(ws + hp.off_cand2);
+    int32_t* ci = reinterpret_cast<int32_t*>(ws + hp.off_cand2_ids);
+    CandArgs ca{};
+    ca.scores = s2; ca.score_stride = hp.s2_stride;
+    ca.n_items = hp.M2; ca.per_task = hp.l2_per_split; ca.tasks = hp.S_l2; ca.k = hp.k2;
+    ca.N = pl.N; ca.M = pl.M; ca.C = pl.C; ca.T = pl.T;
+    ca.cand_scores = cs; ca.cand_ids = ci; ca.cand_stride = hp.cand2_stride;
+    prof_launch(cand_kernel, dim3(pl.units * hp.S_l2), dim3(kThreads), 0, st, ca);
+    c.prev_scores = cs; c.prev_stride = hp.cand2_stride; c.prev_n = hp.S_l2 * hp.k2;
+    c.prev_im = IdMap{ci, 1, hp.S_l2 * hp.k2, 0, hp.cand2_stride};
+  }
   c.sel2_ws = wsel2; c.sel2_stride = hp.sel2_stride; c.sel2_out = sel2;
   c.part_base = hp.S_l2;
   c.out = pl.k > 0 ? nullptr : out; c.lse = pl.k > 0 ? nullptr : lse;

@@ -273,6 +273,14 @@ gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
   off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)d.sel_stride);
   h.off_part = off;
   off = align_up(off + sizeof(float) * (size_t)units * h.NP * (size_t)part_stride(d.g, d.D));
+  h.cand2_stride = 0;
+  if (h.unit_S == 0 && h.k2 > 0 && h.k2 <= kFastSelect && h.S_l2 >= 4 && (int64_t)h.S_l2 * h.k2 * 2 <= h.M2) {
+    h.cand2_stride = line_pad((int64_t)h.S_l2 * h.k2);
+    h.off_cand2 = off;
+    off = align_up(off + sizeof(float) * (size_t)units * (size_t)h.cand2_stride);
+    h.off_cand2_ids = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)units * (size_t)h.cand2_stride);
+  }
   h.total = off;
   *o = h;
   return GSA_OK;

@@ -123,6 +123,11 @@ struct HierPlan {
   // gists and the tail, then one workgroup per unit for the rest; 0 when the
   // gist passes run instead
   int32_t unit_S;
+  // split path, k2 <= 64 and many level-2 gists: the level-2 workgroups'
+  // top-k2 candidates (cand_kernel) replace the M2 scores in the candidate
+  // pass's selection; cand2_stride = 0 otherwise
+  int64_t cand2_stride;
+  size_t off_cand2, off_cand2_ids;
 };
 
 gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* out);

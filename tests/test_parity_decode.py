@@ -222,6 +222,11 @@ HIER_CASES = [
     dict(batch=4, n_raw=16 * 8 * 40 + 16 * 5, fanout=8, topk2=6, topk=12),   # 5 orphans, k1 <= 64
     dict(batch=2, n_raw=16 * 16 * 16, fanout=16, topk2=16, topk=64, plant="none"),  # every group chosen
     dict(batch=1, n_raw=16 * 4 * 300, fanout=4, topk2=40, topk=20, plant="none"),   # k2 > 16
+    # split path with many level-2 gists: the level-2 workgroups' top-k2
+    # candidates feed the level-2 selection (fp32, and bf16 with k1 > 64)
+    dict(batch=1, n_kv_heads=2, n_q_heads=8, dtype="f32", head_dim=64, n_raw=16 * 16 * 2000, fanout=16,
+         topk2=8, topk=16),
+    dict(batch=1, n_kv_heads=2, n_q_heads=8, n_raw=16 * 16 * 2000, fanout=16, topk2=8, topk=80),
 ]
 
 
