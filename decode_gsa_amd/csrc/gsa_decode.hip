@@ -2208,7 +2208,9 @@ struct LevelArgs {
   int32_t* sel_out[GSA_MAX_LEVELS + 1];  // l >= 2: [units][kl[l]] chosen ids, or null
 };
 
-template <int G>
+// TOP: the workgroup also streams the top level and the tail itself (top
+// level <= kUMaxGist gists, its scores kept in LDS): one launch per call.
+template <int G, bool TOP = false>
 __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, LevelArgs lv) {
   __shared__ __attribute__((aligned(16))) UnitLds L;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2236,8 +2238,21 @@ __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, Level
   const int Lv = lv.L, Gf = lv.G;
   float* gsc = a.scores + (size_t)unit * a.score_stride;
   // the top level: its chosen gists, ascending
-  unit_select<kUMaxSel / kThreads, false>(nullptr, (int)lv.Ml[Lv], lv.kl[Lv], a.s2 + (size_t)unit * a.s2_stride,
-                                          a.s2_stride, unit, L.sel2, L.u.sel.s, L.u.sel.t);
+  if constexpr (TOP) {
+    // its gists (dense rows of the top array, a.K2) and the tail, four wave shares
+    const int n1 = (int)a.M2 + a.T;
+    const int per1 = (n1 + kUW - 1) / kUW;
+    const char* K2b = reinterpret_cast<const char*>(a.K2) + (size_t)unit * a.M2 * 256;
+    const char* V2b = reinterpret_cast<const char*>(a.V2) + (size_t)unit * a.M2 * 256;
+    unit_stream<kUKL2>(Kb, Vb, min(n1, w * per1), min(n1, (w + 1) * per1), a, qf, st, ring, L.scores, L.sel, 0,
+                       K2b, V2b);
+    __syncthreads();   // every top-level score is in LDS, every ring idle
+    unit_select<kUMaxGist / kThreads, true>(L.scores, (int)lv.Ml[Lv], lv.kl[Lv], gsc, a.score_stride, unit, L.sel2,
+                                            L.u.sel.s, L.u.sel.t);
+  } else {
+    unit_select<kUMaxSel / kThreads, false>(nullptr, (int)lv.Ml[Lv], lv.kl[Lv], a.s2 + (size_t)unit * a.s2_stride,
+                                            a.s2_stride, unit, L.sel2, L.u.sel.s, L.u.sel.t);
+  }
   __syncthreads();
   if (lv.sel_out[Lv])
     for (int i = tid; i < lv.kl[Lv]; i += kUW * 64) lv.sel_out[Lv][(size_t)unit * lv.kl[Lv] + i] = L.sel2[i];
@@ -2296,12 +2311,16 @@ __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, Level
     unit_stream<kUKUnfold>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
                            L.sel);
   }
-  float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
-  unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)a.S * a.part_stride);
-  done_stores();
-  __syncthreads();
-  merge_unit<128, G>(part_u, a.S + 1, (uint32_t)a.part_stride, a.out + (size_t)unit * G * 128,
-                     a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
+  if constexpr (TOP) {
+    unit_combine<G>(L, st, w, a.out + (size_t)unit * G * 128, a.lse ? a.lse + (size_t)unit * G : nullptr, nullptr);
+  } else {
+    float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
+    unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)a.S * a.part_stride);
+    done_stores();
+    __syncthreads();
+    merge_unit<128, G>(part_u, a.S + 1, (uint32_t)a.part_stride, a.out + (size_t)unit * G * 128,
+                       a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
+  }
   if (a.sel)
     for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
 }
@@ -2337,8 +2356,13 @@ gsa_status_t run_unit_levels(const LevelsPlan& lp, const void* q, const void* K,
     }
   }
   prof_begin_call();
-  prof_launch((unit_kernel<G, true>), dim3(pl.units * lp.unit_S), dim3(kUW * 64), 0, st, u);
-  prof_launch((unit_levels_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
+  if (lp.Ml[Lv] <= kUMaxGist && lp.Ml[Lv] + pl.T <= kUWgItems) {
+    // the top level fits one workgroup's LDS scores: one launch
+    prof_launch((unit_levels_kernel<G, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
+  } else {
+    prof_launch((unit_kernel<G, true>), dim3(pl.units * lp.unit_S), dim3(kUW * 64), 0, st, u);
+    prof_launch((unit_levels_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
+  }
   return launch_status("gsa_decode_levels launch");
 }
 

@@ -406,8 +406,10 @@ gsa_status_t plan_levels(const gsa_levels_params* p, LevelsPlan* o) {
     h.score_stride[l] = (h.items[l] + 63) / 64 * 64;
     // the one-workgroup-per-unit descent reuses level 1's region for every
     // lower level's selection fallback
-    if (l == 1)
+    if (l == 1) {
       for (int j = 2; j < L; ++j) h.score_stride[1] = std::max(h.score_stride[1], (h.items[j] + 63) / 64 * 64);
+      h.score_stride[1] = std::max(h.score_stride[1], (h.Ml[L] + 63) / 64 * 64);   // the top level, selected in LDS
+    }
     h.off_scores[l] = off;
     off = align_up(off + sizeof(float) * (size_t)units * (size_t)h.score_stride[l]);
     if (l >= 2) {
