@@ -89,3 +89,36 @@ def test_prefill_planted_blocks_match_oracle_on_sampled_queries():
                               q_start=cfg.q_start, queries=qs)
     for i, j in qs:
         np.testing.assert_array_equal(sel[j, i], to_np(inp.planted[i // cfg.q_block, j]))
+
+
+# ------------------------------------- variable lengths, levels, streams ---
+
+@pytest.mark.parametrize("n_min,n_max,chunk", [(16, 4000, 16), (300, 8192, 16), (80, 3000, 8), (1, 40, 4)])
+def test_varlen_lengths_keep_the_layout(n_min, n_max, chunk):
+    """Every generated (n, m) pair is a valid interleaved cache: gists only of
+    complete chunks, at most one full chunk waiting for its gist; both kinds
+    of sequence end (ragged tail, full chunk without its gist) occur."""
+    n, m = gi.varlen_lengths(64, n_min, n_max, chunk, 11)
+    assert len(n) == len(m) == 64
+    for a, b in zip(n, m):
+        assert n_min <= a <= n_max
+        assert b * chunk <= a <= b * chunk + chunk
+    assert n == gi.varlen_lengths(64, n_min, n_max, chunk, 11)[0]      # seeded
+
+
+def test_level_sizes_and_make_levels_shapes():
+    assert gi.level_sizes(1010, 3, 4) == [1010, 336, 112, 37]
+    q, k, v, ku, vu = gi.make_levels(2, 8, 2, 64, 16 * 100 + 5, 100, 16, 4, 3, 5, values="int")
+    assert q.shape == (2, 8, 64) and k.shape == (2, 2, 1705, 64)
+    assert [t.shape[2] for t in ku] == [25, 6] and [t.shape[2] for t in vu] == [25, 6]
+    assert set(torch.unique(k.float()).tolist()) <= {-2.0, -1.0, 0.0, 1.0, 2.0}
+    q2 = gi.make_levels(2, 8, 2, 64, 16 * 100 + 5, 100, 16, 4, 3, 5, values="int")[0]
+    assert torch.equal(q, q2)                                           # seeded
+
+
+def test_token_stream_and_gist_shapes():
+    s = gi.make_token_stream(3, 8, 2, 64, 50, 8, 2)
+    assert s.raw_k.shape == (50, 3, 2, 64) and s.gist_k.shape == (6, 3, 2, 64)
+    assert s.gist_q.shape == (6, 3, 8, 64) and s.q.shape == (3, 8, 64)
+    q, k, v = gi.make_gist(8, 2, 128, 16 * 10, 10, 10, 3)
+    assert q.shape == (8, 10, 128) and k.shape == (2, 170, 128) and k.dtype == torch.bfloat16
