@@ -32,6 +32,7 @@ __all__ = [
     "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse", "gsa_profile_events",
     "gsa_profile_marks", "topk_for_budget", "GIST_SETS", "gsa_gist_prefill", "gsa_cache_append",
     "gsa_decode_levels", "levels_workspace_size", "gsa_decode_varlen", "check_seq_lens",
+    "launches",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -45,6 +46,8 @@ EXPORTED_SYMBOLS = (
     "gsa_profile_events", "gsa_profile_marks", "gsa_status_string", "gsa_last_error",
     "gsa_topk_for_budget", "gsa_gist_prefill", "gsa_cache_append",
     "gsa_decode_levels_workspace_size", "gsa_decode_levels", "gsa_decode_varlen", "gsa_check_seq_lens",
+    "gsa_decode_launches", "gsa_decode_hier_launches", "gsa_decode_levels_launches",
+    "gsa_prefill_launches",
 )
 MAX_LEVELS = 6
 
@@ -123,9 +126,15 @@ def lib() -> ctypes.CDLL:
         L.gsa_cache_append.argtypes = [P(AppendParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.gsa_profile_events.argtypes = [P(_vp), _c_i32]
         L.gsa_profile_marks.argtypes = [P(_c_i32)]
+        L.gsa_decode_launches.argtypes = [P(DecodeParams), P(_c_i32)]
+        L.gsa_decode_hier_launches.argtypes = [P(HierParams), P(_c_i32)]
+        L.gsa_decode_levels_launches.argtypes = [P(LevelsParams), P(_c_i32)]
+        L.gsa_prefill_launches.argtypes = [P(PrefillParams), P(_c_i32)]
         for f in ("gsa_decode_workspace_size", "gsa_decode", "gsa_decode_hier_workspace_size",
                   "gsa_decode_hier", "gsa_prefill_workspace_size", "gsa_prefill_blocksparse",
-                  "gsa_profile_events", "gsa_profile_marks"):
+                  "gsa_profile_events", "gsa_profile_marks", "gsa_decode_launches",
+                  "gsa_decode_hier_launches", "gsa_decode_levels_launches",
+                  "gsa_prefill_launches"):
             getattr(L, f).restype = _c_i32
         L.gsa_topk_for_budget.argtypes = [_c_i64, _c_i64, _c_i32, _c_i32, _c_i32, P(_c_i32)]
         L.gsa_topk_for_budget.restype = _c_i32
@@ -148,6 +157,16 @@ def gsa_profile_marks() -> int:
     """Kernel launches + 1 of the last library call on this thread."""
     n = _c_i32(0)
     _check(lib().gsa_profile_marks(ctypes.byref(n)), "gsa_profile_marks")
+    return n.value
+
+
+def launches(p) -> int:
+    """Kernel launches a call with these parameters makes (host only): p is a
+    DecodeParams, HierParams, LevelsParams or PrefillParams."""
+    f = {DecodeParams: "gsa_decode_launches", HierParams: "gsa_decode_hier_launches",
+         LevelsParams: "gsa_decode_levels_launches", PrefillParams: "gsa_prefill_launches"}[type(p)]
+    n = _c_i32(0)
+    _check(getattr(lib(), f)(ctypes.byref(p), ctypes.byref(n)), f)
     return n.value
 
 
@@ -244,10 +263,16 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
-def _stream(stream, device) -> Optional[int]:
+def _on_stream(stream, device):
+    """The call's stream (the current one when None) and a context that makes it
+    current: outputs and temporary workspaces are allocated (and zero-filled)
+    under it, so they are ordered before the launch and the caching allocator
+    reuses them only after the work queued on that stream."""
     import torch
+    if torch.device(device).type != "cuda":
+        raise ValueError("tensors must live on the GPU")
     s = torch.cuda.current_stream(device) if stream is None else stream
-    return s.cuda_stream
+    return s, torch.cuda.stream(s)
 
 
 def _workspace(ws, nbytes, device):
@@ -315,16 +340,17 @@ def gsa_decode(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int,
     if tuple(k_cache.shape) != (B, Hkv, R, D) or tuple(v_cache.shape) != (B, Hkv, R, D):
         raise ValueError("cache shape mismatch")
     dev = q.device
-    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
-    if lse is None and want_lse:
-        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
-    if sel_idx is None and want_sel:
-        sel_idx = torch.empty(B, Hkv, max(topk, 0), dtype=torch.int32, device=dev)
-    nbytes = decode_workspace_size(p)
-    ws = _workspace(workspace, nbytes, dev)
-    _check(lib().gsa_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
-                            _ptr(lse), _ptr(sel_idx) if topk > 0 else None, _ptr(ws),
-                            _nbytes(ws), _stream(stream, dev)), "gsa_decode")
+    s, on_s = _on_stream(stream, dev)
+    with on_s:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
+        if lse is None and want_lse:
+            lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        if sel_idx is None and want_sel:
+            sel_idx = torch.empty(B, Hkv, max(topk, 0), dtype=torch.int32, device=dev)
+        ws = _workspace(workspace, decode_workspace_size(p), dev)
+        _check(lib().gsa_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                _ptr(lse), _ptr(sel_idx) if topk > 0 else None, _ptr(ws),
+                                _nbytes(ws), s.cuda_stream), "gsa_decode")
     return out, lse, sel_idx
 
 
@@ -367,18 +393,21 @@ def gsa_decode_varlen(q, k_cache, v_cache, *, seq_n_raw, seq_n_gist, chunk: int,
                       0, cap)
     if not on_dev:
         check_seq_lens(p, hn, hm)
-        sn = torch.tensor(hn, dtype=torch.int32, device=dev)
-        sm = torch.tensor(hm, dtype=torch.int32, device=dev)
-    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
-    if lse is None and want_lse:
-        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
-    if sel_idx is None and want_sel:
-        sel_idx = torch.empty(B, Hkv, max(topk, 0), dtype=torch.int32, device=dev)
-    ws = _workspace(workspace, decode_workspace_size(p), dev)
-    _check(lib().gsa_decode_varlen(ctypes.byref(p), _ptr(sn), _ptr(sm), _ptr(q), _ptr(k_cache),
-                                   _ptr(v_cache), _ptr(out), _ptr(lse),
-                                   _ptr(sel_idx) if topk > 0 else None, _ptr(ws), _nbytes(ws),
-                                   _stream(stream, dev)), "gsa_decode_varlen")
+    s, on_s = _on_stream(stream, dev)
+    with on_s:
+        if not on_dev:
+            sn = torch.tensor(hn, dtype=torch.int32, device=dev)
+            sm = torch.tensor(hm, dtype=torch.int32, device=dev)
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
+        if lse is None and want_lse:
+            lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        if sel_idx is None and want_sel:
+            sel_idx = torch.empty(B, Hkv, max(topk, 0), dtype=torch.int32, device=dev)
+        ws = _workspace(workspace, decode_workspace_size(p), dev)
+        _check(lib().gsa_decode_varlen(ctypes.byref(p), _ptr(sn), _ptr(sm), _ptr(q), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(out), _ptr(lse),
+                                       _ptr(sel_idx) if topk > 0 else None, _ptr(ws), _nbytes(ws),
+                                       s.cuda_stream), "gsa_decode_varlen")
     return out, lse, sel_idx
 
 
@@ -398,21 +427,22 @@ def gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int,
                          row_capacity=cap)
     p = hier_params(base, fanout, topk2)
     dev = q.device
-    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
-    if lse is None and want_lse:
-        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
-    if want_sel:
-        if sel2 is None:
-            sel2 = torch.empty(B, Hkv, max(topk2, 0), dtype=torch.int32, device=dev)
-        if sel1 is None:
-            sel1 = torch.empty(B, Hkv, max(topk1, 0), dtype=torch.int32, device=dev)
-    nbytes = hier_workspace_size(p)
-    ws = _workspace(workspace, nbytes, dev)
-    _check(lib().gsa_decode_hier(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                 _ptr(k_l2), _ptr(v_l2), _ptr(out), _ptr(lse),
-                                 _ptr(sel2) if topk2 > 0 else None,
-                                 _ptr(sel1) if topk1 > 0 else None, _ptr(ws), _nbytes(ws),
-                                 _stream(stream, dev)), "gsa_decode_hier")
+    s, on_s = _on_stream(stream, dev)
+    with on_s:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
+        if lse is None and want_lse:
+            lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        if want_sel:
+            if sel2 is None:
+                sel2 = torch.empty(B, Hkv, max(topk2, 0), dtype=torch.int32, device=dev)
+            if sel1 is None:
+                sel1 = torch.empty(B, Hkv, max(topk1, 0), dtype=torch.int32, device=dev)
+        ws = _workspace(workspace, hier_workspace_size(p), dev)
+        _check(lib().gsa_decode_hier(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(k_l2), _ptr(v_l2), _ptr(out), _ptr(lse),
+                                     _ptr(sel2) if topk2 > 0 else None,
+                                     _ptr(sel1) if topk1 > 0 else None, _ptr(ws), _nbytes(ws),
+                                     s.cuda_stream), "gsa_decode_hier")
     return out, lse, sel2, sel1
 
 
@@ -437,21 +467,22 @@ def gsa_decode_levels(q, k_cache, v_cache, k_up, v_up, *, chunk: int, fanout: in
                          row_capacity=cap)
     p = levels_params(base, fanout, topks[1:])
     dev = q.device
-    out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
-    if lse is None and want_lse:
-        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
-    sels = ([torch.empty(B, Hkv, max(k, 0), dtype=torch.int32, device=dev) for k in topks]
-            if want_sel else None)
-    n_up = len(k_up)
-    kp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in k_up])
-    vp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in v_up])
-    sp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in sels[1:]]) if want_sel else None
-    nbytes = levels_workspace_size(p)
-    ws = _workspace(workspace, nbytes, dev)
-    _check(lib().gsa_decode_levels(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), kp, vp,
-                                   _ptr(out), _ptr(lse), sp,
-                                   _ptr(sels[0]) if want_sel and topks[0] > 0 else None, _ptr(ws),
-                                   _nbytes(ws), _stream(stream, dev)), "gsa_decode_levels")
+    s, on_s = _on_stream(stream, dev)
+    with on_s:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
+        if lse is None and want_lse:
+            lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        sels = ([torch.empty(B, Hkv, max(k, 0), dtype=torch.int32, device=dev) for k in topks]
+                if want_sel else None)
+        n_up = len(k_up)
+        kp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in k_up])
+        vp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in v_up])
+        sp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in sels[1:]]) if want_sel else None
+        ws = _workspace(workspace, levels_workspace_size(p), dev)
+        _check(lib().gsa_decode_levels(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), kp,
+                                       vp, _ptr(out), _ptr(lse), sp,
+                                       _ptr(sels[0]) if want_sel and topks[0] > 0 else None,
+                                       _ptr(ws), _nbytes(ws), s.cuda_stream), "gsa_decode_levels")
     return out, lse, sels
 
 
@@ -470,15 +501,17 @@ def gsa_prefill_blocksparse(q, k_cache, v_cache, *, chunk: int, topk: int, windo
     p = prefill_params(Hq, Hkv, D, chunk, topk, window, N, M, q_start, n_q, scale,
                        _dtype_code(q), cap)
     dev = q.device
-    out = torch.empty(Hq, n_q, D, dtype=torch.float32, device=dev) if out is None else out
-    if sel is None and want_sel:
-        sel = torch.empty(Hkv, n_q, max(topk, 0), dtype=torch.int32, device=dev)
-    nbytes = prefill_workspace_size(p)
-    ws = _workspace(workspace, nbytes, dev)
-    _check(lib().gsa_prefill_blocksparse(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                         _ptr(out), _ptr(sel) if topk > 0 else None, _ptr(ws),
-                                         _nbytes(ws), _stream(stream, dev)),
-           "gsa_prefill_blocksparse")
+    s, on_s = _on_stream(stream, dev)
+    with on_s:
+        out = torch.empty(Hq, n_q, D, dtype=torch.float32, device=dev) if out is None else out
+        if sel is None and want_sel:
+            sel = torch.empty(Hkv, n_q, max(topk, 0), dtype=torch.int32, device=dev)
+        ws = _workspace(workspace, prefill_workspace_size(p), dev)
+        _check(lib().gsa_prefill_blocksparse(ctypes.byref(p), _ptr(q), _ptr(k_cache),
+                                             _ptr(v_cache), _ptr(out),
+                                             _ptr(sel) if topk > 0 else None, _ptr(ws),
+                                             _nbytes(ws), s.cuda_stream),
+               "gsa_prefill_blocksparse")
     return out, sel
 
 
@@ -496,9 +529,11 @@ def gsa_gist_prefill(q, k_cache, v_cache, *, chunk: int, m_start: int,
     N, M, cap = _geometry(R, chunk, n_gist, n_raw)
     p = gist_params(Hq, Hkv, D, chunk, N, M, m_start, n_q, scale, _dtype_code(q), cap)
     dev = q.device
-    out = torch.empty(Hq, n_q, D, dtype=torch.float32, device=dev) if out is None else out
-    _check(lib().gsa_gist_prefill(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
-                                  _stream(stream, dev)), "gsa_gist_prefill")
+    s, on_s = _on_stream(stream, dev)
+    with on_s:
+        out = torch.empty(Hq, n_q, D, dtype=torch.float32, device=dev) if out is None else out
+        _check(lib().gsa_gist_prefill(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(out), s.cuda_stream), "gsa_gist_prefill")
     return out
 
 
@@ -533,5 +568,6 @@ def gsa_cache_append(k_cache, v_cache, *, chunk: int, n_raw: int, n_gist: int, k
     _check(lib().gsa_cache_append(ctypes.byref(p), _ptr(k_raw) if n_new else None,
                                   _ptr(v_raw) if n_new else None, _ptr(k_gist) if g_new else None,
                                   _ptr(v_gist) if g_new else None, _ptr(k_cache), _ptr(v_cache),
-                                  _stream(stream, k_cache.device)), "gsa_cache_append")
+                                  _on_stream(stream, k_cache.device)[0].cuda_stream),
+           "gsa_cache_append")
 

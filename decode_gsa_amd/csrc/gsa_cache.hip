@@ -62,6 +62,7 @@ extern "C" gsa_status_t gsa_cache_append(const gsa_append_params* p, const void*
                                          const void* k_gist, const void* v_gist, void* k_cache, void* v_cache,
                                          void* stream) {
   clear_error();
+  prof_begin_call();
   AppendPlan pl;
   gsa_status_t s = plan_append(p, &pl);
   if (s != GSA_OK) return s;
@@ -108,7 +109,6 @@ extern "C" gsa_status_t gsa_cache_append(const gsa_append_params* p, const void*
   const int64_t vecs = pl.units * most * a.vpr;
   const int64_t wgs = (vecs + 255) / 256;
   const unsigned gx = (unsigned)(wgs < 4096 ? wgs : 4096);
-  prof_begin_call();
   prof_launch(cache_append, dim3(gx, nj), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(GSA_ERR_HIP, "gsa_cache_append launch: %s", hipGetErrorString(e));

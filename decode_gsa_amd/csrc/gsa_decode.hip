@@ -2356,7 +2356,7 @@ gsa_status_t run_unit_levels(const LevelsPlan& lp, const void* q, const void* K,
     }
   }
   prof_begin_call();
-  if (lp.Ml[Lv] <= kUMaxGist && lp.Ml[Lv] + pl.T <= kUWgItems) {
+  if (levels_top_in_lds(lp)) {
     // the top level fits one workgroup's LDS scores: one launch
     prof_launch((unit_levels_kernel<G, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
   } else {
@@ -2541,6 +2541,7 @@ extern "C" gsa_status_t gsa_decode(const gsa_decode_params* p, const void* q, co
                                    const void* v_cache, float* out, float* lse, int32_t* sel_idx,
                                    void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
+  prof_begin_call();
   DecodePlan pl;
   gsa_status_t s = plan_decode(p, &pl);
   if (s != GSA_OK) return s;
@@ -2577,6 +2578,7 @@ extern "C" gsa_status_t gsa_decode_hier(const gsa_hier_params* p, const void* q,
                                         float* out, float* lse, int32_t* sel2, int32_t* sel1,
                                         void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
+  prof_begin_call();
   HierPlan hp;
   gsa_status_t s = plan_hier(p, &hp);
   if (s != GSA_OK) return s;
@@ -2619,6 +2621,7 @@ extern "C" gsa_status_t gsa_decode_levels(const gsa_levels_params* p, const void
                                           int32_t* const* sel_up, int32_t* sel1, void* workspace,
                                           size_t workspace_bytes, void* stream) {
   clear_error();
+  prof_begin_call();
   LevelsPlan lp;
   gsa_status_t s = plan_levels(p, &lp);
   if (s != GSA_OK) return s;
@@ -2657,6 +2660,7 @@ extern "C" gsa_status_t gsa_decode_varlen(const gsa_decode_params* p, const int3
                                           const void* v_cache, float* out, float* lse, int32_t* sel_idx,
                                           void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
+  prof_begin_call();
   DecodePlan pl;
   gsa_status_t s = plan_decode(p, &pl);
   if (s != GSA_OK) return s;

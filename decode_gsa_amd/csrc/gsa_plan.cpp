@@ -511,6 +511,26 @@ gsa_status_t plan_append(const gsa_append_params* p, AppendPlan* o) {
   return GSA_OK;
 }
 
+int32_t decode_launches(const DecodePlan& d) {
+  if (d.unit_S > 0) return 1 + (d.unit_S2 > 0 ? 1 : 0);
+  return 1 + (d.cand_stride > 0 ? 1 : 0) + (d.k > 0 ? 1 : 0);
+}
+
+int32_t hier_launches(const HierPlan& h) {
+  if (h.unit_S > 0) return 2;
+  return 2 + (h.cand2_stride > 0 ? 1 : 0) + (h.base.k > 0 ? 1 : 0);
+}
+
+int32_t levels_launches(const LevelsPlan& l) {
+  if (l.unit_S > 0) return levels_top_in_lds(l) ? 1 : 2;
+  return l.L + (l.base.k > 0 ? 1 : 0);
+}
+
+int32_t prefill_launches(const PrefillPlan& p) {
+  if (p.n_q == 0) return 0;
+  return (p.k > 0 ? 1 : 0) + 1;
+}
+
 }  // namespace gsa
 
 extern "C" gsa_status_t gsa_check_seq_lens(const gsa_decode_params* p, const int32_t* seq_n_raw,
@@ -564,3 +584,43 @@ extern "C" const char* gsa_status_string(gsa_status_t s) {
 }
 
 extern "C" const char* gsa_last_error(void) { return gsa::last_error_message(); }
+
+extern "C" gsa_status_t gsa_decode_launches(const gsa_decode_params* p, int32_t* n) {
+  gsa::clear_error();
+  if (!n) return gsa::fail(GSA_ERR_INVALID_ARG, "n is NULL");
+  gsa::DecodePlan d;
+  gsa_status_t s = gsa::plan_decode(p, &d);
+  if (s != GSA_OK) return s;
+  *n = gsa::decode_launches(d);
+  return GSA_OK;
+}
+
+extern "C" gsa_status_t gsa_decode_hier_launches(const gsa_hier_params* p, int32_t* n) {
+  gsa::clear_error();
+  if (!n) return gsa::fail(GSA_ERR_INVALID_ARG, "n is NULL");
+  gsa::HierPlan h;
+  gsa_status_t s = gsa::plan_hier(p, &h);
+  if (s != GSA_OK) return s;
+  *n = gsa::hier_launches(h);
+  return GSA_OK;
+}
+
+extern "C" gsa_status_t gsa_decode_levels_launches(const gsa_levels_params* p, int32_t* n) {
+  gsa::clear_error();
+  if (!n) return gsa::fail(GSA_ERR_INVALID_ARG, "n is NULL");
+  gsa::LevelsPlan l;
+  gsa_status_t s = gsa::plan_levels(p, &l);
+  if (s != GSA_OK) return s;
+  *n = gsa::levels_launches(l);
+  return GSA_OK;
+}
+
+extern "C" gsa_status_t gsa_prefill_launches(const gsa_prefill_params* p, int32_t* n) {
+  gsa::clear_error();
+  if (!n) return gsa::fail(GSA_ERR_INVALID_ARG, "n is NULL");
+  gsa::PrefillPlan pl;
+  gsa_status_t s = gsa::plan_prefill(p, &pl);
+  if (s != GSA_OK) return s;
+  *n = gsa::prefill_launches(pl);
+  return GSA_OK;
+}

@@ -159,6 +159,12 @@ struct LevelsPlan {
 
 gsa_status_t plan_levels(const gsa_levels_params* p, LevelsPlan* out);
 
+// One-workgroup-per-unit L-level path: the top level fits one workgroup's LDS
+// scores, so the descent's workgroup streams it itself (one launch per call).
+inline bool levels_top_in_lds(const LevelsPlan& l) {
+  return l.Ml[l.L] <= kUnitMaxGist && l.Ml[l.L] + l.base.T <= kUnitWgItems;
+}
+
 // Prefill plan.
 struct PrefillPlan {
   int32_t Hq, Hkv, g, D, C, k, W;
@@ -187,6 +193,13 @@ struct AppendPlan {
   int64_t N, M, raw_new, gist_new, R;
 };
 gsa_status_t plan_append(const gsa_append_params* p, AppendPlan* out);
+
+// Kernel launches a call with this plan makes (what gsa_profile_marks reports,
+// minus one). Each matches the launch sequence of the entry point's runner.
+int32_t decode_launches(const DecodePlan& d);
+int32_t hier_launches(const HierPlan& h);
+int32_t levels_launches(const LevelsPlan& l);
+int32_t prefill_launches(const PrefillPlan& p);
 
 // Pointer checks shared by the entry points.
 gsa_status_t check_ptr(const void* p, const char* name, bool allow_null = false);

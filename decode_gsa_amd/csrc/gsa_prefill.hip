@@ -1030,10 +1030,10 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
 template <int G>
 gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, const void* V, float* out,
                          int32_t* sel, char* ws, hipStream_t stream) {
+  prof_begin_call();
   if (pl.n_q == 0) return GSA_OK;
   int32_t* wsel = reinterpret_cast<int32_t*>(ws);
   const int grid = pl.n_blocks * pl.Hkv;
-  prof_begin_call();
   if (pl.k > 0) {
     SelArgs s{};
     s.q = q; s.K = K; s.R = pl.R;
@@ -1076,11 +1076,13 @@ extern "C" gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, con
                                                 int32_t* sel, void* workspace, size_t workspace_bytes,
                                                 void* stream) {
   clear_error();
+  prof_begin_call();
   PrefillPlan pl;
   gsa_status_t s = plan_prefill(p, &pl);
   if (s != GSA_OK) return s;
-  if ((s = check_ptr(q, "q")) != GSA_OK || (s = check_ptr(k_cache, "k_cache")) != GSA_OK ||
-      (s = check_ptr(v_cache, "v_cache")) != GSA_OK || (s = check_ptr(out, "out")) != GSA_OK ||
+  const bool none = pl.n_q == 0;   // no queries: q, out (and sel) may be NULL
+  if ((s = check_ptr(q, "q", none)) != GSA_OK || (s = check_ptr(k_cache, "k_cache")) != GSA_OK ||
+      (s = check_ptr(v_cache, "v_cache")) != GSA_OK || (s = check_ptr(out, "out", none)) != GSA_OK ||
       (s = check_ptr(sel, "sel", true)) != GSA_OK)
     return s;
   if ((s = check_workspace(workspace, workspace_bytes, pl.total)) != GSA_OK) return s;
@@ -1097,11 +1099,13 @@ extern "C" gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, con
 extern "C" gsa_status_t gsa_gist_prefill(const gsa_gist_params* p, const void* q, const void* k_cache,
                                          const void* v_cache, float* out, void* stream) {
   clear_error();
+  prof_begin_call();
   PrefillPlan pl;
   gsa_status_t s = plan_gist(p, &pl);
   if (s != GSA_OK) return s;
-  if ((s = check_ptr(q, "q")) != GSA_OK || (s = check_ptr(k_cache, "k_cache")) != GSA_OK ||
-      (s = check_ptr(v_cache, "v_cache")) != GSA_OK || (s = check_ptr(out, "out")) != GSA_OK)
+  const bool none = pl.n_q == 0;   // no queries: q and out may be NULL
+  if ((s = check_ptr(q, "q", none)) != GSA_OK || (s = check_ptr(k_cache, "k_cache")) != GSA_OK ||
+      (s = check_ptr(v_cache, "v_cache")) != GSA_OK || (s = check_ptr(out, "out", none)) != GSA_OK)
     return s;
   // k = 0: no selection launch, no workspace
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -219,9 +219,9 @@ gsa_status_t gsa_decode_levels_workspace_size(const gsa_levels_params* p, size_t
  *              (ascending); an entry may be NULL
  * sel1         [B, Hkv, k_1] int32 chosen chunk ids (ascending) or NULL
  * workspace    as gsa_decode (zero-filled once; left zero by each call)
- * Runs a pass over the top level and the tail, one pass per lower level
- * (scoring and attending its candidates, selecting among the level above's
- * scores), and the unfold: L + 1 launches (L when k_1 = 0).
+ * The work is a pass over the top level and the tail, then per lower level a
+ * selection among the level above's scores and a pass over its candidates,
+ * then the unfold. gsa_decode_levels_launches gives the launch count.
  * GSA_ERR_INVALID_ARG for out-of-range sizes or NULL arrays;
  * GSA_ERR_UNSUPPORTED for g outside {1, 2, 4, 8}, D outside {64, 128}.
  */
@@ -245,18 +245,20 @@ gsa_status_t gsa_decode_levels(const gsa_levels_params* p, const void* q, const 
  * [t - W + 1, t].
  * ---------------------------------------------------------------------- */
 typedef struct {
-  int32_t n_q_heads;   /* Hq, multiple of n_kv_heads; g in {1, 2, 4, 8} */
+  int32_t n_q_heads;   /* Hq, multiple of n_kv_heads; g = Hq/Hkv in {1, 2, 4}
+                          (other g: GSA_ERR_UNSUPPORTED) */
   int32_t n_kv_heads;  /* Hkv >= 1 */
-  int32_t head_dim;    /* D: 128 */
+  int32_t head_dim;    /* D: 128 (others: GSA_ERR_UNSUPPORTED) */
   int32_t chunk;       /* C >= 1 */
-  int32_t topk;        /* k >= 0 */
+  int32_t topk;        /* 0 <= k <= 32 (k > 32: GSA_ERR_UNSUPPORTED) */
   int32_t window;      /* W >= 1 */
   int64_t n_raw;       /* N raw tokens in the cache */
-  int64_t n_gist;      /* M; 0 <= N - M*C <= C */
+  int64_t n_gist;      /* M; 0 <= N - M*C <= C; M <= 65536 (above:
+                          GSA_ERR_UNSUPPORTED) */
   int64_t q_start;     /* first query position, 0 <= q_start */
   int64_t n_q;         /* queries; q_start + n_q <= N */
   float scale;         /* <= 0: 1/sqrt(D) */
-  int32_t dtype;       /* GSA_BF16 */
+  int32_t dtype;       /* GSA_BF16 (GSA_F32: GSA_ERR_UNSUPPORTED) */
   int64_t row_capacity; /* rows per kv-head in the caches (their stride);
                            0: R = N + M, else >= N + M */
 } gsa_prefill_params;
@@ -271,6 +273,7 @@ gsa_status_t gsa_prefill_workspace_size(const gsa_prefill_params* p, size_t* byt
  * out     [Hq, n_q, D] fp32   attention output (written)
  * sel     [Hkv, n_q, k] int32 chosen chunks per query, ascending, -1 padded,
  *                             or NULL
+ * With n_q = 0 nothing is launched and q, out may be NULL.
  */
 gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, const void* q,
                                      const void* k_cache, const void* v_cache, float* out,
@@ -309,7 +312,8 @@ typedef struct {
  * k_cache [Hkv, R, D]         interleaved cache of the sequence
  * v_cache [Hkv, R, D]
  * out     [Hq, n_q, D] fp32   attention output (written)
- * No workspace. GSA_ERR_INVALID_ARG for a NULL pointer or a query range the
+ * No workspace. With n_q = 0 nothing is launched and q, out may be NULL.
+ * GSA_ERR_INVALID_ARG for a NULL pointer or a query range the
  * cache cannot serve; GSA_ERR_UNSUPPORTED for shapes the kernel does not
  * run (as gsa_prefill_blocksparse: bf16, D = 128, g in {1, 2, 4},
  * M <= 65536, N + M < 2^31).
@@ -363,28 +367,43 @@ gsa_status_t gsa_cache_append(const gsa_append_params* p, const void* k_raw, con
  * hipEvent_t handles (passed as void*). Every later call on this thread
  * attaches them to its kernel launches (hipExtLaunchKernel): events[0] takes
  * the start of the call's first kernel and events[i] the end of its i-th
- * kernel, for as many events as there are. Launches per call:
- *   gsa_decode, bf16 with D = 128, topk <= 64, n_gist <= 16384 when topk > 0
- *     and n_gist + tail <= 256 * 5120: one launch when each (batch, kv-head)
- *     unit takes one workgroup (B*Hkv >= 256 and n_gist <= 4096) or topk = 0;
- *     otherwise a stream launch (several workgroups per unit) and a
- *     select-and-unfold launch;
- *   gsa_decode, other shapes: a gist pass, then an unfold pass when topk > 0;
- *   gsa_decode_varlen: as gsa_decode for the same parameters;
- *   gsa_decode_hier: level-2 pass, level-1 candidate pass, unfold pass when
- *     topk1 > 0;
- *   gsa_decode_levels: top-level pass, one pass per lower level, unfold pass
- *     when k_1 > 0;
- *   gsa_prefill_blocksparse: selection when topk > 0, then attention.
- *   gsa_gist_prefill: attention; gsa_cache_append: one copy launch.
+ * kernel, for as many events as there are. The launch count of a call comes
+ * from the gsa_*_launches queries below (gsa_gist_prefill: 1 launch when
+ * n_q > 0; gsa_cache_append: 1 when anything is appended; 0 otherwise).
  * The library never creates, waits on or destroys the events. n = 0 disarms.
  * Returns GSA_ERR_INVALID_ARG for n outside [0, 8] or a NULL handle.
  * ---------------------------------------------------------------------- */
 gsa_status_t gsa_profile_events(void* const* events, int32_t n);
 
-/* Number of marks (kernel launches + 1) the last call on this thread made,
- * armed or not; 0 before any call. GSA_ERR_INVALID_ARG for a NULL n. */
+/* Number of marks (kernel launches + 1) the last call of a launching entry
+ * point on this thread made, armed or not (a rejected call launched nothing:
+ * 1); 0 before any such call. GSA_ERR_INVALID_ARG for a NULL n. */
 gsa_status_t gsa_profile_marks(int32_t* n);
+
+/* Host-only queries: *n = the number of kernel launches a call with these
+ * parameters makes (the timing hook takes *n + 1 events), after the same
+ * validation as the call itself (its status on failure). The counts:
+ *   gsa_decode / gsa_decode_varlen on the bf16, D = 128, topk <= 64 path
+ *     (n_gist <= 16384 when topk > 0): 1 when each (batch, kv-head) unit
+ *     takes one workgroup (B*Hkv >= 256 and n_gist <= 4096) or topk = 0,
+ *     else 2 (a stream launch, then a select-unfold-merge launch);
+ *     other shapes: 1 when topk = 0, else 2 or 3 (a gist pass, a pass that
+ *     takes each split's top-k when there are many gists per unit, an
+ *     unfold pass);
+ *   gsa_decode_hier on the bf16, D = 128, k1, k2 <= 64 path: 2 (the
+ *     level-2 stream, then the descent); other shapes: 2 to 4 (a level-2
+ *     pass, possibly a pass over its splits' top-k2, a level-1 candidate
+ *     pass, and an unfold pass when topk1 > 0);
+ *   gsa_decode_levels on the bf16, D = 128, every k <= 64 path: 1 when the
+ *     top level holds <= 4096 gists and top + tail <= 5120 rows, else 2;
+ *     other shapes: one pass per level and an unfold pass when k_1 > 0;
+ *   gsa_prefill_blocksparse: 0 when n_q = 0, else a selection launch when
+ *     topk > 0 and an attention launch.
+ * GSA_ERR_INVALID_ARG for a NULL n. */
+gsa_status_t gsa_decode_launches(const gsa_decode_params* p, int32_t* n);
+gsa_status_t gsa_decode_hier_launches(const gsa_hier_params* p, int32_t* n);
+gsa_status_t gsa_decode_levels_launches(const gsa_levels_params* p, int32_t* n);
+gsa_status_t gsa_prefill_launches(const gsa_prefill_params* p, int32_t* n);
 
 /* ------------------------------------------------------------------------
  * Fixed-token-budget mode (slide deck, slide 17: under one token budget,

@@ -52,14 +52,19 @@ Readings where the pages are silent (each also listed in the design notes):
      (0..C of them) must lie inside the tail;
   R6 prefill eligibility: query t may use gist m only if m < floor(t / C);
      the window is raw positions [t - W + 1, t];
-  R8 gist causal mask: the listed rows are the chunk's C raw tokens and the
-     earlier gists; the gist token's own key is not among them (slide 7
-     lists g1 -> x1, x2 and g2 -> g1, x3, x4);
   R7 two-level: level-2 gists live in their own array; group i covers chunks
      [i G, (i + 1) G); the level-1 gists that no full group covers are always
      candidates; the attention set holds every level-2 gist, every candidate
-     level-1 gist, the raw rows of the selected chunks and the tail.
-  R9 L levels: level l >= 2 has M_l = floor(M_{l-1} / G) gists in its own
+     level-1 gist, the raw rows of the selected chunks and the tail;
+  R8 the default attention set keeps every gist (all gists + selected raw +
+     tail); R12 the slide 17 variants keep the chosen chunks' gists or none;
+  R13 gist causal mask: the listed rows are the chunk's C raw tokens and the
+     earlier gists; the gist token's own key is not among them (slide 7
+     lists g1 -> x1, x2 and g2 -> g1, x3, x4; its third line, which reads
+     g3 -> g1, g2, x5, g3, is taken as g3 -> g1, g2, x5, x6: one garbled
+     symbol, where a literal self-key would also break the first two lines'
+     pattern and leave chunk 3 without its second raw token);
+  R15 L levels: level l >= 2 has M_l = floor(M_{l-1} / G) gists in its own
      array, gist i of level l summarising gists [i G, (i + 1) G) of level
      l - 1; top-down, every level's candidates are the children of the
      level above's selection plus that level's ungrouped gists (every gist at
@@ -78,8 +83,8 @@ import numpy as np
 
 __all__ = [
     "gist_row_index", "raw_row_index", "topk_ascending",
-    "decode_unit", "decode", "decode_hier_unit", "decode_hier", "decode_levels_unit", "decode_levels", "topk_for_budget", "GIST_SETS",
-    "prefill_query", "prefill", "cache_row", "gist_query", "gist_prefill",
+    "decode_unit", "decode", "decode_hier_unit", "decode_hier", "decode_levels_unit", "topk_for_budget", "GIST_SETS",
+    "prefill_query", "prefill", "cache_row", "gist_query",
 ]
 
 
@@ -357,7 +362,7 @@ def decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int, top
 def decode_levels_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, upper, *, n_raw: int,
                        n_gist: int, chunk: int, fanout: int, topks, tail: int,
                        scale: Optional[float] = None) -> Dict[str, object]:
-    """One unit of L-level decode (R9; explainer 'Hierarchical Extension
+    """One unit of L-level decode (R15; explainer 'Hierarchical Extension
     (H-GSA)' and 'Coarse-to-Fine Selection', slide 11).
 
     upper: [(K_2, V_2), ..., (K_L, V_L)], K_l: [M_l, D] with
@@ -414,31 +419,6 @@ def decode_levels_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, upper, *, n
     return {"out": out, "lse": lse, "wsum": wsum,
             "sels": [np.array(sels[l], dtype=np.int64) for l in range(1, L + 1)],
             "cands": [np.array(cands[l], dtype=np.int64) for l in range(1, L + 1)], "rows": rows}
-
-
-def decode_levels(q, k_cache, v_cache, upper, *, chunk: int, fanout: int, topks, tail: int,
-                  n_gist: Optional[int] = None, scale: Optional[float] = None, units=None):
-    """Batched L-level decode. upper: [(K_2, V_2), ...] each [B, Hkv, M_l, D].
-    Returns out [B, Hq, D], lse [B, Hq], sels [[B, Hkv, k_l] for l = 1..L]."""
-    B, Hq, D = q.shape
-    Hkv, R = k_cache.shape[1], k_cache.shape[2]
-    g = Hq // Hkv
-    if n_gist is None:
-        n_gist = R // (chunk + 1)
-    n_raw = R - n_gist
-    out = np.full((B, Hq, D), np.nan)
-    lse = np.full((B, Hq), np.nan)
-    sels = [np.full((B, Hkv, k), -1, dtype=np.int64) for k in topks]
-    todo = [(b, j) for b in range(B) for j in range(Hkv)] if units is None else units
-    for b, j in todo:
-        r = decode_levels_unit(q[b, j * g:(j + 1) * g], k_cache[b, j], v_cache[b, j],
-                               [(Ku[b, j], Vu[b, j]) for Ku, Vu in upper], n_raw=n_raw, n_gist=n_gist,
-                               chunk=chunk, fanout=fanout, topks=topks, tail=tail, scale=scale)
-        out[b, j * g:(j + 1) * g] = r["out"]
-        lse[b, j * g:(j + 1) * g] = r["lse"]
-        for l, sl in enumerate(r["sels"]):
-            sels[l][b, j] = sl
-    return out, lse, sels
 
 
 # --------------------------------------------------------------- prefill ---
@@ -525,7 +505,7 @@ def cache_row(position: int, chunk: int, is_gist: bool) -> int:
 
 def gist_query(qg: np.ndarray, K: np.ndarray, V: np.ndarray, *, m: int, n_raw: int,
                n_gist: int, chunk: int, scale: Optional[float] = None) -> Dict[str, np.ndarray]:
-    """Attention of chunk m's gist token under the gist causal mask (R8): its
+    """Attention of chunk m's gist token under the gist causal mask (R13): its
     own chunk's C raw tokens and the gists of chunks 0..m-1.
 
     qg: [g, D] the gist token's query heads of one kv-group.  K, V: [R, D].
@@ -544,25 +524,4 @@ def gist_query(qg: np.ndarray, K: np.ndarray, V: np.ndarray, *, m: int, n_raw: i
     rows = np.array(sorted(rows), dtype=np.int64)
     out, lse, wsum = _softmax_attend(qg, _f64(K[rows]), _f64(V[rows]), scale)
     return {"out": out, "lse": lse, "wsum": wsum, "rows": rows}
-
-
-def gist_prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, *, chunk: int,
-                 m_start: int, n_gist: Optional[int] = None, scale: Optional[float] = None,
-                 queries: Optional[Iterable[Tuple[int, int]]] = None):
-    """Gist tokens of chunks [m_start, m_start + n) for one sequence.
-    q [Hq, n, D]; caches [Hkv, R, D]. Returns out [Hq, n, D] (entries not in
-    ``queries`` -- (i, kv-head) pairs -- are NaN)."""
-    Hq, n, D = q.shape
-    Hkv, R = k_cache.shape[0], k_cache.shape[1]
-    g = Hq // Hkv
-    if n_gist is None:
-        n_gist = R // (chunk + 1)
-    n_raw = R - n_gist
-    out = np.full((Hq, n, D), np.nan)
-    todo = [(i, j) for i in range(n) for j in range(Hkv)] if queries is None else queries
-    for i, j in todo:
-        r = gist_query(q[j * g:(j + 1) * g, i], k_cache[j], v_cache[j], m=m_start + i, n_raw=n_raw,
-                       n_gist=n_gist, chunk=chunk, scale=scale)
-        out[j * g:(j + 1) * g, i] = r["out"]
-    return out
 

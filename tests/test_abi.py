@@ -298,7 +298,7 @@ def good_gist(**kw):
     ({"n_q_heads": 16, "n_kv_heads": 2}, UNSUPPORTED),
     ({"chunk": 0}, INVALID),
     ({"row_capacity": 1000}, INVALID),
-    ({"n_q": 0}, "ok"),
+    ({"n_q": 0}, OK),                   # nothing to launch: NULL q and out are allowed
 ])
 def test_gist_prefill_validation(L, kw, status):
     """Shape errors come back with their status; shapes that pass validation
@@ -450,3 +450,109 @@ def test_decode_varlen_rejections(L):
     assert call(p, FAKE, FAKE + 4) == INVALID                       # misaligned
     assert call(varlen_params(gist_set=1, batch=128), FAKE, FAKE) == UNSUPPORTED
 
+
+
+# ------------------------------------------- documented sets vs validation ---
+
+def _block(text, start, end):
+    i = text.index(start)
+    return text[i:text.index(end, i)]
+
+
+def test_documented_head_and_type_sets_match_validation(L):
+    """The g / head_dim / dtype sets the header documents for each entry point
+    are exactly the ones host validation accepts (everything else is
+    GSA_ERR_UNSUPPORTED), and the header still states those sets."""
+    text = open(HEADER).read()
+    dec = _block(text, "typedef struct {\n  int32_t batch;", "} gsa_decode_params;")
+    assert "g = Hq/Hkv must be 1, 2, 4 or 8" in dec and "D: 64 or 128" in dec
+    pre = _block(text, "typedef struct {\n  int32_t n_q_heads;", "} gsa_prefill_params;")
+    assert "g = Hq/Hkv in {1, 2, 4}" in pre and "D: 128" in pre and "GSA_BF16 (GSA_F32" in pre
+    gis = _block(text, "gsa_status_t gsa_prefill_blocksparse(", "gsa_status_t gsa_gist_prefill(")
+    assert "g in {1, 2, 4}" in gis
+    n = ctypes.c_size_t(0)
+    for g in range(1, 10):
+        for D in (32, 64, 96, 128, 256):
+            for dt in (gsa.GSA_F32, gsa.GSA_BF16):
+                want = OK if g in (1, 2, 4, 8) and D in (64, 128) else UNSUPPORTED
+                p = good_decode(n_q_heads=2 * g, n_kv_heads=2, head_dim=D, dtype=dt)
+                assert L.gsa_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == want, (g, D, dt)
+                h = gsa.HierParams(p, 4, 2)
+                assert L.gsa_decode_hier_workspace_size(ctypes.byref(h), ctypes.byref(n)) == want
+                lv = gsa.levels_params(p, 4, [2, 1])
+                assert L.gsa_decode_levels_workspace_size(ctypes.byref(lv), ctypes.byref(n)) == want
+                want_p = OK if g in (1, 2, 4) and D == 128 and dt == gsa.GSA_BF16 else UNSUPPORTED
+                pp = good_prefill(n_q_heads=2 * g, n_kv_heads=2, head_dim=D, dtype=dt)
+                assert L.gsa_prefill_workspace_size(ctypes.byref(pp), ctypes.byref(n)) == want_p, (g, D, dt)
+                gp = gsa.gist_params(2 * g, 2, D, 16, 1024, 64, 0, 8, dtype=dt)
+                # validation runs before the NULL-pointer checks: a rejected shape
+                # reports its status, an accepted one fails on the NULL q
+                st = L.gsa_gist_prefill(ctypes.byref(gp), None, None, None, None, None)
+                assert st == (INVALID if want_p == OK else UNSUPPORTED), (g, D, dt)
+
+
+def test_prefill_documented_limits(L):
+    n = ctypes.c_size_t(0)
+    for k, want in ((32, OK), (33, UNSUPPORTED)):
+        assert L.gsa_prefill_workspace_size(ctypes.byref(good_prefill(topk=k)), ctypes.byref(n)) == want
+    big = good_prefill(n_raw=16 * 65537, n_gist=65537, q_start=0, n_q=64)
+    assert L.gsa_prefill_workspace_size(ctypes.byref(big), ctypes.byref(n)) == UNSUPPORTED
+    ok = good_prefill(n_raw=16 * 65536, n_gist=65536, q_start=0, n_q=64)
+    assert L.gsa_prefill_workspace_size(ctypes.byref(ok), ctypes.byref(n)) == OK
+
+
+def _launches(L, fn, p):
+    n = ctypes.c_int32(-1)
+    st = getattr(L, fn)(ctypes.byref(p), ctypes.byref(n))
+    return st, n.value
+
+
+def test_launch_counts_follow_the_documented_rules(L):
+    """gsa_*_launches against the counts the header documents per path."""
+    assert L.gsa_decode_launches(ctypes.byref(good_decode()), None) == INVALID
+    # unit path, one workgroup per unit: 256 units, <= 4096 gists
+    one = gsa.decode_params(32, 32, 8, 128, 32768, 2048, 16, 16, 64)
+    assert _launches(L, "gsa_decode_launches", one) == (OK, 1)
+    # unit path, several workgroups per unit: a stream and a select-unfold launch
+    few = gsa.decode_params(8, 32, 8, 128, 131072, 4096, 32, 16, 64)
+    assert _launches(L, "gsa_decode_launches", few) == (OK, 2)
+    few0 = gsa.decode_params(8, 32, 8, 128, 131072, 4096, 32, 0, 64)
+    assert _launches(L, "gsa_decode_launches", few0) == (OK, 1)
+    many = gsa.decode_params(32, 32, 8, 128, 5000 * 16, 5000, 16, 16, 64)   # > 4096 gists
+    assert _launches(L, "gsa_decode_launches", many) == (OK, 2)
+    # split path (fp32 / D = 64 / k > 64): 1 with k = 0, else 2 or 3
+    for kw in (dict(dtype=gsa.GSA_F32), dict(head_dim=64), dict(topk=80)):
+        st, n = _launches(L, "gsa_decode_launches", good_decode(n_raw=4096, n_gist=256, **kw))
+        assert st == OK and n in (2, 3), kw
+        st, n = _launches(L, "gsa_decode_launches", good_decode(n_raw=4096, n_gist=256, **{**kw, "topk": 0}))
+        assert (st, n) == (OK, 1), kw
+    # a split path with many gists per unit takes the candidate pass
+    st, n = _launches(L, "gsa_decode_launches", gsa.decode_params(1, 4, 1, 128, 1 << 20, 1 << 16, 16, 16, 64,
+                                                                  dtype=gsa.GSA_F32))
+    assert (st, n) == (OK, 3)
+    tiny = gsa.decode_params(1, 1, 1, 64, 4096, 256, 16, 8, 16, dtype=gsa.GSA_F32)
+    assert _launches(L, "gsa_decode_launches", tiny) == (OK, 3)   # 4 splits of 64 gists, k = 8
+    # two-level
+    hb = gsa.decode_params(4, 32, 8, 128, 1 << 20, 1 << 16, 16, 16, 64)
+    assert _launches(L, "gsa_decode_hier_launches", gsa.HierParams(hb, 16, 8)) == (OK, 2)
+    hf = gsa.decode_params(2, 8, 2, 64, 1 << 16, 1 << 12, 16, 16, 64, dtype=gsa.GSA_F32)
+    st, n = _launches(L, "gsa_decode_hier_launches", gsa.HierParams(hf, 16, 8))
+    assert st == OK and n in (3, 4)
+    hf0 = gsa.decode_params(2, 8, 2, 64, 1 << 16, 1 << 12, 16, 0, 64, dtype=gsa.GSA_F32)
+    st, n = _launches(L, "gsa_decode_hier_launches", gsa.HierParams(hf0, 16, 8))
+    assert st == OK and n in (2, 3)
+    # L levels
+    lb = gsa.decode_params(1, 32, 8, 128, 1 << 21, 1 << 17, 16, 16, 64)
+    small_top = gsa.levels_params(lb, 16, [8, 8, 8])      # top level 32 gists
+    assert _launches(L, "gsa_decode_levels_launches", small_top) == (OK, 1)
+    big_top = gsa.levels_params(lb, 16, [8])              # top level 8192 gists
+    assert _launches(L, "gsa_decode_levels_launches", big_top) == (OK, 2)
+    lf = gsa.decode_params(1, 4, 1, 64, 1 << 16, 1 << 12, 16, 4, 64, dtype=gsa.GSA_F32)
+    assert _launches(L, "gsa_decode_levels_launches", gsa.levels_params(lf, 4, [4, 2])) == (OK, 4)
+    lf0 = gsa.decode_params(1, 4, 1, 64, 1 << 16, 1 << 12, 16, 0, 64, dtype=gsa.GSA_F32)
+    assert _launches(L, "gsa_decode_levels_launches", gsa.levels_params(lf0, 4, [4, 2])) == (OK, 3)
+    # prefill
+    assert _launches(L, "gsa_prefill_launches", good_prefill()) == (OK, 2)
+    assert _launches(L, "gsa_prefill_launches", good_prefill(topk=0)) == (OK, 1)
+    assert _launches(L, "gsa_prefill_launches", good_prefill(n_q=0)) == (OK, 0)
+    assert _launches(L, "gsa_prefill_launches", good_prefill(topk=33)) == (UNSUPPORTED, -1)

@@ -156,6 +156,33 @@ def test_decode_repeatable_and_stream(gsa):
     assert torch.equal(a[0], b[0]) and torch.equal(a[2], b[2]) and torch.equal(a[1], b[1])
 
 
+def test_decode_on_a_stream_that_is_not_current(gsa):
+    """stream=s while another stream is current and no workspace is given: the
+    binding allocates the outputs and the zero-filled workspace on s, so the
+    fill is ordered before the launch (the several-workgroups-per-unit launch
+    uses the workspace's arrival counters). Checked against the oracle, then
+    again after the allocator has had the chance to reuse the freed memory."""
+    cfg = small("c32_131k", batch=2, n_kv_heads=2, n_q_heads=8, n_raw=65536)
+    inp = gi.make_decode(cfg, 2011, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    for rep in range(2):
+        out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=cfg.chunk,
+                                       topk=cfg.topk, tail=cfg.tail, stream=s)
+        junk = torch.full((1 << 22,), 7, dtype=torch.uint8, device="cuda")   # current stream
+        s.synchronize()
+        del junk
+        for b in range(cfg.batch):
+            for j in range(cfg.n_kv_heads):
+                r = oracle.decode_unit(to_np(inp.q[b, j * g:(j + 1) * g]), to_np(inp.k_cache[b, j]),
+                                       to_np(inp.v_cache[b, j]), n_raw=cfg.n_raw, n_gist=cfg.M,
+                                       chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail)
+                np.testing.assert_array_equal(to_np(sel[b, j]), r["sel"])
+                check_out(to_np(out[b, j * g:(j + 1) * g]), r["out"], cfg.dtype, f"rep {rep}")
+                check_lse(to_np(lse[b, j * g:(j + 1) * g]), r["lse"], cfg.dtype, f"rep {rep}")
+
+
 # ----------------------------------------------------------- full sizes ---
 
 def sample_units(cfg, n=6, seed=0):
