@@ -32,7 +32,7 @@ __all__ = [
     "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse", "gsa_profile_events",
     "gsa_profile_marks", "topk_for_budget", "GIST_SETS", "gsa_gist_prefill", "gsa_cache_append",
     "gsa_decode_levels", "levels_workspace_size", "gsa_decode_varlen", "check_seq_lens",
-    "launches",
+    "launches", "gsa_decode_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -47,7 +47,7 @@ EXPORTED_SYMBOLS = (
     "gsa_topk_for_budget", "gsa_gist_prefill", "gsa_cache_append",
     "gsa_decode_levels_workspace_size", "gsa_decode_levels", "gsa_decode_varlen", "gsa_check_seq_lens",
     "gsa_decode_launches", "gsa_decode_hier_launches", "gsa_decode_levels_launches",
-    "gsa_prefill_launches",
+    "gsa_prefill_launches", "gsa_decode_noalloc",
 )
 MAX_LEVELS = 6
 
@@ -126,6 +126,8 @@ def lib() -> ctypes.CDLL:
         L.gsa_cache_append.argtypes = [P(AppendParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.gsa_profile_events.argtypes = [P(_vp), _c_i32]
         L.gsa_profile_marks.argtypes = [P(_c_i32)]
+        L.gsa_decode_noalloc.argtypes = [P(DecodeParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.gsa_decode_noalloc.restype = _c_i32
         L.gsa_decode_launches.argtypes = [P(DecodeParams), P(_c_i32)]
         L.gsa_decode_hier_launches.argtypes = [P(HierParams), P(_c_i32)]
         L.gsa_decode_levels_launches.argtypes = [P(LevelsParams), P(_c_i32)]
@@ -351,6 +353,24 @@ def gsa_decode(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int,
         _check(lib().gsa_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
                                 _ptr(lse), _ptr(sel_idx) if topk > 0 else None, _ptr(ws),
                                 _nbytes(ws), s.cuda_stream), "gsa_decode")
+    return out, lse, sel_idx
+
+
+def gsa_decode_noalloc(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int, out, lse=None,
+                       sel_idx=None, n_gist: Optional[int] = None, n_raw: Optional[int] = None,
+                       scale: float = 0.0, stream=None, gist_set: str = "all"):
+    """gsa_decode with the library's own scratch as its workspace: nothing is
+    allocated, so the outputs are the caller's (out [B,Hq,D] fp32, lse
+    [B,Hq] or None, sel_idx [B,Hkv,k] int32 or None)."""
+    B, Hq, D = q.shape
+    Hkv, R = k_cache.shape[1], k_cache.shape[2]
+    N, M, cap = _geometry(R, chunk, n_gist, n_raw)
+    p = decode_params(B, Hq, Hkv, D, N, M, chunk, topk, tail, scale, _dtype_code(q),
+                      GIST_SETS[gist_set], cap)
+    s, _ = _on_stream(stream, q.device)
+    _check(lib().gsa_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(out), _ptr(lse), _ptr(sel_idx) if topk > 0 else None,
+                                    s.cuda_stream), "gsa_decode_noalloc")
     return out, lse, sel_idx
 
 

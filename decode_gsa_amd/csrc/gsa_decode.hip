@@ -46,6 +46,8 @@
 // and read with device-scope loads: the XCDs' L2s are not coherent.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "gsa.h"
 #include "gsa_device.hpp"
 #include "gsa_plan.hpp"
@@ -2525,6 +2527,24 @@ struct LevelsRunner {
 }  // namespace
 }  // namespace gsa
 
+namespace gsa {
+namespace {
+// The launches of one single-level decode call, after validation.
+gsa_status_t run_decode_plan(const DecodePlan& pl, const void* q, const void* K, const void* V, float* out,
+                             float* lse, int32_t* sel_idx, char* ws, hipStream_t hs) {
+  if (pl.unit_S > 0) {
+    switch (pl.g) {
+      case 1: return run_unit<1>(pl, q, K, V, out, lse, sel_idx, ws, hs);
+      case 2: return run_unit<2>(pl, q, K, V, out, lse, sel_idx, ws, hs);
+      case 4: return run_unit<4>(pl, q, K, V, out, lse, sel_idx, ws, hs);
+      case 8: return run_unit<8>(pl, q, K, V, out, lse, sel_idx, ws, hs);
+    }
+  }
+  return dispatch<DecodeRunner>(pl.dtype, pl.D, pl.g, pl, q, K, V, out, lse, sel_idx, ws, hs);
+}
+}  // namespace
+}  // namespace gsa
+
 using namespace gsa;
 
 extern "C" gsa_status_t gsa_decode_workspace_size(const gsa_decode_params* p, size_t* bytes) {
@@ -2550,17 +2570,8 @@ extern "C" gsa_status_t gsa_decode(const gsa_decode_params* p, const void* q, co
       (s = check_ptr(lse, "lse", true)) != GSA_OK || (s = check_ptr(sel_idx, "sel_idx", true)) != GSA_OK)
     return s;
   if ((s = check_workspace(workspace, workspace_bytes, pl.total)) != GSA_OK) return s;
-  char* ws = reinterpret_cast<char*>(workspace);
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (pl.unit_S > 0) {
-    switch (pl.g) {
-      case 1: return run_unit<1>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
-      case 2: return run_unit<2>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
-      case 4: return run_unit<4>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
-      case 8: return run_unit<8>(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
-    }
-  }
-  return dispatch<DecodeRunner>(pl.dtype, pl.D, pl.g, pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
+  return run_decode_plan(pl, q, k_cache, v_cache, out, lse, sel_idx, reinterpret_cast<char*>(workspace),
+                         reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" gsa_status_t gsa_decode_hier_workspace_size(const gsa_hier_params* p, size_t* bytes) {
@@ -2687,3 +2698,76 @@ extern "C" gsa_status_t gsa_decode_varlen(const gsa_decode_params* p, const int3
   return dispatch<DecodeRunner>(pl.dtype, pl.D, pl.g, pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
 }
 
+// ------------------------------------------------ decode without allocation
+//
+// gsa_decode_noalloc: gsa_decode for callers that cannot allocate device
+// memory (code under stream capture, tight serving loops). Its workspace is
+// this file's own device array, one copy per GPU, held until the process
+// ends. Host code never uses the array's name as an address: the address of
+// each device's copy comes from hipGetSymbolAddress with that device current.
+
+constexpr size_t kScratchBytes = (size_t)16 << 20;   // 16 MiB per GPU
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace gsa {
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch[kMaxScratchDevices];   // per device: the array's device address, once set up
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The current device's copy of the scratch array; at its first use on a
+// device the control words (the first kCtrlBytes) are cleared on `st`, with a
+// fill kernel rather than a memset node.
+gsa_status_t scratch_of_current_device(hipStream_t st, char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices) return fail(GSA_ERR_UNSUPPORTED, "device %d above %d", dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(GSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, st, reinterpret_cast<uint4*>(ptr),
+                       kCtrlBytes / 16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(GSA_ERR_HIP, "scratch clear launch: %s", hipGetErrorString(e));
+    g_scratch[dev] = reinterpret_cast<char*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return GSA_OK;
+}
+
+}  // namespace
+}  // namespace gsa
+
+extern "C" gsa_status_t gsa_decode_noalloc(const gsa_decode_params* p, const void* q, const void* k_cache,
+                                           const void* v_cache, float* out, float* lse, int32_t* sel_idx,
+                                           void* stream) {
+  clear_error();
+  prof_begin_call();
+  DecodePlan pl;
+  gsa_status_t s = plan_decode(p, &pl);
+  if (s != GSA_OK) return s;
+  if ((s = check_ptr(q, "q")) != GSA_OK || (s = check_ptr(k_cache, "k_cache")) != GSA_OK ||
+      (s = check_ptr(v_cache, "v_cache")) != GSA_OK || (s = check_ptr(out, "out")) != GSA_OK ||
+      (s = check_ptr(lse, "lse", true)) != GSA_OK || (s = check_ptr(sel_idx, "sel_idx", true)) != GSA_OK)
+    return s;
+  if (pl.total > kScratchBytes)
+    return fail(GSA_ERR_WORKSPACE, "the call needs %zu bytes of workspace, the library's scratch holds %zu",
+                pl.total, kScratchBytes);
+  if (ctrl_bytes(pl.units) > kCtrlBytes)
+    return fail(GSA_ERR_UNSUPPORTED, "%d (batch, kv-head) units: at most %zu without a workspace", pl.units,
+                kCtrlBytes / (sizeof(uint32_t) * kCtrlUnitWords));
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  char* ws = nullptr;
+  if ((s = scratch_of_current_device(hs, &ws)) != GSA_OK) return s;
+  return run_decode_plan(pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
+}

@@ -122,6 +122,24 @@ gsa_status_t gsa_decode(const gsa_decode_params* p, const void* q, const void* k
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * gsa_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, hosts that
+ * forbid hipMalloc). It allocates nothing: its workspace is a 16 MiB device
+ * array inside the library, one copy per GPU, held until the process ends.
+ * Arguments, results and launches are gsa_decode's; the first call on a
+ * device also clears the array's control words (one more launch, outside the
+ * timing hook's count). Every call on a GPU shares that GPU's array and
+ * leaves its control words zero: calls that overlap on one GPU (on different
+ * streams, or from several threads) race and give wrong results; serialize
+ * them. GSA_ERR_WORKSPACE when gsa_decode_workspace_size exceeds 16 MiB (see
+ * that call's size), GSA_ERR_UNSUPPORTED above 4096 (batch, kv-head) units;
+ * nothing is launched then.
+ * ---------------------------------------------------------------------- */
+gsa_status_t gsa_decode_noalloc(const gsa_decode_params* p, const void* q, const void* k_cache,
+                                const void* v_cache, float* out, float* lse, int32_t* sel_idx,
+                                void* stream);
+
+/* ------------------------------------------------------------------------
  * Variable-length batch: the same step as gsa_decode, for sequences of
  * different lengths (each (sequence, kv-head) block holds its own raw tokens
  * and gists, read only up to its own N_b + M_b rows).

@@ -556,3 +556,17 @@ def test_launch_counts_follow_the_documented_rules(L):
     assert _launches(L, "gsa_prefill_launches", good_prefill(topk=0)) == (OK, 1)
     assert _launches(L, "gsa_prefill_launches", good_prefill(n_q=0)) == (OK, 0)
     assert _launches(L, "gsa_prefill_launches", good_prefill(topk=33)) == (UNSUPPORTED, -1)
+
+
+def test_decode_noalloc_host_rejections(L):
+    """gsa_decode_noalloc validates on the host before it touches the device:
+    bad shapes, NULL pointers and a workspace beyond the library's scratch."""
+    big = gsa.decode_params(32, 32, 8, 128, 131072, 16384, 8, 64, 64)   # 16+ MiB of scores
+    assert L.gsa_decode_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, None, None, None) == WORKSPACE
+    assert b"scratch" in L.gsa_last_error()
+    assert L.gsa_decode_noalloc(ctypes.byref(good_decode(batch=0)), FAKE, FAKE, FAKE, FAKE, None, None,
+                                None) == INVALID
+    assert L.gsa_decode_noalloc(ctypes.byref(good_decode()), None, FAKE, FAKE, FAKE, None, None,
+                                None) == INVALID
+    n = ctypes.c_int32(-1)
+    assert L.gsa_profile_marks(ctypes.byref(n)) == OK and n.value == 1   # nothing launched
