@@ -274,12 +274,16 @@ def run_decode_bench(args):
         names, nbytes = ["unit_kernel"], [alg_b]
     elif unit_path:
         names, nbytes = ["unit_kernel", "unit_unfold_kernel"], [gist_b, unfold_b]
+    elif n_marks == 4:   # gist pass, per-split candidates, unfold
+        names, nbytes = ["gist_kernel", "cand_kernel", "unfold_kernel"], [gist_b, 0, unfold_b]
     else:
         names, nbytes = ["gist_kernel", "unfold_kernel"][:n_marks - 1], [gist_b, unfold_b][:n_marks - 1]
     kernels = {}
     for j, (nm, nb) in enumerate(zip(names, nbytes)):
         ms = float(per[:, j].mean())
         kernels[nm] = {"ms": ms, "alg_bytes": nb, "GB_s": nb / (ms / 1e3) / 1e9, **pcts(per[:, j])}
+    kernels["whole_call"] = {"ms": call_ms, "alg_bytes": alg_b, "GB_s": alg_b / (call_ms / 1e3) / 1e9,
+                             **pcts(per.sum(axis=1))}
     main, main_b, main_ms = names[0], nbytes[0], kernels[names[0]]["ms"]
     achieved = main_b / (main_ms / 1e3) / 1e9
     res = {
@@ -386,9 +390,12 @@ def run_hier_bench(args):
         assert torch.equal(s1.long(), inp.planted1), "level-1 selection differs from the planted set"
     nb = hier_bytes(cfg, s1.cpu().numpy() if b.topk else [])
     n_marks = gsa.gsa_profile_marks()
-    if n_marks == 3:   # unit_kernel over level 2 + tail, then unit_hier_kernel for the rest
-        names = ["unit_kernel (level 2)", "unit_hier_kernel"]
-        nbytes = [nb["l2"], nb["cand"] + nb["unfold"]]
+    if n_marks == 2:   # unit_kernel over level 2 + tail, its last workgroup per unit descends
+        names = ["unit_kernel (level 2 + descent)"]
+        nbytes = [nb["l2"] + nb["cand"] + nb["unfold"]]
+    elif n_marks == 5:   # level 2, its per-split candidates, level-1 candidates, unfold
+        names = ["gist_kernel (level 2)", "cand_kernel", "gist_kernel (candidates)", "unfold_kernel"]
+        nbytes = [nb["l2"], 0, nb["cand"], nb["unfold"]]
     else:
         names = ["gist_kernel (level 2)", "gist_kernel (candidates)", "unfold_kernel"][:n_marks - 1]
         nbytes = [nb["l2"], nb["cand"], nb["unfold"]][:n_marks - 1]

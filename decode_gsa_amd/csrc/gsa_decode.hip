@@ -18,15 +18,17 @@
 //                 states. Nothing is handed off through memory.
 //     unit_kernel + unit_unfold_kernel (fewer units or more gists): S
 //                 workgroups per unit stream shares of the gists and tail and
-//                 hand their partial states and group scores on; S2
-//                 workgroups per unit then each make the unit's selection,
-//                 stream a share of the chosen raw rows, and the last one
-//                 merges every partial (k = 0: the stream launch's last
-//                 workgroup merges).
-//     unit_kernel<HIER> + unit_hier_kernel (two-level decode): the level-2
-//                 gists and the tail, then one workgroup per unit for the
-//                 level-2 selection, the candidate level-1 gists, the
-//                 level-1 selection, the unfold and the merge.
+//                 hand on their partial states and either the scores at or
+//                 above a bound on their own k-th best (k <= 16) or all
+//                 their group scores; S2 workgroups per unit then each make
+//                 the unit's selection among those, stream a share of the
+//                 chosen raw rows, and the last one merges every partial
+//                 (k = 0: the stream launch's last workgroup merges).
+//     unit_kernel<HIER> (two-level decode, one launch): S workgroups per
+//                 unit stream the level-2 gists and the tail and hand on
+//                 their partial states and level-2 scores; the unit's last
+//                 one then selects the level-2 groups, streams the candidate
+//                 level-1 gists, selects the chunks, unfolds them and merges.
 //   gist_kernel + unfold_kernel (every other shape: fp32, D = 64, k > 64, ...)
 //                 split-K over gists: each gist workgroup streams a range of
 //                 gist rows (and a share of the tail), keeps its group scores
@@ -1492,37 +1494,25 @@ __device__ __forceinline__ void lds_read4x16(const uint32_t (&ad)[4], uint4 (&v)
       : "memory");
 }
 
-// PER: keys per thread at most (n <= PER * kThreads). FROM_LDS: the scores are
-// an LDS array of PER * kThreads floats; otherwise gscores holds them in
-// device memory, written by other workgroups with device-scope stores.
-template <int PER, bool FROM_LDS>
-__device__ __forceinline__ void unit_select(const float* __restrict__ sc, int n, int k, float* __restrict__ gscores,
-                                            int64_t gstride, int unit, int32_t* __restrict__ dst, UnitSelLds& S,
-                                            TopkLds& T) {
-  // Written to keep decisions in vector arithmetic: with one wave per SIMD
-  // every vector -> scalar -> vector round trip costs a full pipeline drain.
-  typedef unsigned long long u64;
-  constexpr int kPerMax = PER;
+// The steps of the exact top-k below, shared with the candidate hand-off.
+// Thread t holds items t*per .. t*per + per - 1 (per a multiple of 4).
+__device__ __forceinline__ int select_per(int n) { return (n + 4 * kThreads - 1) / (4 * kThreads) * 4; }
+
+// 1. this thread's keys (order-preserving images of the scores; 0 past its
+// nv items), every read in bounds and in flight with the others of its group.
+// FROM_LDS: an LDS array of LDS_N floats; otherwise device memory written by
+// other workgroups with device-scope stores (gstride floats per row).
+template <int PER, bool FROM_LDS, int LDS_N>
+__device__ __forceinline__ void select_keys(const float* __restrict__ sc, const float* __restrict__ gscores,
+                                            int64_t gstride, int i0, int per, int nv, uint32_t (&key)[PER]) {
   static_assert(PER % 16 == 0, "keys come in groups of 16");
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (k <= 0) return;
-  if (k >= n) {
-    for (int i = tid; i < n; i += kThreads) dst[i] = i;
-    return;
-  }
-  const int per = (n + 4 * kThreads - 1) / (4 * kThreads) * 4;   // a multiple of 4, <= PER
-  const int i0 = tid * per;
-  const int nv = max(0, min(per, n - i0));   // this thread's items
-  // 1. keys, every read in bounds and in flight with the others of its group
-  uint32_t key[kPerMax];
   if constexpr (FROM_LDS) {
     const uint32_t base = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) float*)sc;
 #pragma unroll
     for (int grp = 0; grp < PER / 16; ++grp) {
       uint32_t ad[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ad[q] = base + 16u * (uint32_t)min(i0 / 4 + 4 * grp + q, PER * kThreads / 4 - 1);
+      for (int q = 0; q < 4; ++q) ad[q] = base + 16u * (uint32_t)min(i0 / 4 + 4 * grp + q, LDS_N / 4 - 1);
       uint4 v[4];
       lds_read4x16(ad, v);
 #pragma unroll
@@ -1542,38 +1532,52 @@ __device__ __forceinline__ void unit_select(const float* __restrict__ sc, int n,
     // `per` items are sent there
     const CohBuf P(gscores, (uint32_t)gstride * 4u);
 #pragma unroll
-    for (int q = 0; q < kPerMax / 4; ++q) {
+    for (int q = 0; q < PER / 4; ++q) {
       const uint4 v = P.u128(4 * q < per ? (uint32_t)(i0 + 4 * q) : (uint32_t)gstride);
       const uint32_t raw[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) key[4 * q + e] = 4 * q + e < nv ? order_key(__uint_as_float(raw[e])) : 0u;
     }
   }
-  uint32_t mx = 0u;
-#pragma unroll
-  for (int j = 0; j < kPerMax; ++j) mx = max(mx, key[j]);
+}
+
+// 2. a lower bound tau >= 1 on the k-th largest key (k <= 64) that keeps few
+// keys above it: k <= 16, the k-th largest of every thread's maximum
+// (distinct items), each wave's 16 largest merged by one wave; k > 16, the
+// k-th largest of the union of the threads' four largest (tau_top4). Items
+// that are not there have key 0 (a real item has key 0 only for a NaN score
+// with every bit set), so tau >= 1 selects exactly the items.
+template <int PER>
+__device__ __forceinline__ uint32_t select_tau(const uint32_t (&key)[PER], int k, UnitSelLds& S) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t tau;
   if (k <= 16) {
-    // (the lane read stays outside any branch: every lane takes part)
-    const uint32_t tw = (uint32_t)__builtin_amdgcn_readlane((int)wave_sort<true>(mx), k - 1);
-    if (lane == 0) S.tw[w] = tw;
-    __syncthreads();
-    tau = S.tw[0];
+    uint32_t mx = 0u;
 #pragma unroll
-    for (int i = 1; i < kWaves; ++i) tau = max(tau, S.tw[i]);
+    for (int j = 0; j < PER; ++j) mx = max(mx, key[j]);
+    const uint32_t srt = wave_sort<true>(mx);
+    if (lane < 16) S.top[w][lane] = srt;
+    __syncthreads();
+    if (w == 0) {   // a scalar branch: the whole wave takes it
+      const uint32_t v = wave_sort<true>(S.top[lane >> 4][lane & 15]);
+      const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)v, k - 1);
+      if (lane == 0) S.tau = t;
+    }
+    __syncthreads();
+    tau = S.tau;
   } else {
-    // a wave's k-th largest thread maximum is a weak bound for large k
     tau = tau_top4(key, k, S);
   }
-  // Items that are not there have key 0; a real item has key 0 only for a
-  // NaN score with every bit set, so tau >= 1 selects exactly the items.
-  tau = max(tau, 1u);
-  // 2. count, scan, compact
-  int c = 0;
-#pragma unroll
-  for (int j = 0; j < kPerMax; ++j) c += key[j] >= tau ? 1 : 0;
-  // inclusive scan over the wave: rows of 16 (row_shr 1, 2, 4, 8 with 0 fill),
-  // then the totals of the rows below
+  return max(tau, 1u);
+}
+
+// 3. this thread's exclusive prefix (in item order) of the per-thread counts
+// c over the workgroup; *total gets the sum. DPP row scan, then the totals of
+// the rows and waves below.
+__device__ __forceinline__ int select_scan(int c, UnitSelLds& S, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int x = c;
   x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
   x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
@@ -1587,15 +1591,49 @@ __device__ __forceinline__ void unit_select(const float* __restrict__ sc, int n,
   const int wtot = __builtin_amdgcn_readlane(x, 63);
   if (lane == 0) S.wsum[w] = wtot;
   __syncthreads();
-  int run = x - c, total = 0;
+  int run = x - c, t = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
-    const int t = S.wsum[i];
-    run += i < w ? t : 0;
-    total += t;
+    const int v = S.wsum[i];
+    run += i < w ? v : 0;
+    t += v;
   }
+  *total = t;
+  return run;
+}
+
+// PER: keys per thread at most (n <= PER * kThreads). FROM_LDS: the scores are
+// an LDS array of LDS_N floats (n <= LDS_N, a multiple of 4); otherwise
+// gscores holds them in device memory, written by other workgroups with
+// device-scope stores. The selected item indices go to dst ascending.
+template <int PER, bool FROM_LDS, int LDS_N = PER * kThreads>
+__device__ __forceinline__ void unit_select(const float* __restrict__ sc, int n, int k, float* __restrict__ gscores,
+                                            int64_t gstride, int unit, int32_t* __restrict__ dst, UnitSelLds& S,
+                                            TopkLds& T) {
+  // Written to keep decisions in vector arithmetic: with one wave per SIMD
+  // every vector -> scalar -> vector round trip costs a full pipeline drain.
+  typedef unsigned long long u64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (k <= 0) return;
+  if (k >= n) {
+    for (int i = tid; i < n; i += kThreads) dst[i] = i;
+    return;
+  }
+  const int per = select_per(n);   // <= PER
+  const int i0 = tid * per;
+  const int nv = max(0, min(per, n - i0));   // this thread's items
+  uint32_t key[PER];
+  select_keys<PER, FROM_LDS, LDS_N>(sc, gscores, gstride, i0, per, nv, key);
+  const uint32_t tau = select_tau(key, k, S);
+  // count, scan, compact (candidates in id order)
+  int c = 0;
 #pragma unroll
-  for (int j = 0; j < kPerMax; ++j) {
+  for (int j = 0; j < PER; ++j) c += key[j] >= tau ? 1 : 0;
+  int total;
+  int run = select_scan(c, S, &total);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
     const bool f = key[j] >= tau;
     const int p = f ? run : kCandMax;
     S.ck[p < kCandMax ? p : kCandMax + lane] = ((u64)key[j] << 32) | (uint32_t)~(uint32_t)(i0 + j);
@@ -1611,7 +1649,7 @@ __device__ __forceinline__ void unit_select(const float* __restrict__ sc, int n,
     block_topk(gscores, n, k, IdMap{nullptr, 0, 0, 0, 0}, unit, dst, T);
     return;
   }
-  // 3. rank of candidate `lane` against candidates 16 w .. 16 w + 15: the
+  // rank of candidate `lane` against candidates 16 w .. 16 w + 15: the
   // composite keys are distinct, larger first (equal scores: smaller id)
   {
     const u64 mine = S.ck[lane];
@@ -1669,6 +1707,24 @@ struct UnitArgs {
   int32_t gist_set;
   SeqLens seq;            // per-sequence lengths (single-level decode)
 };
+
+// Several workgroups per unit: each split's top-kk group scores and ids
+// (kk = k, or k2 over level-2 gists) follow the partial states in the
+// workspace, [units][cand_stride] scores then [units][cand_stride] ids, split
+// s at [s kk, (s + 1) kk). (Derived here rather than passed: the kernels'
+// arguments already fill the scalar registers.)
+struct Cands {
+  float* s;
+  int32_t* id;
+  int32_t stride;
+};
+__device__ __forceinline__ Cands cands_of(const UnitArgs& a, int units, int kk) {
+  Cands c;
+  c.stride = (a.S * cand_cap(a.S, kk) + 31) / 32 * 32;
+  c.s = a.part + (size_t)units * a.NP * a.part_stride;
+  c.id = reinterpret_cast<int32_t*>(c.s + (size_t)units * c.stride);
+  return c;
+}
 
 struct UnitLds {
   union {
@@ -1966,10 +2022,126 @@ __device__ __forceinline__ void unit_combine(UnitLds& L, const UState& st, int w
   }
 }
 
-// HIER: the first launch of two-level decode -- the level-2 gists (their own
-// arrays) and the tail; every workgroup hands its partial state and level-2
-// scores to unit_hier_kernel.
-template <int G, bool HIER, bool SETS = false, bool VARLEN = false>
+// A stream workgroup's candidates, written with device-scope stores to its
+// cap = cand_cap(S, kk) slots of the unit's candidate rows (scores, ids):
+// every one of its n group scores (LDS, items id0 .. id0 + n - 1) at or
+// above tau, a lower bound on its kk-th largest (select_tau), in id order,
+// padded with -inf scores. The unit's top-kk lies in the union of its splits'
+// top-kk (under the total order: larger score, then smaller id), so in the
+// union of these lists, whose slots are in id order: a selection over them
+// with ties to the earlier slot is the selection over every score. When more
+// than cap scores reach tau (ties over a range, or cap = kk), the exact top-kk
+// (unit_select) is written instead. gscr: the unit's score row at id0 (the
+// radix fallback's copy of the scores).
+constexpr int kCandPer = 32;   // keys per thread of a stream workgroup's own selection
+// Candidates pay off while the bound on a workgroup's k-th score is cheap
+// (k <= 16, select_tau); above that each stream workgroup hands all its
+// scores on and the unfold launch selects among them.
+constexpr int kCandMaxK = kUnitCandMaxK;
+static_assert(kCandMaxK <= 16, "select_tau's tight bound");
+static_assert(kCandPer * kThreads >= kUWgItems && kCandPer % 16 == 0, "a workgroup's scores fit the selection");
+__device__ __forceinline__ void unit_cands(UnitLds& L, int n, int kk, int id0, float* gscr, float* cs, int32_t* ci,
+                                           int S, int split, int unit) {
+  __syncthreads();   // the LDS union is free again (the merge is done)
+  if (kk <= 0) return;   // uniform
+  const int cap = cand_cap(S, kk);
+  float* csp = cs + (size_t)split * cap;
+  int32_t* cip = ci + (size_t)split * cap;
+  const int tid = threadIdx.x;
+  int written;
+  if (kk >= n) {
+    for (int i = tid; i < n; i += kThreads) {
+      st_coh(csp + i, L.scores[i]);
+      st_coh(cip + i, (int32_t)(id0 + i));
+    }
+    written = n;
+  } else {
+    const int per = select_per(n);
+    const int i0 = tid * per;
+    const int nv = max(0, min(per, n - i0));
+    uint32_t key[kCandPer];
+    select_keys<kCandPer, true, kUWgItems>(L.scores, nullptr, 0, i0, per, nv, key);
+    const uint32_t tau = select_tau(key, kk, L.u.sel.s);
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < kCandPer; ++j) c += key[j] >= tau ? 1 : 0;
+    int total;
+    int run = select_scan(c, L.u.sel.s, &total);
+    if (total <= cap) {   // uniform
+#pragma unroll
+      for (int j = 0; j < kCandPer; ++j) {
+        if (key[j] >= tau) {
+          st_coh(csp + run, L.scores[i0 + j]);
+          st_coh(cip + run, (int32_t)(id0 + i0 + j));
+          ++run;
+        }
+      }
+      written = total;
+    } else {
+      __syncthreads();
+      unit_select<kCandPer, true, kUWgItems>(L.scores, n, kk, gscr, 0, unit, L.sel, L.u.sel.s, L.u.sel.t);
+      __syncthreads();
+      for (int i = tid; i < kk; i += kThreads) {
+        const int j = L.sel[i];
+        st_coh(csp + i, L.scores[j]);
+        st_coh(cip + i, (int32_t)(id0 + j));
+      }
+      written = kk;
+    }
+  }
+  for (int i = written + tid; i < cap; i += kThreads) {
+    st_coh(csp + i, -INFINITY);
+    st_coh(cip + i, (int32_t)id0);
+  }
+}
+
+// The unit's top-kk among its S splits' candidate lists, ids ascending, into
+// dst (LDS); every thread of the workgroup takes part. The ids travel with
+// the scores (staged in the LDS score array when they fit), so the mapping
+// from list position to id costs no further round trip.
+__device__ __forceinline__ void select_cands(const Cands& c, int S, int unit, int kk, int32_t* dst, UnitLds& L) {
+  if (kk <= 0) return;
+  const int nc = S * cand_cap(S, kk);
+  float* cs = c.s + (size_t)unit * c.stride;
+  const CohBuf ids(c.id + (size_t)unit * c.stride, (uint32_t)c.stride * 4u);
+  const int tid = threadIdx.x;
+  const bool staged = nc <= kUWgItems;   // uniform
+  int32_t* idl = reinterpret_cast<int32_t*>(L.scores);
+  // the id loads go out with the score loads; they land in LDS after them
+  constexpr int kIdsPer = kUWgItems / kThreads;
+  uint32_t idr[kIdsPer];
+#pragma unroll
+  for (int q = 0; q < kIdsPer; ++q) {
+    const int i = tid + q * kThreads;
+    idr[q] = staged && i < nc ? ids.u32((uint32_t)i) : 0u;
+  }
+  unit_select<kUMaxSel / kThreads, false>(nullptr, nc, kk, cs, c.stride, unit, dst, L.u.sel.s, L.u.sel.t);
+  if (staged) {
+#pragma unroll
+    for (int q = 0; q < kIdsPer; ++q) {
+      const int i = tid + q * kThreads;
+      if (i < nc) idl[i] = (int32_t)idr[q];
+    }
+  }
+  __syncthreads();
+  const int id = tid < kk ? (staged ? idl[dst[tid]] : (int)ids.u32((uint32_t)dst[tid])) : 0;
+  __syncthreads();
+  if (tid < kk) dst[tid] = id;
+  __syncthreads();
+}
+
+template <int G>
+__device__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16x8u (&qf)[4]);
+
+// HIER (kHierDescend, kHierTop): the level-2 gists (their own arrays) and the
+// tail; every workgroup hands its partial state and its top-k2 level-2
+// candidates on. kHierDescend (two-level decode): the unit's last workgroup
+// then runs the descent. kHierTop (the top level of L-level decode):
+// unit_levels_kernel does, in a second launch.
+enum { kHierNone = 0, kHierDescend = 1, kHierTop = 2 };
+// SPLIT: several workgroups per unit (a.S > 1); the one-workgroup-per-unit
+// instantiation carries none of the hand-off code.
+template <int G, int HIER, bool SETS = false, bool VARLEN = false, bool SPLIT = true>
 __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
   __shared__ __attribute__((aligned(16))) UnitLds L;
   UnitArgs a = args;
@@ -1977,7 +2149,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
   // then uniform, and the row loops branch on scalars
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq = lane & 15, jg = lane >> 4;
-  const int S = a.S;
+  const int S = SPLIT ? a.S : 1;
   const int unit = blockIdx.x / S, split = blockIdx.x - unit * S;
   if constexpr (VARLEN) unit_lengths(args.seq, unit, args.N, args.M, args.C, args.T, &a.N, &a.M);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
@@ -2017,6 +2189,10 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
     unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)split * a.part_stride);
     float* s2u = a.s2 + (size_t)unit * a.s2_stride;
     for (int i = w0 + tid; i < min(w1, nf); i += kUW * 64) st_coh(s2u + i, L.scores[i - w0]);
+    if constexpr (HIER == kHierDescend) {
+      if (!arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)S, &L.s_old)) return;
+      hier_descent<G>(a, L, unit, qf);
+    }
     return;
   }
   if constexpr (SETS) {
@@ -2045,7 +2221,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
   float* gs = a.scores + (size_t)unit * a.score_stride;
   const int items = a.k * a.C;
   const int per2 = (items + kUW - 1) / kUW;
-  if (S == 1) {
+  if constexpr (!SPLIT) {
     if (a.k > 0) {
       __syncthreads();   // every group score is in LDS, every ring idle
       unit_select<kUMaxGist / kThreads, true>(L.scores, M, a.k, gs, a.score_stride, unit, L.sel, L.u.sel.s,
@@ -2062,8 +2238,14 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
     // (device-scope stores: the XCDs' L2s are not coherent)
     float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
     unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)split * a.part_stride);
-    if (a.k > 0) {
+    if (a.k > kCandMaxK) {   // the unfold launch selects among every score
       for (int i = w0 + tid; i < min(w1, M); i += kUW * 64) st_coh(gs + i, L.scores[i - w0]);
+      return;
+    }
+    if (a.k > 0) {   // the unfold launch selects among the splits' candidates
+      const Cands c = cands_of(a, (int)(gridDim.x / S), a.k);
+      unit_cands(L, max(0, min(w1, M) - w0), a.k, w0, gs + w0, c.s + (size_t)unit * c.stride,
+                 c.id + (size_t)unit * c.stride, S, split, unit);
       return;
     }
     if (!arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)S, &L.s_old)) return;
@@ -2108,10 +2290,13 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   st.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4u{0.f, 0.f, 0.f, 0.f};
-  float* gs = a.scores + (size_t)unit * a.score_stride;
-  unit_select<kUMaxSel / kThreads, false>(nullptr, (int)a.M, a.k, gs, a.score_stride, unit, L.sel, L.u.sel.s,
-                                          L.u.sel.t);
-  __syncthreads();
+  if (a.k > kCandMaxK) {
+    unit_select<kUMaxSel / kThreads, false>(nullptr, (int)a.M, a.k, a.scores + (size_t)unit * a.score_stride,
+                                            a.score_stride, unit, L.sel, L.u.sel.s, L.u.sel.t);
+    __syncthreads();
+  } else {
+    select_cands(cands_of(a, (int)(gridDim.x / S2), a.k), a.S, unit, a.k, L.sel, L);
+  }
   const int items = a.k * a.C;
   const int perp = (items + S2 - 1) / S2;
   const int p0 = min(items, part * perp), p1 = min(items, p0 + perp);
@@ -2127,36 +2312,22 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
     for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
 }
 
-// Second launch of two-level decode, one workgroup per unit: the level-2
-// selection from the first launch's scores, the level-1 candidates (group
-// scores kept in LDS), their selection, the chosen chunks' raw rows, and the
-// merge of every partial state.
+// Two-level decode, the rest of a unit after its level-2 stream (run by the
+// unit's last stream workgroup): the level-2 selection among the splits'
+// candidates, the level-1 candidates (group scores kept in LDS), their
+// selection, the chosen chunks' raw rows, and the merge of every partial.
 template <int G>
-__global__ __launch_bounds__(kUW * 64) void unit_hier_kernel(UnitArgs a) {
-  __shared__ __attribute__((aligned(16))) UnitLds L;
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hq = lane & 15, jg = lane >> 4;
-  const int unit = blockIdx.x;
+__device__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16x8u (&qf)[4]) {
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
   const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
-  bf16x8u qf[4];
-  {
-    const char* qb = reinterpret_cast<const char*>(a.q) + ((size_t)unit * G + (hq < G ? hq : 0)) * 256 + 16 * jg;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 v = hq < G ? load16(qb + 64 * ks) : make_uint4(0u, 0u, 0u, 0u);
-      qf[ks] = __builtin_bit_cast(bf16x8u, v);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) __asm__ volatile("" : "+v"(qf[ks]));
-  }
   UState st;
   st.m = kMinus;
   st.l = 0.f;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) st.o[dt] = f32x4u{0.f, 0.f, 0.f, 0.f};
   char* ring = L.u.ring[w][0];
-  // level 2: the chosen groups, ascending
+  // level 2: the chosen groups, ascending, from the stream workgroups' scores
   float* s2u = a.s2 + (size_t)unit * a.s2_stride;
   unit_select<kUMaxSel / kThreads, false>(nullptr, (int)a.M2, a.k2, s2u, a.s2_stride, unit, L.sel2, L.u.sel.s,
                                           L.u.sel.t);
@@ -2199,7 +2370,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_hier_kernel(UnitArgs a) {
 // candidates (the chosen gists' children and the ungrouped gists: dense rows
 // of the level's array, gist rows of the interleaved cache at level 1) into
 // the wave states with their scores in LDS, choose among them, and finally
-// unfold the chosen chunks and merge. The level-1 part is unit_hier_kernel's.
+// unfold the chosen chunks and merge. The level-1 part is hier_descent's.
 struct LevelArgs {
   int32_t L, G;
   const void* K[GSA_MAX_LEVELS + 1];     // l >= 2: [units][Ml[l]][D]
@@ -2345,6 +2516,7 @@ gsa_status_t run_unit_levels(const LevelsPlan& lp, const void* q, const void* K,
   u.K2 = Ku[Lv - 2]; u.V2 = Vu[Lv - 2]; u.M2 = lp.Ml[Lv]; u.G2 = lp.G; u.k2 = lp.kl[Lv]; u.n_cand = 0;
   u.s2 = reinterpret_cast<float*>(ws + lp.off_scores[Lv]); u.s2_stride = lp.score_stride[Lv];
   u.sel2 = nullptr;
+
   LevelArgs lv{};
   lv.L = Lv; lv.G = lp.G;
   for (int l = 1; l <= Lv; ++l) {
@@ -2362,7 +2534,7 @@ gsa_status_t run_unit_levels(const LevelsPlan& lp, const void* q, const void* K,
     // the top level fits one workgroup's LDS scores: one launch
     prof_launch((unit_levels_kernel<G, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
   } else {
-    prof_launch((unit_kernel<G, true>), dim3(pl.units * lp.unit_S), dim3(kUW * 64), 0, st, u);
+    prof_launch((unit_kernel<G, kHierTop>), dim3(pl.units * lp.unit_S), dim3(kUW * 64), 0, st, u);
     prof_launch((unit_levels_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
   }
   return launch_status("gsa_decode_levels launch");
@@ -2384,9 +2556,9 @@ gsa_status_t run_unit_hier(const HierPlan& hp, const void* q, const void* K, con
   u.K2 = K2; u.V2 = V2; u.M2 = hp.M2; u.G2 = hp.G; u.k2 = hp.k2; u.n_cand = hp.n_cand;
   u.s2 = reinterpret_cast<float*>(ws + hp.off_s2); u.s2_stride = hp.s2_stride;
   u.sel2 = hp.k2 > 0 ? sel2 : nullptr;
+  u.cnt = ctrl_of(ws, hp.off_ctrl, 0);
   prof_begin_call();
-  prof_launch((unit_kernel<G, true>), dim3(pl.units * hp.unit_S), dim3(kUW * 64), 0, st, u);
-  prof_launch((unit_hier_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+  prof_launch((unit_kernel<G, kHierDescend>), dim3(pl.units * hp.unit_S), dim3(kUW * 64), 0, st, u);
   return launch_status("gsa_decode_hier launch");
 }
 
@@ -2406,11 +2578,15 @@ gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const 
   prof_begin_call();
   const bool varlen = pl.seq_n != nullptr;
   if (pl.gist_set != GSA_GISTS_ALL)
-    prof_launch((unit_kernel<G, false, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+    prof_launch((unit_kernel<G, kHierNone, true, false, false>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+  else if (varlen && pl.unit_S == 1)
+    prof_launch((unit_kernel<G, kHierNone, false, true, false>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
   else if (varlen)
-    prof_launch((unit_kernel<G, false, false, true>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0, st, u);
+    prof_launch((unit_kernel<G, kHierNone, false, true, true>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0, st, u);
+  else if (pl.unit_S == 1)
+    prof_launch((unit_kernel<G, kHierNone, false, false, false>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
   else
-    prof_launch((unit_kernel<G, false>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0, st, u);
+    prof_launch((unit_kernel<G, kHierNone, false, false, true>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0, st, u);
   if (pl.unit_S2 > 0) {
     if (varlen)
       prof_launch((unit_unfold_kernel<G, true>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st, u);
@@ -2697,6 +2873,7 @@ extern "C" gsa_status_t gsa_decode_varlen(const gsa_decode_params* p, const int3
   }
   return dispatch<DecodeRunner>(pl.dtype, pl.D, pl.g, pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
 }
+
 
 // ------------------------------------------------ decode without allocation
 //

@@ -198,7 +198,15 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   d.off_part = off;
   off = align_up(off + sizeof(float) * (size_t)units * d.NP * (size_t)part_stride(d.g, d.D));
   d.cand_stride = 0;
-  if (d.unit_S == 0 && d.k > 0 && d.k <= kFastSelect && d.S >= 4 && (int64_t)d.S * d.k * 2 <= d.M) {
+  if (d.unit_S > 1 && d.k > 0 && d.k <= kUnitCandMaxK) {
+    // each stream workgroup's top-k, selected among by the unfold launch: the
+    // scores, then the ids, directly after the partial states (the kernels
+    // derive the place from the partial region)
+    d.cand_stride = line_pad((int64_t)d.unit_S * cand_cap(d.unit_S, d.k));
+    d.off_cand = d.off_part + sizeof(float) * (size_t)units * d.NP * (size_t)part_stride(d.g, d.D);
+    d.off_cand_ids = d.off_cand + sizeof(float) * (size_t)units * (size_t)d.cand_stride;
+    off = align_up(d.off_cand_ids + sizeof(int32_t) * (size_t)units * (size_t)d.cand_stride);
+  } else if (d.unit_S == 0 && d.k > 0 && d.k <= kFastSelect && d.S >= 4 && (int64_t)d.S * d.k * 2 <= d.M) {
     d.cand_stride = line_pad((int64_t)d.S * d.k);
     d.off_cand = off;
     off = align_up(off + sizeof(float) * (size_t)units * (size_t)d.cand_stride);
@@ -517,7 +525,7 @@ int32_t decode_launches(const DecodePlan& d) {
 }
 
 int32_t hier_launches(const HierPlan& h) {
-  if (h.unit_S > 0) return 2;
+  if (h.unit_S > 0) return 1;
   return 2 + (h.cand2_stride > 0 ? 1 : 0) + (h.base.k > 0 ? 1 : 0);
 }
 

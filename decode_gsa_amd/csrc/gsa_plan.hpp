@@ -52,6 +52,24 @@ inline size_t ctrl_bytes(int64_t units) {
   return need > kCtrlBytes ? need : kCtrlBytes;
 }
 
+#ifdef __HIP__
+#define GSA_HD __host__ __device__
+#else
+#define GSA_HD
+#endif
+
+// Candidate hand-off of the several-workgroups-per-unit launches: each of the
+// S stream workgroups of a unit writes `cand_cap` (score, id) slots, the
+// scores at or above a bound on its kk-th largest (2 kk slots), or its exact
+// top kk when 2 kk slots per split would make the unit's list longer than
+// kUnitMaxSel. The kernels and the plan both use this.
+// The several-workgroups-per-unit launch hands candidates on for k up to
+// this; above it every group score.
+constexpr int32_t kUnitCandMaxK = 16;
+GSA_HD inline int32_t cand_cap(int32_t S, int32_t kk) {
+  return (int64_t)S * 2 * kk <= kUnitMaxSel ? 2 * kk : kk;
+}
+
 // Per-unit strides of workspace regions that other workgroups read back are
 // whole 128-byte lines, so no two units (or partial slots) share a line.
 inline int64_t line_pad(int64_t n_words) { return (n_words + 31) / 32 * 32; }

@@ -408,8 +408,9 @@ gsa_status_t gsa_profile_marks(int32_t* n);
  *     other shapes: 1 when topk = 0, else 2 or 3 (a gist pass, a pass that
  *     takes each split's top-k when there are many gists per unit, an
  *     unfold pass);
- *   gsa_decode_hier on the bf16, D = 128, k1, k2 <= 64 path: 2 (the
- *     level-2 stream, then the descent); other shapes: 2 to 4 (a level-2
+ *   gsa_decode_hier on the bf16, D = 128, k1, k2 <= 64 path: 1 (the
+ *     level-2 stream, whose last workgroup per unit runs the descent);
+ *     other shapes: 2 to 4 (a level-2
  *     pass, possibly a pass over its splits' top-k2, a level-1 candidate
  *     pass, and an unfold pass when topk1 > 0);
  *   gsa_decode_levels on the bf16, D = 128, every k <= 64 path: 1 when the

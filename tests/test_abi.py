@@ -534,7 +534,7 @@ def test_launch_counts_follow_the_documented_rules(L):
     assert _launches(L, "gsa_decode_launches", tiny) == (OK, 3)   # 4 splits of 64 gists, k = 8
     # two-level
     hb = gsa.decode_params(4, 32, 8, 128, 1 << 20, 1 << 16, 16, 16, 64)
-    assert _launches(L, "gsa_decode_hier_launches", gsa.HierParams(hb, 16, 8)) == (OK, 2)
+    assert _launches(L, "gsa_decode_hier_launches", gsa.HierParams(hb, 16, 8)) == (OK, 1)
     hf = gsa.decode_params(2, 8, 2, 64, 1 << 16, 1 << 12, 16, 16, 64, dtype=gsa.GSA_F32)
     st, n = _launches(L, "gsa_decode_hier_launches", gsa.HierParams(hf, 16, 8))
     assert st == OK and n in (3, 4)

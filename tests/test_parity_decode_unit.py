@@ -150,3 +150,30 @@ def test_decode_unit_ties_inside_candidates(gsa):
     want = np.array(sorted(first + sorted(second)[:6]))
     assert (to_np(sel) == want[None, None, :]).all()
     run_decode(gsa, inp, cfg, units=sample_units(cfg, n=24, seed=3))
+
+
+@pytest.mark.parametrize("n_raw", [16 * 4096, 16 * 16384])
+def test_decode_unit_ties_across_splits(gsa, n_raw):
+    """Several workgroups per unit, each handing on its own top-k: 10 gists
+    share the best score and 12 the second best, spread over every split, and
+    8 more of the second score sit together in the last split. With k = 16 the
+    first group and the 6 smallest ids of the second are chosen, so the
+    candidates of different splits must break the tie by id."""
+    cfg = cfg_of("gqa_32k", batch=1, n_kv_heads=2, n_q_heads=8, n_raw=n_raw, topk=16, plant="none")
+    say(f"decode unit-path ties across splits {cfg}")
+    inp = gi.make_decode(cfg, 3110, device="cuda")
+    C, M = cfg.chunk, cfg.M
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    qbar = inp.q.float().view(cfg.batch, cfg.n_kv_heads, g, -1).mean(2)
+    unit_dir = qbar / qbar.norm(dim=-1, keepdim=True)
+    first = [(M // 10) * i + 3 for i in range(10)]
+    second = [(M // 12) * i + 5 for i in range(12)] + [M - 20 + i for i in range(8)]
+    for ids, mag in ((first, 40.0), (second, 30.0)):
+        for m in ids:
+            inp.k_cache[:, :, m * (C + 1) + C] = (unit_dir * mag).to(inp.k_cache.dtype)
+    out, lse, sel = gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=C, topk=16, tail=cfg.tail)
+    torch.cuda.synchronize()
+    assert gsa.gsa_profile_marks() == 3        # stream launch + select-unfold-merge launch
+    want = np.array(sorted(first + sorted(second)[:6]))
+    assert (to_np(sel) == want[None, None, :]).all()
+    run_decode(gsa, inp, cfg)
