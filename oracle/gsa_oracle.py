@@ -64,6 +64,14 @@ Readings where the pages are silent (each also listed in the design notes):
      g3 -> g1, g2, x5, g3, is taken as g3 -> g1, g2, x5, x6: one garbled
      symbol, where a literal self-key would also break the first two lines'
      pattern and leave chunk 3 without its second raw token);
+  R18 paged caches: a sequence's interleaved cache may live in pages of P
+     chunk slots (P (C + 1) rows each) taken from a shared pool, in the
+     order its block table lists them; the computation is that of the cache
+     the pages spell out (``gather_pages``);
+  R19 reused documents that end mid-chunk: a document of length M_d C + r_d
+     contributes its M_d gisted chunks to the routing and its last r_d raw
+     tokens, which no gist summarises, are attended directly like the tail
+     (``decode_unit(extra=...)``);
   R15 L levels: level l >= 2 has M_l = floor(M_{l-1} / G) gists in its own
      array, gist i of level l summarising gists [i G, (i + 1) G) of level
      l - 1; top-down, every level's candidates are the children of the
@@ -85,6 +93,7 @@ __all__ = [
     "gist_row_index", "raw_row_index", "topk_ascending",
     "decode_unit", "decode", "decode_hier_unit", "decode_hier", "decode_levels_unit", "topk_for_budget", "GIST_SETS",
     "prefill_query", "prefill", "cache_row", "gist_query",
+    "page_slot", "gather_pages", "decode_paged_unit",
 ]
 
 
@@ -196,16 +205,20 @@ def topk_for_budget(budget: int, n_gist: int, chunk: int, tail: int, gist_set: s
 
 def decode_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, *, n_raw: int,
                 n_gist: int, chunk: int, topk: int, tail: int,
-                scale: Optional[float] = None, gist_set: str = "all") -> Dict[str, np.ndarray]:
+                scale: Optional[float] = None, gist_set: str = "all",
+                extra: Optional[Tuple[np.ndarray, np.ndarray]] = None) -> Dict[str, np.ndarray]:
     """One (batch, kv-head) unit of single-level GSA decode.
 
     qg: [g, D] query heads sharing this kv-head.  K, V: [R, D] interleaved
     cache of the unit, R = n_raw + n_gist.  gist_set: which gist rows join
     the attention set -- "all" (every gist; the hybrid attention of section 2),
     "selected" (the selected chunks' gists) or "none" (raw tokens only); the
-    last two are slide 17's SG+SR and SR-only rules.  Returns out [g, D],
+    last two are slide 17's SG+SR and SR-only rules.  extra: (K_x, V_x)
+    [x, D] rows outside the cache that join the attention set as they are
+    (R19: the ungisted last tokens of reused documents).  Returns out [g, D],
     lse [g], wsum [g], sel [k] (ascending chunk ids), rows (sorted
-    attention-set rows) and scores [M] (group scores of every gist).
+    attention-set rows of the cache) and scores [M] (group scores of every
+    gist).
     """
     qg = _f64(qg)
     g, D = qg.shape
@@ -240,8 +253,12 @@ def decode_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, *, n_raw: int,
     for p in range(N - T, N):
         A.add(raw_row_index(p, C, M))
     rows = np.array(sorted(A), dtype=np.int64)
+    keys, vals = _f64(K[rows]), _f64(V[rows])
+    if extra is not None and len(extra[0]):
+        keys = np.concatenate([keys, _f64(extra[0])])
+        vals = np.concatenate([vals, _f64(extra[1])])
     # 4. hybrid softmax attention
-    out, lse, wsum = _softmax_attend(qg, _f64(K[rows]), _f64(V[rows]), scale)
+    out, lse, wsum = _softmax_attend(qg, keys, vals, scale)
     return {"out": out, "lse": lse, "wsum": wsum,
             "sel": np.array(sel, dtype=np.int64), "rows": rows, "scores": S}
 
@@ -281,6 +298,45 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, *, chunk: in
 
 
 # ----------------------------------------------------- two-level decode ---
+
+# ---------------------------------------------------------------- paging ---
+
+def page_slot(r: int, page_chunks: int, chunk: int) -> Tuple[int, int]:
+    """(i, s): logical cache row r of a sequence sits at row s of the i-th page
+    its block table lists, pages holding page_chunks chunk slots of C + 1
+    rows (R18). A chunk (its C raw rows and its gist) never straddles two
+    pages."""
+    rows_per_page = page_chunks * (chunk + 1)
+    return r // rows_per_page, r % rows_per_page
+
+
+def gather_pages(pool: np.ndarray, pages: Sequence[int], *, page_chunks: int, chunk: int,
+                 n_rows: int) -> np.ndarray:
+    """Rows 0 .. n_rows - 1 of a sequence's interleaved cache (one kv-head),
+    read page by page: pool [n_pages, P (C + 1), D] holds that kv-head's rows
+    of every page, pages the sequence's block table."""
+    out = []
+    for r in range(n_rows):
+        i, s = page_slot(r, page_chunks, chunk)
+        out.append(pool[pages[i], s])
+    return np.stack(out) if out else np.zeros((0, pool.shape[-1]))
+
+
+def decode_paged_unit(qg: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, pages: Sequence[int], *,
+                      page_chunks: int, n_raw: int, n_gist: int, chunk: int, topk: int, tail: int,
+                      extra_rows: Sequence[Tuple[int, int]] = (), scale: Optional[float] = None):
+    """One (sequence, kv-head) unit of decode over a paged cache (R18): the
+    cache the pages spell out, plus the rows extra_rows lists as (page, row in
+    page) attended directly (R19). k_pool, v_pool: [n_pages, P (C + 1), D]
+    of this kv-head."""
+    R = n_raw + n_gist
+    K = gather_pages(k_pool, pages, page_chunks=page_chunks, chunk=chunk, n_rows=R)
+    V = gather_pages(v_pool, pages, page_chunks=page_chunks, chunk=chunk, n_rows=R)
+    xk = np.stack([k_pool[pg, r] for pg, r in extra_rows]) if len(extra_rows) else np.zeros((0, K.shape[1]))
+    xv = np.stack([v_pool[pg, r] for pg, r in extra_rows]) if len(extra_rows) else np.zeros((0, K.shape[1]))
+    return decode_unit(qg, K, V, n_raw=n_raw, n_gist=n_gist, chunk=chunk, topk=topk, tail=tail, scale=scale,
+                       extra=(xk, xv))
+
 
 def decode_hier_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, K2: np.ndarray,
                      V2: np.ndarray, *, n_raw: int, n_gist: int, chunk: int,

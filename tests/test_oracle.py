@@ -694,3 +694,130 @@ def test_levels_middle_orphan_is_always_a_candidate():
     assert list(res["cands"][1]) == [0, 1, 2, 3]
     assert list(res["sels"][1]) == [3]
     assert list(res["cands"][0]) == [9, 10, 11, 12, 13]   # children of 3, then level-1 orphans 12, 13
+
+
+# ------------------------------------------------------------- paging ----
+
+def _scatter_to_pages(rng, dense, P, C, n_pages):
+    """Independent of the oracle: place a dense [R, D] cache into a pool of
+    n_pages pages of P (C + 1) rows, page q of the sequence at pool page
+    perm[q] (the rest of the pool random); returns (pool, block table)."""
+    rpp = P * (C + 1)
+    need = -(-dense.shape[0] // rpp)
+    perm = rng.permutation(n_pages)[:need]
+    pool = rng.standard_normal((n_pages, rpp, dense.shape[1]))
+    for r in range(dense.shape[0]):
+        pool[perm[r // rpp], r - (r // rpp) * rpp] = dense[r]
+    return pool, [int(x) for x in perm]
+
+
+@pytest.mark.parametrize("P,C,M,r", [(1, 4, 9, 3), (2, 16, 7, 0), (4, 8, 13, 8), (8, 2, 20, 1)])
+def test_gather_pages_inverts_a_scatter(P, C, M, r):
+    rng = np.random.default_rng(900 + P)
+    R = M * C + r + M
+    dense = rng.standard_normal((R, 5))
+    pool, pages = _scatter_to_pages(rng, dense, P, C, 3 * (R // (P * (C + 1)) + 2))
+    got = oracle.gather_pages(pool, pages, page_chunks=P, chunk=C, n_rows=R)
+    np.testing.assert_array_equal(got, dense)
+    # a chunk's C raw rows and its gist share one page
+    for m in range(M):
+        pg = {oracle.page_slot(m * (C + 1) + j, P, C)[0] for j in range(C + 1)}
+        assert len(pg) == 1
+
+
+@pytest.mark.parametrize("k", [0, 3, "M"])
+def test_paged_decode_with_extra_rows_is_masked_sdpa(k):
+    """Paged decode with extra rows: the dense-cache set (independent mask) plus
+    the extra rows, as float64 SDPA; k = M is full attention over every cache
+    row and the extras."""
+    rng = np.random.default_rng(910)
+    g, D, C, M, r, T, P = 2, 6, 4, 9, 2, 5, 2
+    N = M * C + r
+    qg, K, V, M, R = rand_unit(rng, g, D, N, C, M)
+    kk = M if k == "M" else k
+    kpool, pages = _scatter_to_pages(np.random.default_rng(1), K, P, C, 12)
+    vpool, pages_v = _scatter_to_pages(np.random.default_rng(1), V, P, C, 12)
+    assert pages == pages_v
+    extra = [(pages[-1], P * (C + 1) - 1), (next(x for x in range(12) if x not in pages), 3)]
+    res = oracle.decode_paged_unit(qg, kpool, vpool, pages, page_chunks=P, n_raw=N, n_gist=M, chunk=C, topk=kk,
+                                   tail=T, extra_rows=extra)
+    sel = set(res["sel"].tolist())
+    mask = np.zeros(R, bool)
+    for row in range(R):
+        kind, x = row_kind(row, C, M)
+        mask[row] = kind == "gist" or x >= N - T or (x < M * C and x // C in sel)
+    xk = np.stack([kpool[pg, s] for pg, s in extra])
+    xv = np.stack([vpool[pg, s] for pg, s in extra])
+    keys, vals = np.concatenate([K, xk]), np.concatenate([V, xv])
+    ref = sdpa(qg, keys, vals, np.concatenate([mask, np.ones(len(extra), bool)]), 1 / math.sqrt(D))
+    np.testing.assert_allclose(res["out"], ref, rtol=0, atol=1e-12)
+    if k == "M":
+        np.testing.assert_allclose(res["out"], sdpa(qg, keys, vals, np.ones(len(keys), bool), 1 / math.sqrt(D)),
+                                   rtol=0, atol=1e-12)
+
+
+def test_extra_rows_q_zero_closed_form():
+    """q = 0: every weight is equal, so the output is the plain mean of V over
+    the cache rows of the set and the extra rows."""
+    rng = np.random.default_rng(920)
+    g, D, C, M, T = 1, 4, 4, 6, 4
+    N = M * C
+    _, K, V, M, R = rand_unit(rng, g, D, N, C, M)
+    xk, xv = rng.standard_normal((3, D)), rng.standard_normal((3, D))
+    res = oracle.decode_unit(np.zeros((g, D)), K, V, n_raw=N, n_gist=M, chunk=C, topk=2, tail=T, extra=(xk, xv))
+    # q = 0 ties every score: chunks 0 and 1; tail = chunk 5's raw rows
+    rows = [m * (C + 1) + C for m in range(M)] + [m * (C + 1) + j for m in (0, 1) for j in range(C)]
+    rows += [5 * (C + 1) + j for j in range(C)]
+    want = (V[rows].sum(0) + xv.sum(0)) / (len(rows) + 3)
+    np.testing.assert_allclose(res["out"][0], want, rtol=0, atol=1e-12)
+
+
+def test_documents_ending_mid_chunk_route_and_keep_their_last_tokens():
+    """Two documents built apart and reused (chunk-sized pages): the first ends
+    two tokens into a chunk. Its complete chunks and the second document's
+    chunks form the routed sequence, its last two tokens are extra rows. With
+    every chunk selected the result is full attention over every token and
+    gist of both documents; with k = 1 the chosen chunk is the one whose gist
+    is aligned with the query."""
+    rng = np.random.default_rng(930)
+    g, D, C = 2, 8, 4
+    L1, L2 = 5 * C + 2, 4 * C + 3           # doc 2 is the query's own sequence (3 trailing raw rows)
+    M1, M2 = L1 // C, L2 // C
+
+    def doc(L, M):
+        rows = []
+        for m in range(M):
+            rows += [("raw", m * C + j) for j in range(C)] + [("gist", m)]
+        rows += [("raw", M * C + j) for j in range(L - M * C)]
+        return rows, rng.standard_normal((len(rows), D)), rng.standard_normal((len(rows), D))
+
+    r1, K1, V1 = doc(L1, M1)
+    r2, K2, V2 = doc(L2, M2)
+    n_pages = M1 + 1 + M2 + 1 + 3
+    kpool = rng.standard_normal((n_pages, C + 1, D))
+    vpool = rng.standard_normal((n_pages, C + 1, D))
+    slots = rng.permutation(n_pages)
+    def place(rows, K, V, first):
+        used = []
+        for i in range(0, len(rows), C + 1):
+            pg = int(slots[first + len(used)])
+            used.append(pg)
+            for j in range(min(C + 1, len(rows) - i)):
+                kpool[pg, j], vpool[pg, j] = K[i + j], V[i + j]
+        return used
+    p1 = place(r1, K1, V1, 0)                # M1 full chunk pages + one page with 2 raw rows
+    p2 = place(r2, K2, V2, len(p1))
+    pages = p1[:M1] + p2                      # the routed sequence: doc 1's chunks, then doc 2
+    extra = [(p1[M1], 0), (p1[M1], 1)]        # doc 1's last two tokens
+    N, M, T = M1 * C + L2, M1 + M2, 3
+    qg = rng.standard_normal((g, D))
+    res = oracle.decode_paged_unit(qg, kpool, vpool, pages, page_chunks=1, n_raw=N, n_gist=M, chunk=C, topk=M,
+                                   tail=T, extra_rows=extra)
+    keys, vals = np.concatenate([K1, K2]), np.concatenate([V1, V2])
+    np.testing.assert_allclose(res["out"], sdpa(qg, keys, vals, np.ones(len(keys), bool), 1 / math.sqrt(D)),
+                               rtol=0, atol=1e-12)
+    # plant doc 1's chunk 3 gist along the mean query: it is the one chosen
+    kpool[p1[3], C] = 50 * qg.mean(0) / np.linalg.norm(qg.mean(0))
+    res1 = oracle.decode_paged_unit(qg, kpool, vpool, pages, page_chunks=1, n_raw=N, n_gist=M, chunk=C, topk=1,
+                                    tail=T, extra_rows=extra)
+    assert res1["sel"].tolist() == [3]
