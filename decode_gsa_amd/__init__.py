@@ -8,6 +8,7 @@ built, every call raises (there is no fallback path).
 Entry points (same names as the C ABI):
   gsa_decode(q, k_cache, v_cache, chunk=, topk=, tail=, ...)
   gsa_decode_varlen(q, k_cache, v_cache, seq_n_raw=, seq_n_gist=, chunk=, topk=, tail=, ...)
+  gsa_decode_paged(q, k_pool, v_pool, block_table=, seq_n_raw=, seq_n_gist=, page_chunks=, ...)
   gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, chunk=, fanout=, topk1=, topk2=, tail=, ...)
   gsa_decode_levels(q, k_cache, v_cache, k_up, v_up, chunk=, fanout=, topks=, tail=, ...)
   gsa_prefill_blocksparse(q, k_cache, v_cache, chunk=, topk=, window=, q_start=, ...)
@@ -32,7 +33,8 @@ __all__ = [
     "gsa_decode", "gsa_decode_hier", "gsa_prefill_blocksparse", "gsa_profile_events",
     "gsa_profile_marks", "topk_for_budget", "GIST_SETS", "gsa_gist_prefill", "gsa_cache_append",
     "gsa_decode_levels", "levels_workspace_size", "gsa_decode_varlen", "check_seq_lens",
-    "launches", "gsa_decode_noalloc",
+    "launches", "gsa_decode_noalloc", "PagedParams", "paged_params", "paged_workspace_size",
+    "check_pages", "gsa_decode_paged",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -47,7 +49,8 @@ EXPORTED_SYMBOLS = (
     "gsa_topk_for_budget", "gsa_gist_prefill", "gsa_cache_append",
     "gsa_decode_levels_workspace_size", "gsa_decode_levels", "gsa_decode_varlen", "gsa_check_seq_lens",
     "gsa_decode_launches", "gsa_decode_hier_launches", "gsa_decode_levels_launches",
-    "gsa_prefill_launches", "gsa_decode_noalloc",
+    "gsa_prefill_launches", "gsa_decode_noalloc", "gsa_decode_paged_workspace_size",
+    "gsa_decode_paged", "gsa_check_pages",
 )
 MAX_LEVELS = 6
 
@@ -60,6 +63,11 @@ class DecodeParams(ctypes.Structure):
                 ("head_dim", _c_i32), ("n_raw", _c_i64), ("n_gist", _c_i64),
                 ("chunk", _c_i32), ("topk", _c_i32), ("tail", _c_i32), ("scale", _c_f32),
                 ("dtype", _c_i32), ("gist_set", _c_i32), ("row_capacity", _c_i64)]
+
+
+class PagedParams(ctypes.Structure):
+    _fields_ = [("base", DecodeParams), ("page_chunks", _c_i32), ("max_pages", _c_i32),
+                ("n_pages", _c_i64), ("max_extra", _c_i32)]
 
 
 class HierParams(ctypes.Structure):
@@ -126,6 +134,12 @@ def lib() -> ctypes.CDLL:
         L.gsa_cache_append.argtypes = [P(AppendParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.gsa_profile_events.argtypes = [P(_vp), _c_i32]
         L.gsa_profile_marks.argtypes = [P(_c_i32)]
+        L.gsa_decode_paged_workspace_size.argtypes = [P(PagedParams), P(_sz)]
+        L.gsa_decode_paged_workspace_size.restype = _c_i32
+        L.gsa_decode_paged.argtypes = [P(PagedParams)] + [_vp] * 11 + [_sz, _vp]
+        L.gsa_decode_paged.restype = _c_i32
+        L.gsa_check_pages.argtypes = [P(PagedParams), _vp, _vp, _vp, _vp]
+        L.gsa_check_pages.restype = _c_i32
         L.gsa_decode_noalloc.argtypes = [P(DecodeParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.gsa_decode_noalloc.restype = _c_i32
         L.gsa_decode_launches.argtypes = [P(DecodeParams), P(_c_i32)]
@@ -371,6 +385,91 @@ def gsa_decode_noalloc(q, k_cache, v_cache, *, chunk: int, topk: int, tail: int,
     _check(lib().gsa_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(out), _ptr(lse), _ptr(sel_idx) if topk > 0 else None,
                                     s.cuda_stream), "gsa_decode_noalloc")
+    return out, lse, sel_idx
+
+
+def paged_params(base: DecodeParams, page_chunks: int, max_pages: int, n_pages: int,
+                 max_extra: int = 0) -> PagedParams:
+    return PagedParams(base, page_chunks, max_pages, n_pages, max_extra)
+
+
+def paged_workspace_size(p: PagedParams) -> int:
+    n = _sz(0)
+    _check(lib().gsa_decode_paged_workspace_size(ctypes.byref(p), ctypes.byref(n)),
+           "gsa_decode_paged_workspace_size")
+    return n.value
+
+
+def _host_i32(x):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(x.cpu() if hasattr(x, "cpu") else x, dtype=np.int32))
+    return a
+
+
+def check_pages(p: PagedParams, block_table, seq_n_raw, seq_n_gist, extra_rows=None) -> None:
+    """Host check of paged inputs (see gsa_check_pages in include/gsa.h)."""
+    bt, n, m = _host_i32(block_table), _host_i32(seq_n_raw), _host_i32(seq_n_gist)
+    ex = _host_i32(extra_rows) if extra_rows is not None else None
+    _check(lib().gsa_check_pages(ctypes.byref(p), bt.ctypes.data, n.ctypes.data, m.ctypes.data,
+                                 ex.ctypes.data if ex is not None else None), "gsa_check_pages")
+
+
+def gsa_decode_paged(q, k_pool, v_pool, *, block_table, seq_n_raw, seq_n_gist, chunk: int, topk: int,
+                     tail: int, page_chunks: int, extra_rows=None, n_raw: Optional[int] = None,
+                     n_gist: Optional[int] = None, scale: float = 0.0, out=None, lse=None,
+                     sel_idx=None, workspace=None, stream=None, want_lse: bool = True,
+                     want_sel: bool = True):
+    """Decode over paged caches. k_pool, v_pool [n_pages, Hkv, P(C+1), D];
+    block_table [B, max_pages], seq_n_raw / seq_n_gist [B], extra_rows
+    [B, max_extra, 2] (page, row) or None. Host arrays are checked with
+    gsa_check_pages and copied to the device; device int32 tensors are used as
+    given (then n_raw= and n_gist=, the batch's largest, are required).
+
+    Returns (out [B,Hq,D] fp32, lse [B,Hq] or None, sel [B,Hkv,k] or None).
+    """
+    import torch
+    B, Hq, D = q.shape
+    n_pages, Hkv, rpp = k_pool.shape[0], k_pool.shape[1], k_pool.shape[2]
+    if rpp != page_chunks * (chunk + 1) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("pools must be [n_pages, Hkv, page_chunks * (chunk + 1), D], K and V alike")
+    dev = q.device
+    on_dev = isinstance(block_table, torch.Tensor) and block_table.is_cuda
+    if on_dev:
+        if n_raw is None or n_gist is None:
+            raise ValueError("device tables need n_raw= and n_gist= (the batch's largest)")
+        max_pages = block_table.shape[1]
+        max_extra = extra_rows.shape[1] if extra_rows is not None else 0
+    else:
+        n_h, m_h = _host_i32(seq_n_raw), _host_i32(seq_n_gist)
+        bt_h = _host_i32(block_table)
+        ex_h = _host_i32(extra_rows) if extra_rows is not None else None
+        n_raw = int(n_h.max()) if n_raw is None else n_raw
+        n_gist = int(m_h.max()) if n_gist is None else n_gist
+        max_pages = bt_h.shape[1]
+        max_extra = ex_h.shape[1] if ex_h is not None else 0
+    base = decode_params(B, Hq, Hkv, D, n_raw, n_gist, chunk, topk, tail, scale, _dtype_code(q))
+    p = paged_params(base, page_chunks, max_pages, n_pages, max_extra)
+    if not on_dev:
+        check_pages(p, bt_h, n_h, m_h, ex_h)
+    s, on_s = _on_stream(stream, dev)
+    with on_s:
+        if on_dev:
+            bt, sn, sm, ex = block_table, seq_n_raw, seq_n_gist, extra_rows
+        else:
+            bt = torch.from_numpy(bt_h).to(dev)
+            sn, sm = torch.from_numpy(n_h).to(dev), torch.from_numpy(m_h).to(dev)
+            ex = torch.from_numpy(ex_h).to(dev) if ex_h is not None else None
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
+        if lse is None and want_lse:
+            lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        if sel_idx is None and want_sel:
+            sel_idx = torch.empty(B, Hkv, max(topk, 0), dtype=torch.int32, device=dev)
+        ws = _workspace(workspace, paged_workspace_size(p), dev)
+        _check(lib().gsa_decode_paged(ctypes.byref(p), _ptr(bt), _ptr(sn), _ptr(sm),
+                                      _ptr(ex) if max_extra > 0 else None, _ptr(q), _ptr(k_pool),
+                                      _ptr(v_pool), _ptr(out), _ptr(lse),
+                                      _ptr(sel_idx) if topk > 0 else None, _ptr(ws), _nbytes(ws),
+                                      s.cuda_stream), "gsa_decode_paged")
     return out, lse, sel_idx
 
 

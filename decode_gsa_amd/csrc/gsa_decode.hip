@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "gsa.h"
 #include "gsa_device.hpp"
@@ -1706,6 +1707,16 @@ struct UnitArgs {
   // which gists the attention set holds: 0 all, 1 the selected chunks', 2 none
   int32_t gist_set;
   SeqLens seq;            // per-sequence lengths (single-level decode)
+  // paged caches (read only by the PAGED instantiations): K and V are pools
+  // [n_pages][Hkv][rpp][D] of pages of 2^lp chunk slots (rpp = 2^lp (C + 1)
+  // rows); sequence b's logical row r is row r mod rpp of page
+  // table[b][r / rpp]; extra [B][max_extra][2] (page, row) pairs of rows
+  // attended directly, the list ending at the first negative page
+  const int32_t* pg_table;
+  const int32_t* pg_extra;
+  int64_t pg_count;       // pages in the pool
+  int64_t pg_bytes;       // bytes between consecutive pages (Hkv rpp 256)
+  int32_t pg_max, pg_lp, pg_rpp, pg_max_extra, Hkv;
 };
 
 // Several workgroups per unit: each split's top-kk group scores and ids
@@ -1744,6 +1755,51 @@ struct UnitLds {
   uint32_t s_old;
 };
 
+// Paged caches: the sequence's block table and extra rows, staged in LDS at
+// the start of the launch (page ids clamped into the pool, so that every read
+// stays inside it whatever the tables hold).
+constexpr int kMaxPages = (int)kPagedMaxPages;
+constexpr int kMaxExtra = (int)kPagedMaxExtra;
+struct PagedLds : UnitLds {
+  int32_t pages[kMaxPages];
+  int32_t extra[2 * kMaxExtra];
+  int32_t n_extra;
+};
+// Logical row of extra row e in the item streams (above every cache row).
+constexpr int kExtraRow = 1 << 30;
+
+__device__ __forceinline__ void stage_pages(const UnitArgs& a, int unit, PagedLds& L) {
+  const int tid = threadIdx.x;
+  const int b = unit / a.Hkv;
+  if (tid == 0) L.n_extra = a.pg_max_extra;
+  const int32_t* tb = a.pg_table + (size_t)b * a.pg_max;
+  for (int i = tid; i < a.pg_max; i += kThreads)
+    L.pages[i] = (int32_t)min((int64_t)max(tb[i], 0), a.pg_count - 1);
+  __syncthreads();
+  const int32_t* ex = a.pg_extra + (size_t)b * a.pg_max_extra * 2;
+  for (int i = tid; i < a.pg_max_extra; i += kThreads) {
+    const int32_t pg = ex[2 * i], r = ex[2 * i + 1];
+    if (pg < 0) atomicMin(&L.n_extra, i);
+    L.extra[2 * i] = (int32_t)min((int64_t)max(pg, 0), a.pg_count - 1);
+    L.extra[2 * i + 1] = min(max(r, 0), a.pg_rpp - 1);
+  }
+  __syncthreads();
+}
+
+// Byte offset (from the unit's kv-head base in page 0) of a logical row, an
+// extra row (kExtraRow + e) or a masked item (-1: page 0, row 0).
+__device__ __forceinline__ int64_t paged_off(const UnitArgs& a, const PagedLds& L, int row) {
+  if (row < 0) return 0;
+  if (row >= kExtraRow) {
+    const int e = row - kExtraRow;
+    return (int64_t)L.extra[2 * e] * a.pg_bytes + (int64_t)L.extra[2 * e + 1] * 256;
+  }
+  const unsigned m = (unsigned)row / (unsigned)(a.C + 1);
+  const unsigned pi = m >> a.pg_lp;
+  const unsigned r = (unsigned)row - (pi << a.pg_lp) * (unsigned)(a.C + 1);
+  return (int64_t)L.pages[pi] * a.pg_bytes + (int64_t)r * 256;
+}
+
 // One wave's running softmax state: lane (h, j) holds head h's max and its
 // share of the sum, and O^T[16 dt + 4 j + r][h] in o[dt][r].
 struct UState {
@@ -1768,12 +1824,15 @@ struct UState {
 enum { kUKGists = 0, kUKUnfold = 1, kUKL2 = 2, kUKCand = 3, kUKScore = 4, kUKSet = 5 };
 
 // Stream items [i0, i1) of one kind through the wave's state.
-template <int KIND>
+// PAGED: Kb / Vb are the unit's kv-head base in page 0 of the pools, rows are
+// translated through the staged block table (pl), and kUKGists streams the
+// sequence's extra rows after the tail.
+template <int KIND, bool PAGED = false>
 __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const char* __restrict__ Vb, int i0,
                                             int i1, const UnitArgs& a, const bf16x8u (&qf)[4], UState& st,
                                             char* ring, float* lds_scores, const int32_t* lds_sel,
                                             int score_base = 0, const char* K2b = nullptr,
-                                            const char* V2b = nullptr) {
+                                            const char* V2b = nullptr, const PagedLds* pl = nullptr) {
   const int n = i1 - i0;
   if (n <= 0) return;
   const int lane = threadIdx.x & 63;
@@ -1800,6 +1859,7 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     if (KIND == kUKGists || KIND == kUKL2) {
       const int nf = KIND == kUKGists ? M : (int)a.M2;
       if (i < nf) return KIND == kUKGists ? i * (C + 1) + C : -2 - i;
+      if (PAGED && i - nf >= a.T) return kExtraRow + (i - nf - a.T);
       const unsigned pos = tail0 + (unsigned)(i - nf);
       return (int)(pos + min(pos / (unsigned)C, (unsigned)M));
     }
@@ -1840,7 +1900,10 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     for (int u = 0; u < 4; ++u) {
       const int r = 4 * u + (lane >> 4);
       const int row = row_of(i0 + b * kRows + r);
-      int64_t koffr = (int64_t)(row >= 0 ? row : 0) * 256, voffr = koffr;
+      int64_t koffr, voffr;
+      if constexpr (PAGED) koffr = paged_off(a, *pl, row);
+      else koffr = (int64_t)(row >= 0 ? row : 0) * 256;
+      voffr = koffr;
       if (KIND == kUKL2 && row <= -2) {
         koffr = k2off + (int64_t)(-2 - row) * 256;
         voffr = v2off + (int64_t)(-2 - row) * 256;
@@ -2141,9 +2204,11 @@ __device__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16
 enum { kHierNone = 0, kHierDescend = 1, kHierTop = 2 };
 // SPLIT: several workgroups per unit (a.S > 1); the one-workgroup-per-unit
 // instantiation carries none of the hand-off code.
-template <int G, int HIER, bool SETS = false, bool VARLEN = false, bool SPLIT = true>
+// PAGED (with VARLEN): the caches are page pools (gsa_decode_paged).
+template <int G, int HIER, bool SETS = false, bool VARLEN = false, bool SPLIT = true, bool PAGED = false>
 __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
-  __shared__ __attribute__((aligned(16))) UnitLds L;
+  static_assert(!PAGED || (VARLEN && !HIER && !SETS), "paged caches: single-level, per-sequence lengths");
+  __shared__ __attribute__((aligned(16))) std::conditional_t<PAGED, PagedLds, UnitLds> L;
   UnitArgs a = args;
   // the wave index as a scalar: each wave's item ranges and trip counts are
   // then uniform, and the row loops branch on scalars
@@ -2154,6 +2219,15 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
   if constexpr (VARLEN) unit_lengths(args.seq, unit, args.N, args.M, args.C, args.T, &a.N, &a.M);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
   const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
+  const PagedLds* pl = nullptr;
+  int n_extra = 0;
+  if constexpr (PAGED) {
+    stage_pages(a, unit, L);
+    pl = &L;
+    n_extra = L.n_extra;
+    Kb = reinterpret_cast<const char*>(a.K) + (size_t)(unit % a.Hkv) * a.pg_rpp * 256;
+    Vb = reinterpret_cast<const char*>(a.V) + (size_t)(unit % a.Hkv) * a.pg_rpp * 256;
+  }
   // query fragments: lane (h, j) holds q_h[32 ks + 8 j .. +8], zero past g heads
   bf16x8u qf[4];
   {
@@ -2176,7 +2250,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
   // gists and tail as one item range: S consecutive shares, each in four wave shares
   const int M = (int)a.M;
   const int nf = HIER ? (int)a.M2 : M;   // scored items ahead of the tail
-  const int n1 = nf + a.T;
+  const int n1 = nf + a.T + n_extra;     // (paged: the extra rows after the tail)
   const int perw = (n1 + S - 1) / S;
   const int w0 = min(n1, split * perw), w1 = min(n1, w0 + perw);
   const int per1 = (w1 - w0 + kUW - 1) / kUW;
@@ -2216,8 +2290,8 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
       for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
     return;
   }
-  unit_stream<kUKGists>(Kb, Vb, min(w1, w0 + w * per1), min(w1, w0 + (w + 1) * per1), a, qf, st, ring, L.scores,
-                        L.sel, w0);
+  unit_stream<kUKGists, PAGED>(Kb, Vb, min(w1, w0 + w * per1), min(w1, w0 + (w + 1) * per1), a, qf, st, ring,
+                               L.scores, L.sel, w0, nullptr, nullptr, pl);
   float* gs = a.scores + (size_t)unit * a.score_stride;
   const int items = a.k * a.C;
   const int per2 = (items + kUW - 1) / kUW;
@@ -2227,8 +2301,8 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
       unit_select<kUMaxGist / kThreads, true>(L.scores, M, a.k, gs, a.score_stride, unit, L.sel, L.u.sel.s,
                                                L.u.sel.t);
       __syncthreads();
-      unit_stream<kUKUnfold>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
-                         L.sel);
+      unit_stream<kUKUnfold, PAGED>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring,
+                                    L.scores, L.sel, 0, nullptr, nullptr, pl);
     }
     unit_combine<G>(L, st, w, a.out + (size_t)unit * G * 128, a.lse ? a.lse + (size_t)unit * G : nullptr,
                     nullptr);
@@ -2263,9 +2337,10 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
 // launch wrote (every workgroup of the unit makes the same one), streams
 // share p of the chosen chunks' raw rows, and hands its partial state on; the
 // unit's last workgroup merges the S stream and S2 unfold partials.
-template <int G, bool VARLEN = false>
+template <int G, bool VARLEN = false, bool PAGED = false>
 __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
-  __shared__ __attribute__((aligned(16))) UnitLds L;
+  static_assert(!PAGED || VARLEN, "paged caches: per-sequence lengths");
+  __shared__ __attribute__((aligned(16))) std::conditional_t<PAGED, PagedLds, UnitLds> L;
   UnitArgs a = args;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq = lane & 15, jg = lane >> 4;
@@ -2274,6 +2349,13 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   if constexpr (VARLEN) unit_lengths(args.seq, unit, args.N, args.M, args.C, args.T, &a.N, &a.M);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
   const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
+  const PagedLds* pl = nullptr;
+  if constexpr (PAGED) {
+    stage_pages(a, unit, L);
+    pl = &L;
+    Kb = reinterpret_cast<const char*>(a.K) + (size_t)(unit % a.Hkv) * a.pg_rpp * 256;
+    Vb = reinterpret_cast<const char*>(a.V) + (size_t)(unit % a.Hkv) * a.pg_rpp * 256;
+  }
   bf16x8u qf[4];
   {
     const char* qb = reinterpret_cast<const char*>(a.q) + ((size_t)unit * G + (hq < G ? hq : 0)) * 256 + 16 * jg;
@@ -2301,8 +2383,8 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   const int perp = (items + S2 - 1) / S2;
   const int p0 = min(items, part * perp), p1 = min(items, p0 + perp);
   const int per2 = (p1 - p0 + kUW - 1) / kUW;
-  unit_stream<kUKUnfold>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st, L.u.ring[w][0],
-                     L.scores, L.sel);
+  unit_stream<kUKUnfold, PAGED>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st,
+                                L.u.ring[w][0], L.scores, L.sel, 0, nullptr, nullptr, pl);
   float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
   unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)(a.S + part) * a.part_stride);
   if (!arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)S2, &L.s_old)) return;
@@ -2575,8 +2657,26 @@ gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const 
   u.part = reinterpret_cast<float*>(ws + pl.off_part);
   u.cnt = ctrl_of(ws, pl.off_ctrl, 0);
   u.seq = SeqLens{pl.seq_n, pl.seq_m, pl.Hkv, pl.k};
+  u.Hkv = pl.Hkv;
   prof_begin_call();
   const bool varlen = pl.seq_n != nullptr;
+  if (pl.pg_table != nullptr) {   // paged caches (per-sequence lengths)
+    u.pg_table = pl.pg_table; u.pg_extra = pl.pg_extra; u.pg_count = pl.pg_count;
+    u.pg_max = pl.pg_max; u.pg_max_extra = pl.pg_max_extra;
+    int lp = 0;
+    while ((1 << lp) < pl.pg_P) ++lp;
+    u.pg_lp = lp;
+    u.pg_rpp = pl.pg_P * (pl.C + 1);
+    u.pg_bytes = (int64_t)pl.Hkv * u.pg_rpp * 256;
+    if (pl.unit_S == 1)
+      prof_launch((unit_kernel<G, kHierNone, false, true, false, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+    else
+      prof_launch((unit_kernel<G, kHierNone, false, true, true, true>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0,
+                  st, u);
+    if (pl.unit_S2 > 0)
+      prof_launch((unit_unfold_kernel<G, true, true>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st, u);
+    return launch_status("gsa_decode_paged launch");
+  }
   if (pl.gist_set != GSA_GISTS_ALL)
     prof_launch((unit_kernel<G, kHierNone, true, false, false>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
   else if (varlen && pl.unit_S == 1)
@@ -2874,6 +2974,51 @@ extern "C" gsa_status_t gsa_decode_varlen(const gsa_decode_params* p, const int3
   return dispatch<DecodeRunner>(pl.dtype, pl.D, pl.g, pl, q, k_cache, v_cache, out, lse, sel_idx, ws, hs);
 }
 
+
+extern "C" gsa_status_t gsa_decode_paged_workspace_size(const gsa_paged_params* p, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(GSA_ERR_INVALID_ARG, "bytes is NULL");
+  DecodePlan pl;
+  gsa_status_t s = plan_paged(p, &pl);
+  if (s != GSA_OK) return s;
+  *bytes = pl.total;
+  return GSA_OK;
+}
+
+extern "C" gsa_status_t gsa_decode_paged(const gsa_paged_params* p, const int32_t* block_table,
+                                         const int32_t* seq_n_raw, const int32_t* seq_n_gist,
+                                         const int32_t* extra_rows, const void* q, const void* k_pool,
+                                         const void* v_pool, float* out, float* lse, int32_t* sel_idx,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  prof_begin_call();
+  DecodePlan pl;
+  gsa_status_t s = plan_paged(p, &pl);
+  if (s != GSA_OK) return s;
+  if ((s = check_ptr(block_table, "block_table")) != GSA_OK || (s = check_ptr(seq_n_raw, "seq_n_raw")) != GSA_OK ||
+      (s = check_ptr(seq_n_gist, "seq_n_gist")) != GSA_OK ||
+      (s = check_ptr(extra_rows, "extra_rows", p->max_extra == 0)) != GSA_OK || (s = check_ptr(q, "q")) != GSA_OK ||
+      (s = check_ptr(k_pool, "k_pool")) != GSA_OK || (s = check_ptr(v_pool, "v_pool")) != GSA_OK ||
+      (s = check_ptr(out, "out")) != GSA_OK || (s = check_ptr(lse, "lse", true)) != GSA_OK ||
+      (s = check_ptr(sel_idx, "sel_idx", true)) != GSA_OK)
+    return s;
+  if ((s = check_workspace(workspace, workspace_bytes, pl.total)) != GSA_OK) return s;
+  pl.seq_n = seq_n_raw;
+  pl.seq_m = seq_n_gist;
+  pl.pg_table = block_table;
+  // no extra rows: an empty list (the pointer is never read)
+  pl.pg_extra = extra_rows != nullptr ? extra_rows : block_table;
+  if (extra_rows == nullptr) pl.pg_max_extra = 0;
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  switch (pl.g) {
+    case 1: return run_unit<1>(pl, q, k_pool, v_pool, out, lse, sel_idx, ws, hs);
+    case 2: return run_unit<2>(pl, q, k_pool, v_pool, out, lse, sel_idx, ws, hs);
+    case 4: return run_unit<4>(pl, q, k_pool, v_pool, out, lse, sel_idx, ws, hs);
+    case 8: return run_unit<8>(pl, q, k_pool, v_pool, out, lse, sel_idx, ws, hs);
+  }
+  return fail(GSA_ERR_UNSUPPORTED, "no kernel for g=%d", pl.g);
+}
 
 // ------------------------------------------------ decode without allocation
 //

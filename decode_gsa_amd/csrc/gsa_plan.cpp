@@ -218,6 +218,41 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   return GSA_OK;
 }
 
+gsa_status_t plan_paged(const gsa_paged_params* p, DecodePlan* o) {
+  if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->base.row_capacity != 0)
+    return fail(GSA_ERR_INVALID_ARG, "paged decode: base.row_capacity must be 0 (pages hold the rows)");
+  if (p->base.gist_set != GSA_GISTS_ALL)
+    return fail(GSA_ERR_UNSUPPORTED, "paged decode attends every gist: base.gist_set must be 0");
+  gsa_status_t s = plan_decode(&p->base, o);
+  if (s != GSA_OK) return s;
+  const int32_t P = p->page_chunks;
+  if (P < 1 || P > 64 || (P & (P - 1)) != 0)
+    return fail(GSA_ERR_INVALID_ARG, "page_chunks=%d must be a power of two in [1, 64]", P);
+  const int64_t rpp = (int64_t)P * (p->base.chunk + 1);
+  const int64_t need = (o->N + o->M + rpp - 1) / rpp;   // pages of the longest sequence
+  if (p->max_pages < need || p->max_pages < 1)
+    return fail(GSA_ERR_INVALID_ARG, "max_pages=%d below the %lld pages of n_raw + n_gist rows", p->max_pages,
+                (long long)need);
+  if (p->max_pages > kPagedMaxPages)
+    return fail(GSA_ERR_UNSUPPORTED, "max_pages=%d above %d", p->max_pages, kPagedMaxPages);
+  if (p->n_pages < 1 || p->n_pages > ((int64_t)1 << 31) - 1)
+    return fail(GSA_ERR_INVALID_ARG, "n_pages=%lld must be in [1, 2^31)", (long long)p->n_pages);
+  if (p->max_extra < 0 || p->max_extra > kPagedMaxExtra)
+    return fail(p->max_extra < 0 ? GSA_ERR_INVALID_ARG : GSA_ERR_UNSUPPORTED, "max_extra=%d outside [0, %d]",
+                p->max_extra, kPagedMaxExtra);
+  if (o->unit_S == 0)
+    return fail(GSA_ERR_UNSUPPORTED,
+                "paged decode runs on the bf16, head_dim 128, topk <= 64 path (n_gist <= 16384 when topk > 0)");
+  if (o->N + o->M + (int64_t)p->max_extra >= ((int64_t)1 << 30))
+    return fail(GSA_ERR_UNSUPPORTED, "paged decode: sequences up to 2^30 rows");
+  o->pg_P = P;
+  o->pg_max = p->max_pages;
+  o->pg_max_extra = p->max_extra;
+  o->pg_count = p->n_pages;
+  return GSA_OK;
+}
+
 gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
   if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
   if (p->base.gist_set != GSA_GISTS_ALL)
@@ -558,6 +593,36 @@ extern "C" gsa_status_t gsa_check_seq_lens(const gsa_decode_params* p, const int
                        "sequence %d: n_raw=%lld, n_gist=%lld break 1 <= n <= %lld, %d <= m <= %lld, "
                        "0 <= n - m*C <= C, n - m*C <= tail=%d <= n",
                        b, (long long)n, (long long)m, (long long)p->n_raw, p->topk, (long long)p->n_gist, p->tail);
+  }
+  return GSA_OK;
+}
+
+extern "C" gsa_status_t gsa_check_pages(const gsa_paged_params* p, const int32_t* block_table,
+                                        const int32_t* seq_n_raw, const int32_t* seq_n_gist,
+                                        const int32_t* extra_rows) {
+  gsa::clear_error();
+  gsa::DecodePlan d;
+  gsa_status_t s = gsa::plan_paged(p, &d);
+  if (s != GSA_OK) return s;
+  if ((s = gsa_check_seq_lens(&p->base, seq_n_raw, seq_n_gist)) != GSA_OK) return s;
+  if (!block_table) return gsa::fail(GSA_ERR_INVALID_ARG, "block_table is NULL");
+  if (p->max_extra > 0 && !extra_rows) return gsa::fail(GSA_ERR_INVALID_ARG, "extra_rows is NULL");
+  const int64_t rpp = (int64_t)p->page_chunks * (p->base.chunk + 1);
+  for (int32_t b = 0; b < p->base.batch; ++b) {
+    const int64_t rows = (int64_t)seq_n_raw[b] + seq_n_gist[b];
+    const int64_t pages = (rows + rpp - 1) / rpp;
+    for (int64_t i = 0; i < pages; ++i) {
+      const int32_t pg = block_table[(size_t)b * p->max_pages + i];
+      if (pg < 0 || pg >= p->n_pages)
+        return gsa::fail(GSA_ERR_INVALID_ARG, "sequence %d: page %lld of its table is %d, outside [0, %lld)", b,
+                         (long long)i, pg, (long long)p->n_pages);
+    }
+    for (int32_t e = 0; e < p->max_extra; ++e) {
+      const int32_t pg = extra_rows[((size_t)b * p->max_extra + e) * 2], r = extra_rows[((size_t)b * p->max_extra + e) * 2 + 1];
+      if (pg < 0) break;
+      if (pg >= p->n_pages || r < 0 || r >= rpp)
+        return gsa::fail(GSA_ERR_INVALID_ARG, "sequence %d: extra row %d is (%d, %d), outside the pool", b, e, pg, r);
+    }
   }
   return GSA_OK;
 }

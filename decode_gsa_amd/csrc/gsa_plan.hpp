@@ -63,6 +63,11 @@ inline size_t ctrl_bytes(int64_t units) {
 // scores at or above a bound on its kk-th largest (2 kk slots), or its exact
 // top kk when 2 kk slots per split would make the unit's list longer than
 // kUnitMaxSel. The kernels and the plan both use this.
+// Paged caches (gsa_decode_paged): a sequence's block table and extra rows
+// are staged in LDS, so they hold at most this many entries.
+constexpr int32_t kPagedMaxPages = 2048;
+constexpr int32_t kPagedMaxExtra = 64;
+
 // The several-workgroups-per-unit launch hands candidates on for k up to
 // this; above it every group score.
 constexpr int32_t kUnitCandMaxK = 16;
@@ -117,9 +122,18 @@ struct DecodePlan {
   // sequence's raw tokens and gists, null for uniform lengths
   const int32_t* seq_n;
   const int32_t* seq_m;
+  // paged caches (gsa_decode_paged): block tables [B][pg_max], extra rows
+  // [B][pg_max_extra][2], pages of pg_P chunk slots; null otherwise
+  const int32_t* pg_table;
+  const int32_t* pg_extra;
+  int64_t pg_count;
+  int32_t pg_P, pg_max, pg_max_extra;
 };
 
 gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* out);
+// Paged decode: plan_decode of the base, then the paging checks; the launch
+// must be the one-workgroup-per-unit path (bf16, D = 128, k <= 64).
+gsa_status_t plan_paged(const gsa_paged_params* p, DecodePlan* out);
 
 // Two-level plan: level-2 gist pass, candidate level-1 gist pass, unfold.
 struct HierPlan {

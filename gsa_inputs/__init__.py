@@ -30,7 +30,7 @@ __all__ = [
     "DecodeConfig", "HierConfig", "PrefillConfig", "GistConfig", "VarlenConfig", "CONFIGS",
     "DecodeInputs", "HierInputs", "PrefillInputs",
     "make_decode", "make_hier", "make_prefill", "make_gist", "TokenStream", "make_token_stream",
-    "make_levels", "level_sizes", "varlen_lengths",
+    "make_levels", "level_sizes", "varlen_lengths", "to_pages",
     "raw_row", "gist_row", "n_rows",
 ]
 
@@ -609,6 +609,35 @@ def make_levels(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, n_ra
     k_up = [draw(batch, n_kv_heads, m) for m in sizes[1:]]
     v_up = [draw(batch, n_kv_heads, m) for m in sizes[1:]]
     return q, k, v, k_up, v_up
+
+
+def to_pages(k_cache, v_cache, rows, page_chunks: int, chunk: int, seed: int, spare: int = 3):
+    """Scatter dense caches [B, Hkv, cap, D] into shuffled page pools: sequence
+    b's first rows[b] rows go page by page (P(C+1) rows each) to distinct
+    random pages of one pool, `spare` unused pages (random values) mixed in.
+    Returns (k_pool, v_pool [n_pages, Hkv, P(C+1), D], block_table [B,
+    max_pages] int32 with -1 past a sequence's pages)."""
+    B, Hkv, cap, D = k_cache.shape
+    rpp = page_chunks * (chunk + 1)
+    need = [-(-int(r) // rpp) for r in rows]
+    max_pages = max(1, max(need))
+    n_pages = sum(need) + spare
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(n_pages)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    k_pool = torch.randn(n_pages, Hkv, rpp, D, generator=g).to(k_cache.dtype).to(k_cache.device)
+    v_pool = torch.randn(n_pages, Hkv, rpp, D, generator=g).to(k_cache.dtype).to(k_cache.device)
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    nxt = 0
+    for b in range(B):
+        for i in range(need[b]):
+            pg = int(perm[nxt])
+            nxt += 1
+            table[b, i] = pg
+            r0, r1 = i * rpp, min(int(rows[b]), (i + 1) * rpp)
+            k_pool[pg, :, :r1 - r0] = k_cache[b, :, r0:r1]
+            v_pool[pg, :, :r1 - r0] = v_cache[b, :, r0:r1]
+    return k_pool, v_pool, table
 
 
 def varlen_lengths(batch: int, n_min: int, n_max: int, chunk: int, seed: int):

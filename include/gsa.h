@@ -161,6 +161,65 @@ gsa_status_t gsa_decode_varlen(const gsa_decode_params* p, const int32_t* seq_n_
                                const void* v_cache, float* out, float* lse, int32_t* sel_idx,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Paged caches: gsa_decode_varlen's step over caches that live in pages of a
+ * shared pool, plus rows attended directly.
+ * Source: the explainer's section 4 'Experimental Results' (KV-cache reuse:
+ * document caches computed once and reused, the query routed among their
+ * gists) with the decode rule of section 2 'Key Concepts'. A page holds P
+ * chunk slots of C + 1 rows (C raw rows and the chunk's gist), so no chunk
+ * straddles two pages. Sequence b's interleaved cache (gsa_decode's layout)
+ * is its block table's pages in order: logical row r is row r mod P(C+1) of
+ * page block_table[b][r / (P(C+1))]. Documents reused from separate caches
+ * concatenate by listing their pages (P = 1 concatenates at any chunk); a
+ * document that ends mid-chunk lists its complete chunks, and its last raw
+ * tokens, which no gist summarises, go in extra_rows: they are attended
+ * directly, like the tail.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  gsa_decode_params base; /* as gsa_decode_varlen: n_raw / n_gist are the
+                             batch's largest; bf16, head_dim 128, topk <= 64
+                             (n_gist <= 16384 when topk > 0), gist_set 0,
+                             row_capacity 0; else GSA_ERR_UNSUPPORTED /
+                             GSA_ERR_INVALID_ARG */
+  int32_t page_chunks;    /* P: chunk slots per page, a power of two in [1, 64] */
+  int32_t max_pages;      /* columns of block_table, >= the pages of
+                             n_raw + n_gist rows, <= 2048 */
+  int64_t n_pages;        /* pages in each pool, >= 1 */
+  int32_t max_extra;      /* columns of extra_rows, 0..64 */
+} gsa_paged_params;
+
+/* Bytes of device workspace gsa_decode_paged needs (as gsa_decode's). */
+gsa_status_t gsa_decode_paged_workspace_size(const gsa_paged_params* p, size_t* bytes);
+
+/*
+ * block_table  [B, max_pages] int32 (device): page ids of each sequence's
+ *              logical pages; entries past its rows are not read
+ * seq_n_raw, seq_n_gist  [B] int32 (device): as gsa_decode_varlen
+ * extra_rows   [B, max_extra, 2] int32 (device) (page, row within the page)
+ *              pairs attended by every query head of the sequence's kv-heads
+ *              (the same row of each kv-head's slab of the page); a
+ *              sequence's list ends at its first entry with a negative page;
+ *              NULL when max_extra = 0
+ * q            [B, Hq, D]
+ * k_pool, v_pool [n_pages, Hkv, P(C+1), D]: page p's rows of kv-head j
+ * out, lse, sel_idx, workspace: as gsa_decode (zero-filled once).
+ * The kernels clamp page ids and rows into the pools (a bad table gives a
+ * wrong result, never a read outside them); gsa_check_pages validates host
+ * copies. Launches as gsa_decode_varlen of the same base parameters.
+ */
+gsa_status_t gsa_decode_paged(const gsa_paged_params* p, const int32_t* block_table, const int32_t* seq_n_raw,
+                              const int32_t* seq_n_gist, const int32_t* extra_rows, const void* q,
+                              const void* k_pool, const void* v_pool, float* out, float* lse, int32_t* sel_idx,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host check of paged inputs (host arrays): the lengths as
+ * gsa_check_seq_lens, every page id a sequence reads in [0, n_pages), every
+ * extra row's page in [0, n_pages) and row in [0, P(C+1)). GSA_OK or
+ * GSA_ERR_INVALID_ARG naming the first bad entry (gsa_last_error). */
+gsa_status_t gsa_check_pages(const gsa_paged_params* p, const int32_t* block_table, const int32_t* seq_n_raw,
+                             const int32_t* seq_n_gist, const int32_t* extra_rows);
+
 /* Host check of per-sequence lengths (host arrays [p->batch]) against the
  * rules above: GSA_OK, or GSA_ERR_INVALID_ARG naming the first sequence that
  * breaks one (gsa_last_error). */
@@ -401,7 +460,8 @@ gsa_status_t gsa_profile_marks(int32_t* n);
 /* Host-only queries: *n = the number of kernel launches a call with these
  * parameters makes (the timing hook takes *n + 1 events), after the same
  * validation as the call itself (its status on failure). The counts:
- *   gsa_decode / gsa_decode_varlen on the bf16, D = 128, topk <= 64 path
+ *   gsa_decode / gsa_decode_varlen / gsa_decode_paged (its base) on the
+ *     bf16, D = 128, topk <= 64 path
  *     (n_gist <= 16384 when topk > 0): 1 when each (batch, kv-head) unit
  *     takes one workgroup (B*Hkv >= 256 and n_gist <= 4096) or topk = 0,
  *     else 2 (a stream launch, then a select-unfold-merge launch);

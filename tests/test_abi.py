@@ -48,6 +48,9 @@ int main(void) {
   printf("gsa_prefill_params %zu\n", sizeof(gsa_prefill_params));
   printf("gsa_gist_params %zu\n", sizeof(gsa_gist_params));
   printf("gsa_levels_params %zu\n", sizeof(gsa_levels_params));
+  printf("gsa_paged_params %zu\n", sizeof(gsa_paged_params));
+  F(gsa_paged_params, page_chunks); F(gsa_paged_params, max_pages); F(gsa_paged_params, n_pages);
+  F(gsa_paged_params, max_extra);
   printf("GSA_MAX_LEVELS %d\n", GSA_MAX_LEVELS);
   F(gsa_levels_params, n_levels); F(gsa_levels_params, fanout); F(gsa_levels_params, topk_up);
   printf("gsa_append_params %zu\n", sizeof(gsa_append_params));
@@ -77,6 +80,7 @@ int main(void) {
     assert int(got["gsa_prefill_params"]) == ctypes.sizeof(gsa.PrefillParams)
     assert int(got["gsa_gist_params"]) == ctypes.sizeof(gsa.GistParams)
     assert int(got["gsa_levels_params"]) == ctypes.sizeof(gsa.LevelsParams)
+    assert int(got["gsa_paged_params"]) == ctypes.sizeof(gsa.PagedParams)
     assert int(got["GSA_MAX_LEVELS"]) == gsa.MAX_LEVELS
     assert int(got["gsa_append_params"]) == ctypes.sizeof(gsa.AppendParams)
     assert [int(got[f"GSA_GISTS_{n}"]) for n in ("ALL", "SELECTED", "NONE")] == \
@@ -86,7 +90,8 @@ int main(void) {
             t, m = key.split(".")
             cls = {"gsa_decode_params": gsa.DecodeParams, "gsa_hier_params": gsa.HierParams,
                    "gsa_prefill_params": gsa.PrefillParams, "gsa_gist_params": gsa.GistParams,
-                   "gsa_append_params": gsa.AppendParams, "gsa_levels_params": gsa.LevelsParams}[t]
+                   "gsa_append_params": gsa.AppendParams, "gsa_levels_params": gsa.LevelsParams,
+                   "gsa_paged_params": gsa.PagedParams}[t]
             assert getattr(cls, m).offset == int(val), key
 
 
@@ -570,3 +575,65 @@ def test_decode_noalloc_host_rejections(L):
                                 None) == INVALID
     n = ctypes.c_int32(-1)
     assert L.gsa_profile_marks(ctypes.byref(n)) == OK and n.value == 1   # nothing launched
+
+
+# ---------------------------------------------------------------- paged ---
+
+def good_paged(base_kw=None, **kw):
+    b = dict(batch=4, n_q_heads=8, n_kv_heads=2, head_dim=128, n_raw=4096, n_gist=256, chunk=16, topk=8,
+             tail=64, scale=0.0, dtype=gsa.GSA_BF16)
+    b.update(base_kw or {})
+    p = dict(page_chunks=4, max_pages=64, n_pages=300, max_extra=8)
+    p.update(kw)
+    return gsa.PagedParams(gsa.DecodeParams(**b), **p)
+
+
+@pytest.mark.parametrize("base_kw,kw,status", [
+    ({}, {}, OK),
+    ({}, {"page_chunks": 3}, INVALID),                 # not a power of two
+    ({}, {"page_chunks": 128}, INVALID),
+    ({}, {"max_pages": 63}, INVALID),                  # 4352 rows need 64 pages of 68
+    ({}, {"max_pages": 4096}, UNSUPPORTED),
+    ({}, {"n_pages": 0}, INVALID),
+    ({}, {"max_extra": -1}, INVALID),
+    ({}, {"max_extra": 65}, UNSUPPORTED),
+    ({"dtype": gsa.GSA_F32}, {}, UNSUPPORTED),         # split path shapes
+    ({"head_dim": 64}, {}, UNSUPPORTED),
+    ({"topk": 80, "n_raw": 4096 * 4, "n_gist": 1024}, {"max_pages": 256}, UNSUPPORTED),
+    ({"row_capacity": 9000}, {}, INVALID),
+    ({"gist_set": 1}, {}, UNSUPPORTED),
+])
+def test_paged_param_validation(L, base_kw, kw, status):
+    n = ctypes.c_size_t(0)
+    assert L.gsa_decode_paged_workspace_size(ctypes.byref(good_paged(base_kw, **kw)), ctypes.byref(n)) == status
+
+
+def test_check_pages(L):
+    import numpy as np
+    p = good_paged()
+    B, P, C = 4, 4, 16
+    rpp = P * (C + 1)
+    n = np.array([4096, 1000, 2048, 200], dtype=np.int32)
+    m = np.array([256, 62, 127, 12], dtype=np.int32)
+    table = np.full((B, 64), -1, dtype=np.int32)
+    for b in range(B):
+        need = -(-(int(n[b]) + int(m[b])) // rpp)
+        table[b, :need] = np.arange(need) + 70 * b
+    extra = np.full((B, 8, 2), -1, dtype=np.int32)
+    extra[1, 0] = (299, rpp - 1)
+    extra[2, :3] = [(0, 0), (5, 3), (7, 9)]
+    def chk(t=table, e=extra, nn=n, mm=m):
+        return L.gsa_check_pages(ctypes.byref(p), t.ctypes.data, nn.ctypes.data, mm.ctypes.data, e.ctypes.data)
+    assert chk() == OK
+    bad = table.copy(); bad[0, 63] = 300                 # outside the pool
+    assert chk(t=bad) == INVALID and b"sequence 0" in L.gsa_last_error()
+    short = table.copy(); short[3, 0] = -1               # a page the sequence reads
+    assert chk(t=short) == INVALID
+    past = table.copy(); past[3, 5] = 999                # past the sequence's pages: not read
+    assert chk(t=past) == OK
+    e2 = extra.copy(); e2[1, 0] = (299, rpp)             # row outside the page
+    assert chk(e=e2) == INVALID and b"extra row" in L.gsa_last_error()
+    e3 = extra.copy(); e3[2, 1] = (-1, 0); e3[2, 2] = (5000, 0)   # after the list's end: not read
+    assert chk(e=e3) == OK
+    nn = n.copy(); nn[1] = 5000                          # longer than n_raw
+    assert chk(nn=nn) == INVALID
