@@ -63,6 +63,7 @@ sys.path.insert(0, ROOT)
 DECODE_METRIC = "GSA decode query-heads/s + achieved HBM GB/s (32K ctx, C=16, k=16, bf16)"
 PREFILL_METRIC = "GSA block-sparse prefill query-positions/s + MFMA utilisation (64K ctx, 4096 queries)"
 VARLEN_METRIC = "GSA variable-length decode query-heads/s + achieved HBM GB/s (4K-32K ctx, C=16, k=16, bf16)"
+PAGED_METRIC = "GSA paged decode query-heads/s + achieved HBM GB/s (4K-32K ctx, 16-chunk pages, C=16, k=16, bf16)"
 GIST_METRIC = "GSA cache build (append + gist-token attention) prompt tokens/s (64K prompt, C=16)"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
@@ -196,30 +197,110 @@ def decode_bytes(cfg, sel, gist_set="all"):
     return gist, unfold
 
 
+def host_cpu():
+    """(cores this process may run on, CPU model name)."""
+    cores = len(os.sched_getaffinity(0))
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def _oracle_decode_worker(job):
+    """One process of the CPU baseline's pool (spawned: it never touches the
+    GPU): the oracle's decode over units of a memory-mapped sample, round robin
+    from its own first unit, until its wall-clock budget is spent. Returns
+    (units done, seconds)."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    path, first, stride, budget_s, kw = job
+    data = np.load(path, mmap_mode="r")          # [units, 2, R, D] fp32 K and V, then q apart
+    qs = np.load(path + ".q.npy")                 # [units, g, D]
+    n, i, t0 = 0, first, time.perf_counter()
+    with threadpool_limits(1):
+        while time.perf_counter() - t0 < budget_s:
+            u = i % data.shape[0]
+            oracle.decode_unit(qs[u], np.asarray(data[u, 0]), np.asarray(data[u, 1]), **kw)
+            n += 1
+            i += stride
+    return n, time.perf_counter() - t0
+
+
 def cpu_baseline_decode(inp, cfg, budget_s: float, gist_set: str = "all"):
-    """The fp64 oracle (as it stands) on whole decode units, one thread."""
+    """The fp64 oracle (as it stands) on whole decode units: one thread, then a
+    pool of processes (one thread each) over the host's cores, up to 16."""
+    import concurrent.futures
+    import multiprocessing
+    import tempfile
     import oracle
     from threadpoolctl import threadpool_limits
     g = cfg.n_q_heads // cfg.n_kv_heads
     q = inp.q.float().cpu().numpy()
     units = [(b, j) for b in range(cfg.batch) for j in range(cfg.n_kv_heads)]
+    kw = dict(n_raw=cfg.n_raw, n_gist=cfg.M, chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail, gist_set=gist_set)
     t_total, n_qh, reps = 0.0, 0, 0
+    single_s = budget_s / 3
     with threadpool_limits(1):
-        while t_total < budget_s and reps < 1000:
+        while t_total < single_s and reps < 1000:
             for b, j in units:
                 K = inp.k_cache[b, j].float().cpu().numpy()   # host copy, not timed
                 V = inp.v_cache[b, j].float().cpu().numpy()
                 t0 = time.perf_counter()
-                oracle.decode_unit(q[b, j * g:(j + 1) * g], K, V, n_raw=cfg.n_raw, n_gist=cfg.M,
-                                   chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail, gist_set=gist_set)
+                oracle.decode_unit(q[b, j * g:(j + 1) * g], K, V, **kw)
                 t_total += time.perf_counter() - t0
                 n_qh += g
-                if t_total >= budget_s:
+                if t_total >= single_s:
                     break
             reps += 1
-    return {"value": n_qh / t_total, "unit": "query-heads/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_qh // g} (batch, kv-head) units of the same workload "
-                      f"({n_qh} query heads), fp64 numpy, 1 thread, {t_total:.1f} s"}
+    one = n_qh / t_total
+    cores, model = host_cpu()
+    workers = max(1, min(16, cores))
+    res = {"value": one, "unit": "query-heads/s", "cores": 1, "kind": "oracle",
+           "sample": f"{n_qh // g} (batch, kv-head) units of the same workload ({n_qh} query heads), "
+                     f"fp64 numpy, 1 thread, {t_total:.1f} s",
+           "host_cores": cores, "cpu_model": model, "single_thread_value": one}
+    if workers > 1:
+        # a sample of units written once to a memory-mapped file the workers share
+        pick = units[:: max(1, len(units) // (2 * workers))][: 2 * workers]
+        tmp = tempfile.mkdtemp(prefix="gsa_cpu_")
+        path = os.path.join(tmp, "units.npy")
+        K0 = inp.k_cache[0, 0]
+        arr = np.lib.format.open_memmap(path, mode="w+", dtype=np.float32,
+                                        shape=(len(pick), 2, K0.shape[0], K0.shape[1]))
+        for i, (b, j) in enumerate(pick):
+            arr[i, 0] = inp.k_cache[b, j].float().cpu().numpy()
+            arr[i, 1] = inp.v_cache[b, j].float().cpu().numpy()
+        arr.flush()
+        del arr
+        np.save(path + ".q.npy", np.stack([q[b, j * g:(j + 1) * g] for b, j in pick]))
+        pool_s = budget_s / 2
+        try:
+            ctx = multiprocessing.get_context("spawn")
+            with concurrent.futures.ProcessPoolExecutor(workers, mp_context=ctx) as ex:
+                list(ex.map(_oracle_decode_worker, [(path, w, workers, 0.2, kw) for w in range(workers)]))  # start-up
+                t0 = time.perf_counter()
+                done = list(ex.map(_oracle_decode_worker, [(path, w, workers, pool_s, kw) for w in range(workers)]))
+                wall = time.perf_counter() - t0
+        finally:
+            for f in (path, path + ".q.npy"):
+                try:
+                    os.remove(f)
+                except OSError:
+                    pass
+            os.rmdir(tmp)
+        n_units = sum(d[0] for d in done)
+        res.update({"value": n_units * g / wall, "cores": workers,
+                    "sample": f"{n_units} decode units of the same workload ({n_units * g} query heads) in "
+                              f"{wall:.1f} s over {workers} processes of 1 thread each (fp64 numpy), sampled "
+                              f"from {len(pick)} units; one thread alone: {one:.0f} query-heads/s over "
+                              f"{n_qh // g} units in {t_total:.1f} s"})
+    return res
 
 
 def run_decode_bench(args):
@@ -272,6 +353,11 @@ def run_decode_bench(args):
     sha = source_sha("gsa_decode.hip", "gsa_device.hpp")
     if unit_path and n_marks == 2:
         names, nbytes = ["unit_kernel"], [alg_b]
+    elif unit_path and args.gist_set != "all":
+        # the scoring launch reads the gists' K rows; the set (tail included)
+        # is read by the second launch
+        tail_b = cfg.batch * cfg.n_kv_heads * cfg.tail * 2 * cfg.head_dim * 2
+        names, nbytes = ["unit_kernel", "unit_unfold_kernel"], [gist_b - tail_b, unfold_b + tail_b]
     elif unit_path:
         names, nbytes = ["unit_kernel", "unit_unfold_kernel"], [gist_b, unfold_b]
     elif n_marks == 4:   # gist pass, per-split candidates, unfold
@@ -317,6 +403,20 @@ def run_decode_bench(args):
         "kernels": kernels,
         "source_sha": sha,
     }
+    # warm cache, labelled as such: the same cache copy every step (a working
+    # set under 256 MB then stays in the Infinity Cache)
+    def step_warm(i):
+        step(0)
+    warm_ms, warm_per = timed_steps(gsa, step_warm, args, n_marks)
+    res["warm_cache"] = {"ms_per_step": warm_ms, "call_ms_p50": float(np.percentile(warm_per.sum(axis=1), 50)),
+                         "note": "one cache copy reused every step (not the headline: the headline rotates "
+                                 f"{layers} copies so that each step reads from HBM)"}
+    res["latency_us"] = {"call_p50": 1e3 * kernels["whole_call"]["ms_p50"],
+                         "call_p10": 1e3 * kernels["whole_call"]["ms_p10"],
+                         "call_p90": 1e3 * kernels["whole_call"]["ms_p90"],
+                         "wall_per_step": 1e3 * ms_per_step,
+                         "note": "device time of one call (first kernel start to last kernel end), and the "
+                                 "wall clock per step including the host launch"}
     res["roofline"]["machine_stream_rates"] = hbm_stream_rates()
     if not args.no_cpu:
         log("[bench] timing the CPU oracle ...")
@@ -565,25 +665,53 @@ def run_varlen_bench(args):
     q, kc, vc, _, _ = gi.make_levels(B, Hq, Hkv, D, N, M, C, 2, 2, 2000 + 9, device=dev, values="gauss")
     sn = torch.tensor(n, dtype=torch.int32, device=dev)
     sm = torch.tensor(m, dtype=torch.int32, device=dev)
+    P = cfg.page_chunks
     p = gsa.decode_params(B, Hq, Hkv, D, N, M, C, k, T, row_capacity=cap)
     gsa.check_seq_lens(p, n, m)
-    ws = gsa.new_workspace(gsa.decode_workspace_size(p), dev)
+    if P:
+        # the caches in shuffled pages of P chunk slots; the dense copies go
+        kp, vp, table_h = gi.to_pages(kc, vc, [a + b for a, b in zip(n, m)], P, C, 2000 + 10)
+        del kc, vc
+        torch.cuda.empty_cache()
+        pp = gsa.paged_params(p, P, table_h.shape[1], kp.shape[0], 0)
+        pp.base.row_capacity = 0
+        gsa.check_pages(pp, table_h, n, m)
+        table = torch.from_numpy(table_h).to(dev)
+        ws = gsa.new_workspace(gsa.paged_workspace_size(pp), dev)
+    else:
+        ws = gsa.new_workspace(gsa.decode_workspace_size(p), dev)
     out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
     sel = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
-        gsa.gsa_decode_varlen(q, kc, vc, seq_n_raw=sn, seq_n_gist=sm, n_raw=N, n_gist=M, chunk=C, topk=k, tail=T,
-                              out=out, lse=lse, sel_idx=sel, workspace=ws, stream=stream)
+        if P:
+            gsa.gsa_decode_paged(q, kp, vp, block_table=table, seq_n_raw=sn, seq_n_gist=sm, n_raw=N, n_gist=M,
+                                 chunk=C, topk=k, tail=T, page_chunks=P, out=out, lse=lse, sel_idx=sel,
+                                 workspace=ws, stream=stream)
+        else:
+            gsa.gsa_decode_varlen(q, kc, vc, seq_n_raw=sn, seq_n_gist=sm, n_raw=N, n_gist=M, chunk=C, topk=k,
+                                  tail=T, out=out, lse=lse, sel_idx=sel, workspace=ws, stream=stream)
+
+    def unit_rows(b, j):
+        """Host fp32 copies of (q, K, V) of one unit, K/V gathered through the
+        pages for a paged cache (the oracle's page gather)."""
+        R = n[b] + m[b]
+        qh = q[b, j * g:(j + 1) * g].float().cpu().numpy()
+        if P:
+            pages = [int(x) for x in table_h[b]]
+            K = oracle.gather_pages(kp[:, j].float().cpu().numpy(), pages, page_chunks=P, chunk=C, n_rows=R)
+            V = oracle.gather_pages(vp[:, j].float().cpu().numpy(), pages, page_chunks=P, chunk=C, n_rows=R)
+            return qh, K, V
+        return qh, kc[b, j, :R].float().cpu().numpy(), vc[b, j, :R].float().cpu().numpy()
 
     step(0)
     torch.cuda.synchronize()
     g = Hq // Hkv
     for b, j in ((int(np.argmin(n)), 0), (int(np.argmax(n)), Hkv - 1)):
-        R = n[b] + m[b]
-        r = oracle.decode_unit(q[b, j * g:(j + 1) * g].float().cpu().numpy(), kc[b, j, :R].float().cpu().numpy(),
-                               vc[b, j, :R].float().cpu().numpy(), n_raw=n[b], n_gist=m[b], chunk=C, topk=k, tail=T)
+        qh, Kh, Vh = unit_rows(b, j)
+        r = oracle.decode_unit(qh, Kh, Vh, n_raw=n[b], n_gist=m[b], chunk=C, topk=k, tail=T)
         got = out[b, j * g:(j + 1) * g].double().cpu().numpy()
         rms = float(np.sqrt(np.mean(r["out"] ** 2)))
         if not np.array_equal(sel[b, j].cpu().numpy(), r["sel"]) or float(np.abs(got - r["out"]).max()) > 2e-3 * rms:
@@ -597,19 +725,20 @@ def run_varlen_bench(args):
     achieved = nb / (k_ms / 1e3) / 1e9
     mean_n = float(np.mean(n))
     res = {
-        "metric": VARLEN_METRIC,
+        "metric": PAGED_METRIC if P else VARLEN_METRIC,
         "value": B * Hq / (ms_per_step / 1e3),
         "unit": "query-heads/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded Gaussian q/K/V, seeded lengths)",
         "config": {"workload": f"{cfg.name}: decode step of {B} sequences of {min(n)}..{N} tokens (mean "
-                               f"{mean_n:.0f}), Hq={Hq}, Hkv={Hkv}, D={D}, C={C}, k={k}, T={T}, bf16 cache",
+                               f"{mean_n:.0f}), Hq={Hq}, Hkv={Hkv}, D={D}, C={C}, k={k}, T={T}, bf16 cache"
+                               + (f" in shuffled pages of {P} chunk slots ({P * (C + 1)} rows)" if P else ""),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(f"unit_kernel/{cfg.name}", source_sha("gsa_decode.hip", "gsa_device.hpp")),
-                     "kernel": "unit_kernel (VARLEN)",
+                     "kernel": "unit_kernel (VARLEN, PAGED)" if P else "unit_kernel (VARLEN)",
                      "alg_bytes_per_launch": nb, "launch_ms_mean": k_ms,
                      "longest_share": float(max(n)) / mean_n},
         "kernels": {"unit_kernel": {"ms": k_ms, "alg_bytes": nb, "GB_s": achieved, **pcts(per[:, 0])}},
@@ -624,9 +753,7 @@ def run_varlen_bench(args):
             while t_total < args.cpu_seconds and cnt < 100000:
                 b, j = int(rng.integers(B)), int(rng.integers(Hkv))
                 if (b, j) not in host:
-                    R = n[b] + m[b]
-                    host[(b, j)] = (q[b, j * g:(j + 1) * g].float().cpu().numpy(), kc[b, j, :R].float().cpu().numpy(),
-                                    vc[b, j, :R].float().cpu().numpy())
+                    host[(b, j)] = unit_rows(b, j)
                 qh, Kh, Vh = host[(b, j)]
                 t0 = time.perf_counter()
                 oracle.decode_unit(qh, Kh, Vh, n_raw=n[b], n_gist=m[b], chunk=C, topk=k, tail=T)

@@ -1874,6 +1874,33 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     const unsigned pos = m * (unsigned)C + jj;
     return pos >= tail0 ? -1 : (int)(pos + m);
   };
+  // Paged caches: byte offset of item i (whose row_of is row) from the
+  // unit's kv-head base in page 0, from its chunk m and slot j, so that no
+  // row is divided by C + 1; masked items read page 0, row 0.
+  auto paged_item = [&](int i, int row) -> int64_t {
+    if constexpr (PAGED) {
+      if (row < 0) return 0;
+      if (row >= kExtraRow) return paged_off(a, *pl, row);
+      unsigned m, j;
+      if (KIND == kUKGists && i < M) {
+        m = (unsigned)i;
+        j = (unsigned)C;
+      } else if (KIND == kUKGists) {   // tail position
+        const unsigned pos = tail0 + (unsigned)(i - M);
+        m = min(pos / (unsigned)C, (unsigned)M);
+        j = pos - m * (unsigned)C;
+      } else {                         // chosen chunk's raw row
+        const unsigned ci = (unsigned)i / (unsigned)C;
+        m = min((unsigned)lds_sel[ci], (unsigned)(M - 1));
+        j = (unsigned)i - ci * (unsigned)C;
+      }
+      const unsigned pi = m >> a.pg_lp;
+      const unsigned slot = (m - (pi << a.pg_lp)) * (unsigned)(C + 1) + j;
+      return (int64_t)pl->pages[pi] * a.pg_bytes + (int64_t)slot * 256;
+    } else {
+      return 0;
+    }
+  };
   // the unit's level-2 arrays (K2b, V2b), as offsets from the level-1 bases
   const int64_t k2off = KIND == kUKL2 ? K2b - Kb : 0;
   const int64_t v2off = KIND == kUKL2 ? V2b - Vb : 0;
@@ -1901,7 +1928,7 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
       const int r = 4 * u + (lane >> 4);
       const int row = row_of(i0 + b * kRows + r);
       int64_t koffr, voffr;
-      if constexpr (PAGED) koffr = paged_off(a, *pl, row);
+      if constexpr (PAGED) koffr = paged_item(i0 + b * kRows + r, row);
       else koffr = (int64_t)(row >= 0 ? row : 0) * 256;
       voffr = koffr;
       if (KIND == kUKL2 && row <= -2) {
@@ -2269,6 +2296,27 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
     }
     return;
   }
+  if constexpr (SETS && SPLIT) {
+    // selection-rule variants, several workgroups per unit: each scores its
+    // share of the gists (K rows only, no attention) and hands on candidates
+    // (k <= 16) or its scores; unit_unfold_kernel<SETS> selects and attends
+    // the set (chosen raw rows, their gists if the set keeps them, the tail)
+    const int perg = (M + S - 1) / S;
+    const int g0 = min(M, split * perg), g1 = min(M, g0 + perg);
+    const int pw = (g1 - g0 + kUW - 1) / kUW;
+    unit_stream<kUKScore>(Kb, Vb, min(g1, g0 + w * pw), min(g1, g0 + (w + 1) * pw), a, qf, st, ring, L.scores,
+                          L.sel, g0);
+    float* gs = a.scores + (size_t)unit * a.score_stride;
+    __syncthreads();   // every score of the share is in LDS
+    if (a.k > kCandMaxK) {
+      for (int i = g0 + tid; i < g1; i += kUW * 64) st_coh(gs + i, L.scores[i - g0]);
+    } else if (a.k > 0) {
+      const Cands c = cands_of(a, (int)(gridDim.x / S), a.k);
+      unit_cands(L, g1 - g0, a.k, g0, gs + g0, c.s + (size_t)unit * c.stride, c.id + (size_t)unit * c.stride, S,
+                 split, unit);
+    }
+    return;
+  }
   if constexpr (SETS) {
     // selection-rule variants (one workgroup per unit): the gists' K rows for
     // the scores only; then the chosen chunks' raw rows, their gists if the
@@ -2337,9 +2385,13 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
 // launch wrote (every workgroup of the unit makes the same one), streams
 // share p of the chosen chunks' raw rows, and hands its partial state on; the
 // unit's last workgroup merges the S stream and S2 unfold partials.
-template <int G, bool VARLEN = false, bool PAGED = false>
+// SETS: the selection-rule variants, whose stream launch only scored the
+// gists: the workgroups attend the set (chosen raw rows, their gists if the
+// set keeps them, the tail) and the last merges their S2 partials alone.
+template <int G, bool VARLEN = false, bool PAGED = false, bool SETS = false>
 __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   static_assert(!PAGED || VARLEN, "paged caches: per-sequence lengths");
+  static_assert(!SETS || (!VARLEN && !PAGED), "selection-rule variants: uniform lengths");
   __shared__ __attribute__((aligned(16))) std::conditional_t<PAGED, PagedLds, UnitLds> L;
   UnitArgs a = args;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2379,17 +2431,24 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   } else {
     select_cands(cands_of(a, (int)(gridDim.x / S2), a.k), a.S, unit, a.k, L.sel, L);
   }
-  const int items = a.k * a.C;
+  // SETS: raw rows of the chosen chunks, their gists (rule 1), then the tail
+  const int items = a.k * a.C + (SETS ? (a.gist_set == 1 ? a.k : 0) + a.T : 0);
   const int perp = (items + S2 - 1) / S2;
   const int p0 = min(items, part * perp), p1 = min(items, p0 + perp);
   const int per2 = (p1 - p0 + kUW - 1) / kUW;
-  unit_stream<kUKUnfold, PAGED>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st,
-                                L.u.ring[w][0], L.scores, L.sel, 0, nullptr, nullptr, pl);
+  if constexpr (SETS)
+    unit_stream<kUKSet>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st, L.u.ring[w][0],
+                        L.scores, L.sel);
+  else
+    unit_stream<kUKUnfold, PAGED>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st,
+                                  L.u.ring[w][0], L.scores, L.sel, 0, nullptr, nullptr, pl);
   float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
   unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)(a.S + part) * a.part_stride);
   if (!arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)S2, &L.s_old)) return;
-  merge_unit<128, G>(part_u, a.S + S2, (uint32_t)a.part_stride, a.out + (size_t)unit * G * 128,
-                     a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
+  // the stream launch's partials, then these; SETS: these alone
+  const int m0 = SETS ? a.S : 0;
+  merge_unit<128, G>(part_u + (size_t)m0 * a.part_stride, a.S + S2 - m0, (uint32_t)a.part_stride,
+                     a.out + (size_t)unit * G * 128, a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
   if (a.sel)
     for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
 }
@@ -2677,8 +2736,19 @@ gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const 
       prof_launch((unit_unfold_kernel<G, true, true>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st, u);
     return launch_status("gsa_decode_paged launch");
   }
-  if (pl.gist_set != GSA_GISTS_ALL)
-    prof_launch((unit_kernel<G, kHierNone, true, false, false>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+  if (pl.gist_set != GSA_GISTS_ALL) {
+    if (pl.unit_S == 1) {
+      prof_launch((unit_kernel<G, kHierNone, true, false, false>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+    } else {
+      // the gists' scores (none needed with k = 0), then the set
+      if (pl.k > 0)
+        prof_launch((unit_kernel<G, kHierNone, true, false, true>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0,
+                    st, u);
+      prof_launch((unit_unfold_kernel<G, false, false, true>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st,
+                  u);
+    }
+    return launch_status("gsa_decode launch");
+  }
   else if (varlen && pl.unit_S == 1)
     prof_launch((unit_kernel<G, kHierNone, false, true, false>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
   else if (varlen)

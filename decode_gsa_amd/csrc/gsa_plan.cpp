@@ -177,14 +177,20 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   d.NP = d.S + d.S2;
   d.score_stride = d.k > 0 ? (d.M + 63) / 64 * 64 : 0;
   d.unit_S = unit_splits(d);
-  if (d.gist_set != GSA_GISTS_ALL && d.unit_S != 1)
+  if (d.gist_set != GSA_GISTS_ALL && d.unit_S == 0)
     return fail(GSA_ERR_UNSUPPORTED,
-                "gist_set=%d runs on the one-workgroup-per-unit launch only (bf16, D = 128, topk <= 64, "
-                ">= 256 units, <= 4096 gists)", d.gist_set);
+                "gist_set=%d runs on the bf16, head_dim 128, topk <= 64 launches (n_gist <= 16384 when topk > 0)",
+                d.gist_set);
   d.unit_S2 = 0;
   if (d.unit_S > 1) {
     // the unfold launch: the stream's workgroup count, at least 64 rows each
-    d.unit_S2 = d.k > 0 ? (int32_t)std::min<int64_t>(d.unit_S, ceil_div(items, 64)) : 0;
+    // (selection-rule variants: its items are the whole set)
+    const int64_t set_items = d.gist_set == GSA_GISTS_ALL
+                                  ? items
+                                  : items + (d.gist_set == GSA_GISTS_SELECTED ? d.k : 0) + d.T;
+    d.unit_S2 = set_items > 0 && (d.k > 0 || d.gist_set != GSA_GISTS_ALL)
+                    ? (int32_t)std::max<int64_t>(1, std::min<int64_t>(d.unit_S, ceil_div(set_items, 64)))
+                    : 0;
     if (d.NP < d.unit_S + d.unit_S2) d.NP = d.unit_S + d.unit_S2;   // stream + unfold partials
   }
   size_t off = 0;
@@ -555,6 +561,7 @@ gsa_status_t plan_append(const gsa_append_params* p, AppendPlan* o) {
 }
 
 int32_t decode_launches(const DecodePlan& d) {
+  if (d.unit_S > 1 && d.gist_set != GSA_GISTS_ALL) return (d.k > 0 ? 1 : 0) + 1;
   if (d.unit_S > 0) return 1 + (d.unit_S2 > 0 ? 1 : 0);
   return 1 + (d.cand_stride > 0 ? 1 : 0) + (d.k > 0 ? 1 : 0);
 }

@@ -125,6 +125,7 @@ class VarlenConfig:
     chunk: int
     topk: int
     tail: int
+    page_chunks: int = 0   # > 0: the caches live in shuffled pages of this many chunk slots
 
 
 @dataclasses.dataclass(frozen=True)
@@ -167,6 +168,8 @@ CONFIGS = {
     "gist_64k": GistConfig("gist_64k", 32, 8, 128, "bf16", 65536, 16),
     # the batched GQA decode step with sequence lengths uniform in [4K, 32K]
     "varlen_32k": VarlenConfig("varlen_32k", 32, 32, 8, 128, "bf16", 4096, 32768, 16, 16, 64),
+    # the same batch with its caches in shuffled pages of 16 chunk slots (272 rows)
+    "paged_32k": VarlenConfig("paged_32k", 32, 32, 8, 128, "bf16", 4096, 32768, 16, 16, 64, page_chunks=16),
 }
 
 

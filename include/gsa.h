@@ -84,10 +84,11 @@ typedef struct {
                           (1, the chosen chunks' gists: SG+SR) or
                           GSA_GISTS_NONE (2, raw tokens only: SR-only).
                           1 and 2 need k > 0 or T > 0 (a non-empty set) and
-                          run on the one-workgroup-per-unit launch only (bf16,
-                          D = 128, k <= 64, >= 256 units, <= 4096 gists);
-                          other shapes return GSA_ERR_UNSUPPORTED.
-                          gsa_decode_hier requires 0. */
+                          run on the bf16, D = 128, k <= 64 launches
+                          (n_gist <= 16384 when k > 0); other shapes return
+                          GSA_ERR_UNSUPPORTED. gsa_decode_varlen, _paged,
+                          _hier and _levels require 0 (they attend every
+                          gist of every level). */
   int64_t row_capacity; /* rows allocated per (sequence, kv-head) in the
                           caches, the stride between their [R, D] blocks:
                           0 means exactly R = N + M; else it must be
@@ -464,7 +465,9 @@ gsa_status_t gsa_profile_marks(int32_t* n);
  *     bf16, D = 128, topk <= 64 path
  *     (n_gist <= 16384 when topk > 0): 1 when each (batch, kv-head) unit
  *     takes one workgroup (B*Hkv >= 256 and n_gist <= 4096) or topk = 0,
- *     else 2 (a stream launch, then a select-unfold-merge launch);
+ *     else 2 (a stream launch, then a select-unfold-merge launch); with
+ *     gist_set 1 or 2 and several workgroups per unit: a scoring launch
+ *     (none when topk = 0), then the launch that selects and attends;
  *     other shapes: 1 when topk = 0, else 2 or 3 (a gist pass, a pass that
  *     takes each split's top-k when there are many gists per unit, an
  *     unfold pass);

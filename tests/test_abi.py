@@ -130,7 +130,9 @@ def ws_size(L, p):
     ({"scale": float("nan")}, INVALID),
     ({"gist_set": 3}, INVALID),
     ({"gist_set": -1}, INVALID),
-    ({"gist_set": 1}, UNSUPPORTED),           # 4 units: not the one-workgroup-per-unit launch
+    ({"gist_set": 1}, OK),                    # 4 units: several workgroups per unit
+    ({"gist_set": 1, "head_dim": 64}, UNSUPPORTED),   # the split path (D = 64)
+    ({"gist_set": 2, "topk": 65, "n_raw": 16 * 128, "n_gist": 128}, UNSUPPORTED),   # k > 64
     ({"gist_set": 2, "batch": 128}, OK),      # 256 units
     ({"gist_set": 1, "batch": 128, "topk": 0, "tail": 0}, INVALID),   # nothing to attend
     ({"gist_set": 2, "batch": 128, "dtype": gsa.GSA_F32}, UNSUPPORTED),

@@ -1,12 +1,14 @@
 """GPU parity of gsa_decode's selection-rule variants (slide deck, slide 17
 'Selective Rules Comparison'): the attention set keeps the selected chunks'
 gists with their raw tokens (gist_set "selected", SG+SR) or the selected raw
-tokens alone ("none", SR-only), plus the tail. They run on the
-one-workgroup-per-unit launch (256 or more units, at most 4096 gists):
-gist keys are read for the scores only, then the chosen chunks' rows, their
-gists and the tail are attended. Checked against the fp64 oracle with the
-same rule: bit-exact selections, outputs and lse within the stated
-tolerance (tests/gpu_util.py).
+tokens alone ("none", SR-only), plus the tail. They run on the bf16,
+head_dim 128, topk <= 64 launches: with one workgroup per unit (256 or more
+units, at most 4096 gists) the gist keys are read for the scores only, then
+the chosen chunks' rows, their gists and the tail are attended; with several
+workgroups per unit (fewer units or more gists) a scoring launch hands on
+candidates or scores and a second launch selects and attends the set.
+Checked against the fp64 oracle with the same rule: bit-exact selections,
+outputs and lse within the stated tolerance (tests/gpu_util.py).
 """
 import dataclasses
 
@@ -45,6 +47,13 @@ CASES = [
     (cfg_of("gqa_32k", n_raw=2048, topk=0, plant="none"), 64),              # k = 0: the tail alone
     (cfg_of("gqa_32k", n_raw=1024, topk=64, plant="none"), 64),             # every chunk selected
     (cfg_of("gqa_32k", n_raw=65536, tail=300), 12),                         # 4096 gists
+    # several workgroups per unit
+    (cfg_of("c8_131k", n_raw=32768), 24),                                   # 64 units x 4, C = 8, k = 64
+    (cfg_of("c32_131k", n_raw=65536), 24),                                  # 64 units, C = 32, k = 16
+    (cfg_of("gqa_32k", batch=2, n_raw=8192, tail=70), None),                # 16 units, candidates
+    (cfg_of("gqa_32k", batch=1, n_kv_heads=1, n_q_heads=4, n_raw=16 * 5000, tail=64), None),   # 5000 gists
+    (cfg_of("gqa_32k", batch=2, n_raw=4096, topk=0, plant="none"), None),   # k = 0: the tail alone
+    (cfg_of("gqa_32k", batch=1, n_kv_heads=2, n_q_heads=8, n_raw=1024, topk=64, plant="none"), None),   # k = M
 ]
 
 
@@ -78,9 +87,9 @@ def test_decode_gist_set_ties_and_tail_overlap(gsa, gist_set):
 
 
 def test_decode_gist_set_rejections(gsa):
-    """Shapes off the one-workgroup-per-unit launch, an empty set and the
-    two-level entry point are refused before any launch."""
-    cfg = cfg_of("gqa_32k", batch=2, n_raw=4096)        # 16 units: several workgroups per unit
+    """Shapes off the bf16, head_dim 128, topk <= 64 launches and an empty set
+    are refused before any launch."""
+    cfg = cfg_of("gqa_32k", batch=2, n_raw=4096, head_dim=64)   # D = 64: the split path
     inp = gi.make_decode(cfg, 5200, device="cuda")
     with pytest.raises(gsa.GsaError) as e:
         gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=16, tail=64, gist_set="selected")
