@@ -1061,6 +1061,52 @@ def hbm_stream_rates(reps: int = 8) -> dict:
     return {"torch_copy_1GiB_GB_s": gbs}
 
 
+def run_phase_stamps(args):
+    """Phase edges of the one-workgroup-per-unit decode kernel, read from the
+    diagnostic build libgsa_stamps.so (`python -m decode_gsa_amd.build
+    --stamps`): per workgroup, thread 0 stamps the chip's 100 MHz clock at the
+    start, after its wave's gists + tail, after the selection, after the
+    unfold and after the output. Prints one JSON line: medians and maxima over
+    the workgroups of each phase (us), averaged over the calls, and the
+    per-XCD median end of the streaming phase (workgroup i runs on XCD i mod 8)."""
+    import torch
+    import decode_gsa_amd as gsa
+    import gsa_inputs as gi
+    from decode_gsa_amd import build as gb
+    if not os.path.exists(gb.STAMPS_LIB):
+        raise SystemExit("build the diagnostic library first: python -m decode_gsa_amd.build --stamps")
+    gsa.LIB_PATH = gb.STAMPS_LIB
+    L = gsa.lib()
+    L.gsa_debug_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    L.gsa_debug_phase_stamps.restype = ctypes.c_int
+    cfg = gi.CONFIGS[args.config]
+    dev = torch.device("cuda", 0)
+    inp = gi.make_decode(cfg, 1000 + 2, device=dev)
+    units = cfg.batch * cfg.n_kv_heads
+    layers = [(inp.k_cache, inp.v_cache)] + [(inp.k_cache.clone(), inp.v_cache.clone()) for _ in range(4)]
+    buf = np.zeros(units * 8, dtype=np.uint64)
+    rows = []
+    for rep in range(args.warmup + args.steps):
+        k, v = layers[rep % len(layers)]
+        out, lse, sel = gsa.gsa_decode(inp.q, k, v, chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail, n_gist=cfg.M)
+        torch.cuda.synchronize()
+        if gsa.gsa_profile_marks() != 2:
+            raise SystemExit("phase stamps cover the one-workgroup-per-unit launch only")
+        if L.gsa_debug_phase_stamps(buf.ctypes.data, buf.nbytes) != 0:
+            raise SystemExit("reading the stamps failed")
+        if rep >= args.warmup:
+            rows.append(buf.reshape(units, 8)[:, :5].astype(np.int64).copy())
+    res = {"metric": "decode kernel phase edges (us, 100 MHz clock)", "config": cfg.name, "calls": len(rows)}
+    phases = {"stream (gists + tail)": (0, 1), "selection": (1, 2), "unfold": (2, 3), "merge + output": (3, 4)}
+    for name, (a, b) in phases.items():
+        d = np.array([(r[:, b] - r[:, a]) / 100.0 for r in rows])
+        res[name] = {"median": float(np.median(d)), "max_mean": float(d.max(axis=1).mean())}
+    res["first start to last end"] = float(np.mean([(r[:, 4].max() - r[:, 0].min()) / 100.0 for r in rows]))
+    res["stream end, median per XCD"] = [
+        float(np.mean([np.median((r[x::8, 1] - r[:, 0].min()) / 100.0) for r in rows])) for x in range(8)]
+    print(json.dumps(res), flush=True)
+
+
 def run_copy_calibration():
     """A plain device copy of a known size (for scaling FETCH_SIZE / WRITE_SIZE
     counters: run under rocprofv3 --pmc and compare with the bytes moved)."""
@@ -1084,6 +1130,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="phase edges of the decode kernel (diagnostic library libgsa_stamps.so)")
     ap.add_argument("--scaling", action="store_true", help="decode time and bytes per step vs context length")
     ap.add_argument("--scaling-max", type=int, default=1 << 24)
     ap.add_argument("--scaling-min", type=int, default=0)
@@ -1101,6 +1149,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         run_copy_calibration()
+        return
+    if args.phase_stamps:
+        run_phase_stamps(args)
         return
     if args.scaling:
         run_scaling(args)

@@ -27,17 +27,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source under csrc/ into decode_gsa_amd/libgsa.so; returns its path."""
+STAMPS_LIB = os.path.join(PKG, "libgsa_stamps.so")
+
+
+def build(verbose: bool = False, stamps: bool = False) -> str:
+    """Compile every source under csrc/ into decode_gsa_amd/libgsa.so; returns
+    its path. stamps=True builds the diagnostic libgsa_stamps.so instead (the
+    decode kernel records its phase edges; bench.py --phase-stamps reads
+    them)."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    out_dir = os.path.join(ROOT, "_build")
+    out_dir = os.path.join(ROOT, "_build", "stamps" if stamps else "")
     os.makedirs(out_dir, exist_ok=True)
     objs = []
     procs = []
+    extra = ["-DGSA_PHASE_STAMPS"] if stamps else []
     for s in srcs:
         o = os.path.join(out_dir, os.path.basename(s) + ".o")
         lang = ["-x", "hip"] if s.endswith(".hip") else []
-        cmd = [hipcc()] + HIP_FLAGS + ["-I", INCLUDE, "-I", CSRC] + lang + ["-c", s, "-o", o]
+        cmd = [hipcc()] + HIP_FLAGS + extra + ["-I", INCLUDE, "-I", CSRC] + lang + ["-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((s, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -54,14 +61,15 @@ def build(verbose: bool = False) -> str:
         for s, m in failed:
             sys.stderr.write(f"--- {s}\n{m}\n")
         raise RuntimeError("libgsa build failed: " + ", ".join(os.path.basename(s) for s, _ in failed))
-    tmp = LIB + ".tmp"
+    lib = STAMPS_LIB if stamps else LIB
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, stamps="--stamps" in sys.argv))

@@ -56,6 +56,29 @@
 #include "gsa_plan.hpp"
 #include "gsa_profile.hpp"
 
+// Phase stamps: a diagnostic build of the library (-DGSA_PHASE_STAMPS,
+// libgsa_stamps.so; the product build has none of it). Thread 0 of every
+// workgroup of the one-workgroup-per-unit decode kernel records the chip's
+// 100 MHz real-time counter at the edges of its phases: 0 start, 1 its wave's
+// gists + tail streamed, 2 selection made, 3 chosen rows unfolded, 4 output
+// written. gsa_debug_phase_stamps copies [workgroups][kStampSlots] out.
+#ifdef GSA_PHASE_STAMPS
+constexpr int kStampSlots = 8;
+constexpr int kStampWGs = 65536;
+__device__ unsigned long long g_phase_stamps[kStampWGs * kStampSlots];
+#define GSA_STAMP(slot)                                                                               \
+  do {                                                                                                \
+    if (threadIdx.x == 0 && blockIdx.x < kStampWGs)                                                   \
+      g_phase_stamps[(size_t)blockIdx.x * kStampSlots + (slot)] = __builtin_amdgcn_s_memrealtime();   \
+  } while (0)
+extern "C" int gsa_debug_phase_stamps(void* host, size_t bytes) {
+  if (bytes > sizeof(g_phase_stamps)) bytes = sizeof(g_phase_stamps);
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_stamps), bytes, 0, hipMemcpyDeviceToHost);
+}
+#else
+#define GSA_STAMP(slot) ((void)0)
+#endif
+
 namespace gsa {
 namespace {
 
@@ -1716,6 +1739,7 @@ struct UnitArgs {
   const int32_t* pg_extra;
   int64_t pg_count;       // pages in the pool
   int64_t pg_bytes;       // bytes between consecutive pages (Hkv rpp 256)
+  int64_t pg_head_bytes;  // bytes between a page's kv-heads (rpp 256)
   int32_t pg_max, pg_lp, pg_rpp, pg_max_extra, Hkv;
 };
 
@@ -1786,18 +1810,19 @@ __device__ __forceinline__ void stage_pages(const UnitArgs& a, int unit, PagedLd
   __syncthreads();
 }
 
-// Byte offset (from the unit's kv-head base in page 0) of a logical row, an
-// extra row (kExtraRow + e) or a masked item (-1: page 0, row 0).
+// The staged tables read as LDS (ds_read): through a generic pointer the
+// compiler would emit flat loads, which count against the vector-memory
+// counter the row streams wait on and would stall the loads in flight.
+typedef const __attribute__((address_space(3))) int32_t* lds_i32p;
+__device__ __forceinline__ int32_t lds_at(const int32_t* p, unsigned i) {
+  return reinterpret_cast<lds_i32p>(reinterpret_cast<uintptr_t>(p) & 0xffffffffu)[i];
+}
+
+// Byte offset (from the unit's kv-head base in page 0) of an extra row
+// (kExtraRow + e).
 __device__ __forceinline__ int64_t paged_off(const UnitArgs& a, const PagedLds& L, int row) {
-  if (row < 0) return 0;
-  if (row >= kExtraRow) {
-    const int e = row - kExtraRow;
-    return (int64_t)L.extra[2 * e] * a.pg_bytes + (int64_t)L.extra[2 * e + 1] * 256;
-  }
-  const unsigned m = (unsigned)row / (unsigned)(a.C + 1);
-  const unsigned pi = m >> a.pg_lp;
-  const unsigned r = (unsigned)row - (pi << a.pg_lp) * (unsigned)(a.C + 1);
-  return (int64_t)L.pages[pi] * a.pg_bytes + (int64_t)r * 256;
+  const unsigned e = (unsigned)(row - kExtraRow);
+  return (int64_t)lds_at(L.extra, 2 * e) * a.pg_bytes + (int64_t)lds_at(L.extra, 2 * e + 1) * 256;
 }
 
 // One wave's running softmax state: lane (h, j) holds head h's max and its
@@ -1874,14 +1899,13 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     const unsigned pos = m * (unsigned)C + jj;
     return pos >= tail0 ? -1 : (int)(pos + m);
   };
-  // Paged caches: byte offset of item i (whose row_of is row) from the
-  // unit's kv-head base in page 0, from its chunk m and slot j, so that no
-  // row is divided by C + 1; masked items read page 0, row 0.
-  auto paged_item = [&](int i, int row) -> int64_t {
-    if constexpr (PAGED) {
-      if (row < 0) return 0;
-      if (row >= kExtraRow) return paged_off(a, *pl, row);
-      unsigned m, j;
+  // Paged caches: page-table index and row within the page of item i
+  // (whose row_of is row), from its chunk m and slot j, so that no row is
+  // divided by C + 1 (masked and extra items: index 0, the address comes
+  // from elsewhere).
+  auto paged_slot = [&](int i, int row, unsigned& pi, unsigned& slot) {
+    unsigned m = 0, j = 0;
+    if (row >= 0 && row < kExtraRow) {
       if (KIND == kUKGists && i < M) {
         m = (unsigned)i;
         j = (unsigned)C;
@@ -1894,12 +1918,9 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
         m = min((unsigned)lds_sel[ci], (unsigned)(M - 1));
         j = (unsigned)i - ci * (unsigned)C;
       }
-      const unsigned pi = m >> a.pg_lp;
-      const unsigned slot = (m - (pi << a.pg_lp)) * (unsigned)(C + 1) + j;
-      return (int64_t)pl->pages[pi] * a.pg_bytes + (int64_t)slot * 256;
-    } else {
-      return 0;
     }
+    pi = PAGED ? m >> a.pg_lp : 0;
+    slot = PAGED ? (m - (pi << a.pg_lp)) * (unsigned)(C + 1) + j : 0;
   };
   // the unit's level-2 arrays (K2b, V2b), as offsets from the level-1 bases
   const int64_t k2off = KIND == kUKL2 ? K2b - Kb : 0;
@@ -1923,13 +1944,37 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
       }
       return;
     }
+    if constexpr (PAGED) {
+      // the four rows' chunk slots first, then their four page-table reads
+      // together (one LDS wait), then the loads
+      int32_t rw[4];
+      unsigned pi[4], slot[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + b * kRows + 4 * u + (lane >> 4);
+        rw[u] = row_of(i);
+        paged_slot(i, rw[u], pi[u], slot[u]);
+      }
+      int32_t pg[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pg[u] = lds_at(pl->pages, pi[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * u + (lane >> 4);
+        const int64_t off = rw[u] < 0 ? 0
+                            : rw[u] >= kExtraRow ? paged_off(a, *pl, rw[u])
+                                                 : (int64_t)pg[u] * a.pg_bytes + (int64_t)slot[u] * 256;
+        __builtin_amdgcn_global_load_lds(Kb + off + uk_slot(sl, r) * 16, kd + u * 1024, 16, 0, kUNt);
+        __builtin_amdgcn_global_load_lds(Vb + off + uv_slot(sl, r) * 16, vd + u * 1024, 16, 0, kUNt);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int r = 4 * u + (lane >> 4);
       const int row = row_of(i0 + b * kRows + r);
       int64_t koffr, voffr;
-      if constexpr (PAGED) koffr = paged_item(i0 + b * kRows + r, row);
-      else koffr = (int64_t)(row >= 0 ? row : 0) * 256;
+      koffr = (int64_t)(row >= 0 ? row : 0) * 256;
       voffr = koffr;
       if (KIND == kUKL2 && row <= -2) {
         koffr = k2off + (int64_t)(-2 - row) * 256;
@@ -2243,6 +2288,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
   const int hq = lane & 15, jg = lane >> 4;
   const int S = SPLIT ? a.S : 1;
   const int unit = blockIdx.x / S, split = blockIdx.x - unit * S;
+  if constexpr (!SPLIT && !HIER && !SETS) GSA_STAMP(0);
   if constexpr (VARLEN) unit_lengths(args.seq, unit, args.N, args.M, args.C, args.T, &a.N, &a.M);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
   const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
@@ -2252,8 +2298,8 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
     stage_pages(a, unit, L);
     pl = &L;
     n_extra = L.n_extra;
-    Kb = reinterpret_cast<const char*>(a.K) + (size_t)(unit % a.Hkv) * a.pg_rpp * 256;
-    Vb = reinterpret_cast<const char*>(a.V) + (size_t)(unit % a.Hkv) * a.pg_rpp * 256;
+    Kb = reinterpret_cast<const char*>(a.K) + (size_t)(unit % a.Hkv) * a.pg_head_bytes;
+    Vb = reinterpret_cast<const char*>(a.V) + (size_t)(unit % a.Hkv) * a.pg_head_bytes;
   }
   // query fragments: lane (h, j) holds q_h[32 ks + 8 j .. +8], zero past g heads
   bf16x8u qf[4];
@@ -2344,16 +2390,20 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
   const int items = a.k * a.C;
   const int per2 = (items + kUW - 1) / kUW;
   if constexpr (!SPLIT) {
+    GSA_STAMP(1);
     if (a.k > 0) {
       __syncthreads();   // every group score is in LDS, every ring idle
       unit_select<kUMaxGist / kThreads, true>(L.scores, M, a.k, gs, a.score_stride, unit, L.sel, L.u.sel.s,
                                                L.u.sel.t);
       __syncthreads();
+      GSA_STAMP(2);
       unit_stream<kUKUnfold, PAGED>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring,
                                     L.scores, L.sel, 0, nullptr, nullptr, pl);
     }
+    GSA_STAMP(3);
     unit_combine<G>(L, st, w, a.out + (size_t)unit * G * 128, a.lse ? a.lse + (size_t)unit * G : nullptr,
                     nullptr);
+    GSA_STAMP(4);
   } else {
     // hand the split's partial state (and group scores) on: with k > 0 to the
     // unfold launch, else to the unit's last workgroup, which merges
@@ -2405,8 +2455,8 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   if constexpr (PAGED) {
     stage_pages(a, unit, L);
     pl = &L;
-    Kb = reinterpret_cast<const char*>(a.K) + (size_t)(unit % a.Hkv) * a.pg_rpp * 256;
-    Vb = reinterpret_cast<const char*>(a.V) + (size_t)(unit % a.Hkv) * a.pg_rpp * 256;
+    Kb = reinterpret_cast<const char*>(a.K) + (size_t)(unit % a.Hkv) * a.pg_head_bytes;
+    Vb = reinterpret_cast<const char*>(a.V) + (size_t)(unit % a.Hkv) * a.pg_head_bytes;
   }
   bf16x8u qf[4];
   {
@@ -2727,6 +2777,7 @@ gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const 
     u.pg_lp = lp;
     u.pg_rpp = pl.pg_P * (pl.C + 1);
     u.pg_bytes = (int64_t)pl.Hkv * u.pg_rpp * 256;
+    u.pg_head_bytes = (int64_t)u.pg_rpp * 256;
     if (pl.unit_S == 1)
       prof_launch((unit_kernel<G, kHierNone, false, true, false, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
     else
