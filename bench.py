@@ -1062,13 +1062,15 @@ def hbm_stream_rates(reps: int = 8) -> dict:
 
 
 def run_phase_stamps(args):
-    """Phase edges of the one-workgroup-per-unit decode kernel, read from the
-    diagnostic build libgsa_stamps.so (`python -m decode_gsa_amd.build
-    --stamps`): per workgroup, thread 0 stamps the chip's 100 MHz clock at the
-    start, after its wave's gists + tail, after the selection, after the
-    unfold and after the output. Prints one JSON line: medians and maxima over
-    the workgroups of each phase (us), averaged over the calls, and the
-    per-XCD median end of the streaming phase (workgroup i runs on XCD i mod 8)."""
+    """Phase edges of the unit-path decode kernels, read from the diagnostic
+    build libgsa_stamps.so (`python -m decode_gsa_amd.build --stamps`): per
+    workgroup, thread 0 stamps the chip's 100 MHz clock at its phase edges
+    (the slots are listed with the stamps in gsa_decode.hip). Prints one JSON
+    line: for each stamped slot, the median and the maximum over the
+    workgroups that stamped it of the time since the call's first start (us),
+    averaged over the calls; with one workgroup per unit also the phase
+    lengths and the per-XCD median end of the streaming phase (workgroup i
+    runs on XCD i mod 8)."""
     import torch
     import decode_gsa_amd as gsa
     import gsa_inputs as gi
@@ -1081,29 +1083,59 @@ def run_phase_stamps(args):
     L.gsa_debug_phase_stamps.restype = ctypes.c_int
     cfg = gi.CONFIGS[args.config]
     dev = torch.device("cuda", 0)
-    inp = gi.make_decode(cfg, 1000 + 2, device=dev)
-    units = cfg.batch * cfg.n_kv_heads
-    layers = [(inp.k_cache, inp.v_cache)] + [(inp.k_cache.clone(), inp.v_cache.clone()) for _ in range(4)]
-    buf = np.zeros(units * 8, dtype=np.uint64)
+    slots, max_wg = 16, 32768
+    buf = np.zeros(max_wg * slots, dtype=np.uint64)
+    if hasattr(cfg, "fanout"):
+        b = cfg.base
+        inp = gi.make_hier(cfg, 1000 + 4, device=dev)
+        layers = [(inp.k_cache, inp.v_cache, inp.k_l2, inp.v_l2)] + [
+            tuple(t.clone() for t in (inp.k_cache, inp.v_cache, inp.k_l2, inp.v_l2)) for _ in range(2)]
+
+        def call(x):
+            gsa.gsa_decode_hier(inp.q, *x, chunk=b.chunk, fanout=cfg.fanout, topk1=b.topk, topk2=cfg.topk2,
+                                tail=b.tail, n_gist=b.M)
+    else:
+        inp = gi.make_decode(cfg, 1000 + 2, device=dev)
+        layers = [(inp.k_cache, inp.v_cache)] + [(inp.k_cache.clone(), inp.v_cache.clone()) for _ in range(4)]
+
+        def call(x):
+            gsa.gsa_decode(inp.q, x[0], x[1], chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail, n_gist=cfg.M)
     rows = []
+    L.gsa_debug_phase_stamps(buf.ctypes.data, buf.nbytes)   # clears the stamps
     for rep in range(args.warmup + args.steps):
-        k, v = layers[rep % len(layers)]
-        out, lse, sel = gsa.gsa_decode(inp.q, k, v, chunk=cfg.chunk, topk=cfg.topk, tail=cfg.tail, n_gist=cfg.M)
+        call(layers[rep % len(layers)])
         torch.cuda.synchronize()
-        if gsa.gsa_profile_marks() != 2:
-            raise SystemExit("phase stamps cover the one-workgroup-per-unit launch only")
+        marks = gsa.gsa_profile_marks()
         if L.gsa_debug_phase_stamps(buf.ctypes.data, buf.nbytes) != 0:
             raise SystemExit("reading the stamps failed")
         if rep >= args.warmup:
-            rows.append(buf.reshape(units, 8)[:, :5].astype(np.int64).copy())
-    res = {"metric": "decode kernel phase edges (us, 100 MHz clock)", "config": cfg.name, "calls": len(rows)}
-    phases = {"stream (gists + tail)": (0, 1), "selection": (1, 2), "unfold": (2, 3), "merge + output": (3, 4)}
-    for name, (a, b) in phases.items():
-        d = np.array([(r[:, b] - r[:, a]) / 100.0 for r in rows])
-        res[name] = {"median": float(np.median(d)), "max_mean": float(d.max(axis=1).mean())}
-    res["first start to last end"] = float(np.mean([(r[:, 4].max() - r[:, 0].min()) / 100.0 for r in rows]))
-    res["stream end, median per XCD"] = [
-        float(np.mean([np.median((r[x::8, 1] - r[:, 0].min()) / 100.0) for r in rows])) for x in range(8)]
+            rows.append(buf.reshape(max_wg, slots).astype(np.int64).copy())
+    res = {"metric": "decode kernel phase edges (us since the call's first workgroup start, 100 MHz clock)",
+           "config": cfg.name, "calls": len(rows), "launches": marks - 1}
+    for sl in range(slots):
+        med, mx, n = [], [], 0
+        for r in rows:
+            t0 = r[:, 0][r[:, 0] > 0].min()
+            v = r[:, sl][r[:, sl] > 0]
+            if v.size == 0:
+                continue
+            d = (v - t0) / 100.0
+            med.append(float(np.median(d)))
+            mx.append(float(d.max()))
+            n = v.size
+        if med:
+            res[f"slot {sl}"] = {"median": round(float(np.mean(med)), 2), "max": round(float(np.mean(mx)), 2),
+                                 "workgroups": n}
+    if marks == 2 and not hasattr(cfg, "fanout") and all(f"slot {i}" in res for i in range(5)):
+        phases = {"stream (gists + tail)": (0, 1), "selection": (1, 2), "unfold": (2, 3),
+                  "merge + output": (3, 4)}
+        units = cfg.batch * cfg.n_kv_heads
+        for name, (a, b2) in phases.items():
+            d = np.array([(r[:units, b2] - r[:units, a]) / 100.0 for r in rows])
+            res[name] = {"median": float(np.median(d)), "max_mean": float(d.max(axis=1).mean())}
+        res["stream end, median per XCD"] = [
+            float(np.mean([np.median((r[x:units:8, 1] - r[:units, 0].min()) / 100.0) for r in rows]))
+            for x in range(8)]
     print(json.dumps(res), flush=True)
 
 

@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <vector>
 #include <type_traits>
 
 #include "gsa.h"
@@ -57,14 +58,22 @@
 #include "gsa_profile.hpp"
 
 // Phase stamps: a diagnostic build of the library (-DGSA_PHASE_STAMPS,
-// libgsa_stamps.so; the product build has none of it). Thread 0 of every
-// workgroup of the one-workgroup-per-unit decode kernel records the chip's
-// 100 MHz real-time counter at the edges of its phases: 0 start, 1 its wave's
-// gists + tail streamed, 2 selection made, 3 chosen rows unfolded, 4 output
-// written. gsa_debug_phase_stamps copies [workgroups][kStampSlots] out.
+// libgsa_stamps.so; the product build has none of it). Thread 0 of a
+// workgroup of the unit-path decode kernels records the chip's 100 MHz
+// real-time counter at the edges of its phases, in slot [blockIdx][slot]:
+//   unit_kernel: 0 start, 1 its wave's gists + tail streamed, then with one
+//     workgroup per unit 2 selection made, 3 chosen rows unfolded, 4 output
+//     written; with several (and two-level): 5 partial state written,
+//     6 candidates or scores handed on;
+//   unit_unfold_kernel: 8 start, 9 selection made, 10 its rows unfolded,
+//     11 partial state written, 12 merged (the unit's last workgroup);
+//   two-level descent (the unit's last stream workgroup): 8 start, 9 level-2
+//     choice, 10 candidates streamed, 11 level-1 choice, 12 unfolded,
+//     13 partial state written, 14 merged.
+// gsa_debug_phase_stamps copies [workgroups][kStampSlots] out and clears it.
 #ifdef GSA_PHASE_STAMPS
-constexpr int kStampSlots = 8;
-constexpr int kStampWGs = 65536;
+constexpr int kStampSlots = 16;
+constexpr int kStampWGs = 32768;
 __device__ unsigned long long g_phase_stamps[kStampWGs * kStampSlots];
 #define GSA_STAMP(slot)                                                                               \
   do {                                                                                                \
@@ -73,7 +82,11 @@ __device__ unsigned long long g_phase_stamps[kStampWGs * kStampSlots];
   } while (0)
 extern "C" int gsa_debug_phase_stamps(void* host, size_t bytes) {
   if (bytes > sizeof(g_phase_stamps)) bytes = sizeof(g_phase_stamps);
-  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_stamps), bytes, 0, hipMemcpyDeviceToHost);
+  hipError_t e = hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_stamps), bytes, 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return (int)e;
+  static std::vector<unsigned long long> zeros(sizeof(g_phase_stamps) / sizeof(unsigned long long), 0ull);
+  return (int)hipMemcpyToSymbol(HIP_SYMBOL(g_phase_stamps), zeros.data(), sizeof(g_phase_stamps), 0,
+                                hipMemcpyHostToDevice);
 }
 #else
 #define GSA_STAMP(slot) ((void)0)
@@ -1330,7 +1343,7 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
 // tail row, the selection, the chosen chunks' raw rows and the merge -- with
 // no hand-off through memory. Each of the four waves streams its own share of
 // rows, 16 at a time, through a private ring of LDS stages filled by
-// direct-to-LDS loads three stages ahead, and folds them in on MFMA:
+// direct-to-LDS loads up to four stages ahead, and folds them in on MFMA:
 //   S^T = K Q^T     16x16x32: A = 16 K rows (LDS, 16-byte reads), B = the g
 //                   query heads padded to 16 columns with zeros;
 //   O^T += V^T P^T  16x16x16: A = V^T read transposed (ds_read_b64_tr_b16),
@@ -1389,22 +1402,35 @@ __device__ __forceinline__ void u_k_frag(const uint32_t (&addr)[4], bf16x8u (&kf
 }
 
 // The V^T operands of a stage for the eight 16-column blocks of d.
-__device__ __forceinline__ void u_v_frag(const uint32_t (&addr)[8], i16x4u (&vf)[8]) {
+// A stage's K fragments (4 x 16-byte reads) and V^T fragments (8 transposed
+// reads) in one block with one wait: the V reads' latency hides under the K
+// reads' instead of following the score and softmax work.
+__device__ __forceinline__ void u_kv_frag(const uint32_t (&ka)[4], const uint32_t (&va)[8], bf16x8u (&kf)[4],
+                                          i16x4u (&vf)[8]) {
+  uint4 a0, a1, a2, a3;
   __asm__ volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %9\n\t"
-      "ds_read_b64_tr_b16 %2, %10\n\t"
-      "ds_read_b64_tr_b16 %3, %11\n\t"
-      "ds_read_b64_tr_b16 %4, %12\n\t"
-      "ds_read_b64_tr_b16 %5, %13\n\t"
-      "ds_read_b64_tr_b16 %6, %14\n\t"
-      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %14\n\t"
+      "ds_read_b128 %3, %15\n\t"
+      "ds_read_b64_tr_b16 %4, %16\n\t"
+      "ds_read_b64_tr_b16 %5, %17\n\t"
+      "ds_read_b64_tr_b16 %6, %18\n\t"
+      "ds_read_b64_tr_b16 %7, %19\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %21\n\t"
+      "ds_read_b64_tr_b16 %10, %22\n\t"
+      "ds_read_b64_tr_b16 %11, %23\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3]), "=&v"(vf[4]), "=&v"(vf[5]), "=&v"(vf[6]),
-        "=&v"(vf[7])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
-        "v"(addr[7])
+      : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(vf[0]), "=&v"(vf[1]), "=&v"(vf[2]), "=&v"(vf[3]),
+        "=&v"(vf[4]), "=&v"(vf[5]), "=&v"(vf[6]), "=&v"(vf[7])
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]),
+        "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
       : "memory");
+  kf[0] = __builtin_bit_cast(bf16x8u, a0);
+  kf[1] = __builtin_bit_cast(bf16x8u, a1);
+  kf[2] = __builtin_bit_cast(bf16x8u, a2);
+  kf[3] = __builtin_bit_cast(bf16x8u, a3);
 }
 
 // Exact top-k of the unit's n group scores (k <= 64 < n <= 4096), all in
@@ -2020,14 +2046,24 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
       }
       return;
     }
-    uint32_t ka[4];
+    uint32_t ka[4], va[8];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) ka[ks] = base + koff[ks];
-    bf16x8u kf[4];
-    u_k_frag(ka, kf);
-    f32x4u s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], s, 0, 0, 0);
+    for (int dt = 0; dt < 8; ++dt) va[dt] = base + voff[dt];
+    bf16x8u kf[4];
+    i16x4u vf[8];
+    u_kv_frag(ka, va, kf, vf);
+    // two independent chains of two products, then their sum: half the
+    // dependent MFMA latency of one chain of four
+    f32x4u s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0], qf[0], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1], qf[1], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[2], qf[2], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[3], qf[3], s1, 0, 0, 0);
+    f32x4u s;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[r] = s0[r] + s1[r];
     // s[r]: head hq against stage row 4 jg + r
     const int i_base = i0 + b * kRows + 4 * jg;
     bool ok[4];
@@ -2067,11 +2103,6 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
       phi[r] = __builtin_bit_cast(short, hi);
       plo[r] = __builtin_bit_cast(short, lo);
     }
-    uint32_t va[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) va[dt] = base + voff[dt];
-    i16x4u vf[8];
-    u_v_frag(va, vf);
     // every hi product, then every lo product (no product waits on the one
     // just issued)
 #pragma unroll
@@ -2081,15 +2112,17 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     for (int dt = 0; dt < 8; ++dt)
       st.o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[dt], plo, st.o[dt], 0, 0, 0);
   };
-  // stages 0..2 in flight; step b issues stage b + 3 (if any) into the slot
-  // stage b - 1 left (its reads completed inside their asm blocks) and waits
-  // for stage b: the 8 loads of each later stage may still be outstanding
+  // The ring's four slots are free when a stream starts: stages 0..3 go out
+  // at once (a stream of at most four stages, such as a chosen chunk's rows,
+  // waits for one memory round trip). Step b waits for stage b (the 8 loads
+  // of each later stage may still be outstanding), computes it, and issues
+  // stage b + 4 into its slot (its reads completed inside their asm blocks).
   issue(0);
   if (nb > 1) issue(1);
   if (nb > 2) issue(2);
+  if (nb > 3) issue(3);
   for (int b = 0; b < nb; ++b) {
     if (b + 3 < nb) {
-      issue(b + 3);
       uwait_vm<24>();
     } else if (b + 2 < nb) {
       uwait_vm<16>();
@@ -2099,6 +2132,7 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
       uwait_vm<0>();   // the last stage: nothing of this stream left in flight
     }
     compute(b);
+    if (b + 4 < nb) issue(b + 4);
   }
 }
 
@@ -2288,7 +2322,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
   const int hq = lane & 15, jg = lane >> 4;
   const int S = SPLIT ? a.S : 1;
   const int unit = blockIdx.x / S, split = blockIdx.x - unit * S;
-  if constexpr (!SPLIT && !HIER && !SETS) GSA_STAMP(0);
+  if constexpr (!SETS) GSA_STAMP(0);
   if constexpr (VARLEN) unit_lengths(args.seq, unit, args.N, args.M, args.C, args.T, &a.N, &a.M);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
   const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
@@ -2332,12 +2366,15 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
     const char* V2b = reinterpret_cast<const char*>(a.V2) + (size_t)unit * a.M2 * 256;
     unit_stream<kUKL2>(Kb, Vb, min(w1, w0 + w * per1), min(w1, w0 + (w + 1) * per1), a, qf, st, ring, L.scores,
                        L.sel, w0, K2b, V2b);
+    GSA_STAMP(1);
     float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
     unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)split * a.part_stride);
+    GSA_STAMP(5);
     float* s2u = a.s2 + (size_t)unit * a.s2_stride;
     for (int i = w0 + tid; i < min(w1, nf); i += kUW * 64) st_coh(s2u + i, L.scores[i - w0]);
     if constexpr (HIER == kHierDescend) {
       if (!arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)S, &L.s_old)) return;
+      GSA_STAMP(6);
       hier_descent<G>(a, L, unit, qf);
     }
     return;
@@ -2408,16 +2445,20 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
     // hand the split's partial state (and group scores) on: with k > 0 to the
     // unfold launch, else to the unit's last workgroup, which merges
     // (device-scope stores: the XCDs' L2s are not coherent)
+    GSA_STAMP(1);
     float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
     unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)split * a.part_stride);
+    GSA_STAMP(5);
     if (a.k > kCandMaxK) {   // the unfold launch selects among every score
       for (int i = w0 + tid; i < min(w1, M); i += kUW * 64) st_coh(gs + i, L.scores[i - w0]);
+      GSA_STAMP(6);
       return;
     }
     if (a.k > 0) {   // the unfold launch selects among the splits' candidates
       const Cands c = cands_of(a, (int)(gridDim.x / S), a.k);
       unit_cands(L, max(0, min(w1, M) - w0), a.k, w0, gs + w0, c.s + (size_t)unit * c.stride,
                  c.id + (size_t)unit * c.stride, S, split, unit);
+      GSA_STAMP(6);
       return;
     }
     if (!arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)S, &L.s_old)) return;
@@ -2448,6 +2489,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   const int hq = lane & 15, jg = lane >> 4;
   const int S2 = a.S2;
   const int unit = blockIdx.x / S2, part = blockIdx.x - unit * S2;
+  GSA_STAMP(8);
   if constexpr (VARLEN) unit_lengths(args.seq, unit, args.N, args.M, args.C, args.T, &a.N, &a.M);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
   const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
@@ -2481,6 +2523,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   } else {
     select_cands(cands_of(a, (int)(gridDim.x / S2), a.k), a.S, unit, a.k, L.sel, L);
   }
+  GSA_STAMP(9);
   // SETS: raw rows of the chosen chunks, their gists (rule 1), then the tail
   const int items = a.k * a.C + (SETS ? (a.gist_set == 1 ? a.k : 0) + a.T : 0);
   const int perp = (items + S2 - 1) / S2;
@@ -2492,13 +2535,16 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   else
     unit_stream<kUKUnfold, PAGED>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st,
                                   L.u.ring[w][0], L.scores, L.sel, 0, nullptr, nullptr, pl);
+  GSA_STAMP(10);
   float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
   unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)(a.S + part) * a.part_stride);
+  GSA_STAMP(11);
   if (!arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)S2, &L.s_old)) return;
   // the stream launch's partials, then these; SETS: these alone
   const int m0 = SETS ? a.S : 0;
   merge_unit<128, G>(part_u + (size_t)m0 * a.part_stride, a.S + S2 - m0, (uint32_t)a.part_stride,
                      a.out + (size_t)unit * G * 128, a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
+  GSA_STAMP(12);
   if (a.sel)
     for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
 }
@@ -2520,19 +2566,23 @@ __device__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16
   char* ring = L.u.ring[w][0];
   // level 2: the chosen groups, ascending, from the stream workgroups' scores
   float* s2u = a.s2 + (size_t)unit * a.s2_stride;
+  GSA_STAMP(8);
   unit_select<kUMaxSel / kThreads, false>(nullptr, (int)a.M2, a.k2, s2u, a.s2_stride, unit, L.sel2, L.u.sel.s,
                                           L.u.sel.t);
   __syncthreads();
+  GSA_STAMP(9);
   // level 1: every candidate gist (scored), four wave shares
   const int nc = a.n_cand;
   const int perc = (nc + kUW - 1) / kUW;
   unit_stream<kUKCand>(Kb, Vb, min(nc, w * perc), min(nc, (w + 1) * perc), a, qf, st, ring, L.scores, L.sel2);
+  GSA_STAMP(10);
   if (a.k > 0) {
     __syncthreads();   // every candidate score is in LDS, every ring idle
     float* gsc = a.scores + (size_t)unit * a.score_stride;
     unit_select<kUMaxGist / kThreads, true>(L.scores, nc, a.k, gsc, a.score_stride, unit, L.sel, L.u.sel.s,
                                             L.u.sel.t);
     __syncthreads();
+    GSA_STAMP(11);
     // candidate index -> chunk id (candidates are in chunk order)
     if (tid < a.k) {
       const int c = L.sel[tid], kg = a.k2 * a.G2;
@@ -2543,13 +2593,16 @@ __device__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16
     const int per2 = (items + kUW - 1) / kUW;
     unit_stream<kUKUnfold>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
                            L.sel);
+    GSA_STAMP(12);
   }
   float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
   unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)a.S * a.part_stride);
   done_stores();
   __syncthreads();
+  GSA_STAMP(13);
   merge_unit<128, G>(part_u, a.S + 1, (uint32_t)a.part_stride, a.out + (size_t)unit * G * 128,
                      a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
+  GSA_STAMP(14);
   if (a.sel2)
     for (int i = tid; i < a.k2; i += kUW * 64) a.sel2[(size_t)unit * a.k2 + i] = L.sel2[i];
   if (a.sel)
