@@ -1802,6 +1802,7 @@ struct UnitLds {
   float scores[kUWgItems];
   int32_t sel[kFastSel];
   int32_t sel2[kFastSel];
+  unsigned long long wtop[kUW][16];     // the waves' best keys (select_small)
   uint32_t s_old;
 };
 
@@ -2268,10 +2269,60 @@ __device__ __forceinline__ void unit_cands(UnitLds& L, int n, int kk, int id0, f
 // dst (LDS); every thread of the workgroup takes part. The ids travel with
 // the scores (staged in the LDS score array when they fit), so the mapping
 // from list position to id costs no further round trip.
+// Few candidates (nc <= 256, kk <= 16): thread t takes candidate t as the
+// composite key order_key(score) << 32 | ~id (equal scores: the smaller id
+// ranks first; ids are distinct among real candidates, and the -inf padding
+// ranks below every real one), each wave sorts its 64 keys, and one wave
+// sorts the four waves' 16 best: two sorts, no threshold, scan or rank pass.
+// top: LDS for the waves' 16 best. dst (LDS) gets the kk ids ascending; it is
+// valid after the barrier at the end.
+__device__ __forceinline__ void select_small_keys(unsigned long long key, int nc, int kk, int32_t* dst,
+                                                  unsigned long long (&top)[kUW][16]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (w * 64 < nc) {   // uniform per wave: a wave past the candidates holds only zeros
+    key = wave_sort<true>(key);
+  }
+  if (lane < 16) top[w][lane] = key;
+  __syncthreads();
+  if (w == 0) {
+    unsigned long long k2 = top[lane >> 4][lane & 15];
+    k2 = wave_sort<true>(k2);
+    uint32_t id = lane < kk ? ~(uint32_t)k2 : 0xFFFFFFFFu;
+    id = wave_sort<false>(id);
+    if (lane < kk) dst[lane] = (int32_t)id;
+  }
+  __syncthreads();
+}
+// candidates in device memory, written by other workgroups
+__device__ __forceinline__ void select_small(const float* cs, const int32_t* ci, int stride, int nc, int kk,
+                                             int32_t* dst, unsigned long long (&top)[kUW][16]) {
+  const int tid = threadIdx.x;
+  const CohBuf sb(cs, (uint32_t)stride * 4u), ib(ci, (uint32_t)stride * 4u);
+  unsigned long long key = 0ull;
+  if (tid < nc) {
+    const uint32_t sv = sb.u32((uint32_t)tid), iv = ib.u32((uint32_t)tid);
+    key = ((unsigned long long)order_key(__uint_as_float(sv)) << 32) | (uint32_t)~iv;
+  }
+  select_small_keys(key, nc, kk, dst, top);
+}
+// scores in LDS, the id of item i being i
+__device__ __forceinline__ void select_small_lds(const float* sc, int nc, int kk, int32_t* dst,
+                                                 unsigned long long (&top)[kUW][16]) {
+  const int tid = threadIdx.x;
+  const unsigned long long key =
+      tid < nc ? ((unsigned long long)order_key(sc[tid]) << 32) | (uint32_t)~(uint32_t)tid : 0ull;
+  select_small_keys(key, nc, kk, dst, top);
+}
+
 __device__ __forceinline__ void select_cands(const Cands& c, int S, int unit, int kk, int32_t* dst, UnitLds& L) {
   if (kk <= 0) return;
   const int nc = S * cand_cap(S, kk);
   float* cs = c.s + (size_t)unit * c.stride;
+  if (nc <= kUW * 64 && kk <= 16) {   // uniform
+    select_small(cs, c.id + (size_t)unit * c.stride, c.stride, nc, kk, dst, L.wtop);
+    return;
+  }
   const CohBuf ids(c.id + (size_t)unit * c.stride, (uint32_t)c.stride * 4u);
   const int tid = threadIdx.x;
   const bool staged = nc <= kUWgItems;   // uniform
@@ -2284,7 +2335,10 @@ __device__ __forceinline__ void select_cands(const Cands& c, int S, int unit, in
     const int i = tid + q * kThreads;
     idr[q] = staged && i < nc ? ids.u32((uint32_t)i) : 0u;
   }
-  unit_select<kUMaxSel / kThreads, false>(nullptr, nc, kk, cs, c.stride, unit, dst, L.u.sel.s, L.u.sel.t);
+  if (nc <= kUMaxGist)   // uniform: fewer keys per thread, a shorter selection
+    unit_select<kUMaxGist / kThreads, false>(nullptr, nc, kk, cs, c.stride, unit, dst, L.u.sel.s, L.u.sel.t);
+  else
+    unit_select<kUMaxSel / kThreads, false>(nullptr, nc, kk, cs, c.stride, unit, dst, L.u.sel.s, L.u.sel.t);
   if (staged) {
 #pragma unroll
     for (int q = 0; q < kIdsPer; ++q) {
@@ -2567,8 +2621,12 @@ __device__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16
   // level 2: the chosen groups, ascending, from the stream workgroups' scores
   float* s2u = a.s2 + (size_t)unit * a.s2_stride;
   GSA_STAMP(8);
-  unit_select<kUMaxSel / kThreads, false>(nullptr, (int)a.M2, a.k2, s2u, a.s2_stride, unit, L.sel2, L.u.sel.s,
-                                          L.u.sel.t);
+  if (a.M2 <= kUMaxGist)   // uniform: fewer keys per thread, a shorter selection
+    unit_select<kUMaxGist / kThreads, false>(nullptr, (int)a.M2, a.k2, s2u, a.s2_stride, unit, L.sel2, L.u.sel.s,
+                                             L.u.sel.t);
+  else
+    unit_select<kUMaxSel / kThreads, false>(nullptr, (int)a.M2, a.k2, s2u, a.s2_stride, unit, L.sel2, L.u.sel.s,
+                                            L.u.sel.t);
   __syncthreads();
   GSA_STAMP(9);
   // level 1: every candidate gist (scored), four wave shares
@@ -2579,9 +2637,13 @@ __device__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16
   if (a.k > 0) {
     __syncthreads();   // every candidate score is in LDS, every ring idle
     float* gsc = a.scores + (size_t)unit * a.score_stride;
-    unit_select<kUMaxGist / kThreads, true>(L.scores, nc, a.k, gsc, a.score_stride, unit, L.sel, L.u.sel.s,
-                                            L.u.sel.t);
-    __syncthreads();
+    if (nc <= kUW * 64 && a.k <= 16 && a.k < nc) {
+      select_small_lds(L.scores, nc, a.k, L.sel, L.wtop);
+    } else {
+      unit_select<kUMaxGist / kThreads, true>(L.scores, nc, a.k, gsc, a.score_stride, unit, L.sel, L.u.sel.s,
+                                              L.u.sel.t);
+      __syncthreads();
+    }
     GSA_STAMP(11);
     // candidate index -> chunk id (candidates are in chunk order)
     if (tid < a.k) {
