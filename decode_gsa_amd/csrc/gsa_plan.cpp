@@ -349,8 +349,8 @@ gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* o) {
   if (p->head_dim != 128) return fail(GSA_ERR_UNSUPPORTED, "prefill needs head_dim=128");
   if (p->dtype != GSA_BF16) return fail(GSA_ERR_UNSUPPORTED, "prefill needs bf16 inputs");
   const int32_t g = p->n_q_heads / p->n_kv_heads;
-  if (g != 1 && g != 2 && g != 4)
-    return fail(GSA_ERR_UNSUPPORTED, "prefill: %d query heads per kv-head not in {1, 2, 4}", g);
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(GSA_ERR_UNSUPPORTED, "prefill: %d query heads per kv-head not in {1, 2, 4, 8}", g);
   if (p->topk > kPrefillMaxK)
     return fail(GSA_ERR_UNSUPPORTED, "prefill: topk=%d above %d", p->topk, kPrefillMaxK);
   if (p->n_gist > kPrefillMaxGist)

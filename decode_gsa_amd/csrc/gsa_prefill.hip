@@ -691,6 +691,9 @@ struct AttArgs {
   int32_t M, C, k, W, Hkv, n_blocks, q_start, n_q;
   int32_t q_stride;       // query i sits at position q_start + i * q_stride
   float scale_log2;
+  // query heads per kv-head = kv_div * G: each kv-head's heads go to kv_div
+  // workgroups of G heads each (head group v = kv-head v / kv_div)
+  int32_t kv_div;
 };
 
 struct AttLds {
@@ -914,8 +917,9 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
   using S = AttShape<G>;
   constexpr int H = S::HPW, NT = S::NT;
   __shared__ __attribute__((aligned(16))) AttLds L;
-  int kvh, blk;
-  wg_coords(a.n_blocks, a.Hkv, &kvh, &blk);
+  int hg, blk;
+  wg_coords(a.n_blocks, a.Hkv * a.kv_div, &hg, &blk);
+  const int kvh = hg / a.kv_div;        // the kv-head of head group hg (G query heads)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int qi = lane & 15, jg = lane >> 4;
   const int qt = w % 4;                 // 16-query tile of this wave
@@ -985,7 +989,7 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
   __syncthreads();
 
   bf16x8 qf[H][4];
-  load_qfrag<H>(reinterpret_cast<const char*>(a.q) + (int64_t)kvh * G * a.n_q * kRowBytes, a.n_q, t_idx,
+  load_qfrag<H>(reinterpret_cast<const char*>(a.q) + (int64_t)hg * G * a.n_q * kRowBytes, a.n_q, t_idx,
                 valid, h0, jg, qf);
   const char* Kh = reinterpret_cast<const char*>(a.K) + (int64_t)kvh * a.R * kRowBytes;
   const char* Vh = reinterpret_cast<const char*>(a.V) + (int64_t)kvh * a.R * kRowBytes;
@@ -1017,7 +1021,7 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
 #pragma unroll
   for (int h = 0; h < H; ++h) {
     const float inv = 1.f / fsum4(st.l[h]);
-    float* o = a.out + (((int64_t)kvh * G + h0 + h) * a.n_q + t_idx) * kD;
+    float* o = a.out + (((int64_t)hg * G + h0 + h) * a.n_q + t_idx) * kD;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const float4 v = make_float4(st.o[h][dt][0] * inv, st.o[h][dt][1] * inv, st.o[h][dt][2] * inv,
@@ -1027,9 +1031,13 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
   }
 }
 
+// G query heads per kv-head; the attention launch takes them in groups of AG
+// (g = 8: two workgroups of four heads per kv-head and query block, each
+// reading the kv-head's tiles).
 template <int G>
 gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, const void* V, float* out,
                          int32_t* sel, char* ws, hipStream_t stream) {
+  constexpr int AG = G == 8 ? 4 : G;
   prof_begin_call();
   if (pl.n_q == 0) return GSA_OK;
   int32_t* wsel = reinterpret_cast<int32_t*>(ws);
@@ -1048,7 +1056,8 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
   t.M = (int32_t)pl.M; t.C = pl.C; t.k = pl.k; t.W = pl.W; t.Hkv = pl.Hkv; t.n_blocks = pl.n_blocks;
   t.q_start = (int32_t)pl.q_start; t.n_q = (int32_t)pl.n_q; t.q_stride = pl.q_stride;
   t.scale_log2 = pl.scale * kLog2e;
-  prof_launch((prefill_attend<G>), dim3(grid), dim3(AttShape<G>::NT), 0, stream, t);
+  t.kv_div = G / AG;
+  prof_launch((prefill_attend<AG>), dim3(grid * (G / AG)), dim3(AttShape<AG>::NT), 0, stream, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return fail(GSA_ERR_HIP, "%s launch: %s", pl.q_stride == 1 ? "gsa_prefill_blocksparse" : "gsa_gist_prefill",
@@ -1092,6 +1101,7 @@ extern "C" gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, con
     case 1: return run_prefill<1>(pl, q, k_cache, v_cache, out, sel, ws, st);
     case 2: return run_prefill<2>(pl, q, k_cache, v_cache, out, sel, ws, st);
     case 4: return run_prefill<4>(pl, q, k_cache, v_cache, out, sel, ws, st);
+    case 8: return run_prefill<8>(pl, q, k_cache, v_cache, out, sel, ws, st);
   }
   return fail(GSA_ERR_UNSUPPORTED, "prefill: %d query heads per kv-head not in {1, 2, 4}", pl.g);
 }
@@ -1113,6 +1123,7 @@ extern "C" gsa_status_t gsa_gist_prefill(const gsa_gist_params* p, const void* q
     case 1: return run_prefill<1>(pl, q, k_cache, v_cache, out, nullptr, nullptr, st);
     case 2: return run_prefill<2>(pl, q, k_cache, v_cache, out, nullptr, nullptr, st);
     case 4: return run_prefill<4>(pl, q, k_cache, v_cache, out, nullptr, nullptr, st);
+    case 8: return run_prefill<8>(pl, q, k_cache, v_cache, out, nullptr, nullptr, st);
   }
   return fail(GSA_ERR_UNSUPPORTED, "gist prefill: %d query heads per kv-head not in {1, 2, 4}", pl.g);
 }

@@ -323,7 +323,7 @@ gsa_status_t gsa_decode_levels(const gsa_levels_params* p, const void* q, const 
  * [t - W + 1, t].
  * ---------------------------------------------------------------------- */
 typedef struct {
-  int32_t n_q_heads;   /* Hq, multiple of n_kv_heads; g = Hq/Hkv in {1, 2, 4}
+  int32_t n_q_heads;   /* Hq, multiple of n_kv_heads; g = Hq/Hkv in {1, 2, 4, 8}
                           (other g: GSA_ERR_UNSUPPORTED) */
   int32_t n_kv_heads;  /* Hkv >= 1 */
   int32_t head_dim;    /* D: 128 (others: GSA_ERR_UNSUPPORTED) */
@@ -370,7 +370,7 @@ gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, const void* q,
  * gist M not yet appended) is gsa_decode with topk = 0 and tail = C.
  * ---------------------------------------------------------------------- */
 typedef struct {
-  int32_t n_q_heads;   /* Hq, multiple of n_kv_heads; g in {1, 2, 4} */
+  int32_t n_q_heads;   /* Hq, multiple of n_kv_heads; g in {1, 2, 4, 8} */
   int32_t n_kv_heads;  /* Hkv >= 1 */
   int32_t head_dim;    /* D: 128 */
   int32_t chunk;       /* C >= 1 */
@@ -393,7 +393,7 @@ typedef struct {
  * No workspace. With n_q = 0 nothing is launched and q, out may be NULL.
  * GSA_ERR_INVALID_ARG for a NULL pointer or a query range the
  * cache cannot serve; GSA_ERR_UNSUPPORTED for shapes the kernel does not
- * run (as gsa_prefill_blocksparse: bf16, D = 128, g in {1, 2, 4},
+ * run (as gsa_prefill_blocksparse: bf16, D = 128, g in {1, 2, 4, 8},
  * M <= 65536, N + M < 2^31).
  */
 gsa_status_t gsa_gist_prefill(const gsa_gist_params* p, const void* q, const void* k_cache,

@@ -208,7 +208,8 @@ def good_prefill(**kw):
     ({"n_q": 1025}, INVALID),                   # runs past n_raw
     ({"n_gist": 257}, INVALID),
     ({"n_q_heads": 12, "n_kv_heads": 4}, UNSUPPORTED),
-    ({"n_q_heads": 16, "n_kv_heads": 2}, UNSUPPORTED),   # g = 8: no prefill kernel
+    ({"n_q_heads": 16, "n_kv_heads": 2}, OK),            # g = 8
+    ({"n_q_heads": 32, "n_kv_heads": 2}, UNSUPPORTED),   # g = 16
     ({"topk": 32}, OK),
     ({"topk": 33}, UNSUPPORTED),                  # above the per-block union bound
     ({"n_raw": 16 * 65537, "n_gist": 65537, "q_start": 0, "n_q": 64}, UNSUPPORTED),
@@ -302,7 +303,8 @@ def good_gist(**kw):
     ({"n_gist": 61, "n_raw": 992, "n_q": 62}, "ok"),
     ({"head_dim": 64}, UNSUPPORTED),
     ({"dtype": gsa.GSA_F32}, UNSUPPORTED),
-    ({"n_q_heads": 16, "n_kv_heads": 2}, UNSUPPORTED),
+    ({"n_q_heads": 16, "n_kv_heads": 2}, "ok"),             # g = 8
+    ({"n_q_heads": 32, "n_kv_heads": 2}, UNSUPPORTED),      # g = 16
     ({"chunk": 0}, INVALID),
     ({"row_capacity": 1000}, INVALID),
     ({"n_q": 0}, OK),                   # nothing to launch: NULL q and out are allowed
@@ -474,9 +476,9 @@ def test_documented_head_and_type_sets_match_validation(L):
     dec = _block(text, "typedef struct {\n  int32_t batch;", "} gsa_decode_params;")
     assert "g = Hq/Hkv must be 1, 2, 4 or 8" in dec and "D: 64 or 128" in dec
     pre = _block(text, "typedef struct {\n  int32_t n_q_heads;", "} gsa_prefill_params;")
-    assert "g = Hq/Hkv in {1, 2, 4}" in pre and "D: 128" in pre and "GSA_BF16 (GSA_F32" in pre
+    assert "g = Hq/Hkv in {1, 2, 4, 8}" in pre and "D: 128" in pre and "GSA_BF16 (GSA_F32" in pre
     gis = _block(text, "gsa_status_t gsa_prefill_blocksparse(", "gsa_status_t gsa_gist_prefill(")
-    assert "g in {1, 2, 4}" in gis
+    assert "g in {1, 2, 4, 8}" in gis
     n = ctypes.c_size_t(0)
     for g in range(1, 10):
         for D in (32, 64, 96, 128, 256):
@@ -488,7 +490,7 @@ def test_documented_head_and_type_sets_match_validation(L):
                 assert L.gsa_decode_hier_workspace_size(ctypes.byref(h), ctypes.byref(n)) == want
                 lv = gsa.levels_params(p, 4, [2, 1])
                 assert L.gsa_decode_levels_workspace_size(ctypes.byref(lv), ctypes.byref(n)) == want
-                want_p = OK if g in (1, 2, 4) and D == 128 and dt == gsa.GSA_BF16 else UNSUPPORTED
+                want_p = OK if g in (1, 2, 4, 8) and D == 128 and dt == gsa.GSA_BF16 else UNSUPPORTED
                 pp = good_prefill(n_q_heads=2 * g, n_kv_heads=2, head_dim=D, dtype=dt)
                 assert L.gsa_prefill_workspace_size(ctypes.byref(pp), ctypes.byref(n)) == want_p, (g, D, dt)
                 gp = gsa.gist_params(2 * g, 2, D, 16, 1024, 64, 0, 8, dtype=dt)

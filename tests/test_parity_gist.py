@@ -55,6 +55,7 @@ GIST_CASES = [
     dict(Hq=4, Hkv=1, C=64, M=70, r=10, m_start=5, n_q=65),      # C = 64
     dict(Hq=4, Hkv=1, C=1, M=200, r=1, m_start=0, n_q=130),      # C = 1: one raw token per gist
     dict(Hq=8, Hkv=2, C=16, M=64, r=0, m_start=63, n_q=1),       # one query
+    dict(Hq=16, Hkv=2, C=16, M=150, r=7, m_start=0, n_q=150),    # g = 8
 ]
 
 

@@ -63,6 +63,7 @@ CASES = [
     dict(n_raw=4096, n_q=200, n_kv_heads=2, n_q_heads=8, topk=8),
     dict(n_raw=4096, n_q=130, n_kv_heads=2, n_q_heads=2, topk=8),            # g = 1
     dict(n_raw=4096, n_q=64, n_kv_heads=1, n_q_heads=2, topk=16),            # g = 2
+    dict(n_raw=4096, n_q=200, n_kv_heads=2, n_q_heads=16, topk=8),           # g = 8
     dict(n_raw=4096, n_q=96, n_kv_heads=2, n_q_heads=8, topk=0),             # gists + window only
     dict(n_raw=3000, n_gist=187, n_q=70, n_kv_heads=1, n_q_heads=4, topk=8, chunk=16),  # partial chunk
     dict(n_raw=4096, n_q=128, n_kv_heads=1, n_q_heads=4, topk=32, chunk=8, window=40),  # k = 32, C = 8
@@ -74,6 +75,7 @@ CASES = [
     dict(n_raw=300, n_gist=37, n_q=300, n_kv_heads=1, n_q_heads=4, topk=5, chunk=8, window=3,
          values="int"),
     dict(n_raw=256, n_q=256, n_kv_heads=1, n_q_heads=2, topk=32, chunk=4, window=1, values="int"),
+    dict(n_raw=520, n_q=520, n_kv_heads=1, n_q_heads=8, topk=8, chunk=16, window=20, values="int"),  # g = 8
 ]
 
 
