@@ -1952,9 +1952,29 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
   // the unit's level-2 arrays (K2b, V2b), as offsets from the level-1 bases
   const int64_t k2off = KIND == kUKL2 ? K2b - Kb : 0;
   const int64_t v2off = KIND == kUKL2 ? V2b - Vb : 0;
+  // Paged caches: a stage's four rows per lane, their page-table entries and
+  // slots, read from LDS one stage before the stage's loads go out.
+  struct PLook {
+    int32_t rw[4], pg[4];
+    unsigned slot[4];
+  } look;
+  auto plook = [&](int b) {
+    if constexpr (PAGED) {
+      unsigned pi[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + b * kRows + 4 * u + (lane >> 4);
+        look.rw[u] = row_of(i);
+        paged_slot(i, look.rw[u], pi[u], look.slot[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) look.pg[u] = lds_at(pl->pages, pi[u]);
+    }
+  };
   // stage b -> ring slot b % kUNB: lane i loads 16 bytes of row 4u + i/16 into
   // LDS slot i%16, K and V alike. Items past the end of the last stage read
   // row 0 (in bounds, masked), so that every stage issues the same eight loads.
+  // Paged: stage b's rows are in `look` (plook(b) ran before).
   auto issue = [&](int b) {
     char* kd = ring + (b % kUNB) * kUStage;
     char* vd = kd + kUTile;
@@ -1972,25 +1992,15 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
       return;
     }
     if constexpr (PAGED) {
-      // the four rows' chunk slots first, then their four page-table reads
-      // together (one LDS wait), then the loads
-      int32_t rw[4];
-      unsigned pi[4], slot[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + b * kRows + 4 * u + (lane >> 4);
-        rw[u] = row_of(i);
-        paged_slot(i, rw[u], pi[u], slot[u]);
-      }
-      int32_t pg[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) pg[u] = lds_at(pl->pages, pi[u]);
+      // the stage's rows were looked up in the page table one stage earlier
+      // (plook), so the loads wait for no LDS read here
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int r = 4 * u + (lane >> 4);
-        const int64_t off = rw[u] < 0 ? 0
-                            : rw[u] >= kExtraRow ? paged_off(a, *pl, rw[u])
-                                                 : (int64_t)pg[u] * a.pg_bytes + (int64_t)slot[u] * 256;
+        const int rw = look.rw[u];
+        const int64_t off = rw < 0 ? 0
+                            : rw >= kExtraRow ? paged_off(a, *pl, rw)
+                                              : (int64_t)look.pg[u] * a.pg_bytes + (int64_t)look.slot[u] * 256;
         __builtin_amdgcn_global_load_lds(Kb + off + uk_slot(sl, r) * 16, kd + u * 1024, 16, 0, kUNt);
         __builtin_amdgcn_global_load_lds(Vb + off + uv_slot(sl, r) * 16, vd + u * 1024, 16, 0, kUNt);
       }
@@ -2118,10 +2128,11 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
   // waits for one memory round trip). Step b waits for stage b (the 8 loads
   // of each later stage may still be outstanding), computes it, and issues
   // stage b + 4 into its slot (its reads completed inside their asm blocks).
-  issue(0);
-  if (nb > 1) issue(1);
-  if (nb > 2) issue(2);
-  if (nb > 3) issue(3);
+  for (int b = 0; b < nb && b < 4; ++b) {
+    plook(b);
+    issue(b);
+  }
+  if (nb > 4) plook(4);
   for (int b = 0; b < nb; ++b) {
     if (b + 3 < nb) {
       uwait_vm<24>();
@@ -2133,7 +2144,10 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
       uwait_vm<0>();   // the last stage: nothing of this stream left in flight
     }
     compute(b);
-    if (b + 4 < nb) issue(b + 4);
+    if (b + 4 < nb) {
+      issue(b + 4);
+      if (b + 5 < nb) plook(b + 5);   // its page-table reads land while stage b + 1 computes
+    }
   }
 }
 
