@@ -2218,11 +2218,11 @@ __device__ __forceinline__ void unit_combine(UnitLds& L, const UState& st, int w
 // (unit_select) is written instead. gscr: the unit's score row at id0 (the
 // radix fallback's copy of the scores).
 constexpr int kCandPer = 32;   // keys per thread of a stream workgroup's own selection
-// Candidates pay off while the bound on a workgroup's k-th score is cheap
-// (k <= 16, select_tau); above that each stream workgroup hands all its
-// scores on and the unfold launch selects among them.
+// k <= 64: select_tau bounds a workgroup's k-th score (k > 16: from its
+// threads' four largest), and the unfold launch selects among S cap
+// candidates instead of every score.
 constexpr int kCandMaxK = kUnitCandMaxK;
-static_assert(kCandMaxK <= 16, "select_tau's tight bound");
+static_assert(kCandMaxK <= kFastSel, "select_tau bounds the k-th score for k <= 64");
 static_assert(kCandPer * kThreads >= kUWgItems && kCandPer % 16 == 0, "a workgroup's scores fit the selection");
 __device__ __forceinline__ void unit_cands(UnitLds& L, int n, int kk, int id0, float* gscr, float* cs, int32_t* ci,
                                            int S, int split, int unit) {

@@ -70,7 +70,7 @@ constexpr int32_t kPagedMaxExtra = 64;
 
 // The several-workgroups-per-unit launch hands candidates on for k up to
 // this; above it every group score.
-constexpr int32_t kUnitCandMaxK = 16;
+constexpr int32_t kUnitCandMaxK = 64;
 GSA_HD inline int32_t cand_cap(int32_t S, int32_t kk) {
   return (int64_t)S * 2 * kk <= kUnitMaxSel ? 2 * kk : kk;
 }
