@@ -109,36 +109,48 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const char*)p);
 }
 
-// The V^T operands of a 32-row tile for all 8 column blocks of 16: two
-// transposed 8-byte reads per block (rows 0-15 and 16-31 of the tile, the
-// second 4096 bytes further). Written out as one asm block that also waits
-// for its reads: the builtin form makes the compiler wait for every direct-to-
-// LDS load in flight first.
-__device__ __forceinline__ void lds_tr_tile(const uint32_t (&addr)[8], bf16x8 (&vf)[8]) {
+
+// A tile's K operand reads (eight 16-byte reads) and its V^T operands for
+// all 8 column blocks of 16 (two transposed 8-byte reads per block: rows
+// 0-15 and 16-31 of the tile, the second 4096 bytes further) in one asm block
+// that also waits for them: the V reads' latency hides under the K reads'
+// instead of following the score and softmax work, and the builtin form
+// would make the compiler wait for every direct-to-LDS load in flight first.
+__device__ __forceinline__ void lds_kv_tile(const uint32_t (&ka)[8], const uint32_t (&va)[8], uint4 (&r)[8],
+                                            bf16x8 (&vf)[8]) {
   i16x4 a[8], b[8];
   __asm__ volatile(
-      "ds_read_b64_tr_b16 %0, %16\n\t"
-      "ds_read_b64_tr_b16 %1, %16 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %2, %17\n\t"
-      "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %4, %18\n\t"
-      "ds_read_b64_tr_b16 %5, %18 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %6, %19\n\t"
-      "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %8, %20\n\t"
-      "ds_read_b64_tr_b16 %9, %20 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %10, %21\n\t"
-      "ds_read_b64_tr_b16 %11, %21 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %12, %22\n\t"
-      "ds_read_b64_tr_b16 %13, %22 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %14, %23\n\t"
-      "ds_read_b64_tr_b16 %15, %23 offset:4096\n\t"
+      "ds_read_b128 %0, %24\n\t"
+      "ds_read_b128 %1, %25\n\t"
+      "ds_read_b128 %2, %26\n\t"
+      "ds_read_b128 %3, %27\n\t"
+      "ds_read_b128 %4, %28\n\t"
+      "ds_read_b128 %5, %29\n\t"
+      "ds_read_b128 %6, %30\n\t"
+      "ds_read_b128 %7, %31\n\t"
+      "ds_read_b64_tr_b16 %8, %32\n\t"
+      "ds_read_b64_tr_b16 %9, %32 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %10, %33\n\t"
+      "ds_read_b64_tr_b16 %11, %33 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %12, %34\n\t"
+      "ds_read_b64_tr_b16 %13, %34 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %14, %35\n\t"
+      "ds_read_b64_tr_b16 %15, %35 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %16, %36\n\t"
+      "ds_read_b64_tr_b16 %17, %36 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %18, %37\n\t"
+      "ds_read_b64_tr_b16 %19, %37 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %20, %38\n\t"
+      "ds_read_b64_tr_b16 %21, %38 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %22, %39\n\t"
+      "ds_read_b64_tr_b16 %23, %39 offset:4096\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a[0]), "=&v"(b[0]), "=&v"(a[1]), "=&v"(b[1]), "=&v"(a[2]), "=&v"(b[2]), "=&v"(a[3]),
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+        "=&v"(a[0]), "=&v"(b[0]), "=&v"(a[1]), "=&v"(b[1]), "=&v"(a[2]), "=&v"(b[2]), "=&v"(a[3]),
         "=&v"(b[3]), "=&v"(a[4]), "=&v"(b[4]), "=&v"(a[5]), "=&v"(b[5]), "=&v"(a[6]), "=&v"(b[6]),
         "=&v"(a[7]), "=&v"(b[7])
-      : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
-        "v"(addr[7])
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), "v"(ka[7]),
+        "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
       : "memory");
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) vf[dt] = cat8(a[dt], b[dt]);
@@ -790,9 +802,11 @@ __device__ __forceinline__ void att_tile(const char* kt, const char* vt, const A
   for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
     for (int h = 0; h < H; ++h) s[sb][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the tile's eight K operand reads in one round trip, then 2 H independent
-  // MFMA chains, interleaved so that no product waits on the one just issued
+  // the tile's eight K operand reads and its V^T operand reads in one round
+  // trip, then 2 H independent MFMA chains, interleaved so that no product
+  // waits on the one just issued
   bf16x8 kf[4][2];
+  bf16x8 vf[8];
   {
     uint32_t ad[8];
 #pragma unroll
@@ -800,8 +814,15 @@ __device__ __forceinline__ void att_tile(const char* kt, const char* vt, const A
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
         ad[2 * ks + sb] = lds_addr(kt) + (16 * sb + qi) * kRowBytes + k_slot(4 * ks + jg, qi) * 16;
+    // V^T: lane (s16, jg) reads 4 columns of row 4 jg + s16 / 4
+    const int s16 = lane & 15;
+    const int R = 4 * jg + (s16 >> 2);
+    const uint32_t vrow = lds_addr(vt) + R * kRowBytes + 8 * (s16 & 1);
+    uint32_t va[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) va[dt] = vrow + v_slot(2 * dt + ((s16 & 3) >> 1), R) * 16;
     uint4 r[8];
-    lds_read8x16(ad, r);
+    lds_kv_tile(ad, va, r, vf);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -862,15 +883,7 @@ __device__ __forceinline__ void att_tile(const char* kt, const char* vt, const A
     }
     phi[h] = __builtin_bit_cast(bf16x8, hp);
   }
-  // O^T += V^T P^T; the V^T operand comes transposed out of LDS
-  const int s16 = lane & 15;
-  const int R = 4 * jg + (s16 >> 2);
-  const uint32_t vrow = lds_addr(vt) + R * kRowBytes + 8 * (s16 & 1);
-  uint32_t va[8];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) va[dt] = vrow + v_slot(2 * dt + ((s16 & 3) >> 1), R) * 16;
-  bf16x8 vf[8];
-  lds_tr_tile(va, vf);
+  // O^T += V^T P^T (the V^T operand came transposed out of LDS above):
   // every hi product, then every lo product: 8 H independent accumulators
   // between the two products of one
 #pragma unroll
