@@ -1124,6 +1124,11 @@ struct UnfoldArgs {
   uint32_t* cnt;
   float scale_log2;
   SeqLens seq;            // per-sequence lengths (single-level decode)
+  // selection-rule variants (gist_set 1 or 2): after the k C raw items come
+  // set_kg chosen gists (k with rule 1, else 0) and the T tail rows; the
+  // partial states merged are [merge_base, NP) (the scoring pass's are not
+  // in the set)
+  int32_t set_kg, set_tail, merge_base;
 };
 
 template <int D, int G>
@@ -1146,7 +1151,8 @@ __global__ __launch_bounds__(kThreads) void unfold_kernel(UnfoldArgs a) {
   const int tid = threadIdx.x;
   const int unit = blockIdx.x / a.tasks, split = blockIdx.x % a.tasks;
   const bool in_lds = a.k <= kSelLdsMax;
-  int32_t* us = in_lds ? lds.sel : a.sel_ws + (size_t)unit * a.sel_stride;
+  int32_t* const gsel = a.sel_ws + (size_t)unit * a.sel_stride;
+  int32_t* us = in_lds ? lds.sel : gsel;
   int64_t uN = a.N, uM = a.M;
   unit_lengths(a.seq, unit, a.N, a.M, a.C, a.T, &uN, &uM);
   if (a.scores != nullptr) {
@@ -1173,23 +1179,44 @@ __global__ __launch_bounds__(kThreads) void unfold_kernel(UnfoldArgs a) {
   // 32-bit index math: items < 2^30
   const uint32_t C = (uint32_t)a.C;
   const int64_t M = uM, tail0 = uN - a.T;
-  auto row_of = [&](int64_t i64) -> int64_t {
-    const uint32_t i = (uint32_t)i64;
-    const uint32_t ci = i / C, j = i - ci * C;
-    const int64_t m = us[ci];
-    if (m < 0 || m >= M) return -1;         // never taken for a valid selection
-    if (m * C + j >= tail0) return -1;      // the tail attends this row
-    return m * (C + 1) + j;
+  const int64_t kC = (int64_t)a.k * a.C;
+  const int32_t T = a.T;
+  // The row lookups read the selection through a pointer of a fixed address
+  // space (one stream per place): through a generic pointer into LDS the
+  // compiler may fold part of a computed index into the flat access's
+  // immediate offset, and a base address below the LDS aperture is rejected
+  // by the hardware.
+  auto stream = [&](auto sel_id) {
+    auto row_of = [&](int64_t i64) -> int64_t {
+      if (i64 >= kC) {   // selection-rule variants: the chosen gists, then the tail
+        const int64_t j = i64 - kC;
+        if (j < a.set_kg) {
+          const int64_t m = sel_id(j);
+          return m < 0 || m >= M ? -1 : m * (C + 1) + C;
+        }
+        return tail_row(j - a.set_kg, uN, T, M, (int32_t)C);
+      }
+      const uint32_t i = (uint32_t)i64;
+      const uint32_t ci = i / C, j = i - ci * C;
+      const int64_t m = sel_id(ci);
+      if (m < 0 || m >= M) return -1;         // never taken for a valid selection
+      if (m * C + j >= tail0) return -1;      // the tail attends this row
+      return m * (C + 1) + j;
+    };
+    stream_rows<BF16, D, G, true>(reinterpret_cast<const char*>(a.K) + ub,
+                                  reinterpret_cast<const char*>(a.V) + ub, i0, i1, row_of, qv, st,
+                                  a.scale_log2, nullptr, 0.f);
   };
-  stream_rows<BF16, D, G, true>(reinterpret_cast<const char*>(a.K) + ub,
-                                reinterpret_cast<const char*>(a.V) + ub, i0, i1, row_of, qv, st,
-                                a.scale_log2, nullptr, 0.f);
+  if (in_lds)
+    stream([&](int64_t x) -> int64_t { return lds.sel[x]; });
+  else
+    stream([&](int64_t x) -> int64_t { return gsel[x]; });
   float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
   __syncthreads();   // LDS changes role: selection scratch -> partial merge
   write_partial<BF16, D, G>(st, part_u + (size_t)(a.part_base + split) * a.part_stride, lds.u.part, false);
   if (arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)a.tasks, &s_old))
-    merge_unit<D, G>(part_u, a.NP, (uint32_t)a.part_stride, a.out + (size_t)unit * G * D,
-                     a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
+    merge_unit<D, G>(part_u + (size_t)a.merge_base * a.part_stride, a.NP - a.merge_base, (uint32_t)a.part_stride,
+                     a.out + (size_t)unit * G * D, a.lse ? a.lse + (size_t)unit * G : nullptr, kWaves);
 }
 
 // ------------------------------------------------------------------ host ---
@@ -1227,8 +1254,14 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
   g.fuse_k = cand ? 0 : pl.k;   // with candidates the unfold pass selects
   g.sel_ws = wsel; g.sel_stride = pl.sel_stride; g.sel_out = sel_idx;
   g.seq = SeqLens{pl.seq_n, pl.seq_m, pl.Hkv, pl.k};
+  // selection-rule variants: the gist pass only scores (its partial states
+  // are not merged) and leaves the tail to the set's pass; with k = 0 there
+  // is nothing to score
+  const bool sets = pl.gist_set != GSA_GISTS_ALL;
+  if (sets) g.tail_per_task = 0;
   prof_begin_call();
-  prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st, g);
+  if (!sets || pl.k > 0)
+    prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st, g);
   float* cand_s = reinterpret_cast<float*>(ws + pl.off_cand);
   int32_t* cand_i = reinterpret_cast<int32_t*>(ws + pl.off_cand_ids);
   if (cand) {
@@ -1239,7 +1272,7 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
     c.cand_scores = cand_s; c.cand_ids = cand_i; c.cand_stride = pl.cand_stride;
     prof_launch(cand_kernel, dim3(pl.units * pl.S), dim3(kThreads), 0, st, c);
   }
-  if (pl.k > 0) {
+  if (pl.k > 0 || sets) {
     UnfoldArgs u{};
     u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
     u.scores = nullptr;
@@ -1257,6 +1290,9 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
     u.cnt = ctrl_of(ws, pl.off_ctrl, 2);
     u.scale_log2 = pl.scale * kLog2e;
     u.seq = g.seq;
+    u.set_kg = pl.gist_set == GSA_GISTS_SELECTED ? pl.k : 0;
+    u.set_tail = sets ? pl.T : 0;
+    u.merge_base = sets ? pl.S : 0;
     prof_launch((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
   }
   return launch_status("gsa_decode launch");

@@ -177,10 +177,18 @@ gsa_status_t plan_decode(const gsa_decode_params* p, DecodePlan* o) {
   d.NP = d.S + d.S2;
   d.score_stride = d.k > 0 ? (d.M + 63) / 64 * 64 : 0;
   d.unit_S = unit_splits(d);
-  if (d.gist_set != GSA_GISTS_ALL && d.unit_S == 0)
-    return fail(GSA_ERR_UNSUPPORTED,
-                "gist_set=%d runs on the bf16, head_dim 128, topk <= 64 launches (n_gist <= 16384 when topk > 0)",
-                d.gist_set);
+  if (d.gist_set != GSA_GISTS_ALL && d.unit_S == 0) {
+    // split path, selection-rule variants: the gist pass only scores; the
+    // unfold pass attends the whole set (chosen raw rows, the chosen gists
+    // with rule 1, the tail) and merges its own partial states alone
+    const int64_t set_items = items + (d.gist_set == GSA_GISTS_SELECTED ? d.k : 0) + d.T;
+    if (set_items > (1 << 30)) return fail(GSA_ERR_UNSUPPORTED, "selection too large");
+    d.n_items = (int32_t)set_items;
+    d.S2 = splits_for(set_items, units, kMinUnfoldRows);
+    d.items_per_split = (int32_t)ceil_div(set_items, d.S2);
+    d.S2 = (int32_t)ceil_div(set_items, d.items_per_split);
+    d.NP = d.S + d.S2;
+  }
   d.unit_S2 = 0;
   if (d.unit_S > 1) {
     // the unfold launch: the stream's workgroup count, at least 64 rows each
@@ -563,6 +571,8 @@ gsa_status_t plan_append(const gsa_append_params* p, AppendPlan* o) {
 int32_t decode_launches(const DecodePlan& d) {
   if (d.unit_S > 1 && d.gist_set != GSA_GISTS_ALL) return (d.k > 0 ? 1 : 0) + 1;
   if (d.unit_S > 0) return 1 + (d.unit_S2 > 0 ? 1 : 0);
+  if (d.gist_set != GSA_GISTS_ALL)   // split path: scoring pass (k > 0), candidates, the set's pass
+    return (d.k > 0 ? 1 : 0) + (d.cand_stride > 0 ? 1 : 0) + 1;
   return 1 + (d.cand_stride > 0 ? 1 : 0) + (d.k > 0 ? 1 : 0);
 }
 

@@ -102,7 +102,7 @@ struct DecodePlan {
   // the selected chunks
   int32_t S2;
   int32_t items_per_split;
-  int32_t n_items;      // k*C
+  int32_t n_items;      // k*C (selection-rule variants on the split path: the whole set)
   int32_t NP;           // partial states per unit = S (+ S2 when k > 0)
   // byte offsets inside the workspace (control words first)
   size_t off_ctrl, off_scores, off_sel, off_part, total;

@@ -83,12 +83,11 @@ typedef struct {
                           explainer's hybrid attention), GSA_GISTS_SELECTED
                           (1, the chosen chunks' gists: SG+SR) or
                           GSA_GISTS_NONE (2, raw tokens only: SR-only).
-                          1 and 2 need k > 0 or T > 0 (a non-empty set) and
-                          run on the bf16, D = 128, k <= 64 launches
-                          (n_gist <= 16384 when k > 0); other shapes return
-                          GSA_ERR_UNSUPPORTED. gsa_decode_varlen, _paged,
-                          _hier and _levels require 0 (they attend every
-                          gist of every level). */
+                          1 and 2 need k > 0 or T > 0 (a non-empty set);
+                          gsa_decode and gsa_decode_noalloc run them on
+                          every shape they accept. gsa_decode_varlen,
+                          _paged, _hier and _levels require 0 (they attend
+                          every gist of every level). */
   int64_t row_capacity; /* rows allocated per (sequence, kv-head) in the
                           caches, the stride between their [R, D] blocks:
                           0 means exactly R = N + M; else it must be
@@ -470,7 +469,9 @@ gsa_status_t gsa_profile_marks(int32_t* n);
  *     (none when topk = 0), then the launch that selects and attends;
  *     other shapes: 1 when topk = 0, else 2 or 3 (a gist pass, a pass that
  *     takes each split's top-k when there are many gists per unit, an
- *     unfold pass);
+ *     unfold pass); with gist_set 1 or 2: a scoring pass (none when
+ *     topk = 0), the split top-k pass when there is one, and the pass that
+ *     attends the set;
  *   gsa_decode_hier on the bf16, D = 128, k1, k2 <= 64 path: 1 (the
  *     level-2 stream, whose last workgroup per unit runs the descent);
  *     other shapes: 2 to 4 (a level-2

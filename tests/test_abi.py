@@ -131,11 +131,11 @@ def ws_size(L, p):
     ({"gist_set": 3}, INVALID),
     ({"gist_set": -1}, INVALID),
     ({"gist_set": 1}, OK),                    # 4 units: several workgroups per unit
-    ({"gist_set": 1, "head_dim": 64}, UNSUPPORTED),   # the split path (D = 64)
-    ({"gist_set": 2, "topk": 65, "n_raw": 16 * 128, "n_gist": 128}, UNSUPPORTED),   # k > 64
+    ({"gist_set": 1, "head_dim": 64}, OK),    # the split path (D = 64)
+    ({"gist_set": 2, "topk": 65, "n_raw": 16 * 128, "n_gist": 128}, OK),   # k > 64: the split path
     ({"gist_set": 2, "batch": 128}, OK),      # 256 units
     ({"gist_set": 1, "batch": 128, "topk": 0, "tail": 0}, INVALID),   # nothing to attend
-    ({"gist_set": 2, "batch": 128, "dtype": gsa.GSA_F32}, UNSUPPORTED),
+    ({"gist_set": 2, "batch": 128, "dtype": gsa.GSA_F32}, OK),        # fp32: the split path
     ({"row_capacity": 1088}, OK),              # exactly N + M
     ({"row_capacity": 4096}, OK),
     ({"row_capacity": 1087}, INVALID),         # below N + M

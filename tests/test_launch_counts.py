@@ -26,7 +26,7 @@ def cache(B, Hkv, N, M, D, dtype, seed):
     return k, v
 
 
-DECODE = [  # B, Hq, Hkv, D, dtype, N, C, k, T
+DECODE = [  # B, Hq, Hkv, D, dtype, N, C, k, T (, gist_set)
     (32, 32, 8, 128, torch.bfloat16, 1024, 16, 8, 64),     # one workgroup per unit
     (1, 8, 2, 128, torch.bfloat16, 8192, 16, 8, 64),       # several per unit + select/unfold
     (1, 8, 2, 128, torch.bfloat16, 8192, 16, 0, 64),
@@ -34,20 +34,25 @@ DECODE = [  # B, Hq, Hkv, D, dtype, N, C, k, T
     (2, 4, 2, 128, torch.float32, 1024, 16, 4, 16),        # split path
     (2, 4, 2, 64, torch.float32, 1024, 16, 0, 16),
     (1, 4, 1, 128, torch.bfloat16, 4096, 16, 80, 64),      # k > 64: split path
+    (1, 4, 1, 64, torch.float32, 4096, 16, 8, 16, 1),      # split path, selection rule 1
+    (2, 4, 2, 128, torch.float32, 1024, 16, 4, 16, 2),     # split path, selection rule 2
+    (2, 4, 2, 64, torch.float32, 1024, 16, 0, 16, 2),      # k = 0: the tail alone
 ]
 
 
 @pytest.mark.parametrize("case", DECODE)
 def test_decode_marks(gsa, case):
-    B, Hq, Hkv, D, dt, N, C, k, T = case
+    B, Hq, Hkv, D, dt, N, C, k, T = case[:9]
+    rule = case[9] if len(case) > 9 else 0
     M = N // C
     say("decode launches", case)
     kc, vc = cache(B, Hkv, N, M, D, dt, 1)
     q = torch.randn(B, Hq, D).to(dt).cuda()
-    gsa.gsa_decode(q, kc, vc, chunk=C, topk=k, tail=T)
+    gsa.gsa_decode(q, kc, vc, chunk=C, topk=k, tail=T, gist_set=["all", "selected", "none"][rule])
     torch.cuda.synchronize()
     p = gsa.decode_params(B, Hq, Hkv, D, N, M, C, k, T, 0.0,
                           gsa.GSA_BF16 if dt == torch.bfloat16 else gsa.GSA_F32)
+    p.gist_set = rule
     assert gsa.gsa_profile_marks() == gsa.launches(p) + 1
 
 

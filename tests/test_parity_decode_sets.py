@@ -54,6 +54,12 @@ CASES = [
     (cfg_of("gqa_32k", batch=1, n_kv_heads=1, n_q_heads=4, n_raw=16 * 5000, tail=64), None),   # 5000 gists
     (cfg_of("gqa_32k", batch=2, n_raw=4096, topk=0, plant="none"), None),   # k = 0: the tail alone
     (cfg_of("gqa_32k", batch=1, n_kv_heads=2, n_q_heads=8, n_raw=1024, topk=64, plant="none"), None),   # k = M
+    # the split path: a scoring pass, then one pass over the set
+    (cfg_of("tiny_f32"), None),                                             # fp32, D = 64, per-split candidates
+    (cfg_of("tiny_f32", n_raw=4000, n_gist=250, tail=20, topk=5), None),    # ragged, partial chunk
+    (cfg_of("gqa_32k", batch=2, n_raw=4096, head_dim=64), None),            # bf16, D = 64
+    (cfg_of("gqa_32k", batch=2, n_raw=8192, topk=80, plant="none"), None),  # bf16, D = 128, k > 64
+    (cfg_of("tiny_f32", topk=0, plant="none"), None),                       # k = 0: the tail alone
 ]
 
 
@@ -87,13 +93,7 @@ def test_decode_gist_set_ties_and_tail_overlap(gsa, gist_set):
 
 
 def test_decode_gist_set_rejections(gsa):
-    """Shapes off the bf16, head_dim 128, topk <= 64 launches and an empty set
-    are refused before any launch."""
-    cfg = cfg_of("gqa_32k", batch=2, n_raw=4096, head_dim=64)   # D = 64: the split path
-    inp = gi.make_decode(cfg, 5200, device="cuda")
-    with pytest.raises(gsa.GsaError) as e:
-        gsa.gsa_decode(inp.q, inp.k_cache, inp.v_cache, chunk=16, topk=16, tail=64, gist_set="selected")
-    assert e.value.status == gsa.GSA_ERR_UNSUPPORTED
+    """An empty set is refused before any launch."""
     cfg = cfg_of("gqa_32k", n_raw=1024)
     inp = gi.make_decode(cfg, 5201, device="cuda")
     with pytest.raises(gsa.GsaError) as e:
