@@ -211,8 +211,8 @@ constexpr int kQBlock = 64;
 // Prefill limits: chunks a query block can select are tracked in an LDS
 // bitmap (n_gist <= kPrefillMaxGist), and the union of a block's selections
 // holds at most 64 * kPrefillMaxK chunks.
-constexpr int32_t kPrefillMaxGist = 65536;
-constexpr int32_t kPrefillMaxK = 32;
+constexpr int32_t kPrefillMaxGist = 262144;
+constexpr int32_t kPrefillMaxK = 64;
 
 gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* out);
 // Gist-token queries as prefill queries at positions mC + C - 1 (stride C),

@@ -285,9 +285,11 @@ constexpr int kSelNB = 3;               // tiles in the LDS ring
 constexpr int kSelTileBytes = kSelTile * kRowBytes;
 constexpr int kSelPer = kSelTile / 4 / kSelWaves;   // direct loads per wave per tile (4 rows each)
 constexpr int kLaneCand = kSelTile / 4;             // scores one lane sees per tile
-constexpr int kListCap = 24;            // entries of a lane's candidate list
-static_assert(kListCap % 8 == 0, "lists are read in groups of 8 entries");
-static_assert(kPrefillMaxGist <= 65536, "candidate ids fit the id field");
+// Entries of a lane's candidate list: 24 for k <= 32 (two workgroups per
+// compute unit), 32 for k up to 64.
+template <int K> struct SelCap {
+  static constexpr int CAP = K <= 32 ? 24 : 32;
+};
 
 struct SelArgs {
   const void* q;          // [Hq][n_q][D] bf16
@@ -299,14 +301,17 @@ struct SelArgs {
   int32_t* sel_out;       // [Hkv][n_q][k] or null
 };
 
-// Each lane keeps a list of candidate entries of its query: entry e of lane
-// tid is ent[e][tid] = (score bits, gist id).
+// Each lane keeps a list of CAP candidate entries of its query: entry e of
+// lane tid is ent[e][tid] = (score bits, gist id).
+template <int CAP_>
 struct SelLds {
+  static constexpr int CAP = CAP_;
+  static_assert(CAP % 8 == 0, "lists are read in groups of 8 entries");
   char ring[kSelNB][kSelTileBytes];
-  uint2 ent[kListCap][kSelThreads];
+  uint2 ent[CAP][kSelThreads];
   uint32_t full[2][kSelWaves];   // per tile parity: a wave's lists need a compaction
 };
-static_assert(sizeof(SelLds) <= 80 * 1024, "two workgroups per CU");
+static_assert(sizeof(SelLds<24>) <= 80 * 1024, "two workgroups per CU");
 
 // Score of an order key (inverse of order_key on canonical values).
 __device__ __forceinline__ float key_score(uint32_t key) {
@@ -318,12 +323,13 @@ __device__ __forceinline__ float key_score(uint32_t key) {
 // of them that still holds the query's top-k, dealt round-robin over the
 // four lists (kept entry p goes to list p % 4, slot p / 4). The last slot of
 // every list is a spare that takes the writes of dropped entries.
-constexpr int kKeepMax = 4 * (kListCap - 1 - kLaneCand);   // entries a compaction may keep
+constexpr int keep_max(int cap) { return 4 * (cap - 1 - kLaneCand); }   // entries a compaction may keep
 constexpr int kPruneSlack = 8;          // a prune stops once at most k + this many remain
-static_assert(kPrefillMaxK + kPruneSlack <= kKeepMax, "a prune can always keep k + slack entries");
+static_assert(32 + kPruneSlack <= keep_max(SelCap<32>::CAP) && kPrefillMaxK + kPruneSlack <= keep_max(SelCap<kPrefillMaxK>::CAP),
+              "a prune can always keep k + slack entries");
 
-template <int NE>
-__device__ __forceinline__ void sel_load(const SelLds& L, int tid, float (&v)[NE], uint32_t (&id)[NE]) {
+template <int NE, class SL>
+__device__ __forceinline__ void sel_load(const SL& L, int tid, float (&v)[NE], uint32_t (&id)[NE]) {
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
     const uint2 x = L.ent[e][tid];
@@ -334,8 +340,8 @@ __device__ __forceinline__ void sel_load(const SelLds& L, int tid, float (&v)[NE
 
 // Rewrite the lists with the entries marked `take`; returns this lane's new
 // list length and the query's kept count in *tot.
-template <int NE>
-__device__ __forceinline__ int sel_deal(SelLds& L, int w, int lane, const float (&v)[NE],
+template <int NE, class SL>
+__device__ __forceinline__ int sel_deal(SL& L, int w, int lane, const float (&v)[NE],
                                         const uint32_t (&id)[NE], const bool (&take)[NE], int* tot) {
   const int qi = lane & 15, jg = lane >> 4;
   int ct = 0;
@@ -346,7 +352,7 @@ __device__ __forceinline__ int sel_deal(SelLds& L, int w, int lane, const float 
 #pragma unroll
   for (int e = 0; e < NE; ++e) {
     const int jt = take[e] ? (p & 3) : jg;
-    const int slot = take[e] ? (p >> 2) : kListCap - 1;
+    const int slot = take[e] ? (p >> 2) : SL::CAP - 1;
     L.ent[slot][64 * w + qi + 16 * jt] = make_uint2(__float_as_uint(v[e]), id[e]);
     p += take[e] ? 1 : 0;
   }
@@ -359,8 +365,10 @@ __device__ __forceinline__ int sel_deal(SelLds& L, int w, int lane, const float 
 // with the smallest ids (ties go to the smaller gist index). *tau becomes the
 // k-th best score, or -inf while the query has fewer than k candidates.
 // NE: list entries that may be in use (wave-uniform).
-template <int NE>
-__device__ __forceinline__ int sel_exact_n(SelLds& L, int w, int lane, int pos, int k, float* tau) {
+constexpr int kIdBits = 18;             // gist ids below 2^18
+static_assert(kPrefillMaxGist <= (1 << kIdBits), "gist ids fit the bisection");
+template <int NE, class SL>
+__device__ __forceinline__ int sel_exact_n(SL& L, int w, int lane, int pos, int k, float* tau) {
   float v[NE];
   uint32_t id[NE], key[NE];
   sel_load<NE>(L, 64 * w + lane, v, id);
@@ -388,7 +396,7 @@ __device__ __forceinline__ int sel_exact_n(SelLds& L, int w, int lane, int pos, 
   if (__ballot(ce_tot > need) != 0ull) {
     // need-th smallest id among the entries equal to P (ids are distinct)
     uint32_t lo = 0u;
-    for (int b = 15; b >= 0; --b) {
+    for (int b = kIdBits - 1; b >= 0; --b) {
       const uint32_t trial = lo + (1u << b);
       int n = 0;
 #pragma unroll
@@ -412,10 +420,10 @@ __device__ __forceinline__ int sel_exact_n(SelLds& L, int w, int lane, int pos, 
 // them). lo becomes *tau: a later gist scoring <= lo has k earlier entries at
 // least as good. The bisection stops once at most k + kPruneSlack entries are
 // >= lo. Returns -1 (lists untouched) if some query would keep more than
-// kKeepMax entries (scores tied over a wide range); an exact compaction
+// keep_max(CAP) entries (scores tied over a wide range); an exact compaction
 // follows then.
-template <int NE>
-__device__ __forceinline__ int sel_prune_n(SelLds& L, int w, int lane, int pos, int k, float* tau) {
+template <int NE, class SL>
+__device__ __forceinline__ int sel_prune_n(SL& L, int w, int lane, int pos, int k, float* tau) {
   float v[NE];
   uint32_t id[NE];
   sel_load<NE>(L, 64 * w + lane, v, id);
@@ -446,7 +454,7 @@ __device__ __forceinline__ int sel_prune_n(SelLds& L, int w, int lane, int pos, 
       hi = mid;
     }
   }
-  if (__ballot(n_lo > kKeepMax) != 0ull) return -1;
+  if (__ballot(n_lo > keep_max(SL::CAP)) != 0ull) return -1;
   bool take[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e) take[e] = e < pos && (!full || v[e] >= lo);
@@ -457,27 +465,32 @@ __device__ __forceinline__ int sel_prune_n(SelLds& L, int w, int lane, int pos, 
 }
 
 // Entries per list in use, rounded up to groups of 8 (wave-uniform).
+template <int CAP>
 __device__ __forceinline__ int list_groups(int pos) {
-  static_assert(kListCap == 24, "three groups");
+  if constexpr (CAP > 24)
+    if (__ballot(pos > 24)) return 4;
   return __ballot(pos > 16) ? 3 : __ballot(pos > 8) ? 2 : 1;
 }
 
-__device__ __forceinline__ int sel_exact(SelLds& L, int w, int lane, int pos, int k, float* tau) {
-  switch (list_groups(pos)) {
-    case 1: return sel_exact_n<8>(L, w, lane, pos, k, tau);
-    case 2: return sel_exact_n<16>(L, w, lane, pos, k, tau);
-    default: return sel_exact_n<24>(L, w, lane, pos, k, tau);
-  }
+template <class SL>
+__device__ __forceinline__ int sel_exact(SL& L, int w, int lane, int pos, int k, float* tau) {
+  static_assert(SL::CAP == 24 || SL::CAP == 32, "three or four groups");
+  const int grp = list_groups<SL::CAP>(pos);
+  if (grp == 1) return sel_exact_n<8>(L, w, lane, pos, k, tau);
+  if (grp == 2) return sel_exact_n<16>(L, w, lane, pos, k, tau);
+  if (SL::CAP == 24 || grp == 3) return sel_exact_n<24>(L, w, lane, pos, k, tau);
+  return sel_exact_n<SL::CAP == 24 ? 24 : 32>(L, w, lane, pos, k, tau);
 }
 
 // Make room in the lists: prune, or compact exactly if a prune cannot.
-__device__ __forceinline__ int sel_compact(SelLds& L, int w, int lane, int pos, int k, float* tau) {
+template <class SL>
+__device__ __forceinline__ int sel_compact(SL& L, int w, int lane, int pos, int k, float* tau) {
   int n;
-  switch (list_groups(pos)) {
-    case 1: n = sel_prune_n<8>(L, w, lane, pos, k, tau); break;
-    case 2: n = sel_prune_n<16>(L, w, lane, pos, k, tau); break;
-    default: n = sel_prune_n<24>(L, w, lane, pos, k, tau); break;
-  }
+  const int grp = list_groups<SL::CAP>(pos);
+  if (grp == 1) n = sel_prune_n<8>(L, w, lane, pos, k, tau);
+  else if (grp == 2) n = sel_prune_n<16>(L, w, lane, pos, k, tau);
+  else if (SL::CAP == 24 || grp == 3) n = sel_prune_n<24>(L, w, lane, pos, k, tau);
+  else n = sel_prune_n<SL::CAP == 24 ? 24 : 32>(L, w, lane, pos, k, tau);
   return n >= 0 ? n : sel_exact(L, w, lane, pos, k, tau);
 }
 
@@ -521,8 +534,8 @@ __device__ __forceinline__ void load_qbar(const char* qbase, int64_t n_q, int64_
 // Append the candidates of one 16-gist subtile (score[r]: gist m0 + r) that
 // beat tau. Every score is written at the list's end, and the end advances
 // past the ones that beat tau: no branch per score.
-template <bool MASK>
-__device__ __forceinline__ void sel_append(SelLds& L, int tid, const float (&score)[4], int m0, int elig,
+template <bool MASK, class SL>
+__device__ __forceinline__ void sel_append(SL& L, int tid, const float (&score)[4], int m0, int elig,
                                            float tau, int* pos) {
   float v[4];
   bool ok[4];
@@ -547,9 +560,12 @@ __device__ __forceinline__ void sel_append(SelLds& L, int tid, const float (&sco
   *pos = p;
 }
 
-template <int G>
-__global__ __launch_bounds__(kSelThreads, 2) void prefill_select(SelArgs a) {
-  __shared__ __attribute__((aligned(16))) SelLds L;
+// KMAX: the largest k the launch takes (32: lists of 24 entries, two
+// workgroups per compute unit; 64: lists of 32).
+template <int G, int KMAX>
+__global__ __launch_bounds__(kSelThreads, KMAX <= 32 ? 2 : 1) void prefill_select(SelArgs a) {
+  __shared__ __attribute__((aligned(16))) SelLds<SelCap<KMAX>::CAP> L;
+  constexpr int kCap = SelCap<KMAX>::CAP;
   int kvh, blk;
   wg_coords(a.n_blocks, a.Hkv, &kvh, &blk);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -640,7 +656,7 @@ __global__ __launch_bounds__(kSelThreads, 2) void prefill_select(SelArgs a) {
       if (masked) sel_append<true>(L, tid, sc, m0 + 16 * s, elig, tau, &pos);
       else sel_append<false>(L, tid, sc, m0 + 16 * s, elig, tau, &pos);
     }
-    const bool full = __ballot(pos > kListCap - 1 - kLaneCand) != 0ull;
+    const bool full = __ballot(pos > kCap - 1 - kLaneCand) != 0ull;
     if (lane == 0) L.full[it & 1][w] = full ? 1u : 0u;
   }
   wave_lds_sync();
@@ -649,19 +665,19 @@ __global__ __launch_bounds__(kSelThreads, 2) void prefill_select(SelArgs a) {
   // the query's kept entries in ascending id order: each lane ranks its own
   // entries among all of the query's (at most k, dealt round-robin)
   const int tot = sum4(pos);
-  uint32_t ids[kPrefillMaxK];
+  uint32_t ids[KMAX];
 #pragma unroll
-  for (int p = 0; p < kPrefillMaxK; ++p)
+  for (int p = 0; p < KMAX; ++p)
     ids[p] = p < tot ? L.ent[p >> 2][64 * w + qi + 16 * (p & 3)].y : 0xffffffffu;
   if (valid) {
     const int64_t o = ((int64_t)kvh * a.n_q + t_idx) * a.k;
 #pragma unroll
-    for (int e = 0; e < (kPrefillMaxK + 3) / 4; ++e) {
+    for (int e = 0; e < (KMAX + 3) / 4; ++e) {
       if (e < pos) {
         const uint32_t mine = ids[4 * e + jg];
         int rank = 0;
 #pragma unroll
-        for (int p = 0; p < kPrefillMaxK; ++p) rank += ids[p] < mine ? 1 : 0;
+        for (int p = 0; p < KMAX; ++p) rank += ids[p] < mine ? 1 : 0;
         a.sel_ws[o + rank] = (int32_t)mine;
         if (a.sel_out) a.sel_out[o + rank] = (int32_t)mine;
       }
@@ -711,7 +727,6 @@ struct AttArgs {
 struct AttLds {
   char ring[kAttNB][2 * kHalfTile];   // [tile][K rows | V rows]
   uint32_t bitmap[kMaxChunkWords];
-  uint32_t wpre[kMaxChunkWords];
   int32_t U[kMaxUnion];
   uint32_t qm[kMaxUnion][2];
   int scan[8];
@@ -971,7 +986,6 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
     for (int e = 0; e < kPer; ++e) {
       const int wd = tid * kPer + e;
       if (wd < nwords) {
-        L.wpre[wd] = (uint32_t)run;
         uint32_t bits = L.bitmap[wd];
         int r = run;
         while (bits) {
@@ -994,7 +1008,14 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
   for (int pr = tid; pr < nq_blk * a.k; pr += NT) {
     const int m = sb[pr];
     if (m >= 0 && m < E) {
-      const int u = (int)L.wpre[m >> 5] + __popc(L.bitmap[m >> 5] & ((1u << (m & 31)) - 1u));
+      // m's place in the ascending union (it is there): a binary search
+      int lo = 0, hi = nU;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (L.U[mid] <= m) lo = mid;
+        else hi = mid;
+      }
+      const int u = lo;
       const int ql = pr / a.k;
       atomicOr(&L.qm[u][ql >> 5], 1u << (ql & 31));
     }
@@ -1062,7 +1083,10 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
     s.q_start = (int32_t)pl.q_start; s.n_q = (int32_t)pl.n_q;
     s.score_mul = pl.scale / G;
     s.sel_ws = wsel; s.sel_out = sel;
-    prof_launch((prefill_select<G>), dim3(grid), dim3(kSelThreads), 0, stream, s);
+    if (pl.k <= 32)
+      prof_launch((prefill_select<G, 32>), dim3(grid), dim3(kSelThreads), 0, stream, s);
+    else
+      prof_launch((prefill_select<G, 64>), dim3(grid), dim3(kSelThreads), 0, stream, s);
   }
   AttArgs t{};
   t.q = q; t.K = K; t.V = V; t.out = out; t.sel = wsel; t.R = pl.R;

@@ -327,10 +327,10 @@ typedef struct {
   int32_t n_kv_heads;  /* Hkv >= 1 */
   int32_t head_dim;    /* D: 128 (others: GSA_ERR_UNSUPPORTED) */
   int32_t chunk;       /* C >= 1 */
-  int32_t topk;        /* 0 <= k <= 32 (k > 32: GSA_ERR_UNSUPPORTED) */
+  int32_t topk;        /* 0 <= k <= 64 (k > 64: GSA_ERR_UNSUPPORTED) */
   int32_t window;      /* W >= 1 */
   int64_t n_raw;       /* N raw tokens in the cache */
-  int64_t n_gist;      /* M; 0 <= N - M*C <= C; M <= 65536 (above:
+  int64_t n_gist;      /* M; 0 <= N - M*C <= C; M <= 262144 (above:
                           GSA_ERR_UNSUPPORTED) */
   int64_t q_start;     /* first query position, 0 <= q_start */
   int64_t n_q;         /* queries; q_start + n_q <= N */
@@ -393,7 +393,7 @@ typedef struct {
  * GSA_ERR_INVALID_ARG for a NULL pointer or a query range the
  * cache cannot serve; GSA_ERR_UNSUPPORTED for shapes the kernel does not
  * run (as gsa_prefill_blocksparse: bf16, D = 128, g in {1, 2, 4, 8},
- * M <= 65536, N + M < 2^31).
+ * M <= 262144, N + M < 2^31).
  */
 gsa_status_t gsa_gist_prefill(const gsa_gist_params* p, const void* q, const void* k_cache,
                               const void* v_cache, float* out, void* stream);

@@ -211,8 +211,12 @@ def good_prefill(**kw):
     ({"n_q_heads": 16, "n_kv_heads": 2}, OK),            # g = 8
     ({"n_q_heads": 32, "n_kv_heads": 2}, UNSUPPORTED),   # g = 16
     ({"topk": 32}, OK),
-    ({"topk": 33}, UNSUPPORTED),                  # above the per-block union bound
-    ({"n_raw": 16 * 65537, "n_gist": 65537, "q_start": 0, "n_q": 64}, UNSUPPORTED),
+    ({"topk": 33}, OK),                          # longer candidate lists
+    ({"topk": 64}, OK),
+    ({"topk": 65}, UNSUPPORTED),                  # above the per-block union bound
+    ({"n_raw": 16 * 65537, "n_gist": 65537, "q_start": 0, "n_q": 64}, OK),
+    ({"n_raw": 16 * 262144, "n_gist": 262144, "q_start": 0, "n_q": 64}, OK),
+    ({"n_raw": 16 * 262145, "n_gist": 262145, "q_start": 0, "n_q": 64}, UNSUPPORTED),
     ({"n_q": 0}, OK),
     ({"row_capacity": 4352}, OK),              # exactly N + M
     ({"row_capacity": 8192}, OK),
@@ -502,11 +506,11 @@ def test_documented_head_and_type_sets_match_validation(L):
 
 def test_prefill_documented_limits(L):
     n = ctypes.c_size_t(0)
-    for k, want in ((32, OK), (33, UNSUPPORTED)):
+    for k, want in ((64, OK), (65, UNSUPPORTED)):
         assert L.gsa_prefill_workspace_size(ctypes.byref(good_prefill(topk=k)), ctypes.byref(n)) == want
-    big = good_prefill(n_raw=16 * 65537, n_gist=65537, q_start=0, n_q=64)
+    big = good_prefill(n_raw=16 * 262145, n_gist=262145, q_start=0, n_q=64)
     assert L.gsa_prefill_workspace_size(ctypes.byref(big), ctypes.byref(n)) == UNSUPPORTED
-    ok = good_prefill(n_raw=16 * 65536, n_gist=65536, q_start=0, n_q=64)
+    ok = good_prefill(n_raw=16 * 262144, n_gist=262144, q_start=0, n_q=64)
     assert L.gsa_prefill_workspace_size(ctypes.byref(ok), ctypes.byref(n)) == OK
 
 
@@ -564,7 +568,8 @@ def test_launch_counts_follow_the_documented_rules(L):
     assert _launches(L, "gsa_prefill_launches", good_prefill()) == (OK, 2)
     assert _launches(L, "gsa_prefill_launches", good_prefill(topk=0)) == (OK, 1)
     assert _launches(L, "gsa_prefill_launches", good_prefill(n_q=0)) == (OK, 0)
-    assert _launches(L, "gsa_prefill_launches", good_prefill(topk=33)) == (UNSUPPORTED, -1)
+    assert _launches(L, "gsa_prefill_launches", good_prefill(topk=33)) == (OK, 2)
+    assert _launches(L, "gsa_prefill_launches", good_prefill(topk=65)) == (UNSUPPORTED, -1)
 
 
 def test_decode_noalloc_host_rejections(L):

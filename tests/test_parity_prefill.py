@@ -76,6 +76,9 @@ CASES = [
          values="int"),
     dict(n_raw=256, n_q=256, n_kv_heads=1, n_q_heads=2, topk=32, chunk=4, window=1, values="int"),
     dict(n_raw=520, n_q=520, n_kv_heads=1, n_q_heads=8, topk=8, chunk=16, window=20, values="int"),  # g = 8
+    # k above 32: candidate lists of 32 entries, a union of up to 64 k chunks
+    dict(n_raw=4096, n_q=160, n_kv_heads=2, n_q_heads=8, topk=48, chunk=8, window=40),
+    dict(n_raw=600, n_q=600, n_kv_heads=1, n_q_heads=4, topk=64, chunk=4, window=10, values="int"),
 ]
 
 
@@ -119,7 +122,21 @@ def test_prefill_full_size_sampled(gsa):
     say(f"  max err / rms = {err:.2e}")
 
 
-@pytest.mark.parametrize("topk", [16, 32])
+def test_prefill_beyond_65536_gists(gsa):
+    """70000 gists (a 1.12M-token context): chunk ids above 2^16 in the
+    selection, its index tie rule and the attention's chunk union. Integer
+    values make scores exact, so ties at the k-th place are decided by id."""
+    cfg = small(n_raw=16 * 70000, n_q=128, n_kv_heads=1, n_q_heads=4, topk=16, chunk=16, window=64,
+                values="int")
+    say(f"prefill beyond 65536 gists {cfg}")
+    inp = gi.make_prefill(cfg, 6100, device="cuda")
+    qs = [(i, 0) for i in range(0, cfg.n_q, 5)] + [(cfg.n_q - 1, 0)]
+    err, _, sel = run_prefill(gsa, inp, cfg, queries=qs)
+    assert int(sel.max()) >= 65536          # ids past 16 bits were chosen
+    say(f"  max err / rms = {err:.2e}")
+
+
+@pytest.mark.parametrize("topk", [16, 32, 64])
 def test_prefill_all_scores_tied(gsa, topk):
     """q = 0: every group score is 0, so a query keeps the topk smallest
     eligible gist indices. More tied candidates than the candidate lists can
