@@ -34,7 +34,7 @@ __all__ = [
     "gsa_profile_marks", "topk_for_budget", "GIST_SETS", "gsa_gist_prefill", "gsa_cache_append",
     "gsa_decode_levels", "levels_workspace_size", "gsa_decode_varlen", "check_seq_lens",
     "launches", "gsa_decode_noalloc", "PagedParams", "paged_params", "paged_workspace_size",
-    "check_pages", "gsa_decode_paged",
+    "check_pages", "gsa_decode_paged", "gsa_decode_hier_varlen", "check_hier_seq_lens",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -50,7 +50,7 @@ EXPORTED_SYMBOLS = (
     "gsa_decode_levels_workspace_size", "gsa_decode_levels", "gsa_decode_varlen", "gsa_check_seq_lens",
     "gsa_decode_launches", "gsa_decode_hier_launches", "gsa_decode_levels_launches",
     "gsa_prefill_launches", "gsa_decode_noalloc", "gsa_decode_paged_workspace_size",
-    "gsa_decode_paged", "gsa_check_pages",
+    "gsa_decode_paged", "gsa_check_pages", "gsa_decode_hier_varlen", "gsa_check_hier_seq_lens",
 )
 MAX_LEVELS = 6
 
@@ -130,6 +130,10 @@ def lib() -> ctypes.CDLL:
         L.gsa_decode_varlen.argtypes = [P(DecodeParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _sz, _vp]
         L.gsa_check_seq_lens.argtypes = [P(DecodeParams), P(_c_i32), P(_c_i32)]
+        L.gsa_decode_hier_varlen.argtypes = [P(HierParams)] + [_vp] * 11 + [_sz, _vp]
+        L.gsa_decode_hier_varlen.restype = _c_i32
+        L.gsa_check_hier_seq_lens.argtypes = [P(HierParams), P(_c_i32), P(_c_i32)]
+        L.gsa_check_hier_seq_lens.restype = _c_i32
         L.gsa_gist_prefill.argtypes = [P(GistParams), _vp, _vp, _vp, _vp, _vp]
         L.gsa_cache_append.argtypes = [P(AppendParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.gsa_profile_events.argtypes = [P(_vp), _c_i32]
@@ -562,6 +566,73 @@ def gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int,
                                      _ptr(sel2) if topk2 > 0 else None,
                                      _ptr(sel1) if topk1 > 0 else None, _ptr(ws), _nbytes(ws),
                                      s.cuda_stream), "gsa_decode_hier")
+    return out, lse, sel2, sel1
+
+
+def check_hier_seq_lens(p: HierParams, seq_n_raw, seq_n_gist) -> None:
+    """Host check of per-sequence lengths against a two-level call's parameters."""
+    n = (_c_i32 * p.base.batch)(*[int(x) for x in seq_n_raw])
+    m = (_c_i32 * p.base.batch)(*[int(x) for x in seq_n_gist])
+    _check(lib().gsa_check_hier_seq_lens(ctypes.byref(p), n, m), "gsa_check_hier_seq_lens")
+
+
+def gsa_decode_hier_varlen(q, k_cache, v_cache, k_l2, v_l2, *, seq_n_raw, seq_n_gist, chunk: int,
+                           fanout: int, topk1: int, topk2: int, tail: int, n_raw: Optional[int] = None,
+                           n_gist: Optional[int] = None, scale: float = 0.0, out=None, lse=None,
+                           sel2=None, sel1=None, workspace=None, stream=None, want_lse: bool = True,
+                           want_sel: bool = True):
+    """Two-level decode of sequences of different lengths. Caches
+    [B,Hkv,cap,D] (sequence b: its first seq_n_raw[b] + seq_n_gist[b] rows);
+    k_l2, v_l2 [B,Hkv,M2,D] with M2 = n_gist // fanout (sequence b: its first
+    seq_n_gist[b] // fanout rows).
+
+    seq_n_raw / seq_n_gist: host sequences (checked with
+    gsa_check_hier_seq_lens, then copied to the device) or device int32
+    tensors [B], used as given (then n_raw= and n_gist=, the batch's largest
+    values, are required). Returns (out, lse, sel2, sel1) as gsa_decode_hier.
+    """
+    import torch
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    on_dev = isinstance(seq_n_raw, torch.Tensor) and seq_n_raw.is_cuda
+    if on_dev:
+        if n_raw is None or n_gist is None:
+            raise ValueError("device length arrays need n_raw= and n_gist= (the batch's largest)")
+        sn, sm = seq_n_raw, seq_n_gist
+    else:
+        hn = [int(x) for x in (seq_n_raw.tolist() if hasattr(seq_n_raw, "tolist") else seq_n_raw)]
+        hm = [int(x) for x in (seq_n_gist.tolist() if hasattr(seq_n_gist, "tolist") else seq_n_gist)]
+        if len(hn) != B or len(hm) != B:
+            raise ValueError("one length per sequence")
+        n_raw = max(hn) if n_raw is None else n_raw
+        n_gist = max(hm) if n_gist is None else n_gist
+    base = decode_params(B, Hq, Hkv, D, n_raw, n_gist, chunk, topk1, tail, scale, _dtype_code(q),
+                         row_capacity=cap)
+    p = hier_params(base, fanout, topk2)
+    if k_l2.shape[2] != n_gist // fanout:
+        raise ValueError(f"level-2 arrays hold {k_l2.shape[2]} rows per slab, expected {n_gist // fanout}")
+    if not on_dev:
+        check_hier_seq_lens(p, hn, hm)
+    s, on_s = _on_stream(stream, dev)
+    with on_s:
+        if not on_dev:
+            sn = torch.tensor(hn, dtype=torch.int32, device=dev)
+            sm = torch.tensor(hm, dtype=torch.int32, device=dev)
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
+        if lse is None and want_lse:
+            lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        if want_sel:
+            if sel2 is None:
+                sel2 = torch.empty(B, Hkv, max(topk2, 0), dtype=torch.int32, device=dev)
+            if sel1 is None:
+                sel1 = torch.empty(B, Hkv, max(topk1, 0), dtype=torch.int32, device=dev)
+        ws = _workspace(workspace, hier_workspace_size(p), dev)
+        _check(lib().gsa_decode_hier_varlen(ctypes.byref(p), _ptr(sn), _ptr(sm), _ptr(q), _ptr(k_cache),
+                                            _ptr(v_cache), _ptr(k_l2), _ptr(v_l2), _ptr(out), _ptr(lse),
+                                            _ptr(sel2) if topk2 > 0 and want_sel else None,
+                                            _ptr(sel1) if topk1 > 0 and want_sel else None, _ptr(ws),
+                                            _nbytes(ws), s.cuda_stream), "gsa_decode_hier_varlen")
     return out, lse, sel2, sel1
 
 

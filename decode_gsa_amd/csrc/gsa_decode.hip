@@ -171,6 +171,7 @@ struct SeqLens {
   const int32_t* m;
   int32_t Hkv;
   int32_t k;              // the call's top-k (a sequence needs k <= m)
+  int32_t G2, k2;         // two-level decode: fanout and top-k2 (else 0)
 };
 
 __device__ __forceinline__ void unit_lengths(const SeqLens& sl, int unit, int64_t N, int64_t M, int32_t C,
@@ -185,6 +186,29 @@ __device__ __forceinline__ void unit_lengths(const SeqLens& sl, int unit, int64_
   if (ok) {
     *n_out = n;
     *m_out = m;
+  }
+}
+
+// Two-level decode with per-sequence lengths: the sequence's N and M as
+// unit_lengths gives them, its level-2 gists M2 = floor(M / G) (the first
+// rows of its level-2 slab) and its level-1 candidates k2 G + (M - M2 G). A
+// sequence whose lengths break a rule (unit_lengths', k2 <= M2, k1 at most
+// its candidates) runs with the call's maxima.
+__device__ __forceinline__ void hier_lengths(const SeqLens& sl, int unit, int64_t N, int64_t M, int32_t C,
+                                             int32_t T, int64_t M2, int32_t n_cand, int64_t* n_out,
+                                             int64_t* m_out, int64_t* m2_out, int32_t* nc_out) {
+  *m2_out = M2;
+  *nc_out = n_cand;
+  unit_lengths(sl, unit, N, M, C, T, n_out, m_out);
+  if (sl.n == nullptr || *m_out == M) return;   // maxima (also a sequence at the largest M)
+  const int64_t m = *m_out, m2 = m / sl.G2;
+  const int64_t nc = (int64_t)sl.k2 * sl.G2 + (m - m2 * sl.G2);
+  if (sl.k2 <= m2 && sl.k <= nc) {
+    *m2_out = m2;
+    *nc_out = (int32_t)nc;
+  } else {
+    *n_out = N;
+    *m_out = M;
   }
 }
 
@@ -2404,7 +2428,7 @@ __device__ __forceinline__ void select_cands(const Cands& c, int S, int unit, in
 }
 
 template <int G>
-__device__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16x8u (&qf)[4]);
+__device__ __forceinline__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16x8u (&qf)[4]);
 
 // HIER (kHierDescend, kHierTop): the level-2 gists (their own arrays) and the
 // tail; every workgroup hands its partial state and its top-k2 level-2
@@ -2427,7 +2451,12 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
   const int S = SPLIT ? a.S : 1;
   const int unit = blockIdx.x / S, split = blockIdx.x - unit * S;
   if constexpr (!SETS) GSA_STAMP(0);
-  if constexpr (VARLEN) unit_lengths(args.seq, unit, args.N, args.M, args.C, args.T, &a.N, &a.M);
+  const int64_t m2_slab = a.M2;   // rows of a level-2 slab (the call's M2)
+  if constexpr (VARLEN && HIER)
+    hier_lengths(args.seq, unit, args.N, args.M, args.C, args.T, args.M2, args.n_cand, &a.N, &a.M, &a.M2,
+                 &a.n_cand);
+  else if constexpr (VARLEN)
+    unit_lengths(args.seq, unit, args.N, args.M, args.C, args.T, &a.N, &a.M);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
   const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
   const PagedLds* pl = nullptr;
@@ -2466,8 +2495,9 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
   const int w0 = min(n1, split * perw), w1 = min(n1, w0 + perw);
   const int per1 = (w1 - w0 + kUW - 1) / kUW;
   if constexpr (HIER) {
-    const char* K2b = reinterpret_cast<const char*>(a.K2) + (size_t)unit * a.M2 * 256;
-    const char* V2b = reinterpret_cast<const char*>(a.V2) + (size_t)unit * a.M2 * 256;
+    // level-2 slabs hold the call's M2 rows (a sequence's own first)
+    const char* K2b = reinterpret_cast<const char*>(a.K2) + (size_t)unit * m2_slab * 256;
+    const char* V2b = reinterpret_cast<const char*>(a.V2) + (size_t)unit * m2_slab * 256;
     unit_stream<kUKL2>(Kb, Vb, min(w1, w0 + w * per1), min(w1, w0 + (w + 1) * per1), a, qf, st, ring, L.scores,
                        L.sel, w0, K2b, V2b);
     GSA_STAMP(1);
@@ -2658,7 +2688,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
 // candidates, the level-1 candidates (group scores kept in LDS), their
 // selection, the chosen chunks' raw rows, and the merge of every partial.
 template <int G>
-__device__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16x8u (&qf)[4]) {
+__device__ __forceinline__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16x8u (&qf)[4]) {
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
   const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
@@ -2896,10 +2926,11 @@ gsa_status_t run_unit_levels(const LevelsPlan& lp, const void* q, const void* K,
   return launch_status("gsa_decode_levels launch");
 }
 
+// seq_n, seq_m: per-sequence lengths (device arrays), or null.
 template <int G>
 gsa_status_t run_unit_hier(const HierPlan& hp, const void* q, const void* K, const void* V, const void* K2,
                            const void* V2, float* out, float* lse, int32_t* sel2, int32_t* sel1, char* ws,
-                           hipStream_t st) {
+                           hipStream_t st, const int32_t* seq_n = nullptr, const int32_t* seq_m = nullptr) {
   const DecodePlan& pl = hp.base;
   UnitArgs u{};
   u.q = q; u.K = K; u.V = V; u.out = out; u.lse = lse; u.sel = pl.k > 0 ? sel1 : nullptr;
@@ -2913,8 +2944,12 @@ gsa_status_t run_unit_hier(const HierPlan& hp, const void* q, const void* K, con
   u.s2 = reinterpret_cast<float*>(ws + hp.off_s2); u.s2_stride = hp.s2_stride;
   u.sel2 = hp.k2 > 0 ? sel2 : nullptr;
   u.cnt = ctrl_of(ws, hp.off_ctrl, 0);
+  u.seq = SeqLens{seq_n, seq_m, pl.Hkv, pl.k, hp.G, hp.k2};
   prof_begin_call();
-  prof_launch((unit_kernel<G, kHierDescend>), dim3(pl.units * hp.unit_S), dim3(kUW * 64), 0, st, u);
+  if (seq_n != nullptr)
+    prof_launch((unit_kernel<G, kHierDescend, false, true>), dim3(pl.units * hp.unit_S), dim3(kUW * 64), 0, st, u);
+  else
+    prof_launch((unit_kernel<G, kHierDescend>), dim3(pl.units * hp.unit_S), dim3(kUW * 64), 0, st, u);
   return launch_status("gsa_decode_hier launch");
 }
 
@@ -3176,6 +3211,40 @@ extern "C" gsa_status_t gsa_decode_hier(const gsa_hier_params* p, const void* q,
   return dispatch<HierRunner>(hp.base.dtype, hp.base.D, hp.base.g, hp, q, k_cache, v_cache, k_l2, v_l2,
                               out, lse, sel2, sel1, reinterpret_cast<char*>(workspace),
                               reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" gsa_status_t gsa_decode_hier_varlen(const gsa_hier_params* p, const int32_t* seq_n_raw,
+                                               const int32_t* seq_n_gist, const void* q, const void* k_cache,
+                                               const void* v_cache, const void* k_l2, const void* v_l2,
+                                               float* out, float* lse, int32_t* sel2, int32_t* sel1,
+                                               void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  prof_begin_call();
+  HierPlan hp;
+  gsa_status_t s = plan_hier(p, &hp);
+  if (s != GSA_OK) return s;
+  if (hp.unit_S == 0)
+    return fail(GSA_ERR_UNSUPPORTED,
+                "variable-length two-level decode runs on the bf16, head_dim 128 path (topk, topk2 <= 64, at most "
+                "4096 level-1 candidates)");
+  const bool need_l2 = hp.M2 > 0;
+  if ((s = check_ptr(seq_n_raw, "seq_n_raw")) != GSA_OK || (s = check_ptr(seq_n_gist, "seq_n_gist")) != GSA_OK ||
+      (s = check_ptr(q, "q")) != GSA_OK || (s = check_ptr(k_cache, "k_cache")) != GSA_OK ||
+      (s = check_ptr(v_cache, "v_cache")) != GSA_OK || (s = check_ptr(k_l2, "k_l2", !need_l2)) != GSA_OK ||
+      (s = check_ptr(v_l2, "v_l2", !need_l2)) != GSA_OK || (s = check_ptr(out, "out")) != GSA_OK ||
+      (s = check_ptr(lse, "lse", true)) != GSA_OK || (s = check_ptr(sel2, "sel2", true)) != GSA_OK ||
+      (s = check_ptr(sel1, "sel1", true)) != GSA_OK)
+    return s;
+  if ((s = check_workspace(workspace, workspace_bytes, hp.total)) != GSA_OK) return s;
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  switch (hp.base.g) {
+    case 1: return run_unit_hier<1>(hp, q, k_cache, v_cache, k_l2, v_l2, out, lse, sel2, sel1, ws, hs, seq_n_raw, seq_n_gist);
+    case 2: return run_unit_hier<2>(hp, q, k_cache, v_cache, k_l2, v_l2, out, lse, sel2, sel1, ws, hs, seq_n_raw, seq_n_gist);
+    case 4: return run_unit_hier<4>(hp, q, k_cache, v_cache, k_l2, v_l2, out, lse, sel2, sel1, ws, hs, seq_n_raw, seq_n_gist);
+    case 8: return run_unit_hier<8>(hp, q, k_cache, v_cache, k_l2, v_l2, out, lse, sel2, sel1, ws, hs, seq_n_raw, seq_n_gist);
+  }
+  return fail(GSA_ERR_UNSUPPORTED, "no kernel for g=%d", hp.base.g);
 }
 
 extern "C" gsa_status_t gsa_decode_levels_workspace_size(const gsa_levels_params* p, size_t* bytes) {

@@ -614,6 +614,25 @@ extern "C" gsa_status_t gsa_check_seq_lens(const gsa_decode_params* p, const int
   return GSA_OK;
 }
 
+extern "C" gsa_status_t gsa_check_hier_seq_lens(const gsa_hier_params* p, const int32_t* seq_n_raw,
+                                                const int32_t* seq_n_gist) {
+  gsa::clear_error();
+  gsa::HierPlan h;
+  gsa_status_t s = gsa::plan_hier(p, &h);
+  if (s != GSA_OK) return s;
+  if ((s = gsa_check_seq_lens(&p->base, seq_n_raw, seq_n_gist)) != GSA_OK) return s;
+  for (int32_t b = 0; b < p->base.batch; ++b) {
+    const int64_t m = seq_n_gist[b], m2 = m / p->fanout;
+    const int64_t nc = (int64_t)p->topk2 * p->fanout + (m - m2 * p->fanout);
+    if (p->topk2 > m2 || p->base.topk > nc)
+      return gsa::fail(GSA_ERR_INVALID_ARG,
+                       "sequence %d: n_gist=%lld gives %lld level-2 gists and %lld level-1 candidates: need "
+                       "topk2=%d <= level-2 gists and topk=%d <= candidates",
+                       b, (long long)m, (long long)m2, (long long)nc, p->topk2, p->base.topk);
+  }
+  return GSA_OK;
+}
+
 extern "C" gsa_status_t gsa_check_pages(const gsa_paged_params* p, const int32_t* block_table,
                                         const int32_t* seq_n_raw, const int32_t* seq_n_gist,
                                         const int32_t* extra_rows) {

@@ -258,6 +258,37 @@ gsa_status_t gsa_decode_hier(const gsa_hier_params* p, const void* q, const void
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Variable-length two-level decode: gsa_decode_hier's step for sequences of
+ * different lengths.
+ * Source: the two-level rule of gsa_decode_hier (explainer 'Hierarchical
+ * Extension (H-GSA)'), applied per sequence, as gsa_decode_varlen applies
+ * gsa_decode's.
+ * p->base.n_raw and p->base.n_gist are the batch's largest values N, M
+ * (they size the workspace: gsa_decode_hier_workspace_size(p) applies, and
+ * the launches); p->base.row_capacity (or N + M) is the cache slab stride
+ * and M2 = floor(M / G) the level-2 slab stride: sequence b's M2_b =
+ * floor(M_b / G) level-2 gists are the first rows of its [M2, D] slab.
+ * seq_n_raw, seq_n_gist: device arrays [B] int32 (16-byte aligned), the
+ * rules of gsa_decode_varlen plus topk2 <= M2_b and base.topk <= topk2*G +
+ * (M_b - M2_b*G); gsa_check_hier_seq_lens validates a host copy. A sequence
+ * that breaks them runs with (N, M) instead, so no read leaves its slabs.
+ * Other arguments as gsa_decode_hier. Runs on the bf16, head_dim 128 path
+ * (topk, topk2 <= 64, at most 4096 level-1 candidates; else
+ * GSA_ERR_UNSUPPORTED); gist_set must be 0. One launch.
+ * ---------------------------------------------------------------------- */
+gsa_status_t gsa_decode_hier_varlen(const gsa_hier_params* p, const int32_t* seq_n_raw,
+                                    const int32_t* seq_n_gist, const void* q, const void* k_cache,
+                                    const void* v_cache, const void* k_l2, const void* v_l2, float* out,
+                                    float* lse, int32_t* sel2, int32_t* sel1, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Host check of per-sequence lengths (host arrays [p->base.batch]) against
+ * gsa_decode_hier_varlen's rules: GSA_OK, or GSA_ERR_INVALID_ARG naming the
+ * first sequence that breaks one (gsa_last_error). */
+gsa_status_t gsa_check_hier_seq_lens(const gsa_hier_params* p, const int32_t* seq_n_raw,
+                                     const int32_t* seq_n_gist);
+
+/* ------------------------------------------------------------------------
  * L-level decode (gists of gists of gists ...).
  * Source: gist.science explainer, 'Hierarchical Extension (H-GSA)' and
  * 'Coarse-to-Fine Selection' (multi-resolution access: the selection walks

@@ -465,6 +465,39 @@ def test_decode_varlen_rejections(L):
 
 
 
+def hier_varlen_params(**kw):
+    """batch 3, N 1024, M 64, C 16, k1 4, G 8, k2 2: M2 = 8, candidates 16."""
+    base = varlen_params(topk=kw.pop("topk", 4), **{k: kw.pop(k) for k in list(kw) if k in ("head_dim", "dtype")})
+    return gsa.hier_params(base, kw.pop("fanout", 8), kw.pop("topk2", 2))
+
+
+# the varlen rules, plus topk2 = 2 <= floor(m / 8) and topk = 4 <= 2*8 + m mod 8
+@pytest.mark.parametrize("n,m,status", [
+    ([1024, 500, 260], [64, 31, 16], OK),
+    ([1024, 500, 256], [64, 31, 15], INVALID),     # 15 gists: one level-2 gist < topk2
+    ([1024, 500, 40], [64, 31, 2], INVALID),       # no level-2 gist
+    ([1024, 1024, 300], [64, 64, 18], OK),         # 2 level-2 gists and 2 orphans
+    ([1025, 500, 260], [64, 31, 16], INVALID),     # the varlen rules still hold
+])
+def test_check_hier_seq_lens(L, n, m, status):
+    p = hier_varlen_params()
+    arr = lambda v: (ctypes.c_int32 * 3)(*v)
+    st = L.gsa_check_hier_seq_lens(ctypes.byref(p), arr(n), arr(m))
+    assert st == status, L.gsa_last_error()
+
+
+def test_decode_hier_varlen_rejections(L):
+    p = hier_varlen_params()
+    need = ctypes.c_size_t(0)
+    assert L.gsa_decode_hier_workspace_size(ctypes.byref(p), ctypes.byref(need)) == OK
+    call = lambda pp, sn, sm: L.gsa_decode_hier_varlen(ctypes.byref(pp), sn, sm, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                       FAKE, None, None, None, FAKE, need.value, None)
+    assert call(p, None, FAKE) == INVALID and "seq_n_raw" in L.gsa_last_error().decode()
+    assert call(p, FAKE, FAKE + 4) == INVALID                       # misaligned
+    assert call(hier_varlen_params(dtype=gsa.GSA_F32), FAKE, FAKE) == UNSUPPORTED
+    assert call(hier_varlen_params(head_dim=64), FAKE, FAKE) == UNSUPPORTED
+
+
 # ------------------------------------------- documented sets vs validation ---
 
 def _block(text, start, end):
