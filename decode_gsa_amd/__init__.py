@@ -35,6 +35,7 @@ __all__ = [
     "gsa_decode_levels", "levels_workspace_size", "gsa_decode_varlen", "check_seq_lens",
     "launches", "gsa_decode_noalloc", "PagedParams", "paged_params", "paged_workspace_size",
     "check_pages", "gsa_decode_paged", "gsa_decode_hier_varlen", "check_hier_seq_lens",
+    "PrefillVarlenParams", "gsa_prefill_varlen", "check_prefill_seqs",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -51,6 +52,7 @@ EXPORTED_SYMBOLS = (
     "gsa_decode_launches", "gsa_decode_hier_launches", "gsa_decode_levels_launches",
     "gsa_prefill_launches", "gsa_decode_noalloc", "gsa_decode_paged_workspace_size",
     "gsa_decode_paged", "gsa_check_pages", "gsa_decode_hier_varlen", "gsa_check_hier_seq_lens",
+    "gsa_prefill_varlen_workspace_size", "gsa_prefill_varlen", "gsa_check_prefill_seqs",
 )
 MAX_LEVELS = 6
 
@@ -84,6 +86,10 @@ class PrefillParams(ctypes.Structure):
                 ("chunk", _c_i32), ("topk", _c_i32), ("window", _c_i32), ("n_raw", _c_i64),
                 ("n_gist", _c_i64), ("q_start", _c_i64), ("n_q", _c_i64), ("scale", _c_f32),
                 ("dtype", _c_i32), ("row_capacity", _c_i64)]
+
+
+class PrefillVarlenParams(ctypes.Structure):
+    _fields_ = [("base", PrefillParams), ("batch", _c_i32)]
 
 
 class GistParams(ctypes.Structure):
@@ -134,6 +140,12 @@ def lib() -> ctypes.CDLL:
         L.gsa_decode_hier_varlen.restype = _c_i32
         L.gsa_check_hier_seq_lens.argtypes = [P(HierParams), P(_c_i32), P(_c_i32)]
         L.gsa_check_hier_seq_lens.restype = _c_i32
+        L.gsa_prefill_varlen_workspace_size.argtypes = [P(PrefillVarlenParams), P(_sz)]
+        L.gsa_prefill_varlen_workspace_size.restype = _c_i32
+        L.gsa_prefill_varlen.argtypes = [P(PrefillVarlenParams)] + [_vp] * 7 + [_sz, _vp]
+        L.gsa_prefill_varlen.restype = _c_i32
+        L.gsa_check_prefill_seqs.argtypes = [P(PrefillVarlenParams), P(_c_i32)]
+        L.gsa_check_prefill_seqs.restype = _c_i32
         L.gsa_gist_prefill.argtypes = [P(GistParams), _vp, _vp, _vp, _vp, _vp]
         L.gsa_cache_append.argtypes = [P(AppendParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.gsa_profile_events.argtypes = [P(_vp), _c_i32]
@@ -702,6 +714,63 @@ def gsa_prefill_blocksparse(q, k_cache, v_cache, *, chunk: int, topk: int, windo
                                              _ptr(sel) if topk > 0 else None, _ptr(ws),
                                              _nbytes(ws), s.cuda_stream),
                "gsa_prefill_blocksparse")
+    return out, sel
+
+
+def check_prefill_seqs(p: PrefillVarlenParams, seqs) -> None:
+    """Host check of a batched prefill's per-sequence (n_raw, n_gist, q_start, n_q)."""
+    flat = [int(x) for row in seqs for x in row]
+    arr = (_c_i32 * len(flat))(*flat)
+    _check(lib().gsa_check_prefill_seqs(ctypes.byref(p), arr), "gsa_check_prefill_seqs")
+
+
+def gsa_prefill_varlen(q, k_cache, v_cache, *, seqs, chunk: int, topk: int, window: int,
+                       n_raw: Optional[int] = None, n_gist: Optional[int] = None, scale: float = 0.0,
+                       out=None, sel=None, workspace=None, stream=None, want_sel: bool = True):
+    """Causal block-sparse prefill of B sequences of different lengths in one
+    call. q [B,Hq,n_q,D] (sequence b's query i at position q_start_b + i in
+    row i); caches [B,Hkv,R,D] (bf16).
+
+    seqs: host rows (n_raw, n_gist, q_start, n_q) per sequence (checked with
+    gsa_check_prefill_seqs, then copied to the device) or a device int32
+    tensor [B, 4] used as given (then n_raw= and n_gist=, the batch's
+    largest, are required). Returns (out [B,Hq,n_q,D] fp32, sel [B,Hkv,n_q,k]
+    int32 or None); rows past a sequence's n_q are not written.
+    """
+    import torch
+    B, Hq, n_q, D = q.shape
+    Hkv, R = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    on_dev = isinstance(seqs, torch.Tensor) and seqs.is_cuda
+    if on_dev:
+        if n_raw is None or n_gist is None:
+            raise ValueError("a device seqs array needs n_raw= and n_gist= (the batch's largest)")
+        sd = seqs
+    else:
+        rows = [[int(x) for x in r] for r in (seqs.tolist() if hasattr(seqs, "tolist") else seqs)]
+        if len(rows) != B or any(len(r) != 4 for r in rows):
+            raise ValueError("one (n_raw, n_gist, q_start, n_q) row per sequence")
+        n_raw = max(r[0] for r in rows) if n_raw is None else n_raw
+        n_gist = max(r[1] for r in rows) if n_gist is None else n_gist
+    base = prefill_params(Hq, Hkv, D, chunk, topk, window, n_raw, n_gist, 0, n_q, scale,
+                          _dtype_code(q), R)
+    p = PrefillVarlenParams(base, B)
+    if not on_dev:
+        check_prefill_seqs(p, rows)
+    nbytes = _sz(0)
+    _check(lib().gsa_prefill_varlen_workspace_size(ctypes.byref(p), ctypes.byref(nbytes)),
+           "gsa_prefill_varlen_workspace_size")
+    s, on_s = _on_stream(stream, dev)
+    with on_s:
+        if not on_dev:
+            sd = torch.tensor(rows, dtype=torch.int32, device=dev)
+        out = torch.empty(B, Hq, n_q, D, dtype=torch.float32, device=dev) if out is None else out
+        if sel is None and want_sel:
+            sel = torch.empty(B, Hkv, n_q, max(topk, 0), dtype=torch.int32, device=dev)
+        ws = _workspace(workspace, nbytes.value, dev)
+        _check(lib().gsa_prefill_varlen(ctypes.byref(p), _ptr(sd), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(out), _ptr(sel) if topk > 0 and want_sel else None, _ptr(ws),
+                                        _nbytes(ws), s.cuda_stream), "gsa_prefill_varlen")
     return out, sel
 
 

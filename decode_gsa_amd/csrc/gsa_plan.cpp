@@ -384,7 +384,24 @@ gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* o) {
   if ((int64_t)d.n_blocks * d.Hkv > (1 << 30)) return fail(GSA_ERR_UNSUPPORTED, "prefill: too many blocks");
   // workspace: the selection [Hkv][n_q][k] handed from the select to the attend kernel
   d.total = align_up(sizeof(int32_t) * (size_t)d.Hkv * (size_t)d.n_q * (size_t)d.k);
+  d.B = 1;
+  d.seqs = nullptr;
   *o = d;
+  return GSA_OK;
+}
+
+gsa_status_t plan_prefill_varlen(const gsa_prefill_varlen_params* p, PrefillPlan* o) {
+  if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->batch < 1) return fail(GSA_ERR_INVALID_ARG, "batch=%d must be >= 1", p->batch);
+  if (p->base.q_start != 0)
+    return fail(GSA_ERR_INVALID_ARG, "base.q_start=%lld must be 0 (each sequence's start is in its lengths)",
+                (long long)p->base.q_start);
+  gsa_status_t s = plan_prefill(&p->base, o);
+  if (s != GSA_OK) return s;
+  const int64_t wgs = (int64_t)o->n_blocks * o->Hkv * (o->g == 8 ? 2 : 1);
+  if ((int64_t)p->batch * wgs > (1 << 30)) return fail(GSA_ERR_UNSUPPORTED, "prefill: too many blocks");
+  o->B = p->batch;
+  o->total = align_up(sizeof(int32_t) * (size_t)p->batch * (size_t)o->Hkv * (size_t)o->n_q * (size_t)o->k);
   return GSA_OK;
 }
 
@@ -610,6 +627,27 @@ extern "C" gsa_status_t gsa_check_seq_lens(const gsa_decode_params* p, const int
                        "sequence %d: n_raw=%lld, n_gist=%lld break 1 <= n <= %lld, %d <= m <= %lld, "
                        "0 <= n - m*C <= C, n - m*C <= tail=%d <= n",
                        b, (long long)n, (long long)m, (long long)p->n_raw, p->topk, (long long)p->n_gist, p->tail);
+  }
+  return GSA_OK;
+}
+
+extern "C" gsa_status_t gsa_check_prefill_seqs(const gsa_prefill_varlen_params* p, const int32_t* seqs) {
+  gsa::clear_error();
+  gsa::PrefillPlan d;
+  gsa_status_t s = gsa::plan_prefill_varlen(p, &d);
+  if (s != GSA_OK) return s;
+  if (!seqs) return gsa::fail(GSA_ERR_INVALID_ARG, "seqs is NULL");
+  const int64_t C = p->base.chunk;
+  for (int32_t b = 0; b < p->batch; ++b) {
+    const int64_t n = seqs[4 * b], m = seqs[4 * b + 1], qs = seqs[4 * b + 2], nq = seqs[4 * b + 3];
+    const bool ok = n >= 1 && n <= p->base.n_raw && m >= 0 && m <= p->base.n_gist && m * C <= n && n <= m * C + C &&
+                    qs >= 0 && nq >= 0 && nq <= p->base.n_q && qs + nq <= n;
+    if (!ok)
+      return gsa::fail(GSA_ERR_INVALID_ARG,
+                       "sequence %d: (n_raw=%lld, n_gist=%lld, q_start=%lld, n_q=%lld) break 1 <= n <= %lld, "
+                       "m <= %lld, 0 <= n - m*C <= C, 0 <= q_start, 0 <= n_q <= %lld, q_start + n_q <= n",
+                       b, (long long)n, (long long)m, (long long)qs, (long long)nq, (long long)p->base.n_raw,
+                       (long long)p->base.n_gist, (long long)p->base.n_q);
   }
   return GSA_OK;
 }

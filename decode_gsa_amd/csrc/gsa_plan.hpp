@@ -205,6 +205,12 @@ struct PrefillPlan {
   float scale;
   int32_t n_blocks;     // query blocks of kQBlock queries
   size_t total;
+  // a batch of sequences (gsa_prefill_varlen): B sequences, each with its
+  // lengths at seqs[4 b ..] (device); n_q (the rows per head of q, out and
+  // the selection) and N, M are the batch's largest. B = 1, seqs = null for
+  // one sequence.
+  int32_t B;
+  const int32_t* seqs;
 };
 
 constexpr int kQBlock = 64;
@@ -215,6 +221,7 @@ constexpr int32_t kPrefillMaxGist = 262144;
 constexpr int32_t kPrefillMaxK = 64;
 
 gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* out);
+gsa_status_t plan_prefill_varlen(const gsa_prefill_varlen_params* p, PrefillPlan* out);
 // Gist-token queries as prefill queries at positions mC + C - 1 (stride C),
 // k = 0, W = C.
 gsa_status_t plan_gist(const gsa_gist_params* p, PrefillPlan* out);

@@ -243,9 +243,42 @@ __device__ __forceinline__ void wave_lds_sync() {
 // Blocks go out last first: under the causal order a later block sees more
 // gists, so the longest workgroups start first and the short ones fill in
 // behind them (a CU that ends a long block early takes a short one).
-__device__ __forceinline__ void wg_coords(int n_blocks, int Hkv, int* kvh, int* blk) {
+// A batch of sequences of different lengths (gsa_prefill_varlen): sequence
+// b's (n_raw, n_gist, q_start, n_q) at seqs[4 b ..], its workgroups the
+// consecutive range [b wgs, (b + 1) wgs) of the grid, its q / K / V / out /
+// selection rows `*_bs` elements after sequence b - 1's.
+struct SeqBatch {
+  const int32_t* seqs;    // [B][4] device array, or null (one sequence)
+  int32_t wgs;            // workgroups per sequence
+  int32_t n_max, m_max;   // the call's largest n_raw, n_gist (the slabs hold N + M rows)
+  int64_t q_bs, kv_bs, out_bs, sel_bs;
+};
+
+// The sequence of this workgroup: its lengths replace the call's and the
+// returned offsets move the base pointers to its rows. False for a sequence
+// whose lengths break the rules (it gets no work) and for a query block past
+// its queries. *x becomes the workgroup's index inside its sequence.
+__device__ __forceinline__ bool seq_of(const SeqBatch& sb, int C, int q_ld, int* x, int* M, int* q_start, int* n_q,
+                                       int64_t* b_out) {
+  if (sb.seqs == nullptr) {
+    *b_out = 0;
+    return true;
+  }
+  const int b = *x / sb.wgs;
+  *x -= b * sb.wgs;
+  const int4 v = *reinterpret_cast<const int4*>(sb.seqs + 4 * b);
+  const int64_t n = v.x, m = v.y, qs = v.z, nq = v.w;
+  const bool ok = n >= 1 && n <= sb.n_max && m >= 0 && m <= sb.m_max && m * C <= n && n <= m * C + C &&
+                  qs >= 0 && nq >= 0 && nq <= q_ld && qs + nq <= n;
+  *M = (int)m;
+  *q_start = (int)qs;
+  *n_q = (int)nq;
+  *b_out = b;
+  return ok;
+}
+
+__device__ __forceinline__ void wg_coords(int x, int n_blocks, int Hkv, int* kvh, int* blk) {
   const int total = n_blocks * Hkv;
-  int x = (int)blockIdx.x;
   if (total % 8 == 0) x = (x % 8) * (total / 8) + x / 8;
   *kvh = x / n_blocks;
   *blk = n_blocks - 1 - x % n_blocks;
@@ -297,8 +330,10 @@ struct SelArgs {
   int64_t R;
   int32_t M, C, k, Hkv, n_blocks, q_start, n_q;
   float score_mul;        // scale / g
-  int32_t* sel_ws;        // [Hkv][n_q][k]
-  int32_t* sel_out;       // [Hkv][n_q][k] or null
+  int32_t* sel_ws;        // [Hkv][q_ld][k]
+  int32_t* sel_out;       // [Hkv][q_ld][k] or null
+  int32_t q_ld;           // query rows per head in q and sel (n_q of one sequence)
+  SeqBatch sb;            // a batch of sequences, or none
 };
 
 // Each lane keeps a list of CAP candidate entries of its query: entry e of
@@ -566,8 +601,17 @@ template <int G, int KMAX>
 __global__ __launch_bounds__(kSelThreads, KMAX <= 32 ? 2 : 1) void prefill_select(SelArgs a) {
   __shared__ __attribute__((aligned(16))) SelLds<SelCap<KMAX>::CAP> L;
   constexpr int kCap = SelCap<KMAX>::CAP;
-  int kvh, blk;
-  wg_coords(a.n_blocks, a.Hkv, &kvh, &blk);
+  int kvh, blk, wx = (int)blockIdx.x;
+  int64_t sq;
+  if (!seq_of(a.sb, a.C, a.q_ld, &wx, &a.M, &a.q_start, &a.n_q, &sq)) return;
+  wg_coords(wx, a.n_blocks, a.Hkv, &kvh, &blk);
+  if (blk * kQB >= a.n_q) return;   // past this sequence's queries (uniform)
+  if (sq > 0) {
+    a.q = reinterpret_cast<const char*>(a.q) + sq * a.sb.q_bs * 2;
+    a.K = reinterpret_cast<const char*>(a.K) + sq * a.sb.kv_bs * 2;
+    a.sel_ws += sq * a.sb.sel_bs;
+    if (a.sel_out) a.sel_out += sq * a.sb.sel_bs;
+  }
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int qi = lane & 15, jg = lane >> 4;
   const int qloc = 16 * w + qi;
@@ -581,7 +625,7 @@ __global__ __launch_bounds__(kSelThreads, KMAX <= 32 ? 2 : 1) void prefill_selec
   const int e_lo = min(a.M, (a.q_start + blk * kQB + 16 * w) / a.C);
 
   bf16x8 qh[4], ql[4];
-  load_qbar<G>(reinterpret_cast<const char*>(a.q) + (int64_t)kvh * G * a.n_q * kRowBytes, a.n_q, t_idx, valid,
+  load_qbar<G>(reinterpret_cast<const char*>(a.q) + (int64_t)kvh * G * a.q_ld * kRowBytes, a.q_ld, t_idx, valid,
                jg, qh, ql);
   const char* Kh = reinterpret_cast<const char*>(a.K) + (int64_t)kvh * a.R * kRowBytes;
 
@@ -670,7 +714,7 @@ __global__ __launch_bounds__(kSelThreads, KMAX <= 32 ? 2 : 1) void prefill_selec
   for (int p = 0; p < KMAX; ++p)
     ids[p] = p < tot ? L.ent[p >> 2][64 * w + qi + 16 * (p & 3)].y : 0xffffffffu;
   if (valid) {
-    const int64_t o = ((int64_t)kvh * a.n_q + t_idx) * a.k;
+    const int64_t o = ((int64_t)kvh * a.q_ld + t_idx) * a.k;
 #pragma unroll
     for (int e = 0; e < (KMAX + 3) / 4; ++e) {
       if (e < pos) {
@@ -718,6 +762,8 @@ struct AttArgs {
   int64_t R;
   int32_t M, C, k, W, Hkv, n_blocks, q_start, n_q;
   int32_t q_stride;       // query i sits at position q_start + i * q_stride
+  int32_t q_ld;           // query rows per head in q, out and sel
+  SeqBatch sb;            // a batch of sequences, or none
   float scale_log2;
   // query heads per kv-head = kv_div * G: each kv-head's heads go to kv_div
   // workgroups of G heads each (head group v = kv-head v / kv_div)
@@ -945,8 +991,18 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
   using S = AttShape<G>;
   constexpr int H = S::HPW, NT = S::NT;
   __shared__ __attribute__((aligned(16))) AttLds L;
-  int hg, blk;
-  wg_coords(a.n_blocks, a.Hkv * a.kv_div, &hg, &blk);
+  int hg, blk, wx = (int)blockIdx.x;
+  int64_t sq;
+  if (!seq_of(a.sb, a.C, a.q_ld, &wx, &a.M, &a.q_start, &a.n_q, &sq)) return;
+  wg_coords(wx, a.n_blocks, a.Hkv * a.kv_div, &hg, &blk);
+  if (blk * kQB >= a.n_q) return;   // past this sequence's queries (uniform)
+  if (sq > 0) {
+    a.q = reinterpret_cast<const char*>(a.q) + sq * a.sb.q_bs * 2;
+    a.K = reinterpret_cast<const char*>(a.K) + sq * a.sb.kv_bs * 2;
+    a.V = reinterpret_cast<const char*>(a.V) + sq * a.sb.kv_bs * 2;
+    a.out += sq * a.sb.out_bs;
+    a.sel += sq * a.sb.sel_bs;
+  }
   const int kvh = hg / a.kv_div;        // the kv-head of head group hg (G query heads)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int qi = lane & 15, jg = lane >> 4;
@@ -967,7 +1023,7 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
   const int nwords = (E + 31) / 32;
   for (int i = tid; i < nwords; i += NT) L.bitmap[i] = 0u;
   __syncthreads();
-  const int32_t* sb = a.sel + ((int64_t)kvh * a.n_q + (int64_t)blk * kQB) * a.k;
+  const int32_t* sb = a.sel + ((int64_t)kvh * a.q_ld + (int64_t)blk * kQB) * a.k;
   for (int pr = tid; pr < nq_blk * a.k; pr += NT) {
     const int m = sb[pr];
     if (m >= 0 && m < E) atomicOr(&L.bitmap[m >> 5], 1u << (m & 31));
@@ -1023,7 +1079,7 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
   __syncthreads();
 
   bf16x8 qf[H][4];
-  load_qfrag<H>(reinterpret_cast<const char*>(a.q) + (int64_t)hg * G * a.n_q * kRowBytes, a.n_q, t_idx,
+  load_qfrag<H>(reinterpret_cast<const char*>(a.q) + (int64_t)hg * G * a.q_ld * kRowBytes, a.q_ld, t_idx,
                 valid, h0, jg, qf);
   const char* Kh = reinterpret_cast<const char*>(a.K) + (int64_t)kvh * a.R * kRowBytes;
   const char* Vh = reinterpret_cast<const char*>(a.V) + (int64_t)kvh * a.R * kRowBytes;
@@ -1055,7 +1111,7 @@ __global__ __launch_bounds__(AttShape<G>::NT) void prefill_attend(AttArgs a) {
 #pragma unroll
   for (int h = 0; h < H; ++h) {
     const float inv = 1.f / fsum4(st.l[h]);
-    float* o = a.out + (((int64_t)hg * G + h0 + h) * a.n_q + t_idx) * kD;
+    float* o = a.out + (((int64_t)hg * G + h0 + h) * a.q_ld + t_idx) * kD;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const float4 v = make_float4(st.o[h][dt][0] * inv, st.o[h][dt][1] * inv, st.o[h][dt][2] * inv,
@@ -1075,7 +1131,16 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
   prof_begin_call();
   if (pl.n_q == 0) return GSA_OK;
   int32_t* wsel = reinterpret_cast<int32_t*>(ws);
-  const int grid = pl.n_blocks * pl.Hkv;
+  const int grid = pl.n_blocks * pl.Hkv;   // per sequence
+  // a batch of sequences: each one's rows lie these many elements apart
+  SeqBatch sb{};
+  sb.seqs = pl.seqs;
+  sb.n_max = (int32_t)pl.N;
+  sb.m_max = (int32_t)pl.M;
+  sb.q_bs = (int64_t)pl.Hq * pl.n_q * kD;
+  sb.kv_bs = (int64_t)pl.Hkv * pl.R * kD;
+  sb.out_bs = (int64_t)pl.Hq * pl.n_q * kD;
+  sb.sel_bs = (int64_t)pl.Hkv * pl.n_q * pl.k;
   if (pl.k > 0) {
     SelArgs s{};
     s.q = q; s.K = K; s.R = pl.R;
@@ -1083,10 +1148,13 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
     s.q_start = (int32_t)pl.q_start; s.n_q = (int32_t)pl.n_q;
     s.score_mul = pl.scale / G;
     s.sel_ws = wsel; s.sel_out = sel;
+    s.q_ld = (int32_t)pl.n_q;
+    s.sb = sb;
+    s.sb.wgs = grid;
     if (pl.k <= 32)
-      prof_launch((prefill_select<G, 32>), dim3(grid), dim3(kSelThreads), 0, stream, s);
+      prof_launch((prefill_select<G, 32>), dim3(grid * pl.B), dim3(kSelThreads), 0, stream, s);
     else
-      prof_launch((prefill_select<G, 64>), dim3(grid), dim3(kSelThreads), 0, stream, s);
+      prof_launch((prefill_select<G, 64>), dim3(grid * pl.B), dim3(kSelThreads), 0, stream, s);
   }
   AttArgs t{};
   t.q = q; t.K = K; t.V = V; t.out = out; t.sel = wsel; t.R = pl.R;
@@ -1094,7 +1162,10 @@ gsa_status_t run_prefill(const PrefillPlan& pl, const void* q, const void* K, co
   t.q_start = (int32_t)pl.q_start; t.n_q = (int32_t)pl.n_q; t.q_stride = pl.q_stride;
   t.scale_log2 = pl.scale * kLog2e;
   t.kv_div = G / AG;
-  prof_launch((prefill_attend<AG>), dim3(grid * (G / AG)), dim3(AttShape<AG>::NT), 0, stream, t);
+  t.q_ld = (int32_t)pl.n_q;
+  t.sb = sb;
+  t.sb.wgs = grid * (G / AG);
+  prof_launch((prefill_attend<AG>), dim3(grid * (G / AG) * pl.B), dim3(AttShape<AG>::NT), 0, stream, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
     return fail(GSA_ERR_HIP, "%s launch: %s", pl.q_stride == 1 ? "gsa_prefill_blocksparse" : "gsa_gist_prefill",
@@ -1141,6 +1212,42 @@ extern "C" gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, con
     case 8: return run_prefill<8>(pl, q, k_cache, v_cache, out, sel, ws, st);
   }
   return fail(GSA_ERR_UNSUPPORTED, "prefill: %d query heads per kv-head not in {1, 2, 4}", pl.g);
+}
+
+extern "C" gsa_status_t gsa_prefill_varlen_workspace_size(const gsa_prefill_varlen_params* p, size_t* bytes) {
+  clear_error();
+  if (!bytes) return fail(GSA_ERR_INVALID_ARG, "bytes is NULL");
+  PrefillPlan pl;
+  gsa_status_t s = plan_prefill_varlen(p, &pl);
+  if (s != GSA_OK) return s;
+  *bytes = pl.total;
+  return GSA_OK;
+}
+
+extern "C" gsa_status_t gsa_prefill_varlen(const gsa_prefill_varlen_params* p, const int32_t* seqs,
+                                           const void* q, const void* k_cache, const void* v_cache, float* out,
+                                           int32_t* sel, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  prof_begin_call();
+  PrefillPlan pl;
+  gsa_status_t s = plan_prefill_varlen(p, &pl);
+  if (s != GSA_OK) return s;
+  const bool none = pl.n_q == 0;   // no queries: q, out (and sel) may be NULL
+  if ((s = check_ptr(seqs, "seqs")) != GSA_OK || (s = check_ptr(q, "q", none)) != GSA_OK ||
+      (s = check_ptr(k_cache, "k_cache")) != GSA_OK || (s = check_ptr(v_cache, "v_cache")) != GSA_OK ||
+      (s = check_ptr(out, "out", none)) != GSA_OK || (s = check_ptr(sel, "sel", true)) != GSA_OK)
+    return s;
+  if ((s = check_workspace(workspace, workspace_bytes, pl.total)) != GSA_OK) return s;
+  pl.seqs = seqs;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  switch (pl.g) {
+    case 1: return run_prefill<1>(pl, q, k_cache, v_cache, out, sel, ws, st);
+    case 2: return run_prefill<2>(pl, q, k_cache, v_cache, out, sel, ws, st);
+    case 4: return run_prefill<4>(pl, q, k_cache, v_cache, out, sel, ws, st);
+    case 8: return run_prefill<8>(pl, q, k_cache, v_cache, out, sel, ws, st);
+  }
+  return fail(GSA_ERR_UNSUPPORTED, "prefill: %d query heads per kv-head not in {1, 2, 4, 8}", pl.g);
 }
 
 extern "C" gsa_status_t gsa_gist_prefill(const gsa_gist_params* p, const void* q, const void* k_cache,

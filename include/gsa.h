@@ -389,6 +389,43 @@ gsa_status_t gsa_prefill_blocksparse(const gsa_prefill_params* p, const void* q,
                                      void* stream);
 
 /* ------------------------------------------------------------------------
+ * Batched prefill of sequences of different lengths: gsa_prefill_blocksparse
+ * for B sequences in one call.
+ * Source: the selection rule of 'Training Procedure: Selective Finetuning'
+ * (explainer) applied to each sequence on its own, as gsa_decode_varlen
+ * applies the decode rule per sequence.
+ * base.n_raw / base.n_gist are the batch's largest N, M (the cache slabs
+ * hold base.row_capacity rows, or N + M); base.n_q is the most queries of
+ * any sequence and the row stride of q, out and sel; base.q_start must be
+ * 0. Other base fields as gsa_prefill_blocksparse (the same limits).
+ * seqs: device array [B][4] int32, 16-byte aligned: sequence b's (N_b, M_b,
+ * q_start_b, n_q_b) with 1 <= N_b <= N, M_b <= M, 0 <= N_b - M_b*C <= C,
+ * 0 <= q_start_b, 0 <= n_q_b <= base.n_q, q_start_b + n_q_b <= N_b. A
+ * sequence that breaks these gets no work (its rows of out and sel are not
+ * written); gsa_check_prefill_seqs validates a host copy.
+ * q       [B, Hq, n_q, D]      sequence b's query i (position q_start_b + i) in row i
+ * k_cache [B, Hkv, R, D]       sequence b's interleaved cache
+ * v_cache [B, Hkv, R, D]
+ * out     [B, Hq, n_q, D] fp32 (rows past a sequence's n_q_b are not written)
+ * sel     [B, Hkv, n_q, k] int32 or NULL (rows past n_q_b not written)
+ * workspace: gsa_prefill_varlen_workspace_size bytes (no zero-fill needed).
+ * GSA_ERR_INVALID_ARG / GSA_ERR_UNSUPPORTED as gsa_prefill_blocksparse, and
+ * for batch < 1 or base.q_start != 0. Launches as gsa_prefill_blocksparse.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  gsa_prefill_params base; /* the batch's largest lengths, q_start = 0 */
+  int32_t batch;           /* B >= 1 */
+} gsa_prefill_varlen_params;
+
+gsa_status_t gsa_prefill_varlen_workspace_size(const gsa_prefill_varlen_params* p, size_t* bytes);
+gsa_status_t gsa_prefill_varlen(const gsa_prefill_varlen_params* p, const int32_t* seqs, const void* q,
+                                const void* k_cache, const void* v_cache, float* out, int32_t* sel,
+                                void* workspace, size_t workspace_bytes, void* stream);
+/* Host check of the per-sequence lengths (host array [B][4]): GSA_OK, or
+ * GSA_ERR_INVALID_ARG naming the first sequence that breaks a rule. */
+gsa_status_t gsa_check_prefill_seqs(const gsa_prefill_varlen_params* p, const int32_t* seqs);
+
+/* ------------------------------------------------------------------------
  * Gist-token attention of one sequence (the step that builds the cache).
  * Source: gist.science explainer, section 2 'Key Concepts: Interleaved Gist
  * Tokens' and 'Technical Innovations' (the gist causal mask), slide deck

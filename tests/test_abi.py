@@ -49,6 +49,8 @@ int main(void) {
   printf("gsa_gist_params %zu\n", sizeof(gsa_gist_params));
   printf("gsa_levels_params %zu\n", sizeof(gsa_levels_params));
   printf("gsa_paged_params %zu\n", sizeof(gsa_paged_params));
+  printf("gsa_prefill_varlen_params %zu\n", sizeof(gsa_prefill_varlen_params));
+  F(gsa_prefill_varlen_params, batch);
   F(gsa_paged_params, page_chunks); F(gsa_paged_params, max_pages); F(gsa_paged_params, n_pages);
   F(gsa_paged_params, max_extra);
   printf("GSA_MAX_LEVELS %d\n", GSA_MAX_LEVELS);
@@ -81,6 +83,7 @@ int main(void) {
     assert int(got["gsa_gist_params"]) == ctypes.sizeof(gsa.GistParams)
     assert int(got["gsa_levels_params"]) == ctypes.sizeof(gsa.LevelsParams)
     assert int(got["gsa_paged_params"]) == ctypes.sizeof(gsa.PagedParams)
+    assert int(got["gsa_prefill_varlen_params"]) == ctypes.sizeof(gsa.PrefillVarlenParams)
     assert int(got["GSA_MAX_LEVELS"]) == gsa.MAX_LEVELS
     assert int(got["gsa_append_params"]) == ctypes.sizeof(gsa.AppendParams)
     assert [int(got[f"GSA_GISTS_{n}"]) for n in ("ALL", "SELECTED", "NONE")] == \
@@ -91,7 +94,8 @@ int main(void) {
             cls = {"gsa_decode_params": gsa.DecodeParams, "gsa_hier_params": gsa.HierParams,
                    "gsa_prefill_params": gsa.PrefillParams, "gsa_gist_params": gsa.GistParams,
                    "gsa_append_params": gsa.AppendParams, "gsa_levels_params": gsa.LevelsParams,
-                   "gsa_paged_params": gsa.PagedParams}[t]
+                   "gsa_paged_params": gsa.PagedParams,
+                   "gsa_prefill_varlen_params": gsa.PrefillVarlenParams}[t]
             assert getattr(cls, m).offset == int(val), key
 
 
@@ -496,6 +500,47 @@ def test_decode_hier_varlen_rejections(L):
     assert call(p, FAKE, FAKE + 4) == INVALID                       # misaligned
     assert call(hier_varlen_params(dtype=gsa.GSA_F32), FAKE, FAKE) == UNSUPPORTED
     assert call(hier_varlen_params(head_dim=64), FAKE, FAKE) == UNSUPPORTED
+
+
+def prefill_varlen_params(batch=3, **kw):
+    p = good_prefill(q_start=0, n_q=512, **kw)
+    return gsa.PrefillVarlenParams(p, batch)
+
+
+# N 4096, M 256, C 16, n_q 512: 1 <= n <= 4096, m <= 256, 16 m <= n <= 16 m + 16,
+# 0 <= q_start, 0 <= n_q <= 512, q_start + n_q <= n
+@pytest.mark.parametrize("rows,status", [
+    ([[4096, 256, 3584, 512], [1000, 62, 900, 100], [17, 1, 0, 17]], OK),
+    ([[4096, 256, 3584, 512], [1000, 62, 900, 100], [16, 1, 0, 0]], OK),     # no queries
+    ([[4096, 256, 3584, 512], [1000, 62, 901, 100], [17, 1, 0, 17]], INVALID),   # runs past n
+    ([[4096, 256, 3584, 512], [1000, 63, 900, 100], [17, 1, 0, 17]], INVALID),   # gist of an incomplete chunk
+    ([[4096, 256, 3000, 513], [1000, 62, 900, 100], [17, 1, 0, 17]], INVALID),   # more than base.n_q
+    ([[4097, 256, 3584, 512], [1000, 62, 900, 100], [17, 1, 0, 17]], INVALID),   # above base.n_raw
+    ([[4096, 256, -1, 5], [1000, 62, 900, 100], [17, 1, 0, 17]], INVALID),
+])
+def test_check_prefill_seqs(L, rows, status):
+    p = prefill_varlen_params()
+    flat = [x for r in rows for x in r]
+    st = L.gsa_check_prefill_seqs(ctypes.byref(p), (ctypes.c_int32 * len(flat))(*flat))
+    assert st == status, L.gsa_last_error()
+
+
+def test_prefill_varlen_validation(L):
+    n = ctypes.c_size_t(0)
+    assert L.gsa_prefill_varlen_workspace_size(ctypes.byref(prefill_varlen_params()), ctypes.byref(n)) == OK
+    assert n.value >= 3 * 2 * 512 * 4 * 4                     # [B, Hkv, n_q, k] int32
+    assert L.gsa_prefill_varlen_workspace_size(ctypes.byref(prefill_varlen_params(batch=0)),
+                                               ctypes.byref(n)) == INVALID
+    bad = gsa.PrefillVarlenParams(good_prefill(q_start=1, n_q=512), 3)
+    assert L.gsa_prefill_varlen_workspace_size(ctypes.byref(bad), ctypes.byref(n)) == INVALID
+    assert L.gsa_prefill_varlen_workspace_size(ctypes.byref(prefill_varlen_params(head_dim=64)),
+                                               ctypes.byref(n)) == UNSUPPORTED
+    p = prefill_varlen_params()
+    assert L.gsa_prefill_varlen_workspace_size(ctypes.byref(p), ctypes.byref(n)) == OK
+    call = lambda seqs: L.gsa_prefill_varlen(ctypes.byref(p), seqs, FAKE, FAKE, FAKE, FAKE, None, FAKE, n.value,
+                                             None)
+    assert call(None) == INVALID and "seqs" in L.gsa_last_error().decode()
+    assert call(FAKE + 4) == INVALID                          # misaligned
 
 
 # ------------------------------------------- documented sets vs validation ---
