@@ -79,6 +79,11 @@ Readings where the pages are silent (each also listed in the design notes):
      the top); the set holds every top-level gist, every candidate of the
      levels below, the raw rows of the selected chunks and the tail. L = 2 is
      R7.
+  R20 the slide 17 rules under the hierarchy: the rule decides which gists
+     join the attention set, the routing is unchanged. "selected" keeps the
+     chosen level-1 chunks' gists only (level-2 and candidate gists route
+     but are not attended), "none" keeps no gist; both attend the chosen
+     chunks' raw rows and the tail as R7 does.
 
 Parity pins for every function here live in tests/test_oracle.py.
 """
@@ -341,8 +346,8 @@ def decode_paged_unit(qg: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, pa
 def decode_hier_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, K2: np.ndarray,
                      V2: np.ndarray, *, n_raw: int, n_gist: int, chunk: int,
                      fanout: int, topk1: int, topk2: int, tail: int,
-                     scale: Optional[float] = None) -> Dict[str, np.ndarray]:
-    """One unit of two-level (gist-of-gist) decode (R7).
+                     scale: Optional[float] = None, gist_set: str = "all") -> Dict[str, np.ndarray]:
+    """One unit of two-level (gist-of-gist) decode (R7; gist_set: R20).
 
     K2, V2: [M2, D] level-2 gists, M2 = floor(M / G).
     Returns out, lse, wsum, sel2 [k2], sel1 [k1] (ascending), cand1 (sorted
@@ -363,6 +368,10 @@ def decode_hier_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, K2: np.ndarra
         raise ValueError("topk1 exceeds the number of level-1 candidates")
     if not (N - M * C <= T <= N):
         raise ValueError("tail must cover the raw tokens after the last gist")
+    if gist_set not in GIST_SETS:
+        raise ValueError(f"gist_set must be one of {GIST_SETS}")
+    if gist_set != "all" and topk1 == 0 and T == 0:
+        raise ValueError("the attention set would be empty")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
 
     # level 2: score the meta-gists, keep the top-k2 groups
@@ -373,16 +382,24 @@ def decode_hier_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, K2: np.ndarra
     cand_rows = [gist_row_index(m, C) for m in cand]
     S1 = _group_scores(qg, _f64(K[cand_rows]), scale) if cand else np.zeros(0)
     sel1 = topk_ascending(S1, cand, topk1)
-    # attention set: every level-2 gist + candidate gists + unfolded + tail
-    A = set(cand_rows)
+    # attention set: the gists of the rule (all: every level-2 gist and every
+    # candidate gist; selected: the chosen chunks' gists; none) + unfolded +
+    # tail
+    if gist_set == "all":
+        A = set(cand_rows)
+    elif gist_set == "selected":
+        A = {gist_row_index(m, C) for m in sel1}
+    else:
+        A = set()
     for m in sel1:
         for j in range(C):
             A.add(raw_row_index(m * C + j, C, M))
     for p in range(N - T, N):
         A.add(raw_row_index(p, C, M))
     rows = np.array(sorted(A), dtype=np.int64)
-    keys = np.concatenate([_f64(K2), _f64(K[rows])], axis=0)
-    vals = np.concatenate([_f64(V2), _f64(V[rows])], axis=0)
+    n2 = M2 if gist_set == "all" else 0
+    keys = np.concatenate([_f64(K2[:n2]), _f64(K[rows])], axis=0)
+    vals = np.concatenate([_f64(V2[:n2]), _f64(V[rows])], axis=0)
     out, lse, wsum = _softmax_attend(qg, keys, vals, scale)
     return {"out": out, "lse": lse, "wsum": wsum,
             "sel2": np.array(sel2, dtype=np.int64), "sel1": np.array(sel1, dtype=np.int64),

@@ -361,6 +361,48 @@ def test_hier_coarse_to_fine_bruteforce(seed):
     assert gist_rows <= set(h["rows"].tolist())
 
 
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+def test_hier_rules_with_every_group_reduce_to_single_level_rules(gist_set):
+    """R20: with every group chosen and no orphan, the level-1 candidates are
+    all gists, so the two-level step under a rule is the single-level step
+    under that rule (no level-2 row joins the set)."""
+    rng = np.random.default_rng(14)
+    g, D, C, M, G, k1, T = 2, 8, 4, 16, 4, 3, 6
+    qg, K, V, K2, V2, N, R, M2 = _hier_inputs(rng, g, D, C, M, G)
+    h = oracle.decode_hier_unit(qg, K, V, K2, V2, n_raw=N, n_gist=M, chunk=C, fanout=G,
+                                topk1=k1, topk2=M2, tail=T, gist_set=gist_set)
+    s = oracle.decode_unit(qg, K, V, n_raw=N, n_gist=M, chunk=C, topk=k1, tail=T, gist_set=gist_set)
+    assert list(h["sel1"]) == list(s["sel"])
+    assert list(h["rows"]) == list(s["rows"])
+    np.testing.assert_allclose(h["out"], s["out"], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+def test_hier_rules_attention_set_by_mask(gist_set):
+    """R20 against a dense masked softmax: routing through two groups of a
+    hierarchy with orphans, the set holds the chosen chunks' raw rows and the
+    tail, plus (selected) the chosen chunks' gist rows; no level-2 row."""
+    rng = np.random.default_rng(15)
+    g, D, C, M, G, k2, k1, T = 3, 8, 4, 23, 4, 2, 3, 5     # M2 = 5, 3 orphans
+    qg, K, V, K2, V2, N, R, M2 = _hier_inputs(rng, g, D, C, M, G, r=2)
+    h = oracle.decode_hier_unit(qg, K, V, K2, V2, n_raw=N, n_gist=M, chunk=C, fanout=G,
+                                topk1=k1, topk2=k2, tail=T, gist_set=gist_set)
+    sel = set(h["sel1"].tolist())
+    mask = np.zeros(R, bool)
+    for x in range(R):
+        kind, v = row_kind(x, C, M)
+        if kind == "gist":
+            mask[x] = gist_set == "selected" and v in sel
+        elif v >= N - T or (v // C < M and v // C in sel):
+            mask[x] = True
+    ref = sdpa(qg, K, V, mask, 1 / math.sqrt(D))
+    np.testing.assert_allclose(h["out"], ref, rtol=0, atol=1e-12)
+    # the routing is the default rule's
+    a = oracle.decode_hier_unit(qg, K, V, K2, V2, n_raw=N, n_gist=M, chunk=C, fanout=G,
+                                topk1=k1, topk2=k2, tail=T)
+    assert list(a["sel1"]) == list(h["sel1"]) and list(a["sel2"]) == list(h["sel2"])
+
+
 def test_hier_orphan_gist_is_always_a_candidate():
     rng = np.random.default_rng(13)
     g, D, C, M, G = 1, 4, 2, 7, 3            # groups {0,1,2},{3,4,5}; orphan 6
