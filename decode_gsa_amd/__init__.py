@@ -549,8 +549,10 @@ def gsa_decode_varlen(q, k_cache, v_cache, *, seq_n_raw, seq_n_gist, chunk: int,
 def gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int, topk1: int,
                     topk2: int, tail: int, n_gist: Optional[int] = None, scale: float = 0.0,
                     out=None, lse=None, sel2=None, sel1=None, workspace=None, stream=None,
-                    want_lse: bool = True, want_sel: bool = True, n_raw: Optional[int] = None):
-    """Two-level (gist-of-gist) decode. k_l2, v_l2 [B,Hkv,M2,D].
+                    want_lse: bool = True, want_sel: bool = True, n_raw: Optional[int] = None,
+                    gist_set: str = "all"):
+    """Two-level (gist-of-gist) decode. k_l2, v_l2 [B,Hkv,M2,D]. gist_set:
+    which gists are attended ("all"; "selected": the chosen chunks'; "none").
 
     Returns (out, lse, sel2 [B,Hkv,k2], sel1 [B,Hkv,k1]).
     """
@@ -558,8 +560,10 @@ def gsa_decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int,
     B, Hq, D = q.shape
     Hkv, R = k_cache.shape[1], k_cache.shape[2]
     N, M, cap = _geometry(R, chunk, n_gist, n_raw)
+    if gist_set not in GIST_SETS:
+        raise ValueError(f"gist_set must be one of {tuple(GIST_SETS)}")
     base = decode_params(B, Hq, Hkv, D, N, M, chunk, topk1, tail, scale, _dtype_code(q),
-                         row_capacity=cap)
+                         gist_set=GIST_SETS[gist_set], row_capacity=cap)
     p = hier_params(base, fanout, topk2)
     dev = q.device
     s, on_s = _on_stream(stream, dev)
@@ -592,7 +596,7 @@ def gsa_decode_hier_varlen(q, k_cache, v_cache, k_l2, v_l2, *, seq_n_raw, seq_n_
                            fanout: int, topk1: int, topk2: int, tail: int, n_raw: Optional[int] = None,
                            n_gist: Optional[int] = None, scale: float = 0.0, out=None, lse=None,
                            sel2=None, sel1=None, workspace=None, stream=None, want_lse: bool = True,
-                           want_sel: bool = True):
+                           want_sel: bool = True, gist_set: str = "all"):
     """Two-level decode of sequences of different lengths. Caches
     [B,Hkv,cap,D] (sequence b: its first seq_n_raw[b] + seq_n_gist[b] rows);
     k_l2, v_l2 [B,Hkv,M2,D] with M2 = n_gist // fanout (sequence b: its first
@@ -619,8 +623,10 @@ def gsa_decode_hier_varlen(q, k_cache, v_cache, k_l2, v_l2, *, seq_n_raw, seq_n_
             raise ValueError("one length per sequence")
         n_raw = max(hn) if n_raw is None else n_raw
         n_gist = max(hm) if n_gist is None else n_gist
+    if gist_set not in GIST_SETS:
+        raise ValueError(f"gist_set must be one of {tuple(GIST_SETS)}")
     base = decode_params(B, Hq, Hkv, D, n_raw, n_gist, chunk, topk1, tail, scale, _dtype_code(q),
-                         row_capacity=cap)
+                         gist_set=GIST_SETS[gist_set], row_capacity=cap)
     p = hier_params(base, fanout, topk2)
     if k_l2.shape[2] != n_gist // fanout:
         raise ValueError(f"level-2 arrays hold {k_l2.shape[2]} rows per slab, expected {n_gist // fanout}")

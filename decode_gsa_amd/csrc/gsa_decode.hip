@@ -1939,7 +1939,9 @@ enum { kUKGists = 0, kUKUnfold = 1, kUKL2 = 2, kUKCand = 3, kUKScore = 4, kUKSet
 // PAGED: Kb / Vb are the unit's kv-head base in page 0 of the pools, rows are
 // translated through the staged block table (pl), and kUKGists streams the
 // sequence's extra rows after the tail.
-template <int KIND, bool PAGED = false>
+// SCORE_ONLY: the scored items are scored but not attended (the selection
+// rules under the hierarchy); kUKL2's tail rows are still attended.
+template <int KIND, bool PAGED = false, bool SCORE_ONLY = false>
 __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const char* __restrict__ Vb, int i0,
                                             int i1, const UnitArgs& a, const bf16x8u (&qf)[4], UState& st,
                                             char* ring, float* lds_scores, const int32_t* lds_sel,
@@ -2140,6 +2142,10 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     bool ok[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) ok[r] = kScored ? i_base + r < i1 : row_of(i_base + r) >= 0;
+    if constexpr (SCORE_ONLY) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ok[r] = ok[r] && i_base + r >= n_scored;
+    }
     if (kScored) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -2427,7 +2433,7 @@ __device__ __forceinline__ void select_cands(const Cands& c, int S, int unit, in
   __syncthreads();
 }
 
-template <int G>
+template <int G, bool SETS = false>
 __device__ __forceinline__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16x8u (&qf)[4]);
 
 // HIER (kHierDescend, kHierTop): the level-2 gists (their own arrays) and the
@@ -2498,8 +2504,9 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
     // level-2 slabs hold the call's M2 rows (a sequence's own first)
     const char* K2b = reinterpret_cast<const char*>(a.K2) + (size_t)unit * m2_slab * 256;
     const char* V2b = reinterpret_cast<const char*>(a.V2) + (size_t)unit * m2_slab * 256;
-    unit_stream<kUKL2>(Kb, Vb, min(w1, w0 + w * per1), min(w1, w0 + (w + 1) * per1), a, qf, st, ring, L.scores,
-                       L.sel, w0, K2b, V2b);
+    // selection rules (SETS): the level-2 gists route but are not attended
+    unit_stream<kUKL2, false, SETS>(Kb, Vb, min(w1, w0 + w * per1), min(w1, w0 + (w + 1) * per1), a, qf, st, ring,
+                                    L.scores, L.sel, w0, K2b, V2b);
     GSA_STAMP(1);
     float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
     unit_combine<G>(L, st, w, nullptr, nullptr, part_u + (size_t)split * a.part_stride);
@@ -2509,7 +2516,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
     if constexpr (HIER == kHierDescend) {
       if (!arrive_last(a.cnt + (size_t)unit * kCtrlUnitWords, (uint32_t)S, &L.s_old)) return;
       GSA_STAMP(6);
-      hier_descent<G>(a, L, unit, qf);
+      hier_descent<G, SETS>(a, L, unit, qf);
     }
     return;
   }
@@ -2687,7 +2694,10 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
 // unit's last stream workgroup): the level-2 selection among the splits'
 // candidates, the level-1 candidates (group scores kept in LDS), their
 // selection, the chosen chunks' raw rows, and the merge of every partial.
-template <int G>
+// SETS: the selection rules (R20): the candidates are scored only, and the
+// set's rows after the routing are the chosen chunks' raw rows and, with
+// gist_set 1, their gists (the tail came with the level-2 stream).
+template <int G, bool SETS>
 __device__ __forceinline__ void hier_descent(const UnitArgs& a, UnitLds& L, int unit, const bf16x8u (&qf)[4]) {
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
@@ -2712,7 +2722,8 @@ __device__ __forceinline__ void hier_descent(const UnitArgs& a, UnitLds& L, int 
   // level 1: every candidate gist (scored), four wave shares
   const int nc = a.n_cand;
   const int perc = (nc + kUW - 1) / kUW;
-  unit_stream<kUKCand>(Kb, Vb, min(nc, w * perc), min(nc, (w + 1) * perc), a, qf, st, ring, L.scores, L.sel2);
+  unit_stream<kUKCand, false, SETS>(Kb, Vb, min(nc, w * perc), min(nc, (w + 1) * perc), a, qf, st, ring, L.scores,
+                                     L.sel2);
   GSA_STAMP(10);
   if (a.k > 0) {
     __syncthreads();   // every candidate score is in LDS, every ring idle
@@ -2731,10 +2742,19 @@ __device__ __forceinline__ void hier_descent(const UnitArgs& a, UnitLds& L, int 
       L.sel[tid] = c < kg ? L.sel2[c / a.G2] * a.G2 + c % a.G2 : (int)(a.M2 * a.G2) + (c - kg);
     }
     __syncthreads();
-    const int items = a.k * a.C;
-    const int per2 = (items + kUW - 1) / kUW;
-    unit_stream<kUKUnfold>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
-                           L.sel);
+    if constexpr (SETS) {
+      // the chosen chunks' raw rows, then their gists under rule 1 (kUKSet's
+      // items before the tail)
+      const int items = a.k * a.C + (a.gist_set == 1 ? a.k : 0);
+      const int per2 = (items + kUW - 1) / kUW;
+      unit_stream<kUKSet>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
+                          L.sel);
+    } else {
+      const int items = a.k * a.C;
+      const int per2 = (items + kUW - 1) / kUW;
+      unit_stream<kUKUnfold>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
+                             L.sel);
+    }
     GSA_STAMP(12);
   }
   float* part_u = a.part + (size_t)unit * a.NP * a.part_stride;
@@ -2945,11 +2965,18 @@ gsa_status_t run_unit_hier(const HierPlan& hp, const void* q, const void* K, con
   u.sel2 = hp.k2 > 0 ? sel2 : nullptr;
   u.cnt = ctrl_of(ws, hp.off_ctrl, 0);
   u.seq = SeqLens{seq_n, seq_m, pl.Hkv, pl.k, hp.G, hp.k2};
+  u.gist_set = pl.gist_set;
   prof_begin_call();
-  if (seq_n != nullptr)
-    prof_launch((unit_kernel<G, kHierDescend, false, true>), dim3(pl.units * hp.unit_S), dim3(kUW * 64), 0, st, u);
+  const bool sets = pl.gist_set != GSA_GISTS_ALL;
+  const dim3 grid(pl.units * hp.unit_S), block(kUW * 64);
+  if (seq_n != nullptr && sets)
+    prof_launch((unit_kernel<G, kHierDescend, true, true>), grid, block, 0, st, u);
+  else if (seq_n != nullptr)
+    prof_launch((unit_kernel<G, kHierDescend, false, true>), grid, block, 0, st, u);
+  else if (sets)
+    prof_launch((unit_kernel<G, kHierDescend, true>), grid, block, 0, st, u);
   else
-    prof_launch((unit_kernel<G, kHierDescend>), dim3(pl.units * hp.unit_S), dim3(kUW * 64), 0, st, u);
+    prof_launch((unit_kernel<G, kHierDescend>), grid, block, 0, st, u);
   return launch_status("gsa_decode_hier launch");
 }
 

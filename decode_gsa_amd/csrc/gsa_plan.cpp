@@ -269,8 +269,6 @@ gsa_status_t plan_paged(const gsa_paged_params* p, DecodePlan* o) {
 
 gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
   if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
-  if (p->base.gist_set != GSA_GISTS_ALL)
-    return fail(GSA_ERR_UNSUPPORTED, "two-level decode attends every gist: base.gist_set must be 0");
   gsa_status_t s = plan_decode(&p->base, &o->base);
   if (s != GSA_OK) return s;
   HierPlan h{};
@@ -314,6 +312,10 @@ gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
       if (h.NP < h.unit_S + 1) h.NP = h.unit_S + 1;   // level-2 stream partials + the rest's
     }
   }
+  if (d.gist_set != GSA_GISTS_ALL && h.unit_S == 0)
+    return fail(GSA_ERR_UNSUPPORTED,
+                "two-level decode with gist_set=%d runs on the bf16, head_dim 128 path (topk, topk2 <= 64, at "
+                "most 4096 level-1 candidates)", d.gist_set);
   h.s2_stride = (h.M2 + 63) / 64 * 64;
   h.sc_stride = d.k > 0 ? (h.n_cand + 63) / 64 * 64 : 0;
   size_t off = 0;

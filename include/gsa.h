@@ -85,9 +85,12 @@ typedef struct {
                           GSA_GISTS_NONE (2, raw tokens only: SR-only).
                           1 and 2 need k > 0 or T > 0 (a non-empty set);
                           gsa_decode and gsa_decode_noalloc run them on
-                          every shape they accept. gsa_decode_varlen,
-                          _paged, _hier and _levels require 0 (they attend
-                          every gist of every level). */
+                          every shape they accept; gsa_decode_hier and
+                          gsa_decode_hier_varlen on their bf16, head_dim
+                          128 path (else GSA_ERR_UNSUPPORTED), the rule
+                          deciding which gists are attended while the
+                          routing stays the same. gsa_decode_varlen,
+                          _paged and _levels require 0. */
   int64_t row_capacity; /* rows allocated per (sequence, kv-head) in the
                           caches, the stride between their [R, D] blocks:
                           0 means exactly R = N + M; else it must be
@@ -236,7 +239,10 @@ gsa_status_t gsa_check_seq_lens(const gsa_decode_params* p, const int32_t* seq_n
  * The M - M2*G level-1 gists no group covers are always candidates.
  * Attention set: every level-2 gist, every candidate level-1 gist (all G
  * children of each chosen group, plus the ungrouped ones), the raw rows of
- * the k1 chosen chunks and the tail.
+ * the k1 chosen chunks and the tail. With base.gist_set 1 (2) the set is the
+ * chosen chunks' gists (no gist), their raw rows and the tail: the level-2
+ * and candidate gists only route (bf16, head_dim 128, topk, topk2 <= 64, at
+ * most 4096 level-1 candidates; else GSA_ERR_UNSUPPORTED).
  * ---------------------------------------------------------------------- */
 typedef struct {
   gsa_decode_params base; /* level-1 cache; base.topk = k1 */
@@ -274,7 +280,7 @@ gsa_status_t gsa_decode_hier(const gsa_hier_params* p, const void* q, const void
  * that breaks them runs with (N, M) instead, so no read leaves its slabs.
  * Other arguments as gsa_decode_hier. Runs on the bf16, head_dim 128 path
  * (topk, topk2 <= 64, at most 4096 level-1 candidates; else
- * GSA_ERR_UNSUPPORTED); gist_set must be 0. One launch.
+ * GSA_ERR_UNSUPPORTED); gist_set as gsa_decode_hier. One launch.
  * ---------------------------------------------------------------------- */
 gsa_status_t gsa_decode_hier_varlen(const gsa_hier_params* p, const int32_t* seq_n_raw,
                                     const int32_t* seq_n_gist, const void* q, const void* k_cache,

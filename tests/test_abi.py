@@ -502,6 +502,20 @@ def test_decode_hier_varlen_rejections(L):
     assert call(hier_varlen_params(head_dim=64), FAKE, FAKE) == UNSUPPORTED
 
 
+@pytest.mark.parametrize("kw,status", [
+    ({"gist_set": 1}, OK),
+    ({"gist_set": 2}, OK),
+    ({"gist_set": 2, "dtype": gsa.GSA_F32}, UNSUPPORTED),     # the split path runs every gist only
+    ({"gist_set": 1, "head_dim": 64}, UNSUPPORTED),
+    ({"gist_set": 3}, INVALID),
+    ({"gist_set": 1, "topk": 0, "tail": 0}, INVALID),         # nothing to attend
+])
+def test_hier_gist_set_validation(L, kw, status):
+    p = gsa.HierParams(good_decode(**kw), 4, 2)
+    n = ctypes.c_size_t(0)
+    assert L.gsa_decode_hier_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status, L.gsa_last_error()
+
+
 def prefill_varlen_params(batch=3, **kw):
     p = good_prefill(q_start=0, n_q=512, **kw)
     return gsa.PrefillVarlenParams(p, batch)

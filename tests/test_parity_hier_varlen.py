@@ -47,7 +47,7 @@ def make_case(c, seed):
     return q, k, v, k2, v2, n, m
 
 
-def check(c, q, k, v, k2, v2, n, m, out, lse, sel2, sel1, seqs=None):
+def check(c, q, k, v, k2, v2, n, m, out, lse, sel2, sel1, seqs=None, gist_set="all"):
     g = c["Hq"] // c["Hkv"]
     got, ref, got_l, ref_l = [], [], [], []
     for b in (range(c["B"]) if seqs is None else seqs):
@@ -55,7 +55,8 @@ def check(c, q, k, v, k2, v2, n, m, out, lse, sel2, sel1, seqs=None):
         for j in range(c["Hkv"]):
             r = oracle.decode_hier_unit(to_np(q[b, j * g:(j + 1) * g]), to_np(k[b, j, :R]), to_np(v[b, j, :R]),
                                         to_np(k2[b, j, :m2]), to_np(v2[b, j, :m2]), n_raw=n[b], n_gist=m[b],
-                                        chunk=c["C"], fanout=c["G"], topk1=c["k1"], topk2=c["k2"], tail=c["T"])
+                                        chunk=c["C"], fanout=c["G"], topk1=c["k1"], topk2=c["k2"], tail=c["T"],
+                                        gist_set=gist_set)
             np.testing.assert_array_equal(to_np(sel2[b, j]), r["sel2"], err_msg=f"level 2, sequence {b} kv-head {j}")
             np.testing.assert_array_equal(to_np(sel1[b, j]), r["sel1"], err_msg=f"level 1, sequence {b} kv-head {j}")
             got.append(to_np(out[b, j * g:(j + 1) * g]))
@@ -141,3 +142,31 @@ def test_hier_varlen_device_lengths_and_fallback(gsa):
                                     tail=c["T"])
         np.testing.assert_array_equal(to_np(sel1[bad, j]), r["sel1"])
         check_out(to_np(out[bad, j * g:(j + 1) * g]), r["out"], "bf16", f"sequence {bad}")
+
+
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+@pytest.mark.parametrize("i", [0, 1])
+def test_hier_selection_rules(gsa, gist_set, i):
+    """The slide 17 rules on the two-level decode (the rule picks which gists
+    are attended; the routing is unchanged): uniform lengths through
+    gsa_decode_hier and different lengths through gsa_decode_hier_varlen,
+    both against the oracle with the same rule."""
+    c = CASES[i]
+    say(f"hier {gist_set} {c}")
+    q, k, v, k2, v2, n, m = make_case(c, 7900 + i)
+    kw = dict(chunk=c["C"], fanout=c["G"], topk1=c["k1"], topk2=c["k2"], tail=c["T"], gist_set=gist_set)
+    out, lse, s2, s1 = gsa.gsa_decode_hier_varlen(q, k, v, k2, v2, seq_n_raw=n, seq_n_gist=m, **kw)
+    torch.cuda.synchronize()
+    err = check(c, q, k, v, k2, v2, n, m, out, lse, s2, s1, gist_set=gist_set)
+    # the longest sequence's cache for every sequence: the uniform entry point
+    b = int(np.argmax(n))
+    N, M = n[b], m[b]
+    nn, mm = [N] * c["B"], [M] * c["B"]
+    kk = k[b:b + 1].expand(c["B"], -1, -1, -1)[:, :, :N + M].contiguous()
+    vv = v[b:b + 1].expand(c["B"], -1, -1, -1)[:, :, :N + M].contiguous()
+    k2u = k2[b:b + 1].expand(c["B"], -1, -1, -1)[:, :, :M // c["G"]].contiguous()
+    v2u = v2[b:b + 1].expand(c["B"], -1, -1, -1)[:, :, :M // c["G"]].contiguous()
+    out, lse, s2, s1 = gsa.gsa_decode_hier(q, kk, vv, k2u, v2u, n_gist=M, **kw)
+    torch.cuda.synchronize()
+    err2 = check(c, q, kk, vv, k2u, v2u, nn, mm, out, lse, s2, s1, gist_set=gist_set)
+    say(f"  max err / rms = {err:.2e} (varlen), {err2:.2e} (uniform)")
