@@ -35,7 +35,8 @@ __all__ = [
     "gsa_decode_levels", "levels_workspace_size", "gsa_decode_varlen", "check_seq_lens",
     "launches", "gsa_decode_noalloc", "PagedParams", "paged_params", "paged_workspace_size",
     "check_pages", "gsa_decode_paged", "gsa_decode_hier_varlen", "check_hier_seq_lens",
-    "PrefillVarlenParams", "gsa_prefill_varlen", "check_prefill_seqs",
+    "PrefillVarlenParams", "gsa_prefill_varlen", "check_prefill_seqs", "gsa_decode_levels_varlen",
+    "check_levels_seq_lens",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
@@ -53,6 +54,7 @@ EXPORTED_SYMBOLS = (
     "gsa_prefill_launches", "gsa_decode_noalloc", "gsa_decode_paged_workspace_size",
     "gsa_decode_paged", "gsa_check_pages", "gsa_decode_hier_varlen", "gsa_check_hier_seq_lens",
     "gsa_prefill_varlen_workspace_size", "gsa_prefill_varlen", "gsa_check_prefill_seqs",
+    "gsa_decode_levels_varlen", "gsa_check_levels_seq_lens",
 )
 MAX_LEVELS = 6
 
@@ -146,6 +148,11 @@ def lib() -> ctypes.CDLL:
         L.gsa_prefill_varlen.restype = _c_i32
         L.gsa_check_prefill_seqs.argtypes = [P(PrefillVarlenParams), P(_c_i32)]
         L.gsa_check_prefill_seqs.restype = _c_i32
+        L.gsa_decode_levels_varlen.argtypes = [P(LevelsParams), _vp, _vp, _vp, _vp, _vp, P(_vp), P(_vp), _vp,
+                                               _vp, P(_vp), _vp, _vp, _sz, _vp]
+        L.gsa_decode_levels_varlen.restype = _c_i32
+        L.gsa_check_levels_seq_lens.argtypes = [P(LevelsParams), P(_c_i32), P(_c_i32)]
+        L.gsa_check_levels_seq_lens.restype = _c_i32
         L.gsa_gist_prefill.argtypes = [P(GistParams), _vp, _vp, _vp, _vp, _vp]
         L.gsa_cache_append.argtypes = [P(AppendParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp]
         L.gsa_profile_events.argtypes = [P(_vp), _c_i32]
@@ -691,6 +698,71 @@ def gsa_decode_levels(q, k_cache, v_cache, k_up, v_up, *, chunk: int, fanout: in
                                        vp, _ptr(out), _ptr(lse), sp,
                                        _ptr(sels[0]) if want_sel and topks[0] > 0 else None,
                                        _ptr(ws), _nbytes(ws), s.cuda_stream), "gsa_decode_levels")
+    return out, lse, sels
+
+
+def check_levels_seq_lens(p: LevelsParams, seq_n_raw, seq_n_gist) -> None:
+    """Host check of per-sequence lengths against an L-level call's parameters."""
+    n = (_c_i32 * p.base.batch)(*[int(x) for x in seq_n_raw])
+    m = (_c_i32 * p.base.batch)(*[int(x) for x in seq_n_gist])
+    _check(lib().gsa_check_levels_seq_lens(ctypes.byref(p), n, m), "gsa_check_levels_seq_lens")
+
+
+def gsa_decode_levels_varlen(q, k_cache, v_cache, k_up, v_up, *, seq_n_raw, seq_n_gist, chunk: int,
+                             fanout: int, topks, tail: int, n_raw: Optional[int] = None,
+                             n_gist: Optional[int] = None, scale: float = 0.0, out=None, lse=None,
+                             workspace=None, stream=None, want_lse: bool = True, want_sel: bool = True):
+    """L-level decode of sequences of different lengths. Caches [B,Hkv,cap,D]
+    (sequence b: its first seq_n_raw[b] + seq_n_gist[b] rows); k_up, v_up:
+    level l's arrays [B,Hkv,M_l,D] with M_l = n_gist // fanout^(l-1) (sequence
+    b: its first seq_n_gist[b] // fanout^(l-1) rows). seq_n_raw / seq_n_gist:
+    host sequences (checked with gsa_check_levels_seq_lens) or device int32
+    tensors [B] (then n_raw= and n_gist=, the batch's largest, are required).
+    Returns (out, lse, sels) as gsa_decode_levels.
+    """
+    import torch
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    on_dev = isinstance(seq_n_raw, torch.Tensor) and seq_n_raw.is_cuda
+    if on_dev:
+        if n_raw is None or n_gist is None:
+            raise ValueError("device length arrays need n_raw= and n_gist= (the batch's largest)")
+        sn, sm = seq_n_raw, seq_n_gist
+    else:
+        hn = [int(x) for x in (seq_n_raw.tolist() if hasattr(seq_n_raw, "tolist") else seq_n_raw)]
+        hm = [int(x) for x in (seq_n_gist.tolist() if hasattr(seq_n_gist, "tolist") else seq_n_gist)]
+        if len(hn) != B or len(hm) != B:
+            raise ValueError("one length per sequence")
+        n_raw = max(hn) if n_raw is None else n_raw
+        n_gist = max(hm) if n_gist is None else n_gist
+    topks = [int(k) for k in topks]
+    if len(k_up) != len(topks) - 1 or len(v_up) != len(topks) - 1:
+        raise ValueError("one k per level and one array pair per level above the first")
+    base = decode_params(B, Hq, Hkv, D, n_raw, n_gist, chunk, topks[0], tail, scale, _dtype_code(q),
+                         row_capacity=cap)
+    p = levels_params(base, fanout, topks[1:])
+    if not on_dev:
+        check_levels_seq_lens(p, hn, hm)
+    s, on_s = _on_stream(stream, dev)
+    with on_s:
+        if not on_dev:
+            sn = torch.tensor(hn, dtype=torch.int32, device=dev)
+            sm = torch.tensor(hm, dtype=torch.int32, device=dev)
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=dev) if out is None else out
+        if lse is None and want_lse:
+            lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+        sels = ([torch.empty(B, Hkv, max(k, 0), dtype=torch.int32, device=dev) for k in topks]
+                if want_sel else None)
+        n_up = len(k_up)
+        kp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in k_up])
+        vp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in v_up])
+        sp = (_vp * n_up)(*[_ptr(t) if t.numel() else None for t in sels[1:]]) if want_sel else None
+        ws = _workspace(workspace, levels_workspace_size(p), dev)
+        _check(lib().gsa_decode_levels_varlen(ctypes.byref(p), _ptr(sn), _ptr(sm), _ptr(q), _ptr(k_cache),
+                                              _ptr(v_cache), kp, vp, _ptr(out), _ptr(lse), sp,
+                                              _ptr(sels[0]) if want_sel and topks[0] > 0 else None,
+                                              _ptr(ws), _nbytes(ws), s.cuda_stream), "gsa_decode_levels_varlen")
     return out, lse, sels
 
 

@@ -2789,12 +2789,41 @@ struct LevelArgs {
 
 // TOP: the workgroup also streams the top level and the tail itself (top
 // level <= kUMaxGist gists, its scores kept in LDS): one launch per call.
-template <int G, bool TOP = false>
+// VARLEN (with TOP): per-sequence lengths; sequence b's level l holds
+// floor(M_b / G^(l-1)) gists, the first rows of its slab of that level, and a
+// sequence whose lengths break a rule (unit_lengths', k_L at most its top
+// level, each k_l at most its candidates) runs with the call's maxima.
+template <int G, bool TOP = false, bool VARLEN = false>
 __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, LevelArgs lv) {
+  static_assert(!VARLEN || TOP, "per-sequence lengths: the one-launch path");
   __shared__ __attribute__((aligned(16))) UnitLds L;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hq = lane & 15, jg = lane >> 4;
   const int unit = blockIdx.x;
+  // gists of level l (>= 1) and candidates of level l < L of this unit's
+  // sequence (the call's, from the plan, for uniform lengths)
+  int64_t m_seq = a.M;
+  auto count = [&](int l) -> int64_t {
+    if constexpr (!VARLEN) return lv.Ml[l];
+    int64_t c = m_seq;
+    for (int i = 1; i < l; ++i) c /= lv.G;
+    return c;
+  };
+  auto cands = [&](int l) -> int32_t {
+    if constexpr (!VARLEN) return lv.items[l];
+    return (int32_t)((int64_t)lv.kl[l + 1] * lv.G + count(l) - count(l + 1) * lv.G);
+  };
+  if constexpr (VARLEN) {
+    const int64_t N0 = a.N, M0 = a.M;
+    unit_lengths(a.seq, unit, N0, M0, a.C, a.T, &a.N, &m_seq);
+    bool ok = lv.kl[lv.L] <= count(lv.L);
+    for (int l = 1; l < lv.L; ++l) ok = ok && (l == 1 ? a.k : lv.kl[l]) <= cands(l);
+    if (!ok) {   // the call's maxima
+      a.N = N0;
+      m_seq = M0;
+    }
+    a.M = m_seq;
+  }
   const char* Kb = reinterpret_cast<const char*>(a.K) + (size_t)unit * a.R * 256;
   const char* Vb = reinterpret_cast<const char*>(a.V) + (size_t)unit * a.R * 256;
   bf16x8u qf[4];
@@ -2819,14 +2848,15 @@ __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, Level
   // the top level: its chosen gists, ascending
   if constexpr (TOP) {
     // its gists (dense rows of the top array, a.K2) and the tail, four wave shares
+    const char* K2b = reinterpret_cast<const char*>(a.K2) + (size_t)unit * a.M2 * 256;   // slabs of the call's M_L
+    const char* V2b = reinterpret_cast<const char*>(a.V2) + (size_t)unit * a.M2 * 256;
+    if constexpr (VARLEN) a.M2 = count(Lv);
     const int n1 = (int)a.M2 + a.T;
     const int per1 = (n1 + kUW - 1) / kUW;
-    const char* K2b = reinterpret_cast<const char*>(a.K2) + (size_t)unit * a.M2 * 256;
-    const char* V2b = reinterpret_cast<const char*>(a.V2) + (size_t)unit * a.M2 * 256;
     unit_stream<kUKL2>(Kb, Vb, min(n1, w * per1), min(n1, (w + 1) * per1), a, qf, st, ring, L.scores, L.sel, 0,
                        K2b, V2b);
     __syncthreads();   // every top-level score is in LDS, every ring idle
-    unit_select<kUMaxGist / kThreads, true>(L.scores, (int)lv.Ml[Lv], lv.kl[Lv], gsc, a.score_stride, unit, L.sel2,
+    unit_select<kUMaxGist / kThreads, true>(L.scores, (int)count(Lv), lv.kl[Lv], gsc, a.score_stride, unit, L.sel2,
                                             L.u.sel.s, L.u.sel.t);
   } else {
     unit_select<kUMaxSel / kThreads, false>(nullptr, (int)lv.Ml[Lv], lv.kl[Lv], a.s2 + (size_t)unit * a.s2_stride,
@@ -2839,13 +2869,13 @@ __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, Level
   for (int l = Lv - 1; l >= 2; --l) {
     UnitArgs b = a;
     b.C = 0;                 // row of gist id = id
-    b.M = lv.Ml[l];
-    b.M2 = lv.Ml[l + 1];
+    b.M = count(l);
+    b.M2 = count(l + 1);
     b.k2 = lv.kl[l + 1];
     b.G2 = Gf;
-    const char* Kl = reinterpret_cast<const char*>(lv.K[l]) + (size_t)unit * lv.Ml[l] * 256;
+    const char* Kl = reinterpret_cast<const char*>(lv.K[l]) + (size_t)unit * lv.Ml[l] * 256;   // the call's slabs
     const char* Vl = reinterpret_cast<const char*>(lv.V[l]) + (size_t)unit * lv.Ml[l] * 256;
-    const int nc = lv.items[l];
+    const int nc = cands(l);
     const int perc = (nc + kUW - 1) / kUW;
     unit_stream<kUKCand>(Kl, Vl, min(nc, w * perc), min(nc, (w + 1) * perc), b, qf, st, ring, L.scores, L.sel2);
     __syncthreads();   // every candidate score is in LDS, every ring idle
@@ -2858,7 +2888,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, Level
     int id = 0;
     if (tid < k) {
       const int c = L.sel[tid], kg = lv.kl[l + 1] * Gf;
-      id = c < kg ? L.sel2[c / Gf] * Gf + c % Gf : (int)(lv.Ml[l + 1] * Gf) + (c - kg);
+      id = c < kg ? L.sel2[c / Gf] * Gf + c % Gf : (int)(b.M2 * Gf) + (c - kg);
     }
     __syncthreads();
     if (tid < k) {
@@ -2869,10 +2899,10 @@ __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, Level
   }
   // level 1: gist rows of the interleaved cache, then the chunks
   UnitArgs b = a;
-  b.M2 = lv.Ml[2];
+  b.M2 = count(2);
   b.k2 = lv.kl[2];
   b.G2 = Gf;
-  const int nc = lv.items[1];
+  const int nc = cands(1);
   const int perc = (nc + kUW - 1) / kUW;
   unit_stream<kUKCand>(Kb, Vb, min(nc, w * perc), min(nc, (w + 1) * perc), b, qf, st, ring, L.scores, L.sel2);
   if (a.k > 0) {
@@ -2904,10 +2934,13 @@ __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, Level
     for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
 }
 
+// seq_n, seq_m: per-sequence lengths (device arrays; the one-launch path
+// only), or null.
 template <int G>
 gsa_status_t run_unit_levels(const LevelsPlan& lp, const void* q, const void* K, const void* V,
                              const void* const* Ku, const void* const* Vu, float* out, float* lse,
-                             int32_t* const* sel_up, int32_t* sel1, char* ws, hipStream_t st) {
+                             int32_t* const* sel_up, int32_t* sel1, char* ws, hipStream_t st,
+                             const int32_t* seq_n = nullptr, const int32_t* seq_m = nullptr) {
   const DecodePlan& pl = lp.base;
   const int Lv = lp.L;
   UnitArgs u{};
@@ -2938,7 +2971,12 @@ gsa_status_t run_unit_levels(const LevelsPlan& lp, const void* q, const void* K,
   prof_begin_call();
   if (levels_top_in_lds(lp)) {
     // the top level fits one workgroup's LDS scores: one launch
-    prof_launch((unit_levels_kernel<G, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
+    if (seq_n != nullptr) {
+      u.seq = SeqLens{seq_n, seq_m, pl.Hkv, pl.k};
+      prof_launch((unit_levels_kernel<G, true, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
+    } else {
+      prof_launch((unit_levels_kernel<G, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
+    }
   } else {
     prof_launch((unit_kernel<G, kHierTop>), dim3(pl.units * lp.unit_S), dim3(kUW * 64), 0, st, u);
     prof_launch((unit_levels_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
@@ -3322,6 +3360,45 @@ extern "C" gsa_status_t gsa_decode_levels(const gsa_levels_params* p, const void
   return dispatch<LevelsRunner>(lp.base.dtype, lp.base.D, lp.base.g, lp, q, k_cache, v_cache, k_up, v_up, out,
                                 lse, sel_up, sel1, reinterpret_cast<char*>(workspace),
                                 reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" gsa_status_t gsa_decode_levels_varlen(const gsa_levels_params* p, const int32_t* seq_n_raw,
+                                                 const int32_t* seq_n_gist, const void* q, const void* k_cache,
+                                                 const void* v_cache, const void* const* k_up,
+                                                 const void* const* v_up, float* out, float* lse,
+                                                 int32_t* const* sel_up, int32_t* sel1, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  clear_error();
+  prof_begin_call();
+  LevelsPlan lp;
+  gsa_status_t s = plan_levels(p, &lp);
+  if (s != GSA_OK) return s;
+  if (lp.unit_S == 0 || !levels_top_in_lds(lp))
+    return fail(GSA_ERR_UNSUPPORTED,
+                "variable-length L-level decode runs on the one-launch path (bf16, head_dim 128, every k <= 64, "
+                "at most 4096 top-level gists and 4096 candidates per level)");
+  if ((s = check_ptr(seq_n_raw, "seq_n_raw")) != GSA_OK || (s = check_ptr(seq_n_gist, "seq_n_gist")) != GSA_OK ||
+      (s = check_ptr(q, "q")) != GSA_OK || (s = check_ptr(k_cache, "k_cache")) != GSA_OK ||
+      (s = check_ptr(v_cache, "v_cache")) != GSA_OK || (s = check_ptr(out, "out")) != GSA_OK ||
+      (s = check_ptr(lse, "lse", true)) != GSA_OK || (s = check_ptr(sel1, "sel1", true)) != GSA_OK)
+    return s;
+  if (!k_up || !v_up) return fail(GSA_ERR_INVALID_ARG, "k_up / v_up is NULL");
+  for (int i = 0; i + 2 <= lp.L; ++i) {
+    const bool need = lp.Ml[i + 2] > 0;
+    if ((s = check_ptr(k_up[i], "k_up[i]", !need)) != GSA_OK || (s = check_ptr(v_up[i], "v_up[i]", !need)) != GSA_OK)
+      return s;
+    if (sel_up && (s = check_ptr(sel_up[i], "sel_up[i]", true)) != GSA_OK) return s;
+  }
+  if ((s = check_workspace(workspace, workspace_bytes, lp.total)) != GSA_OK) return s;
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  switch (lp.base.g) {
+    case 1: return run_unit_levels<1>(lp, q, k_cache, v_cache, k_up, v_up, out, lse, sel_up, sel1, ws, hs, seq_n_raw, seq_n_gist);
+    case 2: return run_unit_levels<2>(lp, q, k_cache, v_cache, k_up, v_up, out, lse, sel_up, sel1, ws, hs, seq_n_raw, seq_n_gist);
+    case 4: return run_unit_levels<4>(lp, q, k_cache, v_cache, k_up, v_up, out, lse, sel_up, sel1, ws, hs, seq_n_raw, seq_n_gist);
+    case 8: return run_unit_levels<8>(lp, q, k_cache, v_cache, k_up, v_up, out, lse, sel_up, sel1, ws, hs, seq_n_raw, seq_n_gist);
+  }
+  return fail(GSA_ERR_UNSUPPORTED, "no kernel for g=%d", lp.base.g);
 }
 
 extern "C" gsa_status_t gsa_decode_varlen(const gsa_decode_params* p, const int32_t* seq_n_raw,

@@ -654,6 +654,28 @@ extern "C" gsa_status_t gsa_check_prefill_seqs(const gsa_prefill_varlen_params* 
   return GSA_OK;
 }
 
+extern "C" gsa_status_t gsa_check_levels_seq_lens(const gsa_levels_params* p, const int32_t* seq_n_raw,
+                                                  const int32_t* seq_n_gist) {
+  gsa::clear_error();
+  gsa::LevelsPlan lp;
+  gsa_status_t s = gsa::plan_levels(p, &lp);
+  if (s != GSA_OK) return s;
+  if ((s = gsa_check_seq_lens(&p->base, seq_n_raw, seq_n_gist)) != GSA_OK) return s;
+  const int32_t L = p->n_levels, G = p->fanout;
+  for (int32_t b = 0; b < p->base.batch; ++b) {
+    int64_t cnt[GSA_MAX_LEVELS + 2];
+    cnt[1] = seq_n_gist[b];
+    for (int l = 2; l <= L + 1; ++l) cnt[l] = cnt[l - 1] / G;
+    bool ok = lp.kl[L] <= cnt[L];
+    for (int l = 1; l < L; ++l) ok = ok && lp.kl[l] <= (int64_t)lp.kl[l + 1] * G + cnt[l] - cnt[l + 1] * G;
+    if (!ok)
+      return gsa::fail(GSA_ERR_INVALID_ARG,
+                       "sequence %d: n_gist=%lld leaves a level with fewer gists or candidates than its k", b,
+                       (long long)seq_n_gist[b]);
+  }
+  return GSA_OK;
+}
+
 extern "C" gsa_status_t gsa_check_hier_seq_lens(const gsa_hier_params* p, const int32_t* seq_n_raw,
                                                 const int32_t* seq_n_gist) {
   gsa::clear_error();

@@ -346,6 +346,37 @@ gsa_status_t gsa_decode_levels(const gsa_levels_params* p, const void* q, const 
                                size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Variable-length L-level decode: gsa_decode_levels' step for sequences of
+ * different lengths.
+ * Source: the L-level rule above applied per sequence, as gsa_decode_varlen
+ * applies gsa_decode's.
+ * p->base.n_raw, p->base.n_gist are the batch's largest N, M; they size the
+ * workspace (gsa_decode_levels_workspace_size(p)) and the slabs: the cache
+ * slabs hold base.row_capacity (or N + M) rows, level l's slabs M_l =
+ * floor(M / G^(l-1)) rows, and sequence b's level l has M_l(b) =
+ * floor(M_b / G^(l-1)) gists, the first rows of its slab.
+ * seq_n_raw, seq_n_gist: device arrays [B] int32 (16-byte aligned), the
+ * rules of gsa_decode_varlen plus k_L <= M_L(b) and each k_l at most
+ * sequence b's candidates of level l; gsa_check_levels_seq_lens validates a
+ * host copy. A sequence that breaks them runs with (N, M) instead, so no
+ * read leaves its slabs. Runs on the one-launch path only (bf16, head_dim
+ * 128, every k <= 64, at most 4096 top-level gists and 4096 candidates per
+ * level; else GSA_ERR_UNSUPPORTED). Other arguments as gsa_decode_levels.
+ * ---------------------------------------------------------------------- */
+gsa_status_t gsa_decode_levels_varlen(const gsa_levels_params* p, const int32_t* seq_n_raw,
+                                      const int32_t* seq_n_gist, const void* q, const void* k_cache,
+                                      const void* v_cache, const void* const* k_up,
+                                      const void* const* v_up, float* out, float* lse,
+                                      int32_t* const* sel_up, int32_t* sel1, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* Host check of per-sequence lengths (host arrays [p->base.batch]) against
+ * gsa_decode_levels_varlen's rules: GSA_OK, or GSA_ERR_INVALID_ARG naming
+ * the first sequence that breaks one (gsa_last_error). */
+gsa_status_t gsa_check_levels_seq_lens(const gsa_levels_params* p, const int32_t* seq_n_raw,
+                                       const int32_t* seq_n_gist);
+
+/* ------------------------------------------------------------------------
  * Causal block-sparse prefill of query positions [q_start, q_start + n_q)
  * of one sequence.
  * Source: gist.science explainer, 'Training Procedure: Selective Finetuning'

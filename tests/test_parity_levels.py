@@ -130,3 +130,85 @@ def test_levels_1m_three_levels_sampled(gsa):
     say("levels 1m")
     err, _ = run_levels(gsa, c, 6300, units=[(0, 0), (1, 3), (3, 7)])
     say(f"  max err / rms = {err:.2e}")
+
+
+# ------------------------------------------------ variable lengths ---
+
+def levels_varlen_case(c, seed):
+    """Per-sequence lengths and the level arrays of the batch's largest M;
+    rows past a sequence's own rows (cache and every level) hold a constant
+    the attention would notice."""
+    B, Hq, Hkv, C, G, L = c["B"], c["Hq"], c["Hkv"], c["C"], c["G"], len(c["topks"])
+    n, m = gi.varlen_lengths(B, c["n_min"], c["n_max"], C, seed)
+    N, M = max(n), max(m)
+    q, k, v, ku, vu = gi.make_levels(B, Hq, Hkv, 128, N + 3, M, C, G, L, seed, device="cuda", values="int")
+    cap = N + M + 3
+    for b in range(B):
+        k[b, :, n[b] + m[b]:] = 3.0
+        v[b, :, n[b] + m[b]:] = 3.0
+        ml = m[b]
+        for i in range(L - 1):
+            ml //= G
+            ku[i][b, :, ml:] = 3.0
+            vu[i][b, :, ml:] = 3.0
+    return q, k[:, :, :cap].contiguous(), v[:, :, :cap].contiguous(), ku, vu, n, m
+
+
+VARLEN_CASES = [
+    # three levels, lengths 8K-40K (top level at most 156 gists)
+    dict(B=4, Hq=8, Hkv=2, C=16, G=4, topks=[8, 6, 4], T=64, n_min=8000, n_max=40000),
+    # four levels, G = 2, 256 units
+    dict(B=32, Hq=32, Hkv=8, C=16, G=2, topks=[8, 6, 4, 3], T=32, n_min=2000, n_max=9000),
+]
+
+
+@pytest.mark.parametrize("i", range(len(VARLEN_CASES)), ids=[f"varlen{i}" for i in range(len(VARLEN_CASES))])
+def test_levels_varlen_matches_oracle_per_sequence(gsa, i):
+    c = VARLEN_CASES[i]
+    say(f"levels varlen {c}")
+    q, k, v, ku, vu, n, m = levels_varlen_case(c, 9100 + i)
+    topks, G, L = c["topks"], c["G"], len(c["topks"])
+    out, lse, sels = gsa.gsa_decode_levels_varlen(q, k, v, ku, vu, seq_n_raw=n, seq_n_gist=m, chunk=c["C"],
+                                                  fanout=G, topks=topks, tail=c["T"])
+    torch.cuda.synchronize()
+    assert gsa.gsa_profile_marks() == 2
+    g = c["Hq"] // c["Hkv"]
+    got, ref, got_l, ref_l = [], [], [], []
+    for b in range(c["B"]):
+        sizes = [m[b]]
+        for _ in range(L - 1):
+            sizes.append(sizes[-1] // G)
+        for j in range(c["Hkv"]):
+            r_ = oracle.decode_levels_unit(to_np(q[b, j * g:(j + 1) * g]), to_np(k[b, j, :n[b] + m[b]]),
+                                           to_np(v[b, j, :n[b] + m[b]]),
+                                           [(to_np(ku[l][b, j, :sizes[l + 1]]), to_np(vu[l][b, j, :sizes[l + 1]]))
+                                            for l in range(L - 1)],
+                                           n_raw=n[b], n_gist=m[b], chunk=c["C"], fanout=G, topks=topks,
+                                           tail=c["T"])
+            for lvl in range(L):
+                np.testing.assert_array_equal(to_np(sels[lvl][b, j]), r_["sels"][lvl],
+                                              err_msg=f"sequence {b} kv {j} level {lvl + 1}")
+            got.append(to_np(out[b, j * g:(j + 1) * g]))
+            ref.append(r_["out"])
+            got_l.append(to_np(lse[b, j * g:(j + 1) * g]))
+            ref_l.append(r_["lse"])
+    err = check_out(np.stack(got), np.stack(ref), "bf16", str(c))
+    check_lse(np.stack(got_l), np.stack(ref_l), "bf16", str(c))
+    say(f"  max err / rms = {err:.2e}")
+
+
+def test_levels_varlen_equal_lengths_is_levels(gsa):
+    """Every sequence at the call's largest lengths: bit-identical to
+    gsa_decode_levels."""
+    c = dict(VARLEN_CASES[0])
+    B, C, G, L = c["B"], c["C"], c["G"], len(c["topks"])
+    M = 1500
+    N = M * C + 7
+    q, k, v, ku, vu = gi.make_levels(B, c["Hq"], c["Hkv"], 128, N, M, C, G, L, 9200, device="cuda", values="int")
+    kw = dict(chunk=C, fanout=G, topks=c["topks"], tail=c["T"])
+    a = gsa.gsa_decode_levels(q, k, v, ku, vu, n_gist=M, **kw)
+    b = gsa.gsa_decode_levels_varlen(q, k, v, ku, vu, seq_n_raw=[N] * B, seq_n_gist=[M] * B, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    for x, y in zip(a[2], b[2]):
+        assert torch.equal(x, y)
