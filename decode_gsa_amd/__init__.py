@@ -506,8 +506,10 @@ def check_seq_lens(p: DecodeParams, seq_n_raw, seq_n_gist) -> None:
 def gsa_decode_varlen(q, k_cache, v_cache, *, seq_n_raw, seq_n_gist, chunk: int, topk: int,
                       tail: int, n_raw: Optional[int] = None, n_gist: Optional[int] = None,
                       scale: float = 0.0, out=None, lse=None, sel_idx=None, workspace=None,
-                      stream=None, want_lse: bool = True, want_sel: bool = True):
-    """Single-level decode of sequences of different lengths. Caches
+                      stream=None, want_lse: bool = True, want_sel: bool = True,
+                      gist_set: str = "all"):
+    """Single-level decode of sequences of different lengths (gist_set: as
+    gsa_decode). Caches
     [B,Hkv,cap,D]: sequence b uses its first seq_n_raw[b] + seq_n_gist[b] rows.
 
     seq_n_raw / seq_n_gist: host sequences (checked with gsa_check_seq_lens,
@@ -531,8 +533,10 @@ def gsa_decode_varlen(q, k_cache, v_cache, *, seq_n_raw, seq_n_gist, chunk: int,
             raise ValueError("one length per sequence")
         n_raw = max(hn) if n_raw is None else n_raw
         n_gist = max(hm) if n_gist is None else n_gist
+    if gist_set not in GIST_SETS:
+        raise ValueError(f"gist_set must be one of {tuple(GIST_SETS)}")
     p = decode_params(B, Hq, Hkv, D, n_raw, n_gist, chunk, topk, tail, scale, _dtype_code(q),
-                      0, cap)
+                      GIST_SETS[gist_set], cap)
     if not on_dev:
         check_seq_lens(p, hn, hm)
     s, on_s = _on_stream(stream, dev)

@@ -2623,7 +2623,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
 template <int G, bool VARLEN = false, bool PAGED = false, bool SETS = false>
 __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   static_assert(!PAGED || VARLEN, "paged caches: per-sequence lengths");
-  static_assert(!SETS || (!VARLEN && !PAGED), "selection-rule variants: uniform lengths");
+  static_assert(!SETS || !PAGED, "selection-rule variants: unpaged caches");
   __shared__ __attribute__((aligned(16))) std::conditional_t<PAGED, PagedLds, UnitLds> L;
   UnitArgs a = args;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -3053,17 +3053,24 @@ gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const 
     return launch_status("gsa_decode_paged launch");
   }
   if (pl.gist_set != GSA_GISTS_ALL) {
+    const dim3 block(kUW * 64);
     if (pl.unit_S == 1) {
-      prof_launch((unit_kernel<G, kHierNone, true, false, false>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+      if (varlen)
+        prof_launch((unit_kernel<G, kHierNone, true, true, false>), dim3(pl.units), block, 0, st, u);
+      else
+        prof_launch((unit_kernel<G, kHierNone, true, false, false>), dim3(pl.units), block, 0, st, u);
     } else {
       // the gists' scores (none needed with k = 0), then the set
-      if (pl.k > 0)
-        prof_launch((unit_kernel<G, kHierNone, true, false, true>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0,
-                    st, u);
-      prof_launch((unit_unfold_kernel<G, false, false, true>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st,
-                  u);
+      if (pl.k > 0 && varlen)
+        prof_launch((unit_kernel<G, kHierNone, true, true, true>), dim3(pl.units * pl.unit_S), block, 0, st, u);
+      else if (pl.k > 0)
+        prof_launch((unit_kernel<G, kHierNone, true, false, true>), dim3(pl.units * pl.unit_S), block, 0, st, u);
+      if (varlen)
+        prof_launch((unit_unfold_kernel<G, true, false, true>), dim3(pl.units * pl.unit_S2), block, 0, st, u);
+      else
+        prof_launch((unit_unfold_kernel<G, false, false, true>), dim3(pl.units * pl.unit_S2), block, 0, st, u);
     }
-    return launch_status("gsa_decode launch");
+    return launch_status(varlen ? "gsa_decode_varlen launch" : "gsa_decode launch");
   }
   else if (varlen && pl.unit_S == 1)
     prof_launch((unit_kernel<G, kHierNone, false, true, false>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
@@ -3410,8 +3417,6 @@ extern "C" gsa_status_t gsa_decode_varlen(const gsa_decode_params* p, const int3
   DecodePlan pl;
   gsa_status_t s = plan_decode(p, &pl);
   if (s != GSA_OK) return s;
-  if (pl.gist_set != GSA_GISTS_ALL)
-    return fail(GSA_ERR_UNSUPPORTED, "variable-length decode attends every gist: gist_set must be 0");
   if ((s = check_ptr(seq_n_raw, "seq_n_raw")) != GSA_OK || (s = check_ptr(seq_n_gist, "seq_n_gist")) != GSA_OK ||
       (s = check_ptr(q, "q")) != GSA_OK || (s = check_ptr(k_cache, "k_cache")) != GSA_OK ||
       (s = check_ptr(v_cache, "v_cache")) != GSA_OK || (s = check_ptr(out, "out")) != GSA_OK ||

@@ -89,8 +89,9 @@ typedef struct {
                           gsa_decode_hier_varlen on their bf16, head_dim
                           128 path (else GSA_ERR_UNSUPPORTED), the rule
                           deciding which gists are attended while the
-                          routing stays the same. gsa_decode_varlen,
-                          _paged and _levels require 0. */
+                          routing stays the same; gsa_decode_varlen on
+                          every shape. gsa_decode_paged and _levels
+                          require 0. */
   int64_t row_capacity; /* rows allocated per (sequence, kv-head) in the
                           caches, the stride between their [R, D] blocks:
                           0 means exactly R = N + M; else it must be
@@ -157,7 +158,8 @@ gsa_status_t gsa_decode_noalloc(const gsa_decode_params* p, const void* q, const
  * 0 <= N_b - M_b*C <= C and N_b - M_b*C <= tail <= N_b. They stay on the
  * device (read by the kernels); gsa_check_seq_lens validates a host copy.
  * A sequence that breaks these rules is run with (N, M) instead, so no read
- * leaves its slab. gist_set must be 0 (else GSA_ERR_UNSUPPORTED).
+ * leaves its slab. gist_set: the selection rules, as gsa_decode (every
+ * shape).
  * ---------------------------------------------------------------------- */
 gsa_status_t gsa_decode_varlen(const gsa_decode_params* p, const int32_t* seq_n_raw,
                                const int32_t* seq_n_gist, const void* q, const void* k_cache,

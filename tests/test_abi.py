@@ -465,7 +465,6 @@ def test_decode_varlen_rejections(L):
                                                   FAKE, need, None)
     assert call(p, None, FAKE) == INVALID and "seq_n_raw" in L.gsa_last_error().decode()
     assert call(p, FAKE, FAKE + 4) == INVALID                       # misaligned
-    assert call(varlen_params(gist_set=1, batch=128), FAKE, FAKE) == UNSUPPORTED
 
 
 

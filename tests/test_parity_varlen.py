@@ -42,7 +42,7 @@ def make_case(c, seed):
     return q, k, v, n, m
 
 
-def check(gsa, c, q, k, v, n, m, out, lse, sel):
+def check(gsa, c, q, k, v, n, m, out, lse, sel, gist_set="all"):
     g = c["Hq"] // c["Hkv"]
     dtype = c.get("dtype", "bf16")
     got, ref, got_l, ref_l = [], [], [], []
@@ -50,7 +50,8 @@ def check(gsa, c, q, k, v, n, m, out, lse, sel):
         R = n[b] + m[b]
         for j in range(c["Hkv"]):
             r = oracle.decode_unit(to_np(q[b, j * g:(j + 1) * g]), to_np(k[b, j, :R]), to_np(v[b, j, :R]),
-                                   n_raw=n[b], n_gist=m[b], chunk=c["C"], topk=c["k"], tail=c["T"])
+                                   n_raw=n[b], n_gist=m[b], chunk=c["C"], topk=c["k"], tail=c["T"],
+                                   gist_set=gist_set)
             if c["k"] > 0:
                 np.testing.assert_array_equal(to_np(sel[b, j]), r["sel"], err_msg=f"sequence {b} kv-head {j}")
             got.append(to_np(out[b, j * g:(j + 1) * g]))
@@ -132,3 +133,19 @@ def test_varlen_device_lengths_and_fallback(gsa):
                                    n_raw=n3[b], n_gist=m3[b], chunk=c["C"], topk=c["k"], tail=c["T"])
             np.testing.assert_array_equal(to_np(sel[b, j]), r["sel"])
             check_out(to_np(out[b, j * g:(j + 1) * g]), r["out"], "bf16", f"sequence {b}")
+
+
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+@pytest.mark.parametrize("i", [0, 1, 2], ids=["units256", "units16", "split_f32"])
+def test_varlen_selection_rules(gsa, i, gist_set):
+    """The slide 17 rules with sequences of different lengths: one workgroup
+    per unit, several per unit (scoring launch, then the set's launch) and
+    the split path, each sequence against the oracle with the same rule."""
+    c = CASES[i]
+    say(f"varlen {gist_set} {c}")
+    q, k, v, n, m = make_case(c, 7400 + i)
+    out, lse, sel = gsa.gsa_decode_varlen(q, k, v, seq_n_raw=n, seq_n_gist=m, chunk=c["C"], topk=c["k"],
+                                          tail=c["T"], gist_set=gist_set)
+    torch.cuda.synchronize()
+    err = check(gsa, c, q, k, v, n, m, out, lse, sel, gist_set=gist_set)
+    say(f"  max err / rms = {err:.2e}, {gsa.gsa_profile_marks() - 1} launches")
