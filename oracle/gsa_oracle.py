@@ -434,9 +434,9 @@ def decode_hier(q, k_cache, v_cache, k_l2, v_l2, *, chunk: int, fanout: int, top
 
 def decode_levels_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, upper, *, n_raw: int,
                        n_gist: int, chunk: int, fanout: int, topks, tail: int,
-                       scale: Optional[float] = None) -> Dict[str, object]:
+                       scale: Optional[float] = None, gist_set: str = "all") -> Dict[str, object]:
     """One unit of L-level decode (R15; explainer 'Hierarchical Extension
-    (H-GSA)' and 'Coarse-to-Fine Selection', slide 11).
+    (H-GSA)' and 'Coarse-to-Fine Selection', slide 11; gist_set: R20).
 
     upper: [(K_2, V_2), ..., (K_L, V_L)], K_l: [M_l, D] with
     M_l = floor(M_{l-1} / G), M_1 = n_gist.  topks: [k_1, ..., k_L], k_1 the
@@ -458,6 +458,10 @@ def decode_levels_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, upper, *, n
             raise ValueError(f"level {l} array has {upper[l - 2][0].shape[0]} rows, expected {sizes[-1]}")
     if not (N - M * C <= T <= N):
         raise ValueError("tail must cover the raw tokens after the last gist")
+    if gist_set not in GIST_SETS:
+        raise ValueError(f"gist_set must be one of {GIST_SETS}")
+    if gist_set != "all" and topks[0] == 0 and T == 0:
+        raise ValueError("the attention set would be empty")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
 
     def keys_of(l, ids):           # key rows of gists `ids` at level l (1-based)
@@ -477,17 +481,25 @@ def decode_levels_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, upper, *, n
             raise ValueError(f"k at level {l} exceeds its {len(cands[l])} candidates")
         S = _group_scores(qg, keys_of(l, cands[l]), scale) if cands[l] else np.zeros(0)
         sels[l] = topk_ascending(S, cands[l], k)
-    # attention set: the top level, every lower level's candidates, the raw
-    # rows of the chosen chunks and the tail (rows of the level-1 cache)
-    A = {gist_row_index(m, C) for m in cands[1]}
+    # attention set: the gists of the rule (all: the top level and every
+    # lower level's candidates; selected: the chosen chunks' gists; none),
+    # the raw rows of the chosen chunks and the tail (rows of the level-1
+    # cache)
+    if gist_set == "all":
+        A = {gist_row_index(m, C) for m in cands[1]}
+    elif gist_set == "selected":
+        A = {gist_row_index(m, C) for m in sels[1]}
+    else:
+        A = set()
     for m in sels[1]:
         for j in range(C):
             A.add(raw_row_index(m * C + j, C, M))
     for p in range(N - T, N):
         A.add(raw_row_index(p, C, M))
     rows = np.array(sorted(A), dtype=np.int64)
-    keys = [_f64(upper[l - 2][0][cands[l]]) for l in range(L, 1, -1)] + [_f64(K[rows])]
-    vals = [_f64(upper[l - 2][1][cands[l]]) for l in range(L, 1, -1)] + [_f64(V[rows])]
+    up = range(L, 1, -1) if gist_set == "all" else []
+    keys = [_f64(upper[l - 2][0][cands[l]]) for l in up] + [_f64(K[rows])]
+    vals = [_f64(upper[l - 2][1][cands[l]]) for l in up] + [_f64(V[rows])]
     out, lse, wsum = _softmax_attend(qg, np.concatenate(keys), np.concatenate(vals), scale)
     return {"out": out, "lse": lse, "wsum": wsum,
             "sels": [np.array(sels[l], dtype=np.int64) for l in range(1, L + 1)],

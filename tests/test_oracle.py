@@ -668,6 +668,55 @@ def test_levels_two_is_the_two_level_decode(seed):
     np.testing.assert_allclose(a["out"], b["out"], rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+@pytest.mark.parametrize("seed", range(3))
+def test_levels_rules_two_levels_are_the_two_level_rules(gist_set, seed):
+    """R20 on L levels: L = 2 under a rule is the two-level step under it."""
+    rng = np.random.default_rng(520 + seed)
+    g, D, C, G = 2, 8, 4, int(rng.integers(2, 5))
+    M = int(rng.integers(G, 40))
+    r = int(rng.integers(0, C + 1))
+    qg, K, V, upper, N, sizes = _levels_inputs(rng, g, D, C, M, G, 2, r)
+    k2 = int(rng.integers(0, sizes[1] + 1))
+    k1 = int(rng.integers(1, max(2, k2 * G + (M - sizes[1] * G) + 1)))
+    k1 = min(k1, k2 * G + (M - sizes[1] * G))
+    T = int(rng.integers(max(r, 1), N + 1))
+    a = oracle.decode_levels_unit(qg, K, V, upper, n_raw=N, n_gist=M, chunk=C, fanout=G, topks=[k1, k2], tail=T,
+                                  gist_set=gist_set)
+    b = oracle.decode_hier_unit(qg, K, V, upper[0][0], upper[0][1], n_raw=N, n_gist=M, chunk=C, fanout=G,
+                                topk1=k1, topk2=k2, tail=T, gist_set=gist_set)
+    assert list(a["sels"][0]) == list(b["sel1"]) and list(a["sels"][1]) == list(b["sel2"])
+    np.testing.assert_array_equal(a["rows"], b["rows"])
+    np.testing.assert_allclose(a["out"], b["out"], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+def test_levels_rules_attention_set_by_mask(gist_set):
+    """R20 on four levels against a dense masked softmax over the level-1
+    cache: no upper-level row, the chosen chunks' raw rows and the tail, and
+    (selected) the chosen chunks' gist rows; the routing is the default
+    rule's."""
+    rng = np.random.default_rng(530)
+    g, D, C, M, G, T = 2, 8, 4, 70, 3, 5
+    qg, K, V, upper, N, sizes = _levels_inputs(rng, g, D, C, M, G, 4, r=1)
+    topks = [4, 3, 2, 2]
+    h = oracle.decode_levels_unit(qg, K, V, upper, n_raw=N, n_gist=M, chunk=C, fanout=G, topks=topks, tail=T,
+                                  gist_set=gist_set)
+    a = oracle.decode_levels_unit(qg, K, V, upper, n_raw=N, n_gist=M, chunk=C, fanout=G, topks=topks, tail=T)
+    assert all(list(x) == list(y) for x, y in zip(h["sels"], a["sels"]))
+    sel = set(h["sels"][0].tolist())
+    R = N + M
+    mask = np.zeros(R, bool)
+    for x in range(R):
+        kind, v = row_kind(x, C, M)
+        if kind == "gist":
+            mask[x] = gist_set == "selected" and v in sel
+        elif v >= N - T or (v // C < M and v // C in sel):
+            mask[x] = True
+    ref = sdpa(qg, K, V, mask, 1 / math.sqrt(D))
+    np.testing.assert_allclose(h["out"], ref, rtol=0, atol=1e-12)
+
+
 def test_levels_everything_selected_is_full_attention_over_every_level():
     rng = np.random.default_rng(510)
     g, D, C, M, G, L = 2, 16, 3, 29, 3, 4      # sizes 29, 9, 3, 1: orphans at levels 1 and 2
