@@ -668,7 +668,7 @@ def gsa_decode_hier_varlen(q, k_cache, v_cache, k_l2, v_l2, *, seq_n_raw, seq_n_
 def gsa_decode_levels(q, k_cache, v_cache, k_up, v_up, *, chunk: int, fanout: int, topks,
                       tail: int, n_gist: Optional[int] = None, n_raw: Optional[int] = None,
                       scale: float = 0.0, out=None, lse=None, workspace=None, stream=None,
-                      want_lse: bool = True, want_sel: bool = True):
+                      want_lse: bool = True, want_sel: bool = True, gist_set: str = "all"):
     """L-level decode. k_up, v_up: [level 2, ..., level L] arrays [B,Hkv,M_l,D];
     topks = [k_1, ..., k_L].
 
@@ -682,8 +682,10 @@ def gsa_decode_levels(q, k_cache, v_cache, k_up, v_up, *, chunk: int, fanout: in
     topks = [int(k) for k in topks]
     if len(k_up) != len(topks) - 1 or len(v_up) != len(topks) - 1:
         raise ValueError("one k per level and one array pair per level above the first")
+    if gist_set not in GIST_SETS:
+        raise ValueError(f"gist_set must be one of {tuple(GIST_SETS)}")
     base = decode_params(B, Hq, Hkv, D, N, M, chunk, topks[0], tail, scale, _dtype_code(q),
-                         row_capacity=cap)
+                         gist_set=GIST_SETS[gist_set], row_capacity=cap)
     p = levels_params(base, fanout, topks[1:])
     dev = q.device
     s, on_s = _on_stream(stream, dev)
@@ -715,7 +717,8 @@ def check_levels_seq_lens(p: LevelsParams, seq_n_raw, seq_n_gist) -> None:
 def gsa_decode_levels_varlen(q, k_cache, v_cache, k_up, v_up, *, seq_n_raw, seq_n_gist, chunk: int,
                              fanout: int, topks, tail: int, n_raw: Optional[int] = None,
                              n_gist: Optional[int] = None, scale: float = 0.0, out=None, lse=None,
-                             workspace=None, stream=None, want_lse: bool = True, want_sel: bool = True):
+                             workspace=None, stream=None, want_lse: bool = True, want_sel: bool = True,
+                             gist_set: str = "all"):
     """L-level decode of sequences of different lengths. Caches [B,Hkv,cap,D]
     (sequence b: its first seq_n_raw[b] + seq_n_gist[b] rows); k_up, v_up:
     level l's arrays [B,Hkv,M_l,D] with M_l = n_gist // fanout^(l-1) (sequence
@@ -743,8 +746,10 @@ def gsa_decode_levels_varlen(q, k_cache, v_cache, k_up, v_up, *, seq_n_raw, seq_
     topks = [int(k) for k in topks]
     if len(k_up) != len(topks) - 1 or len(v_up) != len(topks) - 1:
         raise ValueError("one k per level and one array pair per level above the first")
+    if gist_set not in GIST_SETS:
+        raise ValueError(f"gist_set must be one of {tuple(GIST_SETS)}")
     base = decode_params(B, Hq, Hkv, D, n_raw, n_gist, chunk, topks[0], tail, scale, _dtype_code(q),
-                         row_capacity=cap)
+                         gist_set=GIST_SETS[gist_set], row_capacity=cap)
     p = levels_params(base, fanout, topks[1:])
     if not on_dev:
         check_levels_seq_lens(p, hn, hm)

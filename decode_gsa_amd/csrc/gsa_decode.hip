@@ -2793,7 +2793,10 @@ struct LevelArgs {
 // floor(M_b / G^(l-1)) gists, the first rows of its slab of that level, and a
 // sequence whose lengths break a rule (unit_lengths', k_L at most its top
 // level, each k_l at most its candidates) runs with the call's maxima.
-template <int G, bool TOP = false, bool VARLEN = false>
+// SETS: the selection rules (R20): every level's gists are scored only, and
+// after the routing the chosen chunks' raw rows and, with gist_set 1, their
+// gists are attended (the tail came with the top level's stream).
+template <int G, bool TOP = false, bool VARLEN = false, bool SETS = false>
 __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, LevelArgs lv) {
   static_assert(!VARLEN || TOP, "per-sequence lengths: the one-launch path");
   __shared__ __attribute__((aligned(16))) UnitLds L;
@@ -2853,8 +2856,8 @@ __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, Level
     if constexpr (VARLEN) a.M2 = count(Lv);
     const int n1 = (int)a.M2 + a.T;
     const int per1 = (n1 + kUW - 1) / kUW;
-    unit_stream<kUKL2>(Kb, Vb, min(n1, w * per1), min(n1, (w + 1) * per1), a, qf, st, ring, L.scores, L.sel, 0,
-                       K2b, V2b);
+    unit_stream<kUKL2, false, SETS>(Kb, Vb, min(n1, w * per1), min(n1, (w + 1) * per1), a, qf, st, ring, L.scores,
+                                    L.sel, 0, K2b, V2b);
     __syncthreads();   // every top-level score is in LDS, every ring idle
     unit_select<kUMaxGist / kThreads, true>(L.scores, (int)count(Lv), lv.kl[Lv], gsc, a.score_stride, unit, L.sel2,
                                             L.u.sel.s, L.u.sel.t);
@@ -2877,7 +2880,8 @@ __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, Level
     const char* Vl = reinterpret_cast<const char*>(lv.V[l]) + (size_t)unit * lv.Ml[l] * 256;
     const int nc = cands(l);
     const int perc = (nc + kUW - 1) / kUW;
-    unit_stream<kUKCand>(Kl, Vl, min(nc, w * perc), min(nc, (w + 1) * perc), b, qf, st, ring, L.scores, L.sel2);
+    unit_stream<kUKCand, false, SETS>(Kl, Vl, min(nc, w * perc), min(nc, (w + 1) * perc), b, qf, st, ring, L.scores,
+                                      L.sel2);
     __syncthreads();   // every candidate score is in LDS, every ring idle
     const int k = lv.kl[l];
     unit_select<kUMaxGist / kThreads, true>(L.scores, nc, k, gsc, a.score_stride, unit, L.sel, L.u.sel.s,
@@ -2904,7 +2908,8 @@ __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, Level
   b.G2 = Gf;
   const int nc = cands(1);
   const int perc = (nc + kUW - 1) / kUW;
-  unit_stream<kUKCand>(Kb, Vb, min(nc, w * perc), min(nc, (w + 1) * perc), b, qf, st, ring, L.scores, L.sel2);
+  unit_stream<kUKCand, false, SETS>(Kb, Vb, min(nc, w * perc), min(nc, (w + 1) * perc), b, qf, st, ring, L.scores,
+                                    L.sel2);
   if (a.k > 0) {
     __syncthreads();
     unit_select<kUMaxGist / kThreads, true>(L.scores, nc, a.k, gsc, a.score_stride, unit, L.sel, L.u.sel.s,
@@ -2915,10 +2920,18 @@ __global__ __launch_bounds__(kUW * 64) void unit_levels_kernel(UnitArgs a, Level
       L.sel[tid] = c < kg ? L.sel2[c / Gf] * Gf + c % Gf : (int)(b.M2 * Gf) + (c - kg);
     }
     __syncthreads();
-    const int items = a.k * a.C;
-    const int per2 = (items + kUW - 1) / kUW;
-    unit_stream<kUKUnfold>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
-                           L.sel);
+    if constexpr (SETS) {
+      // the chosen chunks' raw rows, then their gists under rule 1
+      const int items = a.k * a.C + (a.gist_set == 1 ? a.k : 0);
+      const int per2 = (items + kUW - 1) / kUW;
+      unit_stream<kUKSet>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
+                          L.sel);
+    } else {
+      const int items = a.k * a.C;
+      const int per2 = (items + kUW - 1) / kUW;
+      unit_stream<kUKUnfold>(Kb, Vb, min(items, w * per2), min(items, (w + 1) * per2), a, qf, st, ring, L.scores,
+                             L.sel);
+    }
   }
   if constexpr (TOP) {
     unit_combine<G>(L, st, w, a.out + (size_t)unit * G * 128, a.lse ? a.lse + (size_t)unit * G : nullptr, nullptr);
@@ -2943,7 +2956,9 @@ gsa_status_t run_unit_levels(const LevelsPlan& lp, const void* q, const void* K,
                              const int32_t* seq_n = nullptr, const int32_t* seq_m = nullptr) {
   const DecodePlan& pl = lp.base;
   const int Lv = lp.L;
+  const bool sets = lp.base.gist_set != GSA_GISTS_ALL;
   UnitArgs u{};
+  u.gist_set = lp.base.gist_set;
   u.q = q; u.K = K; u.V = V; u.out = out; u.lse = lse; u.sel = pl.k > 0 ? sel1 : nullptr;
   u.scores = reinterpret_cast<float*>(ws + lp.off_scores[1]); u.score_stride = lp.score_stride[1];
   u.R = pl.R; u.N = pl.N; u.M = pl.M; u.C = pl.C; u.k = pl.k; u.T = pl.T;
@@ -2971,15 +2986,24 @@ gsa_status_t run_unit_levels(const LevelsPlan& lp, const void* q, const void* K,
   prof_begin_call();
   if (levels_top_in_lds(lp)) {
     // the top level fits one workgroup's LDS scores: one launch
-    if (seq_n != nullptr) {
-      u.seq = SeqLens{seq_n, seq_m, pl.Hkv, pl.k};
-      prof_launch((unit_levels_kernel<G, true, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
-    } else {
-      prof_launch((unit_levels_kernel<G, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
-    }
+    const dim3 grid(pl.units), block(kUW * 64);
+    if (seq_n != nullptr) u.seq = SeqLens{seq_n, seq_m, pl.Hkv, pl.k};
+    if (seq_n != nullptr && sets)
+      prof_launch((unit_levels_kernel<G, true, true, true>), grid, block, 0, st, u, lv);
+    else if (seq_n != nullptr)
+      prof_launch((unit_levels_kernel<G, true, true>), grid, block, 0, st, u, lv);
+    else if (sets)
+      prof_launch((unit_levels_kernel<G, true, false, true>), grid, block, 0, st, u, lv);
+    else
+      prof_launch((unit_levels_kernel<G, true>), grid, block, 0, st, u, lv);
   } else {
-    prof_launch((unit_kernel<G, kHierTop>), dim3(pl.units * lp.unit_S), dim3(kUW * 64), 0, st, u);
-    prof_launch((unit_levels_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
+    if (sets) {
+      prof_launch((unit_kernel<G, kHierTop, true>), dim3(pl.units * lp.unit_S), dim3(kUW * 64), 0, st, u);
+      prof_launch((unit_levels_kernel<G, false, false, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
+    } else {
+      prof_launch((unit_kernel<G, kHierTop>), dim3(pl.units * lp.unit_S), dim3(kUW * 64), 0, st, u);
+      prof_launch((unit_levels_kernel<G>), dim3(pl.units), dim3(kUW * 64), 0, st, u, lv);
+    }
   }
   return launch_status("gsa_decode_levels launch");
 }

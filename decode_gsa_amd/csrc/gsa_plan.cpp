@@ -409,8 +409,6 @@ gsa_status_t plan_prefill_varlen(const gsa_prefill_varlen_params* p, PrefillPlan
 
 gsa_status_t plan_levels(const gsa_levels_params* p, LevelsPlan* o) {
   if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
-  if (p->base.gist_set != GSA_GISTS_ALL)
-    return fail(GSA_ERR_UNSUPPORTED, "L-level decode attends every gist: base.gist_set must be 0");
   if (p->n_levels < 2 || p->n_levels > GSA_MAX_LEVELS)
     return fail(GSA_ERR_INVALID_ARG, "n_levels=%d outside [2, %d]", p->n_levels, GSA_MAX_LEVELS);
   if (p->fanout < 2) return fail(GSA_ERR_INVALID_ARG, "fanout=%d must be >= 2", p->fanout);
@@ -475,6 +473,10 @@ gsa_status_t plan_levels(const gsa_levels_params* p, LevelsPlan* o) {
       }
     }
   }
+  if (d.gist_set != GSA_GISTS_ALL && h.unit_S == 0)
+    return fail(GSA_ERR_UNSUPPORTED,
+                "L-level decode with gist_set=%d runs on the bf16, head_dim 128 path (every k <= 64, at most 4096 "
+                "candidates per level)", d.gist_set);
   size_t off = 0;
   h.off_ctrl = off;
   off = align_up(off + ctrl_bytes(units));

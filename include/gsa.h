@@ -90,8 +90,9 @@ typedef struct {
                           128 path (else GSA_ERR_UNSUPPORTED), the rule
                           deciding which gists are attended while the
                           routing stays the same; gsa_decode_varlen on
-                          every shape. gsa_decode_paged and _levels
-                          require 0. */
+                          every shape; gsa_decode_levels and
+                          gsa_decode_levels_varlen on their bf16,
+                          head_dim 128 path. gsa_decode_paged requires 0. */
   int64_t row_capacity; /* rows allocated per (sequence, kv-head) in the
                           caches, the stride between their [R, D] blocks:
                           0 means exactly R = N + M; else it must be
@@ -315,7 +316,11 @@ gsa_status_t gsa_check_hier_seq_lens(const gsa_hier_params* p, const int32_t* se
 
 typedef struct {
   gsa_decode_params base; /* level 1 and the step: base.topk = k_1 chunks
-                             unfolded; base.gist_set must be 0 */
+                             unfolded; base.gist_set 1 or 2 (the chosen
+                             chunks' gists, or none, attended; every
+                             level's gists only route) on the bf16,
+                             head_dim 128 path (else
+                             GSA_ERR_UNSUPPORTED) */
   int32_t n_levels;       /* L, 2 <= L <= GSA_MAX_LEVELS */
   int32_t fanout;         /* G >= 2 */
   int32_t topk_up[GSA_MAX_LEVELS - 1]; /* topk_up[i] = k_{i+2}, for levels

@@ -401,7 +401,8 @@ def levels_ws(L, p):
     (lambda: good_levels(topk_up=(1, 6)), INVALID),              # k_1 = 8 > 4 level-1 candidates
     (lambda: good_levels(topk_up=(2, 6)), OK),
     (lambda: good_levels(fanout=1), INVALID),
-    (lambda: good_levels(gist_set=2, batch=128), UNSUPPORTED),
+    (lambda: good_levels(gist_set=2, batch=128), OK),              # the selection rules (unit path)
+    (lambda: good_levels(gist_set=1, head_dim=64), UNSUPPORTED),   # not on the split path
     (lambda: gsa.LevelsParams(good_decode(), 1, 4), INVALID),    # one level
     (lambda: gsa.LevelsParams(good_decode(), 7, 4), INVALID),    # above GSA_MAX_LEVELS
     (lambda: gsa.levels_params(good_decode(n_raw=16 * 4096, n_gist=4096, topk=8, tail=64), 2,

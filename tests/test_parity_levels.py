@@ -212,3 +212,74 @@ def test_levels_varlen_equal_lengths_is_levels(gsa):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     for x, y in zip(a[2], b[2]):
         assert torch.equal(x, y)
+
+
+# ------------------------------------------------------ selection rules ---
+
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+@pytest.mark.parametrize("i", [0, 2, 4])
+def test_levels_selection_rules(gsa, i, gist_set):
+    """The slide 17 rules on L-level decode (R20: every level's gists route,
+    the rule picks which gists are attended): one launch (top level in LDS)
+    and the two-launch path (top level above 4096 gists), against the oracle
+    with the same rule."""
+    c = CASES[i]
+    if i == 4:
+        # three levels with a top level of 5000 gists: the stream launch, then the descent
+        c = dict(B=1, Hq=8, Hkv=2, D=128, C=4, M=5000 * 16, r=2, G=4, topks=[8, 6, 4], T=16)
+    B, Hq, Hkv, D, C, M, r, G, topks, T = (c[k] for k in ("B", "Hq", "Hkv", "D", "C", "M", "r", "G", "topks", "T"))
+    if c.get("dtype", "bf16") != "bf16":
+        pytest.skip("the rules run on the bf16 path")
+    say(f"levels {gist_set} {c}")
+    L = len(topks)
+    N = M * C + r
+    q, k, v, ku, vu = gi.make_levels(B, Hq, Hkv, D, N, M, C, G, L, 9300 + i, device="cuda", values="int")
+    out, lse, sels = gsa.gsa_decode_levels(q, k, v, ku, vu, chunk=C, fanout=G, topks=topks, tail=T, n_gist=M,
+                                           gist_set=gist_set)
+    torch.cuda.synchronize()
+    g = Hq // Hkv
+    got, ref = [], []
+    units = [(b, j) for b in range(B) for j in range(Hkv)]
+    for b, j in units:
+        r_ = oracle.decode_levels_unit(to_np(q[b, j * g:(j + 1) * g]), to_np(k[b, j]), to_np(v[b, j]),
+                                       [(to_np(ku[l][b, j]), to_np(vu[l][b, j])) for l in range(L - 1)],
+                                       n_raw=N, n_gist=M, chunk=C, fanout=G, topks=topks, tail=T, gist_set=gist_set)
+        for lvl in range(L):
+            if topks[lvl] > 0:
+                np.testing.assert_array_equal(to_np(sels[lvl][b, j]), r_["sels"][lvl],
+                                              err_msg=f"unit {(b, j)} level {lvl + 1}")
+        got.append(to_np(out[b, j * g:(j + 1) * g]))
+        ref.append(r_["out"])
+        check_lse(to_np(lse[b, j * g:(j + 1) * g]), r_["lse"], "bf16", f"unit {(b, j)}")
+    err = check_out(np.stack(got), np.stack(ref), "bf16", str(c))
+    say(f"  max err / rms = {err:.2e}, {gsa.gsa_profile_marks() - 1} launches")
+
+
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+def test_levels_varlen_selection_rules(gsa, gist_set):
+    c = VARLEN_CASES[0]
+    say(f"levels varlen {gist_set} {c}")
+    q, k, v, ku, vu, n, m = levels_varlen_case(c, 9400)
+    topks, G, L = c["topks"], c["G"], len(c["topks"])
+    out, lse, sels = gsa.gsa_decode_levels_varlen(q, k, v, ku, vu, seq_n_raw=n, seq_n_gist=m, chunk=c["C"],
+                                                  fanout=G, topks=topks, tail=c["T"], gist_set=gist_set)
+    torch.cuda.synchronize()
+    g = c["Hq"] // c["Hkv"]
+    got, ref = [], []
+    for b in range(c["B"]):
+        sizes = [m[b]]
+        for _ in range(L - 1):
+            sizes.append(sizes[-1] // G)
+        for j in range(c["Hkv"]):
+            r_ = oracle.decode_levels_unit(to_np(q[b, j * g:(j + 1) * g]), to_np(k[b, j, :n[b] + m[b]]),
+                                           to_np(v[b, j, :n[b] + m[b]]),
+                                           [(to_np(ku[l][b, j, :sizes[l + 1]]), to_np(vu[l][b, j, :sizes[l + 1]]))
+                                            for l in range(L - 1)],
+                                           n_raw=n[b], n_gist=m[b], chunk=c["C"], fanout=G, topks=topks,
+                                           tail=c["T"], gist_set=gist_set)
+            for lvl in range(L):
+                np.testing.assert_array_equal(to_np(sels[lvl][b, j]), r_["sels"][lvl])
+            got.append(to_np(out[b, j * g:(j + 1) * g]))
+            ref.append(r_["out"])
+    err = check_out(np.stack(got), np.stack(ref), "bf16", str(c))
+    say(f"  max err / rms = {err:.2e}")
