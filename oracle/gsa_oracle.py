@@ -329,18 +329,19 @@ def gather_pages(pool: np.ndarray, pages: Sequence[int], *, page_chunks: int, ch
 
 def decode_paged_unit(qg: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, pages: Sequence[int], *,
                       page_chunks: int, n_raw: int, n_gist: int, chunk: int, topk: int, tail: int,
-                      extra_rows: Sequence[Tuple[int, int]] = (), scale: Optional[float] = None):
+                      extra_rows: Sequence[Tuple[int, int]] = (), scale: Optional[float] = None,
+                      gist_set: str = "all"):
     """One (sequence, kv-head) unit of decode over a paged cache (R18): the
     cache the pages spell out, plus the rows extra_rows lists as (page, row in
-    page) attended directly (R19). k_pool, v_pool: [n_pages, P (C + 1), D]
-    of this kv-head."""
+    page) attended directly (R19), under the selection rule gist_set (R12).
+    k_pool, v_pool: [n_pages, P (C + 1), D] of this kv-head."""
     R = n_raw + n_gist
     K = gather_pages(k_pool, pages, page_chunks=page_chunks, chunk=chunk, n_rows=R)
     V = gather_pages(v_pool, pages, page_chunks=page_chunks, chunk=chunk, n_rows=R)
     xk = np.stack([k_pool[pg, r] for pg, r in extra_rows]) if len(extra_rows) else np.zeros((0, K.shape[1]))
     xv = np.stack([v_pool[pg, r] for pg, r in extra_rows]) if len(extra_rows) else np.zeros((0, K.shape[1]))
     return decode_unit(qg, K, V, n_raw=n_raw, n_gist=n_gist, chunk=chunk, topk=topk, tail=tail, scale=scale,
-                       extra=(xk, xv))
+                       extra=(xk, xv), gist_set=gist_set)
 
 
 def decode_hier_unit(qg: np.ndarray, K: np.ndarray, V: np.ndarray, K2: np.ndarray,

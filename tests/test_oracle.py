@@ -863,6 +863,24 @@ def test_extra_rows_q_zero_closed_form():
     np.testing.assert_allclose(res["out"][0], want, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+def test_extra_rows_under_the_selection_rules_q_zero(gist_set):
+    """R12 with R19: the rule only changes which gist rows join the set; the
+    extra rows are attended under every rule. q = 0 makes the output the plain
+    mean of V over the set."""
+    rng = np.random.default_rng(921)
+    g, D, C, M, T = 1, 4, 4, 6, 4
+    N = M * C
+    _, K, V, M, R = rand_unit(rng, g, D, N, C, M)
+    xk, xv = rng.standard_normal((3, D)), rng.standard_normal((3, D))
+    res = oracle.decode_unit(np.zeros((g, D)), K, V, n_raw=N, n_gist=M, chunk=C, topk=2, tail=T, extra=(xk, xv),
+                             gist_set=gist_set)
+    rows = [m * (C + 1) + C for m in (0, 1)] if gist_set == "selected" else []
+    rows += [m * (C + 1) + j for m in (0, 1) for j in range(C)] + [5 * (C + 1) + j for j in range(C)]
+    want = (V[rows].sum(0) + xv.sum(0)) / (len(rows) + 3)
+    np.testing.assert_allclose(res["out"][0], want, rtol=0, atol=1e-12)
+
+
 def test_documents_ending_mid_chunk_route_and_keep_their_last_tokens():
     """Two documents built apart and reused (chunk-sized pages): the first ends
     two tokens into a chunk. Its complete chunks and the second document's
