@@ -441,8 +441,9 @@ def gsa_decode_paged(q, k_pool, v_pool, *, block_table, seq_n_raw, seq_n_gist, c
                      tail: int, page_chunks: int, extra_rows=None, n_raw: Optional[int] = None,
                      n_gist: Optional[int] = None, scale: float = 0.0, out=None, lse=None,
                      sel_idx=None, workspace=None, stream=None, want_lse: bool = True,
-                     want_sel: bool = True):
-    """Decode over paged caches. k_pool, v_pool [n_pages, Hkv, P(C+1), D];
+                     want_sel: bool = True, gist_set: str = "all"):
+    """Decode over paged caches (gist_set: as gsa_decode; extra rows are
+    attended under every rule). k_pool, v_pool [n_pages, Hkv, P(C+1), D];
     block_table [B, max_pages], seq_n_raw / seq_n_gist [B], extra_rows
     [B, max_extra, 2] (page, row) or None. Host arrays are checked with
     gsa_check_pages and copied to the device; device int32 tensors are used as
@@ -470,7 +471,10 @@ def gsa_decode_paged(q, k_pool, v_pool, *, block_table, seq_n_raw, seq_n_gist, c
         n_gist = int(m_h.max()) if n_gist is None else n_gist
         max_pages = bt_h.shape[1]
         max_extra = ex_h.shape[1] if ex_h is not None else 0
-    base = decode_params(B, Hq, Hkv, D, n_raw, n_gist, chunk, topk, tail, scale, _dtype_code(q))
+    if gist_set not in GIST_SETS:
+        raise ValueError(f"gist_set must be one of {tuple(GIST_SETS)}")
+    base = decode_params(B, Hq, Hkv, D, n_raw, n_gist, chunk, topk, tail, scale, _dtype_code(q),
+                         GIST_SETS[gist_set])
     p = paged_params(base, page_chunks, max_pages, n_pages, max_extra)
     if not on_dev:
         check_pages(p, bt_h, n_h, m_h, ex_h)

@@ -1967,6 +1967,7 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
     if (KIND == kUKScore) return i * (C + 1) + C;
     if (KIND == kUKSet && i >= kC) {
       if (i < kC + kg) return (int)(min((unsigned)lds_sel[i - kC], (unsigned)(M - 1)) * (unsigned)(C + 1) + (unsigned)C);
+      if (PAGED && i - kC - kg >= a.T) return kExtraRow + (i - kC - kg - a.T);
       const unsigned pos = tail0 + (unsigned)(i - kC - kg);
       return (int)(pos + min(pos / (unsigned)C, (unsigned)M));
     }
@@ -1995,13 +1996,16 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
   auto paged_slot = [&](int i, int row, unsigned& pi, unsigned& slot) {
     unsigned m = 0, j = 0;
     if (row >= 0 && row < kExtraRow) {
-      if (KIND == kUKGists && i < M) {
+      if ((KIND == kUKGists || KIND == kUKScore) && i < M) {
         m = (unsigned)i;
         j = (unsigned)C;
-      } else if (KIND == kUKGists) {   // tail position
-        const unsigned pos = tail0 + (unsigned)(i - M);
+      } else if (KIND == kUKGists || (KIND == kUKSet && i >= kC + kg)) {   // tail position
+        const unsigned pos = tail0 + (unsigned)(i - (KIND == kUKGists ? M : kC + kg));
         m = min(pos / (unsigned)C, (unsigned)M);
         j = pos - m * (unsigned)C;
+      } else if (KIND == kUKSet && i >= kC) {   // a chosen chunk's gist (rule 1)
+        m = min((unsigned)lds_sel[i - kC], (unsigned)(M - 1));
+        j = (unsigned)C;
       } else {                         // chosen chunk's raw row
         const unsigned ci = (unsigned)i / (unsigned)C;
         m = min((unsigned)lds_sel[ci], (unsigned)(M - 1));
@@ -2046,8 +2050,15 @@ __device__ __forceinline__ void unit_stream(const char* __restrict__ Kb, const c
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int r = 4 * (u & 3) + (lane >> 4);
-        const int row = row_of(i0 + b * kRows + 16 * (u >> 2) + r);
-        const int64_t koffr = (int64_t)(row >= 0 ? row : 0) * 256;
+        const int i = i0 + b * kRows + 16 * (u >> 2) + r;
+        const int row = row_of(i);
+        int64_t koffr = (int64_t)(row >= 0 ? row : 0) * 256;
+        if constexpr (PAGED) {
+          // gist i of the sequence: its page's slot, through the staged block table
+          unsigned pi, slot;
+          paged_slot(i, row, pi, slot);
+          koffr = row >= 0 ? (int64_t)lds_at(pl->pages, pi) * a.pg_bytes + (int64_t)slot * 256 : 0;
+        }
         __builtin_amdgcn_global_load_lds(Kb + koffr + uk_slot(sl, r) * 16, kd + (u >> 2) * kUTile + (u & 3) * 1024, 16,
                                          0, kUNt);
       }
@@ -2447,7 +2458,7 @@ enum { kHierNone = 0, kHierDescend = 1, kHierTop = 2 };
 // PAGED (with VARLEN): the caches are page pools (gsa_decode_paged).
 template <int G, int HIER, bool SETS = false, bool VARLEN = false, bool SPLIT = true, bool PAGED = false>
 __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
-  static_assert(!PAGED || (VARLEN && !HIER && !SETS), "paged caches: single-level, per-sequence lengths");
+  static_assert(!PAGED || (VARLEN && !HIER), "paged caches: single-level, per-sequence lengths");
   __shared__ __attribute__((aligned(16))) std::conditional_t<PAGED, PagedLds, UnitLds> L;
   UnitArgs a = args;
   // the wave index as a scalar: each wave's item ranges and trip counts are
@@ -2528,8 +2539,8 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
     const int perg = (M + S - 1) / S;
     const int g0 = min(M, split * perg), g1 = min(M, g0 + perg);
     const int pw = (g1 - g0 + kUW - 1) / kUW;
-    unit_stream<kUKScore>(Kb, Vb, min(g1, g0 + w * pw), min(g1, g0 + (w + 1) * pw), a, qf, st, ring, L.scores,
-                          L.sel, g0);
+    unit_stream<kUKScore, PAGED>(Kb, Vb, min(g1, g0 + w * pw), min(g1, g0 + (w + 1) * pw), a, qf, st, ring,
+                                 L.scores, L.sel, g0, nullptr, nullptr, pl);
     float* gs = a.scores + (size_t)unit * a.score_stride;
     __syncthreads();   // every score of the share is in LDS
     if (a.k > kCandMaxK) {
@@ -2546,7 +2557,8 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
     // the scores only; then the chosen chunks' raw rows, their gists if the
     // set keeps them, and the tail, all attended
     const int perg = (M + kUW - 1) / kUW;
-    unit_stream<kUKScore>(Kb, Vb, min(M, w * perg), min(M, (w + 1) * perg), a, qf, st, ring, L.scores, L.sel);
+    unit_stream<kUKScore, PAGED>(Kb, Vb, min(M, w * perg), min(M, (w + 1) * perg), a, qf, st, ring, L.scores, L.sel,
+                                 0, nullptr, nullptr, pl);
     __syncthreads();   // every group score is in LDS, every ring idle
     float* gsv = a.scores + (size_t)unit * a.score_stride;
     if (a.k > 0) {
@@ -2554,9 +2566,10 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
                                                L.u.sel.t);
       __syncthreads();
     }
-    const int n3 = a.k * a.C + (a.gist_set == 1 ? a.k : 0) + a.T;
+    const int n3 = a.k * a.C + (a.gist_set == 1 ? a.k : 0) + a.T + n_extra;   // (paged: the extra rows last)
     const int per3 = (n3 + kUW - 1) / kUW;
-    unit_stream<kUKSet>(Kb, Vb, min(n3, w * per3), min(n3, (w + 1) * per3), a, qf, st, ring, L.scores, L.sel);
+    unit_stream<kUKSet, PAGED>(Kb, Vb, min(n3, w * per3), min(n3, (w + 1) * per3), a, qf, st, ring, L.scores, L.sel,
+                               0, nullptr, nullptr, pl);
     unit_combine<G>(L, st, w, a.out + (size_t)unit * G * 128, a.lse ? a.lse + (size_t)unit * G : nullptr, nullptr);
     if (a.sel)
       for (int i = tid; i < a.k; i += kUW * 64) a.sel[(size_t)unit * a.k + i] = L.sel[i];
@@ -2623,7 +2636,7 @@ __global__ __launch_bounds__(kUW * 64) void unit_kernel(UnitArgs args) {
 template <int G, bool VARLEN = false, bool PAGED = false, bool SETS = false>
 __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   static_assert(!PAGED || VARLEN, "paged caches: per-sequence lengths");
-  static_assert(!SETS || !PAGED, "selection-rule variants: unpaged caches");
+
   __shared__ __attribute__((aligned(16))) std::conditional_t<PAGED, PagedLds, UnitLds> L;
   UnitArgs a = args;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2666,13 +2679,15 @@ __global__ __launch_bounds__(kUW * 64) void unit_unfold_kernel(UnitArgs args) {
   }
   GSA_STAMP(9);
   // SETS: raw rows of the chosen chunks, their gists (rule 1), then the tail
-  const int items = a.k * a.C + (SETS ? (a.gist_set == 1 ? a.k : 0) + a.T : 0);
+  // SETS: raw rows, their gists (rule 1), the tail, then (paged) the extra rows
+  int items = a.k * a.C + (SETS ? (a.gist_set == 1 ? a.k : 0) + a.T : 0);
+  if constexpr (SETS && PAGED) items += L.n_extra;
   const int perp = (items + S2 - 1) / S2;
   const int p0 = min(items, part * perp), p1 = min(items, p0 + perp);
   const int per2 = (p1 - p0 + kUW - 1) / kUW;
   if constexpr (SETS)
-    unit_stream<kUKSet>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st, L.u.ring[w][0],
-                        L.scores, L.sel);
+    unit_stream<kUKSet, PAGED>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st, L.u.ring[w][0],
+                        L.scores, L.sel, 0, nullptr, nullptr, pl);
   else
     unit_stream<kUKUnfold, PAGED>(Kb, Vb, min(p1, p0 + w * per2), min(p1, p0 + (w + 1) * per2), a, qf, st,
                                   L.u.ring[w][0], L.scores, L.sel, 0, nullptr, nullptr, pl);
@@ -3067,13 +3082,23 @@ gsa_status_t run_unit(const DecodePlan& pl, const void* q, const void* K, const 
     u.pg_rpp = pl.pg_P * (pl.C + 1);
     u.pg_bytes = (int64_t)pl.Hkv * u.pg_rpp * 256;
     u.pg_head_bytes = (int64_t)u.pg_rpp * 256;
+    const dim3 block(kUW * 64);
+    if (pl.gist_set != GSA_GISTS_ALL) {   // the selection rules: score, then attend the set
+      if (pl.unit_S == 1) {
+        prof_launch((unit_kernel<G, kHierNone, true, true, false, true>), dim3(pl.units), block, 0, st, u);
+      } else {
+        if (pl.k > 0)
+          prof_launch((unit_kernel<G, kHierNone, true, true, true, true>), dim3(pl.units * pl.unit_S), block, 0, st, u);
+        prof_launch((unit_unfold_kernel<G, true, true, true>), dim3(pl.units * pl.unit_S2), block, 0, st, u);
+      }
+      return launch_status("gsa_decode_paged launch");
+    }
     if (pl.unit_S == 1)
-      prof_launch((unit_kernel<G, kHierNone, false, true, false, true>), dim3(pl.units), dim3(kUW * 64), 0, st, u);
+      prof_launch((unit_kernel<G, kHierNone, false, true, false, true>), dim3(pl.units), block, 0, st, u);
     else
-      prof_launch((unit_kernel<G, kHierNone, false, true, true, true>), dim3(pl.units * pl.unit_S), dim3(kUW * 64), 0,
-                  st, u);
+      prof_launch((unit_kernel<G, kHierNone, false, true, true, true>), dim3(pl.units * pl.unit_S), block, 0, st, u);
     if (pl.unit_S2 > 0)
-      prof_launch((unit_unfold_kernel<G, true, true>), dim3(pl.units * pl.unit_S2), dim3(kUW * 64), 0, st, u);
+      prof_launch((unit_unfold_kernel<G, true, true>), dim3(pl.units * pl.unit_S2), block, 0, st, u);
     return launch_status("gsa_decode_paged launch");
   }
   if (pl.gist_set != GSA_GISTS_ALL) {

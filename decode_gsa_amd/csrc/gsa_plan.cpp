@@ -236,8 +236,6 @@ gsa_status_t plan_paged(const gsa_paged_params* p, DecodePlan* o) {
   if (!p || !o) return fail(GSA_ERR_INVALID_ARG, "params is NULL");
   if (p->base.row_capacity != 0)
     return fail(GSA_ERR_INVALID_ARG, "paged decode: base.row_capacity must be 0 (pages hold the rows)");
-  if (p->base.gist_set != GSA_GISTS_ALL)
-    return fail(GSA_ERR_UNSUPPORTED, "paged decode attends every gist: base.gist_set must be 0");
   gsa_status_t s = plan_decode(&p->base, o);
   if (s != GSA_OK) return s;
   const int32_t P = p->page_chunks;

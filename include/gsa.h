@@ -92,7 +92,8 @@ typedef struct {
                           routing stays the same; gsa_decode_varlen on
                           every shape; gsa_decode_levels and
                           gsa_decode_levels_varlen on their bf16,
-                          head_dim 128 path. gsa_decode_paged requires 0. */
+                          head_dim 128 path; gsa_decode_paged on every
+                          shape it accepts. */
   int64_t row_capacity; /* rows allocated per (sequence, kv-head) in the
                           caches, the stride between their [R, D] blocks:
                           0 means exactly R = N + M; else it must be
@@ -185,9 +186,10 @@ gsa_status_t gsa_decode_varlen(const gsa_decode_params* p, const int32_t* seq_n_
 typedef struct {
   gsa_decode_params base; /* as gsa_decode_varlen: n_raw / n_gist are the
                              batch's largest; bf16, head_dim 128, topk <= 64
-                             (n_gist <= 16384 when topk > 0), gist_set 0,
-                             row_capacity 0; else GSA_ERR_UNSUPPORTED /
-                             GSA_ERR_INVALID_ARG */
+                             (n_gist <= 16384 when topk > 0), row_capacity
+                             0; else GSA_ERR_UNSUPPORTED /
+                             GSA_ERR_INVALID_ARG. gist_set as gsa_decode:
+                             the extra rows are attended under every rule */
   int32_t page_chunks;    /* P: chunk slots per page, a power of two in [1, 64] */
   int32_t max_pages;      /* columns of block_table, >= the pages of
                              n_raw + n_gist rows, <= 2048 */

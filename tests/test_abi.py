@@ -702,7 +702,8 @@ def good_paged(base_kw=None, **kw):
     ({"head_dim": 64}, {}, UNSUPPORTED),
     ({"topk": 80, "n_raw": 4096 * 4, "n_gist": 1024}, {"max_pages": 256}, UNSUPPORTED),
     ({"row_capacity": 9000}, {}, INVALID),
-    ({"gist_set": 1}, {}, UNSUPPORTED),
+    ({"gist_set": 1}, {}, OK),                         # the selection rules
+    ({"gist_set": 2, "topk": 0, "tail": 0}, {}, INVALID),   # nothing to attend
 ])
 def test_paged_param_validation(L, base_kw, kw, status):
     n = ctypes.c_size_t(0)

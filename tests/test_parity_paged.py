@@ -190,3 +190,44 @@ def test_reused_documents_ending_mid_chunk(gsa):
             ref.append(r["out"])
             check_lse(to_np(lse[b, j * g:(j + 1) * g]), r["lse"], "bf16", f"seq {b}")
     check_out(np.stack(got), np.stack(ref), "bf16", "reused documents")
+
+
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+@pytest.mark.parametrize("many", [False, True], ids=["one-wg", "split"])
+def test_paged_selection_rules(gsa, many, gist_set):
+    """The slide 17 rules over paged caches with extra rows: the gists' K rows
+    are scored through the block table, then the set (chosen raw rows, their
+    gists under rule 1, the tail and the extra rows) is attended; against the
+    oracle with the same rule, unit by unit."""
+    B, Hq, Hkv, C, P, k, T = (2, 8, 2, 16, 4, 16, 64) if many else (32, 32, 8, 16, 4, 16, 64)
+    n_min, n_max = (20000, 40000) if many else (1000, 3000)
+    q, kc, vc, n, m = dense_case(B, Hq, Hkv, C, n_min, n_max, 7600 + many)
+    rows = [a + b for a, b in zip(n, m)]
+    kp, vp, table = gi.to_pages(kc, vc, rows, P, C, 7700, spare=6)
+    n_pages, rpp = kp.shape[0], kp.shape[2]
+    rng = np.random.default_rng(7800 + many)
+    max_extra = 8
+    extra = np.full((B, max_extra, 2), -1, dtype=np.int32)
+    counts = rng.integers(0, max_extra + 1, size=B)
+    for b in range(B):
+        for e in range(counts[b]):
+            extra[b, e] = (rng.integers(n_pages), rng.integers(rpp))
+    say(f"paged {gist_set} many={many}")
+    out, lse, sel = gsa.gsa_decode_paged(q, kp, vp, block_table=table, seq_n_raw=n, seq_n_gist=m, chunk=C,
+                                         topk=k, tail=T, page_chunks=P, extra_rows=extra, gist_set=gist_set)
+    torch.cuda.synchronize()
+    g = Hq // Hkv
+    units = [(b, j) for b in range(B) for j in range(Hkv)]
+    pick = units if len(units) <= 8 else [units[i] for i in rng.choice(len(units), 10, False)]
+    got, ref = [], []
+    for b, j in pick:
+        xs = [(int(p_), int(r_)) for p_, r_ in extra[b] if p_ >= 0][:counts[b]]
+        r = oracle.decode_paged_unit(to_np(q[b, j * g:(j + 1) * g]), to_np(kp[:, j]), to_np(vp[:, j]),
+                                     [int(x) for x in table[b]], page_chunks=P, n_raw=n[b], n_gist=m[b],
+                                     chunk=C, topk=k, tail=T, extra_rows=xs, gist_set=gist_set)
+        np.testing.assert_array_equal(to_np(sel[b, j]), r["sel"], err_msg=f"unit {(b, j)}")
+        got.append(to_np(out[b, j * g:(j + 1) * g]))
+        ref.append(r["out"])
+        check_lse(to_np(lse[b, j * g:(j + 1) * g]), r["lse"], "bf16", f"unit {(b, j)}")
+    err = check_out(np.stack(got), np.stack(ref), "bf16", f"paged {gist_set}")
+    say(f"  max err / rms = {err:.2e}, {gsa.gsa_profile_marks() - 1} launches")
