@@ -1339,7 +1339,10 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   g.unit_rows = hp.M2; g.n_items = hp.M2; g.per_task = hp.l2_per_split; g.tasks = hp.S_l2;
   g.rm = RowMap{1, pl.C, nullptr, 0, 0, 0, 0};
   g.Kt = K; g.Vt = V; g.tail_unit_rows = pl.R;
-  g.N = pl.N; g.M = pl.M; g.C = pl.C; g.T = pl.T; g.tail_per_task = hp.tail_per_split;
+  // selection rules: every pass before the unfold only scores (their partial
+  // states are not merged) and the tail goes to the set's pass
+  const bool sets = pl.gist_set != GSA_GISTS_ALL;
+  g.N = pl.N; g.M = pl.M; g.C = pl.C; g.T = pl.T; g.tail_per_task = sets ? 0 : hp.tail_per_split;
   g.scores = s2; g.score_stride = hp.s2_stride;
   g.part = part; g.part_stride = ps; g.NP = hp.NP; g.part_base = 0;
   g.out = nullptr; g.lse = nullptr;
@@ -1373,14 +1376,15 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   }
   c.sel2_ws = wsel2; c.sel2_stride = hp.sel2_stride; c.sel2_out = sel2;
   c.part_base = hp.S_l2;
-  c.out = pl.k > 0 ? nullptr : out; c.lse = pl.k > 0 ? nullptr : lse;
+  c.out = pl.k > 0 || sets ? nullptr : out; c.lse = pl.k > 0 || sets ? nullptr : lse;
   c.cnt = ctrl_of(ws, hp.off_ctrl, 1);
   prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * hp.S_c), dim3(kThreads), 0, st, c);
-  // unfold the chosen chunks, merge everything
-  if (pl.k > 0) {
+  // unfold the chosen chunks, merge everything (selection rules: attend the
+  // set, merge its own partial states)
+  if (pl.k > 0 || sets) {
     UnfoldArgs u{};
     u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
-    u.scores = sc; u.score_stride = hp.sc_stride; u.n_cand = hp.n_cand;
+    u.scores = pl.k > 0 ? sc : nullptr; u.score_stride = hp.sc_stride; u.n_cand = hp.n_cand;
     u.im = IdMap{wsel2, hp.G, hp.k2, orphan0, hp.sel2_stride};
     u.sel_ws = reinterpret_cast<int32_t*>(ws + hp.off_sel1); u.sel_stride = pl.sel_stride;
     u.sel_out = sel1; u.k = pl.k;
@@ -1389,6 +1393,9 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
     u.part = part; u.part_stride = ps; u.NP = hp.NP; u.part_base = hp.S_l2 + hp.S_c;
     u.out = out; u.lse = lse;
     u.cnt = ctrl_of(ws, hp.off_ctrl, 2);
+    u.set_kg = pl.gist_set == GSA_GISTS_SELECTED ? pl.k : 0;
+    u.set_tail = sets ? pl.T : 0;
+    u.merge_base = sets ? hp.S_l2 + hp.S_c : 0;
     u.scale_log2 = pl.scale * kLog2e;
     prof_launch((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
   }
@@ -3185,7 +3192,10 @@ gsa_status_t run_levels(const LevelsPlan& lp, const void* q, const void* K, cons
   g.unit_rows = lp.Ml[L]; g.n_items = lp.items[L]; g.per_task = lp.per_split[L]; g.tasks = lp.S[L];
   g.rm = RowMap{1, pl.C, nullptr, 0, 0, 0, 0};
   g.Kt = K; g.Vt = V; g.tail_unit_rows = pl.R;
-  g.N = pl.N; g.M = pl.M; g.C = pl.C; g.T = pl.T; g.tail_per_task = lp.tail_per_split;
+  // selection rules: every level pass only scores (their partial states are
+  // not merged) and the tail goes to the set's pass
+  const bool sets = pl.gist_set != GSA_GISTS_ALL;
+  g.N = pl.N; g.M = pl.M; g.C = pl.C; g.T = pl.T; g.tail_per_task = sets ? 0 : lp.tail_per_split;
   g.scores = scores(L); g.score_stride = lp.score_stride[L];
   g.part = part; g.part_stride = ps; g.NP = lp.NP; g.part_base = 0;
   g.out = nullptr; g.lse = nullptr;
@@ -3204,8 +3214,8 @@ gsa_status_t run_levels(const LevelsPlan& lp, const void* q, const void* K, cons
     // kind 2 with C = 0 gives dense rows of a level array
     c.rm = RowMap{2, l >= 2 ? 0 : pl.C, nullptr, lp.G, lp.kl[l + 1], lp.orphan0[l], 0};
     c.T = 0; c.tail_per_task = 0;
-    const bool last = l == 1 && pl.k == 0;
-    c.scores = last ? nullptr : scores(l); c.score_stride = lp.score_stride[l];
+    const bool last = l == 1 && pl.k == 0 && !sets;
+    c.scores = l == 1 && pl.k == 0 ? nullptr : scores(l); c.score_stride = lp.score_stride[l];
     c.prev_scores = scores(l + 1); c.prev_stride = lp.score_stride[l + 1];
     c.prev_n = (int32_t)lp.items[l + 1]; c.prev_k = lp.kl[l + 1];
     c.prev_im = l + 1 == L ? IdMap{nullptr, 0, 0, 0, 0}
@@ -3218,10 +3228,11 @@ gsa_status_t run_levels(const LevelsPlan& lp, const void* q, const void* K, cons
     prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * lp.S[l]), dim3(kThreads), 0, st, c);
     base += lp.S[l];
   }
-  if (pl.k > 0) {
+  if (pl.k > 0 || sets) {
     UnfoldArgs u{};
     u.q = q; u.K = K; u.V = V; u.unit_rows = pl.R;
-    u.scores = scores(1); u.score_stride = lp.score_stride[1]; u.n_cand = (int32_t)lp.items[1];
+    u.scores = pl.k > 0 ? scores(1) : nullptr; u.score_stride = lp.score_stride[1];
+    u.n_cand = (int32_t)lp.items[1];
     u.im = IdMap{selws(2), lp.G, lp.kl[2], lp.orphan0[1], lp.sel_stride[2]};
     u.sel_ws = reinterpret_cast<int32_t*>(ws + lp.off_sel1); u.sel_stride = pl.sel_stride;
     u.sel_out = sel1; u.k = pl.k;
@@ -3230,6 +3241,9 @@ gsa_status_t run_levels(const LevelsPlan& lp, const void* q, const void* K, cons
     u.part = part; u.part_stride = ps; u.NP = lp.NP; u.part_base = base;
     u.out = out; u.lse = lse;
     u.cnt = ctrl_of(ws, lp.off_ctrl, L);
+    u.set_kg = pl.gist_set == GSA_GISTS_SELECTED ? pl.k : 0;
+    u.set_tail = sets ? pl.T : 0;
+    u.merge_base = sets ? base : 0;
     u.scale_log2 = pl.scale * kLog2e;
     prof_launch((unfold_kernel<BF16, D, G>), dim3(pl.units * pl.S2), dim3(kThreads), 0, st, u);
   }

@@ -310,10 +310,18 @@ gsa_status_t plan_hier(const gsa_hier_params* p, HierPlan* o) {
       if (h.NP < h.unit_S + 1) h.NP = h.unit_S + 1;   // level-2 stream partials + the rest's
     }
   }
-  if (d.gist_set != GSA_GISTS_ALL && h.unit_S == 0)
-    return fail(GSA_ERR_UNSUPPORTED,
-                "two-level decode with gist_set=%d runs on the bf16, head_dim 128 path (topk, topk2 <= 64, at "
-                "most 4096 level-1 candidates)", d.gist_set);
+  if (d.gist_set != GSA_GISTS_ALL && h.unit_S == 0) {
+    // split path, selection rules: the level-2 and candidate passes only
+    // score; the unfold pass attends the whole set (chosen raw rows, their
+    // gists with rule 1, the tail) and merges its own partial states alone
+    const int64_t set_items = (int64_t)d.k * d.C + (d.gist_set == GSA_GISTS_SELECTED ? d.k : 0) + d.T;
+    if (set_items > (1 << 30)) return fail(GSA_ERR_UNSUPPORTED, "selection too large");
+    h.base.n_items = (int32_t)set_items;
+    h.base.S2 = splits_for(set_items, units, kMinUnfoldRows);
+    h.base.items_per_split = (int32_t)ceil_div(set_items, h.base.S2);
+    h.base.S2 = (int32_t)ceil_div(set_items, h.base.items_per_split);
+    h.NP = h.S_l2 + h.S_c + h.base.S2;
+  }
   h.s2_stride = (h.M2 + 63) / 64 * 64;
   h.sc_stride = d.k > 0 ? (h.n_cand + 63) / 64 * 64 : 0;
   size_t off = 0;
@@ -471,10 +479,19 @@ gsa_status_t plan_levels(const gsa_levels_params* p, LevelsPlan* o) {
       }
     }
   }
-  if (d.gist_set != GSA_GISTS_ALL && h.unit_S == 0)
-    return fail(GSA_ERR_UNSUPPORTED,
-                "L-level decode with gist_set=%d runs on the bf16, head_dim 128 path (every k <= 64, at most 4096 "
-                "candidates per level)", d.gist_set);
+  if (d.gist_set != GSA_GISTS_ALL && h.unit_S == 0) {
+    // split path, selection rules: the level passes only score; the unfold
+    // pass attends the set (chosen raw rows, their gists with rule 1, the
+    // tail) and merges its own partial states alone
+    const int64_t set_items = (int64_t)d.k * d.C + (d.gist_set == GSA_GISTS_SELECTED ? d.k : 0) + d.T;
+    if (set_items > (1 << 30)) return fail(GSA_ERR_UNSUPPORTED, "selection too large");
+    const int32_t S2_all = d.S2;
+    h.base.n_items = (int32_t)set_items;
+    h.base.S2 = splits_for(set_items, units, kMinUnfoldRows);
+    h.base.items_per_split = (int32_t)ceil_div(set_items, h.base.S2);
+    h.base.S2 = (int32_t)ceil_div(set_items, h.base.items_per_split);
+    h.NP = h.NP - S2_all + h.base.S2;
+  }
   size_t off = 0;
   h.off_ctrl = off;
   off = align_up(off + ctrl_bytes(units));
@@ -597,12 +614,12 @@ int32_t decode_launches(const DecodePlan& d) {
 
 int32_t hier_launches(const HierPlan& h) {
   if (h.unit_S > 0) return 1;
-  return 2 + (h.cand2_stride > 0 ? 1 : 0) + (h.base.k > 0 ? 1 : 0);
+  return 2 + (h.cand2_stride > 0 ? 1 : 0) + (h.base.k > 0 || h.base.gist_set != GSA_GISTS_ALL ? 1 : 0);
 }
 
 int32_t levels_launches(const LevelsPlan& l) {
   if (l.unit_S > 0) return levels_top_in_lds(l) ? 1 : 2;
-  return l.L + (l.base.k > 0 ? 1 : 0);
+  return l.L + (l.base.k > 0 || l.base.gist_set != GSA_GISTS_ALL ? 1 : 0);
 }
 
 int32_t prefill_launches(const PrefillPlan& p) {

@@ -85,14 +85,13 @@ typedef struct {
                           GSA_GISTS_NONE (2, raw tokens only: SR-only).
                           1 and 2 need k > 0 or T > 0 (a non-empty set);
                           gsa_decode and gsa_decode_noalloc run them on
-                          every shape they accept; gsa_decode_hier and
-                          gsa_decode_hier_varlen on their bf16, head_dim
-                          128 path (else GSA_ERR_UNSUPPORTED), the rule
+                          every shape they accept; so do
+                          gsa_decode_hier and gsa_decode_levels, the rule
                           deciding which gists are attended while the
-                          routing stays the same; gsa_decode_varlen on
-                          every shape; gsa_decode_levels and
-                          gsa_decode_levels_varlen on their bf16,
-                          head_dim 128 path; gsa_decode_paged on every
+                          routing stays the same; gsa_decode_varlen,
+                          gsa_decode_hier_varlen and
+                          gsa_decode_levels_varlen on every shape they
+                          accept; gsa_decode_paged on every
                           shape it accepts. */
   int64_t row_capacity; /* rows allocated per (sequence, kv-head) in the
                           caches, the stride between their [R, D] blocks:
@@ -246,8 +245,7 @@ gsa_status_t gsa_check_seq_lens(const gsa_decode_params* p, const int32_t* seq_n
  * children of each chosen group, plus the ungrouped ones), the raw rows of
  * the k1 chosen chunks and the tail. With base.gist_set 1 (2) the set is the
  * chosen chunks' gists (no gist), their raw rows and the tail: the level-2
- * and candidate gists only route (bf16, head_dim 128, topk, topk2 <= 64, at
- * most 4096 level-1 candidates; else GSA_ERR_UNSUPPORTED).
+ * and candidate gists only route (every dtype and head_dim).
  * ---------------------------------------------------------------------- */
 typedef struct {
   gsa_decode_params base; /* level-1 cache; base.topk = k1 */
@@ -320,9 +318,7 @@ typedef struct {
   gsa_decode_params base; /* level 1 and the step: base.topk = k_1 chunks
                              unfolded; base.gist_set 1 or 2 (the chosen
                              chunks' gists, or none, attended; every
-                             level's gists only route) on the bf16,
-                             head_dim 128 path (else
-                             GSA_ERR_UNSUPPORTED) */
+                             level's gists only route) */
   int32_t n_levels;       /* L, 2 <= L <= GSA_MAX_LEVELS */
   int32_t fanout;         /* G >= 2 */
   int32_t topk_up[GSA_MAX_LEVELS - 1]; /* topk_up[i] = k_{i+2}, for levels
@@ -590,10 +586,11 @@ gsa_status_t gsa_profile_marks(int32_t* n);
  *     level-2 stream, whose last workgroup per unit runs the descent);
  *     other shapes: 2 to 4 (a level-2
  *     pass, possibly a pass over its splits' top-k2, a level-1 candidate
- *     pass, and an unfold pass when topk1 > 0);
+ *     pass, and an unfold pass when topk1 > 0 or base.gist_set is 1 or 2);
  *   gsa_decode_levels on the bf16, D = 128, every k <= 64 path: 1 when the
  *     top level holds <= 4096 gists and top + tail <= 5120 rows, else 2;
- *     other shapes: one pass per level and an unfold pass when k_1 > 0;
+ *     other shapes: one pass per level and an unfold pass when k_1 > 0 or
+ *     base.gist_set is 1 or 2;
  *   gsa_prefill_blocksparse: 0 when n_q = 0, else a selection launch when
  *     topk > 0 and an attention launch.
  * GSA_ERR_INVALID_ARG for a NULL n. */

@@ -382,7 +382,8 @@ def test_cache_append_rejects_overlap(L):
 
 def good_levels(n_levels=3, fanout=4, topk_up=(6, 4), **kw):
     # M = 640 gists: level sizes 640, 160, 40 (L = 3)
-    base = good_decode(n_raw=16 * 640, n_gist=640, topk=8, tail=64, **kw)
+    kw = {"topk": 8, **kw}
+    base = good_decode(n_raw=16 * 640, n_gist=640, tail=64, **kw)
     return gsa.levels_params(base, fanout, list(topk_up)[:n_levels - 1]) if n_levels >= 2 else None
 
 
@@ -402,7 +403,8 @@ def levels_ws(L, p):
     (lambda: good_levels(topk_up=(2, 6)), OK),
     (lambda: good_levels(fanout=1), INVALID),
     (lambda: good_levels(gist_set=2, batch=128), OK),              # the selection rules (unit path)
-    (lambda: good_levels(gist_set=1, head_dim=64), UNSUPPORTED),   # not on the split path
+    (lambda: good_levels(gist_set=1, head_dim=64), OK),            # the split path
+    (lambda: good_levels(gist_set=2, head_dim=64, topk=0), OK),    # the tail only
     (lambda: gsa.LevelsParams(good_decode(), 1, 4), INVALID),    # one level
     (lambda: gsa.LevelsParams(good_decode(), 7, 4), INVALID),    # above GSA_MAX_LEVELS
     (lambda: gsa.levels_params(good_decode(n_raw=16 * 4096, n_gist=4096, topk=8, tail=64), 2,
@@ -505,8 +507,9 @@ def test_decode_hier_varlen_rejections(L):
 @pytest.mark.parametrize("kw,status", [
     ({"gist_set": 1}, OK),
     ({"gist_set": 2}, OK),
-    ({"gist_set": 2, "dtype": gsa.GSA_F32}, UNSUPPORTED),     # the split path runs every gist only
-    ({"gist_set": 1, "head_dim": 64}, UNSUPPORTED),
+    ({"gist_set": 2, "dtype": gsa.GSA_F32}, OK),              # the split path
+    ({"gist_set": 1, "head_dim": 64}, OK),
+    ({"gist_set": 2, "dtype": gsa.GSA_F32, "topk": 0}, OK),   # the tail only
     ({"gist_set": 3}, INVALID),
     ({"gist_set": 1, "topk": 0, "tail": 0}, INVALID),         # nothing to attend
 ])
@@ -646,6 +649,9 @@ def test_launch_counts_follow_the_documented_rules(L):
     hf0 = gsa.decode_params(2, 8, 2, 64, 1 << 16, 1 << 12, 16, 0, 64, dtype=gsa.GSA_F32)
     st, n = _launches(L, "gsa_decode_hier_launches", gsa.HierParams(hf0, 16, 8))
     assert st == OK and n in (2, 3)
+    hf0.gist_set = 2   # the selection rules: the set's pass runs with k1 = 0 too
+    st, m = _launches(L, "gsa_decode_hier_launches", gsa.HierParams(hf0, 16, 8))
+    assert st == OK and m == n + 1
     # L levels
     lb = gsa.decode_params(1, 32, 8, 128, 1 << 21, 1 << 17, 16, 16, 64)
     small_top = gsa.levels_params(lb, 16, [8, 8, 8])      # top level 32 gists

@@ -56,26 +56,29 @@ def test_decode_marks(gsa, case):
     assert gsa.gsa_profile_marks() == gsa.launches(p) + 1
 
 
-HIER = [  # D, dtype, N, G, k1, k2
-    (128, torch.bfloat16, 65536, 16, 8, 4),
-    (64, torch.float32, 65536, 16, 8, 4),
-    (64, torch.float32, 65536, 16, 0, 4),
+HIER = [  # D, dtype, N, G, k1, k2, gist_set
+    (128, torch.bfloat16, 65536, 16, 8, 4, 0),
+    (64, torch.float32, 65536, 16, 8, 4, 0),
+    (64, torch.float32, 65536, 16, 0, 4, 0),
+    (64, torch.float32, 65536, 16, 8, 4, 1),
+    (64, torch.float32, 65536, 16, 0, 4, 2),   # the selection rules: the set's pass runs with k1 = 0
 ]
 
 
 @pytest.mark.parametrize("case", HIER)
 def test_hier_marks(gsa, case):
-    D, dt, N, G, k1, k2 = case
+    D, dt, N, G, k1, k2, rule = case
     C, T, Hq, Hkv = 16, 64, 4, 1
     M = N // C
     say("hier launches", case)
     kc, vc = cache(1, Hkv, N, M, D, dt, 2)
     k2a = torch.randn(1, Hkv, M // G, D).to(dt).cuda()
     q = torch.randn(1, Hq, D).to(dt).cuda()
-    gsa.gsa_decode_hier(q, kc, vc, k2a, k2a, chunk=C, fanout=G, topk1=k1, topk2=k2, tail=T)
+    gsa.gsa_decode_hier(q, kc, vc, k2a, k2a, chunk=C, fanout=G, topk1=k1, topk2=k2, tail=T,
+                        gist_set=["all", "selected", "none"][rule])
     torch.cuda.synchronize()
     base = gsa.decode_params(1, Hq, Hkv, D, N, M, C, k1, T, 0.0,
-                             gsa.GSA_BF16 if dt == torch.bfloat16 else gsa.GSA_F32)
+                             gsa.GSA_BF16 if dt == torch.bfloat16 else gsa.GSA_F32, gist_set=rule)
     assert gsa.gsa_profile_marks() == gsa.launches(gsa.hier_params(base, G, k2)) + 1
 
 

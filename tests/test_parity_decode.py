@@ -211,11 +211,11 @@ def test_decode_full_size_sampled(gsa, name):
 
 # ------------------------------------------------------------ two-level ---
 
-def run_hier(gsa, inp, cfg, units=None):
+def run_hier(gsa, inp, cfg, units=None, gist_set="all"):
     b = cfg.base
     out, lse, s2, s1 = gsa.gsa_decode_hier(inp.q, inp.k_cache, inp.v_cache, inp.k_l2, inp.v_l2,
                                            chunk=b.chunk, fanout=cfg.fanout, topk1=b.topk,
-                                           topk2=cfg.topk2, tail=b.tail, n_gist=b.M)
+                                           topk2=cfg.topk2, tail=b.tail, n_gist=b.M, gist_set=gist_set)
     torch.cuda.synchronize()
     g = b.n_q_heads // b.n_kv_heads
     us = ([(x, j) for x in range(b.batch) for j in range(b.n_kv_heads)] if units is None
@@ -226,7 +226,7 @@ def run_hier(gsa, inp, cfg, units=None):
                                     to_np(inp.v_cache[x, j]), to_np(inp.k_l2[x, j]),
                                     to_np(inp.v_l2[x, j]), n_raw=b.n_raw, n_gist=b.M,
                                     chunk=b.chunk, fanout=cfg.fanout, topk1=b.topk,
-                                    topk2=cfg.topk2, tail=b.tail)
+                                    topk2=cfg.topk2, tail=b.tail, gist_set=gist_set)
         if cfg.topk2 > 0:
             np.testing.assert_array_equal(to_np(s2[x, j]), r["sel2"])
         if b.topk > 0:
@@ -266,6 +266,34 @@ def test_hier_small(gsa, kw):
     say(f"hier small {kw} G={fanout} k2={topk2}")
     inp = gi.make_hier(cfg, 3000, device="cuda")
     err = run_hier(gsa, inp, cfg)
+    say(f"  max err / rms = {err:.2e}")
+
+
+# the selection rules on the split path (fp32, head_dim 64, k1 > 64): the
+# level-2 and candidate passes only route, the set's own pass attends
+HIER_SPLIT_SET_CASES = [
+    dict(batch=1, n_kv_heads=2, n_q_heads=8, dtype="f32", head_dim=64, n_raw=16 * (16 * 20 + 5) + 9,
+         n_gist=16 * 20 + 5, fanout=16, topk2=3, topk=10, plant="none"),          # orphans + partial chunk
+    dict(batch=2, n_kv_heads=2, n_q_heads=4, head_dim=64, n_raw=16 * 8 * 40 + 16 * 5, fanout=8, topk2=6,
+         topk=12),                                                               # bf16, D = 64
+    dict(batch=1, n_kv_heads=2, n_q_heads=8, n_raw=16 * 16 * 2000, fanout=16, topk2=8, topk=80),   # k1 > 64
+    dict(batch=1, n_kv_heads=2, n_q_heads=8, dtype="f32", head_dim=64, n_raw=16 * 16 * 2000, fanout=16,
+         topk2=8, topk=16),                                                      # level-2 candidates
+    dict(batch=1, n_kv_heads=2, n_q_heads=8, dtype="f32", head_dim=64, n_raw=16 * 16 * 8 + 7, fanout=16,
+         topk2=2, topk=0, plant="none"),                                         # k1 = 0: the tail only
+]
+
+
+@pytest.mark.parametrize("gist_set", ["selected", "none"])
+@pytest.mark.parametrize("kw", HIER_SPLIT_SET_CASES)
+def test_hier_split_selection_rules(gsa, kw, gist_set):
+    kw = dict(kw)
+    fanout, topk2 = kw.pop("fanout"), kw.pop("topk2")
+    base = dataclasses.replace(gi.CONFIGS["hier_1m"].base, **kw)
+    cfg = gi.HierConfig(base, fanout, topk2)
+    say(f"hier split {gist_set} {kw} G={fanout} k2={topk2}")
+    inp = gi.make_hier(cfg, 3100, device="cuda")
+    err = run_hier(gsa, inp, cfg, gist_set=gist_set)
     say(f"  max err / rms = {err:.2e}")
 
 

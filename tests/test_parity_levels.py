@@ -217,26 +217,33 @@ def test_levels_varlen_equal_lengths_is_levels(gsa):
 # ------------------------------------------------------ selection rules ---
 
 @pytest.mark.parametrize("gist_set", ["selected", "none"])
-@pytest.mark.parametrize("i", [0, 2, 4])
+@pytest.mark.parametrize("i", [0, 1, 2, 4, 7, 8])
 def test_levels_selection_rules(gsa, i, gist_set):
     """The slide 17 rules on L-level decode (R20: every level's gists route,
-    the rule picks which gists are attended): one launch (top level in LDS)
-    and the two-launch path (top level above 4096 gists), against the oracle
-    with the same rule."""
-    c = CASES[i]
+    the rule picks which gists are attended): one launch (top level in LDS),
+    the two-launch path (top level above 4096 gists) and the per-level split
+    path (fp32 with D = 64, k_1 > 64, k_1 = 0), against the oracle with the
+    same rule."""
+    c = CASES[i] if i < len(CASES) else None
     if i == 4:
         # three levels with a top level of 5000 gists: the stream launch, then the descent
         c = dict(B=1, Hq=8, Hkv=2, D=128, C=4, M=5000 * 16, r=2, G=4, topks=[8, 6, 4], T=16)
+    if i == 8:
+        # the split path with k_1 = 0: the levels only route, the set is the tail
+        c = dict(CASES[1], topks=[0, 10, 5, 3])
     B, Hq, Hkv, D, C, M, r, G, topks, T = (c[k] for k in ("B", "Hq", "Hkv", "D", "C", "M", "r", "G", "topks", "T"))
-    if c.get("dtype", "bf16") != "bf16":
-        pytest.skip("the rules run on the bf16 path")
+    dtype = c.get("dtype", "bf16")
+    split = i in (1, 7, 8)
     say(f"levels {gist_set} {c}")
     L = len(topks)
     N = M * C + r
-    q, k, v, ku, vu = gi.make_levels(B, Hq, Hkv, D, N, M, C, G, L, 9300 + i, device="cuda", values="int")
+    q, k, v, ku, vu = gi.make_levels(B, Hq, Hkv, D, N, M, C, G, L, 9300 + i, device="cuda", dtype=dtype,
+                                     values="int")
     out, lse, sels = gsa.gsa_decode_levels(q, k, v, ku, vu, chunk=C, fanout=G, topks=topks, tail=T, n_gist=M,
                                            gist_set=gist_set)
     torch.cuda.synchronize()
+    if split:   # one pass per level, then the set's pass
+        assert gsa.gsa_profile_marks() - 1 == L + 1
     g = Hq // Hkv
     got, ref = [], []
     units = [(b, j) for b in range(B) for j in range(Hkv)]
@@ -250,8 +257,8 @@ def test_levels_selection_rules(gsa, i, gist_set):
                                               err_msg=f"unit {(b, j)} level {lvl + 1}")
         got.append(to_np(out[b, j * g:(j + 1) * g]))
         ref.append(r_["out"])
-        check_lse(to_np(lse[b, j * g:(j + 1) * g]), r_["lse"], "bf16", f"unit {(b, j)}")
-    err = check_out(np.stack(got), np.stack(ref), "bf16", str(c))
+        check_lse(to_np(lse[b, j * g:(j + 1) * g]), r_["lse"], dtype, f"unit {(b, j)}")
+    err = check_out(np.stack(got), np.stack(ref), dtype, str(c))
     say(f"  max err / rms = {err:.2e}, {gsa.gsa_profile_marks() - 1} launches")
 
 
