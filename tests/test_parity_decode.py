@@ -209,6 +209,18 @@ def test_decode_full_size_sampled(gsa, name):
     say(f"  sampled max err / rms = {err:.2e}")
 
 
+@pytest.mark.parametrize("name,dtype,topk", [("gqa_32k", "f32", 64), ("c8_131k", "bf16", 80)])
+def test_decode_full_size_split_path_sampled(gsa, name, dtype, topk):
+    """The split path (fp32; bf16 with k > 64) at a full workload size: every
+    unit's selection against the oracle's on sampled units, their outputs
+    element by element."""
+    cfg = dataclasses.replace(gi.CONFIGS[name], dtype=dtype, topk=topk, plant="none")
+    say(f"decode full split path {name} {dtype} k={topk}")
+    inp = gi.make_decode(cfg, 1100, device="cuda")
+    err = run_decode(gsa, inp, cfg, units=sample_units(cfg, n=4, seed=7))
+    say(f"  sampled max err / rms = {err:.2e}")
+
+
 # ------------------------------------------------------------ two-level ---
 
 def run_hier(gsa, inp, cfg, units=None, gist_set="all"):
