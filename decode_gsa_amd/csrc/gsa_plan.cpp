@@ -359,9 +359,9 @@ gsa_status_t plan_prefill(const gsa_prefill_params* p, PrefillPlan* o) {
   if (isnan(p->scale)) return fail(GSA_ERR_INVALID_ARG, "scale is NaN");
   if (p->topk < 0) return fail(GSA_ERR_INVALID_ARG, "topk=%d is negative", p->topk);
   if (p->window < 1) return fail(GSA_ERR_INVALID_ARG, "window=%d must be >= 1", p->window);
-  if (p->q_start < 0 || p->n_q < 0 || p->q_start + p->n_q > p->n_raw)
-    return fail(GSA_ERR_INVALID_ARG, "query range [%lld, %lld) outside [0, n_raw=%lld)",
-                (long long)p->q_start, (long long)(p->q_start + p->n_q), (long long)p->n_raw);
+  if (p->q_start < 0 || p->n_q < 0 || p->q_start > p->n_raw || p->n_q > p->n_raw - p->q_start)
+    return fail(GSA_ERR_INVALID_ARG, "query range of %lld from %lld outside [0, n_raw=%lld)",
+                (long long)p->n_q, (long long)p->q_start, (long long)p->n_raw);
   if (p->head_dim != 128) return fail(GSA_ERR_UNSUPPORTED, "prefill needs head_dim=128");
   if (p->dtype != GSA_BF16) return fail(GSA_ERR_UNSUPPORTED, "prefill needs bf16 inputs");
   const int32_t g = p->n_q_heads / p->n_kv_heads;
@@ -526,8 +526,9 @@ gsa_status_t plan_gist(const gsa_gist_params* p, PrefillPlan* o) {
   if (p->m_start < 0 || p->n_q < 0 || p->m_start > p->n_raw || p->n_q > p->n_raw)
     return fail(GSA_ERR_INVALID_ARG, "gist queries [%lld, +%lld) outside the sequence", (long long)p->m_start,
                 (long long)p->n_q);
+  if (p->n_raw > ((int64_t)1 << 40)) return fail(GSA_ERR_UNSUPPORTED, "n_raw too large");
   const int64_t m_end = p->m_start + p->n_q;
-  if (p->n_q > 0 && m_end * p->chunk > p->n_raw)
+  if (p->n_q > 0 && m_end > p->n_raw / p->chunk)
     return fail(GSA_ERR_INVALID_ARG, "chunk %lld is not complete (n_raw=%lld, chunk=%d)", (long long)(m_end - 1),
                 (long long)p->n_raw, p->chunk);
   if (p->n_q > 0 && m_end - 1 > p->n_gist)
@@ -751,7 +752,7 @@ extern "C" gsa_status_t gsa_topk_for_budget(int64_t budget, int64_t n_gist, int3
   if (gist_set < GSA_GISTS_ALL || gist_set > GSA_GISTS_NONE)
     return gsa::fail(GSA_ERR_INVALID_ARG, "gist_set=%d not in {0, 1, 2}", gist_set);
   const int64_t fixed = (gist_set == GSA_GISTS_ALL ? n_gist : 0) + tail;   // tokens with k = 0
-  const int64_t per = chunk + (gist_set == GSA_GISTS_SELECTED ? 1 : 0);     // tokens per chosen chunk
+  const int64_t per = (int64_t)chunk + (gist_set == GSA_GISTS_SELECTED ? 1 : 0);   // tokens per chosen chunk
   if (budget < fixed)
     return gsa::fail(GSA_ERR_INVALID_ARG, "budget %lld is below the %lld tokens of the set with k = 0",
                      (long long)budget, (long long)fixed);

@@ -210,6 +210,7 @@ def good_prefill(**kw):
     ({"topk": -1}, INVALID),
     ({"q_start": -1}, INVALID),
     ({"n_q": 1025}, INVALID),                   # runs past n_raw
+    ({"n_q": (1 << 63) - 1}, INVALID),          # q_start + n_q would wrap below n_raw
     ({"n_gist": 257}, INVALID),
     ({"n_q_heads": 12, "n_kv_heads": 4}, UNSUPPORTED),
     ({"n_q_heads": 16, "n_kv_heads": 2}, OK),            # g = 8
@@ -288,6 +289,9 @@ def test_topk_for_budget_matches_the_oracle(L, gist_set):
     assert L.gsa_topk_for_budget(100, 10, 0, 0, 0, ctypes.byref(k)) == INVALID    # chunk < 1
     assert L.gsa_topk_for_budget(100, 10, 4, 0, 3, ctypes.byref(k)) == INVALID    # gist_set
     assert L.gsa_topk_for_budget(100, 10, 4, 0, 0, None) == INVALID
+    # the largest chunk with the chosen gists: no 32-bit wrap in tokens per chunk
+    assert L.gsa_topk_for_budget(1 << 40, 10, 2**31 - 1, 0, 1, ctypes.byref(k)) == OK and k.value == 10
+    assert L.gsa_topk_for_budget(2**31 - 1, 10, 2**31 - 1, 0, 1, ctypes.byref(k)) == OK and k.value == 0
 
 
 # ------------------------------------------------ gist prefill, cache append ---
@@ -316,6 +320,9 @@ def good_gist(**kw):
     ({"chunk": 0}, INVALID),
     ({"row_capacity": 1000}, INVALID),
     ({"n_q": 0}, OK),                   # nothing to launch: NULL q and out are allowed
+    # ranges whose end overflows 64 bits are rejected, not wrapped
+    ({"n_raw": 1 << 62, "m_start": 1 << 61, "n_q": 1 << 62}, UNSUPPORTED),
+    ({"m_start": (1 << 63) - 1, "n_q": 1}, INVALID),
 ])
 def test_gist_prefill_validation(L, kw, status):
     """Shape errors come back with their status; shapes that pass validation
