@@ -215,7 +215,8 @@ __device__ __forceinline__ void hier_lengths(const SeqLens& sl, int unit, int64_
 // Stream items [i0, i1) of one unit through the online softmax. row_of(i)
 // gives the cache row of item i; with CAN_SKIP it may return -1 to skip the
 // item. When score_out is set (LDS), the group score of item i goes to
-// score_out[i - i0].
+// score_out[i - i0]; with score_only the V rows are neither read nor folded
+// in (the items only route: their scores are all that is kept).
 //
 // Rows are double-buffered in registers: the loads of the next batch are in
 // flight while the current one is folded in. A batch is kU rows per lane group
@@ -231,7 +232,7 @@ __device__ __forceinline__ void stream_rows(const char* __restrict__ Kb, const c
                                             int64_t i0, int64_t i1, RowOf row_of,
                                             const uint4 (&qv)[G], State<BF16, G>& st,
                                             float scale_log2, float* __restrict__ score_out,
-                                            float score_mul) {
+                                            float score_mul, bool score_only = false) {
   using Gm = Geo<BF16, D>;
   constexpr int VEC = Gm::VEC, LPR = Gm::LPR, NS = Gm::NS;
   const int lane = threadIdx.x & 63;
@@ -257,7 +258,7 @@ __device__ __forceinline__ void stream_rows(const char* __restrict__ Kb, const c
       if (row >= 0) {
         const size_t off = (size_t)row * Gm::ROW_BYTES + lane_off;
         b.k[u] = load16_stream(Kb + off);
-        b.v[u] = load16_stream(Vb + off);
+        b.v[u] = score_only ? make_uint4(0u, 0u, 0u, 0u) : load16_stream(Vb + off);
       } else {
         b.k[u] = make_uint4(0u, 0u, 0u, 0u);
         b.v[u] = make_uint4(0u, 0u, 0u, 0u);
@@ -282,6 +283,7 @@ __device__ __forceinline__ void stream_rows(const char* __restrict__ Kb, const c
         }
       }
     }
+    if (score_only) return;
 #pragma unroll
     for (int u = 0; u < kU; ++u)
 #pragma unroll
@@ -979,6 +981,9 @@ struct GistArgs {
   int64_t sel_stride;
   int32_t* sel_out;       // [units][k] or null
   SeqLens seq;            // single-level decode: per-sequence lengths
+  // selection rules: the items only route (scores out, no V read); the
+  // partial state written is the empty one and is never merged
+  int32_t score_only;
 };
 
 template <int D, int G>
@@ -1035,7 +1040,7 @@ void gist_kernel(GistArgs a) {
   stream_rows<BF16, D, G, false>(reinterpret_cast<const char*>(a.K) + ub,
                                  reinterpret_cast<const char*>(a.V) + ub, i0, i1,
                                  [&](int64_t i) { return map_row(rm, 0, i); }, qv, st,
-                                 a.scale_log2, lds.scores, a.score_mul);
+                                 a.scale_log2, lds.scores, a.score_mul, a.score_only != 0);
   // this workgroup's share of the tail
   const int64_t t0 = (int64_t)split * a.tail_per_task;
   const int64_t t1 = t0 + a.tail_per_task < a.T ? t0 + a.tail_per_task : a.T;
@@ -1283,6 +1288,7 @@ gsa_status_t run_decode(const DecodePlan& pl, const void* q, const void* K, cons
   // is nothing to score
   const bool sets = pl.gist_set != GSA_GISTS_ALL;
   if (sets) g.tail_per_task = 0;
+  g.score_only = sets ? 1 : 0;
   prof_begin_call();
   if (!sets || pl.k > 0)
     prof_launch((gist_kernel<BF16, D, G>), dim3(pl.units * pl.S), dim3(kThreads), 0, st, g);
@@ -1343,6 +1349,7 @@ gsa_status_t run_hier(const HierPlan& hp, const void* q, const void* K, const vo
   // states are not merged) and the tail goes to the set's pass
   const bool sets = pl.gist_set != GSA_GISTS_ALL;
   g.N = pl.N; g.M = pl.M; g.C = pl.C; g.T = pl.T; g.tail_per_task = sets ? 0 : hp.tail_per_split;
+  g.score_only = sets ? 1 : 0;
   g.scores = s2; g.score_stride = hp.s2_stride;
   g.part = part; g.part_stride = ps; g.NP = hp.NP; g.part_base = 0;
   g.out = nullptr; g.lse = nullptr;
@@ -3196,6 +3203,7 @@ gsa_status_t run_levels(const LevelsPlan& lp, const void* q, const void* K, cons
   // not merged) and the tail goes to the set's pass
   const bool sets = pl.gist_set != GSA_GISTS_ALL;
   g.N = pl.N; g.M = pl.M; g.C = pl.C; g.T = pl.T; g.tail_per_task = sets ? 0 : lp.tail_per_split;
+  g.score_only = sets ? 1 : 0;
   g.scores = scores(L); g.score_stride = lp.score_stride[L];
   g.part = part; g.part_stride = ps; g.NP = lp.NP; g.part_base = 0;
   g.out = nullptr; g.lse = nullptr;
