@@ -324,7 +324,8 @@ def run_decode_bench(args):
     lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
     sel = torch.empty(B, cfg.n_kv_heads, max(cfg.topk, 1), dtype=torch.int32, device=dev)
     p = gsa.decode_params(B, Hq, cfg.n_kv_heads, D, cfg.n_raw, cfg.M, cfg.chunk, cfg.topk,
-                          cfg.tail, 0.0, gsa.GSA_BF16 if cfg.dtype == "bf16" else gsa.GSA_F32)
+                          cfg.tail, 0.0, gsa.GSA_BF16 if cfg.dtype == "bf16" else gsa.GSA_F32,
+                          gist_set=gsa.GIST_SETS[args.gist_set])
     ws = gsa.new_workspace(gsa.decode_workspace_size(p), dev)
 
     def step(i):
@@ -351,13 +352,13 @@ def run_decode_bench(args):
     call_ms = float(per.sum(axis=1).mean())
     qheads = B * Hq
     sha = source_sha("gsa_decode.hip", "gsa_device.hpp")
+    if args.gist_set != "all":
+        # with the selection rules the scoring launch reads the gists' K rows
+        # only; the set (tail included) is read by the launch that attends it
+        tail_b = cfg.batch * cfg.n_kv_heads * cfg.tail * 2 * cfg.head_dim * (2 if cfg.dtype == "bf16" else 4)
+        gist_b, unfold_b = gist_b - tail_b, unfold_b + tail_b
     if unit_path and n_marks == 2:
         names, nbytes = ["unit_kernel"], [alg_b]
-    elif unit_path and args.gist_set != "all":
-        # the scoring launch reads the gists' K rows; the set (tail included)
-        # is read by the second launch
-        tail_b = cfg.batch * cfg.n_kv_heads * cfg.tail * 2 * cfg.head_dim * 2
-        names, nbytes = ["unit_kernel", "unit_unfold_kernel"], [gist_b - tail_b, unfold_b + tail_b]
     elif unit_path:
         names, nbytes = ["unit_kernel", "unit_unfold_kernel"], [gist_b, unfold_b]
     elif n_marks == 4:   # gist pass, per-split candidates, unfold
