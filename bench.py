@@ -427,11 +427,13 @@ def run_decode_bench(args):
 
 # ------------------------------------------------------------- two-level ---
 
-def hier_bytes(cfg, sel1):
+def hier_bytes(cfg, sel1, gist_set="all"):
     """Algorithmic bytes per two-level call: every level-2 gist row, the level-1
     gists of the candidate groups and the orphans, the raw rows of the chosen
     chunks outside the tail, the tail rows (K + V each), q, and the fp32
-    out/lse and both id lists."""
+    out/lse and both id lists. With gist_set "selected" / "none" the level-2
+    and candidate gists are read for their K rows only (they route), the tail
+    moves to the set's part, and "selected" adds the chosen gists' V rows."""
     b = cfg.base
     eb = 2 if b.dtype == "bf16" else 4
     row = 2 * b.head_dim * eb
@@ -445,6 +447,11 @@ def hier_bytes(cfg, sel1):
                 raw_sel += max(0, min(b.chunk, tail0 - int(m) * b.chunk))
     q = b.batch * b.n_q_heads * b.head_dim * eb
     out = b.batch * b.n_q_heads * (b.head_dim + 1) * 4 + units * (b.topk + cfg.topk2) * 4
+    if gist_set != "all":
+        return {"l2": units * cfg.M2 * (row // 2) + q,
+                "cand": units * n_cand * (row // 2),
+                "unfold": raw_sel * row + units * b.tail * row
+                + (units * b.topk * (row // 2) if gist_set == "selected" else 0) + out}
     return {"l2": units * cfg.M2 * row + units * b.tail * row + q,
             "cand": units * n_cand * row,
             "unfold": raw_sel * row + out}
@@ -474,7 +481,8 @@ def run_hier_bench(args):
     s2 = torch.empty(B, b.n_kv_heads, max(cfg.topk2, 1), dtype=torch.int32, device=dev)
     s1 = torch.empty(B, b.n_kv_heads, max(b.topk, 1), dtype=torch.int32, device=dev)
     base = gsa.decode_params(B, Hq, b.n_kv_heads, D, b.n_raw, b.M, b.chunk, b.topk, b.tail, 0.0,
-                             gsa.GSA_BF16 if b.dtype == "bf16" else gsa.GSA_F32)
+                             gsa.GSA_BF16 if b.dtype == "bf16" else gsa.GSA_F32,
+                             gist_set=gsa.GIST_SETS[args.gist_set])
     ws = gsa.new_workspace(gsa.hier_workspace_size(gsa.hier_params(base, cfg.fanout, cfg.topk2)), dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -482,14 +490,14 @@ def run_hier_bench(args):
         k, v, k2, v2 = caches[i % layers]
         gsa.gsa_decode_hier(inp.q, k, v, k2, v2, chunk=b.chunk, fanout=cfg.fanout, topk1=b.topk,
                             topk2=cfg.topk2, tail=b.tail, n_gist=b.M, out=out, lse=lse, sel2=s2,
-                            sel1=s1, workspace=ws, stream=stream)
+                            sel1=s1, workspace=ws, stream=stream, gist_set=args.gist_set)
 
     step(0)
     torch.cuda.synchronize()
     if inp.planted2 is not None:
         assert torch.equal(s2.long(), inp.planted2), "level-2 selection differs from the planted set"
         assert torch.equal(s1.long(), inp.planted1), "level-1 selection differs from the planted set"
-    nb = hier_bytes(cfg, s1.cpu().numpy() if b.topk else [])
+    nb = hier_bytes(cfg, s1.cpu().numpy() if b.topk else [], args.gist_set)
     n_marks = gsa.gsa_profile_marks()
     if n_marks == 2:   # unit_kernel over level 2 + tail, its last workgroup per unit descends
         names = ["unit_kernel (level 2 + descent)"]
@@ -524,7 +532,9 @@ def run_hier_bench(args):
         "data": "synthetic (seeded Gaussian q/K/V, planted top-k at both levels with margin >= 0.5)",
         "config": {"workload": f"{cfg.name}: two-level GQA decode step, B={b.batch}, Hq={b.n_q_heads}, "
                                f"Hkv={b.n_kv_heads}, D={b.head_dim}, N={b.n_raw}, C={b.chunk}, "
-                               f"G={cfg.fanout}, k2={cfg.topk2}, k1={b.topk}, T={b.tail}",
+                               f"G={cfg.fanout}, k2={cfg.topk2}, k1={b.topk}, T={b.tail}"
+                               + ("" if args.gist_set == "all" else
+                                  f", attention set: {GIST_SET_NAMES[args.gist_set]}"),
                    "global_batch": b.batch, "seq_len": b.n_raw, "parallelism": "none (1 GPU)",
                    "cache_layers_rotated": layers},
         "roofline": {"bound": "hbm", "achieved": alg_b / (call_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBPS,
