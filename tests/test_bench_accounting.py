@@ -43,3 +43,14 @@ def test_hier_bytes_hier_1m():
     assert none["unfold"] == 32 * (256 + 64) * 512 + out
     assert sum(none.values()) == 39_947_776
     assert sum(bench.hier_bytes(cfg, sel1, "selected").values()) == 39_947_776 + 32 * 16 * 256
+
+
+def test_prefill_flops_prefill_64k():
+    cfg = gi.CONFIGS["prefill_64k"]             # queries 61440..65535, C 16, k 16, window 64, Hq 32, D 128
+    # eligible gists floor(t / 16): each of 3840..4095 for 16 queries; 16 chosen chunks of 16
+    # rows and a 64-row window for every query; 4 D flops per (query head, row)
+    gists = 16 * sum(range(3840, 4096))
+    rows = gists + 4096 * 16 * 16 + 4096 * 64
+    total, gist_qk = bench.prefill_flops(cfg)
+    assert total == rows * 32 * 128 * 4 == 287_733_350_400
+    assert gist_qk == gists * 32 * 128 * 2
