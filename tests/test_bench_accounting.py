@@ -54,3 +54,18 @@ def test_prefill_flops_prefill_64k():
     total, gist_qk = bench.prefill_flops(cfg)
     assert total == rows * 32 * 128 * 4 == 287_729_254_400
     assert gist_qk == gists * 32 * 128 * 2
+
+
+def test_counter_traffic_only_for_the_source_it_was_taken_on():
+    """The committed counter bytes are reported only while the kernel source
+    they were measured on is the one built; they equal the scaled counters
+    (FETCH_SIZE x 2, WRITE_SIZE x 1, KiB -> bytes)."""
+    import json
+    t = json.load(open(bench.TRAFFIC_FILE))
+    for key, e in t.items():
+        if key.startswith("_"):
+            continue
+        scaled = (e["fetch_kib"] * e["fetch_scale"] + e["write_kib"] * e["write_scale"]) * 1024
+        assert abs(e["bytes_per_launch"] - scaled) <= 1024, key
+        assert bench.measured_traffic(key, e["source_sha"]) == e["bytes_per_launch"]
+        assert bench.measured_traffic(key, "0" * 16) is None
